@@ -1,0 +1,295 @@
+/*
+ * kvcache.h -- C ABI of libkvcache.so: a layer-bound, fixed-capacity KV cache
+ * with a cached decode step and a prefix-cut continuation, on AMD MI355X (gfx950).
+ *
+ * Sources.  "Chapter 37" is the incremental-attention course chapter "Keep the
+ * prefix, project only the new row" (intale.github.io learn_llm).  "The
+ * prefix-reuse note" is "LLM mechanism experiment (5): can only the changed
+ * suffix be recomputed?" (huhohoo.com).  Each declaration names the passage
+ * that defines its operation.
+ *
+ * Conventions for every call.
+ *  - Every call returns kvc_status; KVC_OK is 0.  On any other status the
+ *    cache's logical state (lengths, next positions, row positions, rows below
+ *    the length) AND its whole physical storage are unchanged (Chapter 37,
+ *    "Reset or reject without corrupting retained state"), and
+ *    kvc_last_error() describes the failure.
+ *  - Device pointers are HIP device memory on the cache's device.  Host
+ *    pointers are ordinary host memory.  Each argument below says which.
+ *  - All work of one cache is ordered on the HIP stream given at creation.  A
+ *    handle is not thread-safe; use one cache from one thread at a time.
+ *  - Weights, inputs and outputs are borrowed: the caller owns them and keeps
+ *    them alive until the call (in KVC_ASYNC mode: the stream work) completes.
+ *    The library owns the K/V storage, lengths, positions, candidate rows,
+ *    scratch and the rotary table, allocated only in kvc_cache_create and
+ *    freed only in kvc_cache_destroy.
+ */
+#ifndef KVCACHE_H
+#define KVCACHE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t kvc_status;
+
+enum {
+  KVC_OK = 0,
+  /* Cache construction, checked in this order (Chapter 37, layer-kv-cache
+   * listing: the cache constructor and its error enum). */
+  KVC_ERR_ZERO_BATCH = 1,
+  KVC_ERR_ZERO_CAPACITY = 2,
+  KVC_ERR_CAPACITY_EXCEEDS_POSITIONS = 3, /* capacity > rotary max positions          */
+  KVC_ERR_ELEMENT_COUNT_OVERFLOW = 4,     /* B*H*C*d_h does not fit 64-bit indexing    */
+  KVC_ERR_ALLOCATION_FAILED = 5,          /* device or pinned host allocation failed   */
+  /* Request checks, in the order Chapter 37 gives under "Bind the state,
+   * calculate completely, then commit": rank, one token, batch, width, cache
+   * model width, heads, head width, parameter identity, parameter revision,
+   * rotary configuration, remaining capacity. */
+  KVC_ERR_INPUT_RANK = 10,
+  KVC_ERR_SINGLE_TOKEN_REQUIRED = 11,
+  KVC_ERR_INPUT_BATCH_MISMATCH = 12,
+  KVC_ERR_INPUT_WIDTH_MISMATCH = 13,
+  KVC_ERR_CACHE_MODEL_WIDTH_MISMATCH = 14,
+  KVC_ERR_CACHE_HEAD_COUNT_MISMATCH = 15,
+  KVC_ERR_CACHE_HEAD_WIDTH_MISMATCH = 16,
+  KVC_ERR_CACHE_LAYER_MISMATCH = 17,          /* weights are not the bound parameter set */
+  KVC_ERR_CACHE_LAYER_REVISION_MISMATCH = 18, /* bound weights were updated in place    */
+  KVC_ERR_CACHE_ROPE_MISMATCH = 19,           /* feature width, max positions or base   */
+  KVC_ERR_FULL = 20,                          /* a sequence has no room for the rows    */
+  /* Found on the device before the commit; the commit is then suppressed.
+   * Precedence when several hold: key, value, query, position, output. */
+  KVC_ERR_NONFINITE_KEY = 30,    /* candidate rotated key has a NaN/Inf (first flat index) */
+  KVC_ERR_NONFINITE_VALUE = 31,  /* candidate value has a NaN/Inf                          */
+  KVC_ERR_NONFINITE_QUERY = 32,  /* rotated query has a NaN/Inf                            */
+  KVC_ERR_ROTARY_POSITION = 33,  /* a row's position reaches the rotary max positions      */
+  KVC_ERR_NONFINITE_OUTPUT = 34, /* softmax or mixture produced a NaN/Inf                  */
+  /* Continuation (prefix-reuse note). */
+  KVC_ERR_BAD_CUT = 40,          /* cut < 0 or cut > current length                        */
+  KVC_ERR_EMPTY_QUERY = 41,      /* lcp query with no tokens                               */
+  KVC_ERR_CHUNK_ROWS = 42,       /* n_max outside [1, max_chunk_rows] or n_rows[b] outside [0, n_max] */
+  /* Interface. */
+  KVC_ERR_NULL_ARGUMENT = 50,
+  KVC_ERR_DTYPE_UNSUPPORTED = 51,
+  KVC_ERR_SHAPE_UNSUPPORTED = 52, /* head width not a power of two in [2, 16 B * 64 / elem] */
+  KVC_ERR_BAD_ARGUMENT = 53,
+  KVC_ERR_DEVICE = 60,           /* a HIP runtime call failed                              */
+  KVC_ERR_DEFERRED = 61,         /* an earlier KVC_ASYNC call failed on the device         */
+  KVC_ERR_INTERNAL = 62
+};
+
+/* Storage / arithmetic type.  A cache's K/V storage type must equal its
+ * weights' type; F64 computes in double, F32 and BF16 accumulate in float. */
+typedef enum { KVC_F64 = 0, KVC_F32 = 1, KVC_BF16 = 2 } kvc_dtype;
+
+/* Position handling of a layer.  ROPE rotates q and k by rotate-half RoPE at
+ * their absolute position (Chapter 37, "Append along the position axis").
+ * NONE applies no rotation: the caller adds absolute position encodings to the
+ * hidden rows itself, as the prefix-reuse note's toy decoder does. */
+typedef enum { KVC_POS_ROPE = 0, KVC_POS_NONE = 1 } kvc_pos_mode;
+
+/* Call flags. */
+enum {
+  KVC_SYNC = 0,  /* wait for the stream; device-found errors are returned directly */
+  KVC_ASYNC = 1  /* return after enqueueing; a device-found error is sticky, every
+                    later commit on the cache is suppressed, and the next KVC_SYNC
+                    call or kvc_sync() returns KVC_ERR_DEFERRED with its detail.
+                    Outputs of calls made after a failed one are undefined. */
+};
+
+/* kvc_truncate flags. */
+enum {
+  KVC_TRUNCATE_KEEP_STALE_POSITION = 1 /* negative control of the prefix-reuse note
+                                          ("What must be trimmed together"): trims the
+                                          rows but leaves next_position unchanged.
+                                          For tests; it produces wrong results. */
+};
+
+/* Payload of the last failure on the calling thread (Chapter 37 error enums). */
+typedef struct {
+  kvc_status status;
+  int32_t parameter;        /* revision mismatch: first weight that differs (0 W_q, 1 W_k, 2 W_v) */
+  int32_t sequence;         /* sequence index for FULL, BAD_CUT, CHUNK_ROWS, ROTARY_POSITION */
+  int32_t reserved;
+  int64_t expected, actual; /* rank, tokens, batch, width, heads, head width, capacity, ... */
+  uint64_t cache_revision, layer_revision;
+  int64_t flat_index;       /* NONFINITE_*: first flat index over the candidate [B,H,n,d_h]  */
+  double value;             /* NONFINITE_KEY/VALUE: the offending element                    */
+  int32_t rope_feature_width[2]; /* ROPE_MISMATCH: [cache, layer]                            */
+  int32_t rope_max_positions[2];
+  double rope_base[2];
+  char message[256];
+} kvc_error_detail;
+
+/* Projection-row counts of one call, per Q, K or V projection, summed over
+ * the batch (Chapter 37, "Count projection rows, not hardware time"):
+ * decode: full = sum(len_b + 1), incremental = B, reused = sum(len_b);
+ * chunk:  full = sum(len_b + n_b), incremental = sum(n_b), reused = sum(len_b).
+ * position_min/max: smallest and largest absolute position computed. */
+typedef struct {
+  int64_t full_prefix_rows_per_projection;
+  int64_t incremental_rows_per_projection;
+  int64_t reused_key_value_rows;
+  int32_t position_min, position_max;
+} kvc_work;
+
+/* Geometry of a cache, for callers that size buffers. */
+typedef struct {
+  int32_t batch, heads, head_width, model_width, capacity, max_chunk_rows;
+  int32_t kv_dtype, pos_mode, rope_max_positions, device;
+  double rope_base;
+} kvc_cache_desc;
+
+typedef struct kvc_params kvc_params; /* W_q, W_k, W_v with an identity and per-weight revisions */
+typedef struct kvc_layer kvc_layer;   /* parameters + head count + position handling           */
+typedef struct kvc_cache kvc_cache;   /* one layer's fixed-capacity K/V state                  */
+
+/* Registers a parameter set.  w_q, w_k, w_v: DEVICE, each [D, D] row-major as
+ * [out, in] (a projected row is y[j] = sum_i x[i] W[j, i]), element type
+ * `dtype`, borrowed.  Each call creates a new identity, so a rebuilt layer
+ * with equal shapes and values is still a different parameter set (Chapter
+ * 37, "Bind the state, calculate completely, then commit").
+ * Errors: NULL_ARGUMENT, BAD_ARGUMENT (D <= 0), DTYPE_UNSUPPORTED. */
+kvc_status kvc_params_create(int32_t model_width, kvc_dtype dtype, const void* w_q,
+                             const void* w_k, const void* w_v, kvc_params** out);
+
+/* Records an in-place update of weight `which` (0 W_q, 1 W_k, 2 W_v, -1 all):
+ * its value revision advances and caches bound to the old revision reject
+ * further calls (Chapter 37: an optimiser step keeps the identity but advances
+ * the revision).  Errors: NULL_ARGUMENT, BAD_ARGUMENT. */
+kvc_status kvc_params_mark_updated(kvc_params* params, int32_t which);
+void kvc_params_destroy(kvc_params* params);
+
+/* A layer view over a parameter set: `heads` divides D; d_h = D / heads must
+ * be even and a power of two small enough for one wavefront (see
+ * SHAPE_UNSUPPORTED).  Several layers may share one parameter set with
+ * different rotary configurations (Chapter 37 error evidence: same parameters,
+ * doubled base or one more max position).  rope_base > 0, rope_max_positions > 0.
+ * The params handle must outlive the layer.  Errors: NULL_ARGUMENT,
+ * BAD_ARGUMENT, SHAPE_UNSUPPORTED. */
+kvc_status kvc_layer_create(const kvc_params* params, int32_t heads, kvc_pos_mode pos_mode,
+                            double rope_base, int32_t rope_max_positions, kvc_layer** out);
+void kvc_layer_destroy(kvc_layer* layer);
+
+/* Creates an empty cache bound to `layer` (Chapter 37, the cache constructor):
+ * K/V storage [B, H, C, d_h] in the weights' type, zero-filled; lengths and
+ * next positions 0; binding = the layer's parameter identity and current
+ * revisions and its rotary configuration.  max_chunk_rows (>= 1) bounds n_max
+ * of kvc_continue_chunk and sizes its scratch.  hip_stream: a hipStream_t (or
+ * NULL for the null stream) on the current device; all work of this cache runs
+ * on it.  This is the only call that allocates.
+ * Errors, in order: NULL_ARGUMENT, ZERO_BATCH, ZERO_CAPACITY,
+ * CAPACITY_EXCEEDS_POSITIONS, BAD_ARGUMENT (max_chunk_rows < 1),
+ * ELEMENT_COUNT_OVERFLOW, ALLOCATION_FAILED, DEVICE. */
+kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capacity,
+                            int32_t max_chunk_rows, void* hip_stream, kvc_cache** out);
+void kvc_cache_destroy(kvc_cache* cache);
+
+/* The cached decode step (Chapter 37, "Bind the state, calculate completely,
+ * then commit", and the incremental-attention listing).  x: DEVICE, shape
+ * `shape[0..rank-1]`, which must be [B, 1, D] in the weights' type.  For each
+ * sequence b it projects only the new row, rotates q and k at position
+ * next_position[b] (= the old length), scores q against the len[b] retained
+ * keys plus the candidate key with scale 1/sqrt(d_h), applies a stable
+ * softmax, mixes the retained values plus the candidate value, and writes the
+ * merged heads to out (DEVICE, [B, 1, D]; double for F64 caches, float
+ * otherwise).  Only then does it append the rotated key and unrotated value at
+ * row len[b] and advance len[b] and next_position[b] by one (cache
+ * transition, "Append along the position axis").  The output projection is
+ * not applied.  work (HOST, nullable) receives the row counts.
+ * Errors: the request checks above in their order, then the device-found
+ * ones; DEFERRED. */
+kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const void* x,
+                                 int32_t rank, const int64_t* shape, void* out, int32_t flags,
+                                 kvc_work* work);
+
+/* Suffix-chunk continuation (prefix-reuse note, "What must be trimmed
+ * together"): x DEVICE [B, n_max, D]; n_rows HOST int32[B] with 0 <= n_b <=
+ * n_max (NULL: every n_b = n_max).  Row i < n_b of sequence b is projected,
+ * rotated at next_position[b] + i, and attends causally to the len[b]
+ * retained rows plus its chunk rows 0..i; out DEVICE [B, n_max, D] (rows
+ * i >= n_b untouched).  Then the n_b rows are appended and len[b] and
+ * next_position[b] advance by n_b.  A prefill is this call on an empty cache.
+ * Errors: NULL_ARGUMENT, CHUNK_ROWS, the binding checks (model width .. rotary
+ * configuration), FULL (len[b] + n_b > C), ROTARY_POSITION, device-found
+ * errors, DEFERRED. */
+kvc_status kvc_continue_chunk(const kvc_layer* layer, kvc_cache* cache, const void* x,
+                              int32_t n_max, const int32_t* n_rows, void* out, int32_t flags,
+                              kvc_work* work);
+
+/* Keeps rows 0..cut[b]-1 of every sequence and sets next_position[b] = cut[b]
+ * (prefix-reuse note, "What must be trimmed together").  cut: HOST int32[B],
+ * 0 <= cut[b] <= len[b].  Moves no K/V data and allocates nothing.
+ * flags: 0 or KVC_TRUNCATE_KEEP_STALE_POSITION.  Errors: NULL_ARGUMENT,
+ * BAD_CUT, BAD_ARGUMENT, DEFERRED, DEVICE. */
+kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags);
+
+/* Logical reset (Chapter 37, "Keep layer, logical length, and capacity
+ * separate"): every length and next position becomes 0; capacity, storage
+ * contents, allocation and the parameter binding are unchanged, so a cache
+ * bound to updated weights stays rejected.  Errors: NULL_ARGUMENT, DEVICE. */
+kvc_status kvc_reset(kvc_cache* cache);
+
+/* Logical snapshot of sequence `seq` (Chapter 37, logical key/value
+ * accessors): keys_out, values_out HOST [H, len, d_h] in the storage type,
+ * positions_out HOST int32[len] (each nullable).  rows_capacity: rows the
+ * buffers hold; rows_out (HOST): len.  Synchronises the stream.  Errors:
+ * NULL_ARGUMENT, BAD_ARGUMENT (seq out of range or rows_capacity < len),
+ * DEFERRED, DEVICE. */
+kvc_status kvc_snapshot(kvc_cache* cache, int32_t seq, void* keys_out, void* values_out,
+                        int32_t* positions_out, int64_t rows_capacity, int32_t* rows_out);
+
+/* Lengths and next positions as committed on the device: HOST int32[B] each
+ * (nullable).  Synchronises the stream.  Errors: NULL_ARGUMENT, DEFERRED, DEVICE. */
+kvc_status kvc_lengths(kvc_cache* cache, int32_t* len_out, int32_t* next_position_out);
+
+/* Waits for the cache's stream and reports a deferred device-found error
+ * (KVC_ERR_DEFERRED; kvc_last_error() then holds the original status in
+ * `actual` and the original detail).  Clears the sticky error and resyncs
+ * the host copy of the lengths. */
+kvc_status kvc_sync(kvc_cache* cache);
+
+/* Longest-common-prefix cut (prefix-reuse note, "First, one history edit" and
+ * "Lookup flow and cache ownership"): the length of the contiguous common
+ * prefix of `cached` and `query`, capped at n_query - 1 so the last query
+ * token is always recomputed.  HOST arrays.  Errors: NULL_ARGUMENT (a NULL
+ * pointer with a positive count), EMPTY_QUERY, BAD_ARGUMENT (n_cached < 0). */
+kvc_status kvc_lcp_cut(const int32_t* cached, int64_t n_cached, const int32_t* query,
+                       int64_t n_query, int64_t* cut_out);
+
+/* Geometry of a cache.  Errors: NULL_ARGUMENT. */
+kvc_status kvc_cache_describe(const kvc_cache* cache, kvc_cache_desc* out);
+
+/* State audits (Chapter 37, "Reset or reject without corrupting retained
+ * state": same allocation, storage unchanged).  kvc_storage_pointers returns
+ * the DEVICE base addresses of the K and V storage and their size in bytes;
+ * kvc_copy_storage copies the whole physical storage [B, H, C, d_h] of each
+ * into HOST buffers of that size (either nullable) after synchronising. */
+kvc_status kvc_storage_pointers(const kvc_cache* cache, const void** keys, const void** values,
+                                int64_t* bytes_each);
+kvc_status kvc_copy_storage(kvc_cache* cache, void* keys_out, void* values_out);
+
+/* Per-stage kernel timing with HIP events on the cache's stream.
+ * kvc_profile_enable(cache, slots): slots > 0 starts recording event pairs
+ * around each stage of each call (at most `slots` calls, then recording
+ * stops); 0 stops and frees them.  kvc_profile_read synchronises and writes
+ * per-stage totals: ms_out[s] (HOST float[KVC_STAGES]) and calls_out[s]
+ * (HOST int32[KVC_STAGES]).  Stages: 0 projection+rotary, 1 attention,
+ * 2 split merge, 3 commit. */
+enum { KVC_STAGE_PROJECT = 0, KVC_STAGE_ATTEND = 1, KVC_STAGE_MERGE = 2, KVC_STAGE_COMMIT = 3,
+       KVC_STAGES = 4 };
+kvc_status kvc_profile_enable(kvc_cache* cache, int32_t slots);
+kvc_status kvc_profile_read(kvc_cache* cache, float* ms_out, int32_t* calls_out);
+
+/* Last failure on the calling thread; never NULL. */
+const kvc_error_detail* kvc_last_error(void);
+/* Symbolic name of a status ("KVC_ERR_FULL"); never NULL. */
+const char* kvc_status_name(kvc_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVCACHE_H */

@@ -1,0 +1,644 @@
+// HIP kernels and device backend of libkvcache for gfx950 (MI355X, CDNA4).
+//
+// Pipeline of one call (Chapter 37, "Bind the state, calculate completely,
+// then commit"; prefix-reuse note, "What must be trimmed together"):
+//   project   : new rows through W_q, W_k, W_v, rotary at next_position + i,
+//               candidate key/value rows and the query; non-finite checks.
+//   attend    : decode -- split-K over the position axis, one partial
+//               (max, sum, weighted values) per 256-row tile of each lane;
+//               chunk  -- one workgroup per query row, causal over the
+//               retained rows plus chunk rows 0..i.
+//   merge     : log-sum-exp merge of a decode lane's partials into its head
+//               block of the output (merge_heads).
+//   commit    : candidate rows into slot len[b] (+ i), positions, then
+//               len[b] and next_position[b] advance -- unless a failure word
+//               is set, in which case nothing changes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <utility>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+using bf16_t = uint16_t;
+
+// ------------------------------------------------------------ conversions --
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Round-to-nearest-even float -> bfloat16 (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+template <typename T> struct Acc;
+template <> struct Acc<double> { using type = double; };
+template <> struct Acc<float> { using type = float; };
+template <> struct Acc<bf16_t> { using type = float; };
+
+template <typename A> __device__ __forceinline__ A to_acc(double v) { return A(v); }
+template <typename A> __device__ __forceinline__ A to_acc(float v) { return A(v); }
+template <typename A> __device__ __forceinline__ A to_acc(bf16_t v) { return A(bf16_to_f32(v)); }
+
+template <typename T> __device__ __forceinline__ T from_acc(typename Acc<T>::type v);
+template <> __device__ __forceinline__ double from_acc<double>(double v) { return v; }
+template <> __device__ __forceinline__ float from_acc<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_acc<bf16_t>(float v) { return f32_to_bf16(v); }
+
+__device__ __forceinline__ bool finite(double v) { return isfinite(v); }
+__device__ __forceinline__ bool finite(float v) { return isfinite(v); }
+
+__device__ __forceinline__ double fast_exp(double v) { return exp(v); }
+__device__ __forceinline__ float fast_exp(float v) { return expf(v); }
+
+// ------------------------------------------------------- vector row loads --
+
+template <int BYTES> struct Raw;
+template <> struct Raw<16> { using type = uint4; };
+template <> struct Raw<8> { using type = uint2; };
+template <> struct Raw<4> { using type = uint32_t; };
+template <> struct Raw<2> { using type = uint16_t; };
+
+// Loads VEC consecutive elements (VEC * sizeof(T) bytes, naturally aligned)
+// and widens them to the accumulate type.
+template <typename T, int VEC>
+__device__ __forceinline__ void load_row_chunk(const T* __restrict__ p, typename Acc<T>::type (&out)[VEC]) {
+  using R = typename Raw<VEC * sizeof(T)>::type;
+  union {
+    R raw;
+    T e[VEC];
+  } u;
+  u.raw = *reinterpret_cast<const R*>(p);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) out[i] = to_acc<typename Acc<T>::type>(u.e[i]);
+}
+
+// Lane geometry of a row of DH elements of T: each lane reads one chunk of up
+// to 16 bytes; G lanes cover a row; a wavefront of 64 covers RPW rows.
+template <typename T, int DH>
+struct RowGeo {
+  static constexpr int VEC = (DH * int(sizeof(T)) >= 16) ? 16 / int(sizeof(T)) : DH;
+  static constexpr int G = DH / VEC;
+  static constexpr int RPW = 64 / G;
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "unsupported head width");
+};
+
+template <int G, typename A>
+__device__ __forceinline__ A group_sum(A v) {
+#pragma unroll
+  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ void flag_min(unsigned long long* word, unsigned long long idx) {
+  atomicMin(word, idx);
+}
+
+__device__ __forceinline__ bool any_error(const ErrWords* e) {
+  return (e->key & e->value & e->query & e->position & e->output) != kErrClear;
+}
+
+// --------------------------------------------------------------- project --
+
+// One block = one input row m = (b, i) and one projection p; each thread
+// produces one rotary pair (feature f and f + d_h/2 of head h), so the rotation
+// needs no exchange.  The input row is staged through LDS in the accumulate
+// type, in slices.
+template <typename T>
+__global__ __launch_bounds__(256) void project_kernel(DevState s, const T* __restrict__ x, int n_max,
+                                                      int per_seq_rows) {
+  using A = typename Acc<T>::type;
+  constexpr int SLICE = 2048;
+  __shared__ A xs[SLICE];
+  const int m = blockIdx.y;
+  const int p = blockIdx.z;
+  const int b = m / n_max;
+  const int i = m - b * n_max;
+  const int n_b = per_seq_rows ? s.rows[b] : n_max;
+  if (i >= n_b) return;  // whole block leaves together
+
+  const int D = s.model_width;
+  const int dh = s.head_width;
+  const int half = dh >> 1;
+  const int pair = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool active = pair < s.heads * half;
+  const int h = active ? pair / half : 0;
+  const int f = active ? pair - h * half : 0;
+  const T* W = static_cast<const T*>(p == 0 ? s.wq : (p == 1 ? s.wk : s.wv));
+  const T* w0 = W + size_t(h * dh + f) * D;
+  const T* w1 = W + size_t(h * dh + f + half) * D;
+  const T* xr = x + size_t(m) * D;
+
+  A acc0 = 0, acc1 = 0;
+  for (int k0 = 0; k0 < D; k0 += SLICE) {
+    const int kn = min(SLICE, D - k0);
+    __syncthreads();
+    for (int k = threadIdx.x; k < kn; k += blockDim.x) xs[k] = to_acc<A>(xr[k0 + k]);
+    __syncthreads();
+    if (active) {
+      for (int k = 0; k < kn; ++k) {
+        const A xv = xs[k];
+        acc0 += xv * to_acc<A>(w0[k0 + k]);
+        acc1 += xv * to_acc<A>(w1[k0 + k]);
+      }
+    }
+  }
+  if (!active) return;
+
+  A r0 = acc0, r1 = acc1;
+  if (p < 2 && s.rope) {
+    int pos = s.next_pos[b] + i;
+    if (pos < 0 || pos >= s.max_positions) {
+      flag_min(&s.err->position, (unsigned long long)b);
+      pos = 0;  // stay inside the table; the commit is suppressed
+    }
+    const A* ct = static_cast<const A*>(s.rope_cos);
+    const A* st = static_cast<const A*>(s.rope_sin);
+    const A c = ct[size_t(pos) * half + f];
+    const A sn = st[size_t(pos) * half + f];
+    r0 = acc0 * c - acc1 * sn;
+    r1 = acc1 * c + acc0 * sn;
+  }
+  const size_t flat0 = (size_t(b * s.heads + h) * n_max + i) * dh + f;
+  const size_t flat1 = flat0 + half;
+  if (p == 0) {
+    A* q = static_cast<A*>(s.q);
+    q[flat0] = r0;
+    q[flat1] = r1;
+    if (!finite(r0)) flag_min(&s.err->query, flat0);
+    if (!finite(r1)) flag_min(&s.err->query, flat1);
+  } else {
+    T* dst = static_cast<T*>(p == 1 ? s.cand_k : s.cand_v);
+    const T t0 = from_acc<T>(r0), t1 = from_acc<T>(r1);
+    dst[flat0] = t0;
+    dst[flat1] = t1;
+    unsigned long long* word = p == 1 ? &s.err->key : &s.err->value;
+    if (!finite(to_acc<A>(t0))) flag_min(word, flat0);
+    if (!finite(to_acc<A>(t1))) flag_min(word, flat1);
+  }
+}
+
+// ------------------------------------------------------------ attention ----
+
+// Online-softmax attention of one query over virtual rows [r0, r1) of a lane:
+// virtual row r < len is cache row r, otherwise candidate row r - len.  Each
+// group of G lanes owns one row at a time (its lanes hold one 16-byte chunk
+// each); groups keep private (max, sum, weighted values) and are merged through
+// LDS at the end.  Returns the tile's max and sum in M/L and the weighted
+// values in acc_out[0..DH) (LDS), visible to the whole block after return.
+template <typename T, int DH, int NW>
+__device__ __forceinline__ void attend_rows(const typename Acc<T>::type* __restrict__ q,
+                                            const T* __restrict__ kc, const T* __restrict__ vc,
+                                            const T* __restrict__ kn, const T* __restrict__ vn, int len,
+                                            int r0, int r1, typename Acc<T>::type scale,
+                                            typename Acc<T>::type* sm_m, typename Acc<T>::type* sm_l,
+                                            typename Acc<T>::type* sm_acc, typename Acc<T>::type& M,
+                                            typename Acc<T>::type& L, typename Acc<T>::type* acc_out) {
+  using A = typename Acc<T>::type;
+  using Geo = RowGeo<T, DH>;
+  constexpr int VEC = Geo::VEC, G = Geo::G, RPW = Geo::RPW;
+  constexpr int GROUPS = NW * RPW;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane % G;
+  const int grp = wave * RPW + lane / G;
+
+  A qv[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) qv[e] = q[g * VEC + e];
+
+  A m = -INFINITY, l = 0;
+  A acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0;
+
+  for (int r = r0 + grp; r < r1; r += GROUPS) {
+    const T* kr = (r < len) ? kc + size_t(r) * DH : kn + size_t(r - len) * DH;
+    const T* vr = (r < len) ? vc + size_t(r) * DH : vn + size_t(r - len) * DH;
+    A kv[VEC], vv[VEC];
+    load_row_chunk<T, VEC>(kr + g * VEC, kv);
+    load_row_chunk<T, VEC>(vr + g * VEC, vv);
+    A dot = 0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) dot += qv[e] * kv[e];
+    dot = group_sum<G>(dot);
+    const A sc = dot * scale;
+    const A m_new = fmax(m, sc);
+    const A corr = fast_exp(m - m_new);  // exp(-inf) = 0 on the first row
+    const A pr = fast_exp(sc - m_new);
+    l = l * corr + pr;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = acc[e] * corr + pr * vv[e];
+    m = m_new;
+  }
+
+  if (g == 0) {
+    sm_m[grp] = m;
+    sm_l[grp] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) sm_acc[grp * DH + g * VEC + e] = acc[e];
+  __syncthreads();
+  A mx = -INFINITY;
+  for (int k = 0; k < GROUPS; ++k) mx = fmax(mx, sm_m[k]);
+  A sum = 0;
+  for (int k = 0; k < GROUPS; ++k)
+    if (sm_m[k] != -INFINITY) sum += sm_l[k] * fast_exp(sm_m[k] - mx);
+  for (int j = threadIdx.x; j < DH; j += blockDim.x) {
+    A a = 0;
+    for (int k = 0; k < GROUPS; ++k)
+      if (sm_m[k] != -INFINITY) a += sm_acc[k * DH + j] * fast_exp(sm_m[k] - mx);
+    acc_out[j] = a;
+  }
+  M = mx;
+  L = sum;
+  __syncthreads();
+}
+
+constexpr int kAttendWaves = 4;
+
+// Split-K decode attention: block (tile, h, b) handles rows
+// [tile * 256, min(t_b, (tile + 1) * 256)) of lane (b, h), t_b = len[b] + 1.
+template <typename T, int DH>
+__global__ __launch_bounds__(64 * kAttendWaves) void attend_decode_kernel(DevState s) {
+  using A = typename Acc<T>::type;
+  using Geo = RowGeo<T, DH>;
+  constexpr int GROUPS = kAttendWaves * Geo::RPW;
+  __shared__ A sm_m[GROUPS], sm_l[GROUPS], sm_acc[GROUPS * DH], out_acc[DH];
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int C = s.capacity;
+  const int len = min(max(s.len[b], 0), C - 1);
+  const int t = len + 1;
+  const int r0 = tile * kDecodeTileRows;
+  if (r0 >= t) return;
+  const int r1 = min(t, r0 + kDecodeTileRows);
+  const size_t lane_id = size_t(b) * s.heads + h;
+  const T* kc = static_cast<const T*>(s.keys) + lane_id * C * DH;
+  const T* vc = static_cast<const T*>(s.values) + lane_id * C * DH;
+  const T* kn = static_cast<const T*>(s.cand_k) + lane_id * DH;
+  const T* vn = static_cast<const T*>(s.cand_v) + lane_id * DH;
+  const A* q = static_cast<const A*>(s.q) + lane_id * DH;
+  A M, L;
+  attend_rows<T, DH, kAttendWaves>(q, kc, vc, kn, vn, len, r0, r1, A(s.scale), sm_m, sm_l, sm_acc, M, L,
+                                   out_acc);
+  A* part = static_cast<A*>(s.partials) + (lane_id * s.max_tiles + tile) * (DH + 2);
+  if (threadIdx.x == 0) {
+    part[0] = M;
+    part[1] = L;
+  }
+  for (int j = threadIdx.x; j < DH; j += blockDim.x) part[2 + j] = out_acc[j];
+}
+
+// Log-sum-exp merge of the tiles of lane (b, h) into out[b, 0, h*d_h .. ].
+template <typename T, int DH>
+__global__ __launch_bounds__(64) void merge_decode_kernel(DevState s, typename Acc<T>::type* __restrict__ out) {
+  using A = typename Acc<T>::type;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int C = s.capacity;
+  const int len = min(max(s.len[b], 0), C - 1);
+  const int ntiles = (len + 1 + kDecodeTileRows - 1) / kDecodeTileRows;
+  const size_t lane_id = size_t(b) * s.heads + h;
+  const A* part = static_cast<const A*>(s.partials) + lane_id * s.max_tiles * (DH + 2);
+  A mx = -INFINITY;
+  for (int k = 0; k < ntiles; ++k) mx = fmax(mx, part[k * (DH + 2)]);
+  A sum = 0;
+  for (int k = 0; k < ntiles; ++k) sum += part[k * (DH + 2) + 1] * fast_exp(part[k * (DH + 2)] - mx);
+  for (int j = threadIdx.x; j < DH; j += blockDim.x) {
+    A a = 0;
+    for (int k = 0; k < ntiles; ++k) a += part[k * (DH + 2) + 2 + j] * fast_exp(part[k * (DH + 2)] - mx);
+    const A o = a / sum;
+    const size_t flat = size_t(b) * s.model_width + size_t(h) * DH + j;
+    out[flat] = o;
+    if (!finite(o)) flag_min(&s.err->output, flat);
+  }
+}
+
+// Chunk attention, one block per query row (i, h, b): rows [0, len[b] + i + 1).
+template <typename T, int DH>
+__global__ __launch_bounds__(64 * kAttendWaves) void attend_chunk_kernel(DevState s, int n_max, int per_seq_rows,
+                                                                         typename Acc<T>::type* __restrict__ out) {
+  using A = typename Acc<T>::type;
+  using Geo = RowGeo<T, DH>;
+  constexpr int GROUPS = kAttendWaves * Geo::RPW;
+  __shared__ A sm_m[GROUPS], sm_l[GROUPS], sm_acc[GROUPS * DH], out_acc[DH];
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n_b = per_seq_rows ? s.rows[b] : n_max;
+  if (i >= n_b) return;
+  const int C = s.capacity;
+  const int len = min(max(s.len[b], 0), C);
+  const size_t lane_id = size_t(b) * s.heads + h;
+  const T* kc = static_cast<const T*>(s.keys) + lane_id * C * DH;
+  const T* vc = static_cast<const T*>(s.values) + lane_id * C * DH;
+  const T* kn = static_cast<const T*>(s.cand_k) + lane_id * n_max * DH;
+  const T* vn = static_cast<const T*>(s.cand_v) + lane_id * n_max * DH;
+  const A* q = static_cast<const A*>(s.q) + (lane_id * n_max + i) * DH;
+  A M, L;
+  attend_rows<T, DH, kAttendWaves>(q, kc, vc, kn, vn, len, 0, len + i + 1, A(s.scale), sm_m, sm_l, sm_acc, M, L,
+                                   out_acc);
+  for (int j = threadIdx.x; j < DH; j += blockDim.x) {
+    const A o = out_acc[j] / L;
+    const size_t flat = (size_t(b) * n_max + i) * s.model_width + size_t(h) * DH + j;
+    out[flat] = o;
+    if (!finite(o)) flag_min(&s.err->output, flat);
+  }
+}
+
+// --------------------------------------------------------------- commit ----
+
+// Copies the candidate rows of lane (b, h) into rows len[b] .. len[b]+n_b-1.
+template <typename T>
+__global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max, int per_seq_rows) {
+  if (any_error(s.err)) return;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int n_b = per_seq_rows ? s.rows[b] : n_max;
+  const int len = s.len[b];
+  const int C = s.capacity;
+  if (n_b <= 0 || len < 0 || len + n_b > C) return;
+  const int dh = s.head_width;
+  const size_t lane_id = size_t(b) * s.heads + h;
+  const size_t bytes = size_t(n_b) * dh * sizeof(T);
+  const char* sk = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_k) + lane_id * n_max * dh);
+  const char* sv = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_v) + lane_id * n_max * dh);
+  char* dk = reinterpret_cast<char*>(static_cast<T*>(s.keys) + (lane_id * C + len) * dh);
+  char* dv = reinterpret_cast<char*>(static_cast<T*>(s.values) + (lane_id * C + len) * dh);
+  if ((bytes & 15) == 0 && ((reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(sk)) & 15) == 0) {
+    const size_t n16 = bytes / 16;
+    for (size_t k = threadIdx.x; k < n16; k += blockDim.x) {
+      reinterpret_cast<uint4*>(dk)[k] = reinterpret_cast<const uint4*>(sk)[k];
+      reinterpret_cast<uint4*>(dv)[k] = reinterpret_cast<const uint4*>(sv)[k];
+    }
+  } else {
+    const size_t n = bytes / sizeof(T);
+    for (size_t k = threadIdx.x; k < n; k += blockDim.x) {
+      reinterpret_cast<T*>(dk)[k] = reinterpret_cast<const T*>(sk)[k];
+      reinterpret_cast<T*>(dv)[k] = reinterpret_cast<const T*>(sv)[k];
+    }
+  }
+  if (h == 0) {
+    const int np = s.next_pos[b];
+    for (int k = threadIdx.x; k < n_b; k += blockDim.x) s.positions[size_t(b) * C + len + k] = np + k;
+  }
+}
+
+// Advances len[b] and next_position[b] by n_b (after every copy has read len[b]).
+__global__ __launch_bounds__(256) void commit_advance_kernel(DevState s, int n_max, int per_seq_rows) {
+  if (any_error(s.err)) return;
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= s.batch) return;
+  const int n_b = per_seq_rows ? s.rows[b] : n_max;
+  const int len = s.len[b];
+  if (n_b <= 0 || len < 0 || len + n_b > s.capacity) return;
+  s.len[b] = len + n_b;
+  s.next_pos[b] = s.next_pos[b] + n_b;
+}
+
+// ------------------------------------------------------------ bookkeeping --
+
+struct SetArgs {
+  int32_t vals[kSetChunk];
+  int first, count, mode;
+};
+
+__global__ __launch_bounds__(256) void set_lengths_kernel(DevState s, SetArgs a) {
+  if (any_error(s.err)) return;
+  for (int k = threadIdx.x; k < a.count; k += blockDim.x) {
+    const int b = a.first + k;
+    if (a.mode == 2) {
+      s.len[b] = 0;
+      s.next_pos[b] = 0;
+    } else {
+      s.len[b] = a.vals[k];
+      if (a.mode == 0) s.next_pos[b] = a.vals[k];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void set_rows_kernel(DevState s, SetArgs a) {
+  for (int k = threadIdx.x; k < a.count; k += blockDim.x) s.rows[a.first + k] = a.vals[k];
+}
+
+__global__ void clear_err_kernel(ErrWords* e) {
+  if (threadIdx.x < 8) reinterpret_cast<unsigned long long*>(e)[threadIdx.x] = kErrClear;
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(uint4* p, size_t n16) {
+  for (size_t k = size_t(blockIdx.x) * blockDim.x + threadIdx.x; k < n16; k += size_t(gridDim.x) * blockDim.x)
+    p[k] = make_uint4(0, 0, 0, 0);
+}
+
+inline hipStream_t st(void* s) { return static_cast<hipStream_t>(s); }
+
+inline int last_launch() { return int(hipGetLastError()); }
+
+// Dispatch on (storage type, head width) to a template instance.
+template <template <typename, int> class K, typename... Args>
+int dispatch(int dtype, int dh, Args&&... args) {
+#define KVC_DH_CASES(T)                                              \
+  switch (dh) {                                                      \
+    case 2: return K<T, 2>::run(std::forward<Args>(args)...);        \
+    case 4: return K<T, 4>::run(std::forward<Args>(args)...);        \
+    case 8: return K<T, 8>::run(std::forward<Args>(args)...);        \
+    case 16: return K<T, 16>::run(std::forward<Args>(args)...);      \
+    case 32: return K<T, 32>::run(std::forward<Args>(args)...);      \
+    case 64: return K<T, 64>::run(std::forward<Args>(args)...);      \
+    case 128: return K<T, 128>::run(std::forward<Args>(args)...);    \
+    default: break;                                                  \
+  }
+  if (dtype == KVC_F64) {
+    KVC_DH_CASES(double)
+  } else if (dtype == KVC_F32) {
+    KVC_DH_CASES(float)
+    if (dh == 256) return K<float, 256>::run(std::forward<Args>(args)...);
+  } else if (dtype == KVC_BF16) {
+    KVC_DH_CASES(bf16_t)
+    if (dh == 256) return K<bf16_t, 256>::run(std::forward<Args>(args)...);
+    if (dh == 512) return K<bf16_t, 512>::run(std::forward<Args>(args)...);
+  }
+#undef KVC_DH_CASES
+  return int(hipErrorInvalidValue);
+}
+
+template <typename T, int DH>
+struct AttendDecode {
+  static int run(const DevState& s) {
+    dim3 grid(s.max_tiles, s.heads, s.batch);
+    hipLaunchKernelGGL((attend_decode_kernel<T, DH>), grid, dim3(64 * kAttendWaves), 0, st(s.stream), s);
+    return last_launch();
+  }
+};
+
+template <typename T, int DH>
+struct MergeDecode {
+  static int run(const DevState& s, void* out) {
+    dim3 grid(s.heads, s.batch);
+    hipLaunchKernelGGL((merge_decode_kernel<T, DH>), grid, dim3(64), 0, st(s.stream), s,
+                       static_cast<typename Acc<T>::type*>(out));
+    return last_launch();
+  }
+};
+
+template <typename T, int DH>
+struct AttendChunk {
+  static int run(const DevState& s, int n_max, int per_seq_rows, void* out) {
+    dim3 grid(n_max, s.heads, s.batch);
+    hipLaunchKernelGGL((attend_chunk_kernel<T, DH>), grid, dim3(64 * kAttendWaves), 0, st(s.stream), s, n_max,
+                       per_seq_rows, static_cast<typename Acc<T>::type*>(out));
+    return last_launch();
+  }
+};
+
+template <typename T>
+int project_t(const DevState& s, const void* x, int n_max, int per_seq_rows) {
+  const int pairs = s.heads * (s.head_width / 2);
+  dim3 grid((pairs + 255) / 256, s.batch * n_max, 3);
+  hipLaunchKernelGGL((project_kernel<T>), grid, dim3(256), 0, st(s.stream), s, static_cast<const T*>(x), n_max,
+                     per_seq_rows);
+  return last_launch();
+}
+
+template <typename T>
+int commit_t(const DevState& s, int n_max, int per_seq_rows) {
+  hipLaunchKernelGGL((commit_copy_kernel<T>), dim3(s.heads, s.batch), dim3(256), 0, st(s.stream), s, n_max,
+                     per_seq_rows);
+  int rc = last_launch();
+  if (rc) return rc;
+  hipLaunchKernelGGL(commit_advance_kernel, dim3((s.batch + 255) / 256), dim3(256), 0, st(s.stream), s, n_max,
+                     per_seq_rows);
+  return last_launch();
+}
+
+}  // namespace
+
+// ------------------------------------------------------------- backend API --
+
+const char* dev_error_string(int code) { return hipGetErrorString(hipError_t(code)); }
+
+int dev_current_device(int* device) { return int(hipGetDevice(device)); }
+
+int dev_malloc(void** p, size_t bytes) { return int(hipMalloc(p, bytes ? bytes : 16)); }
+
+void dev_free(void* p) {
+  if (p) (void)hipFree(p);
+}
+
+int dev_host_malloc(void** p, size_t bytes) { return int(hipHostMalloc(p, bytes ? bytes : 16, hipHostMallocDefault)); }
+
+void dev_host_free(void* p) {
+  if (p) (void)hipHostFree(p);
+}
+
+int dev_copy_h2d_sync(void* dst, const void* src, size_t bytes, void* stream) {
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, st(stream));
+  if (e != hipSuccess) return int(e);
+  return int(hipStreamSynchronize(st(stream)));
+}
+
+int dev_copy_d2h_sync(void* dst, const void* src, size_t bytes, void* stream) {
+  hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToHost, st(stream));
+  if (e != hipSuccess) return int(e);
+  return int(hipStreamSynchronize(st(stream)));
+}
+
+int dev_copy_d2h_2d_sync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width, size_t height,
+                         void* stream) {
+  if (width == 0 || height == 0) return int(hipStreamSynchronize(st(stream)));
+  hipError_t e = hipMemcpy2DAsync(dst, dpitch, src, spitch, width, height, hipMemcpyDeviceToHost, st(stream));
+  if (e != hipSuccess) return int(e);
+  return int(hipStreamSynchronize(st(stream)));
+}
+
+int dev_sync(void* stream) { return int(hipStreamSynchronize(st(stream))); }
+
+int dev_zero(void* p, size_t bytes, void* stream) {
+  const size_t n16 = bytes / 16;
+  if (n16 == 0) return 0;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(zero_kernel, dim3(unsigned(blocks)), dim3(256), 0, st(stream), static_cast<uint4*>(p), n16);
+  return last_launch();
+}
+
+int dev_clear_err(ErrWords* err, void* stream) {
+  hipLaunchKernelGGL(clear_err_kernel, dim3(1), dim3(64), 0, st(stream), err);
+  return last_launch();
+}
+
+int dev_set_lengths(const DevState& s, const int32_t* vals, int mode) {
+  for (int first = 0; first < s.batch; first += kSetChunk) {
+    SetArgs a{};
+    a.first = first;
+    a.count = s.batch - first < kSetChunk ? s.batch - first : kSetChunk;
+    a.mode = mode;
+    if (mode != 2)
+      for (int k = 0; k < a.count; ++k) a.vals[k] = vals[first + k];
+    hipLaunchKernelGGL(set_lengths_kernel, dim3(1), dim3(256), 0, st(s.stream), s, a);
+    int rc = last_launch();
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+int dev_set_rows(const DevState& s, const int32_t* vals) {
+  for (int first = 0; first < s.batch; first += kSetChunk) {
+    SetArgs a{};
+    a.first = first;
+    a.count = s.batch - first < kSetChunk ? s.batch - first : kSetChunk;
+    for (int k = 0; k < a.count; ++k) a.vals[k] = vals[first + k];
+    hipLaunchKernelGGL(set_rows_kernel, dim3(1), dim3(256), 0, st(s.stream), s, a);
+    int rc = last_launch();
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows) {
+  switch (s.dtype) {
+    case KVC_F64: return project_t<double>(s, x, n_max, per_seq_rows);
+    case KVC_F32: return project_t<float>(s, x, n_max, per_seq_rows);
+    case KVC_BF16: return project_t<bf16_t>(s, x, n_max, per_seq_rows);
+  }
+  return int(hipErrorInvalidValue);
+}
+
+int dev_attend_decode(const DevState& s) { return dispatch<AttendDecode>(s.dtype, s.head_width, s); }
+
+int dev_merge_decode(const DevState& s, void* out) { return dispatch<MergeDecode>(s.dtype, s.head_width, s, out); }
+
+int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out) {
+  return dispatch<AttendChunk>(s.dtype, s.head_width, s, n_max, per_seq_rows, out);
+}
+
+int dev_commit(const DevState& s, int n_max, int per_seq_rows) {
+  switch (s.dtype) {
+    case KVC_F64: return commit_t<double>(s, n_max, per_seq_rows);
+    case KVC_F32: return commit_t<float>(s, n_max, per_seq_rows);
+    case KVC_BF16: return commit_t<bf16_t>(s, n_max, per_seq_rows);
+  }
+  return int(hipErrorInvalidValue);
+}
+
+int dev_event_create(void** e) { return int(hipEventCreate(reinterpret_cast<hipEvent_t*>(e))); }
+
+void dev_event_destroy(void* e) {
+  if (e) (void)hipEventDestroy(static_cast<hipEvent_t>(e));
+}
+
+int dev_event_record(void* e, void* stream) { return int(hipEventRecord(static_cast<hipEvent_t>(e), st(stream))); }
+
+int dev_event_elapsed(float* ms, void* start, void* stop) {
+  hipError_t e = hipEventSynchronize(static_cast<hipEvent_t>(stop));
+  if (e != hipSuccess) return int(e);
+  return int(hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)));
+}
+
+bool dev_has_kernels() { return true; }
+
+}  // namespace kvc

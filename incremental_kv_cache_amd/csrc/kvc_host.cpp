@@ -1,0 +1,924 @@
+// Host side of libkvcache: handles, request validation in the order Chapter 37
+// fixes, bookkeeping (lengths, next positions, binding), error reporting, and
+// the C ABI declared in include/kvcache.h.  All device work goes through the
+// backend interface in kvc_internal.h.
+//
+// Chapter 37 = "Keep the prefix, project only the new row" (incremental
+// attention course chapter); prefix-reuse note = "LLM mechanism experiment
+// (5): can only the changed suffix be recomputed?".
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kvc_internal.h"
+
+using namespace kvc;
+
+struct kvc_params {
+  int32_t model_width;
+  kvc_dtype dtype;
+  const void* w[3];
+  uint64_t id;           // identity: unique per created parameter set
+  uint64_t revision[3];  // value revision per weight
+};
+
+struct kvc_layer {
+  const kvc_params* params;
+  int32_t heads, head_width;
+  kvc_pos_mode pos_mode;
+  double rope_base;
+  int32_t rope_max_positions;
+  int32_t rope_feature_width() const { return pos_mode == KVC_POS_ROPE ? head_width : 0; }
+};
+
+namespace {
+
+struct Profile {
+  int32_t slots = 0;
+  int32_t used = 0;
+  std::vector<void*> events;  // [slots][KVC_STAGES][2]
+  std::vector<int8_t> recorded;
+};
+
+}  // namespace
+
+struct kvc_cache {
+  // geometry and binding (Chapter 37, layer-kv-cache listing: the cache struct)
+  int32_t batch, heads, head_width, model_width, capacity, max_chunk_rows;
+  kvc_dtype dtype;
+  uint64_t params_id;
+  uint64_t revision[3];
+  int32_t rope_feature_width, rope_max_positions;
+  uint64_t rope_base_bits;
+  double rope_base;
+  kvc_pos_mode pos_mode;
+  int device;
+  // host copy of the committed state
+  std::vector<int32_t> len, next_pos;
+  bool pending_async = false;
+  // device state
+  DevState ds{};
+  ErrWords* err_host = nullptr;  // pinned readback
+  int64_t storage_bytes = 0;
+  Profile prof;
+};
+
+namespace {
+
+std::atomic<uint64_t> g_next_params_id{1};
+thread_local kvc_error_detail g_last;
+
+size_t elem_size(kvc_dtype t) { return t == KVC_F64 ? 8 : (t == KVC_F32 ? 4 : 2); }
+size_t acc_size(kvc_dtype t) { return t == KVC_F64 ? 8 : 4; }
+
+void reset_detail() {
+  std::memset(&g_last, 0, sizeof(g_last));
+  g_last.parameter = -1;
+  g_last.sequence = -1;
+  g_last.flat_index = -1;
+}
+
+kvc_status fail(kvc_status st, const char* fmt, ...) {
+  g_last.status = st;
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last.message, sizeof(g_last.message), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvc_status fail_ea(kvc_status st, int64_t expected, int64_t actual, const char* fmt, ...) {
+  g_last.expected = expected;
+  g_last.actual = actual;
+  g_last.status = st;
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last.message, sizeof(g_last.message), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvc_status device_fail(int code, const char* what) {
+  return fail(KVC_ERR_DEVICE, "%s failed: %s", what, dev_error_string(code));
+}
+
+bool checked_mul(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int max_head_width(kvc_dtype t) { return t == KVC_F64 ? 128 : (t == KVC_F32 ? 256 : 512); }
+
+// Request checks shared by both compute calls, from cache model width through
+// the rotary configuration (Chapter 37, "Bind the state, calculate
+// completely, then commit": the binding check).
+kvc_status check_binding(const kvc_layer* layer, const kvc_cache* c) {
+  const kvc_params* p = layer->params;
+  if (c->model_width != p->model_width)
+    return fail_ea(KVC_ERR_CACHE_MODEL_WIDTH_MISMATCH, p->model_width, c->model_width,
+                   "cache model width %d does not match layer model width %d", c->model_width,
+                   p->model_width);
+  if (c->heads != layer->heads)
+    return fail_ea(KVC_ERR_CACHE_HEAD_COUNT_MISMATCH, layer->heads, c->heads,
+                   "cache head count %d does not match layer head count %d", c->heads, layer->heads);
+  if (c->head_width != layer->head_width)
+    return fail_ea(KVC_ERR_CACHE_HEAD_WIDTH_MISMATCH, layer->head_width, c->head_width,
+                   "cache head width %d does not match layer head width %d", c->head_width,
+                   layer->head_width);
+  if (c->params_id != p->id)
+    return fail(KVC_ERR_CACHE_LAYER_MISMATCH,
+                "cache was created for a different attention layer (parameter identity differs)");
+  for (int k = 0; k < 3; ++k) {
+    if (c->revision[k] != p->revision[k]) {
+      g_last.parameter = k;
+      g_last.cache_revision = c->revision[k];
+      g_last.layer_revision = p->revision[k];
+      return fail(KVC_ERR_CACHE_LAYER_REVISION_MISMATCH,
+                  "cache parameter %d was captured at value revision %llu, but the layer is at revision %llu",
+                  k, (unsigned long long)c->revision[k], (unsigned long long)p->revision[k]);
+    }
+  }
+  uint64_t base_bits;
+  std::memcpy(&base_bits, &layer->rope_base, 8);
+  if (c->rope_feature_width != layer->rope_feature_width() ||
+      c->rope_max_positions != layer->rope_max_positions || c->rope_base_bits != base_bits) {
+    g_last.rope_feature_width[0] = c->rope_feature_width;
+    g_last.rope_feature_width[1] = layer->rope_feature_width();
+    g_last.rope_max_positions[0] = c->rope_max_positions;
+    g_last.rope_max_positions[1] = layer->rope_max_positions;
+    g_last.rope_base[0] = c->rope_base;
+    g_last.rope_base[1] = layer->rope_base;
+    return fail(KVC_ERR_CACHE_ROPE_MISMATCH,
+                "cache RoPE (feature width %d, max positions %d, base %g) does not match layer RoPE "
+                "(feature width %d, max positions %d, base %g)",
+                c->rope_feature_width, c->rope_max_positions, c->rope_base, layer->rope_feature_width(),
+                layer->rope_max_positions, layer->rope_base);
+  }
+  return KVC_OK;
+}
+
+// Reads the device failure words; on a failure fills the detail, clears the
+// words and returns the failure's status (KVC_OK otherwise).  Stream must be idle.
+kvc_status collect_device_error(kvc_cache* c, int64_t n_max_for_index) {
+  int rc = dev_copy_d2h_sync(c->err_host, c->ds.err, sizeof(ErrWords), c->ds.stream);
+  if (rc) return device_fail(rc, "reading the device error words");
+  const ErrWords e = *c->err_host;
+  kvc_status st = KVC_OK;
+  unsigned long long idx = kErrClear;
+  if (e.key != kErrClear) {
+    st = KVC_ERR_NONFINITE_KEY;
+    idx = e.key;
+  } else if (e.value != kErrClear) {
+    st = KVC_ERR_NONFINITE_VALUE;
+    idx = e.value;
+  } else if (e.query != kErrClear) {
+    st = KVC_ERR_NONFINITE_QUERY;
+    idx = e.query;
+  } else if (e.position != kErrClear) {
+    st = KVC_ERR_ROTARY_POSITION;
+    idx = e.position;
+  } else if (e.output != kErrClear) {
+    st = KVC_ERR_NONFINITE_OUTPUT;
+    idx = e.output;
+  }
+  if (st == KVC_OK) return KVC_OK;
+  (void)n_max_for_index;
+  g_last.flat_index = int64_t(idx);
+  if (st == KVC_ERR_NONFINITE_KEY || st == KVC_ERR_NONFINITE_VALUE) {
+    // the offending element is still in the candidate buffer
+    const void* src = static_cast<const char*>(st == KVC_ERR_NONFINITE_KEY ? c->ds.cand_k : c->ds.cand_v) +
+                      idx * elem_size(c->dtype);
+    uint64_t raw = 0;
+    if (dev_copy_d2h_sync(&raw, src, elem_size(c->dtype), c->ds.stream) == 0) {
+      if (c->dtype == KVC_F64) {
+        std::memcpy(&g_last.value, &raw, 8);
+      } else if (c->dtype == KVC_F32) {
+        float f;
+        std::memcpy(&f, &raw, 4);
+        g_last.value = f;
+      } else {
+        uint32_t u = uint32_t(raw & 0xffff) << 16;
+        float f;
+        std::memcpy(&f, &u, 4);
+        g_last.value = f;
+      }
+    }
+  }
+  if (st == KVC_ERR_ROTARY_POSITION) g_last.sequence = int32_t(idx);
+  rc = dev_clear_err(c->ds.err, c->ds.stream);
+  if (rc == 0) rc = dev_sync(c->ds.stream);
+  if (rc) return device_fail(rc, "clearing the device error words");
+  switch (st) {
+    case KVC_ERR_NONFINITE_KEY:
+      return fail(st, "appended key value at flat index %llu must be finite, got %g", idx, g_last.value);
+    case KVC_ERR_NONFINITE_VALUE:
+      return fail(st, "appended value at flat index %llu must be finite, got %g", idx, g_last.value);
+    case KVC_ERR_NONFINITE_QUERY:
+      return fail(st, "rotated query at flat index %llu is not finite", idx);
+    case KVC_ERR_ROTARY_POSITION:
+      return fail(st, "sequence %llu reached the rotary position capacity %d", idx, c->rope_max_positions);
+    default:
+      return fail(st, "attention output at flat index %llu is not finite", idx);
+  }
+}
+
+kvc_status resync_lengths(kvc_cache* c) {
+  const size_t bytes = sizeof(int32_t) * size_t(c->batch);
+  int rc = dev_copy_d2h_sync(c->len.data(), c->ds.len, bytes, c->ds.stream);
+  if (rc == 0) rc = dev_copy_d2h_sync(c->next_pos.data(), c->ds.next_pos, bytes, c->ds.stream);
+  if (rc) return device_fail(rc, "reading lengths");
+  return KVC_OK;
+}
+
+// Reports an error left by earlier KVC_ASYNC calls (synchronises).
+kvc_status check_deferred(kvc_cache* c) {
+  if (!c->pending_async) return KVC_OK;
+  int rc = dev_sync(c->ds.stream);
+  if (rc) return device_fail(rc, "stream synchronisation");
+  c->pending_async = false;
+  kvc_status st = collect_device_error(c, 0);
+  if (st == KVC_ERR_DEVICE) return st;
+  if (st != KVC_OK) {
+    const kvc_status orig = st;
+    kvc_status rs = resync_lengths(c);
+    if (rs != KVC_OK) return rs;
+    g_last.actual = orig;
+    return fail(KVC_ERR_DEFERRED, "an earlier asynchronous call failed: %s (%s)", kvc_status_name(orig),
+                std::string(g_last.message).c_str());
+  }
+  return KVC_OK;
+}
+
+void profile_mark(kvc_cache* c, int stage, int which) {
+  Profile& p = c->prof;
+  if (p.slots <= 0 || p.used >= p.slots) return;
+  const size_t k = (size_t(p.used) * KVC_STAGES + stage) * 2 + which;
+  if (dev_event_record(p.events[k], c->ds.stream) == 0 && which == 1) p.recorded[size_t(p.used) * KVC_STAGES + stage] = 1;
+}
+
+void profile_end_call(kvc_cache* c) {
+  if (c->prof.slots > 0 && c->prof.used < c->prof.slots) c->prof.used++;
+}
+
+void free_cache(kvc_cache* c) {
+  if (!c) return;
+  dev_free(c->ds.keys);
+  dev_free(c->ds.values);
+  dev_free(c->ds.len);
+  dev_free(c->ds.next_pos);
+  dev_free(c->ds.positions);
+  dev_free(c->ds.rows);
+  dev_free(c->ds.cand_k);
+  dev_free(c->ds.cand_v);
+  dev_free(c->ds.q);
+  dev_free(c->ds.partials);
+  dev_free(c->ds.rope_cos);
+  dev_free(c->ds.rope_sin);
+  dev_free(c->ds.err);
+  dev_host_free(c->err_host);
+  for (void* e : c->prof.events) dev_event_destroy(e);
+  delete c;
+}
+
+// Runs the four stages of one call and the sync-mode error collection.
+kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_rows, void* out, int32_t flags,
+                    bool decode) {
+  DevState& s = c->ds;
+  const int per_seq = n_rows != nullptr;
+  int rc = 0;
+  if (per_seq) {
+    rc = dev_set_rows(s, n_rows);
+    if (rc) return device_fail(rc, "chunk row upload");
+  }
+  profile_mark(c, KVC_STAGE_PROJECT, 0);
+  rc = dev_project(s, x, n_max, per_seq);
+  profile_mark(c, KVC_STAGE_PROJECT, 1);
+  if (rc) return device_fail(rc, "projection launch");
+  profile_mark(c, KVC_STAGE_ATTEND, 0);
+  rc = decode ? dev_attend_decode(s) : dev_attend_chunk(s, n_max, per_seq, out);
+  profile_mark(c, KVC_STAGE_ATTEND, 1);
+  if (rc) return device_fail(rc, "attention launch");
+  if (decode) {
+    profile_mark(c, KVC_STAGE_MERGE, 0);
+    rc = dev_merge_decode(s, out);
+    profile_mark(c, KVC_STAGE_MERGE, 1);
+    if (rc) return device_fail(rc, "merge launch");
+  }
+  profile_mark(c, KVC_STAGE_COMMIT, 0);
+  rc = dev_commit(s, n_max, per_seq);
+  profile_mark(c, KVC_STAGE_COMMIT, 1);
+  profile_end_call(c);
+  if (rc) return device_fail(rc, "commit launch");
+
+  if (flags & KVC_ASYNC) {
+    c->pending_async = true;
+    for (int b = 0; b < c->batch; ++b) {
+      const int n = per_seq ? n_rows[b] : n_max;
+      c->len[b] += n;
+      c->next_pos[b] += n;
+    }
+    return KVC_OK;
+  }
+  rc = dev_sync(s.stream);
+  if (rc) return device_fail(rc, "stream synchronisation");
+  kvc_status st = collect_device_error(c, n_max);
+  if (st != KVC_OK) return st;
+  for (int b = 0; b < c->batch; ++b) {
+    const int n = per_seq ? n_rows[b] : n_max;
+    c->len[b] += n;
+    c->next_pos[b] += n;
+  }
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvc_status_name(kvc_status s) {
+  switch (s) {
+#define N(x) \
+  case x: return #x;
+    N(KVC_OK)
+    N(KVC_ERR_ZERO_BATCH)
+    N(KVC_ERR_ZERO_CAPACITY)
+    N(KVC_ERR_CAPACITY_EXCEEDS_POSITIONS)
+    N(KVC_ERR_ELEMENT_COUNT_OVERFLOW)
+    N(KVC_ERR_ALLOCATION_FAILED)
+    N(KVC_ERR_INPUT_RANK)
+    N(KVC_ERR_SINGLE_TOKEN_REQUIRED)
+    N(KVC_ERR_INPUT_BATCH_MISMATCH)
+    N(KVC_ERR_INPUT_WIDTH_MISMATCH)
+    N(KVC_ERR_CACHE_MODEL_WIDTH_MISMATCH)
+    N(KVC_ERR_CACHE_HEAD_COUNT_MISMATCH)
+    N(KVC_ERR_CACHE_HEAD_WIDTH_MISMATCH)
+    N(KVC_ERR_CACHE_LAYER_MISMATCH)
+    N(KVC_ERR_CACHE_LAYER_REVISION_MISMATCH)
+    N(KVC_ERR_CACHE_ROPE_MISMATCH)
+    N(KVC_ERR_FULL)
+    N(KVC_ERR_NONFINITE_KEY)
+    N(KVC_ERR_NONFINITE_VALUE)
+    N(KVC_ERR_NONFINITE_QUERY)
+    N(KVC_ERR_ROTARY_POSITION)
+    N(KVC_ERR_NONFINITE_OUTPUT)
+    N(KVC_ERR_BAD_CUT)
+    N(KVC_ERR_EMPTY_QUERY)
+    N(KVC_ERR_CHUNK_ROWS)
+    N(KVC_ERR_NULL_ARGUMENT)
+    N(KVC_ERR_DTYPE_UNSUPPORTED)
+    N(KVC_ERR_SHAPE_UNSUPPORTED)
+    N(KVC_ERR_BAD_ARGUMENT)
+    N(KVC_ERR_DEVICE)
+    N(KVC_ERR_DEFERRED)
+    N(KVC_ERR_INTERNAL)
+#undef N
+  }
+  return "KVC_ERR_UNKNOWN";
+}
+
+const kvc_error_detail* kvc_last_error(void) { return &g_last; }
+
+kvc_status kvc_params_create(int32_t model_width, kvc_dtype dtype, const void* w_q, const void* w_k,
+                             const void* w_v, kvc_params** out) {
+  reset_detail();
+  if (!out || !w_q || !w_k || !w_v) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_params_create");
+  *out = nullptr;
+  if (model_width <= 0) return fail(KVC_ERR_BAD_ARGUMENT, "model width must be positive, got %d", model_width);
+  if (dtype != KVC_F64 && dtype != KVC_F32 && dtype != KVC_BF16)
+    return fail(KVC_ERR_DTYPE_UNSUPPORTED, "unsupported weight type %d", int(dtype));
+  kvc_params* p = new (std::nothrow) kvc_params;
+  if (!p) return fail(KVC_ERR_ALLOCATION_FAILED, "host allocation failed");
+  p->model_width = model_width;
+  p->dtype = dtype;
+  p->w[0] = w_q;
+  p->w[1] = w_k;
+  p->w[2] = w_v;
+  p->id = g_next_params_id.fetch_add(1);
+  p->revision[0] = p->revision[1] = p->revision[2] = 0;
+  *out = p;
+  return KVC_OK;
+}
+
+kvc_status kvc_params_mark_updated(kvc_params* params, int32_t which) {
+  reset_detail();
+  if (!params) return fail(KVC_ERR_NULL_ARGUMENT, "null parameter set");
+  if (which < -1 || which > 2) return fail(KVC_ERR_BAD_ARGUMENT, "weight index %d out of range", which);
+  for (int k = 0; k < 3; ++k)
+    if (which == -1 || which == k) params->revision[k]++;
+  return KVC_OK;
+}
+
+void kvc_params_destroy(kvc_params* params) { delete params; }
+
+kvc_status kvc_layer_create(const kvc_params* params, int32_t heads, kvc_pos_mode pos_mode, double rope_base,
+                            int32_t rope_max_positions, kvc_layer** out) {
+  reset_detail();
+  if (!params || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_layer_create");
+  *out = nullptr;
+  if (heads <= 0 || params->model_width % heads != 0)
+    return fail(KVC_ERR_BAD_ARGUMENT, "head count %d must divide model width %d", heads, params->model_width);
+  if (pos_mode != KVC_POS_ROPE && pos_mode != KVC_POS_NONE)
+    return fail(KVC_ERR_BAD_ARGUMENT, "unknown position mode %d", int(pos_mode));
+  if (!(rope_base > 0.0) || !std::isfinite(rope_base) || rope_max_positions <= 0)
+    return fail(KVC_ERR_BAD_ARGUMENT, "rotary base must be positive and finite and max positions positive");
+  const int dh = params->model_width / heads;
+  if (dh < 2 || !is_pow2(dh) || dh > max_head_width(params->dtype))
+    return fail(KVC_ERR_SHAPE_UNSUPPORTED, "head width %d must be a power of two in [2, %d] for this type", dh,
+                max_head_width(params->dtype));
+  kvc_layer* l = new (std::nothrow) kvc_layer;
+  if (!l) return fail(KVC_ERR_ALLOCATION_FAILED, "host allocation failed");
+  l->params = params;
+  l->heads = heads;
+  l->head_width = dh;
+  l->pos_mode = pos_mode;
+  l->rope_base = rope_base;
+  l->rope_max_positions = rope_max_positions;
+  *out = l;
+  return KVC_OK;
+}
+
+void kvc_layer_destroy(kvc_layer* layer) { delete layer; }
+
+kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capacity, int32_t max_chunk_rows,
+                            void* hip_stream, kvc_cache** out) {
+  reset_detail();
+  if (!layer || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_cache_create");
+  *out = nullptr;
+  // Chapter 37, layer-kv-cache listing: batch, capacity, position capacity,
+  // element-count overflow, then allocation.
+  if (batch <= 0) return fail_ea(KVC_ERR_ZERO_BATCH, 1, batch, "KV cache batch size must be nonzero");
+  if (capacity <= 0) return fail_ea(KVC_ERR_ZERO_CAPACITY, 1, capacity, "KV cache capacity must be nonzero");
+  if (capacity > layer->rope_max_positions)
+    return fail_ea(KVC_ERR_CAPACITY_EXCEEDS_POSITIONS, layer->rope_max_positions, capacity,
+                   "KV cache capacity %d exceeds RoPE position capacity %d", capacity, layer->rope_max_positions);
+  if (max_chunk_rows <= 0)
+    return fail(KVC_ERR_BAD_ARGUMENT, "max_chunk_rows must be at least 1, got %d", max_chunk_rows);
+  const kvc_params* p = layer->params;
+  const int H = layer->heads, dh = layer->head_width;
+  int64_t elements = 0, cand = 0, pos_elems = 0;
+  if (!checked_mul(batch, H, &elements) || !checked_mul(elements, capacity, &elements) ||
+      !checked_mul(elements, dh, &elements) || !checked_mul(int64_t(batch) * H, int64_t(max_chunk_rows), &cand) ||
+      !checked_mul(cand, dh, &cand) || !checked_mul(batch, capacity, &pos_elems) ||
+      elements > (INT64_MAX / 16) || cand > (INT64_MAX / 16)) {
+    return fail(KVC_ERR_ELEMENT_COUNT_OVERFLOW,
+                "KV cache element count overflows for batch %d, %d heads, capacity %d, and head width %d", batch,
+                H, capacity, dh);
+  }
+  kvc_cache* c = new (std::nothrow) kvc_cache;
+  if (!c) return fail(KVC_ERR_ALLOCATION_FAILED, "host allocation failed");
+  c->batch = batch;
+  c->heads = H;
+  c->head_width = dh;
+  c->model_width = p->model_width;
+  c->capacity = capacity;
+  c->max_chunk_rows = max_chunk_rows;
+  c->dtype = p->dtype;
+  c->params_id = p->id;
+  for (int k = 0; k < 3; ++k) c->revision[k] = p->revision[k];
+  c->rope_feature_width = layer->rope_feature_width();
+  c->rope_max_positions = layer->rope_max_positions;
+  std::memcpy(&c->rope_base_bits, &layer->rope_base, 8);
+  c->rope_base = layer->rope_base;
+  c->pos_mode = layer->pos_mode;
+  c->len.assign(batch, 0);
+  c->next_pos.assign(batch, 0);
+  int rc = dev_current_device(&c->device);
+  if (rc) {
+    free_cache(c);
+    return device_fail(rc, "hipGetDevice");
+  }
+
+  const size_t es = elem_size(p->dtype), as = acc_size(p->dtype);
+  const int max_tiles = (capacity + kDecodeTileRows - 1) / kDecodeTileRows;
+  auto round16 = [](size_t b) { return (b + 15) & ~size_t(15); };
+  DevState& s = c->ds;
+  s.dtype = p->dtype;
+  s.batch = batch;
+  s.heads = H;
+  s.head_width = dh;
+  s.model_width = p->model_width;
+  s.capacity = capacity;
+  s.max_chunk_rows = max_chunk_rows;
+  s.rope = layer->pos_mode == KVC_POS_ROPE;
+  s.max_positions = layer->rope_max_positions;
+  s.scale = 1.0 / std::sqrt(double(dh));
+  s.wq = p->w[0];
+  s.wk = p->w[1];
+  s.wv = p->w[2];
+  s.max_tiles = max_tiles;
+  s.stream = hip_stream;
+  c->storage_bytes = int64_t(round16(size_t(elements) * es));
+  struct Alloc {
+    void** p;
+    size_t bytes;
+  } allocs[] = {
+      {&s.keys, size_t(c->storage_bytes)},
+      {&s.values, size_t(c->storage_bytes)},
+      {reinterpret_cast<void**>(&s.len), round16(sizeof(int32_t) * batch)},
+      {reinterpret_cast<void**>(&s.next_pos), round16(sizeof(int32_t) * batch)},
+      {reinterpret_cast<void**>(&s.positions), round16(sizeof(int32_t) * size_t(pos_elems))},
+      {reinterpret_cast<void**>(&s.rows), round16(sizeof(int32_t) * batch)},
+      {&s.cand_k, round16(size_t(cand) * es)},
+      {&s.cand_v, round16(size_t(cand) * es)},
+      {&s.q, round16(size_t(cand) * as)},
+      {&s.partials, round16(size_t(batch) * H * max_tiles * (dh + 2) * as)},
+      {reinterpret_cast<void**>(&s.err), round16(sizeof(ErrWords))},
+  };
+  for (auto& a : allocs) {
+    rc = dev_malloc(a.p, a.bytes);
+    if (rc) {
+      *a.p = nullptr;
+      free_cache(c);
+      g_last.expected = int64_t(a.bytes);
+      return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate %zu bytes of KV cache storage", a.bytes);
+    }
+  }
+  rc = dev_host_malloc(reinterpret_cast<void**>(&c->err_host), sizeof(ErrWords));
+  if (rc) {
+    c->err_host = nullptr;
+    free_cache(c);
+    return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate pinned host memory");
+  }
+  // Zero-filled storage (Chapter 37: zeroed backing buffers), zero lengths.
+  for (auto& a : allocs) {
+    if (*a.p == s.err) continue;
+    rc = dev_zero(*a.p, a.bytes, s.stream);
+    if (rc) {
+      free_cache(c);
+      return device_fail(rc, "zero fill");
+    }
+  }
+  rc = dev_clear_err(s.err, s.stream);
+  if (rc) {
+    free_cache(c);
+    return device_fail(rc, "error word init");
+  }
+  // Rotary table: cos/sin of p * base^(-2i/d_h), evaluated in double on the host.
+  if (s.rope) {
+    const int half = dh / 2;
+    const size_t n = size_t(layer->rope_max_positions) * half;
+    std::vector<double> cd(n), sd(n);
+    for (int pos = 0; pos < layer->rope_max_positions; ++pos) {
+      for (int i = 0; i < half; ++i) {
+        const double inv = std::pow(layer->rope_base, -2.0 * double(i) / double(dh));
+        const double ang = double(pos) * inv;
+        cd[size_t(pos) * half + i] = std::cos(ang);
+        sd[size_t(pos) * half + i] = std::sin(ang);
+      }
+    }
+    const size_t bytes = n * as;
+    rc = dev_malloc(&s.rope_cos, round16(bytes));
+    if (rc == 0) rc = dev_malloc(&s.rope_sin, round16(bytes));
+    if (rc) {
+      free_cache(c);
+      return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate the rotary table");
+    }
+    if (as == 8) {
+      rc = dev_copy_h2d_sync(s.rope_cos, cd.data(), bytes, s.stream);
+      if (rc == 0) rc = dev_copy_h2d_sync(s.rope_sin, sd.data(), bytes, s.stream);
+    } else {
+      std::vector<float> cf(cd.begin(), cd.end()), sf(sd.begin(), sd.end());
+      rc = dev_copy_h2d_sync(s.rope_cos, cf.data(), bytes, s.stream);
+      if (rc == 0) rc = dev_copy_h2d_sync(s.rope_sin, sf.data(), bytes, s.stream);
+    }
+    if (rc) {
+      free_cache(c);
+      return device_fail(rc, "rotary table upload");
+    }
+  }
+  rc = dev_sync(s.stream);
+  if (rc) {
+    free_cache(c);
+    return device_fail(rc, "stream synchronisation");
+  }
+  *out = c;
+  return KVC_OK;
+}
+
+void kvc_cache_destroy(kvc_cache* cache) {
+  if (!cache) return;
+  (void)dev_sync(cache->ds.stream);
+  free_cache(cache);
+}
+
+kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const void* x, int32_t rank,
+                                 const int64_t* shape, void* out, int32_t flags, kvc_work* work) {
+  reset_detail();
+  if (!layer || !cache || !x || !out || (rank > 0 && !shape))
+    return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_append_and_attend");
+  if (flags & ~int32_t(KVC_ASYNC)) return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
+  if (!(flags & KVC_ASYNC)) {
+    kvc_status d = check_deferred(cache);
+    if (d != KVC_OK) return d;
+  }
+  // Chapter 37, "Bind the state, calculate completely, then commit": rank,
+  // one token, batch, width, binding, capacity -- in that order.
+  if (rank != 3) return fail_ea(KVC_ERR_INPUT_RANK, 3, rank, "incremental input must have rank 3, got %d", rank);
+  if (shape[1] != 1)
+    return fail_ea(KVC_ERR_SINGLE_TOKEN_REQUIRED, 1, shape[1],
+                   "incremental attention accepts exactly one token, got %lld", (long long)shape[1]);
+  if (shape[0] != cache->batch)
+    return fail_ea(KVC_ERR_INPUT_BATCH_MISMATCH, cache->batch, shape[0],
+                   "incremental input batch %lld does not match cache batch %d", (long long)shape[0],
+                   cache->batch);
+  if (shape[2] != layer->params->model_width)
+    return fail_ea(KVC_ERR_INPUT_WIDTH_MISMATCH, layer->params->model_width, shape[2],
+                   "incremental input width %lld does not match model width %d", (long long)shape[2],
+                   layer->params->model_width);
+  kvc_status st = check_binding(layer, cache);
+  if (st != KVC_OK) return st;
+  for (int b = 0; b < cache->batch; ++b) {
+    if (cache->len[b] >= cache->capacity) {
+      g_last.sequence = b;
+      return fail_ea(KVC_ERR_FULL, cache->capacity, cache->len[b], "KV cache is full at capacity %d",
+                     cache->capacity);
+    }
+  }
+  if (cache->ds.rope) {
+    for (int b = 0; b < cache->batch; ++b) {
+      if (cache->next_pos[b] >= cache->rope_max_positions) {
+        g_last.sequence = b;
+        return fail_ea(KVC_ERR_ROTARY_POSITION, cache->rope_max_positions, cache->next_pos[b],
+                       "position %d of sequence %d reaches the rotary position capacity %d",
+                       cache->next_pos[b], b, cache->rope_max_positions);
+      }
+    }
+  }
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "this build has no device kernels");
+  kvc_work w{};
+  w.position_min = INT32_MAX;
+  w.position_max = -1;
+  for (int b = 0; b < cache->batch; ++b) {
+    w.full_prefix_rows_per_projection += cache->len[b] + 1;
+    w.incremental_rows_per_projection += 1;
+    w.reused_key_value_rows += cache->len[b];
+    w.position_min = std::min(w.position_min, cache->next_pos[b]);
+    w.position_max = std::max(w.position_max, cache->next_pos[b]);
+  }
+  st = run_call(cache, x, 1, nullptr, out, flags, true);
+  if (st == KVC_OK && work) *work = w;
+  return st;
+}
+
+kvc_status kvc_continue_chunk(const kvc_layer* layer, kvc_cache* cache, const void* x, int32_t n_max,
+                              const int32_t* n_rows, void* out, int32_t flags, kvc_work* work) {
+  reset_detail();
+  if (!layer || !cache || !x || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_continue_chunk");
+  if (flags & ~int32_t(KVC_ASYNC)) return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
+  if (!(flags & KVC_ASYNC)) {
+    kvc_status d = check_deferred(cache);
+    if (d != KVC_OK) return d;
+  }
+  if (n_max < 1 || n_max > cache->max_chunk_rows)
+    return fail_ea(KVC_ERR_CHUNK_ROWS, cache->max_chunk_rows, n_max, "chunk rows %d outside [1, %d]", n_max,
+                   cache->max_chunk_rows);
+  if (n_rows) {
+    for (int b = 0; b < cache->batch; ++b) {
+      if (n_rows[b] < 0 || n_rows[b] > n_max) {
+        g_last.sequence = b;
+        return fail_ea(KVC_ERR_CHUNK_ROWS, n_max, n_rows[b], "sequence %d has %d chunk rows, outside [0, %d]", b,
+                       n_rows[b], n_max);
+      }
+    }
+  }
+  kvc_status st = check_binding(layer, cache);
+  if (st != KVC_OK) return st;
+  for (int b = 0; b < cache->batch; ++b) {
+    const int n = n_rows ? n_rows[b] : n_max;
+    if (int64_t(cache->len[b]) + n > cache->capacity) {
+      g_last.sequence = b;
+      return fail_ea(KVC_ERR_FULL, cache->capacity, int64_t(cache->len[b]) + n,
+                     "KV cache is full at capacity %d (sequence %d needs %d more rows)", cache->capacity, b, n);
+    }
+  }
+  if (cache->ds.rope) {
+    for (int b = 0; b < cache->batch; ++b) {
+      const int n = n_rows ? n_rows[b] : n_max;
+      if (n > 0 && int64_t(cache->next_pos[b]) + n > cache->rope_max_positions) {
+        g_last.sequence = b;
+        return fail_ea(KVC_ERR_ROTARY_POSITION, cache->rope_max_positions, int64_t(cache->next_pos[b]) + n - 1,
+                       "position %lld of sequence %d reaches the rotary position capacity %d",
+                       (long long)cache->next_pos[b] + n - 1, b, cache->rope_max_positions);
+      }
+    }
+  }
+  kvc_work w{};
+  w.position_min = INT32_MAX;
+  w.position_max = -1;
+  int64_t total = 0;
+  for (int b = 0; b < cache->batch; ++b) {
+    const int n = n_rows ? n_rows[b] : n_max;
+    w.full_prefix_rows_per_projection += cache->len[b] + n;
+    w.incremental_rows_per_projection += n;
+    w.reused_key_value_rows += cache->len[b];
+    total += n;
+    if (n > 0) {
+      w.position_min = std::min(w.position_min, cache->next_pos[b]);
+      w.position_max = std::max(w.position_max, cache->next_pos[b] + n - 1);
+    }
+  }
+  if (total == 0) {
+    w.position_min = w.position_max = -1;
+    if (work) *work = w;
+    return KVC_OK;
+  }
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "this build has no device kernels");
+  st = run_call(cache, x, n_max, n_rows, out, flags, false);
+  if (st == KVC_OK && work) *work = w;
+  return st;
+}
+
+kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags) {
+  reset_detail();
+  if (!cache || !cut) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_truncate");
+  if (flags & ~int32_t(KVC_TRUNCATE_KEEP_STALE_POSITION)) return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
+  for (int b = 0; b < cache->batch; ++b) {
+    if (cut[b] < 0 || cut[b] > cache->len[b]) {
+      g_last.sequence = b;
+      return fail_ea(KVC_ERR_BAD_CUT, cache->len[b], cut[b], "cut %d of sequence %d is outside [0, %d]", cut[b], b,
+                     cache->len[b]);
+    }
+  }
+  const bool stale = flags & KVC_TRUNCATE_KEEP_STALE_POSITION;
+  int rc = dev_set_lengths(cache->ds, cut, stale ? 1 : 0);
+  if (rc) return device_fail(rc, "length update");
+  for (int b = 0; b < cache->batch; ++b) {
+    cache->len[b] = cut[b];
+    if (!stale) cache->next_pos[b] = cut[b];
+  }
+  return KVC_OK;
+}
+
+kvc_status kvc_reset(kvc_cache* cache) {
+  reset_detail();
+  if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
+  int rc = dev_set_lengths(cache->ds, nullptr, 2);
+  if (rc) return device_fail(rc, "length reset");
+  std::fill(cache->len.begin(), cache->len.end(), 0);
+  std::fill(cache->next_pos.begin(), cache->next_pos.end(), 0);
+  return KVC_OK;
+}
+
+kvc_status kvc_sync(kvc_cache* cache) {
+  reset_detail();
+  if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
+  cache->pending_async = true;  // always look at the device words
+  kvc_status st = check_deferred(cache);
+  if (st != KVC_OK) return st;
+  return resync_lengths(cache);
+}
+
+kvc_status kvc_lengths(kvc_cache* cache, int32_t* len_out, int32_t* next_position_out) {
+  reset_detail();
+  if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
+  kvc_status st = check_deferred(cache);
+  if (st != KVC_OK) return st;
+  st = resync_lengths(cache);
+  if (st != KVC_OK) return st;
+  if (len_out) std::memcpy(len_out, cache->len.data(), sizeof(int32_t) * cache->batch);
+  if (next_position_out) std::memcpy(next_position_out, cache->next_pos.data(), sizeof(int32_t) * cache->batch);
+  return KVC_OK;
+}
+
+kvc_status kvc_snapshot(kvc_cache* cache, int32_t seq, void* keys_out, void* values_out, int32_t* positions_out,
+                        int64_t rows_capacity, int32_t* rows_out) {
+  reset_detail();
+  if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
+  if (seq < 0 || seq >= cache->batch)
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, cache->batch, seq, "sequence %d out of range", seq);
+  kvc_status st = check_deferred(cache);
+  if (st != KVC_OK) return st;
+  st = resync_lengths(cache);
+  if (st != KVC_OK) return st;
+  const int len = cache->len[seq];
+  if (rows_out) *rows_out = len;
+  if ((keys_out || values_out || positions_out) && rows_capacity < len)
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, len, rows_capacity, "snapshot buffers hold %lld rows, need %d",
+                   (long long)rows_capacity, len);
+  const size_t es = elem_size(cache->dtype);
+  const size_t row_bytes = size_t(cache->head_width) * es;
+  const size_t lane_bytes = size_t(cache->capacity) * row_bytes;
+  const size_t seq_off = size_t(seq) * cache->heads * lane_bytes;
+  int rc = 0;
+  // [H, len, d_h] out of [H, C, d_h]: one strided copy per buffer.
+  if (keys_out)
+    rc = dev_copy_d2h_2d_sync(keys_out, size_t(len) * row_bytes, static_cast<char*>(cache->ds.keys) + seq_off,
+                              lane_bytes, size_t(len) * row_bytes, cache->heads, cache->ds.stream);
+  if (rc == 0 && values_out)
+    rc = dev_copy_d2h_2d_sync(values_out, size_t(len) * row_bytes, static_cast<char*>(cache->ds.values) + seq_off,
+                              lane_bytes, size_t(len) * row_bytes, cache->heads, cache->ds.stream);
+  if (rc == 0 && positions_out && len > 0)
+    rc = dev_copy_d2h_sync(positions_out, cache->ds.positions + size_t(seq) * cache->capacity,
+                           sizeof(int32_t) * size_t(len), cache->ds.stream);
+  if (rc) return device_fail(rc, "snapshot copy");
+  return KVC_OK;
+}
+
+kvc_status kvc_lcp_cut(const int32_t* cached, int64_t n_cached, const int32_t* query, int64_t n_query,
+                       int64_t* cut_out) {
+  reset_detail();
+  if (!cut_out || (n_cached > 0 && !cached) || (n_query > 0 && !query))
+    return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_lcp_cut");
+  if (n_cached < 0) return fail(KVC_ERR_BAD_ARGUMENT, "negative cached length");
+  if (n_query <= 0) return fail(KVC_ERR_EMPTY_QUERY, "query token IDs must be non-empty");
+  int64_t n = 0;
+  const int64_t lim = std::min(n_cached, n_query);
+  while (n < lim && cached[n] == query[n]) ++n;
+  *cut_out = std::min(n, n_query - 1);
+  return KVC_OK;
+}
+
+kvc_status kvc_cache_describe(const kvc_cache* cache, kvc_cache_desc* out) {
+  reset_detail();
+  if (!cache || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_cache_describe");
+  out->batch = cache->batch;
+  out->heads = cache->heads;
+  out->head_width = cache->head_width;
+  out->model_width = cache->model_width;
+  out->capacity = cache->capacity;
+  out->max_chunk_rows = cache->max_chunk_rows;
+  out->kv_dtype = cache->dtype;
+  out->pos_mode = cache->pos_mode;
+  out->rope_max_positions = cache->rope_max_positions;
+  out->device = cache->device;
+  out->rope_base = cache->rope_base;
+  return KVC_OK;
+}
+
+kvc_status kvc_storage_pointers(const kvc_cache* cache, const void** keys, const void** values, int64_t* bytes_each) {
+  reset_detail();
+  if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
+  if (keys) *keys = cache->ds.keys;
+  if (values) *values = cache->ds.values;
+  if (bytes_each) *bytes_each = cache->storage_bytes;
+  return KVC_OK;
+}
+
+kvc_status kvc_copy_storage(kvc_cache* cache, void* keys_out, void* values_out) {
+  reset_detail();
+  if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
+  int rc = dev_sync(cache->ds.stream);
+  if (rc == 0 && keys_out) rc = dev_copy_d2h_sync(keys_out, cache->ds.keys, size_t(cache->storage_bytes), cache->ds.stream);
+  if (rc == 0 && values_out)
+    rc = dev_copy_d2h_sync(values_out, cache->ds.values, size_t(cache->storage_bytes), cache->ds.stream);
+  if (rc) return device_fail(rc, "storage copy");
+  return KVC_OK;
+}
+
+kvc_status kvc_profile_enable(kvc_cache* cache, int32_t slots) {
+  reset_detail();
+  if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
+  if (slots < 0) return fail(KVC_ERR_BAD_ARGUMENT, "negative slot count");
+  int rc = dev_sync(cache->ds.stream);
+  if (rc) return device_fail(rc, "stream synchronisation");
+  for (void* e : cache->prof.events) dev_event_destroy(e);
+  cache->prof = Profile{};
+  if (slots == 0) return KVC_OK;
+  const size_t n = size_t(slots) * KVC_STAGES * 2;
+  cache->prof.events.assign(n, nullptr);
+  for (size_t k = 0; k < n; ++k) {
+    rc = dev_event_create(&cache->prof.events[k]);
+    if (rc) {
+      for (void* e : cache->prof.events) dev_event_destroy(e);
+      cache->prof = Profile{};
+      return device_fail(rc, "event creation");
+    }
+  }
+  cache->prof.recorded.assign(size_t(slots) * KVC_STAGES, 0);
+  cache->prof.slots = slots;
+  return KVC_OK;
+}
+
+kvc_status kvc_profile_read(kvc_cache* cache, float* ms_out, int32_t* calls_out) {
+  reset_detail();
+  if (!cache || !ms_out || !calls_out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_profile_read");
+  for (int s = 0; s < KVC_STAGES; ++s) {
+    ms_out[s] = 0.f;
+    calls_out[s] = 0;
+  }
+  const Profile& p = cache->prof;
+  for (int call = 0; call < p.used; ++call) {
+    for (int s = 0; s < KVC_STAGES; ++s) {
+      if (!p.recorded[size_t(call) * KVC_STAGES + s]) continue;
+      float ms = 0.f;
+      const size_t k = (size_t(call) * KVC_STAGES + s) * 2;
+      int rc = dev_event_elapsed(&ms, p.events[k], p.events[k + 1]);
+      if (rc) return device_fail(rc, "event timing");
+      ms_out[s] += ms;
+      calls_out[s] += 1;
+    }
+  }
+  return KVC_OK;
+}
+
+}  // extern "C"

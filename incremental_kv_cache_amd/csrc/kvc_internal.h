@@ -1,0 +1,97 @@
+// Interface between the host cache manager (kvc_host.cpp) and the device
+// backend (kvc_device.hip).  The manager owns validation, bookkeeping and
+// the C ABI; the backend owns allocation, copies and kernel launches.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "kvcache.h"
+
+namespace kvc {
+
+// Device-side failure words.  Each holds the smallest flat index at which the
+// condition was seen (atomicMin), or ~0 when it was not.  While any word is
+// set, every state-changing kernel of the cache is a no-op.
+struct ErrWords {
+  unsigned long long key;       // non-finite candidate key, flat index over [B,H,n,d_h]
+  unsigned long long value;     // non-finite candidate value
+  unsigned long long query;     // non-finite rotated query
+  unsigned long long position;  // sequence index whose row position reached max positions
+  unsigned long long output;    // non-finite attention output, flat index over [B,n,D]
+  unsigned long long pad[3];
+};
+constexpr unsigned long long kErrClear = ~0ull;
+
+// Attention rows per split-K work item of the decode kernel.
+constexpr int kDecodeTileRows = 256;
+// Values per by-value length update (kernel-argument payload).
+constexpr int kSetChunk = 480;
+
+// Everything a launch needs about one cache.  Pointers are device memory.
+struct DevState {
+  int dtype;  // kvc_dtype of storage and weights
+  int batch, heads, head_width, model_width, capacity, max_chunk_rows;
+  int rope;           // 1: rotate q, k
+  int max_positions;  // rotary table rows
+  double scale;       // 1 / sqrt(d_h)
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  void* keys;          // [B, H, C, d_h] storage type
+  void* values;        // [B, H, C, d_h]
+  int32_t* len;        // [B] committed rows
+  int32_t* next_pos;   // [B] position of the next row
+  int32_t* positions;  // [B, C] absolute position of each row
+  int32_t* rows;       // [B] rows of the current chunk call
+  void* cand_k;        // [B, H, n, d_h] storage type (n = rows of the call)
+  void* cand_v;        // [B, H, n, d_h]
+  void* q;             // [B, H, n, d_h] accumulate type
+  void* partials;      // [B, H, max_tiles, d_h + 2] accumulate type
+  int max_tiles;
+  void* rope_cos;  // [max_positions, d_h / 2] accumulate type (null without rotation)
+  void* rope_sin;
+  ErrWords* err;
+  void* stream;  // hipStream_t
+};
+
+// ---- backend, implemented by kvc_device.hip (HIP) -------------------------
+// Every function returns 0 on success or a nonzero backend error code;
+// dev_error_string() describes the last one.
+const char* dev_error_string(int code);
+int dev_current_device(int* device);
+int dev_malloc(void** p, size_t bytes);
+void dev_free(void* p);
+int dev_host_malloc(void** p, size_t bytes);
+void dev_host_free(void* p);
+int dev_copy_h2d_sync(void* dst, const void* src, size_t bytes, void* stream);
+int dev_copy_d2h_sync(void* dst, const void* src, size_t bytes, void* stream);
+int dev_copy_d2h_2d_sync(void* dst, size_t dpitch, const void* src, size_t spitch, size_t width,
+                         size_t height, void* stream);
+int dev_sync(void* stream);
+int dev_zero(void* p, size_t bytes, void* stream);  // bytes % 16 == 0, p 16-byte aligned
+int dev_clear_err(ErrWords* err, void* stream);
+
+// Length updates carried in kernel arguments (no host staging buffers).
+// mode 0: len = np = vals; mode 1: len = vals (next position kept); mode 2: len = np = 0.
+int dev_set_lengths(const DevState& s, const int32_t* vals, int mode);
+// rows[b] = vals[b] for the next chunk call.
+int dev_set_rows(const DevState& s, const int32_t* vals);
+
+// Pipeline stages.  n_max: rows per sequence of this call (1 for decode);
+// per_seq_rows: 0 = every sequence has n_max rows, 1 = rows[] holds them.
+int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows);
+int dev_attend_decode(const DevState& s);
+int dev_merge_decode(const DevState& s, void* out);
+int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out);
+int dev_commit(const DevState& s, int n_max, int per_seq_rows);
+
+int dev_event_create(void** e);
+void dev_event_destroy(void* e);
+int dev_event_record(void* e, void* stream);
+int dev_event_elapsed(float* ms, void* start, void* stop);
+
+// True when the backend can run kernels (false in the CPU-only host-check build).
+bool dev_has_kernels();
+
+}  // namespace kvc

@@ -1,0 +1,73 @@
+"""Helpers for the GPU parity tests: seeded inputs to device tensors, tolerances."""
+import numpy as np
+
+from incremental_kv_cache_amd import kvcache as K
+from incremental_kv_cache_amd import synth
+
+# Parity bars: float64 max-abs 1e-12; float32 normwise relative 1e-5
+# (max|gpu - oracle| / max|oracle|); bf16 storage with float32 accumulation
+# max-abs 2e-2.  Bookkeeping is compared exactly.
+TOL = {"f64": 1e-12, "f32": 1e-5, "bf16": 2e-2}
+
+
+def torch_dtype(dtype):
+    import torch
+    return {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+
+def to_device(storage: np.ndarray, dtype: str):
+    """A storage array from synth.quantize on cuda:0, bf16 bit patterns reinterpreted."""
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(storage).view(np.int16).copy()).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(storage).copy())
+    return t.to("cuda:0")
+
+
+def storage_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of a snapshot in the storage type."""
+    if dtype == "bf16":
+        return synth.bf16_bits_to_f64(arr)
+    return np.asarray(arr, np.float64)
+
+
+def to_f64(t) -> np.ndarray:
+    return t.detach().double().cpu().numpy()
+
+
+def max_err(gpu, ref, dtype):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = float(np.max(np.abs(gpu - ref))) if gpu.size else 0.0
+    if dtype == "f32":
+        return err / max(float(np.max(np.abs(ref))), 1e-300)
+    return err
+
+
+def assert_parity(gpu, ref, dtype, what=""):
+    e = max_err(gpu, ref, dtype)
+    assert e <= TOL[dtype], f"{what}: error {e:.3e} above {TOL[dtype]:.0e} ({dtype})"
+    return e
+
+
+def make_layer(seed, model_width, heads, dtype, std=None, base=10000.0, max_positions=4096,
+               pos_mode=K.KVC_POS_ROPE):
+    """Seeded W_q, W_k, W_v ([D, D] as [out, in]) on the device; returns (layer, float64 weights)."""
+    if std is None:
+        std = model_width ** -0.5
+    ws = synth.decode_weights(seed, model_width, std, dtype)
+    tensors = [to_device(s, dtype) for s, _ in ws]
+    params = K.kvc_params_create(*tensors)
+    layer = K.kvc_layer_create(params, heads, pos_mode, base, max_positions)
+    return layer, [f for _, f in ws]
+
+
+def hidden(seed, stream, batch, rows, model_width, dtype, row_stride=None, first_row=0):
+    """Seeded N(0,1) hidden rows [batch, rows, D]: (device tensor, exact float64 values)."""
+    if row_stride is None:
+        row_stride = first_row + rows
+    vals = np.stack([synth.hidden_rows(seed, stream, b, first_row, rows, model_width, row_stride)
+                     for b in range(batch)])
+    s, f = synth.quantize(vals, dtype)
+    return to_device(s, dtype), f

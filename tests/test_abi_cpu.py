@@ -1,0 +1,79 @@
+"""The C ABI library loads and exports every declared symbol; host-only calls work (CPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from incremental_kv_cache_amd import capi
+from incremental_kv_cache_amd import kvcache as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvcache.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(capi.LIB_PATH):
+        pytest.fail(f"{capi.LIB_PATH} not built (run __graft_entry__.build())")
+    return capi.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(capi.PROTOTYPES), "binding prototypes and header disagree"
+
+
+def test_status_names(lib):
+    assert K.kvc_status_name(0) == "KVC_OK"
+    for name in dir(capi):
+        if name.startswith("KVC_ERR_"):
+            assert K.kvc_status_name(getattr(capi, name)) == name
+    assert K.kvc_status_name(9999) == "KVC_ERR_UNKNOWN"
+
+
+def test_lcp_cut_through_the_abi(lib):
+    """Prefix-reuse note cut rules, computed by the library's host helper."""
+    assert K.kvc_lcp_cut([1, 2, 3, 4, 5, 6, 7, 8], [1, 2, 3, 4, 20, 6, 7, 8, 9, 10, 11, 12]) == 4
+    assert K.kvc_lcp_cut([1, 2, 3, 4, 5, 6, 7, 8], list(range(1, 13))) == 8
+    assert K.kvc_lcp_cut([1, 2, 3, 4, 5, 6, 7, 8], [1, 2, 3, 4]) == 3
+    assert K.kvc_lcp_cut([], [7]) == 0
+    with pytest.raises(K.KvcError) as e:
+        K.kvc_lcp_cut([1], [])
+    assert e.value.name == "KVC_ERR_EMPTY_QUERY"
+
+
+def test_params_and_layer_validation_without_device(lib):
+    """Parameter and layer handles need no device; their argument checks run on the host."""
+    dummy = C.c_void_p(16)
+    out = C.c_void_p()
+    assert lib.kvc_params_create(4, capi.KVC_F64, dummy, dummy, dummy, None) == capi.KVC_ERR_NULL_ARGUMENT
+    assert lib.kvc_params_create(0, capi.KVC_F64, dummy, dummy, dummy, C.byref(out)) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_params_create(4, 7, dummy, dummy, dummy, C.byref(out)) == capi.KVC_ERR_DTYPE_UNSUPPORTED
+    assert lib.kvc_params_create(4, capi.KVC_F64, dummy, dummy, dummy, C.byref(out)) == capi.KVC_OK
+    params = out
+    layer = C.c_void_p()
+    assert lib.kvc_layer_create(params, 3, 0, 10000.0, 4, C.byref(layer)) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_layer_create(params, 4, 0, 10000.0, 4, C.byref(layer)) == capi.KVC_ERR_SHAPE_UNSUPPORTED
+    assert lib.kvc_layer_create(params, 2, 0, -1.0, 4, C.byref(layer)) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_layer_create(params, 2, 0, 10000.0, 4, C.byref(layer)) == capi.KVC_OK
+    # cache-constructor checks that precede any allocation (Chapter 37 order)
+    cache = C.c_void_p()
+    assert lib.kvc_cache_create(layer, 0, 4, 1, None, C.byref(cache)) == capi.KVC_ERR_ZERO_BATCH
+    assert lib.kvc_cache_create(layer, 1, 0, 1, None, C.byref(cache)) == capi.KVC_ERR_ZERO_CAPACITY
+    assert lib.kvc_cache_create(layer, 1, 5, 1, None, C.byref(cache)) == capi.KVC_ERR_CAPACITY_EXCEEDS_POSITIONS
+    d = lib.kvc_last_error().contents
+    assert (d.expected, d.actual) == (4, 5)
+    assert b"exceeds RoPE position capacity" in d.message
+    assert lib.kvc_params_mark_updated(params, 3) == capi.KVC_ERR_BAD_ARGUMENT
+    lib.kvc_layer_destroy(layer)
+    lib.kvc_params_destroy(params)

@@ -1,0 +1,223 @@
+"""Host cache manager on the CPU: validation order, binding, truncate/reset bookkeeping.
+
+The manager (incremental_kv_cache_amd/csrc/kvc_host.cpp) is linked here against
+tests/hostcheck_backend.cpp, a stand-in backend whose "device" memory is host
+memory and which cannot run kernels.  Every request that passes validation
+therefore stops with KVC_ERR_DEVICE at the launch point, which is how these
+tests see that validation let it through.  The checks follow Chapter 37's
+order ("Bind the state, calculate completely, then commit") and its
+error-evidence cases.
+"""
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+from incremental_kv_cache_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("hostcheck") / "libkvc_hostcheck.so")
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "incremental_kv_cache_amd", "csrc"),
+           os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_host.cpp"),
+           os.path.join(ROOT, "tests", "hostcheck_backend.cpp"), "-o", out]
+    subprocess.run(cmd, check=True)
+    return capi.declare(C.CDLL(out))
+
+
+DUMMY = C.c_void_p(64)
+
+
+def params(lib, d=4, dtype=capi.KVC_F64):
+    p = C.c_void_p()
+    assert lib.kvc_params_create(d, dtype, DUMMY, DUMMY, DUMMY, C.byref(p)) == 0
+    return p
+
+
+def layer(lib, p, heads=2, base=10000.0, max_pos=4, mode=capi.KVC_POS_ROPE):
+    l = C.c_void_p()
+    assert lib.kvc_layer_create(p, heads, mode, base, max_pos, C.byref(l)) == 0
+    return l
+
+
+def cache(lib, l, batch=1, cap=4, chunk=1):
+    c = C.c_void_p()
+    st = lib.kvc_cache_create(l, batch, cap, chunk, None, C.byref(c))
+    assert st == 0, lib.kvc_last_error().contents.message
+    return c
+
+
+def append(lib, l, c, shape):
+    arr = (C.c_int64 * len(shape))(*shape)
+    w = capi.Work()
+    return lib.kvc_append_and_attend(l, c, DUMMY, len(shape), arr, DUMMY, 0, C.byref(w))
+
+
+def state(lib, c, batch=1):
+    ln = np.zeros(batch, np.int32)
+    npos = np.zeros(batch, np.int32)
+    assert lib.kvc_lengths(c, ln.ctypes.data_as(capi.PI32), npos.ctypes.data_as(capi.PI32)) == 0
+    k = C.c_void_p()
+    v = C.c_void_p()
+    n = C.c_int64()
+    assert lib.kvc_storage_pointers(c, C.byref(k), C.byref(v), C.byref(n)) == 0
+    kb = np.zeros(n.value, np.uint8)
+    vb = np.zeros(n.value, np.uint8)
+    assert lib.kvc_copy_storage(c, kb.ctypes.data_as(C.c_void_p), vb.ctypes.data_as(C.c_void_p)) == 0
+    return ln.tolist(), npos.tolist(), k.value, v.value, kb.tobytes(), vb.tobytes()
+
+
+def test_create_geometry_and_zeroed_storage(lib):
+    p = params(lib)
+    l = layer(lib, p)
+    c = cache(lib, l, batch=3, cap=4, chunk=2)
+    d = capi.CacheDesc()
+    assert lib.kvc_cache_describe(c, C.byref(d)) == 0
+    assert (d.batch, d.heads, d.head_width, d.model_width, d.capacity, d.max_chunk_rows) == (3, 2, 2, 4, 4, 2)
+    ln, npos, kp, vp, kb, vb = state(lib, c, 3)
+    assert ln == [0, 0, 0] and npos == [0, 0, 0]
+    assert len(kb) == 3 * 2 * 4 * 2 * 8 and set(kb) == {0} and set(vb) == {0}
+    lib.kvc_cache_destroy(c)
+
+
+def test_create_checks_in_order(lib):
+    """Chapter 37 constructor: zero batch, zero capacity, capacity over position capacity, overflow."""
+    p = params(lib)
+    l = layer(lib, p, max_pos=4)
+    c = C.c_void_p()
+    assert lib.kvc_cache_create(l, 0, 0, 1, None, C.byref(c)) == capi.KVC_ERR_ZERO_BATCH
+    assert lib.kvc_cache_create(l, 1, 0, 1, None, C.byref(c)) == capi.KVC_ERR_ZERO_CAPACITY
+    assert lib.kvc_cache_create(l, 1, 5, 1, None, C.byref(c)) == capi.KVC_ERR_CAPACITY_EXCEEDS_POSITIONS
+    assert lib.kvc_cache_create(l, 1, 4, 0, None, C.byref(c)) == capi.KVC_ERR_BAD_ARGUMENT
+    big = layer(lib, params(lib, d=128, dtype=capi.KVC_BF16), heads=1, max_pos=2 ** 31 - 1)
+    assert lib.kvc_cache_create(big, 2 ** 31 - 1, 2 ** 31 - 1, 1, None, C.byref(c)) == \
+        capi.KVC_ERR_ELEMENT_COUNT_OVERFLOW
+    assert b"overflows" in lib.kvc_last_error().contents.message
+
+
+def test_request_checks_follow_the_chapter_order_and_leave_state_unchanged(lib):
+    """Rank, one token, batch, width, binding, capacity -- each rejection leaves the
+    cache's lengths, allocation and storage as they were."""
+    p = params(lib)
+    l = layer(lib, p)
+    c = cache(lib, l)
+    before = state(lib, c)
+    cases = [
+        ((1, 4), capi.KVC_ERR_INPUT_RANK),              # rank first, even with other faults
+        ((2, 2, 8), capi.KVC_ERR_SINGLE_TOKEN_REQUIRED),  # two-token input (error evidence)
+        ((2, 1, 8), capi.KVC_ERR_INPUT_BATCH_MISMATCH),
+        ((1, 1, 8), capi.KVC_ERR_INPUT_WIDTH_MISMATCH),
+    ]
+    for shape, want in cases:
+        assert append(lib, l, c, shape) == want, shape
+        d = lib.kvc_last_error().contents
+        assert d.status == want
+        if want == capi.KVC_ERR_INPUT_WIDTH_MISMATCH:
+            assert (d.expected, d.actual) == (4, 8)
+        assert state(lib, c) == before
+    # a valid request passes every host check and reaches the (absent) device
+    assert append(lib, l, c, (1, 1, 4)) == capi.KVC_ERR_DEVICE
+    assert state(lib, c) == before
+
+
+def test_binding_cases_of_the_error_evidence(lib):
+    """Chapter 37 error evidence: model-width mismatch, head mismatch, rebuilt layer,
+    doubled RoPE base, one more max position; plus the in-place update case."""
+    p = params(lib)
+    l = layer(lib, p)
+    x = (1, 1, 4)
+    wider = layer(lib, params(lib, d=8), heads=2)
+    c = cache(lib, wider)
+    assert append(lib, l, c, x) == capi.KVC_ERR_CACHE_MODEL_WIDTH_MISMATCH
+    one_head = layer(lib, params(lib, d=4), heads=1)
+    c = cache(lib, one_head)
+    assert append(lib, l, c, x) == capi.KVC_ERR_CACHE_HEAD_COUNT_MISMATCH
+    rebuilt = layer(lib, params(lib))                 # same shapes, new parameter identity
+    c = cache(lib, rebuilt)
+    assert append(lib, l, c, x) == capi.KVC_ERR_CACHE_LAYER_MISMATCH
+    c = cache(lib, l)
+    doubled = layer(lib, p, base=20000.0)             # same parameters, different rotary base
+    assert append(lib, doubled, c, x) == capi.KVC_ERR_CACHE_ROPE_MISMATCH
+    d = lib.kvc_last_error().contents
+    assert tuple(d.rope_base) == (10000.0, 20000.0)
+    more = layer(lib, p, max_pos=5)
+    assert append(lib, more, c, x) == capi.KVC_ERR_CACHE_ROPE_MISMATCH
+    assert tuple(lib.kvc_last_error().contents.rope_max_positions) == (4, 5)
+    none_mode = layer(lib, p, mode=capi.KVC_POS_NONE)
+    assert append(lib, none_mode, c, x) == capi.KVC_ERR_CACHE_ROPE_MISMATCH
+    # in-place update of W_v: identity kept, revision advanced; reset does not rebind
+    assert lib.kvc_params_mark_updated(p, 2) == 0
+    assert append(lib, l, c, x) == capi.KVC_ERR_CACHE_LAYER_REVISION_MISMATCH
+    d = lib.kvc_last_error().contents
+    assert (d.parameter, d.cache_revision, d.layer_revision) == (2, 0, 1)
+    assert lib.kvc_reset(c) == 0
+    assert append(lib, l, c, x) == capi.KVC_ERR_CACHE_LAYER_REVISION_MISMATCH
+    fresh = cache(lib, l)                             # a new cache binds the new revision
+    assert append(lib, l, fresh, x) == capi.KVC_ERR_DEVICE
+
+
+def test_binding_precedes_shape_of_geometry(lib):
+    """Width mismatch of the *input* is checked before any cache binding check."""
+    p = params(lib)
+    l = layer(lib, p)
+    other = cache(lib, layer(lib, params(lib)))
+    assert append(lib, l, other, (1, 1, 3)) == capi.KVC_ERR_INPUT_WIDTH_MISMATCH
+    assert append(lib, l, other, (1, 1, 4)) == capi.KVC_ERR_CACHE_LAYER_MISMATCH
+
+
+def test_truncate_reset_and_snapshot_bookkeeping(lib):
+    p = params(lib)
+    l = layer(lib, p)
+    c = cache(lib, l, batch=2)
+    cut = np.array([0, 1], np.int32)
+    assert lib.kvc_truncate(c, cut.ctypes.data_as(capi.PI32), 0) == capi.KVC_ERR_BAD_CUT
+    d = lib.kvc_last_error().contents
+    assert (d.sequence, d.expected, d.actual) == (1, 0, 1)
+    cut = np.array([-1, 0], np.int32)
+    assert lib.kvc_truncate(c, cut.ctypes.data_as(capi.PI32), 0) == capi.KVC_ERR_BAD_CUT
+    cut = np.array([0, 0], np.int32)
+    assert lib.kvc_truncate(c, cut.ctypes.data_as(capi.PI32), 4) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_truncate(c, cut.ctypes.data_as(capi.PI32), 0) == 0
+    assert lib.kvc_truncate(c, cut.ctypes.data_as(capi.PI32), capi.KVC_TRUNCATE_KEEP_STALE_POSITION) == 0
+    before = state(lib, c, 2)
+    assert lib.kvc_reset(c) == 0
+    after = state(lib, c, 2)
+    assert after == before                            # same pointers and bytes
+    rows = C.c_int32()
+    assert lib.kvc_snapshot(c, 1, None, None, None, 0, C.byref(rows)) == 0 and rows.value == 0
+    assert lib.kvc_snapshot(c, 2, None, None, None, 0, C.byref(rows)) == capi.KVC_ERR_BAD_ARGUMENT
+
+
+def test_chunk_checks(lib):
+    p = params(lib)
+    l = layer(lib, p, max_pos=8)
+    c = cache(lib, l, batch=2, cap=4, chunk=6)
+    w = capi.Work()
+    assert lib.kvc_continue_chunk(l, c, DUMMY, 7, None, DUMMY, 0, C.byref(w)) == capi.KVC_ERR_CHUNK_ROWS
+    assert lib.kvc_continue_chunk(l, c, DUMMY, 0, None, DUMMY, 0, C.byref(w)) == capi.KVC_ERR_CHUNK_ROWS
+    rows = np.array([2, 3], np.int32)
+    assert lib.kvc_continue_chunk(l, c, DUMMY, 2, rows.ctypes.data_as(capi.PI32), DUMMY, 0,
+                                  C.byref(w)) == capi.KVC_ERR_CHUNK_ROWS
+    assert lib.kvc_last_error().contents.sequence == 1
+    assert lib.kvc_continue_chunk(l, c, DUMMY, 5, None, DUMMY, 0, C.byref(w)) == capi.KVC_ERR_FULL
+    rows = np.array([0, 0], np.int32)                 # nothing to do: OK with zero work
+    assert lib.kvc_continue_chunk(l, c, DUMMY, 3, rows.ctypes.data_as(capi.PI32), DUMMY, 0, C.byref(w)) == 0
+    assert w.incremental_rows_per_projection == 0
+    assert lib.kvc_continue_chunk(l, c, DUMMY, 4, None, DUMMY, 0, C.byref(w)) == capi.KVC_ERR_DEVICE
+    other = layer(lib, params(lib), max_pos=8)
+    assert lib.kvc_continue_chunk(other, c, DUMMY, 2, None, DUMMY, 0, C.byref(w)) == capi.KVC_ERR_CACHE_LAYER_MISMATCH
+
+
+def test_null_arguments(lib):
+    assert lib.kvc_reset(None) == capi.KVC_ERR_NULL_ARGUMENT
+    assert lib.kvc_sync(None) == capi.KVC_ERR_NULL_ARGUMENT
+    assert lib.kvc_truncate(None, None, 0) == capi.KVC_ERR_NULL_ARGUMENT
+    assert lib.kvc_append_and_attend(None, None, None, 3, None, None, 0, None) == capi.KVC_ERR_NULL_ARGUMENT
+    out = C.c_int64()
+    assert lib.kvc_lcp_cut(None, 2, None, 1, C.byref(out)) == capi.KVC_ERR_NULL_ARGUMENT
