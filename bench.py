@@ -1,0 +1,289 @@
+"""Decode-step throughput of the layer-bound KV cache on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one cached decode step of one layer over the whole batch: the new
+rows' Q/K/V projection with RoPE, split-K attention over every retained row
+plus the candidate row, the log-sum-exp merge, and the predicated append
+(kvc_append_and_attend), preceded by kvc_truncate back to the starting length
+so that every timed step sees the same t.  Inputs (weights, hidden rows, the
+prefilled cache) are seeded synthetic data resident in HBM before timing.
+
+Workloads (default: headline):
+  headline  B=32, H=32, d_h=128, C=4096, t=4096 for every sequence, bf16 K/V
+  ragged    same shape, t_b uniform on [1, 4096]
+  long      B=4, C=32768, t=32768 for every sequence
+  chunk     B=8, C=16384, cut_b uniform on [0, 8192], 512-row suffix chunk per
+            sequence (step = truncate to cut + kvc_continue_chunk)
+
+Prints one JSON line (rank 0).  `roofline` describes the dominant kernel, timed
+with HIP events recorded by the library on the cache's stream.  `cpu_baseline`
+times the float64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode tokens/s + KV-read GB/s (% of HBM peak) at B=32,H=32,d_h=128,t=4096"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+SEED = 37
+
+WORKLOADS = {
+    "headline": dict(B=32, H=32, dh=128, C=4096, t="full", kind="decode"),
+    "ragged": dict(B=32, H=32, dh=128, C=4096, t="uniform", kind="decode"),
+    "long": dict(B=4, H=32, dh=128, C=32768, t="full", kind="decode"),
+    "chunk": dict(B=8, H=32, dh=128, C=16384, cut_max=8192, n=512, kind="chunk"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _pool():
+    return cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1))
+
+
+def gen_rows_bf16(stream, B, first, n, D, row_stride, lens=None):
+    """[B, n, D] bf16 bit patterns of hidden rows first..first+n-1 (rows beyond lens[b] zero)."""
+    from incremental_kv_cache_amd import synth
+    out = np.zeros((B, n, D), np.uint16)
+
+    def one(b):
+        m = n if lens is None else max(0, min(n, lens[b] - first))
+        if m > 0:
+            out[b, :m] = synth.round_to_bf16_bits(synth.hidden_rows(SEED, stream, b, first, m, D, row_stride))
+
+    with _pool() as ex:
+        list(ex.map(one, range(B)))
+    return out
+
+
+def to_dev_bf16(bits):
+    import torch
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def setup(wl, max_chunk=512):
+    """Weights, layer, cache prefilled to each sequence's starting length."""
+    import torch
+    from incremental_kv_cache_amd import kvcache as K
+    from incremental_kv_cache_amd import synth
+
+    B, H, dh, C = wl["B"], wl["H"], wl["dh"], wl["C"]
+    D = H * dh
+    t0 = time.time()
+    with _pool() as ex:
+        ws = list(ex.map(lambda s: synth.round_to_bf16_bits(synth.normal(SEED, s, (D, D), std=D ** -0.5)),
+                         (synth.STREAM_WQ, synth.STREAM_WK, synth.STREAM_WV)))
+    wdev = [to_dev_bf16(w) for w in ws]
+    params = K.kvc_params_create(*wdev)
+    layer = K.kvc_layer_create(params, H, K.KVC_POS_ROPE, 10000.0, C)
+    cache = K.kvc_cache_create(layer, B, C, max_chunk_rows=max_chunk)
+    if wl["kind"] == "decode":
+        if wl["t"] == "full":
+            start = [C - 1] * B
+        else:
+            start = [int(v) - 1 for v in synth.uniform_int(SEED, synth.STREAM_LENGTHS, B, 1, C)]
+    else:
+        start = [int(v) for v in synth.uniform_int(SEED, synth.STREAM_LENGTHS, B, 0, wl["cut_max"])]
+    L = max(start)
+    pre_out = torch.empty(B, max_chunk, D, dtype=torch.float32, device="cuda")
+    for first in range(0, L, max_chunk):
+        n = min(max_chunk, L - first)
+        rows = [max(0, min(n, s - first)) for s in start]
+        bits = gen_rows_bf16(synth.STREAM_PREFIX_X, B, first, n, D, C, start)
+        K.kvc_continue_chunk(layer, cache, to_dev_bf16(bits), n_rows=rows,
+                             out=pre_out[:, :n] if n == max_chunk else None, flags=K.KVC_ASYNC)
+    K.kvc_sync(cache)
+    torch.cuda.synchronize()
+    ln, _ = K.kvc_lengths(cache)
+    assert ln.tolist() == start, "prefill lengths differ"
+    log(f"setup: prefilled {sum(start)} rows in {time.time() - t0:.1f}s")
+    return dict(weights_bits=ws, wdev=wdev, params=params, layer=layer, cache=cache, start=start, D=D)
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def stage_times(cache, step, steps):
+    """Average per-stage kernel time (ms) from the library's HIP events."""
+    import torch
+    from incremental_kv_cache_amd import kvcache as K
+    K.kvc_profile_enable(cache, steps)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms, calls = K.kvc_profile_read(cache)
+    K.kvc_profile_enable(cache, 0)
+    return [m / c if c else 0.0 for m, c in zip(ms, calls)]
+
+
+def cpu_baseline_decode(env, wl, out_gpu, x_bits, budget_s=20.0):
+    """Float64 oracle on the host: full-prefix recompute of the newest row for as many
+    sequences as fit the time budget; also returns the parity of those rows."""
+    from incremental_kv_cache_amd import synth
+    from oracle import attention as A
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    D, H = env["D"], wl["H"]
+    w = [synth.bf16_bits_to_f64(b) for b in env["weights_bits"]]
+    done, t_work, worst = 0, 0.0, 0.0
+    for b in range(wl["B"]):
+        s = env["start"][b]
+        prefix = synth.bf16_bits_to_f64(synth.round_to_bf16_bits(
+            synth.hidden_rows(SEED, synth.STREAM_PREFIX_X, b, 0, s, D, wl["C"])))
+        rows = np.concatenate([prefix, synth.bf16_bits_to_f64(x_bits[b])])
+        t0 = time.perf_counter()
+        ref = A.full_prefix_decode(rows, *w, heads=H)
+        t_work += time.perf_counter() - t0
+        worst = max(worst, float(np.max(np.abs(out_gpu[b] - ref["out"]))))
+        done += 1
+        if t_work >= budget_s:
+            break
+    return {"value": done / t_work, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 full-prefix recompute (projection of all t rows + newest-row attention) "
+                      f"for sequences 0..{done - 1} of {wl['B']} (t = "
+                      f"{', '.join(str(env['start'][b] + 1) for b in range(done))}), {t_work:.1f}s of CPU work"}, \
+        worst, done
+
+
+def run_decode(name, wl, steps, warmup, cpu):
+    import torch
+    from incremental_kv_cache_amd import kvcache as K
+    from incremental_kv_cache_amd import synth
+
+    env = setup(wl)
+    B, H, dh = wl["B"], wl["H"], wl["dh"]
+    D = env["D"]
+    layer, cache, start = env["layer"], env["cache"], env["start"]
+    x_bits = np.stack([synth.round_to_bf16_bits(synth.hidden_rows(SEED, synth.STREAM_X, b, 0, 1, D, 1))
+                       for b in range(B)])
+    x = to_dev_bf16(x_bits.reshape(B, 1, D).copy())
+    out = torch.empty(B, 1, D, dtype=torch.float32, device="cuda")
+
+    def step():
+        K.kvc_truncate(cache, start)
+        K.kvc_append_and_attend(layer, cache, x, out=out, flags=K.KVC_ASYNC)
+
+    sec = time_steps(step, steps, warmup)
+    K.kvc_sync(cache)
+    st = stage_times(cache, step, steps)
+    K.kvc_sync(cache)
+    torch.cuda.synchronize()
+    t = [s + 1 for s in start]
+    kv_bytes = sum(2 * H * tb * dh * 2 for tb in t)
+    attend_ms = st[1]
+    att_gbps = kv_bytes / (attend_ms * 1e-3) / 1e9
+    attn_merge_gbps = kv_bytes / ((st[1] + st[2]) * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": B / sec, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: one-layer cached decode, B={B} H={H} d_h={dh} C={wl['C']} "
+                               f"t={'uniform[1,%d]' % wl['C'] if wl['t'] == 'uniform' else t[0]}, bf16 K/V, "
+                               f"fp32 accumulate", "batch": B, "heads": H, "head_width": dh,
+                   "capacity": wl["C"], "t_mean": float(np.mean(t)), "seed": SEED},
+        "kv_read_GBps": attn_merge_gbps, "kv_read_frac_of_peak": attn_merge_gbps / HBM_PEAK_GBPS,
+        "stage_ms": {"project": st[0], "attend": st[1], "merge": st[2], "commit": st[3]},
+        "roofline": {"bound": "hbm", "kernel": "attend_decode_kernel", "achieved": att_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": att_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": kv_bytes},
+    }
+    out_np = out.double().cpu().numpy()[:, 0]
+    if cpu:
+        cb, worst, n = cpu_baseline_decode(env, wl, out_np, x_bits)
+        res["cpu_baseline"] = cb
+        res["parity"] = {"sequences": n, "max_abs_err_vs_oracle": worst, "tolerance": 2e-2}
+    return res
+
+
+def run_chunk(name, wl, steps, warmup, cpu):
+    import torch
+    from incremental_kv_cache_amd import kvcache as K
+    from incremental_kv_cache_amd import synth
+
+    env = setup(wl)
+    B, H, dh, n = wl["B"], wl["H"], wl["dh"], wl["n"]
+    D = env["D"]
+    layer, cache, start = env["layer"], env["cache"], env["start"]
+    # the chunk rows are the rows that follow each cut (stream X, row-addressable)
+    bits = gen_rows_bf16(synth.STREAM_X, B, 0, n, D, n)
+    x = to_dev_bf16(bits)
+    out = torch.zeros(B, n, D, dtype=torch.float32, device="cuda")
+
+    def step():
+        K.kvc_truncate(cache, start)
+        K.kvc_continue_chunk(layer, cache, x, out=out, flags=K.KVC_ASYNC)
+
+    sec = time_steps(step, steps, warmup)
+    K.kvc_sync(cache)
+    st = stage_times(cache, step, steps)
+    K.kvc_sync(cache)
+    attn_flops = sum(4 * H * dh * sum(c + i + 1 for i in range(n)) for c in start)
+    proj_flops = 2 * B * n * D * 3 * D
+    att_tf = attn_flops / (st[1] * 1e-3) / 1e12
+    res = {
+        "metric": "suffix-chunk tokens/s (MFMA utilisation)", "value": B * n / sec, "unit": "tokens/s",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: suffix chunk n={n}, B={B} H={H} d_h={dh} C={wl['C']} "
+                               f"cut uniform[0,{wl['cut_max']}], bf16", "cuts": start, "seed": SEED},
+        "stage_ms": {"project": st[0], "attend": st[1], "merge": st[2], "commit": st[3]},
+        "project_TFLOPs": proj_flops / (st[0] * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "kernel": "attend_flash_kernel", "achieved": att_tf,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": att_tf / BF16_PEAK_TFLOPS,
+                     "traffic": None, "algorithmic_flops_per_launch": attn_flops},
+    }
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    from incremental_kv_cache_amd import capi
+    capi.lib()  # fails loudly if the HIP library is missing
+    wl = WORKLOADS[a.workload]
+    fn = run_decode if wl["kind"] == "decode" else run_chunk
+    res = fn(a.workload, wl, a.steps, a.warmup, not a.no_cpu_baseline)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

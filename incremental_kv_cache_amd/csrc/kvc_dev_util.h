@@ -1,0 +1,115 @@
+// Device helpers shared by the HIP sources of libkvcache (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace dev {
+
+using bf16_t = uint16_t;
+
+// ------------------------------------------------------------ conversions --
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Round-to-nearest-even float -> bfloat16 (NaN kept quiet).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+template <typename T> struct Acc;
+template <> struct Acc<double> { using type = double; };
+template <> struct Acc<float> { using type = float; };
+template <> struct Acc<bf16_t> { using type = float; };
+
+template <typename A> __device__ __forceinline__ A to_acc(double v) { return A(v); }
+template <typename A> __device__ __forceinline__ A to_acc(float v) { return A(v); }
+template <typename A> __device__ __forceinline__ A to_acc(bf16_t v) { return A(bf16_to_f32(v)); }
+
+template <typename T> __device__ __forceinline__ T from_acc(typename Acc<T>::type v);
+template <> __device__ __forceinline__ double from_acc<double>(double v) { return v; }
+template <> __device__ __forceinline__ float from_acc<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_acc<bf16_t>(float v) { return f32_to_bf16(v); }
+
+__device__ __forceinline__ bool finite(double v) { return isfinite(v); }
+__device__ __forceinline__ bool finite(float v) { return isfinite(v); }
+
+__device__ __forceinline__ double fast_exp(double v) { return exp(v); }
+__device__ __forceinline__ float fast_exp(float v) { return expf(v); }
+
+// ------------------------------------------------------- vector row loads --
+
+template <int BYTES> struct Raw;
+template <> struct Raw<16> { using type = uint4; };
+template <> struct Raw<8> { using type = uint2; };
+template <> struct Raw<4> { using type = uint32_t; };
+template <> struct Raw<2> { using type = uint16_t; };
+
+// Loads VEC consecutive elements (VEC * sizeof(T) bytes, naturally aligned)
+// and widens them to the accumulate type.
+template <typename T, int VEC>
+__device__ __forceinline__ void load_row_chunk(const T* __restrict__ p, typename Acc<T>::type (&out)[VEC]) {
+  using R = typename Raw<VEC * sizeof(T)>::type;
+  union {
+    R raw;
+    T e[VEC];
+  } u;
+  u.raw = *reinterpret_cast<const R*>(p);
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) out[i] = to_acc<typename Acc<T>::type>(u.e[i]);
+}
+
+// Lane geometry of a row of DH elements of T: each lane reads one chunk of up
+// to 16 bytes; G lanes cover a row; a wavefront of 64 covers RPW rows.
+template <typename T, int DH>
+struct RowGeo {
+  static constexpr int VEC = (DH * int(sizeof(T)) >= 16) ? 16 / int(sizeof(T)) : DH;
+  static constexpr int G = DH / VEC;
+  static constexpr int RPW = 64 / G;
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "unsupported head width");
+};
+
+template <int G, typename A>
+__device__ __forceinline__ A group_sum(A v) {
+#pragma unroll
+  for (int off = G / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ void flag_min(unsigned long long* word, unsigned long long idx) {
+  atomicMin(word, idx);
+}
+
+__device__ __forceinline__ bool any_error(const ErrWords* e) {
+  return (e->key & e->value & e->query & e->position & e->output) != kErrClear;
+}
+
+
+
+// ------------------------------------------------------------------ MFMA --
+// Operand layouts of the gfx950 bf16 MFMAs used here (checked on the device):
+//  32x32x16: A lane l = row l%32, k 8*(l/32)+e;  B lane l = k 8*(l/32)+e, col l%32;
+//            C register r = row 8*(r/4)+4*(l/32)+(r%4), col l%32.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+union Frag8 {
+  uint4 u;
+  bf16x8_t v;
+  bf16_t h[8];
+};
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace dev
+}  // namespace kvc

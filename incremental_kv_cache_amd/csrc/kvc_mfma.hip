@@ -1,0 +1,435 @@
+// bf16 matrix-core (MFMA) kernels of libkvcache for gfx950.
+//
+//  * project_skinny : the new rows (decode: M = B rows) through W_q, W_k, W_v.
+//                     A [M, D] x [D, 3D] contraction whose time is the weight
+//                     read from HBM; a workgroup owns a 32-row x 16-pair output
+//                     tile and its four waves split the reduction axis, each
+//                     streaming whole 128-byte lines of weight rows.
+//  * project_tiled  : the same contraction for many rows (chunks, prefill):
+//                     128 x 128 tiles staged through LDS, 2 x 2 waves.
+//  * attend_flash   : causal chunk attention (prefix-reuse note: suffix row i
+//                     reads the retained rows plus chunk rows 0..i) with the
+//                     score and value contractions on MFMA and an online
+//                     softmax in between.
+//
+// Rotary pairs: output columns are ordered so that feature f and f + d_h/2 of a
+// head land in the same thread (tiled) or the same LDS row (skinny), so the
+// rotation at position next_position + i is applied in the epilogue.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kvc_dev_util.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+using namespace dev;
+
+__device__ __forceinline__ const bf16_t* weight_of(const DevState& s, int p) {
+  return static_cast<const bf16_t*>(p == 0 ? s.wq : (p == 1 ? s.wk : s.wv));
+}
+
+// Rotates (if needed) and stores rotary pair `pair` (global pair index within
+// projection p: head pair / half, feature pair % half) of row m.
+__device__ __forceinline__ void store_pair(const DevState& s, int p, int m, int pair, float lo, float hi, int M,
+                                           int n_max, int per_seq_rows) {
+  if (m >= M) return;
+  const int b = m / n_max;
+  const int i = m - b * n_max;
+  const int n_b = per_seq_rows ? s.rows[b] : n_max;
+  if (i >= n_b) return;
+  const int dh = s.head_width;
+  const int half = dh >> 1;
+  const int h = pair / half;
+  const int f = pair - h * half;
+  float r0 = lo, r1 = hi;
+  if (p < 2 && s.rope) {
+    int pos = s.next_pos[b] + i;
+    if (pos < 0 || pos >= s.max_positions) {
+      flag_min(&s.err->position, (unsigned long long)b);
+      pos = 0;
+    }
+    const float c = static_cast<const float*>(s.rope_cos)[size_t(pos) * half + f];
+    const float sn = static_cast<const float*>(s.rope_sin)[size_t(pos) * half + f];
+    r0 = lo * c - hi * sn;
+    r1 = hi * c + lo * sn;
+  }
+  const size_t flat0 = (size_t(b * s.heads + h) * n_max + i) * dh + f;
+  const size_t flat1 = flat0 + half;
+  if (p == 0) {
+    float* q = static_cast<float*>(s.q);
+    q[flat0] = r0;
+    q[flat1] = r1;
+    if (!isfinite(r0)) flag_min(&s.err->query, flat0);
+    if (!isfinite(r1)) flag_min(&s.err->query, flat1);
+  } else {
+    bf16_t* dst = static_cast<bf16_t*>(p == 1 ? s.cand_k : s.cand_v);
+    const bf16_t t0 = f32_to_bf16(r0), t1 = f32_to_bf16(r1);
+    dst[flat0] = t0;
+    dst[flat1] = t1;
+    unsigned long long* word = p == 1 ? &s.err->key : &s.err->value;
+    if (!isfinite(bf16_to_f32(t0))) flag_min(word, flat0);
+    if (!isfinite(bf16_to_f32(t1))) flag_min(word, flat1);
+  }
+}
+
+// ------------------------------------------------------------ skinny GEMM --
+// Block (t, mt): rows m0 = 32 mt .. +32, pairs 16 (t mod D/32) .. +16 of
+// projection p = t / (D/32).  Output column j < 16 is the low feature of pair
+// j, column j >= 16 the high feature of pair j - 16.  Wave w reduces the
+// 64-wide k chunks c = w, w + 4, ...; lane l reads 64 contiguous bytes of its
+// weight row (and of its input row) per chunk, with k-slot (8 (l/32) + e) of
+// MFMA step u holding element k = 64 c + 32 (l/32) + 8 u + e on both operands.
+__global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const bf16_t* __restrict__ x, int M,
+                                                             int n_max, int per_seq_rows) {
+  __shared__ float red[4][32][33];
+  const int D = s.model_width;
+  const int half = s.head_width >> 1;
+  const int tiles_per_proj = D / 32;
+  const int p = blockIdx.x / tiles_per_proj;
+  const int pair_base = (blockIdx.x - p * tiles_per_proj) * 16;
+  const int m0 = blockIdx.y * 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 5;
+  const int col = lane & 31;
+
+  const int pair = pair_base + (col & 15);
+  const int h = pair / half;
+  const int f = pair - h * half;
+  const int wrow = h * s.head_width + f + ((col >> 4) ? half : 0);
+  const bf16_t* wp = weight_of(s, p) + size_t(wrow) * D + 32 * g;
+  const int xr = min(m0 + col, M - 1);
+  const bf16_t* xp = x + size_t(xr) * D + 32 * g;
+
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int nchunks = D / 64;
+  int c = wave;
+  Frag8 a[4], b[4];
+  if (c < nchunks) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[k].u = reinterpret_cast<const uint4*>(xp + c * 64)[k];
+      b[k].u = reinterpret_cast<const uint4*>(wp + c * 64)[k];
+    }
+  }
+  while (c < nchunks) {
+    const int cn = c + 4;
+    Frag8 an[4], bn[4];
+    if (cn < nchunks) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        an[k].u = reinterpret_cast<const uint4*>(xp + cn * 64)[k];
+        bn[k].u = reinterpret_cast<const uint4*>(wp + cn * 64)[k];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = mfma32(a[u].v, b[u].v, acc);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[k] = an[k];
+      b[k] = bn[k];
+    }
+    c = cn;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * g + (r & 3)][col] = acc[r];
+  __syncthreads();
+  for (int it = threadIdx.x; it < 32 * 16; it += 256) {
+    const int row = it >> 4;
+    const int j = it & 15;
+    float lo = 0.f, hi = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      lo += red[w][row][j];
+      hi += red[w][row][j + 16];
+    }
+    store_pair(s, p, m0 + row, pair_base + j, lo, hi, M, n_max, per_seq_rows);
+  }
+}
+
+// ------------------------------------------------------------- tiled GEMM --
+// Block (t, mt): rows 128 mt .. +128 and 64 rotary pairs of projection p.
+// Wave (wm, wn) computes rows wm*64 .. +64 and pairs wn*32 .. +32: its
+// n-subtile 0 holds their low features and n-subtile 1 their high features,
+// so each thread owns both halves of its pairs.
+constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;
+
+__global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const bf16_t* __restrict__ x, int M,
+                                                            int n_max, int per_seq_rows) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[TBM * TLD];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[TBN * TLD];
+  const int D = s.model_width;
+  const int dh = s.head_width;
+  const int half = dh >> 1;
+  const int tiles_per_proj = D / TBN;  // (D/2 pairs) / 64
+  const int p = blockIdx.x / tiles_per_proj;
+  const int pair_base = (blockIdx.x - p * tiles_per_proj) * 64;
+  const int m0 = blockIdx.y * TBM;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 5;
+  const int c32 = lane & 31;
+
+  // global -> LDS assignment: thread loads 64 contiguous bytes of row tid/2
+  const int lrow = tid >> 1;
+  const int lk = (tid & 1) * 32;
+  const bf16_t* ag = x + size_t(min(m0 + lrow, M - 1)) * D + lk;
+  const int v = lrow;  // virtual column of the B tile
+  const int vpair = pair_base + (v >> 6) * 32 + (v & 31);
+  const int vh = vpair / half;
+  const int vf = vpair - vh * half;
+  const int vrow = vh * dh + vf + (((v >> 5) & 1) ? half : 0);
+  const bf16_t* bg = weight_of(s, p) + size_t(vrow) * D + lk;
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  uint4 ra[4], rb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    ra[k] = reinterpret_cast<const uint4*>(ag)[k];
+    rb[k] = reinterpret_cast<const uint4*>(bg)[k];
+  }
+  const int ktiles = D / TBK;
+  for (int kt = 0; kt < ktiles; ++kt) {
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      *reinterpret_cast<uint4*>(&As[lrow * TLD + lk + 8 * k]) = ra[k];
+      *reinterpret_cast<uint4*>(&Bs[lrow * TLD + lk + 8 * k]) = rb[k];
+    }
+    __syncthreads();
+    if (kt + 1 < ktiles) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        ra[k] = reinterpret_cast<const uint4*>(ag + (kt + 1) * TBK)[k];
+        rb[k] = reinterpret_cast<const uint4*>(bg + (kt + 1) * TBK)[k];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TBK / 16; ++u) {
+      Frag8 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[i].u = *reinterpret_cast<const uint4*>(&As[(wm * 64 + i * 32 + c32) * TLD + 16 * u + 8 * g]);
+        fb[i].u = *reinterpret_cast<const uint4*>(&Bs[(wn * 64 + i * 32 + c32) * TLD + 16 * u + 8 * g]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fa[i].v, fb[j].v, acc[i][j]);
+    }
+  }
+  const int pair = pair_base + wn * 32 + c32;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      store_pair(s, p, m, pair, acc[i][0][r], acc[i][1][r], M, n_max, per_seq_rows);
+    }
+}
+
+// ---------------------------------------------------------- flash attention --
+// Block (qt, h, b): chunk queries 128 qt .. +128 of lane (b, h), 32 per wave.
+// Virtual key j < len is cache row j, else chunk row j - len; query i sees
+// j <= len + i.  Scores are formed transposed (S^T = K Q^T) so that a lane
+// holds every score of one query: the softmax scale factor is per lane, and
+// the probabilities are already in the operand layout of O^T += V^T P^T.
+template <int DH>
+__global__ __launch_bounds__(256) void attend_flash_kernel(DevState s, int n_max, int per_seq_rows,
+                                                           float* __restrict__ out) {
+  constexpr int KT = 64;
+  constexpr int LDK = DH + 8;
+  constexpr int DSTEPS = DH / 16;
+  constexpr int DTILES = DH / 32;
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[KT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[KT * LDK];
+  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int n_b = per_seq_rows ? s.rows[b] : n_max;
+  if (qt * 128 >= n_b) return;
+  const int C = s.capacity;
+  const int len = min(max(s.len[b], 0), C);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 5;
+  const int c32 = lane & 31;
+  const int qi = qt * 128 + wave * 32 + c32;
+  const int qi_eff = min(qi, n_b - 1);
+  const int limit = len + qi_eff;
+  const int i_max = min(qt * 128 + 127, n_b - 1);
+  const int total = len + i_max + 1;
+  const size_t lane_id = size_t(b) * s.heads + h;
+  const bf16_t* kc = static_cast<const bf16_t*>(s.keys) + lane_id * C * DH;
+  const bf16_t* vc = static_cast<const bf16_t*>(s.values) + lane_id * C * DH;
+  const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + lane_id * n_max * DH;
+  const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + lane_id * n_max * DH;
+
+  // B operand of S^T: lane holds q[qi][16 u + 8 g + e], rounded to bf16.
+  const float* qp = static_cast<const float*>(s.q) + (lane_id * n_max + qi_eff) * DH;
+  Frag8 qf[DSTEPS];
+#pragma unroll
+  for (int u = 0; u < DSTEPS; ++u) {
+    const float4 q0 = reinterpret_cast<const float4*>(qp + 16 * u + 8 * g)[0];
+    const float4 q1 = reinterpret_cast<const float4*>(qp + 16 * u + 8 * g)[1];
+    qf[u].h[0] = f32_to_bf16(q0.x);
+    qf[u].h[1] = f32_to_bf16(q0.y);
+    qf[u].h[2] = f32_to_bf16(q0.z);
+    qf[u].h[3] = f32_to_bf16(q0.w);
+    qf[u].h[4] = f32_to_bf16(q1.x);
+    qf[u].h[5] = f32_to_bf16(q1.y);
+    qf[u].h[6] = f32_to_bf16(q1.z);
+    qf[u].h[7] = f32_to_bf16(q1.w);
+  }
+  f32x16_t o[DTILES];
+#pragma unroll
+  for (int t = 0; t < DTILES; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = float(s.scale) * 1.4426950408889634f;
+
+  constexpr int CHUNKS = KT * DH / 8;  // 16-byte pieces per tile
+  for (int j0 = 0; j0 < total; j0 += KT) {
+    __syncthreads();
+#pragma unroll
+    for (int idx = threadIdx.x; idx < CHUNKS; idx += 256) {
+      const int row = idx / (DH / 8);
+      const int ch = idx - row * (DH / 8);
+      const int j = min(j0 + row, total - 1);
+      const bf16_t* kr = j < len ? kc + size_t(j) * DH : kn + size_t(j - len) * DH;
+      const bf16_t* vr = j < len ? vc + size_t(j) * DH : vn + size_t(j - len) * DH;
+      *reinterpret_cast<uint4*>(&Ks[row * LDK + ch * 8]) = reinterpret_cast<const uint4*>(kr)[ch];
+      *reinterpret_cast<uint4*>(&Vs[row * LDK + ch * 8]) = reinterpret_cast<const uint4*>(vr)[ch];
+    }
+    __syncthreads();
+
+    f32x16_t st[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
+#pragma unroll
+      for (int u = 0; u < DSTEPS; ++u) {
+        Frag8 a;
+        a.u = *reinterpret_cast<const uint4*>(&Ks[(kt * 32 + c32) * LDK + 16 * u + 8 * g]);
+        st[kt] = mfma32(a.v, qf[u].v, st[kt]);
+      }
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float v = key <= limit ? st[kt][r] * sl2 : -INFINITY;
+        st[kt][r] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float corr = exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = exp2f(st[kt][r] - m_new);
+        st[kt][r] = pr;
+        psum += pr;
+      }
+    psum += __shfl_xor(psum, 32, 64);
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < DTILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] *= corr;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        Frag8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb.h[e] = f32_to_bf16(st[kt][8 * u + e]);
+        const int kb = kt * 32 + 16 * u + 4 * g;
+#pragma unroll
+        for (int t = 0; t < DTILES; ++t) {
+          Frag8 a;
+          const int d = t * 32 + c32;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a.h[e] = Vs[(kb + (e < 4 ? e : e + 4)) * LDK + d];
+          o[t] = mfma32(a.v, pb.v, o[t]);
+        }
+      }
+  }
+  if (qi < n_b) {
+    const float inv = 1.f / l_run;
+    float* orow = out + (size_t(b) * n_max + qi) * s.model_width + size_t(h) * DH;
+#pragma unroll
+    for (int t = 0; t < DTILES; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float4 w;
+        w.x = o[t][4 * rr + 0] * inv;
+        w.y = o[t][4 * rr + 1] * inv;
+        w.z = o[t][4 * rr + 2] * inv;
+        w.w = o[t][4 * rr + 3] * inv;
+        const int d = t * 32 + 8 * rr + 4 * g;
+        *reinterpret_cast<float4*>(orow + d) = w;
+        if (!(isfinite(w.x) && isfinite(w.y) && isfinite(w.z) && isfinite(w.w)))
+          flag_min(&s.err->output, (size_t(b) * n_max + qi) * s.model_width + size_t(h) * DH + d);
+      }
+  }
+}
+
+inline hipStream_t st(void* p) { return static_cast<hipStream_t>(p); }
+
+}  // namespace
+
+// Returns -1 when the shape has no MFMA kernel (the caller then uses the
+// vector kernels), else 0 or a HIP error code.
+int mfma_project(const DevState& s, const void* x, int n_max, int per_seq_rows) {
+  if (s.dtype != KVC_BF16 || s.model_width % 128 != 0) return -1;
+  const int M = s.batch * n_max;
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  if (M <= 64) {
+    dim3 grid(3 * (s.model_width / 32), (M + 31) / 32);
+    hipLaunchKernelGGL(project_skinny_kernel, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+  } else {
+    dim3 grid(3 * (s.model_width / TBN), (M + TBM - 1) / TBM);
+    hipLaunchKernelGGL(project_tiled_kernel, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+  }
+  return int(hipGetLastError());
+}
+
+int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out) {
+  if (s.dtype != KVC_BF16) return -1;
+  dim3 grid((n_max + 127) / 128, s.heads, s.batch);
+  if (s.head_width == 128) {
+    hipLaunchKernelGGL(attend_flash_kernel<128>, grid, dim3(256), 0, st(s.stream), s, n_max, per_seq_rows,
+                       static_cast<float*>(out));
+  } else if (s.head_width == 64) {
+    hipLaunchKernelGGL(attend_flash_kernel<64>, grid, dim3(256), 0, st(s.stream), s, n_max, per_seq_rows,
+                       static_cast<float*>(out));
+  } else {
+    return -1;
+  }
+  return int(hipGetLastError());
+}
+
+}  // namespace kvc
