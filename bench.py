@@ -269,6 +269,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (5 times), to scale HBM byte counters")
     a = ap.parse_args()
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
@@ -277,6 +279,15 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
+    if a.calibrate_copy_mib:
+        n = a.calibrate_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_copy": n, "bytes_written_per_copy": n}))
+        return
     from incremental_kv_cache_amd import capi
     capi.lib()  # fails loudly if the HIP library is missing
     wl = WORKLOADS[a.workload]
