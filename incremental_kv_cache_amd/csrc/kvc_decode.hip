@@ -1,0 +1,247 @@
+// bf16 decode attention for gfx950: the HBM-bound core of the cached decode step.
+//
+// One new query per lane (b, h) reads all t_b = len_b + 1 rows: the len_b
+// retained rows of the cache plus the candidate row (Chapter 37, the
+// incremental-attention listing; "Count projection rows, not hardware time":
+// the newest query still reads every retained row).  The position axis is
+// split into 512-row tiles, one workgroup each, so a step has
+// sum_b ceil(t_b / 512) * H workgroups regardless of batch.
+//
+// Inside a workgroup a row is read by G = d_h / 8 lanes, one 16-byte load of
+// K and one of V per lane; a wave covers 64 / G rows per load and issues U
+// such row groups before using any of them, so each lane keeps 2 U loads in
+// flight.  q . k is reduced over the G lanes with DPP row operations.  The
+// softmax runs online in base 2 (q is pre-scaled by log2(e) / sqrt(d_h)), with
+// one rescale per U rows.  Row groups are combined through LDS; then each tile
+// either writes the output directly (a single-tile lane) or stores a partial
+// (max, sum, weighted values) and the last tile of the lane to finish -- found
+// with a device-scope counter that it resets -- merges the partials by
+// log-sum-exp into the lane's head block of the output (merge_heads).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kvc_dev_util.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+namespace {
+
+using namespace dev;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int moved = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+  return v + __builtin_bit_cast(float, moved);
+}
+
+// Sum over aligned groups of G lanes (G = 4, 8 or 16), result in every lane.
+template <int G>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  v = dpp_add<0xB1>(v);                     // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);                     // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) v = dpp_add<0x141>(v);   // row_half_mirror
+  if constexpr (G >= 16) v = dpp_add<0x140>(v);  // row_mirror
+  return v;
+}
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4& u, float (&f)[8]) {
+  f[0] = __uint_as_float(u.x << 16);
+  f[1] = __uint_as_float(u.x & 0xffff0000u);
+  f[2] = __uint_as_float(u.y << 16);
+  f[3] = __uint_as_float(u.y & 0xffff0000u);
+  f[4] = __uint_as_float(u.z << 16);
+  f[5] = __uint_as_float(u.z & 0xffff0000u);
+  f[6] = __uint_as_float(u.w << 16);
+  f[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+constexpr int kWaves = 4;
+
+template <int DH, int U>
+__global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevState s, float* __restrict__ out) {
+  constexpr int G = DH / 8;
+  constexpr int RPW = 64 / G;
+  constexpr int GROUPS = kWaves * RPW;
+  constexpr int STEP = GROUPS * U;
+  constexpr int TR = kDecodeTileRows;
+  static_assert(TR % STEP == 0, "tile must be a whole number of steps");
+  __shared__ float sm_m[GROUPS], sm_l[GROUPS];
+  __shared__ float sm_acc[GROUPS][DH + 4];
+  __shared__ int sm_last;
+
+  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int C = s.capacity;
+  const int len = min(max(s.len[b], 0), C - 1);
+  const int t = len + 1;
+  const int r0 = tile * TR;
+  if (r0 >= t) return;
+  const int r1 = min(t, r0 + TR);
+  const int ntiles = (t + TR - 1) / TR;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane % G;
+  const int grp = wave * RPW + lane / G;
+  const size_t lane_id = size_t(b) * s.heads + h;
+  const bf16_t* kc = static_cast<const bf16_t*>(s.keys) + lane_id * C * DH + g * 8;
+  const bf16_t* vc = static_cast<const bf16_t*>(s.values) + lane_id * C * DH + g * 8;
+  const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + lane_id * DH + g * 8;
+  const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + lane_id * DH + g * 8;
+
+  const float sl2 = float(s.scale) * 1.4426950408889634f;
+  float qv[8];
+  {
+    const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(s.q) + lane_id * DH + g * 8);
+    const float4 a = qp[0], c = qp[1];
+    qv[0] = a.x * sl2;
+    qv[1] = a.y * sl2;
+    qv[2] = a.z * sl2;
+    qv[3] = a.w * sl2;
+    qv[4] = c.x * sl2;
+    qv[5] = c.y * sl2;
+    qv[6] = c.z * sl2;
+    qv[7] = c.w * sl2;
+  }
+  float m = -INFINITY, l = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+
+  for (int base = r0; base < r1; base += STEP) {
+    uint4 kr[U], vr[U];
+    bool ok[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = base + u * GROUPS + grp;
+      ok[u] = r < r1;
+      const int rr = ok[u] ? r : r1 - 1;
+      const bf16_t* kp = rr < len ? kc + size_t(rr) * DH : kn;
+      const bf16_t* vp = rr < len ? vc + size_t(rr) * DH : vn;
+      kr[u] = *reinterpret_cast<const uint4*>(kp);
+      vr[u] = *reinterpret_cast<const uint4*>(vp);
+    }
+    float sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float kf[8];
+      unpack_bf16x8(kr[u], kf);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qv[e], kf[e], d);
+      sc[u] = d;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) sc[u] = group_sum_dpp<G>(sc[u]);
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      sc[u] = ok[u] ? sc[u] : -INFINITY;
+      mx = fmaxf(mx, sc[u]);
+    }
+    // a row group past the tile end sees only masked rows: keep its state at (-inf, 0, 0)
+    const float corr = mx == -INFINITY ? 1.f : exp2f(m - mx);
+    l *= corr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= corr;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = ok[u] ? exp2f(sc[u] - mx) : 0.f;
+      l += p;
+      float vf[8];
+      unpack_bf16x8(vr[u], vf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+    }
+    m = mx;
+  }
+
+  if (g == 0) {
+    sm_m[grp] = m;
+    sm_l[grp] = l;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sm_acc[grp][g * 8 + e] = acc[e];
+  __syncthreads();
+
+  const int j = threadIdx.x;  // output feature handled by this thread (j < DH)
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < GROUPS; ++k) M = fmaxf(M, sm_m[k]);
+  float L = 0.f, A = 0.f;
+#pragma unroll
+  for (int k = 0; k < GROUPS; ++k) {
+    const float w = exp2f(sm_m[k] - M);  // 0 for groups that saw no row
+    L += sm_l[k] * w;
+    if (j < DH) A += sm_acc[k][j] * w;
+  }
+  const size_t out_base = size_t(b) * s.model_width + size_t(h) * DH;
+  if (ntiles == 1) {
+    if (j < DH) {
+      const float o = A / L;
+      out[out_base + j] = o;
+      if (!isfinite(o)) flag_min(&s.err->output, out_base + j);
+    }
+    return;
+  }
+  float* part = static_cast<float*>(s.partials) + (lane_id * s.max_tiles + tile) * (DH + 2);
+  if (j < DH) part[2 + j] = A;
+  if (j == 0) {
+    part[0] = M;
+    part[1] = L;
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int done = atomicAdd(&s.counters[lane_id], 1);
+    sm_last = done == ntiles - 1;
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  __threadfence();
+  if (j < DH) {
+    const float* p0 = static_cast<const float*>(s.partials) + lane_id * s.max_tiles * (DH + 2);
+    float MM = -INFINITY;
+    for (int k = 0; k < ntiles; ++k) MM = fmaxf(MM, __builtin_nontemporal_load(p0 + k * (DH + 2)));
+    float LL = 0.f, AA = 0.f;
+    for (int k = 0; k < ntiles; ++k) {
+      const float* pk = p0 + k * (DH + 2);
+      const float w = exp2f(__builtin_nontemporal_load(pk) - MM);
+      LL += __builtin_nontemporal_load(pk + 1) * w;
+      AA += __builtin_nontemporal_load(pk + 2 + j) * w;
+    }
+    const float o = AA / LL;
+    out[out_base + j] = o;
+    if (!isfinite(o)) flag_min(&s.err->output, out_base + j);
+  }
+  if (threadIdx.x == 0) s.counters[lane_id] = 0;
+}
+
+inline hipStream_t st(void* p) { return static_cast<hipStream_t>(p); }
+
+}  // namespace
+
+// Fused split-K attention + merge for bf16 storage with d_h in {64, 128};
+// returns -1 for other shapes (the vector kernels then run).
+int fast_attend_decode(const DevState& s, void* out) {
+  if (s.dtype != KVC_BF16) return -1;
+  dim3 grid(s.max_tiles, s.heads, s.batch);
+  if (s.head_width == 128) {
+    hipLaunchKernelGGL((attend_decode_bf16_kernel<128, 4>), grid, dim3(64 * kWaves), 0, st(s.stream), s,
+                       static_cast<float*>(out));
+  } else if (s.head_width == 64) {
+    hipLaunchKernelGGL((attend_decode_bf16_kernel<64, 4>), grid, dim3(64 * kWaves), 0, st(s.stream), s,
+                       static_cast<float*>(out));
+  } else {
+    return -1;
+  }
+  return int(hipGetLastError());
+}
+
+bool fast_attend_decode_supported(const DevState& s) {
+  return s.dtype == KVC_BF16 && (s.head_width == 128 || s.head_width == 64);
+}
+
+}  // namespace kvc

@@ -310,6 +310,45 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max,
   }
 }
 
+// Decode commit in one launch: block b copies the H candidate rows of
+// sequence b into row len[b], records the position, then advances len[b] and
+// next_position[b]; no other block touches sequence b.
+template <typename T>
+__global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
+  if (any_error(s.err)) return;
+  const int b = blockIdx.x;
+  const int len = s.len[b];
+  const int C = s.capacity;
+  if (len < 0 || len + 1 > C) return;
+  const int dh = s.head_width;
+  const size_t row_bytes = size_t(dh) * sizeof(T);
+  for (int h = 0; h < s.heads; ++h) {
+    const size_t lane_id = size_t(b) * s.heads + h;
+    const char* sk = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_k) + lane_id * dh);
+    const char* sv = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_v) + lane_id * dh);
+    char* dk = reinterpret_cast<char*>(static_cast<T*>(s.keys) + (lane_id * C + len) * dh);
+    char* dv = reinterpret_cast<char*>(static_cast<T*>(s.values) + (lane_id * C + len) * dh);
+    if ((row_bytes & 15) == 0) {
+      for (size_t k = threadIdx.x; k < row_bytes / 16; k += blockDim.x) {
+        reinterpret_cast<uint4*>(dk)[k] = reinterpret_cast<const uint4*>(sk)[k];
+        reinterpret_cast<uint4*>(dv)[k] = reinterpret_cast<const uint4*>(sv)[k];
+      }
+    } else {
+      for (size_t k = threadIdx.x; k < size_t(dh); k += blockDim.x) {
+        reinterpret_cast<T*>(dk)[k] = reinterpret_cast<const T*>(sk)[k];
+        reinterpret_cast<T*>(dv)[k] = reinterpret_cast<const T*>(sv)[k];
+      }
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int np = s.next_pos[b];
+    s.positions[size_t(b) * C + len] = np;
+    s.len[b] = len + 1;
+    s.next_pos[b] = np + 1;
+  }
+}
+
 // Advances len[b] and next_position[b] by n_b (after every copy has read len[b]).
 __global__ __launch_bounds__(256) void commit_advance_kernel(DevState s, int n_max, int per_seq_rows) {
   if (any_error(s.err)) return;
@@ -428,6 +467,10 @@ int project_t(const DevState& s, const void* x, int n_max, int per_seq_rows) {
 
 template <typename T>
 int commit_t(const DevState& s, int n_max, int per_seq_rows) {
+  if (n_max == 1 && !per_seq_rows) {
+    hipLaunchKernelGGL((commit_decode_kernel<T>), dim3(s.batch), dim3(256), 0, st(s.stream), s);
+    return last_launch();
+  }
   hipLaunchKernelGGL((commit_copy_kernel<T>), dim3(s.heads, s.batch), dim3(256), 0, st(s.stream), s, n_max,
                      per_seq_rows);
   int rc = last_launch();
@@ -535,9 +578,19 @@ int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows) {
   return int(hipErrorInvalidValue);
 }
 
-int dev_attend_decode(const DevState& s) { return dispatch<AttendDecode>(s.dtype, s.head_width, s); }
+int fast_attend_decode(const DevState& s, void* out);
+bool fast_attend_decode_supported(const DevState& s);
 
-int dev_merge_decode(const DevState& s, void* out) { return dispatch<MergeDecode>(s.dtype, s.head_width, s, out); }
+int dev_attend_decode(const DevState& s, void* out) {
+  const int rc = fast_attend_decode(s, out);
+  if (rc >= 0) return rc;
+  return dispatch<AttendDecode>(s.dtype, s.head_width, s);
+}
+
+int dev_merge_decode(const DevState& s, void* out) {
+  if (fast_attend_decode_supported(s)) return 0;  // merged inside the attention kernel
+  return dispatch<MergeDecode>(s.dtype, s.head_width, s, out);
+}
 
 int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out) {
   const int rc = mfma_attend_chunk(s, n_max, per_seq_rows, out);

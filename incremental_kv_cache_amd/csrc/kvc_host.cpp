@@ -278,6 +278,7 @@ void free_cache(kvc_cache* c) {
   dev_free(c->ds.next_pos);
   dev_free(c->ds.positions);
   dev_free(c->ds.rows);
+  dev_free(c->ds.counters);
   dev_free(c->ds.cand_k);
   dev_free(c->ds.cand_v);
   dev_free(c->ds.q);
@@ -305,7 +306,7 @@ kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_row
   profile_mark(c, KVC_STAGE_PROJECT, 1);
   if (rc) return device_fail(rc, "projection launch");
   profile_mark(c, KVC_STAGE_ATTEND, 0);
-  rc = decode ? dev_attend_decode(s) : dev_attend_chunk(s, n_max, per_seq, out);
+  rc = decode ? dev_attend_decode(s, out) : dev_attend_chunk(s, n_max, per_seq, out);
   profile_mark(c, KVC_STAGE_ATTEND, 1);
   if (rc) return device_fail(rc, "attention launch");
   if (decode) {
@@ -528,6 +529,7 @@ kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capac
       {reinterpret_cast<void**>(&s.next_pos), round16(sizeof(int32_t) * batch)},
       {reinterpret_cast<void**>(&s.positions), round16(sizeof(int32_t) * size_t(pos_elems))},
       {reinterpret_cast<void**>(&s.rows), round16(sizeof(int32_t) * batch)},
+      {reinterpret_cast<void**>(&s.counters), round16(sizeof(int32_t) * size_t(batch) * H)},
       {&s.cand_k, round16(size_t(cand) * es)},
       {&s.cand_v, round16(size_t(cand) * es)},
       {&s.q, round16(size_t(cand) * as)},

@@ -24,7 +24,7 @@ struct ErrWords {
 constexpr unsigned long long kErrClear = ~0ull;
 
 // Attention rows per split-K work item of the decode kernel.
-constexpr int kDecodeTileRows = 256;
+constexpr int kDecodeTileRows = 512;
 // Values per by-value length update (kernel-argument payload).
 constexpr int kSetChunk = 480;
 
@@ -44,6 +44,7 @@ struct DevState {
   int32_t* next_pos;   // [B] position of the next row
   int32_t* positions;  // [B, C] absolute position of each row
   int32_t* rows;       // [B] rows of the current chunk call
+  int32_t* counters;   // [B * H] finished split-K tiles per lane (each call leaves them 0)
   void* cand_k;        // [B, H, n, d_h] storage type (n = rows of the call)
   void* cand_v;        // [B, H, n, d_h]
   void* q;             // [B, H, n, d_h] accumulate type
@@ -81,8 +82,8 @@ int dev_set_rows(const DevState& s, const int32_t* vals);
 // Pipeline stages.  n_max: rows per sequence of this call (1 for decode);
 // per_seq_rows: 0 = every sequence has n_max rows, 1 = rows[] holds them.
 int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows);
-int dev_attend_decode(const DevState& s);
-int dev_merge_decode(const DevState& s, void* out);
+int dev_attend_decode(const DevState& s, void* out);
+int dev_merge_decode(const DevState& s, void* out);  // no-op when dev_attend_decode merged already
 int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out);
 int dev_commit(const DevState& s, int n_max, int per_seq_rows);
 

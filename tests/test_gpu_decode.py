@@ -203,3 +203,10 @@ def test_async_decode_matches_sync():
         outs.append(torch.stack(res).cpu())
         assert K.kvc_lengths(cache)[0].tolist() == [8, 8]
     assert torch.equal(outs[0], outs[1])
+
+
+def test_split_tile_edges_bf16():
+    """Lengths at the 512-row split boundaries: t = 512 (one full tile), 513 (a second
+    tile holding only the candidate row), 1024, 1501 and 2049; three steps so the
+    per-lane tile counters are reused after resetting themselves."""
+    _decode_case("bf16", B=5, H=2, dh=128, lens=[511, 512, 1023, 1500, 2048], steps=3, seed=23)
