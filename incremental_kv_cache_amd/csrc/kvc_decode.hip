@@ -4,8 +4,8 @@
 // retained rows of the cache plus the candidate row (Chapter 37, the
 // incremental-attention listing; "Count projection rows, not hardware time":
 // the newest query still reads every retained row).  The position axis is
-// split into 512-row tiles, one workgroup each, so a step has
-// sum_b ceil(t_b / 512) * H workgroups regardless of batch.
+// split into tiles of 512 to 2048 rows (chosen per call for about 2048
+// workgroups), one workgroup each.
 //
 // Inside a workgroup a row is read by G = d_h / 8 lanes, one 16-byte load of
 // K and one of V per lane; a wave covers 64 / G rows per load and issues U
@@ -14,9 +14,10 @@
 // softmax runs online in base 2 (q is pre-scaled by log2(e) / sqrt(d_h)), with
 // one rescale per U rows.  Row groups are combined through LDS; then each tile
 // either writes the output directly (a single-tile lane) or stores a partial
-// (max, sum, weighted values) and the last tile of the lane to finish -- found
-// with a device-scope counter that it resets -- merges the partials by
-// log-sum-exp into the lane's head block of the output (merge_heads).
+// (max, sum, weighted values) that a second, small kernel merges by
+// log-sum-exp into the lane's head block of the output (merge_heads).  The
+// merge stays a separate launch: a device-wide release inside the attention
+// kernel would write back L2 once per workgroup on this multi-die part.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -60,22 +61,29 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float (&f)[8]) {
 
 constexpr int kWaves = 4;
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// K/V rows are read exactly once per step: non-temporal loads keep them from
+// displacing reusable lines and measurably raise the streaming rate.
+__device__ __forceinline__ uint4 load_stream(const bf16_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int DH, int U>
 __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevState s, float* __restrict__ out) {
   constexpr int G = DH / 8;
   constexpr int RPW = 64 / G;
   constexpr int GROUPS = kWaves * RPW;
   constexpr int STEP = GROUPS * U;
-  constexpr int TR = kDecodeTileRows;
-  static_assert(TR % STEP == 0, "tile must be a whole number of steps");
   __shared__ float sm_m[GROUPS], sm_l[GROUPS];
   __shared__ float sm_acc[GROUPS][DH + 4];
-  __shared__ int sm_last;
 
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int C = s.capacity;
   const int len = min(max(s.len[b], 0), C - 1);
   const int t = len + 1;
+  const int TR = s.tile_rows;
   const int r0 = tile * TR;
   if (r0 >= t) return;
   const int r1 = min(t, r0 + TR);
@@ -120,8 +128,8 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
       const int rr = ok[u] ? r : r1 - 1;
       const bf16_t* kp = rr < len ? kc + size_t(rr) * DH : kn;
       const bf16_t* vp = rr < len ? vc + size_t(rr) * DH : vn;
-      kr[u] = *reinterpret_cast<const uint4*>(kp);
-      vr[u] = *reinterpret_cast<const uint4*>(vp);
+      kr[u] = load_stream(kp);
+      vr[u] = load_stream(vp);
     }
     float sc[U];
 #pragma unroll
@@ -192,44 +200,62 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
     part[0] = M;
     part[1] = L;
   }
-  __threadfence();
+}
+
+// Log-sum-exp merge of a lane's tiles (lanes with one tile were written by the
+// attention kernel).  Block = one lane, DH threads: the maximum and the
+// weighted sum over tiles are block reductions, then thread j combines column j.
+template <int DH>
+__global__ __launch_bounds__(DH) void merge_decode_bf16_kernel(DevState s, float* __restrict__ out) {
+  __shared__ float red[DH];
+  const size_t lane_id = blockIdx.x;
+  const int b = int(lane_id / s.heads);
+  const int h = int(lane_id - size_t(b) * s.heads);
+  const int C = s.capacity;
+  const int len = min(max(s.len[b], 0), C - 1);
+  const int ntiles = (len + 1 + s.tile_rows - 1) / s.tile_rows;
+  if (ntiles == 1) return;
+  const int j = threadIdx.x;
+  const float* p0 = static_cast<const float*>(s.partials) + lane_id * s.max_tiles * (DH + 2);
+  float mx = -INFINITY;
+  for (int k = j; k < ntiles; k += DH) mx = fmaxf(mx, p0[k * (DH + 2)]);
+  red[j] = mx;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int done = atomicAdd(&s.counters[lane_id], 1);
-    sm_last = done == ntiles - 1;
+  for (int w = DH / 2; w > 0; w >>= 1) {
+    if (j < w) red[j] = fmaxf(red[j], red[j + w]);
+    __syncthreads();
   }
+  const float M = red[0];
   __syncthreads();
-  if (!sm_last) return;
-  __threadfence();
-  if (j < DH) {
-    const float* p0 = static_cast<const float*>(s.partials) + lane_id * s.max_tiles * (DH + 2);
-    float MM = -INFINITY;
-    for (int k = 0; k < ntiles; ++k) MM = fmaxf(MM, __builtin_nontemporal_load(p0 + k * (DH + 2)));
-    float LL = 0.f, AA = 0.f;
-    for (int k = 0; k < ntiles; ++k) {
-      const float* pk = p0 + k * (DH + 2);
-      const float w = exp2f(__builtin_nontemporal_load(pk) - MM);
-      LL += __builtin_nontemporal_load(pk + 1) * w;
-      AA += __builtin_nontemporal_load(pk + 2 + j) * w;
-    }
-    const float o = AA / LL;
-    out[out_base + j] = o;
-    if (!isfinite(o)) flag_min(&s.err->output, out_base + j);
+  float ls = 0.f;
+  for (int k = j; k < ntiles; k += DH) ls += p0[k * (DH + 2) + 1] * exp2f(p0[k * (DH + 2)] - M);
+  red[j] = ls;
+  __syncthreads();
+  for (int w = DH / 2; w > 0; w >>= 1) {
+    if (j < w) red[j] += red[j + w];
+    __syncthreads();
   }
-  if (threadIdx.x == 0) s.counters[lane_id] = 0;
+  const float L = red[0];
+  float A = 0.f;
+#pragma unroll 8
+  for (int k = 0; k < ntiles; ++k) A += p0[k * (DH + 2) + 2 + j] * exp2f(p0[k * (DH + 2)] - M);
+  const float o = A / L;
+  const size_t flat = size_t(b) * s.model_width + size_t(h) * DH + j;
+  out[flat] = o;
+  if (!isfinite(o)) flag_min(&s.err->output, flat);
 }
 
 inline hipStream_t st(void* p) { return static_cast<hipStream_t>(p); }
 
 }  // namespace
 
-// Fused split-K attention + merge for bf16 storage with d_h in {64, 128};
-// returns -1 for other shapes (the vector kernels then run).
+// Split-K attention for bf16 storage with d_h in {64, 128}; returns -1 for
+// other shapes (the vector kernels then run).
 int fast_attend_decode(const DevState& s, void* out) {
   if (s.dtype != KVC_BF16) return -1;
-  dim3 grid(s.max_tiles, s.heads, s.batch);
+  dim3 grid((s.capacity + s.tile_rows - 1) / s.tile_rows, s.heads, s.batch);
   if (s.head_width == 128) {
-    hipLaunchKernelGGL((attend_decode_bf16_kernel<128, 4>), grid, dim3(64 * kWaves), 0, st(s.stream), s,
+    hipLaunchKernelGGL((attend_decode_bf16_kernel<128, 8>), grid, dim3(64 * kWaves), 0, st(s.stream), s,
                        static_cast<float*>(out));
   } else if (s.head_width == 64) {
     hipLaunchKernelGGL((attend_decode_bf16_kernel<64, 4>), grid, dim3(64 * kWaves), 0, st(s.stream), s,
@@ -240,8 +266,19 @@ int fast_attend_decode(const DevState& s, void* out) {
   return int(hipGetLastError());
 }
 
-bool fast_attend_decode_supported(const DevState& s) {
-  return s.dtype == KVC_BF16 && (s.head_width == 128 || s.head_width == 64);
+int fast_merge_decode(const DevState& s, void* out) {
+  if (s.dtype != KVC_BF16) return -1;
+  const unsigned lanes = unsigned(s.batch) * unsigned(s.heads);
+  if (s.head_width == 128) {
+    hipLaunchKernelGGL(merge_decode_bf16_kernel<128>, dim3(lanes), dim3(128), 0, st(s.stream), s,
+                       static_cast<float*>(out));
+  } else if (s.head_width == 64) {
+    hipLaunchKernelGGL(merge_decode_bf16_kernel<64>, dim3(lanes), dim3(64), 0, st(s.stream), s,
+                       static_cast<float*>(out));
+  } else {
+    return -1;
+  }
+  return int(hipGetLastError());
 }
 
 }  // namespace kvc

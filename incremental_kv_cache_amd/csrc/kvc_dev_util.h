@@ -98,8 +98,11 @@ __device__ __forceinline__ bool any_error(const ErrWords* e) {
 // Operand layouts of the gfx950 bf16 MFMAs used here (checked on the device):
 //  32x32x16: A lane l = row l%32, k 8*(l/32)+e;  B lane l = k 8*(l/32)+e, col l%32;
 //            C register r = row 8*(r/4)+4*(l/32)+(r%4), col l%32.
+//  16x16x32: A lane l = row l%16, k 8*(l/16)+e;  B lane l = k 8*(l/16)+e, col l%16;
+//            C register r = row 4*(l/16)+r, col l%16.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 union Frag8 {
   uint4 u;

@@ -199,9 +199,9 @@ __global__ __launch_bounds__(64 * kAttendWaves) void attend_decode_kernel(DevSta
   const int C = s.capacity;
   const int len = min(max(s.len[b], 0), C - 1);
   const int t = len + 1;
-  const int r0 = tile * kDecodeTileRows;
+  const int r0 = tile * s.tile_rows;
   if (r0 >= t) return;
-  const int r1 = min(t, r0 + kDecodeTileRows);
+  const int r1 = min(t, r0 + s.tile_rows);
   const size_t lane_id = size_t(b) * s.heads + h;
   const T* kc = static_cast<const T*>(s.keys) + lane_id * C * DH;
   const T* vc = static_cast<const T*>(s.values) + lane_id * C * DH;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64) void merge_decode_kernel(DevState s, typename A
   const int h = blockIdx.x, b = blockIdx.y;
   const int C = s.capacity;
   const int len = min(max(s.len[b], 0), C - 1);
-  const int ntiles = (len + 1 + kDecodeTileRows - 1) / kDecodeTileRows;
+  const int ntiles = (len + 1 + s.tile_rows - 1) / s.tile_rows;
   const size_t lane_id = size_t(b) * s.heads + h;
   const A* part = static_cast<const A*>(s.partials) + lane_id * s.max_tiles * (DH + 2);
   A mx = -INFINITY;
@@ -322,22 +322,25 @@ __global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
   if (len < 0 || len + 1 > C) return;
   const int dh = s.head_width;
   const size_t row_bytes = size_t(dh) * sizeof(T);
-  for (int h = 0; h < s.heads; ++h) {
-    const size_t lane_id = size_t(b) * s.heads + h;
-    const char* sk = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_k) + lane_id * dh);
-    const char* sv = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_v) + lane_id * dh);
-    char* dk = reinterpret_cast<char*>(static_cast<T*>(s.keys) + (lane_id * C + len) * dh);
-    char* dv = reinterpret_cast<char*>(static_cast<T*>(s.values) + (lane_id * C + len) * dh);
-    if ((row_bytes & 15) == 0) {
-      for (size_t k = threadIdx.x; k < row_bytes / 16; k += blockDim.x) {
-        reinterpret_cast<uint4*>(dk)[k] = reinterpret_cast<const uint4*>(sk)[k];
-        reinterpret_cast<uint4*>(dv)[k] = reinterpret_cast<const uint4*>(sv)[k];
-      }
-    } else {
-      for (size_t k = threadIdx.x; k < size_t(dh); k += blockDim.x) {
-        reinterpret_cast<T*>(dk)[k] = reinterpret_cast<const T*>(sk)[k];
-        reinterpret_cast<T*>(dv)[k] = reinterpret_cast<const T*>(sv)[k];
-      }
+  const size_t seq_rows = size_t(b) * s.heads;
+  if ((row_bytes & 15) == 0) {
+    const int per_row = int(row_bytes / 16);
+    for (int idx = threadIdx.x; idx < s.heads * per_row; idx += blockDim.x) {
+      const int h = idx / per_row;
+      const int c = idx - h * per_row;
+      const size_t lane_id = seq_rows + h;
+      reinterpret_cast<uint4*>(static_cast<T*>(s.keys) + (lane_id * C + len) * dh)[c] =
+          reinterpret_cast<const uint4*>(static_cast<const T*>(s.cand_k) + lane_id * dh)[c];
+      reinterpret_cast<uint4*>(static_cast<T*>(s.values) + (lane_id * C + len) * dh)[c] =
+          reinterpret_cast<const uint4*>(static_cast<const T*>(s.cand_v) + lane_id * dh)[c];
+    }
+  } else {
+    for (int idx = threadIdx.x; idx < s.heads * dh; idx += blockDim.x) {
+      const int h = idx / dh;
+      const int c = idx - h * dh;
+      const size_t lane_id = seq_rows + h;
+      static_cast<T*>(s.keys)[(lane_id * C + len) * dh + c] = static_cast<const T*>(s.cand_k)[lane_id * dh + c];
+      static_cast<T*>(s.values)[(lane_id * C + len) * dh + c] = static_cast<const T*>(s.cand_v)[lane_id * dh + c];
     }
   }
   __syncthreads();
@@ -430,7 +433,7 @@ int dispatch(int dtype, int dh, Args&&... args) {
 template <typename T, int DH>
 struct AttendDecode {
   static int run(const DevState& s) {
-    dim3 grid(s.max_tiles, s.heads, s.batch);
+    dim3 grid((s.capacity + s.tile_rows - 1) / s.tile_rows, s.heads, s.batch);
     hipLaunchKernelGGL((attend_decode_kernel<T, DH>), grid, dim3(64 * kAttendWaves), 0, st(s.stream), s);
     return last_launch();
   }
@@ -579,7 +582,7 @@ int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows) {
 }
 
 int fast_attend_decode(const DevState& s, void* out);
-bool fast_attend_decode_supported(const DevState& s);
+int fast_merge_decode(const DevState& s, void* out);
 
 int dev_attend_decode(const DevState& s, void* out) {
   const int rc = fast_attend_decode(s, out);
@@ -588,7 +591,8 @@ int dev_attend_decode(const DevState& s, void* out) {
 }
 
 int dev_merge_decode(const DevState& s, void* out) {
-  if (fast_attend_decode_supported(s)) return 0;  // merged inside the attention kernel
+  const int rc = fast_merge_decode(s, out);
+  if (rc >= 0) return rc;
   return dispatch<MergeDecode>(s.dtype, s.head_width, s, out);
 }
 

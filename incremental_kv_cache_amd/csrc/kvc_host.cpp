@@ -278,7 +278,6 @@ void free_cache(kvc_cache* c) {
   dev_free(c->ds.next_pos);
   dev_free(c->ds.positions);
   dev_free(c->ds.rows);
-  dev_free(c->ds.counters);
   dev_free(c->ds.cand_k);
   dev_free(c->ds.cand_v);
   dev_free(c->ds.q);
@@ -517,6 +516,7 @@ kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capac
   s.wk = p->w[1];
   s.wv = p->w[2];
   s.max_tiles = max_tiles;
+  s.tile_rows = kDecodeTileRows;
   s.stream = hip_stream;
   c->storage_bytes = int64_t(round16(size_t(elements) * es));
   struct Alloc {
@@ -529,7 +529,6 @@ kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capac
       {reinterpret_cast<void**>(&s.next_pos), round16(sizeof(int32_t) * batch)},
       {reinterpret_cast<void**>(&s.positions), round16(sizeof(int32_t) * size_t(pos_elems))},
       {reinterpret_cast<void**>(&s.rows), round16(sizeof(int32_t) * batch)},
-      {reinterpret_cast<void**>(&s.counters), round16(sizeof(int32_t) * size_t(batch) * H)},
       {&s.cand_k, round16(size_t(cand) * es)},
       {&s.cand_v, round16(size_t(cand) * es)},
       {&s.q, round16(size_t(cand) * as)},
@@ -667,6 +666,12 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
     w.position_min = std::min(w.position_min, cache->next_pos[b]);
     w.position_max = std::max(w.position_max, cache->next_pos[b]);
   }
+  // Split-K tile: about 2048 workgroups over all lanes, at least one 512-row tile.
+  int64_t rows = 0;
+  for (int b = 0; b < cache->batch; ++b) rows += int64_t(cache->len[b] + 1) * cache->heads;
+  int tile = kDecodeTileRows;
+  while (tile < 4 * kDecodeTileRows && rows / tile > 2048) tile *= 2;
+  cache->ds.tile_rows = tile;
   st = run_call(cache, x, 1, nullptr, out, flags, true);
   if (st == KVC_OK && work) *work = w;
   return st;

@@ -23,7 +23,8 @@ struct ErrWords {
 };
 constexpr unsigned long long kErrClear = ~0ull;
 
-// Attention rows per split-K work item of the decode kernel.
+// Smallest number of attention rows per split-K work item of the decode
+// kernel (sizes the partial buffer); each call picks tile_rows >= this.
 constexpr int kDecodeTileRows = 512;
 // Values per by-value length update (kernel-argument payload).
 constexpr int kSetChunk = 480;
@@ -44,12 +45,12 @@ struct DevState {
   int32_t* next_pos;   // [B] position of the next row
   int32_t* positions;  // [B, C] absolute position of each row
   int32_t* rows;       // [B] rows of the current chunk call
-  int32_t* counters;   // [B * H] finished split-K tiles per lane (each call leaves them 0)
   void* cand_k;        // [B, H, n, d_h] storage type (n = rows of the call)
   void* cand_v;        // [B, H, n, d_h]
   void* q;             // [B, H, n, d_h] accumulate type
   void* partials;      // [B, H, max_tiles, d_h + 2] accumulate type
-  int max_tiles;
+  int max_tiles;       // ceil(C / kDecodeTileRows)
+  int tile_rows;       // split-K tile of the current decode call (multiple of kDecodeTileRows)
   void* rope_cos;  // [max_positions, d_h / 2] accumulate type (null without rotation)
   void* rope_sin;
   ErrWords* err;
@@ -83,7 +84,7 @@ int dev_set_rows(const DevState& s, const int32_t* vals);
 // per_seq_rows: 0 = every sequence has n_max rows, 1 = rows[] holds them.
 int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows);
 int dev_attend_decode(const DevState& s, void* out);
-int dev_merge_decode(const DevState& s, void* out);  // no-op when dev_attend_decode merged already
+int dev_merge_decode(const DevState& s, void* out);
 int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out);
 int dev_commit(const DevState& s, int n_max, int per_seq_rows);
 

@@ -2,9 +2,9 @@
 //
 //  * project_skinny : the new rows (decode: M = B rows) through W_q, W_k, W_v.
 //                     A [M, D] x [D, 3D] contraction whose time is the weight
-//                     read from HBM; a workgroup owns a 32-row x 16-pair output
-//                     tile and its four waves split the reduction axis, each
-//                     streaming whole 128-byte lines of weight rows.
+//                     read from HBM; a workgroup owns a 32-row x 32-pair output
+//                     tile, streams its 64 weight rows once and shares each
+//                     input chunk between its four waves through LDS.
 //  * project_tiled  : the same contraction for many rows (chunks, prefill):
 //                     128 x 128 tiles staged through LDS, 2 x 2 waves.
 //  * attend_flash   : causal chunk attention (prefix-reuse note: suffix row i
@@ -78,79 +78,102 @@ __device__ __forceinline__ void store_pair(const DevState& s, int p, int m, int 
 }
 
 // ------------------------------------------------------------ skinny GEMM --
-// Block (t, mt): rows m0 = 32 mt .. +32, pairs 16 (t mod D/32) .. +16 of
-// projection p = t / (D/32).  Output column j < 16 is the low feature of pair
-// j, column j >= 16 the high feature of pair j - 16.  Wave w reduces the
-// 64-wide k chunks c = w, w + 4, ...; lane l reads 64 contiguous bytes of its
-// weight row (and of its input row) per chunk, with k-slot (8 (l/32) + e) of
-// MFMA step u holding element k = 64 c + 32 (l/32) + 8 u + e on both operands.
+// Block (t, mt): rows 32 mt .. +32 and 32 rotary pairs of projection
+// p = t / (D/64).  Wave w owns 8 pairs: output column j < 8 of its 16 is the
+// low feature of pair j, column j + 8 the high one.  Every wave runs the whole
+// reduction axis over its 16 weight rows (16x16x32 MFMA, lane (c, g) reading
+// 16 bytes at k = 128 c' + 32 u + 8 g of chunk c'); the 32 x 128 input chunk
+// is loaded once per block into a double-buffered LDS tile and shared by the
+// four waves, which is what keeps the small activation matrix from being
+// re-read from L2 by every column tile.
+constexpr int SKC = 128;           // k per chunk
+constexpr int SLDX = SKC + 8;      // LDS row stride (bf16) of the input tile
+constexpr int SUNROLL = 8;         // chunks per statically unrolled group
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const bf16_t* __restrict__ x, int M,
                                                              int n_max, int per_seq_rows) {
-  __shared__ float red[4][32][33];
+  __shared__ __attribute__((aligned(16))) bf16_t Xs[2][32 * SLDX];
   const int D = s.model_width;
   const int half = s.head_width >> 1;
-  const int tiles_per_proj = D / 32;
+  const int tiles_per_proj = D / 64;
   const int p = blockIdx.x / tiles_per_proj;
-  const int pair_base = (blockIdx.x - p * tiles_per_proj) * 16;
+  const int pair_base = (blockIdx.x - p * tiles_per_proj) * 32;
   const int m0 = blockIdx.y * 32;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane >> 5;
-  const int col = lane & 31;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g4 = lane >> 4;
+  const int c16 = lane & 15;
 
-  const int pair = pair_base + (col & 15);
+  const int pair = pair_base + wave * 8 + (c16 & 7);
   const int h = pair / half;
   const int f = pair - h * half;
-  const int wrow = h * s.head_width + f + ((col >> 4) ? half : 0);
-  const bf16_t* wp = weight_of(s, p) + size_t(wrow) * D + 32 * g;
-  const int xr = min(m0 + col, M - 1);
-  const bf16_t* xp = x + size_t(xr) * D + 32 * g;
+  const int wrow = h * s.head_width + f + ((c16 >> 3) ? half : 0);
+  const bf16_t* wp = weight_of(s, p) + size_t(wrow) * D + 8 * g4;
+  // input staging: thread copies 32 bytes of row tid/8
+  const int xrow = tid >> 3;
+  const int xseg = (tid & 7) * 16;
+  const bf16_t* xg = x + size_t(min(m0 + xrow, M - 1)) * D + xseg;
 
-  f32x16_t acc;
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int nch = D / SKC;
+  Frag8 b[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  const int nchunks = D / 64;
-  int c = wave;
-  Frag8 a[4], b[4];
-  if (c < nchunks) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      a[k].u = reinterpret_cast<const uint4*>(xp + c * 64)[k];
-      b[k].u = reinterpret_cast<const uint4*>(wp + c * 64)[k];
-    }
-  }
-  while (c < nchunks) {
-    const int cn = c + 4;
-    Frag8 an[4], bn[4];
-    if (cn < nchunks) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        an[k].u = reinterpret_cast<const uint4*>(xp + cn * 64)[k];
-        bn[k].u = reinterpret_cast<const uint4*>(wp + cn * 64)[k];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc = mfma32(a[u].v, b[u].v, acc);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      a[k] = an[k];
-      b[k] = bn[k];
-    }
-    c = cn;
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) red[wave][8 * (r >> 2) + 4 * g + (r & 3)][col] = acc[r];
+  for (int u = 0; u < 4; ++u) b[u].u = *reinterpret_cast<const uint4*>(wp + 32 * u);
+  uint4 xr0 = reinterpret_cast<const uint4*>(xg)[0];
+  uint4 xr1 = reinterpret_cast<const uint4*>(xg)[1];
+  *reinterpret_cast<uint4*>(&Xs[0][xrow * SLDX + xseg]) = xr0;
+  *reinterpret_cast<uint4*>(&Xs[0][xrow * SLDX + xseg + 8]) = xr1;
   __syncthreads();
-  for (int it = threadIdx.x; it < 32 * 16; it += 256) {
-    const int row = it >> 4;
-    const int j = it & 15;
-    float lo = 0.f, hi = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      lo += red[w][row][j];
-      hi += red[w][row][j + 16];
+
+  // one chunk: prefetch next input chunk and next weight fragments, multiply, publish
+  auto step = [&](int c, int buf) {
+    const bool more = c + 1 < nch;
+    if (more) {
+      xr0 = reinterpret_cast<const uint4*>(xg + (c + 1) * SKC)[0];
+      xr1 = reinterpret_cast<const uint4*>(xg + (c + 1) * SKC)[1];
     }
-    store_pair(s, p, m0 + row, pair_base + j, lo, hi, M, n_max, per_seq_rows);
+    Frag8 bn[4];
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) bn[u].u = *reinterpret_cast<const uint4*>(wp + (c + 1) * SKC + 32 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      Frag8 a0, a1;
+      a0.u = *reinterpret_cast<const uint4*>(&Xs[buf][c16 * SLDX + 32 * u + 8 * g4]);
+      a1.u = *reinterpret_cast<const uint4*>(&Xs[buf][(16 + c16) * SLDX + 32 * u + 8 * g4]);
+      acc0 = mfma16(a0.v, b[u].v, acc0);
+      acc1 = mfma16(a1.v, b[u].v, acc1);
+    }
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) b[u] = bn[u];
+      *reinterpret_cast<uint4*>(&Xs[buf ^ 1][xrow * SLDX + xseg]) = xr0;
+      *reinterpret_cast<uint4*>(&Xs[buf ^ 1][xrow * SLDX + xseg + 8]) = xr1;
+    }
+    __syncthreads();
+  };
+  int c = 0;
+  for (; c + SUNROLL <= nch; c += SUNROLL) {
+#pragma unroll
+    for (int k = 0; k < SUNROLL; ++k) step(c + k, k & 1);
+  }
+  for (; c < nch; ++c) step(c, c & 1);
+
+  // pairs: lanes with column j < 8 take the high feature from lane + 8
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float hi0 = __shfl_xor(acc0[r], 8, 64);
+    const float hi1 = __shfl_xor(acc1[r], 8, 64);
+    if (c16 < 8) {
+      store_pair(s, p, m0 + 4 * g4 + r, pair, acc0[r], hi0, M, n_max, per_seq_rows);
+      store_pair(s, p, m0 + 16 + 4 * g4 + r, pair, acc1[r], hi1, M, n_max, per_seq_rows);
+    }
   }
 }
 
@@ -408,7 +431,7 @@ int mfma_project(const DevState& s, const void* x, int n_max, int per_seq_rows) 
   const int M = s.batch * n_max;
   const bf16_t* xb = static_cast<const bf16_t*>(x);
   if (M <= 64) {
-    dim3 grid(3 * (s.model_width / 32), (M + 31) / 32);
+    dim3 grid(3 * (s.model_width / 64), (M + 31) / 32);
     hipLaunchKernelGGL(project_skinny_kernel, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
   } else {
     dim3 grid(3 * (s.model_width / TBN), (M + TBM - 1) / TBM);
