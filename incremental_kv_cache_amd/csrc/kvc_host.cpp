@@ -666,11 +666,21 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
     w.position_min = std::min(w.position_min, cache->next_pos[b]);
     w.position_max = std::max(w.position_max, cache->next_pos[b]);
   }
-  // Split-K tile: about 2048 workgroups over all lanes, at least one 512-row tile.
-  int64_t rows = 0;
-  for (int b = 0; b < cache->batch; ++b) rows += int64_t(cache->len[b] + 1) * cache->heads;
+  // Split-K tile: the largest of 2048/1024/512 rows that still gives at least
+  // 2048 workgroups with at least 90% of their rows in use (ragged lengths
+  // otherwise leave a few long tiles running alone at the end).
   int tile = kDecodeTileRows;
-  while (tile < 4 * kDecodeTileRows && rows / tile > 2048) tile *= 2;
+  for (int cand = 4 * kDecodeTileRows; cand > kDecodeTileRows; cand /= 2) {
+    int64_t blocks = 0, rows = 0;
+    for (int b = 0; b < cache->batch; ++b) {
+      blocks += (int64_t(cache->len[b]) + cand) / cand;
+      rows += int64_t(cache->len[b]) + 1;
+    }
+    if (blocks * cache->heads >= 2048 && rows * 10 >= blocks * int64_t(cand) * 9) {
+      tile = cand;
+      break;
+    }
+  }
   cache->ds.tile_rows = tile;
   st = run_call(cache, x, 1, nullptr, out, flags, true);
   if (st == KVC_OK && work) *work = w;

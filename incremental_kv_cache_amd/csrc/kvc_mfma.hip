@@ -94,6 +94,8 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// NCH > 0: the reduction axis has exactly NCH chunks (fully unrolled); 0: any D.
+template <int NCH>
 __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const bf16_t* __restrict__ x, int M,
                                                              int n_max, int per_seq_rows) {
   __shared__ __attribute__((aligned(16))) bf16_t Xs[2][32 * SLDX];
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const b
   const bf16_t* xg = x + size_t(min(m0 + xrow, M - 1)) * D + xseg;
 
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int nch = D / SKC;
+  const int nch = NCH > 0 ? NCH : D / SKC;
   Frag8 b[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) b[u].u = *reinterpret_cast<const uint4*>(wp + 32 * u);
@@ -130,17 +132,13 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const b
   *reinterpret_cast<uint4*>(&Xs[0][xrow * SLDX + xseg + 8]) = xr1;
   __syncthreads();
 
-  // one chunk: prefetch next input chunk and next weight fragments, multiply, publish
+  // one chunk: start loading the next input chunk, multiply this one, then start
+  // the next weight fragments and publish the input chunk for the next step
   auto step = [&](int c, int buf) {
     const bool more = c + 1 < nch;
     if (more) {
       xr0 = reinterpret_cast<const uint4*>(xg + (c + 1) * SKC)[0];
       xr1 = reinterpret_cast<const uint4*>(xg + (c + 1) * SKC)[1];
-    }
-    Frag8 bn[4];
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) bn[u].u = *reinterpret_cast<const uint4*>(wp + (c + 1) * SKC + 32 * u);
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -152,18 +150,23 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const b
     }
     if (more) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) b[u] = bn[u];
+      for (int u = 0; u < 4; ++u) b[u].u = *reinterpret_cast<const uint4*>(wp + (c + 1) * SKC + 32 * u);
       *reinterpret_cast<uint4*>(&Xs[buf ^ 1][xrow * SLDX + xseg]) = xr0;
       *reinterpret_cast<uint4*>(&Xs[buf ^ 1][xrow * SLDX + xseg + 8]) = xr1;
     }
     __syncthreads();
   };
-  int c = 0;
-  for (; c + SUNROLL <= nch; c += SUNROLL) {
+  if constexpr (NCH > 0) {
 #pragma unroll
-    for (int k = 0; k < SUNROLL; ++k) step(c + k, k & 1);
+    for (int c = 0; c < NCH; ++c) step(c, c & 1);
+  } else {
+    int c = 0;
+    for (; c + SUNROLL <= nch; c += SUNROLL) {
+#pragma unroll
+      for (int k = 0; k < SUNROLL; ++k) step(c + k, k & 1);
+    }
+    for (; c < nch; ++c) step(c, c & 1);
   }
-  for (; c < nch; ++c) step(c, c & 1);
 
   // pairs: lanes with column j < 8 take the high feature from lane + 8
 #pragma unroll
@@ -432,7 +435,19 @@ int mfma_project(const DevState& s, const void* x, int n_max, int per_seq_rows) 
   const bf16_t* xb = static_cast<const bf16_t*>(x);
   if (M <= 64) {
     dim3 grid(3 * (s.model_width / 64), (M + 31) / 32);
-    hipLaunchKernelGGL(project_skinny_kernel, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+    switch (s.model_width) {
+      case 2048:
+        hipLaunchKernelGGL(project_skinny_kernel<16>, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+        break;
+      case 4096:
+        hipLaunchKernelGGL(project_skinny_kernel<32>, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+        break;
+      case 8192:
+        hipLaunchKernelGGL(project_skinny_kernel<64>, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+        break;
+      default:
+        hipLaunchKernelGGL(project_skinny_kernel<0>, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+    }
   } else {
     dim3 grid(3 * (s.model_width / TBN), (M + TBM - 1) / TBM);
     hipLaunchKernelGGL(project_tiled_kernel, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
