@@ -666,20 +666,18 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
     w.position_min = std::min(w.position_min, cache->next_pos[b]);
     w.position_max = std::max(w.position_max, cache->next_pos[b]);
   }
-  // Split-K tile: the largest of 2048/1024/512 rows that still gives at least
-  // 2048 workgroups with at least 90% of their rows in use (ragged lengths
-  // otherwise leave a few long tiles running alone at the end).
+  // Split-K tile: the largest power-of-two multiple of 512 rows that still
+  // gives at least 1024 workgroups (four per compute unit); measured on the
+  // bench workloads, fewer and longer tiles stream faster than a finer split.
   int tile = kDecodeTileRows;
-  for (int cand = 4 * kDecodeTileRows; cand > kDecodeTileRows; cand /= 2) {
-    int64_t blocks = 0, rows = 0;
-    for (int b = 0; b < cache->batch; ++b) {
-      blocks += (int64_t(cache->len[b]) + cand) / cand;
-      rows += int64_t(cache->len[b]) + 1;
-    }
-    if (blocks * cache->heads >= 2048 && rows * 10 >= blocks * int64_t(cand) * 9) {
-      tile = cand;
-      break;
-    }
+  int max_len = 0;
+  for (int b = 0; b < cache->batch; ++b) max_len = std::max(max_len, cache->len[b]);
+  for (int64_t cand = kDecodeTileRows; cand <= (int64_t(1) << 30); cand *= 2) {
+    int64_t blocks = 0;
+    for (int b = 0; b < cache->batch; ++b) blocks += (int64_t(cache->len[b]) + cand) / cand;
+    if (blocks * cache->heads < 1024) break;
+    tile = int(cand);
+    if (cand > max_len) break;
   }
   cache->ds.tile_rows = tile;
   st = run_call(cache, x, 1, nullptr, out, flags, true);
