@@ -224,28 +224,37 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const bf
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 ra[4], rb[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    ra[k] = reinterpret_cast<const uint4*>(ag)[k];
-    rb[k] = reinterpret_cast<const uint4*>(bg)[k];
-  }
+  // register prefetch of the next K tile: 64 bytes of A and of B per thread,
+  // kept in named registers (an indexed array here ends up in scratch memory)
+  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
+  auto fetch = [&](int kt) {
+    const uint4* a4 = reinterpret_cast<const uint4*>(ag + kt * TBK);
+    const uint4* b4 = reinterpret_cast<const uint4*>(bg + kt * TBK);
+    ra0 = a4[0];
+    ra1 = a4[1];
+    ra2 = a4[2];
+    ra3 = a4[3];
+    rb0 = b4[0];
+    rb1 = b4[1];
+    rb2 = b4[2];
+    rb3 = b4[3];
+  };
+  fetch(0);
   const int ktiles = D / TBK;
   for (int kt = 0; kt < ktiles; ++kt) {
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      *reinterpret_cast<uint4*>(&As[lrow * TLD + lk + 8 * k]) = ra[k];
-      *reinterpret_cast<uint4*>(&Bs[lrow * TLD + lk + 8 * k]) = rb[k];
-    }
+    uint4* as = reinterpret_cast<uint4*>(&As[lrow * TLD + lk]);
+    uint4* bs = reinterpret_cast<uint4*>(&Bs[lrow * TLD + lk]);
+    as[0] = ra0;
+    as[1] = ra1;
+    as[2] = ra2;
+    as[3] = ra3;
+    bs[0] = rb0;
+    bs[1] = rb1;
+    bs[2] = rb2;
+    bs[3] = rb3;
     __syncthreads();
-    if (kt + 1 < ktiles) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        ra[k] = reinterpret_cast<const uint4*>(ag + (kt + 1) * TBK)[k];
-        rb[k] = reinterpret_cast<const uint4*>(bg + (kt + 1) * TBK)[k];
-      }
-    }
+    if (kt + 1 < ktiles) fetch(kt + 1);
 #pragma unroll
     for (int u = 0; u < TBK / 16; ++u) {
       Frag8 fa[2], fb[2];
