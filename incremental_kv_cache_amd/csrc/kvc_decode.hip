@@ -268,6 +268,7 @@ int fast_attend_decode(const DevState& s, void* out) {
 
 int fast_merge_decode(const DevState& s, void* out) {
   if (s.dtype != KVC_BF16) return -1;
+  if (s.single_tile && (s.head_width == 128 || s.head_width == 64)) return 0;  // outputs already written
   const unsigned lanes = unsigned(s.batch) * unsigned(s.heads);
   if (s.head_width == 128) {
     hipLaunchKernelGGL(merge_decode_bf16_kernel<128>, dim3(lanes), dim3(128), 0, st(s.stream), s,

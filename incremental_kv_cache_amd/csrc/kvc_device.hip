@@ -275,22 +275,26 @@ __global__ __launch_bounds__(64 * kAttendWaves) void attend_chunk_kernel(DevStat
 
 // --------------------------------------------------------------- commit ----
 
-// Copies the candidate rows of lane (b, h) into rows len[b] .. len[b]+n_b-1.
+// Copies candidate rows 64 r .. 64 r + 63 of lane (b, h) (block (r, h, b)) into
+// rows len[b] + i of the cache.
+constexpr int kCommitRows = 64;
+
 template <typename T>
 __global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max, int per_seq_rows) {
   if (any_error(s.err)) return;
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int r0 = blockIdx.x * kCommitRows, h = blockIdx.y, b = blockIdx.z;
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
   const int len = s.len[b];
   const int C = s.capacity;
-  if (n_b <= 0 || len < 0 || len + n_b > C) return;
+  if (r0 >= n_b || len < 0 || len + n_b > C) return;
+  const int nr = min(kCommitRows, n_b - r0);
   const int dh = s.head_width;
   const size_t lane_id = size_t(b) * s.heads + h;
-  const size_t bytes = size_t(n_b) * dh * sizeof(T);
-  const char* sk = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_k) + lane_id * n_max * dh);
-  const char* sv = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_v) + lane_id * n_max * dh);
-  char* dk = reinterpret_cast<char*>(static_cast<T*>(s.keys) + (lane_id * C + len) * dh);
-  char* dv = reinterpret_cast<char*>(static_cast<T*>(s.values) + (lane_id * C + len) * dh);
+  const size_t bytes = size_t(nr) * dh * sizeof(T);
+  const char* sk = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_k) + (lane_id * n_max + r0) * dh);
+  const char* sv = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_v) + (lane_id * n_max + r0) * dh);
+  char* dk = reinterpret_cast<char*>(static_cast<T*>(s.keys) + (lane_id * C + len + r0) * dh);
+  char* dv = reinterpret_cast<char*>(static_cast<T*>(s.values) + (lane_id * C + len + r0) * dh);
   if ((bytes & 15) == 0 && ((reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(sk)) & 15) == 0) {
     const size_t n16 = bytes / 16;
     for (size_t k = threadIdx.x; k < n16; k += blockDim.x) {
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max,
   }
   if (h == 0) {
     const int np = s.next_pos[b];
-    for (int k = threadIdx.x; k < n_b; k += blockDim.x) s.positions[size_t(b) * C + len + k] = np + k;
+    for (int k = threadIdx.x; k < nr; k += blockDim.x) s.positions[size_t(b) * C + len + r0 + k] = np + r0 + k;
   }
 }
 
@@ -474,8 +478,8 @@ int commit_t(const DevState& s, int n_max, int per_seq_rows) {
     hipLaunchKernelGGL((commit_decode_kernel<T>), dim3(s.batch), dim3(256), 0, st(s.stream), s);
     return last_launch();
   }
-  hipLaunchKernelGGL((commit_copy_kernel<T>), dim3(s.heads, s.batch), dim3(256), 0, st(s.stream), s, n_max,
-                     per_seq_rows);
+  hipLaunchKernelGGL((commit_copy_kernel<T>), dim3((n_max + kCommitRows - 1) / kCommitRows, s.heads, s.batch),
+                     dim3(256), 0, st(s.stream), s, n_max, per_seq_rows);
   int rc = last_launch();
   if (rc) return rc;
   hipLaunchKernelGGL(commit_advance_kernel, dim3((s.batch + 255) / 256), dim3(256), 0, st(s.stream), s, n_max,

@@ -680,6 +680,7 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
     if (cand > max_len) break;
   }
   cache->ds.tile_rows = tile;
+  cache->ds.single_tile = tile > max_len;
   st = run_call(cache, x, 1, nullptr, out, flags, true);
   if (st == KVC_OK && work) *work = w;
   return st;

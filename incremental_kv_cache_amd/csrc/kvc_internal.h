@@ -51,6 +51,7 @@ struct DevState {
   void* partials;      // [B, H, max_tiles, d_h + 2] accumulate type
   int max_tiles;       // ceil(C / kDecodeTileRows)
   int tile_rows;       // split-K tile of the current decode call (multiple of kDecodeTileRows)
+  int single_tile;     // 1 when every lane of the current decode call fits one tile
   void* rope_cos;  // [max_positions, d_h / 2] accumulate type (null without rotation)
   void* rope_sin;
   ErrWords* err;

@@ -286,14 +286,15 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const bf
 // holds every score of one query: the softmax scale factor is per lane, and
 // the probabilities are already in the operand layout of O^T += V^T P^T.
 template <int DH>
-__global__ __launch_bounds__(256) void attend_flash_kernel(DevState s, int n_max, int per_seq_rows,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_flash_kernel(DevState s, int n_max, int per_seq_rows,
                                                            float* __restrict__ out) {
   constexpr int KT = 64;
   constexpr int LDK = DH + 8;
+  constexpr int LDV = KT + 8;  // V^T row stride: V is stored transposed, [d][key]
   constexpr int DSTEPS = DH / 16;
   constexpr int DTILES = DH / 32;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[KT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[KT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[DH * LDV];
   const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
   if (qt * 128 >= n_b) return;
@@ -314,21 +315,23 @@ __global__ __launch_bounds__(256) void attend_flash_kernel(DevState s, int n_max
   const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + lane_id * n_max * DH;
   const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + lane_id * n_max * DH;
 
-  // B operand of S^T: lane holds q[qi][16 u + 8 g + e], rounded to bf16.
+  // B operand of S^T: lane holds q[qi][16 u + 8 g + e] * scale * log2(e), rounded
+  // to bf16, so scores come out of the MFMA already in base-2 softmax units.
+  const float sl2 = float(s.scale) * 1.4426950408889634f;
   const float* qp = static_cast<const float*>(s.q) + (lane_id * n_max + qi_eff) * DH;
   Frag8 qf[DSTEPS];
 #pragma unroll
   for (int u = 0; u < DSTEPS; ++u) {
     const float4 q0 = reinterpret_cast<const float4*>(qp + 16 * u + 8 * g)[0];
     const float4 q1 = reinterpret_cast<const float4*>(qp + 16 * u + 8 * g)[1];
-    qf[u].h[0] = f32_to_bf16(q0.x);
-    qf[u].h[1] = f32_to_bf16(q0.y);
-    qf[u].h[2] = f32_to_bf16(q0.z);
-    qf[u].h[3] = f32_to_bf16(q0.w);
-    qf[u].h[4] = f32_to_bf16(q1.x);
-    qf[u].h[5] = f32_to_bf16(q1.y);
-    qf[u].h[6] = f32_to_bf16(q1.z);
-    qf[u].h[7] = f32_to_bf16(q1.w);
+    qf[u].v[0] = (__bf16)(q0.x * sl2);
+    qf[u].v[1] = (__bf16)(q0.y * sl2);
+    qf[u].v[2] = (__bf16)(q0.z * sl2);
+    qf[u].v[3] = (__bf16)(q0.w * sl2);
+    qf[u].v[4] = (__bf16)(q1.x * sl2);
+    qf[u].v[5] = (__bf16)(q1.y * sl2);
+    qf[u].v[6] = (__bf16)(q1.z * sl2);
+    qf[u].v[7] = (__bf16)(q1.w * sl2);
   }
   f32x16_t o[DTILES];
 #pragma unroll
@@ -336,20 +339,23 @@ __global__ __launch_bounds__(256) void attend_flash_kernel(DevState s, int n_max
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = float(s.scale) * 1.4426950408889634f;
+  const int wave_limit_min = len + min(qt * 128 + wave * 32, n_b - 1);  // smallest limit in the wave
 
   constexpr int CHUNKS = KT * DH / 8;  // 16-byte pieces per tile
   for (int j0 = 0; j0 < total; j0 += KT) {
     __syncthreads();
 #pragma unroll
     for (int idx = threadIdx.x; idx < CHUNKS; idx += 256) {
-      const int row = idx / (DH / 8);
-      const int ch = idx - row * (DH / 8);
+      const int row = idx % KT;  // consecutive threads take consecutive keys of one chunk
+      const int ch = idx / KT;
       const int j = min(j0 + row, total - 1);
       const bf16_t* kr = j < len ? kc + size_t(j) * DH : kn + size_t(j - len) * DH;
       const bf16_t* vr = j < len ? vc + size_t(j) * DH : vn + size_t(j - len) * DH;
       *reinterpret_cast<uint4*>(&Ks[row * LDK + ch * 8]) = reinterpret_cast<const uint4*>(kr)[ch];
-      *reinterpret_cast<uint4*>(&Vs[row * LDK + ch * 8]) = reinterpret_cast<const uint4*>(vr)[ch];
+      Frag8 vv;
+      vv.u = reinterpret_cast<const uint4*>(vr)[ch];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(ch * 8 + e) * LDV + row] = vv.h[e];
     }
     __syncthreads();
 
@@ -365,19 +371,33 @@ __global__ __launch_bounds__(256) void attend_flash_kernel(DevState s, int n_max
         st[kt] = mfma32(a.v, qf[u].v, st[kt]);
       }
     }
+    // causal mask only where the tile reaches past the wave's first query
+    if (j0 + KT - 1 > wave_limit_min) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key > limit) st[kt][r] = -INFINITY;
+        }
+    }
     float tmax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = j0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float v = key <= limit ? st[kt][r] * sl2 : -INFINITY;
-        st[kt][r] = v;
-        tmax = fmaxf(tmax, v);
-      }
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[kt][r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float m_new = fmaxf(m_run, tmax);
-    const float corr = exp2f(m_run - m_new);
+    // rescale only when some lane's running maximum moved
+    if (__any(m_new > m_run)) {
+      const float corr = exp2f(m_run - m_new);
+      l_run *= corr;
+#pragma unroll
+      for (int t = 0; t < DTILES; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] *= corr;
+    }
+    m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -388,26 +408,25 @@ __global__ __launch_bounds__(256) void attend_flash_kernel(DevState s, int n_max
         psum += pr;
       }
     psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < DTILES; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[t][r] *= corr;
+    l_run += psum;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         Frag8 pb;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb.h[e] = f32_to_bf16(st[kt][8 * u + e]);
+        for (int e = 0; e < 8; ++e) pb.v[e] = (__bf16)st[kt][8 * u + e];
         const int kb = kt * 32 + 16 * u + 4 * g;
 #pragma unroll
         for (int t = 0; t < DTILES; ++t) {
-          Frag8 a;
-          const int d = t * 32 + c32;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) a.h[e] = Vs[(kb + (e < 4 ? e : e + 4)) * LDK + d];
+          // keys kb + {0..3} and kb + {8..11} of feature row t * 32 + c32
+          const bf16_t* vrow = &Vt[(t * 32 + c32) * LDV + kb];
+          union {
+            uint2 h[2];
+            bf16x8_t v;
+          } a;
+          a.h[0] = *reinterpret_cast<const uint2*>(vrow);
+          a.h[1] = *reinterpret_cast<const uint2*>(vrow + 8);
           o[t] = mfma32(a.v, pb.v, o[t]);
         }
       }
