@@ -110,7 +110,7 @@ enum {
 /* Payload of the last failure on the calling thread (Chapter 37 error enums). */
 typedef struct {
   kvc_status status;
-  int32_t parameter;        /* revision mismatch: first weight that differs (0 W_q, 1 W_k, 2 W_v) */
+  int32_t parameter;        /* revision mismatch: first weight that differs (0 W_q .. 3 W_o) */
   int32_t sequence;         /* sequence index for FULL, BAD_CUT, CHUNK_ROWS, ROTARY_POSITION */
   int32_t reserved;
   int64_t expected, actual; /* rank, tokens, batch, width, heads, head width, capacity, ... */
@@ -142,23 +142,28 @@ typedef struct {
   double rope_base;
 } kvc_cache_desc;
 
-typedef struct kvc_params kvc_params; /* W_q, W_k, W_v with an identity and per-weight revisions */
+typedef struct kvc_params kvc_params; /* W_q, W_k, W_v (, W_o) with an identity and revisions */
 typedef struct kvc_layer kvc_layer;   /* parameters + head count + position handling           */
 typedef struct kvc_cache kvc_cache;   /* one layer's fixed-capacity K/V state                  */
 
 /* Registers a parameter set.  w_q, w_k, w_v: DEVICE, each [D, D] row-major as
  * [out, in] (a projected row is y[j] = sum_i x[i] W[j, i]), element type
- * `dtype`, borrowed.  Each call creates a new identity, so a rebuilt layer
- * with equal shapes and values is still a different parameter set (Chapter
- * 37, "Bind the state, calculate completely, then commit").
+ * `dtype`, borrowed.  w_o: the layer's output projection in the same layout,
+ * or NULL for a layer whose calls return the merged heads (Chapter 37, "Bind
+ * the state, calculate completely, then commit": the layer has four
+ * parameters and the output projection is the last step before the commit).
+ * Each call creates a new identity, so a rebuilt layer with equal shapes and
+ * values is still a different parameter set.
  * Errors: NULL_ARGUMENT, BAD_ARGUMENT (D <= 0), DTYPE_UNSUPPORTED. */
 kvc_status kvc_params_create(int32_t model_width, kvc_dtype dtype, const void* w_q,
-                             const void* w_k, const void* w_v, kvc_params** out);
+                             const void* w_k, const void* w_v, const void* w_o,
+                             kvc_params** out);
 
-/* Records an in-place update of weight `which` (0 W_q, 1 W_k, 2 W_v, -1 all):
- * its value revision advances and caches bound to the old revision reject
- * further calls (Chapter 37: an optimiser step keeps the identity but advances
- * the revision).  Errors: NULL_ARGUMENT, BAD_ARGUMENT. */
+/* Records an in-place update of weight `which` (0 W_q, 1 W_k, 2 W_v, 3 W_o, -1
+ * all): its value revision advances and caches bound to the old revision
+ * reject further calls (Chapter 37: an optimiser step keeps the identity but
+ * advances the revision).  Errors: NULL_ARGUMENT, BAD_ARGUMENT (index out of
+ * range, or 3 without W_o). */
 kvc_status kvc_params_mark_updated(kvc_params* params, int32_t which);
 void kvc_params_destroy(kvc_params* params);
 
@@ -193,12 +198,12 @@ void kvc_cache_destroy(kvc_cache* cache);
  * sequence b it projects only the new row, rotates q and k at position
  * next_position[b] (= the old length), scores q against the len[b] retained
  * keys plus the candidate key with scale 1/sqrt(d_h), applies a stable
- * softmax, mixes the retained values plus the candidate value, and writes the
- * merged heads to out (DEVICE, [B, 1, D]; double for F64 caches, float
- * otherwise).  Only then does it append the rotated key and unrotated value at
- * row len[b] and advance len[b] and next_position[b] by one (cache
- * transition, "Append along the position axis").  The output projection is
- * not applied.  work (HOST, nullable) receives the row counts.
+ * softmax, mixes the retained values plus the candidate value, merges the
+ * heads and, when the parameter set has W_o, applies it; the result goes to
+ * out (DEVICE, [B, 1, D]; double for F64 caches, float otherwise).  Only then
+ * does it append the rotated key and unrotated value at row len[b] and
+ * advance len[b] and next_position[b] by one (cache transition, "Append along
+ * the position axis").  work (HOST, nullable) receives the row counts.
  * Errors: the request checks above in their order, then the device-found
  * ones; DEFERRED. */
 kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const void* x,
@@ -209,8 +214,9 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
  * together"): x DEVICE [B, n_max, D]; n_rows HOST int32[B] with 0 <= n_b <=
  * n_max (NULL: every n_b = n_max).  Row i < n_b of sequence b is projected,
  * rotated at next_position[b] + i, and attends causally to the len[b]
- * retained rows plus its chunk rows 0..i; out DEVICE [B, n_max, D] (rows
- * i >= n_b untouched).  Then the n_b rows are appended and len[b] and
+ * retained rows plus its chunk rows 0..i; merged heads (times W_o when the
+ * parameter set has it) go to out DEVICE [B, n_max, D] (rows i >= n_b
+ * untouched).  Then the n_b rows are appended and len[b] and
  * next_position[b] advance by n_b.  A prefill is this call on an empty cache.
  * Errors: NULL_ARGUMENT, CHUNK_ROWS, the binding checks (model width .. rotary
  * configuration), FULL (len[b] + n_b > C), ROTARY_POSITION, device-found
@@ -277,9 +283,9 @@ kvc_status kvc_copy_storage(kvc_cache* cache, void* keys_out, void* values_out);
  * stops); 0 stops and frees them.  kvc_profile_read synchronises and writes
  * per-stage totals: ms_out[s] (HOST float[KVC_STAGES]) and calls_out[s]
  * (HOST int32[KVC_STAGES]).  Stages: 0 projection+rotary, 1 attention,
- * 2 split merge, 3 commit. */
+ * 2 split merge, 3 commit, 4 output projection. */
 enum { KVC_STAGE_PROJECT = 0, KVC_STAGE_ATTEND = 1, KVC_STAGE_MERGE = 2, KVC_STAGE_COMMIT = 3,
-       KVC_STAGES = 4 };
+       KVC_STAGE_OUTPUT = 4, KVC_STAGES = 5 };
 kvc_status kvc_profile_enable(kvc_cache* cache, int32_t slots);
 kvc_status kvc_profile_read(kvc_cache* cache, float* ms_out, int32_t* calls_out);
 

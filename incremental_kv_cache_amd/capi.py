@@ -45,8 +45,8 @@ KVC_F64, KVC_F32, KVC_BF16 = 0, 1, 2
 KVC_POS_ROPE, KVC_POS_NONE = 0, 1
 KVC_SYNC, KVC_ASYNC = 0, 1
 KVC_TRUNCATE_KEEP_STALE_POSITION = 1
-KVC_STAGE_PROJECT, KVC_STAGE_ATTEND, KVC_STAGE_MERGE, KVC_STAGE_COMMIT = 0, 1, 2, 3
-KVC_STAGES = 4
+KVC_STAGE_PROJECT, KVC_STAGE_ATTEND, KVC_STAGE_MERGE, KVC_STAGE_COMMIT, KVC_STAGE_OUTPUT = 0, 1, 2, 3, 4
+KVC_STAGES = 5
 
 
 class ErrorDetail(C.Structure):
@@ -92,7 +92,7 @@ PI32 = C.POINTER(C.c_int32)
 PI64 = C.POINTER(C.c_int64)
 
 PROTOTYPES = {
-    "kvc_params_create": (I32, [I32, I32, P, P, P, PP]),
+    "kvc_params_create": (I32, [I32, I32, P, P, P, P, PP]),
     "kvc_params_mark_updated": (I32, [P, I32]),
     "kvc_params_destroy": (None, [P]),
     "kvc_layer_create": (I32, [P, I32, I32, C.c_double, I32, PP]),

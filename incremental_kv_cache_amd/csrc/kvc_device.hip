@@ -34,14 +34,14 @@ using namespace dev;
 // produces one rotary pair (feature f and f + d_h/2 of head h), so the rotation
 // needs no exchange.  The input row is staged through LDS in the accumulate
 // type, in slices.
-template <typename T>
-__global__ __launch_bounds__(256) void project_kernel(DevState s, const T* __restrict__ x, int n_max,
-                                                      int per_seq_rows) {
+template <typename T, typename XT>
+__global__ __launch_bounds__(256) void project_kernel(DevState s, const XT* __restrict__ x, int n_max,
+                                                      int per_seq_rows, int proj_first) {
   using A = typename Acc<T>::type;
   constexpr int SLICE = 2048;
   __shared__ A xs[SLICE];
   const int m = blockIdx.y;
-  const int p = blockIdx.z;
+  const int p = proj_first + int(blockIdx.z);
   const int b = m / n_max;
   const int i = m - b * n_max;
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
@@ -54,10 +54,10 @@ __global__ __launch_bounds__(256) void project_kernel(DevState s, const T* __res
   const bool active = pair < s.heads * half;
   const int h = active ? pair / half : 0;
   const int f = active ? pair - h * half : 0;
-  const T* W = static_cast<const T*>(p == 0 ? s.wq : (p == 1 ? s.wk : s.wv));
+  const T* W = static_cast<const T*>(p == 0 ? s.wq : (p == 1 ? s.wk : (p == 2 ? s.wv : s.wo)));
   const T* w0 = W + size_t(h * dh + f) * D;
   const T* w1 = W + size_t(h * dh + f + half) * D;
-  const T* xr = x + size_t(m) * D;
+  const XT* xr = x + size_t(m) * D;
 
   A acc0 = 0, acc1 = 0;
   for (int k0 = 0; k0 < D; k0 += SLICE) {
@@ -75,6 +75,14 @@ __global__ __launch_bounds__(256) void project_kernel(DevState s, const T* __res
   }
   if (!active) return;
 
+  if (p == 3) {  // output projection: plain columns of row m
+    A* o = static_cast<A*>(s.out_proj_dst) + size_t(m) * D + size_t(h) * dh + f;
+    o[0] = acc0;
+    o[half] = acc1;
+    if (!finite(acc0)) flag_min(&s.err->output, size_t(m) * D + size_t(h) * dh + f);
+    if (!finite(acc1)) flag_min(&s.err->output, size_t(m) * D + size_t(h) * dh + f + half);
+    return;
+  }
   A r0 = acc0, r1 = acc1;
   if (p < 2 && s.rope) {
     int pos = s.next_pos[b] + i;
@@ -463,12 +471,12 @@ struct AttendChunk {
   }
 };
 
-template <typename T>
-int project_t(const DevState& s, const void* x, int n_max, int per_seq_rows) {
+template <typename T, typename XT>
+int project_t(const DevState& s, const XT* x, int n_max, int per_seq_rows, int proj_first, int nproj) {
   const int pairs = s.heads * (s.head_width / 2);
-  dim3 grid((pairs + 255) / 256, s.batch * n_max, 3);
-  hipLaunchKernelGGL((project_kernel<T>), grid, dim3(256), 0, st(s.stream), s, static_cast<const T*>(x), n_max,
-                     per_seq_rows);
+  dim3 grid((pairs + 255) / 256, s.batch * n_max, nproj);
+  hipLaunchKernelGGL((project_kernel<T, XT>), grid, dim3(256), 0, st(s.stream), s, x, n_max, per_seq_rows,
+                     proj_first);
   return last_launch();
 }
 
@@ -572,21 +580,34 @@ int dev_set_rows(const DevState& s, const int32_t* vals) {
 }
 
 int mfma_project(const DevState& s, const void* x, int n_max, int per_seq_rows);
+int mfma_output_project(const DevState& s, int n_max, int per_seq_rows);
 int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out);
+int fast_attend_decode(const DevState& s, void* out);
+int fast_merge_decode(const DevState& s, void* out);
 
 int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows) {
   const int rc = mfma_project(s, x, n_max, per_seq_rows);
   if (rc >= 0) return rc;
   switch (s.dtype) {
-    case KVC_F64: return project_t<double>(s, x, n_max, per_seq_rows);
-    case KVC_F32: return project_t<float>(s, x, n_max, per_seq_rows);
-    case KVC_BF16: return project_t<bf16_t>(s, x, n_max, per_seq_rows);
+    case KVC_F64: return project_t<double>(s, static_cast<const double*>(x), n_max, per_seq_rows, 0, 3);
+    case KVC_F32: return project_t<float>(s, static_cast<const float*>(x), n_max, per_seq_rows, 0, 3);
+    case KVC_BF16: return project_t<bf16_t>(s, static_cast<const bf16_t*>(x), n_max, per_seq_rows, 0, 3);
   }
   return int(hipErrorInvalidValue);
 }
 
-int fast_attend_decode(const DevState& s, void* out);
-int fast_merge_decode(const DevState& s, void* out);
+int dev_output_project(const DevState& state, int n_max, int per_seq_rows, void* out) {
+  DevState s = state;
+  s.out_proj_dst = out;
+  const int rc = mfma_output_project(s, n_max, per_seq_rows);
+  if (rc >= 0) return rc;
+  switch (s.dtype) {
+    case KVC_F64: return project_t<double>(s, static_cast<const double*>(s.merged), n_max, per_seq_rows, 3, 1);
+    case KVC_F32: return project_t<float>(s, static_cast<const float*>(s.merged), n_max, per_seq_rows, 3, 1);
+    case KVC_BF16: return project_t<bf16_t>(s, static_cast<const float*>(s.merged), n_max, per_seq_rows, 3, 1);
+  }
+  return int(hipErrorInvalidValue);
+}
 
 int dev_attend_decode(const DevState& s, void* out) {
   const int rc = fast_attend_decode(s, out);

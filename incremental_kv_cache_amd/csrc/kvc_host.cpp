@@ -23,9 +23,10 @@ using namespace kvc;
 struct kvc_params {
   int32_t model_width;
   kvc_dtype dtype;
-  const void* w[3];
+  const void* w[4];      // W_q, W_k, W_v, W_o (W_o may be null)
+  int32_t nweights;      // 3 without W_o, 4 with it
   uint64_t id;           // identity: unique per created parameter set
-  uint64_t revision[3];  // value revision per weight
+  uint64_t revision[4];  // value revision per weight
 };
 
 struct kvc_layer {
@@ -53,7 +54,7 @@ struct kvc_cache {
   int32_t batch, heads, head_width, model_width, capacity, max_chunk_rows;
   kvc_dtype dtype;
   uint64_t params_id;
-  uint64_t revision[3];
+  uint64_t revision[4];
   int32_t rope_feature_width, rope_max_positions;
   uint64_t rope_base_bits;
   double rope_base;
@@ -138,7 +139,7 @@ kvc_status check_binding(const kvc_layer* layer, const kvc_cache* c) {
   if (c->params_id != p->id)
     return fail(KVC_ERR_CACHE_LAYER_MISMATCH,
                 "cache was created for a different attention layer (parameter identity differs)");
-  for (int k = 0; k < 3; ++k) {
+  for (int k = 0; k < p->nweights; ++k) {
     if (c->revision[k] != p->revision[k]) {
       g_last.parameter = k;
       g_last.cache_revision = c->revision[k];
@@ -285,6 +286,7 @@ void free_cache(kvc_cache* c) {
   dev_free(c->ds.rope_cos);
   dev_free(c->ds.rope_sin);
   dev_free(c->ds.err);
+  dev_free(c->ds.merged);
   dev_host_free(c->err_host);
   for (void* e : c->prof.events) dev_event_destroy(e);
   delete c;
@@ -304,15 +306,24 @@ kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_row
   rc = dev_project(s, x, n_max, per_seq);
   profile_mark(c, KVC_STAGE_PROJECT, 1);
   if (rc) return device_fail(rc, "projection launch");
+  // merged heads go straight to the caller's output, or to scratch when the
+  // output projection follows
+  void* heads = s.wo ? s.merged : out;
   profile_mark(c, KVC_STAGE_ATTEND, 0);
-  rc = decode ? dev_attend_decode(s, out) : dev_attend_chunk(s, n_max, per_seq, out);
+  rc = decode ? dev_attend_decode(s, heads) : dev_attend_chunk(s, n_max, per_seq, heads);
   profile_mark(c, KVC_STAGE_ATTEND, 1);
   if (rc) return device_fail(rc, "attention launch");
   if (decode) {
     profile_mark(c, KVC_STAGE_MERGE, 0);
-    rc = dev_merge_decode(s, out);
+    rc = dev_merge_decode(s, heads);
     profile_mark(c, KVC_STAGE_MERGE, 1);
     if (rc) return device_fail(rc, "merge launch");
+  }
+  if (s.wo) {
+    profile_mark(c, KVC_STAGE_OUTPUT, 0);
+    rc = dev_output_project(s, n_max, per_seq, out);
+    profile_mark(c, KVC_STAGE_OUTPUT, 1);
+    if (rc) return device_fail(rc, "output projection launch");
   }
   profile_mark(c, KVC_STAGE_COMMIT, 0);
   rc = dev_commit(s, n_max, per_seq);
@@ -389,7 +400,7 @@ const char* kvc_status_name(kvc_status s) {
 const kvc_error_detail* kvc_last_error(void) { return &g_last; }
 
 kvc_status kvc_params_create(int32_t model_width, kvc_dtype dtype, const void* w_q, const void* w_k,
-                             const void* w_v, kvc_params** out) {
+                             const void* w_v, const void* w_o, kvc_params** out) {
   reset_detail();
   if (!out || !w_q || !w_k || !w_v) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_params_create");
   *out = nullptr;
@@ -403,8 +414,10 @@ kvc_status kvc_params_create(int32_t model_width, kvc_dtype dtype, const void* w
   p->w[0] = w_q;
   p->w[1] = w_k;
   p->w[2] = w_v;
+  p->w[3] = w_o;
+  p->nweights = w_o ? 4 : 3;
   p->id = g_next_params_id.fetch_add(1);
-  p->revision[0] = p->revision[1] = p->revision[2] = 0;
+  for (int k = 0; k < 4; ++k) p->revision[k] = 0;
   *out = p;
   return KVC_OK;
 }
@@ -412,8 +425,9 @@ kvc_status kvc_params_create(int32_t model_width, kvc_dtype dtype, const void* w
 kvc_status kvc_params_mark_updated(kvc_params* params, int32_t which) {
   reset_detail();
   if (!params) return fail(KVC_ERR_NULL_ARGUMENT, "null parameter set");
-  if (which < -1 || which > 2) return fail(KVC_ERR_BAD_ARGUMENT, "weight index %d out of range", which);
-  for (int k = 0; k < 3; ++k)
+  if (which < -1 || which >= params->nweights)
+    return fail(KVC_ERR_BAD_ARGUMENT, "weight index %d out of range for %d weights", which, params->nweights);
+  for (int k = 0; k < params->nweights; ++k)
     if (which == -1 || which == k) params->revision[k]++;
   return KVC_OK;
 }
@@ -484,7 +498,7 @@ kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capac
   c->max_chunk_rows = max_chunk_rows;
   c->dtype = p->dtype;
   c->params_id = p->id;
-  for (int k = 0; k < 3; ++k) c->revision[k] = p->revision[k];
+  for (int k = 0; k < 4; ++k) c->revision[k] = p->revision[k];
   c->rope_feature_width = layer->rope_feature_width();
   c->rope_max_positions = layer->rope_max_positions;
   std::memcpy(&c->rope_base_bits, &layer->rope_base, 8);
@@ -515,6 +529,7 @@ kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capac
   s.wq = p->w[0];
   s.wk = p->w[1];
   s.wv = p->w[2];
+  s.wo = p->w[3];
   s.max_tiles = max_tiles;
   s.tile_rows = kDecodeTileRows;
   s.stream = hip_stream;
@@ -534,8 +549,10 @@ kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capac
       {&s.q, round16(size_t(cand) * as)},
       {&s.partials, round16(size_t(batch) * H * max_tiles * (dh + 2) * as)},
       {reinterpret_cast<void**>(&s.err), round16(sizeof(ErrWords))},
+      {&s.merged, p->w[3] ? round16(size_t(cand) * as) : 0},  // [B, max_chunk_rows, D]
   };
   for (auto& a : allocs) {
+    if (a.bytes == 0) continue;
     rc = dev_malloc(a.p, a.bytes);
     if (rc) {
       *a.p = nullptr;
@@ -552,7 +569,7 @@ kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capac
   }
   // Zero-filled storage (Chapter 37: zeroed backing buffers), zero lengths.
   for (auto& a : allocs) {
-    if (*a.p == s.err) continue;
+    if (*a.p == s.err || a.bytes == 0) continue;
     rc = dev_zero(*a.p, a.bytes, s.stream);
     if (rc) {
       free_cache(c);

@@ -39,6 +39,7 @@ struct DevState {
   const void* wq;
   const void* wk;
   const void* wv;
+  const void* wo;      // output projection, or null
   void* keys;          // [B, H, C, d_h] storage type
   void* values;        // [B, H, C, d_h]
   int32_t* len;        // [B] committed rows
@@ -48,6 +49,8 @@ struct DevState {
   void* cand_k;        // [B, H, n, d_h] storage type (n = rows of the call)
   void* cand_v;        // [B, H, n, d_h]
   void* q;             // [B, H, n, d_h] accumulate type
+  void* merged;        // [B, n, D] accumulate type: merged heads before W_o (null without W_o)
+  void* out_proj_dst;  // [B, n, D] accumulate type: destination of the W_o projection (per call)
   void* partials;      // [B, H, max_tiles, d_h + 2] accumulate type
   int max_tiles;       // ceil(C / kDecodeTileRows)
   int tile_rows;       // split-K tile of the current decode call (multiple of kDecodeTileRows)
@@ -87,6 +90,8 @@ int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows);
 int dev_attend_decode(const DevState& s, void* out);
 int dev_merge_decode(const DevState& s, void* out);
 int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out);
+// out[b, i, :] = merged[b, i, :] x W_o (rows i < n_b).
+int dev_output_project(const DevState& s, int n_max, int per_seq_rows, void* out);
 int dev_commit(const DevState& s, int n_max, int per_seq_rows);
 
 int dev_event_create(void** e);

@@ -30,7 +30,30 @@ namespace {
 using namespace dev;
 
 __device__ __forceinline__ const bf16_t* weight_of(const DevState& s, int p) {
-  return static_cast<const bf16_t*>(p == 0 ? s.wq : (p == 1 ? s.wk : s.wv));
+  return static_cast<const bf16_t*>(p == 0 ? s.wq : (p == 1 ? s.wk : (p == 2 ? s.wv : s.wo)));
+}
+
+// 16 input elements starting at p as two bf16x8 pieces (float input is rounded).
+__device__ __forceinline__ void load16(const bf16_t* p, uint4& lo, uint4& hi) {
+  lo = reinterpret_cast<const uint4*>(p)[0];
+  hi = reinterpret_cast<const uint4*>(p)[1];
+}
+__device__ __forceinline__ uint4 pack8(const float4& a, const float4& b) {
+  Frag8 f;
+  f.v[0] = (__bf16)a.x;
+  f.v[1] = (__bf16)a.y;
+  f.v[2] = (__bf16)a.z;
+  f.v[3] = (__bf16)a.w;
+  f.v[4] = (__bf16)b.x;
+  f.v[5] = (__bf16)b.y;
+  f.v[6] = (__bf16)b.z;
+  f.v[7] = (__bf16)b.w;
+  return f.u;
+}
+__device__ __forceinline__ void load16(const float* p, uint4& lo, uint4& hi) {
+  const float4* q = reinterpret_cast<const float4*>(p);
+  lo = pack8(q[0], q[1]);
+  hi = pack8(q[2], q[3]);
 }
 
 // Rotates (if needed) and stores rotary pair `pair` (global pair index within
@@ -46,6 +69,14 @@ __device__ __forceinline__ void store_pair(const DevState& s, int p, int m, int 
   const int half = dh >> 1;
   const int h = pair / half;
   const int f = pair - h * half;
+  if (p == 3) {  // output projection: plain columns h*d_h + f and + d_h/2 of row m
+    float* o = static_cast<float*>(s.out_proj_dst) + size_t(m) * s.model_width + size_t(h) * dh + f;
+    o[0] = lo;
+    o[half] = hi;
+    if (!isfinite(lo)) flag_min(&s.err->output, size_t(m) * s.model_width + size_t(h) * dh + f);
+    if (!isfinite(hi)) flag_min(&s.err->output, size_t(m) * s.model_width + size_t(h) * dh + f + half);
+    return;
+  }
   float r0 = lo, r1 = hi;
   if (p < 2 && s.rope) {
     int pos = s.next_pos[b] + i;
@@ -95,15 +126,17 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 }
 
 // NCH > 0: the reduction axis has exactly NCH chunks (fully unrolled); 0: any D.
-template <int NCH>
-__global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const bf16_t* __restrict__ x, int M,
-                                                             int n_max, int per_seq_rows) {
+// XT: input element type (bf16 rows, or the float32 merged heads for W_o).
+template <int NCH, typename XT>
+__global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const XT* __restrict__ x, int M,
+                                                             int n_max, int per_seq_rows, int proj_first) {
   __shared__ __attribute__((aligned(16))) bf16_t Xs[2][32 * SLDX];
   const int D = s.model_width;
   const int half = s.head_width >> 1;
   const int tiles_per_proj = D / 64;
-  const int p = blockIdx.x / tiles_per_proj;
-  const int pair_base = (blockIdx.x - p * tiles_per_proj) * 32;
+  const int pt = blockIdx.x / tiles_per_proj;
+  const int p = proj_first + pt;
+  const int pair_base = (blockIdx.x - pt * tiles_per_proj) * 32;
   const int m0 = blockIdx.y * 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -119,15 +152,15 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const b
   // input staging: thread copies 32 bytes of row tid/8
   const int xrow = tid >> 3;
   const int xseg = (tid & 7) * 16;
-  const bf16_t* xg = x + size_t(min(m0 + xrow, M - 1)) * D + xseg;
+  const XT* xg = x + size_t(min(m0 + xrow, M - 1)) * D + xseg;
 
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int nch = NCH > 0 ? NCH : D / SKC;
   Frag8 b[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) b[u].u = *reinterpret_cast<const uint4*>(wp + 32 * u);
-  uint4 xr0 = reinterpret_cast<const uint4*>(xg)[0];
-  uint4 xr1 = reinterpret_cast<const uint4*>(xg)[1];
+  uint4 xr0, xr1;
+  load16(xg, xr0, xr1);
   *reinterpret_cast<uint4*>(&Xs[0][xrow * SLDX + xseg]) = xr0;
   *reinterpret_cast<uint4*>(&Xs[0][xrow * SLDX + xseg + 8]) = xr1;
   __syncthreads();
@@ -136,10 +169,7 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const b
   // the next weight fragments and publish the input chunk for the next step
   auto step = [&](int c, int buf) {
     const bool more = c + 1 < nch;
-    if (more) {
-      xr0 = reinterpret_cast<const uint4*>(xg + (c + 1) * SKC)[0];
-      xr1 = reinterpret_cast<const uint4*>(xg + (c + 1) * SKC)[1];
-    }
+    if (more) load16(xg + (c + 1) * SKC, xr0, xr1);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       Frag8 a0, a1;
@@ -187,16 +217,18 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const b
 // so each thread owns both halves of its pairs.
 constexpr int TBM = 128, TBN = 128, TBK = 64, TLD = TBK + 8;
 
-__global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const bf16_t* __restrict__ x, int M,
-                                                            int n_max, int per_seq_rows) {
+template <typename XT>
+__global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT* __restrict__ x, int M,
+                                                            int n_max, int per_seq_rows, int proj_first) {
   __shared__ __attribute__((aligned(16))) bf16_t As[TBM * TLD];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[TBN * TLD];
   const int D = s.model_width;
   const int dh = s.head_width;
   const int half = dh >> 1;
   const int tiles_per_proj = D / TBN;  // (D/2 pairs) / 64
-  const int p = blockIdx.x / tiles_per_proj;
-  const int pair_base = (blockIdx.x - p * tiles_per_proj) * 64;
+  const int pt = blockIdx.x / tiles_per_proj;
+  const int p = proj_first + pt;
+  const int pair_base = (blockIdx.x - pt * tiles_per_proj) * 64;
   const int m0 = blockIdx.y * TBM;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -208,7 +240,7 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const bf
   // global -> LDS assignment: thread loads 64 contiguous bytes of row tid/2
   const int lrow = tid >> 1;
   const int lk = (tid & 1) * 32;
-  const bf16_t* ag = x + size_t(min(m0 + lrow, M - 1)) * D + lk;
+  const XT* ag = x + size_t(min(m0 + lrow, M - 1)) * D + lk;
   const int v = lrow;  // virtual column of the B tile
   const int vpair = pair_base + (v >> 6) * 32 + (v & 31);
   const int vh = vpair / half;
@@ -228,12 +260,9 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const bf
   // kept in named registers (an indexed array here ends up in scratch memory)
   uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
   auto fetch = [&](int kt) {
-    const uint4* a4 = reinterpret_cast<const uint4*>(ag + kt * TBK);
     const uint4* b4 = reinterpret_cast<const uint4*>(bg + kt * TBK);
-    ra0 = a4[0];
-    ra1 = a4[1];
-    ra2 = a4[2];
-    ra3 = a4[3];
+    load16(ag + kt * TBK, ra0, ra1);
+    load16(ag + kt * TBK + 16, ra2, ra3);
     rb0 = b4[0];
     rb1 = b4[1];
     rb2 = b4[2];
@@ -455,32 +484,46 @@ inline hipStream_t st(void* p) { return static_cast<hipStream_t>(p); }
 
 }  // namespace
 
-// Returns -1 when the shape has no MFMA kernel (the caller then uses the
-// vector kernels), else 0 or a HIP error code.
-int mfma_project(const DevState& s, const void* x, int n_max, int per_seq_rows) {
+// Projections proj_first .. proj_first + nproj - 1 (0 W_q, 1 W_k, 2 W_v, 3 W_o)
+// of M = B * n_max rows of x.  Returns -1 when the shape has no MFMA kernel (the
+// caller then uses the vector kernels), else 0 or a HIP error code.
+template <typename XT>
+int mfma_project_t(const DevState& s, const XT* xb, int n_max, int per_seq_rows, int proj_first, int nproj) {
   if (s.dtype != KVC_BF16 || s.model_width % 128 != 0) return -1;
   const int M = s.batch * n_max;
-  const bf16_t* xb = static_cast<const bf16_t*>(x);
   if (M <= 64) {
-    dim3 grid(3 * (s.model_width / 64), (M + 31) / 32);
+    dim3 grid(nproj * (s.model_width / 64), (M + 31) / 32);
     switch (s.model_width) {
       case 2048:
-        hipLaunchKernelGGL(project_skinny_kernel<16>, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+        hipLaunchKernelGGL((project_skinny_kernel<16, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
+                           per_seq_rows, proj_first);
         break;
       case 4096:
-        hipLaunchKernelGGL(project_skinny_kernel<32>, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+        hipLaunchKernelGGL((project_skinny_kernel<32, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
+                           per_seq_rows, proj_first);
         break;
       case 8192:
-        hipLaunchKernelGGL(project_skinny_kernel<64>, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+        hipLaunchKernelGGL((project_skinny_kernel<64, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
+                           per_seq_rows, proj_first);
         break;
       default:
-        hipLaunchKernelGGL(project_skinny_kernel<0>, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+        hipLaunchKernelGGL((project_skinny_kernel<0, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
+                           per_seq_rows, proj_first);
     }
   } else {
-    dim3 grid(3 * (s.model_width / TBN), (M + TBM - 1) / TBM);
-    hipLaunchKernelGGL(project_tiled_kernel, grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, per_seq_rows);
+    dim3 grid(nproj * (s.model_width / TBN), (M + TBM - 1) / TBM);
+    hipLaunchKernelGGL((project_tiled_kernel<XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
+                       per_seq_rows, proj_first);
   }
   return int(hipGetLastError());
+}
+
+int mfma_project(const DevState& s, const void* x, int n_max, int per_seq_rows) {
+  return mfma_project_t(s, static_cast<const bf16_t*>(x), n_max, per_seq_rows, 0, 3);
+}
+
+int mfma_output_project(const DevState& s, int n_max, int per_seq_rows) {
+  return mfma_project_t(s, static_cast<const float*>(s.merged), n_max, per_seq_rows, 3, 1);
 }
 
 int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out) {

@@ -107,19 +107,20 @@ def _lib(lib):
     return lib if lib is not None else capi.lib()
 
 
-def kvc_params_create(w_q, w_k, w_v, *, lib=None) -> Params:
-    """W_q, W_k, W_v: contiguous device tensors [D, D] as [out, in], one dtype."""
+def kvc_params_create(w_q, w_k, w_v, w_o=None, *, lib=None) -> Params:
+    """W_q, W_k, W_v (and optionally W_o): contiguous device tensors [D, D] as [out, in], one dtype."""
     lib = _lib(lib)
     code = _dtype_code(w_q)
-    if any(_dtype_code(w) != code or tuple(w.shape) != tuple(w_q.shape) for w in (w_k, w_v)):
+    ws = (w_q, w_k, w_v) + ((w_o,) if w_o is not None else ())
+    if any(_dtype_code(w) != code or tuple(w.shape) != tuple(w_q.shape) for w in ws):
         raise TypeError("weights must share dtype and shape")
     if w_q.dim() != 2 or w_q.shape[0] != w_q.shape[1]:
         raise ValueError("weights must be square [D, D]")
     out = C.c_void_p()
     _check(lib, lib.kvc_params_create(int(w_q.shape[0]), code, _dev_ptr(w_q), _dev_ptr(w_k), _dev_ptr(w_v),
-                                      C.byref(out)))
+                                      _dev_ptr(w_o) if w_o is not None else None, C.byref(out)))
     h = Params(lib, out)
-    h.tensors = (w_q, w_k, w_v)
+    h.tensors = ws
     h.dtype_code = code
     h.model_width = int(w_q.shape[0])
     return h

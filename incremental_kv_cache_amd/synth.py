@@ -39,6 +39,7 @@ STREAM_EMBED = 6
 STREAM_TOKENS = 7
 STREAM_PREFIX_X = 8
 STREAM_EDIT = 9
+STREAM_WO = 10
 STREAM_TOY_W = 16  # + 3 * layer + {0, 1, 2}
 
 
@@ -136,6 +137,11 @@ def sha256(*arrays: np.ndarray) -> str:
 
 
 # --------------------------------------------------------------- workloads ---
+
+def output_weight(seed: int, model_width: int, std: float, dtype: str):
+    """W_o as a [D_out, D_in] array: (storage, float64 value)."""
+    return quantize(normal(seed, STREAM_WO, (model_width, model_width), std=std), dtype)
+
 
 def decode_weights(seed: int, model_width: int, std: float, dtype: str):
     """W_q, W_k, W_v as [D_out, D_in] arrays: (storage, float64 value) pairs."""

@@ -109,14 +109,17 @@ def layer_projections(x_rows, wq, wk, wv, heads: int, positions, base: float, ro
 
 
 def causal_layer(x_rows, wq, wk, wv, heads: int, base: float = 10000.0,
-                 rope: bool = True, positions=None, rows=None):
+                 rope: bool = True, positions=None, rows=None, wo=None):
     """Full-prefix causal attention of one layer, recomputed from hidden rows.
 
     This is the reference every cached result must reproduce (Chapter 37,
     "From causal attention to managed LLM inference state": Vaswani-style
     masked attention; row p reads rows 0..p).  ``x_rows`` [L, D]; positions
     default to 0..L-1.  ``rows`` selects which output rows to compute (default
-    all).  Returns dict with ``out`` [len(rows), D], ``keys`` / ``values``
+    all).  ``wo``: the layer's output projection, applied to the merged heads
+    (Chapter 37, "Bind the state, calculate completely, then commit": merge
+    heads, then the output projection); None returns the merged heads.
+    Returns dict with ``out`` [len(rows), D], ``keys`` / ``values``
     [H, L, d_h] (the layer's full logical cache), ``weights`` (list per row of
     [H, p+1]).
     """
@@ -136,22 +139,25 @@ def causal_layer(x_rows, wq, wk, wv, heads: int, base: float = 10000.0,
             w_heads.append(w)
         outs.append(np.concatenate(o_heads))
         weights.append(np.stack(w_heads))
+    out = np.stack(outs) if outs else np.zeros((0, x_rows.shape[1]))
+    if wo is not None:
+        out = project(out, wo)
     return {
-        "out": np.stack(outs) if outs else np.zeros((0, x_rows.shape[1])),
+        "out": out,
         "keys": np.transpose(k, (1, 0, 2)),
         "values": np.transpose(v, (1, 0, 2)),
         "weights": weights,
     }
 
 
-def full_prefix_decode(x_rows, wq, wk, wv, heads: int, base: float = 10000.0, rope: bool = True):
+def full_prefix_decode(x_rows, wq, wk, wv, heads: int, base: float = 10000.0, rope: bool = True, wo=None):
     """Output of the newest row t-1 of a t-row prefix, recomputed from scratch.
 
     Equivalent to ``causal_layer(...)`` restricted to the last row; returns the
     same dict (``out`` [D], ``weights`` [H, t]).
     """
     n = np.asarray(x_rows).shape[0]
-    r = causal_layer(x_rows, wq, wk, wv, heads, base, rope, rows=[n - 1])
+    r = causal_layer(x_rows, wq, wk, wv, heads, base, rope, rows=[n - 1], wo=wo)
     r["out"] = r["out"][0]
     r["weights"] = r["weights"][0]
     return r

@@ -52,11 +52,14 @@ def assert_parity(gpu, ref, dtype, what=""):
 
 
 def make_layer(seed, model_width, heads, dtype, std=None, base=10000.0, max_positions=4096,
-               pos_mode=K.KVC_POS_ROPE):
-    """Seeded W_q, W_k, W_v ([D, D] as [out, in]) on the device; returns (layer, float64 weights)."""
+               pos_mode=K.KVC_POS_ROPE, wo=False):
+    """Seeded W_q, W_k, W_v (and W_o when ``wo``; [D, D] as [out, in]) on the device;
+    returns (layer, float64 weights in that order)."""
     if std is None:
         std = model_width ** -0.5
     ws = synth.decode_weights(seed, model_width, std, dtype)
+    if wo:
+        ws.append(synth.output_weight(seed, model_width, std, dtype))
     tensors = [to_device(s, dtype) for s, _ in ws]
     params = K.kvc_params_create(*tensors)
     layer = K.kvc_layer_create(params, heads, pos_mode, base, max_positions)

@@ -69,6 +69,7 @@ int dev_project(const DevState&, const void*, int, int) { return 1; }
 int dev_attend_decode(const DevState&, void*) { return 1; }
 int dev_merge_decode(const DevState&, void*) { return 1; }
 int dev_attend_chunk(const DevState&, int, int, void*) { return 1; }
+int dev_output_project(const DevState&, int, int, void*) { return 1; }
 int dev_commit(const DevState&, int, int) { return 1; }
 int dev_event_create(void** e) {
   *e = std::malloc(1);

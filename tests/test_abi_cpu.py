@@ -56,10 +56,10 @@ def test_params_and_layer_validation_without_device(lib):
     """Parameter and layer handles need no device; their argument checks run on the host."""
     dummy = C.c_void_p(16)
     out = C.c_void_p()
-    assert lib.kvc_params_create(4, capi.KVC_F64, dummy, dummy, dummy, None) == capi.KVC_ERR_NULL_ARGUMENT
-    assert lib.kvc_params_create(0, capi.KVC_F64, dummy, dummy, dummy, C.byref(out)) == capi.KVC_ERR_BAD_ARGUMENT
-    assert lib.kvc_params_create(4, 7, dummy, dummy, dummy, C.byref(out)) == capi.KVC_ERR_DTYPE_UNSUPPORTED
-    assert lib.kvc_params_create(4, capi.KVC_F64, dummy, dummy, dummy, C.byref(out)) == capi.KVC_OK
+    assert lib.kvc_params_create(4, capi.KVC_F64, dummy, dummy, dummy, None, None) == capi.KVC_ERR_NULL_ARGUMENT
+    assert lib.kvc_params_create(0, capi.KVC_F64, dummy, dummy, dummy, None, C.byref(out)) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_params_create(4, 7, dummy, dummy, dummy, None, C.byref(out)) == capi.KVC_ERR_DTYPE_UNSUPPORTED
+    assert lib.kvc_params_create(4, capi.KVC_F64, dummy, dummy, dummy, None, C.byref(out)) == capi.KVC_OK
     params = out
     layer = C.c_void_p()
     assert lib.kvc_layer_create(params, 3, 0, 10000.0, 4, C.byref(layer)) == capi.KVC_ERR_BAD_ARGUMENT

@@ -34,9 +34,9 @@ def lib(tmp_path_factory):
 DUMMY = C.c_void_p(64)
 
 
-def params(lib, d=4, dtype=capi.KVC_F64):
+def params(lib, d=4, dtype=capi.KVC_F64, wo=False):
     p = C.c_void_p()
-    assert lib.kvc_params_create(d, dtype, DUMMY, DUMMY, DUMMY, C.byref(p)) == 0
+    assert lib.kvc_params_create(d, dtype, DUMMY, DUMMY, DUMMY, DUMMY if wo else None, C.byref(p)) == 0
     return p
 
 
@@ -160,6 +160,22 @@ def test_binding_cases_of_the_error_evidence(lib):
     assert append(lib, l, c, x) == capi.KVC_ERR_CACHE_LAYER_REVISION_MISMATCH
     fresh = cache(lib, l)                             # a new cache binds the new revision
     assert append(lib, l, fresh, x) == capi.KVC_ERR_DEVICE
+
+
+def test_output_projection_is_a_bound_parameter(lib):
+    """W_o is the fourth bound weight: its in-place update is reported as parameter 3;
+    a set without W_o has only three weights to update."""
+    p = params(lib, wo=True)
+    l = layer(lib, p)
+    c = cache(lib, l)
+    assert append(lib, l, c, (1, 1, 4)) == capi.KVC_ERR_DEVICE
+    assert lib.kvc_params_mark_updated(p, 3) == 0
+    assert append(lib, l, c, (1, 1, 4)) == capi.KVC_ERR_CACHE_LAYER_REVISION_MISMATCH
+    d = lib.kvc_last_error().contents
+    assert (d.parameter, d.cache_revision, d.layer_revision) == (3, 0, 1)
+    q = params(lib)
+    assert lib.kvc_params_mark_updated(q, 3) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_params_mark_updated(q, -1) == 0
 
 
 def test_binding_precedes_shape_of_geometry(lib):

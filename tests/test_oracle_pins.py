@@ -46,9 +46,8 @@ def test_trace_fixture_reproduces_every_printed_number():
     x, eye, w_o = _fixture()
     for step in g["steps"]:
         p = step["position"]
-        r = A.full_prefix_decode(x[: p + 1], eye, eye, eye, heads=2, base=10000.0)
-        y = A.project(r["out"], w_o)  # the chapter's layer applies its output projection
-        np.testing.assert_allclose(y, step["output"], rtol=0, atol=5.1e-10)
+        r = A.full_prefix_decode(x[: p + 1], eye, eye, eye, heads=2, base=10000.0, wo=w_o)
+        np.testing.assert_allclose(r["out"], step["output"], rtol=0, atol=5.1e-10)
         for h, head in enumerate(step["heads"]):
             np.testing.assert_allclose(r["weights"][h], head["weights"], rtol=0, atol=5.1e-13)
             np.testing.assert_allclose(r["keys"][h], head["keys"], rtol=0, atol=5.1e-10)
@@ -157,6 +156,17 @@ def test_weights_are_a_distribution_and_output_in_convex_hull():
             o = r["out"][p, h * 4:(h + 1) * 4]
             assert np.all(o <= v[h, : p + 1].max(axis=0) + 1e-14)
             assert np.all(o >= v[h, : p + 1].min(axis=0) - 1e-14)
+
+
+def test_output_projection_is_applied_to_merged_heads():
+    """With W_o the layer output is merged heads through W_o; with W_o = I it is the
+    merged heads themselves (Chapter 37, "Bind the state...": merge, then project)."""
+    x = synth.normal(4, 2, (6, 8))
+    w = [synth.normal(4, s, (8, 8), std=0.35) for s in (3, 4, 5)]
+    wo = synth.normal(4, 10, (8, 8), std=0.35)
+    plain = A.causal_layer(x, *w, heads=2)["out"]
+    np.testing.assert_array_equal(A.causal_layer(x, *w, heads=2, wo=np.eye(8))["out"], plain)
+    np.testing.assert_allclose(A.causal_layer(x, *w, heads=2, wo=wo)["out"], plain @ wo.T, rtol=0, atol=1e-15)
 
 
 def test_projection_orientation_and_head_blocks():
