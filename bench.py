@@ -165,36 +165,119 @@ def stage_times(cache, step, steps):
     return [m / c if c else 0.0 for m, c in zip(ms, calls)][:4]
 
 
-def cpu_baseline_decode(env, wl, out_gpu, x_bits, budget_s=20.0):
-    """Float64 oracle on the host: full-prefix recompute of the newest row for as many
-    sequences as fit the time budget; also returns the parity of those rows."""
-    from incremental_kv_cache_amd import synth
-    from oracle import attention as A
+def _cores():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count() or 1
-    D, H = env["D"], wl["H"]
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_decode(env, wl, out_gpu, x_bits, budget_s=20.0):
+    """Float64 oracle on the host, for as many sequences as fit the time budget:
+    the full-prefix recompute of the newest row (projection of all t rows plus the
+    newest row's attention) and the oracle's own cached step (project the new row,
+    attend over its float64 cache of the t-1 retained rows, append).  Returns the
+    baseline record and the worst difference of those rows from the GPU output."""
+    from incremental_kv_cache_amd import synth
+    from oracle import attention as A
+    D, H, dh = env["D"], wl["H"], wl["dh"]
     w = [synth.bf16_bits_to_f64(b) for b in env["weights_bits"]]
-    done, t_work, worst = 0, 0.0, 0.0
+    done, t_full, t_inc, worst = 0, 0.0, 0.0, 0.0
     for b in range(wl["B"]):
         s = env["start"][b]
         prefix = synth.bf16_bits_to_f64(synth.round_to_bf16_bits(
             synth.hidden_rows(SEED, synth.STREAM_PREFIX_X, b, 0, s, D, wl["C"])))
-        rows = np.concatenate([prefix, synth.bf16_bits_to_f64(x_bits[b])])
+        x_new = synth.bf16_bits_to_f64(x_bits[b])
+        rows = np.concatenate([prefix, x_new])
         t0 = time.perf_counter()
         ref = A.full_prefix_decode(rows, *w, heads=H)
-        t_work += time.perf_counter() - t0
-        worst = max(worst, float(np.max(np.abs(out_gpu[b] - ref["out"]))))
+        t_full += time.perf_counter() - t0
+        cache = A.DecodeCache(H, dh, s + 1)
+        cache.keys[:, :s] = ref["keys"][:, :s]
+        cache.values[:, :s] = ref["values"][:, :s]
+        cache.positions[:s] = np.arange(s)
+        cache.len = cache.next_position = s
+        t0 = time.perf_counter()
+        inc, _, _ = A.incremental_step(cache, x_new[0], *w, heads=H)
+        t_inc += time.perf_counter() - t0
+        worst = max(worst, float(np.max(np.abs(out_gpu[b] - ref["out"]))),
+                    float(np.max(np.abs(out_gpu[b] - inc))))
         done += 1
-        if t_work >= budget_s:
+        if t_full + t_inc >= budget_s:
             break
-    return {"value": done / t_work, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"float64 full-prefix recompute (projection of all t rows + newest-row attention) "
-                      f"for sequences 0..{done - 1} of {wl['B']} (t = "
-                      f"{', '.join(str(env['start'][b] + 1) for b in range(done))}), {t_work:.1f}s of CPU work"}, \
-        worst, done
+    return {"value": done / t_inc, "unit": "tokens/s", "cores": int(_cores()), "kind": "oracle",
+            "sample": f"float64 oracle cached step (new-row projection + attention over its float64 cache + "
+                      f"append) for sequences 0..{done - 1} of {wl['B']} (t = "
+                      f"{', '.join(str(env['start'][b] + 1) for b in range(done))}), {t_inc:.2f}s of CPU work",
+            "full_prefix_recompute": {"value": done / t_full, "unit": "tokens/s",
+                                      "sample": f"same sequences, projection of all t rows + newest-row "
+                                                f"attention, {t_full:.1f}s of CPU work"}}, worst, done
+
+
+def cpu_baseline_chunk(env, wl, out_gpu, x_bits, budget_rows=512):
+    """Float64 oracle suffix chunk for the sequence with the shortest cut: its retained
+    rows go into an oracle cache (untimed), then the oracle's continue_chunk computes
+    the chunk rows (timed).  Returns the baseline record and the worst difference
+    from the GPU rows."""
+    from incremental_kv_cache_amd import synth
+    from oracle import attention as A
+    D, H, dh = env["D"], wl["H"], wl["dh"]
+    w = [synth.bf16_bits_to_f64(b) for b in env["weights_bits"]]
+    b = int(np.argmin(env["start"]))
+    cut = env["start"][b]
+    n = min(budget_rows, wl["n"])
+    prefix = synth.bf16_bits_to_f64(synth.round_to_bf16_bits(
+        synth.hidden_rows(SEED, synth.STREAM_PREFIX_X, b, 0, cut, D, wl["C"])))
+    pre = A.causal_layer(prefix, *w, heads=H, rows=[])
+    cache = A.DecodeCache(H, dh, cut + n)
+    cache.keys[:, :cut] = pre["keys"]
+    cache.values[:, :cut] = pre["values"]
+    cache.positions[:cut] = np.arange(cut)
+    cache.len = cache.next_position = cut
+    xn = synth.bf16_bits_to_f64(x_bits[b, :n])
+    t0 = time.perf_counter()
+    out, _ = A.continue_chunk(cache, xn, *w, heads=H)
+    dt = time.perf_counter() - t0
+    worst = float(np.max(np.abs(out_gpu[b, :n] - out)))
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(_cores()), "kind": "oracle",
+            "sample": f"float64 oracle continue_chunk of {n} rows on sequence {b} (cut {cut}), "
+                      f"{dt:.1f}s of CPU work"}, worst
+
+
+def achievable_read_gbps(nbytes=4 << 30, reps=10):
+    """Streaming-read bandwidth of a plain read of a 4 GiB buffer (kvc_stream_read),
+    timed with events on the current stream."""
+    import torch
+    from incremental_kv_cache_amd import kvcache as K
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        K.kvc_stream_read(buf, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        K.kvc_stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return gbps
+
+
+def step_percentiles(step, steps):
+    """p10 / p50 / p90 of one step's duration (ms), from events around each step."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"p10": float(np.percentile(ms, 10)), "p50": float(np.percentile(ms, 50)),
+            "p90": float(np.percentile(ms, 90))}
 
 
 def run_decode(name, wl, steps, warmup, cpu):
@@ -219,7 +302,10 @@ def run_decode(name, wl, steps, warmup, cpu):
     K.kvc_sync(cache)
     st = stage_times(cache, step, steps)
     K.kvc_sync(cache)
+    pct = step_percentiles(step, steps)
+    K.kvc_sync(cache)
     torch.cuda.synchronize()
+    achievable = achievable_read_gbps()
     t = [s + 1 for s in start]
     kv_bytes = sum(2 * H * tb * dh * 2 for tb in t)
     attend_ms = st[1]
@@ -234,10 +320,12 @@ def run_decode(name, wl, steps, warmup, cpu):
                                f"fp32 accumulate", "batch": B, "heads": H, "head_width": dh,
                    "capacity": wl["C"], "t_mean": float(np.mean(t)), "seed": SEED},
         "kv_read_GBps": attn_merge_gbps, "kv_read_frac_of_peak": attn_merge_gbps / HBM_PEAK_GBPS,
+        "step_ms_percentiles": pct,
         "stage_ms": {"project": st[0], "attend": st[1], "merge": st[2], "commit": st[3]},
         "roofline": {"bound": "hbm", "kernel": "attend_decode_bf16_kernel", "achieved": att_gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": att_gbps / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(name), "algorithmic_bytes_per_launch": kv_bytes},
+                     "traffic": measured_traffic(name), "algorithmic_bytes_per_launch": kv_bytes,
+                     "achievable_read_GBps": achievable, "frac_of_achievable": att_gbps / achievable},
     }
     out_np = out.double().cpu().numpy()[:, 0]
     if cpu:
@@ -269,6 +357,9 @@ def run_chunk(name, wl, steps, warmup, cpu):
     K.kvc_sync(cache)
     st = stage_times(cache, step, steps)
     K.kvc_sync(cache)
+    pct = step_percentiles(step, steps)
+    K.kvc_sync(cache)
+    torch.cuda.synchronize()
     attn_flops = sum(4 * H * dh * sum(c + i + 1 for i in range(n)) for c in start)
     proj_flops = 2 * B * n * D * 3 * D
     att_tf = attn_flops / (st[1] * 1e-3) / 1e12
@@ -278,12 +369,17 @@ def run_chunk(name, wl, steps, warmup, cpu):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{name}: suffix chunk n={n}, B={B} H={H} d_h={dh} C={wl['C']} "
                                f"cut uniform[0,{wl['cut_max']}], bf16", "cuts": start, "seed": SEED},
+        "step_ms_percentiles": pct,
         "stage_ms": {"project": st[0], "attend": st[1], "merge": st[2], "commit": st[3]},
         "project_TFLOPs": proj_flops / (st[0] * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "kernel": "attend_flash_kernel", "achieved": att_tf,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": att_tf / BF16_PEAK_TFLOPS,
                      "traffic": None, "algorithmic_flops_per_launch": attn_flops},
     }
+    if cpu:
+        cb, worst = cpu_baseline_chunk(env, wl, out.double().cpu().numpy(), bits)
+        res["cpu_baseline"] = cb
+        res["parity"] = {"sequences": 1, "max_abs_err_vs_oracle": worst, "tolerance": 2e-2}
     return res
 
 

@@ -289,6 +289,18 @@ enum { KVC_STAGE_PROJECT = 0, KVC_STAGE_ATTEND = 1, KVC_STAGE_MERGE = 2, KVC_STA
 kvc_status kvc_profile_enable(kvc_cache* cache, int32_t slots);
 kvc_status kvc_profile_read(kvc_cache* cache, float* ms_out, int32_t* calls_out);
 
+/* Measurement helper: reads `bytes` of DEVICE memory at `buf` once with the
+ * decode attention's access shape (contiguous 32 KiB units, 16-byte
+ * non-temporal loads) and discards it, so that timing it gives the
+ * achievable streaming-read bandwidth the decode attention is bound by
+ * (Chapter 37, "From causal attention to managed LLM inference state":
+ * re-reading the retained keys and values is the bandwidth bottleneck).
+ * Launched on `hip_stream` (NULL: the default stream); no synchronisation.
+ * `buf`: 16-byte aligned, `bytes` a positive multiple of 32768; `sink`: DEVICE,
+ * 16 writable bytes (written only for one improbable xor of the data).
+ * Errors: NULL_ARGUMENT, BAD_ARGUMENT (size or alignment), DEVICE. */
+kvc_status kvc_stream_read(const void* buf, int64_t bytes, void* sink, void* hip_stream);
+
 /* Last failure on the calling thread; never NULL. */
 const kvc_error_detail* kvc_last_error(void);
 /* Symbolic name of a status ("KVC_ERR_FULL"); never NULL. */

@@ -29,7 +29,7 @@ HIP_FLAGS = [
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
 
-DEVICE_SOURCES = ["kvc_device.hip", "kvc_decode.hip", "kvc_mfma.hip"]
+DEVICE_SOURCES = ["kvc_device.hip", "kvc_decode.hip", "kvc_mfma.hip", "kvc_probe.hip"]
 HOST_SOURCES = ["kvc_host.cpp"]
 
 

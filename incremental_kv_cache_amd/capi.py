@@ -112,6 +112,7 @@ PROTOTYPES = {
     "kvc_copy_storage": (I32, [P, P, P]),
     "kvc_profile_enable": (I32, [P, I32]),
     "kvc_profile_read": (I32, [P, C.POINTER(C.c_float), PI32]),
+    "kvc_stream_read": (I32, [P, I64, P, P]),
     "kvc_last_error": (C.POINTER(ErrorDetail), []),
     "kvc_status_name": (C.c_char_p, [I32]),
 }

@@ -954,4 +954,17 @@ kvc_status kvc_profile_read(kvc_cache* cache, float* ms_out, int32_t* calls_out)
   return KVC_OK;
 }
 
+kvc_status kvc_stream_read(const void* buf, int64_t bytes, void* sink, void* hip_stream) {
+  reset_detail();
+  if (!buf || !sink) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_stream_read");
+  if (bytes <= 0 || bytes % kProbeUnitBytes != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, kProbeUnitBytes, bytes,
+                   "stream read needs a 16-byte aligned buffer and a positive multiple of %lld bytes",
+                   static_cast<long long>(kProbeUnitBytes));
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "no device kernels in this build");
+  const int rc = dev_stream_read(buf, bytes, sink, hip_stream);
+  if (rc) return device_fail(rc, "stream read launch");
+  return KVC_OK;
+}
+
 }  // extern "C"

@@ -99,6 +99,11 @@ void dev_event_destroy(void* e);
 int dev_event_record(void* e, void* stream);
 int dev_event_elapsed(float* ms, void* start, void* stop);
 
+// Streaming read of `bytes` (a positive multiple of kProbeUnitBytes) at `buf`;
+// `sink` receives a store only for one improbable xor of the data.
+constexpr int64_t kProbeUnitBytes = 32768;
+int dev_stream_read(const void* buf, int64_t bytes, void* sink, void* stream);
+
 // True when the backend can run kernels (false in the CPU-only host-check build).
 bool dev_has_kernels();
 

@@ -276,6 +276,16 @@ def kvc_profile_read(cache: Cache):
     return list(ms), list(calls)
 
 
+def kvc_stream_read(buf, sink, stream=None, *, lib=None) -> None:
+    """Launches one streaming read of the whole contiguous device tensor ``buf`` on
+    ``stream`` (default: torch's current stream); ``sink`` is a >= 16-byte device tensor."""
+    lib = _lib(lib)
+    if stream is None:
+        stream = _torch().cuda.current_stream().cuda_stream
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib, lib.kvc_stream_read(_dev_ptr(buf), nbytes, _dev_ptr(sink), C.c_void_p(stream or 0)))
+
+
 def kvc_lcp_cut(cached, query, *, lib=None) -> int:
     lib = _lib(lib)
     a = np.ascontiguousarray(np.asarray(cached, dtype=np.int32))

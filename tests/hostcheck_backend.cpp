@@ -81,6 +81,7 @@ int dev_event_elapsed(float* ms, void*, void*) {
   *ms = 0.f;
   return 0;
 }
+int dev_stream_read(const void*, int64_t, void*, void*) { return 1; }
 bool dev_has_kernels() { return false; }
 
 }  // namespace kvc

@@ -150,3 +150,19 @@ def test_revision_mismatch_survives_reset_and_bad_cut():
     _rejected_unchanged(lambda: K.kvc_append_and_attend(layer, c, x), c, "KVC_ERR_CACHE_LAYER_REVISION_MISMATCH")
     fresh = K.kvc_cache_create(layer, 1, 4)
     K.kvc_append_and_attend(layer, fresh, x)
+
+
+def test_stream_read_probe_reads_the_buffer():
+    """The bandwidth probe reads every unit: a buffer whose first thread's words xor to
+    the probe's marker makes it store the marker; an all-zero buffer leaves the sink."""
+    import torch
+    buf = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    K.kvc_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert sink.tolist() == [0, 0, 0, 0]
+    marker = np.array([0x9E3779B9], dtype=np.uint32).view(np.int32)[0]
+    buf[(1 << 20) - 8192] = int(marker)  # first word of the last 32 KiB unit
+    K.kvc_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert sink.tolist() == [int(marker), 0, 0, 0]

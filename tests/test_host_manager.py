@@ -237,3 +237,17 @@ def test_null_arguments(lib):
     assert lib.kvc_append_and_attend(None, None, None, 3, None, None, 0, None) == capi.KVC_ERR_NULL_ARGUMENT
     out = C.c_int64()
     assert lib.kvc_lcp_cut(None, 2, None, 1, C.byref(out)) == capi.KVC_ERR_NULL_ARGUMENT
+
+
+def test_stream_read_argument_checks(lib):
+    """The bandwidth probe checks its arguments on the host before any launch."""
+    buf = C.c_void_p(4096)
+    sink = C.c_void_p(8192)
+    assert lib.kvc_stream_read(None, 32768, sink, None) == capi.KVC_ERR_NULL_ARGUMENT
+    assert lib.kvc_stream_read(buf, 32768, None, None) == capi.KVC_ERR_NULL_ARGUMENT
+    assert lib.kvc_stream_read(buf, 0, sink, None) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_stream_read(buf, 32768 + 16, sink, None) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_stream_read(C.c_void_p(4100), 32768, sink, None) == capi.KVC_ERR_BAD_ARGUMENT
+    d = lib.kvc_last_error().contents
+    assert (d.expected, d.actual) == (32768, 32768)
+    assert lib.kvc_stream_read(buf, 65536, sink, None) == capi.KVC_ERR_DEVICE  # no kernels in this build
