@@ -581,7 +581,7 @@ int dev_set_rows(const DevState& s, const int32_t* vals) {
 
 int mfma_project(const DevState& s, const void* x, int n_max, int per_seq_rows);
 int mfma_output_project(const DevState& s, int n_max, int per_seq_rows);
-int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out);
+int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, const ChunkOrder& order, void* out);
 int fast_attend_decode(const DevState& s, void* out);
 int fast_merge_decode(const DevState& s, void* out);
 
@@ -621,8 +621,8 @@ int dev_merge_decode(const DevState& s, void* out) {
   return dispatch<MergeDecode>(s.dtype, s.head_width, s, out);
 }
 
-int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out) {
-  const int rc = mfma_attend_chunk(s, n_max, per_seq_rows, out);
+int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, const ChunkOrder& order, void* out) {
+  const int rc = mfma_attend_chunk(s, n_max, per_seq_rows, order, out);
   if (rc >= 0) return rc;
   return dispatch<AttendChunk>(s.dtype, s.head_width, s, n_max, per_seq_rows, out);
 }

@@ -68,7 +68,27 @@ struct kvc_cache {
   ErrWords* err_host = nullptr;  // pinned readback
   int64_t storage_bytes = 0;
   Profile prof;
+  ChunkOrder order{};  // work order of the last chunk call
 };
+
+void kvc::build_chunk_order(ChunkOrder* o, int batch, int n_max, const int32_t* len, const int32_t* rows) {
+  o->qtiles = (n_max + kChunkQueryTile - 1) / kChunkQueryTile;
+  o->count = 0;
+  if (int64_t(batch) * o->qtiles > kMaxChunkOrder) return;
+  // (keys read by the tile's last query, item); a stable sort keeps equal
+  // items in sequence order
+  std::vector<std::pair<int64_t, int32_t>> w;
+  for (int b = 0; b < batch; ++b) {
+    const int n_b = rows ? rows[b] : n_max;
+    for (int qt = 0; qt * kChunkQueryTile < n_b; ++qt) {
+      const int64_t keys = int64_t(len[b]) + std::min(n_b, (qt + 1) * kChunkQueryTile);
+      w.emplace_back(keys, (b << 16) | qt);
+    }
+  }
+  std::stable_sort(w.begin(), w.end(), [](const auto& a, const auto& c) { return a.first > c.first; });
+  for (size_t k = 0; k < w.size(); ++k) o->item[k] = w[k].second;
+  o->count = int32_t(w.size());
+}
 
 namespace {
 
@@ -310,7 +330,12 @@ kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_row
   // output projection follows
   void* heads = s.wo ? s.merged : out;
   profile_mark(c, KVC_STAGE_ATTEND, 0);
-  rc = decode ? dev_attend_decode(s, heads) : dev_attend_chunk(s, n_max, per_seq, heads);
+  if (decode) {
+    rc = dev_attend_decode(s, heads);
+  } else {
+    build_chunk_order(&c->order, c->batch, n_max, c->len.data(), per_seq ? n_rows : nullptr);
+    rc = dev_attend_chunk(s, n_max, per_seq, c->order, heads);
+  }
   profile_mark(c, KVC_STAGE_ATTEND, 1);
   if (rc) return device_fail(rc, "attention launch");
   if (decode) {

@@ -89,7 +89,23 @@ int dev_set_rows(const DevState& s, const int32_t* vals);
 int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows);
 int dev_attend_decode(const DevState& s, void* out);
 int dev_merge_decode(const DevState& s, void* out);
-int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out);
+// Work items of the bf16 chunk attention kernel: one per (sequence, tile of
+// kChunkQueryTile chunk rows), listed with the most keys to read first, so
+// that the longest items start early and the ragged tail is short.  With more
+// items than the table holds, count is 0 and the kernel walks sequences in
+// order (query tiles from the last one down).
+constexpr int kChunkQueryTile = 128;
+constexpr int kMaxChunkOrder = 256;
+struct ChunkOrder {
+  int32_t count;                 // items listed (0: natural order)
+  int32_t qtiles;                // query tiles per sequence, ceil(n_max / kChunkQueryTile)
+  int32_t item[kMaxChunkOrder];  // (sequence << 16) | query tile
+};
+// Fills `o` for a chunk call: rows[b] chunk rows and len[b] retained rows of
+// sequence b (the work estimate only orders items; every item with rows is
+// listed exactly once).
+void build_chunk_order(ChunkOrder* o, int batch, int n_max, const int32_t* len, const int32_t* rows);
+int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, const ChunkOrder& order, void* out);
 // out[b, i, :] = merged[b, i, :] x W_o (rows i < n_b).
 int dev_output_project(const DevState& s, int n_max, int per_seq_rows, void* out);
 int dev_commit(const DevState& s, int n_max, int per_seq_rows);

@@ -309,28 +309,67 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT
 }
 
 // ---------------------------------------------------------- flash attention --
-// Block (qt, h, b): chunk queries 128 qt .. +128 of lane (b, h), 32 per wave.
-// Virtual key j < len is cache row j, else chunk row j - len; query i sees
-// j <= len + i.  Scores are formed transposed (S^T = K Q^T) so that a lane
-// holds every score of one query: the softmax scale factor is per lane, and
-// the probabilities are already in the operand layout of O^T += V^T P^T.
+// Block = one work item (sequence b, chunk queries 128 qt .. +128) of head h:
+// 32 queries per wave.  Virtual key j < len is cache row j, else chunk row
+// j - len; query i sees j <= len + i.  Scores are formed transposed
+// (S^T = K Q^T) so that a lane holds every score of one query: the softmax
+// scale factor is per lane, and the probabilities are already in the operand
+// layout of O^T += V^T P^T.
+//
+// Keys and values pass through LDS in tiles of 64 rows, double-buffered: the
+// next tile's rows are loaded into registers (16 lanes per 256-byte row, so a
+// load instruction covers whole rows) while the current tile is multiplied,
+// then written to the other buffer, with one barrier per tile.  V stays
+// row-major in LDS; the V^T operand comes from the transposing LDS read
+// (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte pieces addressed by lanes i / 4 + 4 m, m = 0..3, so
+// lanes addressing (key kb + j / 4, features d0 + 4 (j % 4) ..) hand lane i
+// feature d0 + i of keys kb .. kb + 3.
+//
+// Softmax: base 2 with the scale folded into q; the running maximum is only
+// raised (and the accumulators rescaled) when a score exceeds it by more than
+// 2^8, so probabilities stay below 256 and most tiles skip the rescale.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(const_cast<bf16_t*>(p)));
+  return __builtin_bit_cast(uint2, v);
+}
+
 template <int DH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_flash_kernel(DevState s, int n_max, int per_seq_rows,
-                                                           float* __restrict__ out) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_flash_kernel(
+    DevState s, int n_max, int per_seq_rows, ChunkOrder order, float* __restrict__ out) {
   constexpr int KT = 64;
-  constexpr int LDK = DH + 8;
-  constexpr int LDV = KT + 8;  // V^T row stride: V is stored transposed, [d][key]
+  constexpr int LDK = DH + 8;   // K row stride: conflict-free 16-byte fragment reads
+  constexpr int LDV = DH + 16;  // V row stride: conflict-free transposing reads
   constexpr int DSTEPS = DH / 16;
   constexpr int DTILES = DH / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[KT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[DH * LDV];
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  constexpr int CPR = DH / 8;        // 16-byte pieces per row
+  constexpr int RPI = 256 / CPR;     // rows covered by one load of the workgroup
+  constexpr int PIECES = KT / RPI;   // pieces per thread per tile, each of K and V
+  constexpr float kRescale = 8.f;    // log2 of the largest probability kept unscaled
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * LDK];
+  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * LDV];
+
+  const int H = s.heads;
+  const int item = blockIdx.x / H;
+  const int h = blockIdx.x - item * H;
+  int b, qt;
+  if (order.count) {
+    b = order.item[item] >> 16;
+    qt = order.item[item] & 0xffff;
+  } else {
+    b = item / order.qtiles;
+    qt = order.qtiles - 1 - (item - b * order.qtiles);
+  }
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
   if (qt * 128 >= n_b) return;
   const int C = s.capacity;
   const int len = min(max(s.len[b], 0), C);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int g = lane >> 5;
   const int c32 = lane & 31;
   const int qi = qt * 128 + wave * 32 + c32;
@@ -338,7 +377,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int limit = len + qi_eff;
   const int i_max = min(qt * 128 + 127, n_b - 1);
   const int total = len + i_max + 1;
-  const size_t lane_id = size_t(b) * s.heads + h;
+  const int ntiles = (total + KT - 1) / KT;
+  const size_t lane_id = size_t(b) * H + h;
   const bf16_t* kc = static_cast<const bf16_t*>(s.keys) + lane_id * C * DH;
   const bf16_t* vc = static_cast<const bf16_t*>(s.values) + lane_id * C * DH;
   const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + lane_id * n_max * DH;
@@ -370,23 +410,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run = -INFINITY, l_run = 0.f;
   const int wave_limit_min = len + min(qt * 128 + wave * 32, n_b - 1);  // smallest limit in the wave
 
-  constexpr int CHUNKS = KT * DH / 8;  // 16-byte pieces per tile
-  for (int j0 = 0; j0 < total; j0 += KT) {
-    __syncthreads();
-#pragma unroll
-    for (int idx = threadIdx.x; idx < CHUNKS; idx += 256) {
-      const int row = idx % KT;  // consecutive threads take consecutive keys of one chunk
-      const int ch = idx / KT;
-      const int j = min(j0 + row, total - 1);
-      const bf16_t* kr = j < len ? kc + size_t(j) * DH : kn + size_t(j - len) * DH;
-      const bf16_t* vr = j < len ? vc + size_t(j) * DH : vn + size_t(j - len) * DH;
-      *reinterpret_cast<uint4*>(&Ks[row * LDK + ch * 8]) = reinterpret_cast<const uint4*>(kr)[ch];
-      Frag8 vv;
-      vv.u = reinterpret_cast<const uint4*>(vr)[ch];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(ch * 8 + e) * LDV + row] = vv.h[e];
+  // global -> register -> LDS staging: thread loads piece lch of rows lrow + RPI k
+  const int lrow = tid / CPR;
+  const int lch = tid - lrow * CPR;
+  static_assert(PIECES == 2 || PIECES == 4, "tile staging assumes 2 or 4 pieces per thread");
+  // staged pieces in named registers (an indexed array here is kept in scratch memory)
+  uint4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
+  // tile of contiguous rows (all cache rows, or all chunk rows): loads into registers
+  auto contiguous = [&](int j0) { return j0 + KT <= len || (j0 >= len && j0 + KT <= total); };
+  auto fetch = [&](int j0) {
+    const bool cached = j0 + KT <= len;
+    const size_t r0 = size_t(cached ? j0 : j0 - len) + lrow;
+    const uint4* kp = reinterpret_cast<const uint4*>((cached ? kc : kn) + r0 * DH + lch * 8);
+    const uint4* vp = reinterpret_cast<const uint4*>((cached ? vc : vn) + r0 * DH + lch * 8);
+    constexpr int STRIDE = RPI * DH / 8;  // uint4 between a thread's pieces
+    pk0 = kp[0];
+    pv0 = vp[0];
+    pk1 = kp[STRIDE];
+    pv1 = vp[STRIDE];
+    if constexpr (PIECES == 4) {
+      pk2 = kp[2 * STRIDE];
+      pv2 = vp[2 * STRIDE];
+      pk3 = kp[3 * STRIDE];
+      pv3 = vp[3 * STRIDE];
     }
-    __syncthreads();
+  };
+  auto stash = [&](int buf) {
+    uint4* kd = reinterpret_cast<uint4*>(&Ks[buf][lrow * LDK + lch * 8]);
+    uint4* vd = reinterpret_cast<uint4*>(&Vs[buf][lrow * LDV + lch * 8]);
+    constexpr int KS = RPI * LDK / 8, VS = RPI * LDV / 8;
+    kd[0] = pk0;
+    vd[0] = pv0;
+    kd[KS] = pk1;
+    vd[VS] = pv1;
+    if constexpr (PIECES == 4) {
+      kd[2 * KS] = pk2;
+      vd[2 * VS] = pv2;
+      kd[3 * KS] = pk3;
+      vd[3 * VS] = pv3;
+    }
+  };
+  // a tile across the cache end or past the last key (rows after it repeat the
+  // last key, which the mask hides): loaded row by row straight into LDS
+  auto fetch_mixed = [&](int j0, int buf) {
+#pragma unroll
+    for (int k = 0; k < PIECES; ++k) {
+      const int j = min(j0 + lrow + k * RPI, total - 1);
+      const size_t off = size_t(j < len ? j : j - len) * DH + lch * 8;
+      const uint4 kk = *reinterpret_cast<const uint4*>((j < len ? kc : kn) + off);
+      const uint4 vv = *reinterpret_cast<const uint4*>((j < len ? vc : vn) + off);
+      *reinterpret_cast<uint4*>(&Ks[buf][(lrow + k * RPI) * LDK + lch * 8]) = kk;
+      *reinterpret_cast<uint4*>(&Vs[buf][(lrow + k * RPI) * LDV + lch * 8]) = vv;
+    }
+  };
+  // transposing-read address of this lane within a V tile (see above)
+  const int li = lane & 15;
+  const int vlane = (4 * g + (li >> 2)) * LDV + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+
+  if (contiguous(0)) {
+    fetch(0);
+    stash(0);
+  } else {
+    fetch_mixed(0, 0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = it * KT;
+    const int buf = it & 1;
+    // the other buffer was last read before the previous barrier: fill it now
+    // (contiguous tiles land in registers first and are written after this tile)
+    const bool more = it + 1 < ntiles;
+    const bool staged = more && contiguous(j0 + KT);
+    if (staged) {
+      fetch(j0 + KT);
+    } else if (more) {
+      fetch_mixed(j0 + KT, buf ^ 1);
+    }
 
     f32x16_t st[2];
 #pragma unroll
@@ -396,7 +495,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int u = 0; u < DSTEPS; ++u) {
         Frag8 a;
-        a.u = *reinterpret_cast<const uint4*>(&Ks[(kt * 32 + c32) * LDK + 16 * u + 8 * g]);
+        a.u = *reinterpret_cast<const uint4*>(&Ks[buf][(kt * 32 + c32) * LDK + 16 * u + 8 * g]);
         st[kt] = mfma32(a.v, qf[u].v, st[kt]);
       }
     }
@@ -416,28 +515,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[kt][r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    // rescale only when some lane's running maximum moved
-    if (__any(m_new > m_run)) {
-      const float corr = exp2f(m_run - m_new);
+    if (__any(tmax > m_run + kRescale)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float corr = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
       l_run *= corr;
 #pragma unroll
       for (int t = 0; t < DTILES; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] *= corr;
+      m_run = m_new;
     }
-    m_run = m_new;
-    float psum = 0.f;
+    const float mref = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = exp2f(st[kt][r] - m_new);
+        // v_exp_f32 directly: probabilities below 2^-126 flush to zero
+        const float pr = __builtin_amdgcn_exp2f(st[kt][r] - mref);
         st[kt][r] = pr;
-        psum += pr;
+        l_run += pr;
       }
-    psum += __shfl_xor(psum, 32, 64);
-    l_run += psum;
+    const bf16_t* vt = &Vs[buf][vlane];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -445,21 +543,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         Frag8 pb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb.v[e] = (__bf16)st[kt][8 * u + e];
-        const int kb = kt * 32 + 16 * u + 4 * g;
+        // keys kt*32 + 16u + 4g + {0..3} and + {8..11} of feature t*32 + c32
+        const int krow = (kt * 32 + 16 * u) * LDV;
 #pragma unroll
         for (int t = 0; t < DTILES; ++t) {
-          // keys kb + {0..3} and kb + {8..11} of feature row t * 32 + c32
-          const bf16_t* vrow = &Vt[(t * 32 + c32) * LDV + kb];
           union {
             uint2 h[2];
             bf16x8_t v;
           } a;
-          a.h[0] = *reinterpret_cast<const uint2*>(vrow);
-          a.h[1] = *reinterpret_cast<const uint2*>(vrow + 8);
+          a.h[0] = lds_read_tr16(vt + krow + t * 32);
+          a.h[1] = lds_read_tr16(vt + krow + 8 * LDV + t * 32);
           o[t] = mfma32(a.v, pb.v, o[t]);
         }
       }
+    if (staged) stash(buf ^ 1);
+    __syncthreads();
   }
+  l_run += __shfl_xor(l_run, 32, 64);
   if (qi < n_b) {
     const float inv = 1.f / l_run;
     float* orow = out + (size_t(b) * n_max + qi) * s.model_width + size_t(h) * DH;
@@ -526,14 +626,16 @@ int mfma_output_project(const DevState& s, int n_max, int per_seq_rows) {
   return mfma_project_t(s, static_cast<const float*>(s.merged), n_max, per_seq_rows, 3, 1);
 }
 
-int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, void* out) {
+int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, const ChunkOrder& order, void* out) {
   if (s.dtype != KVC_BF16) return -1;
-  dim3 grid((n_max + 127) / 128, s.heads, s.batch);
+  const int items = order.count ? order.count : s.batch * order.qtiles;
+  if (items == 0) return 0;
+  const dim3 grid(unsigned(items) * unsigned(s.heads));
   if (s.head_width == 128) {
-    hipLaunchKernelGGL(attend_flash_kernel<128>, grid, dim3(256), 0, st(s.stream), s, n_max, per_seq_rows,
+    hipLaunchKernelGGL(attend_flash_kernel<128>, grid, dim3(256), 0, st(s.stream), s, n_max, per_seq_rows, order,
                        static_cast<float*>(out));
   } else if (s.head_width == 64) {
-    hipLaunchKernelGGL(attend_flash_kernel<64>, grid, dim3(256), 0, st(s.stream), s, n_max, per_seq_rows,
+    hipLaunchKernelGGL(attend_flash_kernel<64>, grid, dim3(256), 0, st(s.stream), s, n_max, per_seq_rows, order,
                        static_cast<float*>(out));
   } else {
     return -1;

@@ -68,7 +68,7 @@ int dev_set_rows(const DevState& s, const int32_t* vals) {
 int dev_project(const DevState&, const void*, int, int) { return 1; }
 int dev_attend_decode(const DevState&, void*) { return 1; }
 int dev_merge_decode(const DevState&, void*) { return 1; }
-int dev_attend_chunk(const DevState&, int, int, void*) { return 1; }
+int dev_attend_chunk(const DevState&, int, int, const ChunkOrder&, void*) { return 1; }
 int dev_output_project(const DevState&, int, int, void*) { return 1; }
 int dev_commit(const DevState&, int, int) { return 1; }
 int dev_event_create(void** e) {

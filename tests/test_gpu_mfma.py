@@ -89,3 +89,53 @@ def test_flash_chunk_prefill_matches_causal_reference():
     out_chunk, _ = K.kvc_continue_chunk(layer, cache, x_dev)
     ref = A.causal_layer(x[0], *w, heads=H)["out"]
     assert_parity(to_f64(out_chunk)[0], ref, "bf16", "chunk")
+
+
+def test_flash_chunk_more_items_than_the_order_table():
+    """260 sequences x one query tile is more work items than the host's
+    heaviest-first table holds: the kernel walks them in sequence order, and every
+    ragged sequence (0..16 chunk rows over 0..30 retained rows) still matches."""
+    H, dh, B, n_max, cap = 2, 64, 260, 16, 48
+    D = H * dh
+    layer, w = make_layer(29, D, H, "bf16", max_positions=cap)
+    cache = K.kvc_cache_create(layer, B, cap, max_chunk_rows=32)
+    cuts = [int(c) for c in synth.uniform_int(29, synth.STREAM_LENGTHS, B, 0, 30)]
+    rows = [int(r) for r in synth.uniform_int(31, synth.STREAM_LENGTHS, B, 0, n_max)]
+    xp_dev, xp = hidden(29, synth.STREAM_PREFIX_X, B, 30, D, "bf16")
+    K.kvc_continue_chunk(layer, cache, xp_dev, n_rows=cuts)
+    xn_dev, xn = hidden(29, synth.STREAM_X, B, n_max, D, "bf16")
+    out, _ = K.kvc_continue_chunk(layer, cache, xn_dev, n_rows=rows)
+    o = to_f64(out)
+    for b in range(B):
+        if rows[b]:
+            seq = np.concatenate([xp[b, : cuts[b]], xn[b, : rows[b]]])
+            ref = A.causal_layer(seq, *w, heads=H, rows=range(cuts[b], cuts[b] + rows[b]))
+            assert_parity(o[b, : rows[b]], ref["out"], "bf16", f"seq {b}")
+        assert not np.any(o[b, rows[b]:])
+
+
+def test_flash_chunk_rescales_when_scores_rise():
+    """Scores that climb by more than 2^8 from one key tile to the next force the
+    running maximum up twice (retained keys 0..63 score about -10 in base 2, keys
+    64..149 about 0, the chunk's own keys about +10): identity projections without
+    rotation, so the oracle sees exactly these scores."""
+    import torch
+    H, dh, cut, n = 2, 128, 150, 40
+    D = H * dh
+    eye = torch.eye(D, dtype=torch.bfloat16, device="cuda")
+    params = K.kvc_params_create(eye, eye.clone(), eye.clone())
+    layer = K.kvc_layer_create(params, H, K.KVC_POS_NONE, 10000.0, 256)
+    cache = K.kvc_cache_create(layer, 1, 256, max_chunk_rows=256)
+    a = np.sqrt(10.0 * np.sqrt(dh) / 1.4426950408889634)  # a^2 / sqrt(d_h) = 10 / log2(e)
+    e = np.full(D, a / np.sqrt(dh))
+    noise = 0.3 * synth.normal(41, synth.STREAM_X, (cut + n, D))
+    x = noise.copy()
+    x[:64] -= e
+    x[cut:] += e
+    s, xf = synth.quantize(x, "bf16")
+    xd = torch.from_numpy(s.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    K.kvc_continue_chunk(layer, cache, xd[None, :cut].contiguous())
+    out, _ = K.kvc_continue_chunk(layer, cache, xd[None, cut:].contiguous())
+    w = np.eye(D)
+    ref = A.causal_layer(xf, w, w, w, heads=H, rope=False, rows=range(cut, cut + n))
+    assert_parity(to_f64(out)[0], ref["out"], "bf16", "rising scores")
