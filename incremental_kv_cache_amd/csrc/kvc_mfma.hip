@@ -19,6 +19,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "kvc_dev_util.h"
 #include "kvc_internal.h"
@@ -56,56 +57,152 @@ __device__ __forceinline__ void load16(const float* p, uint4& lo, uint4& hi) {
   hi = pack8(q[2], q[3]);
 }
 
+// Where output row m of a call lands: sequence b, chunk row i (i < 0: past M
+// or past the sequence's rows, nothing stored) and, for rotated projections,
+// the rotary position next_position + i.  A position past the rotary table is
+// recorded in bad_pos (smallest sequence index) and rotates as position 0.
+struct RowDst {
+  int b, i, pos;
+};
+__device__ __forceinline__ RowDst row_dst(const DevState& s, int p, int m, int M, int n_max, int per_seq_rows,
+                                          unsigned long long& bad_pos) {
+  RowDst d{0, -1, 0};
+  if (m >= M) return d;
+  d.b = m / n_max;
+  const int i = m - d.b * n_max;
+  const int n_b = per_seq_rows ? s.rows[d.b] : n_max;
+  if (i >= n_b) return d;
+  d.i = i;
+  if (p < 2 && s.rope) {
+    d.pos = s.next_pos[d.b] + i;
+    if (d.pos < 0 || d.pos >= s.max_positions) {
+      bad_pos = min(bad_pos, (unsigned long long)d.b);
+      d.pos = 0;
+    }
+  }
+  return d;
+}
+
 // Rotates (if needed) and stores rotary pair `pair` (global pair index within
-// projection p: head pair / half, feature pair % half) of row m.
-__device__ __forceinline__ void store_pair(const DevState& s, int p, int m, int pair, float lo, float hi, int M,
-                                           int n_max, int per_seq_rows) {
-  if (m >= M) return;
-  const int b = m / n_max;
-  const int i = m - b * n_max;
-  const int n_b = per_seq_rows ? s.rows[b] : n_max;
-  if (i >= n_b) return;
+// projection p: head pair / half, feature pair % half) of a row; the smallest
+// flat index of a non-finite stored value goes to `bad`.
+__device__ __forceinline__ void put_pair(const DevState& s, int p, const RowDst& d, int pair, float lo, float hi,
+                                         int n_max, unsigned long long& bad) {
+  if (d.i < 0) return;
   const int dh = s.head_width;
   const int half = dh >> 1;
   const int h = pair / half;
   const int f = pair - h * half;
-  if (p == 3) {  // output projection: plain columns h*d_h + f and + d_h/2 of row m
-    float* o = static_cast<float*>(s.out_proj_dst) + size_t(m) * s.model_width + size_t(h) * dh + f;
+  if (p == 3) {  // output projection: plain columns h*d_h + f and + d_h/2 of the row
+    const size_t flat = (size_t(d.b) * n_max + d.i) * s.model_width + size_t(h) * dh + f;
+    float* o = static_cast<float*>(s.out_proj_dst) + flat;
     o[0] = lo;
     o[half] = hi;
-    if (!isfinite(lo)) flag_min(&s.err->output, size_t(m) * s.model_width + size_t(h) * dh + f);
-    if (!isfinite(hi)) flag_min(&s.err->output, size_t(m) * s.model_width + size_t(h) * dh + f + half);
+    if (!isfinite(lo)) bad = min(bad, (unsigned long long)flat);
+    if (!isfinite(hi)) bad = min(bad, (unsigned long long)(flat + half));
     return;
   }
   float r0 = lo, r1 = hi;
   if (p < 2 && s.rope) {
-    int pos = s.next_pos[b] + i;
-    if (pos < 0 || pos >= s.max_positions) {
-      flag_min(&s.err->position, (unsigned long long)b);
-      pos = 0;
-    }
-    const float c = static_cast<const float*>(s.rope_cos)[size_t(pos) * half + f];
-    const float sn = static_cast<const float*>(s.rope_sin)[size_t(pos) * half + f];
+    const float c = static_cast<const float*>(s.rope_cos)[size_t(d.pos) * half + f];
+    const float sn = static_cast<const float*>(s.rope_sin)[size_t(d.pos) * half + f];
     r0 = lo * c - hi * sn;
     r1 = hi * c + lo * sn;
   }
-  const size_t flat0 = (size_t(b * s.heads + h) * n_max + i) * dh + f;
+  const size_t flat0 = (size_t(d.b * s.heads + h) * n_max + d.i) * dh + f;
   const size_t flat1 = flat0 + half;
   if (p == 0) {
     float* q = static_cast<float*>(s.q);
     q[flat0] = r0;
     q[flat1] = r1;
-    if (!isfinite(r0)) flag_min(&s.err->query, flat0);
-    if (!isfinite(r1)) flag_min(&s.err->query, flat1);
+    if (!isfinite(r0)) bad = min(bad, (unsigned long long)flat0);
+    if (!isfinite(r1)) bad = min(bad, (unsigned long long)flat1);
   } else {
     bf16_t* dst = static_cast<bf16_t*>(p == 1 ? s.cand_k : s.cand_v);
     const bf16_t t0 = f32_to_bf16(r0), t1 = f32_to_bf16(r1);
     dst[flat0] = t0;
     dst[flat1] = t1;
-    unsigned long long* word = p == 1 ? &s.err->key : &s.err->value;
-    if (!isfinite(bf16_to_f32(t0))) flag_min(word, flat0);
-    if (!isfinite(bf16_to_f32(t1))) flag_min(word, flat1);
+    if (!isfinite(bf16_to_f32(t0))) bad = min(bad, (unsigned long long)flat0);
+    if (!isfinite(bf16_to_f32(t1))) bad = min(bad, (unsigned long long)flat1);
   }
+}
+
+// Publishes a thread's recorded failures to the projection's failure words.
+__device__ __forceinline__ void flush_bad(const DevState& s, int p, unsigned long long bad,
+                                          unsigned long long bad_pos) {
+  if (bad_pos != kErrClear) flag_min(&s.err->position, bad_pos);
+  if (bad != kErrClear)
+    flag_min(p == 0 ? &s.err->query : (p == 1 ? &s.err->key : (p == 2 ? &s.err->value : &s.err->output)), bad);
+}
+
+// Four consecutive pairs pair0 .. pair0 + 3 of one head (pair0 % 4 == 0 and
+// d_h / 2 % 4 == 0): the same as four put_pair calls, with 16-byte (float) or
+// 8-byte (bf16) stores and one table load per rotary factor.
+__device__ __forceinline__ void put_pairs4(const DevState& s, int p, const RowDst& d, int pair0, float4 lo,
+                                           float4 hi, int n_max, unsigned long long& bad) {
+  if (d.i < 0) return;
+  const int dh = s.head_width;
+  const int half = dh >> 1;
+  const int h = pair0 / half;
+  const int f = pair0 - h * half;
+  auto note = [&](const float4& v, size_t flat) {
+    if (!isfinite(v.x)) bad = min(bad, (unsigned long long)flat);
+    else if (!isfinite(v.y)) bad = min(bad, (unsigned long long)(flat + 1));
+    else if (!isfinite(v.z)) bad = min(bad, (unsigned long long)(flat + 2));
+    else if (!isfinite(v.w)) bad = min(bad, (unsigned long long)(flat + 3));
+  };
+  if (p == 3) {
+    const size_t flat = (size_t(d.b) * n_max + d.i) * s.model_width + size_t(h) * dh + f;
+    float* o = static_cast<float*>(s.out_proj_dst) + flat;
+    *reinterpret_cast<float4*>(o) = lo;
+    *reinterpret_cast<float4*>(o + half) = hi;
+    note(lo, flat);
+    note(hi, flat + half);
+    return;
+  }
+  float4 r0 = lo, r1 = hi;
+  if (p < 2 && s.rope) {
+    const float4 c = *reinterpret_cast<const float4*>(static_cast<const float*>(s.rope_cos) + size_t(d.pos) * half + f);
+    const float4 sn = *reinterpret_cast<const float4*>(static_cast<const float*>(s.rope_sin) + size_t(d.pos) * half + f);
+    r0 = make_float4(lo.x * c.x - hi.x * sn.x, lo.y * c.y - hi.y * sn.y, lo.z * c.z - hi.z * sn.z,
+                     lo.w * c.w - hi.w * sn.w);
+    r1 = make_float4(hi.x * c.x + lo.x * sn.x, hi.y * c.y + lo.y * sn.y, hi.z * c.z + lo.z * sn.z,
+                     hi.w * c.w + lo.w * sn.w);
+  }
+  const size_t flat0 = (size_t(d.b * s.heads + h) * n_max + d.i) * dh + f;
+  if (p == 0) {
+    float* q = static_cast<float*>(s.q) + flat0;
+    *reinterpret_cast<float4*>(q) = r0;
+    *reinterpret_cast<float4*>(q + half) = r1;
+    note(r0, flat0);
+    note(r1, flat0 + half);
+  } else {
+    bf16_t* dst = static_cast<bf16_t*>(p == 1 ? s.cand_k : s.cand_v) + flat0;
+    union {
+      uint2 u;
+      bf16_t e[4];
+    } a, c;
+    a.e[0] = f32_to_bf16(r0.x);
+    a.e[1] = f32_to_bf16(r0.y);
+    a.e[2] = f32_to_bf16(r0.z);
+    a.e[3] = f32_to_bf16(r0.w);
+    c.e[0] = f32_to_bf16(r1.x);
+    c.e[1] = f32_to_bf16(r1.y);
+    c.e[2] = f32_to_bf16(r1.z);
+    c.e[3] = f32_to_bf16(r1.w);
+    *reinterpret_cast<uint2*>(dst) = a.u;
+    *reinterpret_cast<uint2*>(dst + half) = c.u;
+    note(make_float4(bf16_to_f32(a.e[0]), bf16_to_f32(a.e[1]), bf16_to_f32(a.e[2]), bf16_to_f32(a.e[3])), flat0);
+    note(make_float4(bf16_to_f32(c.e[0]), bf16_to_f32(c.e[1]), bf16_to_f32(c.e[2]), bf16_to_f32(c.e[3])),
+         flat0 + half);
+  }
+}
+
+__device__ __forceinline__ void store_pair(const DevState& s, int p, int m, int pair, float lo, float hi, int M,
+                                           int n_max, int per_seq_rows) {
+  unsigned long long bad = kErrClear, bad_pos = kErrClear;
+  put_pair(s, p, row_dst(s, p, m, M, n_max, per_seq_rows, bad_pos), pair, lo, hi, n_max, bad);
+  flush_bad(s, p, bad, bad_pos);
 }
 
 // ------------------------------------------------------------ skinny GEMM --
@@ -306,6 +403,205 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT
       const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
       store_pair(s, p, m, pair, acc[i][0][r], acc[i][1][r], M, n_max, per_seq_rows);
     }
+}
+
+// ------------------------------------------------------- wide tiled GEMM --
+// Many bf16 rows (suffix chunks, prefill): 256 x 256 output tiles, one
+// 256-thread workgroup per compute unit, each wave a 128 x 128 quarter held in
+// sixteen 32x32 accumulators, so a 16-wide step reads 8 fragments from LDS for
+// 16 MFMAs.  The 64-wide K tiles of X and W are double-buffered in LDS
+// (144 KB): the next tile is loaded into registers while the current one is
+// multiplied, then written to the other buffer, one barrier per tile.
+// Columns: block virtual column v holds pair pair_base + 32 (v / 64) + v % 32,
+// low feature for (v / 32) even, high feature for odd, so a wave's
+// n-subtiles 2 gi and 2 gi + 1 hold the two halves of the same 32 pairs.
+// Tile order: consecutive tile ids run on one XCD (blocks are dealt to the
+// eight XCDs in turn) and walk 4 row tiles per column step, so the 32 tiles an
+// XCD runs at once share their X and W tiles through its L2.
+constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8, GGROUP = 4;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void project_wide_kernel(
+    DevState s, const bf16_t* __restrict__ x, int M, int n_max, int per_seq_rows, int proj_first, int m_tiles,
+    int n_tiles) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][GBM * GLD];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][GBN * GLD];
+  const int D = s.model_width;
+  const int dh = s.head_width;
+  const int half = dh >> 1;
+  const int tiles = m_tiles * n_tiles;
+  const int L = blockIdx.x;
+  const int t = (tiles & 7) ? L : (L & 7) * (tiles >> 3) + (L >> 3);
+  const int group = t / (GGROUP * n_tiles);
+  const int within = t - group * GGROUP * n_tiles;
+  const int rows_in_group = min(GGROUP, m_tiles - group * GGROUP);
+  const int mt = group * GGROUP + within % rows_in_group;
+  const int nt = within / rows_in_group;
+  const int blocks_per_proj = D / GBN;  // 128 pairs per block
+  const int pt = nt / blocks_per_proj;
+  const int p = proj_first + pt;
+  const int pair_base = (nt - pt * blocks_per_proj) * 128;
+  const int m0 = mt * GBM;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int g = lane >> 5;
+  const int c32 = lane & 31;
+
+  // global -> LDS: thread copies 16 bytes at k-chunk lk of rows lrow + 32 i (i < 8)
+  const int lrow = tid >> 3;
+  const int lk = (tid & 7) * 8;
+  // element offsets of the thread's rows (32-bit: the dispatch checks M * D < 2^31):
+  // X rows lrow + 32 i (clamped to the last row); W rows of virtual columns
+  // lrow + 32 i, where odd i is the high half of even i's pairs (+ d_h / 2 rows)
+  const bf16_t* xg = x + lk;
+  const bf16_t* wg = weight_of(s, p) + lk;
+  int ao[8], bo[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ao[i] = min(m0 + lrow + 32 * i, M - 1) * D;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int vpair = pair_base + 32 * k + lrow;
+    const int vh = vpair / half;
+    bo[k] = (vh * dh + (vpair - vh * half)) * D;
+  }
+  const int hoff = half * D;
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // the staged next K tile: 8 pieces of X and 8 of W per thread, in named
+  // registers (arrays or structs here are kept in scratch memory)
+  uint4 xa0, xa1, xa2, xa3, xa4, xa5, xa6, xa7, xb0, xb1, xb2, xb3, xb4, xb5, xb6, xb7;
+  constexpr int S = 32 * GLD / 8;  // uint4 between a thread's rows in LDS
+#define KVC_FETCH(T, k0)                                     \
+  do {                                                       \
+    T##a0 = *reinterpret_cast<const uint4*>(xg + ao[0] + (k0));   \
+    T##b0 = *reinterpret_cast<const uint4*>(wg + bo[0] + (k0));   \
+    T##a1 = *reinterpret_cast<const uint4*>(xg + ao[1] + (k0));   \
+    T##b1 = *reinterpret_cast<const uint4*>(wg + bo[0] + hoff + (k0));   \
+    T##a2 = *reinterpret_cast<const uint4*>(xg + ao[2] + (k0));   \
+    T##b2 = *reinterpret_cast<const uint4*>(wg + bo[1] + (k0));   \
+    T##a3 = *reinterpret_cast<const uint4*>(xg + ao[3] + (k0));   \
+    T##b3 = *reinterpret_cast<const uint4*>(wg + bo[1] + hoff + (k0));   \
+    T##a4 = *reinterpret_cast<const uint4*>(xg + ao[4] + (k0));   \
+    T##b4 = *reinterpret_cast<const uint4*>(wg + bo[2] + (k0));   \
+    T##a5 = *reinterpret_cast<const uint4*>(xg + ao[5] + (k0));   \
+    T##b5 = *reinterpret_cast<const uint4*>(wg + bo[2] + hoff + (k0));   \
+    T##a6 = *reinterpret_cast<const uint4*>(xg + ao[6] + (k0));   \
+    T##b6 = *reinterpret_cast<const uint4*>(wg + bo[3] + (k0));   \
+    T##a7 = *reinterpret_cast<const uint4*>(xg + ao[7] + (k0));   \
+    T##b7 = *reinterpret_cast<const uint4*>(wg + bo[3] + hoff + (k0));   \
+  } while (0)
+#define KVC_STASH(T, buf)                                                  \
+  do {                                                                     \
+    uint4* ad = reinterpret_cast<uint4*>(&As[buf][lrow * GLD + lk]);       \
+    uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][lrow * GLD + lk]);       \
+    ad[0] = T##a0;                                                         \
+    ad[S] = T##a1;                                                         \
+    ad[2 * S] = T##a2;                                                     \
+    ad[3 * S] = T##a3;                                                     \
+    ad[4 * S] = T##a4;                                                     \
+    ad[5 * S] = T##a5;                                                     \
+    ad[6 * S] = T##a6;                                                     \
+    ad[7 * S] = T##a7;                                                     \
+    bd[0] = T##b0;                                                         \
+    bd[S] = T##b1;                                                         \
+    bd[2 * S] = T##b2;                                                     \
+    bd[3 * S] = T##b3;                                                     \
+    bd[4 * S] = T##b4;                                                     \
+    bd[5 * S] = T##b5;                                                     \
+    bd[6 * S] = T##b6;                                                     \
+    bd[7 * S] = T##b7;                                                     \
+  } while (0)
+  // fragments of one 16-wide step, double-buffered in registers: step ks + 1
+  // is read from LDS while step ks's 16 MFMAs run
+  Frag8 fa[2][4], fb[2][4];
+  auto read_frags = [&](int buf, int ks, int slot) {
+    const bf16_t* ar = &As[buf][(wm * 128 + c32) * GLD + 8 * g + 16 * ks];
+    const bf16_t* br = &Bs[buf][(wn * 128 + c32) * GLD + 8 * g + 16 * ks];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fa[slot][i].u = *reinterpret_cast<const uint4*>(ar + i * 32 * GLD);
+      fb[slot][i].u = *reinterpret_cast<const uint4*>(br + i * 32 * GLD);
+    }
+  };
+  auto multiply = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < GBK / 16; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < GBK / 16) read_frags(buf, ks + 1, cur ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[cur][i].v, fb[cur][j].v, acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the next K tile is loaded into registers while this one is multiplied,
+  // then written to the other LDS buffer
+  const int ktiles = D / GBK;
+  KVC_FETCH(x, 0);
+  KVC_STASH(x, 0);
+  __syncthreads();
+  read_frags(0, 0, 0);
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < ktiles;
+    if (more) KVC_FETCH(x, (kt + 1) * GBK);
+    multiply(buf);
+    if (more) KVC_STASH(x, buf ^ 1);
+    __syncthreads();
+    if (more) read_frags(buf ^ 1, 0, 0);
+  }
+#undef KVC_FETCH
+#undef KVC_STASH
+  // epilogue, one 32-row quarter of the wave's tile at a time, through LDS (the
+  // K-tile buffers are free now).  Lane (row r4, group gi, c4) then handles four
+  // consecutive pairs of rows r4, r4 + 4, ..: 16 lanes cover one row's 64 pairs,
+  // with one rotary table load per factor and 16-byte stores.
+  constexpr int EPS = 128 + 4;  // staging row stride (floats)
+  float* ep = reinterpret_cast<float*>(&As[0][0]) + __builtin_amdgcn_readfirstlane(wave) * 32 * EPS;
+  const int wrow0 = m0 + __builtin_amdgcn_readfirstlane(wm) * 128;
+  const int r4 = lane >> 4;
+  const int gi = (lane >> 3) & 1;
+  const int c4 = (lane & 7) * 4;
+  const int pair0 = pair_base + (2 * __builtin_amdgcn_readfirstlane(wn) + gi) * 32 + c4;
+  unsigned long long bad = kErrClear, bad_pos = kErrClear;
+  // accumulators are only ever indexed by constants (a runtime index would move them to scratch)
+  auto stage = [&](const f32x16_t (&q)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + 4 * g + (r & 3)) * EPS + j * 32 + c32] = q[j][r];
+  };
+#pragma unroll 1
+  for (int i = 0; i < 4; ++i) {
+    switch (i) {
+      case 0: stage(acc[0]); break;
+      case 1: stage(acc[1]); break;
+      case 2: stage(acc[2]); break;
+      default: stage(acc[3]); break;
+    }
+    __syncthreads();
+    // lane c32 finds where row c32 of the quarter lands; the row's lanes fetch it by shuffle
+    const RowDst mine = row_dst(s, p, wrow0 + i * 32 + c32, M, n_max, per_seq_rows, bad_pos);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int row = 4 * k + r4;
+      const RowDst d{__shfl(mine.b, row, 64), __shfl(mine.i, row, 64), __shfl(mine.pos, row, 64)};
+      const float* er = ep + row * EPS + gi * 64 + c4;
+      put_pairs4(s, p, d, pair0, *reinterpret_cast<const float4*>(er), *reinterpret_cast<const float4*>(er + 32),
+                 n_max, bad);
+    }
+    __syncthreads();
+  }
+  flush_bad(s, p, bad, bad_pos);
 }
 
 // ---------------------------------------------------------- flash attention --
@@ -610,6 +906,12 @@ int mfma_project_t(const DevState& s, const XT* xb, int n_max, int per_seq_rows,
         hipLaunchKernelGGL((project_skinny_kernel<0, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
                            per_seq_rows, proj_first);
     }
+  } else if (std::is_same<XT, bf16_t>::value && M >= 2048 && s.model_width % GBN == 0 && s.head_width % 64 == 0 &&
+             int64_t(M) * s.model_width < (int64_t(1) << 31)) {
+    const int m_tiles = (M + GBM - 1) / GBM;
+    const int n_tiles = nproj * (s.model_width / GBN);
+    hipLaunchKernelGGL(project_wide_kernel, dim3(m_tiles * n_tiles), dim3(256), 0, st(s.stream), s,
+                       reinterpret_cast<const bf16_t*>(xb), M, n_max, per_seq_rows, proj_first, m_tiles, n_tiles);
   } else {
     dim3 grid(nproj * (s.model_width / TBN), (M + TBM - 1) / TBM);
     hipLaunchKernelGGL((project_tiled_kernel<XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,

@@ -139,3 +139,37 @@ def test_flash_chunk_rescales_when_scores_rise():
     w = np.eye(D)
     ref = A.causal_layer(xf, w, w, w, heads=H, rope=False, rows=range(cut, cut + n))
     assert_parity(to_f64(out)[0], ref["out"], "bf16", "rising scores")
+
+
+@pytest.mark.parametrize("B,n_max,H,rows,cuts", [
+    # 2250 rows: a partial last row tile, 54 tiles (not a multiple of the eight XCDs)
+    (5, 450, 4, [450, 1, 0, 300, 449], [0, 5, 3, 100, 17]),
+    # 2048 rows, 48 tiles: the XCD-grouped tile order
+    (16, 128, 2, None, [3 * b for b in range(16)]),
+])
+def test_wide_projection_chunk(B, n_max, H, rows, cuts):
+    """Chunks of >= 2048 bf16 rows take the 256 x 256 projection kernel: stored
+    keys and values (rotated at next_position + i) and the attention outputs
+    match the oracle for ragged rows and retained prefixes."""
+    dh = 128
+    D = H * dh
+    cap = max(cuts) + n_max + 8
+    layer, w = make_layer(43, D, H, "bf16", max_positions=cap)
+    cache = K.kvc_cache_create(layer, B, cap, max_chunk_rows=n_max)
+    xp_dev, xp = hidden(43, synth.STREAM_PREFIX_X, B, max(cuts), D, "bf16")
+    K.kvc_continue_chunk(layer, cache, xp_dev, n_rows=cuts)
+    xn_dev, xn = hidden(43, synth.STREAM_X, B, n_max, D, "bf16")
+    out, _ = K.kvc_continue_chunk(layer, cache, xn_dev, n_rows=rows)
+    o = to_f64(out)
+    rows = rows or [n_max] * B
+    for b in range(B):
+        seq = np.concatenate([xp[b, : cuts[b]], xn[b, : rows[b]]])
+        full = A.causal_layer(seq, *w, heads=H, rows=range(cuts[b], cuts[b] + rows[b]))
+        if rows[b]:
+            assert_parity(o[b, : rows[b]], full["out"], "bf16", f"seq {b}")
+        assert not np.any(o[b, rows[b]:])
+        if len(seq):
+            k, v, pos = K.kvc_snapshot(cache, b)
+            assert list(pos) == list(range(len(seq)))
+            assert_parity(storage_f64(k, "bf16"), full["keys"], "bf16", f"keys {b}")
+            assert_parity(storage_f64(v, "bf16"), full["values"], "bf16", f"values {b}")
