@@ -217,6 +217,7 @@ __device__ __forceinline__ void store_pair(const DevState& s, int p, int m, int 
 constexpr int SKC = 128;           // k per chunk
 constexpr int SLDX = SKC + 8;      // LDS row stride (bf16) of the input tile
 constexpr int SUNROLL = 8;         // chunks per statically unrolled group
+constexpr int SRING = 4;           // weight-fragment ring (chunks in flight + 1); divides SUNROLL
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -253,46 +254,58 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const X
 
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   const int nch = NCH > 0 ? NCH : D / SKC;
-  Frag8 b[4];
+  // weight fragments and input chunks are loaded SRING - 1 chunks ahead of the
+  // multiply, into rings indexed by chunk % SRING (static: chunks are unrolled
+  // in groups of SUNROLL).  The two streams share the distance because vector
+  // loads retire in order: waiting for an input chunk loaded later than the
+  // weights would also wait for those weights.
+  Frag8 b[SRING][4];
+  uint4 xr[SRING][2];
+  auto load_chunk = [&](int c, int slot) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) b[u].u = *reinterpret_cast<const uint4*>(wp + 32 * u);
-  uint4 xr0, xr1;
-  load16(xg, xr0, xr1);
-  *reinterpret_cast<uint4*>(&Xs[0][xrow * SLDX + xseg]) = xr0;
-  *reinterpret_cast<uint4*>(&Xs[0][xrow * SLDX + xseg + 8]) = xr1;
+    for (int u = 0; u < 4; ++u) b[slot][u].u = *reinterpret_cast<const uint4*>(wp + c * SKC + 32 * u);
+    uint4 lo, hi;
+    load16(xg + c * SKC, lo, hi);
+    xr[slot][0] = lo;
+    xr[slot][1] = hi;
+  };
+  auto publish = [&](int slot, int buf) {
+    *reinterpret_cast<uint4*>(&Xs[buf][xrow * SLDX + xseg]) = xr[slot][0];
+    *reinterpret_cast<uint4*>(&Xs[buf][xrow * SLDX + xseg + 8]) = xr[slot][1];
+  };
+#pragma unroll
+  for (int c = 0; c < SRING - 1; ++c)
+    if (c < nch) load_chunk(c, c);
+  publish(0, 0);
   __syncthreads();
 
-  // one chunk: start loading the next input chunk, multiply this one, then start
-  // the next weight fragments and publish the input chunk for the next step
-  auto step = [&](int c, int buf) {
-    const bool more = c + 1 < nch;
-    if (more) load16(xg + (c + 1) * SKC, xr0, xr1);
+  // one chunk: issue the loads SRING - 1 chunks ahead, multiply this chunk,
+  // publish the next input chunk to the other LDS buffer
+  auto step = [&](int c, int slot, int ahead_slot, int next_slot, int buf) {
+    if (c + SRING - 1 < nch) load_chunk(c + SRING - 1, ahead_slot);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       Frag8 a0, a1;
       a0.u = *reinterpret_cast<const uint4*>(&Xs[buf][c16 * SLDX + 32 * u + 8 * g4]);
       a1.u = *reinterpret_cast<const uint4*>(&Xs[buf][(16 + c16) * SLDX + 32 * u + 8 * g4]);
-      acc0 = mfma16(a0.v, b[u].v, acc0);
-      acc1 = mfma16(a1.v, b[u].v, acc1);
+      acc0 = mfma16(a0.v, b[slot][u].v, acc0);
+      acc1 = mfma16(a1.v, b[slot][u].v, acc1);
     }
-    if (more) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) b[u].u = *reinterpret_cast<const uint4*>(wp + (c + 1) * SKC + 32 * u);
-      *reinterpret_cast<uint4*>(&Xs[buf ^ 1][xrow * SLDX + xseg]) = xr0;
-      *reinterpret_cast<uint4*>(&Xs[buf ^ 1][xrow * SLDX + xseg + 8]) = xr1;
-    }
+    if (c + 1 < nch) publish(next_slot, buf ^ 1);
     __syncthreads();
   };
   if constexpr (NCH > 0) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) step(c, c & 1);
+    for (int c = 0; c < NCH; ++c) step(c, c % SRING, (c + SRING - 1) % SRING, (c + 1) % SRING, c & 1);
   } else {
     int c = 0;
     for (; c + SUNROLL <= nch; c += SUNROLL) {
 #pragma unroll
-      for (int k = 0; k < SUNROLL; ++k) step(c + k, k & 1);
+      for (int k = 0; k < SUNROLL; ++k) step(c + k, k % SRING, (k + SRING - 1) % SRING, (k + 1) % SRING, k & 1);
     }
-    for (; c < nch; ++c) step(c, c & 1);
+#pragma unroll
+    for (int k = 0; k < SUNROLL; ++k)
+      if (c + k < nch) step(c + k, k % SRING, (k + SRING - 1) % SRING, (k + 1) % SRING, k & 1);
   }
 
   // pairs: lanes with column j < 8 take the high feature from lane + 8
