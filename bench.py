@@ -40,18 +40,28 @@ HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 SEED = 37
 
-# HBM bytes per launch of the decode attention kernel, measured with
+# HBM bytes per launch of each workload's dominant kernel, measured with
 # `rocprofv3 --pmc FETCH_SIZE` and `--pmc WRITE_SIZE` on this bench (KiB per
-# dispatch) and scaled by what the same counters read for a plain 1 GiB device
-# copy (bench.py --calibrate-copy-mib 1024): FETCH_SIZE reported 0.5 x the bytes
-# the copy read, WRITE_SIZE 1.0 x the bytes it wrote.  The figures belong to the
-# kernel source they were taken on; once kvc_decode.hip changes the bench
-# reports traffic as null until they are measured again.
+# dispatch, a timed step's dispatch) and scaled by what the same counters read
+# for a plain 1 GiB device copy (bench.py --calibrate-copy-mib 1024):
+# FETCH_SIZE reported 0.5 x the bytes the copy read, WRITE_SIZE 1.0 x the bytes
+# it wrote.  The figures belong to the kernel source they were taken on; once
+# that file changes the bench reports traffic as null until they are measured
+# again.
 MEASURED_TRAFFIC = {
-    "headline": {"kernel_source_sha256": "c252cd785e6381c7c87d554be1f86b3733d1cd311f9f3bff1d56364ac523cc6a",
-                 "fetch_kib": 1048887.1, "fetch_scale": 2.0, "write_kib": 512.0, "write_scale": 1.0},
+    # attend_decode_bf16_kernel, headline decode (B=32, t=4096)
+    "headline": {"source": "decode", "fetch_kib": 1048889.5, "fetch_scale": 2.0, "write_kib": 512.0, "write_scale": 1.0,
+                 "kernel_source_sha256": "acf2f8377b31650f61d27c25bed51d3c229df086adf4093628a48a3fa4fe6ce3"},
+    # project_wide_kernel, suffix chunk (B=8, n=512)
+    "chunk": {"source": "mfma", "fetch_kib": 299298.9, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
+              "kernel_source_sha256": "fef7c70244a47b81b1bc7b4b56ce3621e30cf3d8e90333277b23a5c01956709e"},
+    # attend_flash_kernel, suffix chunk (B=8, n=512)
+    "chunk_attention": {"source": "mfma", "fetch_kib": 543921.0, "fetch_scale": 2.0, "write_kib": 65541.9,
+                        "write_scale": 1.0,
+                        "kernel_source_sha256": "fef7c70244a47b81b1bc7b4b56ce3621e30cf3d8e90333277b23a5c01956709e"},
 }
-DECODE_KERNEL_SOURCE = os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip")
+KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
+                  "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}
 
 WORKLOADS = {
     "headline": dict(B=32, H=32, dh=128, C=4096, t="full", kind="decode"),
@@ -129,12 +139,13 @@ def setup(wl, max_chunk=512):
 
 
 def measured_traffic(name):
-    """Counter-derived HBM bytes per attention launch, or None if not measured for this source."""
+    """Counter-derived HBM bytes per launch of the workload's dominant kernel, or
+    None if not measured for the current kernel source."""
     import hashlib
     m = MEASURED_TRAFFIC.get(name)
     if not m:
         return None
-    with open(DECODE_KERNEL_SOURCE, "rb") as f:
+    with open(KERNEL_SOURCES[m["source"]], "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != m["kernel_source_sha256"]:
             return None
     return m["fetch_kib"] * 1024 * m["fetch_scale"] + m["write_kib"] * 1024 * m["write_scale"]
@@ -363,6 +374,7 @@ def run_chunk(name, wl, steps, warmup, cpu):
     attn_flops = sum(4 * H * dh * sum(c + i + 1 for i in range(n)) for c in start)
     proj_flops = 2 * B * n * D * 3 * D
     att_tf = attn_flops / (st[1] * 1e-3) / 1e12
+    proj_tf = proj_flops / (st[0] * 1e-3) / 1e12
     res = {
         "metric": "suffix-chunk tokens/s (MFMA utilisation)", "value": B * n / sec, "unit": "tokens/s",
         "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,
@@ -371,10 +383,14 @@ def run_chunk(name, wl, steps, warmup, cpu):
                                f"cut uniform[0,{wl['cut_max']}], bf16", "cuts": start, "seed": SEED},
         "step_ms_percentiles": pct,
         "stage_ms": {"project": st[0], "attend": st[1], "merge": st[2], "commit": st[3]},
-        "project_TFLOPs": proj_flops / (st[0] * 1e-3) / 1e12,
-        "roofline": {"bound": "mfma", "kernel": "attend_flash_kernel", "achieved": att_tf,
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": att_tf / BF16_PEAK_TFLOPS,
-                     "traffic": None, "algorithmic_flops_per_launch": attn_flops},
+        # the projection is the step's largest kernel; the attention's figures follow it
+        "roofline": {"bound": "mfma", "kernel": "project_wide_kernel", "achieved": proj_tf,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": proj_tf / BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic(name), "algorithmic_flops_per_launch": proj_flops},
+        "attention_roofline": {"bound": "mfma", "kernel": "attend_flash_kernel", "achieved": att_tf,
+                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": att_tf / BF16_PEAK_TFLOPS,
+                               "traffic": measured_traffic("chunk_attention"),
+                               "algorithmic_flops_per_launch": attn_flops},
     }
     if cpu:
         cb, worst = cpu_baseline_chunk(env, wl, out.double().cpu().numpy(), bits)

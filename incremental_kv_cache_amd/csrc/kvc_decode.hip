@@ -71,7 +71,8 @@ __device__ __forceinline__ uint4 load_stream(const bf16_t* p) {
 }
 
 template <int DH, int U>
-__global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevState s, float* __restrict__ out) {
+__global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevState s, SeqOrder order,
+                                                                        float* __restrict__ out) {
   constexpr int G = DH / 8;
   constexpr int RPW = 64 / G;
   constexpr int GROUPS = kWaves * RPW;
@@ -79,7 +80,8 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
   __shared__ float sm_m[GROUPS], sm_l[GROUPS];
   __shared__ float sm_acc[GROUPS][DH + 4];
 
-  const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // sequences with the most rows first (blocks are dispatched with z slowest)
+  const int tile = blockIdx.x, h = blockIdx.y, b = order.count ? order.seq[blockIdx.z] : blockIdx.z;
   const int C = s.capacity;
   const int len = min(max(s.len[b], 0), C - 1);
   const int t = len + 1;
@@ -251,14 +253,14 @@ inline hipStream_t st(void* p) { return static_cast<hipStream_t>(p); }
 
 // Split-K attention for bf16 storage with d_h in {64, 128}; returns -1 for
 // other shapes (the vector kernels then run).
-int fast_attend_decode(const DevState& s, void* out) {
+int fast_attend_decode(const DevState& s, const SeqOrder& order, void* out) {
   if (s.dtype != KVC_BF16) return -1;
   dim3 grid((s.capacity + s.tile_rows - 1) / s.tile_rows, s.heads, s.batch);
   if (s.head_width == 128) {
-    hipLaunchKernelGGL((attend_decode_bf16_kernel<128, 8>), grid, dim3(64 * kWaves), 0, st(s.stream), s,
+    hipLaunchKernelGGL((attend_decode_bf16_kernel<128, 8>), grid, dim3(64 * kWaves), 0, st(s.stream), s, order,
                        static_cast<float*>(out));
   } else if (s.head_width == 64) {
-    hipLaunchKernelGGL((attend_decode_bf16_kernel<64, 4>), grid, dim3(64 * kWaves), 0, st(s.stream), s,
+    hipLaunchKernelGGL((attend_decode_bf16_kernel<64, 4>), grid, dim3(64 * kWaves), 0, st(s.stream), s, order,
                        static_cast<float*>(out));
   } else {
     return -1;

@@ -582,7 +582,7 @@ int dev_set_rows(const DevState& s, const int32_t* vals) {
 int mfma_project(const DevState& s, const void* x, int n_max, int per_seq_rows);
 int mfma_output_project(const DevState& s, int n_max, int per_seq_rows);
 int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, const ChunkOrder& order, void* out);
-int fast_attend_decode(const DevState& s, void* out);
+int fast_attend_decode(const DevState& s, const SeqOrder& order, void* out);
 int fast_merge_decode(const DevState& s, void* out);
 
 int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows) {
@@ -609,8 +609,8 @@ int dev_output_project(const DevState& state, int n_max, int per_seq_rows, void*
   return int(hipErrorInvalidValue);
 }
 
-int dev_attend_decode(const DevState& s, void* out) {
-  const int rc = fast_attend_decode(s, out);
+int dev_attend_decode(const DevState& s, const SeqOrder& order, void* out) {
+  const int rc = fast_attend_decode(s, order, out);
   if (rc >= 0) return rc;
   return dispatch<AttendDecode>(s.dtype, s.head_width, s);
 }

@@ -68,7 +68,8 @@ struct kvc_cache {
   ErrWords* err_host = nullptr;  // pinned readback
   int64_t storage_bytes = 0;
   Profile prof;
-  ChunkOrder order{};  // work order of the last chunk call
+  ChunkOrder order{};     // work order of the last chunk call
+  SeqOrder seq_order{};   // sequence order of the last decode call
 };
 
 void kvc::build_chunk_order(ChunkOrder* o, int batch, int n_max, const int32_t* len, const int32_t* rows) {
@@ -88,6 +89,14 @@ void kvc::build_chunk_order(ChunkOrder* o, int batch, int n_max, const int32_t* 
   std::stable_sort(w.begin(), w.end(), [](const auto& a, const auto& c) { return a.first > c.first; });
   for (size_t k = 0; k < w.size(); ++k) o->item[k] = w[k].second;
   o->count = int32_t(w.size());
+}
+
+void kvc::build_seq_order(SeqOrder* o, int batch, const int32_t* len) {
+  o->count = 0;
+  if (batch > kMaxSeqOrder) return;
+  for (int b = 0; b < batch; ++b) o->seq[b] = b;
+  std::stable_sort(o->seq, o->seq + batch, [&](int32_t a, int32_t c) { return len[a] > len[c]; });
+  o->count = batch;
 }
 
 namespace {
@@ -331,7 +340,8 @@ kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_row
   void* heads = s.wo ? s.merged : out;
   profile_mark(c, KVC_STAGE_ATTEND, 0);
   if (decode) {
-    rc = dev_attend_decode(s, heads);
+    build_seq_order(&c->seq_order, c->batch, c->len.data());
+    rc = dev_attend_decode(s, c->seq_order, heads);
   } else {
     build_chunk_order(&c->order, c->batch, n_max, c->len.data(), per_seq ? n_rows : nullptr);
     rc = dev_attend_chunk(s, n_max, per_seq, c->order, heads);

@@ -87,7 +87,17 @@ int dev_set_rows(const DevState& s, const int32_t* vals);
 // Pipeline stages.  n_max: rows per sequence of this call (1 for decode);
 // per_seq_rows: 0 = every sequence has n_max rows, 1 = rows[] holds them.
 int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows);
-int dev_attend_decode(const DevState& s, void* out);
+// Sequences of a decode call with the most retained rows first: the bf16
+// split-K attention deals its workgroups out in this order so that the longest
+// lanes start early (ragged batches).  count is 0 when the batch exceeds the
+// table (sequence order).
+constexpr int kMaxSeqOrder = 256;
+struct SeqOrder {
+  int32_t count;
+  int32_t seq[kMaxSeqOrder];
+};
+void build_seq_order(SeqOrder* o, int batch, const int32_t* len);
+int dev_attend_decode(const DevState& s, const SeqOrder& order, void* out);
 int dev_merge_decode(const DevState& s, void* out);
 // Work items of the bf16 chunk attention kernel: one per (sequence, tile of
 // kChunkQueryTile chunk rows), listed with the most keys to read first, so

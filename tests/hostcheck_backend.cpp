@@ -66,7 +66,7 @@ int dev_set_rows(const DevState& s, const int32_t* vals) {
   return 0;
 }
 int dev_project(const DevState&, const void*, int, int) { return 1; }
-int dev_attend_decode(const DevState&, void*) { return 1; }
+int dev_attend_decode(const DevState&, const SeqOrder&, void*) { return 1; }
 int dev_merge_decode(const DevState&, void*) { return 1; }
 int dev_attend_chunk(const DevState&, int, int, const ChunkOrder&, void*) { return 1; }
 int dev_output_project(const DevState&, int, int, void*) { return 1; }
@@ -85,3 +85,19 @@ int dev_stream_read(const void*, int64_t, void*, void*) { return 1; }
 bool dev_has_kernels() { return false; }
 
 }  // namespace kvc
+
+// Test hooks for the host-side work orders (not part of the library ABI).
+extern "C" int kvc_test_chunk_order(int batch, int n_max, const int32_t* len, const int32_t* rows, int32_t* qtiles,
+                                    int32_t* items) {
+  kvc::ChunkOrder o;
+  kvc::build_chunk_order(&o, batch, n_max, len, rows);
+  *qtiles = o.qtiles;
+  for (int k = 0; k < o.count; ++k) items[k] = o.item[k];
+  return o.count;
+}
+extern "C" int kvc_test_seq_order(int batch, const int32_t* len, int32_t* seq) {
+  kvc::SeqOrder o;
+  kvc::build_seq_order(&o, batch, len);
+  for (int k = 0; k < o.count; ++k) seq[k] = o.seq[k];
+  return o.count;
+}

@@ -251,3 +251,46 @@ def test_stream_read_argument_checks(lib):
     d = lib.kvc_last_error().contents
     assert (d.expected, d.actual) == (32768, 32768)
     assert lib.kvc_stream_read(buf, 65536, sink, None) == capi.KVC_ERR_DEVICE  # no kernels in this build
+
+
+def _i32(v):
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.int32))
+    return a, a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def test_chunk_work_order_lists_every_item_heaviest_first(lib):
+    """The chunk attention's work order: every (sequence, 128-row query tile) with
+    rows appears once, the keys its last query reads never increase along the
+    list, and equal loads keep sequence order."""
+    lens, rows, n_max = [10, 500, 0, 37, 200], [300, 1, 0, 129, 256], 300
+    la, lp = _i32(lens)
+    ra, rp = _i32(rows)
+    items = np.zeros(256, np.int32)
+    qt = C.c_int32()
+    n = lib.kvc_test_chunk_order(5, n_max, lp, rp, C.byref(qt), items.ctypes.data_as(C.POINTER(C.c_int32)))
+    assert qt.value == 3
+    got = [(int(i) >> 16, int(i) & 0xFFFF) for i in items[:n]]
+    want = {(b, q) for b in range(5) for q in range(3) if q * 128 < rows[b]}
+    assert len(got) == len(want) and set(got) == want
+    keys = [lens[b] + min(rows[b], 128 * (q + 1)) for b, q in got]
+    assert all(keys[k] >= keys[k + 1] for k in range(len(keys) - 1))
+    for k in range(len(keys) - 1):
+        if keys[k] == keys[k + 1]:
+            assert got[k] < got[k + 1]
+    # no per-sequence rows: every sequence has n_max rows
+    n2 = lib.kvc_test_chunk_order(2, 130, lp, None, C.byref(qt), items.ctypes.data_as(C.POINTER(C.c_int32)))
+    assert n2 == 4 and qt.value == 2
+    # more items than the table holds: natural order (count 0)
+    big, bp = _i32(np.arange(300))
+    assert lib.kvc_test_chunk_order(300, 1, bp, None, C.byref(qt), items.ctypes.data_as(C.POINTER(C.c_int32))) == 0
+
+
+def test_decode_sequence_order_longest_first(lib):
+    """The decode attention's sequence order: most retained rows first, ties in
+    sequence order; a batch larger than the table keeps sequence order."""
+    la, lp = _i32([3, 9, 9, 0, 4])
+    seq = np.zeros(256, np.int32)
+    n = lib.kvc_test_seq_order(5, lp, seq.ctypes.data_as(C.POINTER(C.c_int32)))
+    assert n == 5 and list(seq[:5]) == [1, 2, 4, 0, 3]
+    big, bp = _i32(np.arange(300))
+    assert lib.kvc_test_seq_order(300, bp, seq.ctypes.data_as(C.POINTER(C.c_int32))) == 0
