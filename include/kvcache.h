@@ -66,6 +66,8 @@ enum {
   KVC_ERR_NONFINITE_QUERY = 32,  /* rotated query has a NaN/Inf                            */
   KVC_ERR_ROTARY_POSITION = 33,  /* a row's position reaches the rotary max positions      */
   KVC_ERR_NONFINITE_OUTPUT = 34, /* softmax or mixture produced a NaN/Inf                  */
+  KVC_ERR_TOKEN_RANGE = 35,      /* session call: a token id outside [0, vocab); reported
+                                    before the others (flat index over [B, n])             */
   /* Continuation (prefix-reuse note). */
   KVC_ERR_BAD_CUT = 40,          /* cut < 0 or cut > current length                        */
   KVC_ERR_EMPTY_QUERY = 41,      /* lcp query with no tokens                               */
@@ -112,7 +114,7 @@ typedef struct {
   kvc_status status;
   int32_t parameter;        /* revision mismatch: first weight that differs (0 W_q .. 3 W_o) */
   int32_t sequence;         /* sequence index for FULL, BAD_CUT, CHUNK_ROWS, ROTARY_POSITION */
-  int32_t reserved;
+  int32_t layer;            /* session calls: index of the layer that failed; -1 otherwise   */
   int64_t expected, actual; /* rank, tokens, batch, width, heads, head width, capacity, ... */
   uint64_t cache_revision, layer_revision;
   int64_t flat_index;       /* NONFINITE_*: first flat index over the candidate [B,H,n,d_h]  */
@@ -300,6 +302,69 @@ kvc_status kvc_profile_read(kvc_cache* cache, float* ms_out, int32_t* calls_out)
  * 16 writable bytes (written only for one improbable xor of the data).
  * Errors: NULL_ARGUMENT, BAD_ARGUMENT (size or alignment), DEVICE. */
 kvc_status kvc_stream_read(const void* buf, int64_t bytes, void* sink, void* hip_stream);
+
+/* ---- Model-wide session ----------------------------------------------
+ * Several layers behind one token stream, with one cache per layer (Chapter
+ * 37, "Give every decoder block its own state next": a model-wide session
+ * binds one cache per decoder block and threads them through prefill and
+ * decode; "Bind the state, calculate completely, then commit", the
+ * prepared-row listing: every block prepares its row and the stack is
+ * committed only when all of them succeeded; prefix-reuse note, "What must be
+ * trimmed together": every layer's K, V and row positions are trimmed with
+ * next_position as one unit).  The block is the
+ * note's toy decoder block: input rows h0 = E[token] (+ absolute sinusoidal
+ * encoding PE(p, 2i) = sin(p / 10000^(2i/D)), PE(p, 2i+1) = cos(same) at p =
+ * next_position + i), then per layer h <- h + tanh(layer attention of h)
+ * (the layer's W_o applied first when it has one).  In a session call every
+ * layer computes first; the appends of all layers are then made only if no
+ * layer failed, so any failure leaves every layer unchanged. */
+typedef struct kvc_session kvc_session;
+
+enum { KVC_PE_NONE = 0, KVC_PE_SINUSOIDAL = 1 };
+
+/* Creates a session over `layers` (HOST array of n_layers >= 1 layer handles,
+ * borrowed; all with the same model width and type) and one empty cache per
+ * layer (batch, capacity, max_chunk_rows as kvc_cache_create).  embedding:
+ * DEVICE [vocab, D] row-major in the accumulate type (double for F64 layers,
+ * float otherwise), borrowed.  position_encoding: KVC_PE_NONE or
+ * KVC_PE_SINUSOIDAL.  Allocates the caches and the session's row buffers.
+ * Errors: NULL_ARGUMENT, BAD_ARGUMENT (counts, encoding, layers of different
+ * width or type), then kvc_cache_create's errors (detail.layer names the layer). */
+kvc_status kvc_session_create(const kvc_layer* const* layers, int32_t n_layers, const void* embedding,
+                              int32_t vocab, int32_t position_encoding, int32_t batch, int32_t capacity,
+                              int32_t max_chunk_rows, void* hip_stream, kvc_session** out);
+void kvc_session_destroy(kvc_session* session);
+
+/* Suffix chunk through every layer (prefix-reuse note: model.chunk of the
+ * suffix tokens after the cached prefix).  tokens: DEVICE int32 [B, n_max];
+ * n_rows: HOST int32[B] (NULL: all n_max), as kvc_continue_chunk.  out: DEVICE
+ * [B, n_max, D] accumulate type, the last layer's rows (rows i >= n_b
+ * untouched).  work: projection rows summed over the batch and the layers.
+ * Errors: as kvc_continue_chunk for each layer in order (detail.layer), then
+ * TOKEN_RANGE and the device-found errors of any layer; DEFERRED. */
+kvc_status kvc_session_chunk(kvc_session* session, const int32_t* tokens, int32_t n_max, const int32_t* n_rows,
+                             void* out, int32_t flags, kvc_work* work);
+
+/* One cached decode step of the whole stack: tokens DEVICE int32 [B]; out
+ * DEVICE [B, 1, D] accumulate type.  Errors: as kvc_session_chunk, FULL when a
+ * sequence has no room. */
+kvc_status kvc_session_decode(kvc_session* session, const int32_t* tokens, void* out, int32_t flags,
+                              kvc_work* work);
+
+/* Trims every layer to cut[b] rows and sets next_position[b] = cut[b] in one
+ * step (prefix-reuse note, "What must be trimmed together"); flags as
+ * kvc_truncate (KVC_TRUNCATE_KEEP_STALE_POSITION: the note's negative
+ * control).  Errors: NULL_ARGUMENT, BAD_CUT, BAD_ARGUMENT, DEVICE. */
+kvc_status kvc_session_truncate(kvc_session* session, const int32_t* cut, int32_t flags);
+/* Every layer's lengths and next positions to 0 (kvc_reset per layer). */
+kvc_status kvc_session_reset(kvc_session* session);
+/* Waits for the stream and reports a deferred failure of any layer, as kvc_sync. */
+kvc_status kvc_session_sync(kvc_session* session);
+/* The session's cache of layer `layer`, borrowed for the read-only calls
+ * (kvc_snapshot, kvc_lengths, kvc_cache_describe, kvc_copy_storage, ...);
+ * compute, truncate and reset calls on it return BAD_ARGUMENT and
+ * kvc_cache_destroy ignores it.  Errors: NULL_ARGUMENT, BAD_ARGUMENT. */
+kvc_status kvc_session_layer_cache(kvc_session* session, int32_t layer, kvc_cache** out);
 
 /* Last failure on the calling thread; never NULL. */
 const kvc_error_detail* kvc_last_error(void);

@@ -30,6 +30,7 @@ KVC_ERR_NONFINITE_VALUE = 31
 KVC_ERR_NONFINITE_QUERY = 32
 KVC_ERR_ROTARY_POSITION = 33
 KVC_ERR_NONFINITE_OUTPUT = 34
+KVC_ERR_TOKEN_RANGE = 35
 KVC_ERR_BAD_CUT = 40
 KVC_ERR_EMPTY_QUERY = 41
 KVC_ERR_CHUNK_ROWS = 42
@@ -47,11 +48,12 @@ KVC_SYNC, KVC_ASYNC = 0, 1
 KVC_TRUNCATE_KEEP_STALE_POSITION = 1
 KVC_STAGE_PROJECT, KVC_STAGE_ATTEND, KVC_STAGE_MERGE, KVC_STAGE_COMMIT, KVC_STAGE_OUTPUT = 0, 1, 2, 3, 4
 KVC_STAGES = 5
+KVC_PE_NONE, KVC_PE_SINUSOIDAL = 0, 1
 
 
 class ErrorDetail(C.Structure):
     _fields_ = [
-        ("status", C.c_int32), ("parameter", C.c_int32), ("sequence", C.c_int32), ("reserved", C.c_int32),
+        ("status", C.c_int32), ("parameter", C.c_int32), ("sequence", C.c_int32), ("layer", C.c_int32),
         ("expected", C.c_int64), ("actual", C.c_int64),
         ("cache_revision", C.c_uint64), ("layer_revision", C.c_uint64),
         ("flat_index", C.c_int64), ("value", C.c_double),
@@ -113,6 +115,14 @@ PROTOTYPES = {
     "kvc_profile_enable": (I32, [P, I32]),
     "kvc_profile_read": (I32, [P, C.POINTER(C.c_float), PI32]),
     "kvc_stream_read": (I32, [P, I64, P, P]),
+    "kvc_session_create": (I32, [PP, I32, P, I32, I32, I32, I32, I32, P, PP]),
+    "kvc_session_destroy": (None, [P]),
+    "kvc_session_chunk": (I32, [P, P, I32, PI32, P, I32, C.POINTER(Work)]),
+    "kvc_session_decode": (I32, [P, P, P, I32, C.POINTER(Work)]),
+    "kvc_session_truncate": (I32, [P, PI32, I32]),
+    "kvc_session_reset": (I32, [P]),
+    "kvc_session_sync": (I32, [P]),
+    "kvc_session_layer_cache": (I32, [P, I32, PP]),
     "kvc_last_error": (C.POINTER(ErrorDetail), []),
     "kvc_status_name": (C.c_char_p, [I32]),
 }

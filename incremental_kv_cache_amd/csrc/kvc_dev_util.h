@@ -89,7 +89,15 @@ __device__ __forceinline__ void flag_min(unsigned long long* word, unsigned long
 }
 
 __device__ __forceinline__ bool any_error(const ErrWords* e) {
-  return (e->key & e->value & e->query & e->position & e->output) != kErrClear;
+  return (e->key & e->value & e->query & e->position & e->output & e->token) != kErrClear;
+}
+
+// True when a failure word of the cache's gate (its own words, or every layer
+// of its session) is set: state-changing kernels then do nothing.
+__device__ __forceinline__ bool gate_closed(const DevState& s) {
+  for (int k = 0; k < s.gate_count; ++k)
+    if (any_error(&s.gate[k])) return true;
+  return false;
 }
 
 

@@ -289,7 +289,7 @@ constexpr int kCommitRows = 64;
 
 template <typename T>
 __global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max, int per_seq_rows) {
-  if (any_error(s.err)) return;
+  if (gate_closed(s)) return;
   const int r0 = blockIdx.x * kCommitRows, h = blockIdx.y, b = blockIdx.z;
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
   const int len = s.len[b];
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max,
 // next_position[b]; no other block touches sequence b.
 template <typename T>
 __global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
-  if (any_error(s.err)) return;
+  if (gate_closed(s)) return;
   const int b = blockIdx.x;
   const int len = s.len[b];
   const int C = s.capacity;
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
 
 // Advances len[b] and next_position[b] by n_b (after every copy has read len[b]).
 __global__ __launch_bounds__(256) void commit_advance_kernel(DevState s, int n_max, int per_seq_rows) {
-  if (any_error(s.err)) return;
+  if (gate_closed(s)) return;
   const int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= s.batch) return;
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
@@ -384,7 +384,7 @@ struct SetArgs {
 };
 
 __global__ __launch_bounds__(256) void set_lengths_kernel(DevState s, SetArgs a) {
-  if (any_error(s.err)) return;
+  if (gate_closed(s)) return;
   for (int k = threadIdx.x; k < a.count; k += blockDim.x) {
     const int b = a.first + k;
     if (a.mode == 2) {
@@ -408,6 +408,61 @@ __global__ void clear_err_kernel(ErrWords* e) {
 __global__ __launch_bounds__(256) void zero_kernel(uint4* p, size_t n16) {
   for (size_t k = size_t(blockIdx.x) * blockDim.x + threadIdx.x; k < n16; k += size_t(gridDim.x) * blockDim.x)
     p[k] = make_uint4(0, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- session ---
+// Input rows of a model-wide step: token embedding plus the absolute sinusoidal
+// encoding PE(p, 2i) = sin(p / 10000^(2i/D)), PE(p, 2i+1) = cos(same), with p =
+// next_position + i (prefix-reuse note, "Work and error over 27 cases": the toy
+// decoder's absolute sinusoidal positions; the angle is evaluated in double).
+// Block = one row (b, i).
+template <typename A, typename W>
+__global__ __launch_bounds__(256) void embed_kernel(DevState s, const int32_t* __restrict__ tokens,
+                                                    const A* __restrict__ emb, int vocab, int sinusoidal, int n_max,
+                                                    int per_seq_rows, A* __restrict__ h, W* __restrict__ x) {
+  const int row = blockIdx.x;
+  const int b = row / n_max;
+  const int i = row - b * n_max;
+  const int n_b = per_seq_rows ? s.rows[b] : n_max;
+  if (i >= n_b) return;
+  const int tok = tokens[row];
+  if (tok < 0 || tok >= vocab) {
+    if (threadIdx.x == 0) flag_min(&s.err->token, (unsigned long long)row);
+    return;
+  }
+  const int D = s.model_width;
+  const double p = double(s.next_pos[b] + i);
+  for (int j = threadIdx.x; j < D; j += blockDim.x) {
+    A v = emb[size_t(tok) * D + j];
+    if (sinusoidal) {
+      const double ang = p / pow(10000.0, double(2 * (j >> 1)) / double(D));
+      v += A((j & 1) ? cos(ang) : sin(ang));
+    }
+    h[size_t(row) * D + j] = v;
+    if (x) x[size_t(row) * D + j] = from_acc<W>(v);
+  }
+}
+
+__device__ __forceinline__ double tanh_acc(double v) { return tanh(v); }
+__device__ __forceinline__ float tanh_acc(float v) { return tanhf(v); }
+
+// The tanh-residual block between layers: h_out = h_in + tanh(a).
+template <typename A, typename W>
+__global__ __launch_bounds__(256) void residual_kernel(DevState s, const A* __restrict__ h_in,
+                                                       const A* __restrict__ a, A* h_out, W* __restrict__ x,
+                                                       int n_max, int per_seq_rows) {
+  const int row = blockIdx.x;
+  const int b = row / n_max;
+  const int i = row - b * n_max;
+  const int n_b = per_seq_rows ? s.rows[b] : n_max;
+  if (i >= n_b) return;
+  const int D = s.model_width;
+  for (int j = threadIdx.x; j < D; j += blockDim.x) {
+    const size_t k = size_t(row) * D + j;
+    const A v = h_in[k] + tanh_acc(a[k]);
+    h_out[k] = v;
+    if (x) x[k] = from_acc<W>(v);
+  }
 }
 
 inline hipStream_t st(void* s) { return static_cast<hipStream_t>(s); }
@@ -651,5 +706,55 @@ int dev_event_elapsed(float* ms, void* start, void* stop) {
 }
 
 bool dev_has_kernels() { return true; }
+
+int dev_embed(const DevState& s, const int32_t* tokens, const void* embedding, int vocab, int sinusoidal,
+              int n_max, int per_seq_rows, void* h, void* x) {
+  const dim3 grid(unsigned(s.batch) * unsigned(n_max));
+  switch (s.dtype) {
+    case KVC_F64:
+      hipLaunchKernelGGL((embed_kernel<double, double>), grid, dim3(256), 0, st(s.stream), s, tokens,
+                         static_cast<const double*>(embedding), vocab, sinusoidal, n_max, per_seq_rows,
+                         static_cast<double*>(h), static_cast<double*>(x));
+      break;
+    case KVC_F32:
+      hipLaunchKernelGGL((embed_kernel<float, float>), grid, dim3(256), 0, st(s.stream), s, tokens,
+                         static_cast<const float*>(embedding), vocab, sinusoidal, n_max, per_seq_rows,
+                         static_cast<float*>(h), static_cast<float*>(x));
+      break;
+    case KVC_BF16:
+      hipLaunchKernelGGL((embed_kernel<float, bf16_t>), grid, dim3(256), 0, st(s.stream), s, tokens,
+                         static_cast<const float*>(embedding), vocab, sinusoidal, n_max, per_seq_rows,
+                         static_cast<float*>(h), static_cast<bf16_t*>(x));
+      break;
+    default:
+      return int(hipErrorInvalidValue);
+  }
+  return last_launch();
+}
+
+int dev_residual(const DevState& s, const void* h_in, const void* a, void* h_out, void* x, int n_max,
+                 int per_seq_rows) {
+  const dim3 grid(unsigned(s.batch) * unsigned(n_max));
+  switch (s.dtype) {
+    case KVC_F64:
+      hipLaunchKernelGGL((residual_kernel<double, double>), grid, dim3(256), 0, st(s.stream), s,
+                         static_cast<const double*>(h_in), static_cast<const double*>(a), static_cast<double*>(h_out),
+                         static_cast<double*>(x), n_max, per_seq_rows);
+      break;
+    case KVC_F32:
+      hipLaunchKernelGGL((residual_kernel<float, float>), grid, dim3(256), 0, st(s.stream), s,
+                         static_cast<const float*>(h_in), static_cast<const float*>(a), static_cast<float*>(h_out),
+                         static_cast<float*>(x), n_max, per_seq_rows);
+      break;
+    case KVC_BF16:
+      hipLaunchKernelGGL((residual_kernel<float, bf16_t>), grid, dim3(256), 0, st(s.stream), s,
+                         static_cast<const float*>(h_in), static_cast<const float*>(a), static_cast<float*>(h_out),
+                         static_cast<bf16_t*>(x), n_max, per_seq_rows);
+      break;
+    default:
+      return int(hipErrorInvalidValue);
+  }
+  return last_launch();
+}
 
 }  // namespace kvc

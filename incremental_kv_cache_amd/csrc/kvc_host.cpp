@@ -70,6 +70,21 @@ struct kvc_cache {
   Profile prof;
   ChunkOrder order{};     // work order of the last chunk call
   SeqOrder seq_order{};   // sequence order of the last decode call
+  bool session = false;   // a layer cache of a kvc_session: its failure words belong to the session
+};
+
+struct kvc_session {
+  std::vector<const kvc_layer*> layers;
+  std::vector<kvc_cache*> caches;  // one per layer, created and destroyed with the session
+  int32_t batch = 0, max_chunk_rows = 0, model_width = 0, vocab = 0;
+  kvc_dtype dtype = KVC_F64;
+  int sinusoidal = 0;
+  const void* embedding = nullptr;
+  kvc::ErrWords* gate = nullptr;  // device: the layers' failure words, [L]
+  void* h = nullptr;              // device [B, max_chunk_rows, D], accumulate type: the running rows
+  void* a = nullptr;              // device [B, max_chunk_rows, D], accumulate type: a layer's attention
+  void* x = nullptr;              // device [B, max_chunk_rows, D], weight type (bf16 sessions only)
+  bool pending_async = false;
 };
 
 void kvc::build_chunk_order(ChunkOrder* o, int batch, int n_max, const int32_t* len, const int32_t* rows) {
@@ -111,6 +126,7 @@ void reset_detail() {
   std::memset(&g_last, 0, sizeof(g_last));
   g_last.parameter = -1;
   g_last.sequence = -1;
+  g_last.layer = -1;
   g_last.flat_index = -1;
 }
 
@@ -205,7 +221,10 @@ kvc_status collect_device_error(kvc_cache* c, int64_t n_max_for_index) {
   const ErrWords e = *c->err_host;
   kvc_status st = KVC_OK;
   unsigned long long idx = kErrClear;
-  if (e.key != kErrClear) {
+  if (e.token != kErrClear) {
+    st = KVC_ERR_TOKEN_RANGE;
+    idx = e.token;
+  } else if (e.key != kErrClear) {
     st = KVC_ERR_NONFINITE_KEY;
     idx = e.key;
   } else if (e.value != kErrClear) {
@@ -257,6 +276,8 @@ kvc_status collect_device_error(kvc_cache* c, int64_t n_max_for_index) {
       return fail(st, "rotated query at flat index %llu is not finite", idx);
     case KVC_ERR_ROTARY_POSITION:
       return fail(st, "sequence %llu reached the rotary position capacity %d", idx, c->rope_max_positions);
+    case KVC_ERR_TOKEN_RANGE:
+      return fail(st, "token at flat index %llu is outside the embedding", idx);
     default:
       return fail(st, "attention output at flat index %llu is not finite", idx);
   }
@@ -314,16 +335,16 @@ void free_cache(kvc_cache* c) {
   dev_free(c->ds.partials);
   dev_free(c->ds.rope_cos);
   dev_free(c->ds.rope_sin);
-  dev_free(c->ds.err);
+  if (!c->session) dev_free(c->ds.err);
   dev_free(c->ds.merged);
   dev_host_free(c->err_host);
   for (void* e : c->prof.events) dev_event_destroy(e);
   delete c;
 }
 
-// Runs the four stages of one call and the sync-mode error collection.
-kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_rows, void* out, int32_t flags,
-                    bool decode) {
+// The compute stages of one call: projection, attention, split merge, output
+// projection.  Merged heads (or W_o's result) go to `out`.
+kvc_status compute_stages(kvc_cache* c, const void* x, int n_max, const int32_t* n_rows, void* out, bool decode) {
   DevState& s = c->ds;
   const int per_seq = n_rows != nullptr;
   int rc = 0;
@@ -360,30 +381,388 @@ kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_row
     profile_mark(c, KVC_STAGE_OUTPUT, 1);
     if (rc) return device_fail(rc, "output projection launch");
   }
+  return KVC_OK;
+}
+
+// The predicated append (suppressed on the device while a gate word is set).
+kvc_status commit_stage(kvc_cache* c, int n_max, const int32_t* n_rows) {
   profile_mark(c, KVC_STAGE_COMMIT, 0);
-  rc = dev_commit(s, n_max, per_seq);
+  const int rc = dev_commit(c->ds, n_max, n_rows != nullptr);
   profile_mark(c, KVC_STAGE_COMMIT, 1);
   profile_end_call(c);
   if (rc) return device_fail(rc, "commit launch");
+  return KVC_OK;
+}
 
-  if (flags & KVC_ASYNC) {
-    c->pending_async = true;
-    for (int b = 0; b < c->batch; ++b) {
-      const int n = per_seq ? n_rows[b] : n_max;
-      c->len[b] += n;
-      c->next_pos[b] += n;
-    }
-    return KVC_OK;
-  }
-  rc = dev_sync(s.stream);
-  if (rc) return device_fail(rc, "stream synchronisation");
-  kvc_status st = collect_device_error(c, n_max);
-  if (st != KVC_OK) return st;
+void advance_mirror(kvc_cache* c, int n_max, const int32_t* n_rows) {
   for (int b = 0; b < c->batch; ++b) {
-    const int n = per_seq ? n_rows[b] : n_max;
+    const int n = n_rows ? n_rows[b] : n_max;
     c->len[b] += n;
     c->next_pos[b] += n;
   }
+}
+
+// Runs the stages of one call and the sync-mode error collection.
+kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_rows, void* out, int32_t flags,
+                    bool decode) {
+  kvc_status st = compute_stages(c, x, n_max, n_rows, out, decode);
+  if (st != KVC_OK) return st;
+  st = commit_stage(c, n_max, n_rows);
+  if (st != KVC_OK) return st;
+  if (flags & KVC_ASYNC) {
+    c->pending_async = true;
+    advance_mirror(c, n_max, n_rows);
+    return KVC_OK;
+  }
+  const int rc = dev_sync(c->ds.stream);
+  if (rc) return device_fail(rc, "stream synchronisation");
+  st = collect_device_error(c, n_max);
+  if (st != KVC_OK) return st;
+  advance_mirror(c, n_max, n_rows);
+  return KVC_OK;
+}
+
+// Split-K tile of a decode call: the largest power-of-two multiple of 512
+// rows that still gives at least 1024 workgroups (four per compute unit);
+// measured on the bench workloads, fewer and longer tiles stream faster than a
+// finer split.
+void choose_decode_tiles(kvc_cache* cache) {
+  int tile = kDecodeTileRows;
+  int max_len = 0;
+  for (int b = 0; b < cache->batch; ++b) max_len = std::max(max_len, cache->len[b]);
+  for (int64_t cand = kDecodeTileRows; cand <= (int64_t(1) << 30); cand *= 2) {
+    int64_t blocks = 0;
+    for (int b = 0; b < cache->batch; ++b) blocks += (int64_t(cache->len[b]) + cand) / cand;
+    if (blocks * cache->heads < 1024) break;
+    tile = int(cand);
+    if (cand > max_len) break;
+  }
+  cache->ds.tile_rows = tile;
+  cache->ds.single_tile = tile > max_len;
+}
+
+kvc_status reject_session_cache(const char* what) {
+  return fail(KVC_ERR_BAD_ARGUMENT, "%s: this cache is a layer of a session; use the kvc_session_* calls", what);
+}
+
+// Cache construction.  shared_err: NULL for a standalone cache (it allocates
+// its own failure words and gates on them); else this layer's failure words
+// inside a session's block, and gate / gate_count the whole block.
+kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity, int32_t max_chunk_rows,
+                        void* hip_stream, ErrWords* shared_err, const ErrWords* gate, int gate_count,
+                        kvc_cache** out) {
+  *out = nullptr;
+  // Chapter 37, layer-kv-cache listing: batch, capacity, position capacity,
+  // element-count overflow, then allocation.
+  if (batch <= 0) return fail_ea(KVC_ERR_ZERO_BATCH, 1, batch, "KV cache batch size must be nonzero");
+  if (capacity <= 0) return fail_ea(KVC_ERR_ZERO_CAPACITY, 1, capacity, "KV cache capacity must be nonzero");
+  if (capacity > layer->rope_max_positions)
+    return fail_ea(KVC_ERR_CAPACITY_EXCEEDS_POSITIONS, layer->rope_max_positions, capacity,
+                   "KV cache capacity %d exceeds RoPE position capacity %d", capacity, layer->rope_max_positions);
+  if (max_chunk_rows <= 0)
+    return fail(KVC_ERR_BAD_ARGUMENT, "max_chunk_rows must be at least 1, got %d", max_chunk_rows);
+  const kvc_params* p = layer->params;
+  const int H = layer->heads, dh = layer->head_width;
+  int64_t elements = 0, cand = 0, pos_elems = 0;
+  if (!checked_mul(batch, H, &elements) || !checked_mul(elements, capacity, &elements) ||
+      !checked_mul(elements, dh, &elements) || !checked_mul(int64_t(batch) * H, int64_t(max_chunk_rows), &cand) ||
+      !checked_mul(cand, dh, &cand) || !checked_mul(batch, capacity, &pos_elems) ||
+      elements > (INT64_MAX / 16) || cand > (INT64_MAX / 16)) {
+    return fail(KVC_ERR_ELEMENT_COUNT_OVERFLOW,
+                "KV cache element count overflows for batch %d, %d heads, capacity %d, and head width %d", batch,
+                H, capacity, dh);
+  }
+  kvc_cache* c = new (std::nothrow) kvc_cache;
+  if (!c) return fail(KVC_ERR_ALLOCATION_FAILED, "host allocation failed");
+  c->batch = batch;
+  c->heads = H;
+  c->head_width = dh;
+  c->model_width = p->model_width;
+  c->capacity = capacity;
+  c->max_chunk_rows = max_chunk_rows;
+  c->dtype = p->dtype;
+  c->params_id = p->id;
+  for (int k = 0; k < 4; ++k) c->revision[k] = p->revision[k];
+  c->rope_feature_width = layer->rope_feature_width();
+  c->rope_max_positions = layer->rope_max_positions;
+  std::memcpy(&c->rope_base_bits, &layer->rope_base, 8);
+  c->rope_base = layer->rope_base;
+  c->pos_mode = layer->pos_mode;
+  c->len.assign(batch, 0);
+  c->next_pos.assign(batch, 0);
+  c->session = shared_err != nullptr;
+  int rc = dev_current_device(&c->device);
+  if (rc) {
+    free_cache(c);
+    return device_fail(rc, "hipGetDevice");
+  }
+
+  const size_t es = elem_size(p->dtype), as = acc_size(p->dtype);
+  const int max_tiles = (capacity + kDecodeTileRows - 1) / kDecodeTileRows;
+  auto round16 = [](size_t b) { return (b + 15) & ~size_t(15); };
+  DevState& s = c->ds;
+  s.dtype = p->dtype;
+  s.batch = batch;
+  s.heads = H;
+  s.head_width = dh;
+  s.model_width = p->model_width;
+  s.capacity = capacity;
+  s.max_chunk_rows = max_chunk_rows;
+  s.rope = layer->pos_mode == KVC_POS_ROPE;
+  s.max_positions = layer->rope_max_positions;
+  s.scale = 1.0 / std::sqrt(double(dh));
+  s.wq = p->w[0];
+  s.wk = p->w[1];
+  s.wv = p->w[2];
+  s.wo = p->w[3];
+  s.max_tiles = max_tiles;
+  s.tile_rows = kDecodeTileRows;
+  s.stream = hip_stream;
+  c->storage_bytes = int64_t(round16(size_t(elements) * es));
+  struct Alloc {
+    void** p;
+    size_t bytes;
+  } allocs[] = {
+      {&s.keys, size_t(c->storage_bytes)},
+      {&s.values, size_t(c->storage_bytes)},
+      {reinterpret_cast<void**>(&s.len), round16(sizeof(int32_t) * batch)},
+      {reinterpret_cast<void**>(&s.next_pos), round16(sizeof(int32_t) * batch)},
+      {reinterpret_cast<void**>(&s.positions), round16(sizeof(int32_t) * size_t(pos_elems))},
+      {reinterpret_cast<void**>(&s.rows), round16(sizeof(int32_t) * batch)},
+      {&s.cand_k, round16(size_t(cand) * es)},
+      {&s.cand_v, round16(size_t(cand) * es)},
+      {&s.q, round16(size_t(cand) * as)},
+      {&s.partials, round16(size_t(batch) * H * max_tiles * (dh + 2) * as)},
+      {reinterpret_cast<void**>(&s.err), shared_err ? 0 : round16(sizeof(ErrWords))},
+      {&s.merged, p->w[3] ? round16(size_t(cand) * as) : 0},  // [B, max_chunk_rows, D]
+  };
+  for (auto& a : allocs) {
+    if (a.bytes == 0) continue;
+    rc = dev_malloc(a.p, a.bytes);
+    if (rc) {
+      *a.p = nullptr;
+      free_cache(c);
+      g_last.expected = int64_t(a.bytes);
+      return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate %zu bytes of KV cache storage", a.bytes);
+    }
+  }
+  if (shared_err) {
+    s.err = shared_err;
+    s.gate = gate;
+    s.gate_count = gate_count;
+  } else {
+    s.gate = s.err;
+    s.gate_count = 1;
+  }
+  rc = dev_host_malloc(reinterpret_cast<void**>(&c->err_host), sizeof(ErrWords));
+  if (rc) {
+    c->err_host = nullptr;
+    free_cache(c);
+    return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate pinned host memory");
+  }
+  // Zero-filled storage (Chapter 37: zeroed backing buffers), zero lengths.
+  for (auto& a : allocs) {
+    if (*a.p == s.err || a.bytes == 0) continue;
+    rc = dev_zero(*a.p, a.bytes, s.stream);
+    if (rc) {
+      free_cache(c);
+      return device_fail(rc, "zero fill");
+    }
+  }
+  rc = dev_clear_err(s.err, s.stream);
+  if (rc) {
+    free_cache(c);
+    return device_fail(rc, "error word init");
+  }
+  // Rotary table: cos/sin of p * base^(-2i/d_h), evaluated in double on the host.
+  if (s.rope) {
+    const int half = dh / 2;
+    const size_t n = size_t(layer->rope_max_positions) * half;
+    std::vector<double> cd(n), sd(n);
+    for (int pos = 0; pos < layer->rope_max_positions; ++pos) {
+      for (int i = 0; i < half; ++i) {
+        const double inv = std::pow(layer->rope_base, -2.0 * double(i) / double(dh));
+        const double ang = double(pos) * inv;
+        cd[size_t(pos) * half + i] = std::cos(ang);
+        sd[size_t(pos) * half + i] = std::sin(ang);
+      }
+    }
+    const size_t bytes = n * as;
+    rc = dev_malloc(&s.rope_cos, round16(bytes));
+    if (rc == 0) rc = dev_malloc(&s.rope_sin, round16(bytes));
+    if (rc) {
+      free_cache(c);
+      return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate the rotary table");
+    }
+    if (as == 8) {
+      rc = dev_copy_h2d_sync(s.rope_cos, cd.data(), bytes, s.stream);
+      if (rc == 0) rc = dev_copy_h2d_sync(s.rope_sin, sd.data(), bytes, s.stream);
+    } else {
+      std::vector<float> cf(cd.begin(), cd.end()), sf(sd.begin(), sd.end());
+      rc = dev_copy_h2d_sync(s.rope_cos, cf.data(), bytes, s.stream);
+      if (rc == 0) rc = dev_copy_h2d_sync(s.rope_sin, sf.data(), bytes, s.stream);
+    }
+    if (rc) {
+      free_cache(c);
+      return device_fail(rc, "rotary table upload");
+    }
+  }
+  rc = dev_sync(s.stream);
+  if (rc) {
+    free_cache(c);
+    return device_fail(rc, "stream synchronisation");
+  }
+  *out = c;
+  return KVC_OK;
+}
+
+void free_session(kvc_session* S) {
+  if (!S) return;
+  if (!S->caches.empty()) (void)dev_sync(S->caches[0]->ds.stream);
+  for (kvc_cache* c : S->caches) free_cache(c);
+  dev_free(S->gate);
+  dev_free(S->h);
+  dev_free(S->a);
+  dev_free(S->x);
+  delete S;
+}
+
+// Reads and clears every layer's failure words after the stream is idle; the
+// first failing layer (in layer order) is reported, with detail.layer.
+kvc_status collect_session_error(kvc_session* S) {
+  kvc_status first = KVC_OK;
+  kvc_error_detail saved{};
+  for (size_t l = 0; l < S->caches.size(); ++l) {
+    const kvc_status st = collect_device_error(S->caches[l], 0);
+    if (st == KVC_ERR_DEVICE) return st;
+    if (st != KVC_OK && first == KVC_OK) {
+      first = st;
+      g_last.layer = int32_t(l);
+      saved = g_last;
+    }
+  }
+  if (first != KVC_OK) g_last = saved;
+  return first;
+}
+
+kvc_status check_deferred_session(kvc_session* S) {
+  if (!S->pending_async) return KVC_OK;
+  const int rc = dev_sync(S->caches[0]->ds.stream);
+  if (rc) return device_fail(rc, "stream synchronisation");
+  S->pending_async = false;
+  for (kvc_cache* c : S->caches) c->pending_async = false;
+  const kvc_status st = collect_session_error(S);
+  if (st == KVC_ERR_DEVICE) return st;
+  if (st != KVC_OK) {
+    const kvc_error_detail saved = g_last;
+    for (kvc_cache* c : S->caches) {
+      const kvc_status rs = resync_lengths(c);
+      if (rs != KVC_OK) return rs;
+    }
+    g_last = saved;
+    g_last.actual = st;
+    return fail(KVC_ERR_DEFERRED, "an earlier asynchronous session call failed: %s (%s)", kvc_status_name(st),
+                std::string(saved.message).c_str());
+  }
+  return KVC_OK;
+}
+
+// One session call: every layer computes (embedding, then per layer the
+// attention and the tanh residual), then every layer commits; the commits are
+// suppressed on the device if any layer's failure word is set.
+kvc_status session_call(kvc_session* S, const int32_t* tokens, int n_max, const int32_t* n_rows, void* out,
+                        int32_t flags, kvc_work* work, bool decode) {
+  const int L = int(S->layers.size());
+  if (!(flags & KVC_ASYNC)) {
+    kvc_status d = check_deferred_session(S);
+    if (d != KVC_OK) return d;
+  }
+  for (int l = 0; l < L; ++l) {
+    kvc_status st = check_binding(S->layers[l], S->caches[l]);
+    if (st != KVC_OK) {
+      g_last.layer = l;
+      return st;
+    }
+  }
+  for (int l = 0; l < L; ++l) {
+    const kvc_cache* c = S->caches[l];
+    for (int b = 0; b < c->batch; ++b) {
+      const int n = n_rows ? n_rows[b] : n_max;
+      if (int64_t(c->len[b]) + n > c->capacity) {
+        g_last.layer = l;
+        g_last.sequence = b;
+        return fail_ea(KVC_ERR_FULL, c->capacity, int64_t(c->len[b]) + n,
+                       "KV cache of layer %d is full at capacity %d (sequence %d needs %d more rows)", l,
+                       c->capacity, b, n);
+      }
+      if (c->ds.rope && n > 0 && int64_t(c->next_pos[b]) + n > c->rope_max_positions) {
+        g_last.layer = l;
+        g_last.sequence = b;
+        return fail_ea(KVC_ERR_ROTARY_POSITION, c->rope_max_positions, int64_t(c->next_pos[b]) + n - 1,
+                       "position %lld of sequence %d reaches the rotary position capacity %d of layer %d",
+                       (long long)c->next_pos[b] + n - 1, b, c->rope_max_positions, l);
+      }
+    }
+  }
+  kvc_work w{};
+  w.position_min = INT32_MAX;
+  w.position_max = -1;
+  int64_t total = 0;
+  for (int l = 0; l < L; ++l) {
+    const kvc_cache* c = S->caches[l];
+    for (int b = 0; b < c->batch; ++b) {
+      const int n = n_rows ? n_rows[b] : n_max;
+      w.full_prefix_rows_per_projection += c->len[b] + n;
+      w.incremental_rows_per_projection += n;
+      w.reused_key_value_rows += c->len[b];
+      total += n;
+      if (n > 0) {
+        w.position_min = std::min(w.position_min, c->next_pos[b]);
+        w.position_max = std::max(w.position_max, c->next_pos[b] + n - 1);
+      }
+    }
+  }
+  if (total == 0) {
+    w.position_min = w.position_max = -1;
+    if (work) *work = w;
+    return KVC_OK;
+  }
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "this build has no device kernels");
+  const int per_seq = n_rows != nullptr;
+  DevState& s0 = S->caches[0]->ds;
+  int rc = 0;
+  if (per_seq) {
+    rc = dev_set_rows(s0, n_rows);
+    if (rc) return device_fail(rc, "chunk row upload");
+  }
+  rc = dev_embed(s0, tokens, S->embedding, S->vocab, S->sinusoidal, n_max, per_seq, S->h, S->x);
+  if (rc) return device_fail(rc, "embedding launch");
+  const void* xin = S->x ? S->x : S->h;
+  for (int l = 0; l < L; ++l) {
+    kvc_cache* c = S->caches[l];
+    if (decode) choose_decode_tiles(c);
+    kvc_status st = compute_stages(c, xin, n_max, n_rows, S->a, decode);
+    if (st != KVC_OK) return st;
+    const bool last = l == L - 1;
+    rc = dev_residual(c->ds, S->h, S->a, last ? out : S->h, last ? nullptr : S->x, n_max, per_seq);
+    if (rc) return device_fail(rc, "residual launch");
+  }
+  for (int l = 0; l < L; ++l) {
+    kvc_status st = commit_stage(S->caches[l], n_max, n_rows);
+    if (st != KVC_OK) return st;
+  }
+  if (flags & KVC_ASYNC) {
+    S->pending_async = true;
+    for (kvc_cache* c : S->caches) advance_mirror(c, n_max, n_rows);
+    if (work) *work = w;
+    return KVC_OK;
+  }
+  rc = dev_sync(s0.stream);
+  if (rc) return device_fail(rc, "stream synchronisation");
+  kvc_status st = collect_session_error(S);
+  if (st != KVC_OK) return st;
+  for (kvc_cache* c : S->caches) advance_mirror(c, n_max, n_rows);
+  if (work) *work = w;
   return KVC_OK;
 }
 
@@ -417,6 +796,7 @@ const char* kvc_status_name(kvc_status s) {
     N(KVC_ERR_NONFINITE_QUERY)
     N(KVC_ERR_ROTARY_POSITION)
     N(KVC_ERR_NONFINITE_OUTPUT)
+    N(KVC_ERR_TOKEN_RANGE)
     N(KVC_ERR_BAD_CUT)
     N(KVC_ERR_EMPTY_QUERY)
     N(KVC_ERR_CHUNK_ROWS)
@@ -502,164 +882,11 @@ kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capac
                             void* hip_stream, kvc_cache** out) {
   reset_detail();
   if (!layer || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_cache_create");
-  *out = nullptr;
-  // Chapter 37, layer-kv-cache listing: batch, capacity, position capacity,
-  // element-count overflow, then allocation.
-  if (batch <= 0) return fail_ea(KVC_ERR_ZERO_BATCH, 1, batch, "KV cache batch size must be nonzero");
-  if (capacity <= 0) return fail_ea(KVC_ERR_ZERO_CAPACITY, 1, capacity, "KV cache capacity must be nonzero");
-  if (capacity > layer->rope_max_positions)
-    return fail_ea(KVC_ERR_CAPACITY_EXCEEDS_POSITIONS, layer->rope_max_positions, capacity,
-                   "KV cache capacity %d exceeds RoPE position capacity %d", capacity, layer->rope_max_positions);
-  if (max_chunk_rows <= 0)
-    return fail(KVC_ERR_BAD_ARGUMENT, "max_chunk_rows must be at least 1, got %d", max_chunk_rows);
-  const kvc_params* p = layer->params;
-  const int H = layer->heads, dh = layer->head_width;
-  int64_t elements = 0, cand = 0, pos_elems = 0;
-  if (!checked_mul(batch, H, &elements) || !checked_mul(elements, capacity, &elements) ||
-      !checked_mul(elements, dh, &elements) || !checked_mul(int64_t(batch) * H, int64_t(max_chunk_rows), &cand) ||
-      !checked_mul(cand, dh, &cand) || !checked_mul(batch, capacity, &pos_elems) ||
-      elements > (INT64_MAX / 16) || cand > (INT64_MAX / 16)) {
-    return fail(KVC_ERR_ELEMENT_COUNT_OVERFLOW,
-                "KV cache element count overflows for batch %d, %d heads, capacity %d, and head width %d", batch,
-                H, capacity, dh);
-  }
-  kvc_cache* c = new (std::nothrow) kvc_cache;
-  if (!c) return fail(KVC_ERR_ALLOCATION_FAILED, "host allocation failed");
-  c->batch = batch;
-  c->heads = H;
-  c->head_width = dh;
-  c->model_width = p->model_width;
-  c->capacity = capacity;
-  c->max_chunk_rows = max_chunk_rows;
-  c->dtype = p->dtype;
-  c->params_id = p->id;
-  for (int k = 0; k < 4; ++k) c->revision[k] = p->revision[k];
-  c->rope_feature_width = layer->rope_feature_width();
-  c->rope_max_positions = layer->rope_max_positions;
-  std::memcpy(&c->rope_base_bits, &layer->rope_base, 8);
-  c->rope_base = layer->rope_base;
-  c->pos_mode = layer->pos_mode;
-  c->len.assign(batch, 0);
-  c->next_pos.assign(batch, 0);
-  int rc = dev_current_device(&c->device);
-  if (rc) {
-    free_cache(c);
-    return device_fail(rc, "hipGetDevice");
-  }
-
-  const size_t es = elem_size(p->dtype), as = acc_size(p->dtype);
-  const int max_tiles = (capacity + kDecodeTileRows - 1) / kDecodeTileRows;
-  auto round16 = [](size_t b) { return (b + 15) & ~size_t(15); };
-  DevState& s = c->ds;
-  s.dtype = p->dtype;
-  s.batch = batch;
-  s.heads = H;
-  s.head_width = dh;
-  s.model_width = p->model_width;
-  s.capacity = capacity;
-  s.max_chunk_rows = max_chunk_rows;
-  s.rope = layer->pos_mode == KVC_POS_ROPE;
-  s.max_positions = layer->rope_max_positions;
-  s.scale = 1.0 / std::sqrt(double(dh));
-  s.wq = p->w[0];
-  s.wk = p->w[1];
-  s.wv = p->w[2];
-  s.wo = p->w[3];
-  s.max_tiles = max_tiles;
-  s.tile_rows = kDecodeTileRows;
-  s.stream = hip_stream;
-  c->storage_bytes = int64_t(round16(size_t(elements) * es));
-  struct Alloc {
-    void** p;
-    size_t bytes;
-  } allocs[] = {
-      {&s.keys, size_t(c->storage_bytes)},
-      {&s.values, size_t(c->storage_bytes)},
-      {reinterpret_cast<void**>(&s.len), round16(sizeof(int32_t) * batch)},
-      {reinterpret_cast<void**>(&s.next_pos), round16(sizeof(int32_t) * batch)},
-      {reinterpret_cast<void**>(&s.positions), round16(sizeof(int32_t) * size_t(pos_elems))},
-      {reinterpret_cast<void**>(&s.rows), round16(sizeof(int32_t) * batch)},
-      {&s.cand_k, round16(size_t(cand) * es)},
-      {&s.cand_v, round16(size_t(cand) * es)},
-      {&s.q, round16(size_t(cand) * as)},
-      {&s.partials, round16(size_t(batch) * H * max_tiles * (dh + 2) * as)},
-      {reinterpret_cast<void**>(&s.err), round16(sizeof(ErrWords))},
-      {&s.merged, p->w[3] ? round16(size_t(cand) * as) : 0},  // [B, max_chunk_rows, D]
-  };
-  for (auto& a : allocs) {
-    if (a.bytes == 0) continue;
-    rc = dev_malloc(a.p, a.bytes);
-    if (rc) {
-      *a.p = nullptr;
-      free_cache(c);
-      g_last.expected = int64_t(a.bytes);
-      return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate %zu bytes of KV cache storage", a.bytes);
-    }
-  }
-  rc = dev_host_malloc(reinterpret_cast<void**>(&c->err_host), sizeof(ErrWords));
-  if (rc) {
-    c->err_host = nullptr;
-    free_cache(c);
-    return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate pinned host memory");
-  }
-  // Zero-filled storage (Chapter 37: zeroed backing buffers), zero lengths.
-  for (auto& a : allocs) {
-    if (*a.p == s.err || a.bytes == 0) continue;
-    rc = dev_zero(*a.p, a.bytes, s.stream);
-    if (rc) {
-      free_cache(c);
-      return device_fail(rc, "zero fill");
-    }
-  }
-  rc = dev_clear_err(s.err, s.stream);
-  if (rc) {
-    free_cache(c);
-    return device_fail(rc, "error word init");
-  }
-  // Rotary table: cos/sin of p * base^(-2i/d_h), evaluated in double on the host.
-  if (s.rope) {
-    const int half = dh / 2;
-    const size_t n = size_t(layer->rope_max_positions) * half;
-    std::vector<double> cd(n), sd(n);
-    for (int pos = 0; pos < layer->rope_max_positions; ++pos) {
-      for (int i = 0; i < half; ++i) {
-        const double inv = std::pow(layer->rope_base, -2.0 * double(i) / double(dh));
-        const double ang = double(pos) * inv;
-        cd[size_t(pos) * half + i] = std::cos(ang);
-        sd[size_t(pos) * half + i] = std::sin(ang);
-      }
-    }
-    const size_t bytes = n * as;
-    rc = dev_malloc(&s.rope_cos, round16(bytes));
-    if (rc == 0) rc = dev_malloc(&s.rope_sin, round16(bytes));
-    if (rc) {
-      free_cache(c);
-      return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate the rotary table");
-    }
-    if (as == 8) {
-      rc = dev_copy_h2d_sync(s.rope_cos, cd.data(), bytes, s.stream);
-      if (rc == 0) rc = dev_copy_h2d_sync(s.rope_sin, sd.data(), bytes, s.stream);
-    } else {
-      std::vector<float> cf(cd.begin(), cd.end()), sf(sd.begin(), sd.end());
-      rc = dev_copy_h2d_sync(s.rope_cos, cf.data(), bytes, s.stream);
-      if (rc == 0) rc = dev_copy_h2d_sync(s.rope_sin, sf.data(), bytes, s.stream);
-    }
-    if (rc) {
-      free_cache(c);
-      return device_fail(rc, "rotary table upload");
-    }
-  }
-  rc = dev_sync(s.stream);
-  if (rc) {
-    free_cache(c);
-    return device_fail(rc, "stream synchronisation");
-  }
-  *out = c;
-  return KVC_OK;
+  return create_cache(layer, batch, capacity, max_chunk_rows, hip_stream, nullptr, nullptr, 0, out);
 }
 
 void kvc_cache_destroy(kvc_cache* cache) {
-  if (!cache) return;
+  if (!cache || cache->session) return;  // a session's layer caches go with the session
   (void)dev_sync(cache->ds.stream);
   free_cache(cache);
 }
@@ -669,6 +896,7 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
   reset_detail();
   if (!layer || !cache || !x || !out || (rank > 0 && !shape))
     return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_append_and_attend");
+  if (cache->session) return reject_session_cache("kvc_append_and_attend");
   if (flags & ~int32_t(KVC_ASYNC)) return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
   if (!(flags & KVC_ASYNC)) {
     kvc_status d = check_deferred(cache);
@@ -718,21 +946,7 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
     w.position_min = std::min(w.position_min, cache->next_pos[b]);
     w.position_max = std::max(w.position_max, cache->next_pos[b]);
   }
-  // Split-K tile: the largest power-of-two multiple of 512 rows that still
-  // gives at least 1024 workgroups (four per compute unit); measured on the
-  // bench workloads, fewer and longer tiles stream faster than a finer split.
-  int tile = kDecodeTileRows;
-  int max_len = 0;
-  for (int b = 0; b < cache->batch; ++b) max_len = std::max(max_len, cache->len[b]);
-  for (int64_t cand = kDecodeTileRows; cand <= (int64_t(1) << 30); cand *= 2) {
-    int64_t blocks = 0;
-    for (int b = 0; b < cache->batch; ++b) blocks += (int64_t(cache->len[b]) + cand) / cand;
-    if (blocks * cache->heads < 1024) break;
-    tile = int(cand);
-    if (cand > max_len) break;
-  }
-  cache->ds.tile_rows = tile;
-  cache->ds.single_tile = tile > max_len;
+  choose_decode_tiles(cache);
   st = run_call(cache, x, 1, nullptr, out, flags, true);
   if (st == KVC_OK && work) *work = w;
   return st;
@@ -742,6 +956,7 @@ kvc_status kvc_continue_chunk(const kvc_layer* layer, kvc_cache* cache, const vo
                               const int32_t* n_rows, void* out, int32_t flags, kvc_work* work) {
   reset_detail();
   if (!layer || !cache || !x || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_continue_chunk");
+  if (cache->session) return reject_session_cache("kvc_continue_chunk");
   if (flags & ~int32_t(KVC_ASYNC)) return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
   if (!(flags & KVC_ASYNC)) {
     kvc_status d = check_deferred(cache);
@@ -809,6 +1024,7 @@ kvc_status kvc_continue_chunk(const kvc_layer* layer, kvc_cache* cache, const vo
 kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags) {
   reset_detail();
   if (!cache || !cut) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_truncate");
+  if (cache->session) return reject_session_cache("kvc_truncate");
   if (flags & ~int32_t(KVC_TRUNCATE_KEEP_STALE_POSITION)) return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
   for (int b = 0; b < cache->batch; ++b) {
     if (cut[b] < 0 || cut[b] > cache->len[b]) {
@@ -830,6 +1046,7 @@ kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags) {
 kvc_status kvc_reset(kvc_cache* cache) {
   reset_detail();
   if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
+  if (cache->session) return reject_session_cache("kvc_reset");
   int rc = dev_set_lengths(cache->ds, nullptr, 2);
   if (rc) return device_fail(rc, "length reset");
   std::fill(cache->len.begin(), cache->len.end(), 0);
@@ -999,6 +1216,175 @@ kvc_status kvc_stream_read(const void* buf, int64_t bytes, void* sink, void* hip
   if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "no device kernels in this build");
   const int rc = dev_stream_read(buf, bytes, sink, hip_stream);
   if (rc) return device_fail(rc, "stream read launch");
+  return KVC_OK;
+}
+
+kvc_status kvc_session_create(const kvc_layer* const* layers, int32_t n_layers, const void* embedding,
+                              int32_t vocab, int32_t position_encoding, int32_t batch, int32_t capacity,
+                              int32_t max_chunk_rows, void* hip_stream, kvc_session** out) {
+  reset_detail();
+  if (!layers || !embedding || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_session_create");
+  *out = nullptr;
+  if (n_layers < 1) return fail_ea(KVC_ERR_BAD_ARGUMENT, 1, n_layers, "a session needs at least one layer");
+  if (vocab < 1) return fail_ea(KVC_ERR_BAD_ARGUMENT, 1, vocab, "vocabulary size must be positive");
+  if (position_encoding != KVC_PE_NONE && position_encoding != KVC_PE_SINUSOIDAL)
+    return fail(KVC_ERR_BAD_ARGUMENT, "unknown position encoding %d", position_encoding);
+  for (int l = 0; l < n_layers; ++l) {
+    if (!layers[l]) {
+      g_last.layer = l;
+      return fail(KVC_ERR_NULL_ARGUMENT, "layer %d is null", l);
+    }
+  }
+  const int D = layers[0]->params->model_width;
+  const kvc_dtype dt = layers[0]->params->dtype;
+  for (int l = 1; l < n_layers; ++l) {
+    if (layers[l]->params->model_width != D || layers[l]->params->dtype != dt) {
+      g_last.layer = l;
+      return fail_ea(KVC_ERR_BAD_ARGUMENT, D, layers[l]->params->model_width,
+                     "layer %d has model width %d and type %d, layer 0 has %d and %d", l,
+                     layers[l]->params->model_width, int(layers[l]->params->dtype), D, int(dt));
+    }
+  }
+  int64_t rows_elems = 0;
+  if (batch > 0 && max_chunk_rows > 0 &&
+      (!checked_mul(int64_t(batch) * max_chunk_rows, D, &rows_elems) || rows_elems > (INT64_MAX / 16)))
+    return fail(KVC_ERR_ELEMENT_COUNT_OVERFLOW, "session row buffers overflow for batch %d, %d rows, width %d",
+                batch, max_chunk_rows, D);
+  kvc_session* S = new (std::nothrow) kvc_session;
+  if (!S) return fail(KVC_ERR_ALLOCATION_FAILED, "host allocation failed");
+  S->layers.assign(layers, layers + n_layers);
+  S->batch = batch;
+  S->max_chunk_rows = max_chunk_rows;
+  S->model_width = D;
+  S->vocab = vocab;
+  S->dtype = dt;
+  S->sinusoidal = position_encoding == KVC_PE_SINUSOIDAL;
+  S->embedding = embedding;
+  int rc = dev_malloc(reinterpret_cast<void**>(&S->gate), sizeof(ErrWords) * size_t(n_layers));
+  if (rc) {
+    S->gate = nullptr;
+    free_session(S);
+    return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate the session's failure words");
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    kvc_cache* c = nullptr;
+    const kvc_status st = create_cache(layers[l], batch, capacity, max_chunk_rows, hip_stream, &S->gate[l], S->gate,
+                                       n_layers, &c);
+    if (st != KVC_OK) {
+      const kvc_error_detail saved = g_last;
+      free_session(S);
+      g_last = saved;
+      g_last.layer = l;
+      return st;
+    }
+    S->caches.push_back(c);
+  }
+  const size_t as = acc_size(dt), es = elem_size(dt);
+  const size_t rows_bytes = (size_t(rows_elems) * as + 15) & ~size_t(15);
+  rc = dev_malloc(&S->h, rows_bytes);
+  if (rc == 0) rc = dev_malloc(&S->a, rows_bytes);
+  if (rc == 0 && dt == KVC_BF16) rc = dev_malloc(&S->x, (size_t(rows_elems) * es + 15) & ~size_t(15));
+  if (rc) {
+    free_session(S);
+    return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate the session's row buffers");
+  }
+  *out = S;
+  return KVC_OK;
+}
+
+void kvc_session_destroy(kvc_session* session) { free_session(session); }
+
+kvc_status kvc_session_chunk(kvc_session* session, const int32_t* tokens, int32_t n_max, const int32_t* n_rows,
+                             void* out, int32_t flags, kvc_work* work) {
+  reset_detail();
+  if (!session || !tokens || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_session_chunk");
+  if (flags & ~int32_t(KVC_ASYNC)) return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
+  if (n_max < 1 || n_max > session->max_chunk_rows)
+    return fail_ea(KVC_ERR_CHUNK_ROWS, session->max_chunk_rows, n_max, "chunk rows %d outside [1, %d]", n_max,
+                   session->max_chunk_rows);
+  if (n_rows) {
+    for (int b = 0; b < session->batch; ++b) {
+      if (n_rows[b] < 0 || n_rows[b] > n_max) {
+        g_last.sequence = b;
+        return fail_ea(KVC_ERR_CHUNK_ROWS, n_max, n_rows[b], "sequence %d has %d chunk rows, outside [0, %d]", b,
+                       n_rows[b], n_max);
+      }
+    }
+  }
+  return session_call(session, tokens, n_max, n_rows, out, flags, work, false);
+}
+
+kvc_status kvc_session_decode(kvc_session* session, const int32_t* tokens, void* out, int32_t flags,
+                              kvc_work* work) {
+  reset_detail();
+  if (!session || !tokens || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_session_decode");
+  if (flags & ~int32_t(KVC_ASYNC)) return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
+  return session_call(session, tokens, 1, nullptr, out, flags, work, true);
+}
+
+kvc_status kvc_session_truncate(kvc_session* session, const int32_t* cut, int32_t flags) {
+  reset_detail();
+  if (!session || !cut) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_session_truncate");
+  if (flags & ~int32_t(KVC_TRUNCATE_KEEP_STALE_POSITION))
+    return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
+  for (size_t l = 0; l < session->caches.size(); ++l) {
+    const kvc_cache* c = session->caches[l];
+    for (int b = 0; b < c->batch; ++b) {
+      if (cut[b] < 0 || cut[b] > c->len[b]) {
+        g_last.layer = int32_t(l);
+        g_last.sequence = b;
+        return fail_ea(KVC_ERR_BAD_CUT, c->len[b], cut[b], "cut %d of sequence %d is outside [0, %d]", cut[b], b,
+                       c->len[b]);
+      }
+    }
+  }
+  const bool stale = flags & KVC_TRUNCATE_KEEP_STALE_POSITION;
+  for (kvc_cache* c : session->caches) {
+    const int rc = dev_set_lengths(c->ds, cut, stale ? 1 : 0);
+    if (rc) return device_fail(rc, "length update");
+  }
+  for (kvc_cache* c : session->caches) {
+    for (int b = 0; b < c->batch; ++b) {
+      c->len[b] = cut[b];
+      if (!stale) c->next_pos[b] = cut[b];
+    }
+  }
+  return KVC_OK;
+}
+
+kvc_status kvc_session_reset(kvc_session* session) {
+  reset_detail();
+  if (!session) return fail(KVC_ERR_NULL_ARGUMENT, "null session");
+  for (kvc_cache* c : session->caches) {
+    const int rc = dev_set_lengths(c->ds, nullptr, 2);
+    if (rc) return device_fail(rc, "length reset");
+  }
+  for (kvc_cache* c : session->caches) {
+    std::fill(c->len.begin(), c->len.end(), 0);
+    std::fill(c->next_pos.begin(), c->next_pos.end(), 0);
+  }
+  return KVC_OK;
+}
+
+kvc_status kvc_session_sync(kvc_session* session) {
+  reset_detail();
+  if (!session) return fail(KVC_ERR_NULL_ARGUMENT, "null session");
+  session->pending_async = true;  // always look at the device words
+  kvc_status st = check_deferred_session(session);
+  if (st != KVC_OK) return st;
+  for (kvc_cache* c : session->caches) {
+    st = resync_lengths(c);
+    if (st != KVC_OK) return st;
+  }
+  return KVC_OK;
+}
+
+kvc_status kvc_session_layer_cache(kvc_session* session, int32_t layer, kvc_cache** out) {
+  reset_detail();
+  if (!session || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_session_layer_cache");
+  if (layer < 0 || layer >= int32_t(session->caches.size()))
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, int64_t(session->caches.size()), layer, "layer %d out of range", layer);
+  *out = session->caches[layer];
   return KVC_OK;
 }
 

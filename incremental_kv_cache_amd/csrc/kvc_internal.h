@@ -19,7 +19,8 @@ struct ErrWords {
   unsigned long long query;     // non-finite rotated query
   unsigned long long position;  // sequence index whose row position reached max positions
   unsigned long long output;    // non-finite attention output, flat index over [B,n,D]
-  unsigned long long pad[3];
+  unsigned long long token;     // session calls: token id outside the embedding, flat index over [B,n]
+  unsigned long long pad[2];
 };
 constexpr unsigned long long kErrClear = ~0ull;
 
@@ -58,6 +59,11 @@ struct DevState {
   void* rope_cos;  // [max_positions, d_h / 2] accumulate type (null without rotation)
   void* rope_sin;
   ErrWords* err;
+  // The failure words every state-changing kernel checks before it writes:
+  // the cache's own (gate_count 1), or those of every layer of a session, so
+  // that one layer's failure keeps every layer unchanged.
+  const ErrWords* gate;
+  int gate_count;
   void* stream;  // hipStream_t
 };
 
@@ -119,6 +125,16 @@ int dev_attend_chunk(const DevState& s, int n_max, int per_seq_rows, const Chunk
 // out[b, i, :] = merged[b, i, :] x W_o (rows i < n_b).
 int dev_output_project(const DevState& s, int n_max, int per_seq_rows, void* out);
 int dev_commit(const DevState& s, int n_max, int per_seq_rows);
+
+// Session stages (rows i < n_b of [B, n_max, D]; the first layer's DevState
+// supplies geometry, next positions, rows and the token failure word).
+// h[b, i] = embedding[tokens[b, i]] (+ sinusoidal encoding of next_position +
+// i); x (non-null for bf16 sessions) receives h rounded to the weight type.
+int dev_embed(const DevState& s, const int32_t* tokens, const void* embedding, int vocab, int sinusoidal,
+              int n_max, int per_seq_rows, void* h, void* x);
+// h_out = h_in + tanh(a) (the tanh-residual block); x as for dev_embed.
+int dev_residual(const DevState& s, const void* h_in, const void* a, void* h_out, void* x, int n_max,
+                 int per_seq_rows);
 
 int dev_event_create(void** e);
 void dev_event_destroy(void* e);

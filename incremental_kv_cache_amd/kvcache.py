@@ -12,8 +12,8 @@ import ctypes as C
 import numpy as np
 
 from . import capi
-from .capi import (KVC_ASYNC, KVC_BF16, KVC_F32, KVC_F64, KVC_POS_NONE, KVC_POS_ROPE, KVC_STAGES,  # noqa: F401
-                   KVC_SYNC, KVC_TRUNCATE_KEEP_STALE_POSITION)
+from .capi import (KVC_ASYNC, KVC_BF16, KVC_F32, KVC_F64, KVC_PE_NONE, KVC_PE_SINUSOIDAL,  # noqa: F401
+                   KVC_POS_NONE, KVC_POS_ROPE, KVC_STAGES, KVC_SYNC, KVC_TRUNCATE_KEEP_STALE_POSITION)
 
 
 class KvcError(RuntimeError):
@@ -29,7 +29,7 @@ class KvcError(RuntimeError):
 def _detail(lib) -> dict:
     d = lib.kvc_last_error().contents
     return {
-        "status": d.status, "parameter": d.parameter, "sequence": d.sequence,
+        "status": d.status, "parameter": d.parameter, "sequence": d.sequence, "layer": d.layer,
         "expected": d.expected, "actual": d.actual,
         "cache_revision": d.cache_revision, "layer_revision": d.layer_revision,
         "flat_index": d.flat_index, "value": d.value,
@@ -101,6 +101,17 @@ class Layer(_Handle):
 
 class Cache(_Handle):
     _destroy = "kvc_cache_destroy"
+
+
+class Session(_Handle):
+    _destroy = "kvc_session_destroy"
+
+
+class _CacheView(Cache):
+    """A session's layer cache: borrowed, never destroyed through this handle."""
+
+    def close(self):
+        self.ptr = None
 
 
 def _lib(lib):
@@ -302,3 +313,86 @@ def kvc_status_name(status: int, *, lib=None) -> str:
 
 def kvc_last_error(*, lib=None) -> dict:
     return _detail(_lib(lib))
+
+
+# ---- model-wide session ----------------------------------------------------
+
+def kvc_session_create(layers, embedding, vocab: int, position_encoding: int, batch: int, capacity: int,
+                       max_chunk_rows: int = 1, stream=None) -> Session:
+    """One cache per layer of ``layers`` behind one token stream.  embedding:
+    device tensor [vocab, D] in the accumulate type (float64 for f64 layers,
+    float32 otherwise)."""
+    lib = layers[0]._lib
+    if stream is None:
+        try:
+            stream = _torch().cuda.current_stream().cuda_stream
+        except Exception:
+            stream = 0
+    arr = (C.c_void_p * len(layers))(*[l.ptr for l in layers])
+    out = C.c_void_p()
+    _check(lib, lib.kvc_session_create(arr, len(layers), _dev_ptr(embedding), vocab, position_encoding, batch,
+                                       capacity, max_chunk_rows, C.c_void_p(stream or 0), C.byref(out)))
+    h = Session(lib, out)
+    h.layers = list(layers)
+    h.embedding = embedding
+    h.caches = [kvc_session_layer_cache(h, l) for l in range(len(layers))]
+    h.desc = h.caches[0].desc
+    return h
+
+
+def kvc_session_layer_cache(session: Session, layer: int) -> Cache:
+    """A borrowed view of the session's cache of ``layer`` (read-only calls)."""
+    out = C.c_void_p()
+    _check(session._lib, session._lib.kvc_session_layer_cache(session.ptr, layer, C.byref(out)))
+    c = _CacheView(session._lib, out)
+    c.desc = kvc_cache_describe(c)
+    c.session = session
+    return c
+
+
+def kvc_session_chunk(session: Session, tokens, n_rows=None, out=None, flags: int = KVC_SYNC):
+    """tokens: device int32 tensor [B, n_max]; n_rows: host ints [B] or None.
+    Returns (last layer's rows [B, n_max, D], work summed over the layers)."""
+    lib = session._lib
+    torch = _torch()
+    if tokens.dtype != torch.int32 or tokens.dim() != 2:
+        raise TypeError("tokens must be a device int32 tensor [B, n]")
+    n_max = int(tokens.shape[1])
+    if out is None:
+        out = torch.zeros((session.desc["batch"], n_max, session.desc["model_width"]),
+                          dtype=_out_dtype(session.desc["kv_dtype"]), device=tokens.device)
+    rows_ptr = None
+    if n_rows is not None:
+        arr = np.ascontiguousarray(np.asarray(n_rows, dtype=np.int32))
+        rows_ptr = arr.ctypes.data_as(capi.PI32)
+    w = capi.Work()
+    _check(lib, lib.kvc_session_chunk(session.ptr, _dev_ptr(tokens), n_max, rows_ptr, _dev_ptr(out), flags,
+                                      C.byref(w)))
+    return out, w.as_dict()
+
+
+def kvc_session_decode(session: Session, tokens, out=None, flags: int = KVC_SYNC):
+    """tokens: device int32 tensor [B].  Returns (last layer's rows [B, 1, D], work)."""
+    lib = session._lib
+    torch = _torch()
+    if tokens.dtype != torch.int32:
+        raise TypeError("tokens must be a device int32 tensor [B]")
+    if out is None:
+        out = torch.empty((session.desc["batch"], 1, session.desc["model_width"]),
+                          dtype=_out_dtype(session.desc["kv_dtype"]), device=tokens.device)
+    w = capi.Work()
+    _check(lib, lib.kvc_session_decode(session.ptr, _dev_ptr(tokens), _dev_ptr(out), flags, C.byref(w)))
+    return out, w.as_dict()
+
+
+def kvc_session_truncate(session: Session, cut, flags: int = 0) -> None:
+    arr = np.ascontiguousarray(np.broadcast_to(np.asarray(cut, dtype=np.int32), (session.desc["batch"],)))
+    _check(session._lib, session._lib.kvc_session_truncate(session.ptr, arr.ctypes.data_as(capi.PI32), flags))
+
+
+def kvc_session_reset(session: Session) -> None:
+    _check(session._lib, session._lib.kvc_session_reset(session.ptr))
+
+
+def kvc_session_sync(session: Session) -> None:
+    _check(session._lib, session._lib.kvc_session_sync(session.ptr))

@@ -22,9 +22,11 @@ Everything is plain NumPy in float64, written for a reader to check by eye:
   incremental decode and prefix-continuation steps in the pages' order, used
   only to pin the invariants the pages state.
 * ``toy_decoder`` -- the prefix-reuse note's two-layer, one-head decoder.
+* ``stack``       -- the model-wide stack (embedding, positions, several layers
+  with the tanh residual) that a session of per-layer caches must reproduce.
 * ``prefix``      -- longest-common-prefix cut and projection-row counts.
 
 Parity status of each function is given in its docstring; the pins live in
 ``tests/test_oracle_pins.py``.  Functions with no pin say "parity unpinned".
 """
-from . import attention, prefix, toy_decoder  # noqa: F401
+from . import attention, prefix, stack, toy_decoder  # noqa: F401

@@ -46,10 +46,15 @@ int dev_clear_err(ErrWords* err, void*) {
   return 0;
 }
 static bool any_error(const ErrWords* e) {
-  return (e->key & e->value & e->query & e->position & e->output) != kErrClear;
+  return (e->key & e->value & e->query & e->position & e->output & e->token) != kErrClear;
+}
+static bool gate_closed(const DevState& s) {
+  for (int k = 0; k < s.gate_count; ++k)
+    if (any_error(&s.gate[k])) return true;
+  return false;
 }
 int dev_set_lengths(const DevState& s, const int32_t* vals, int mode) {
-  if (any_error(s.err)) return 0;
+  if (gate_closed(s)) return 0;
   for (int b = 0; b < s.batch; ++b) {
     if (mode == 2) {
       s.len[b] = 0;
@@ -71,6 +76,8 @@ int dev_merge_decode(const DevState&, void*) { return 1; }
 int dev_attend_chunk(const DevState&, int, int, const ChunkOrder&, void*) { return 1; }
 int dev_output_project(const DevState&, int, int, void*) { return 1; }
 int dev_commit(const DevState&, int, int) { return 1; }
+int dev_embed(const DevState&, const int32_t*, const void*, int, int, int, int, void*, void*) { return 1; }
+int dev_residual(const DevState&, const void*, const void*, void*, void*, int, int) { return 1; }
 int dev_event_create(void** e) {
   *e = std::malloc(1);
   return 0;

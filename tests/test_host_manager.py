@@ -294,3 +294,86 @@ def test_decode_sequence_order_longest_first(lib):
     assert n == 5 and list(seq[:5]) == [1, 2, 4, 0, 3]
     big, bp = _i32(np.arange(300))
     assert lib.kvc_test_seq_order(300, bp, seq.ctypes.data_as(C.POINTER(C.c_int32))) == 0
+
+
+# ------------------------------------------------------------- session ----
+
+def session(lib, layers, vocab=10, pe=capi.KVC_PE_SINUSOIDAL, batch=2, cap=4, chunk=4):
+    arr = (C.c_void_p * max(1, len(layers)))(*layers)
+    s = C.c_void_p()
+    st = lib.kvc_session_create(arr, len(layers), DUMMY, vocab, pe, batch, cap, chunk, None, C.byref(s))
+    return st, s
+
+
+def test_session_create_checks_and_names_the_layer(lib):
+    """Session construction: null arguments, counts, encoding, layers of other width,
+    then each layer's cache construction with detail.layer naming the layer."""
+    p = params(lib)
+    l0, l1 = layer(lib, p), layer(lib, p, max_pos=4)
+    assert lib.kvc_session_create(None, 1, DUMMY, 10, 1, 1, 4, 1, None, C.byref(C.c_void_p())) == \
+        capi.KVC_ERR_NULL_ARGUMENT
+    assert session(lib, [])[0] == capi.KVC_ERR_BAD_ARGUMENT
+    assert session(lib, [l0], vocab=0)[0] == capi.KVC_ERR_BAD_ARGUMENT
+    assert session(lib, [l0], pe=7)[0] == capi.KVC_ERR_BAD_ARGUMENT
+    st, _ = session(lib, [l0, None])
+    assert st == capi.KVC_ERR_NULL_ARGUMENT and lib.kvc_last_error().contents.layer == 1
+    wide = layer(lib, params(lib, d=8))
+    st, _ = session(lib, [l0, wide])
+    assert st == capi.KVC_ERR_BAD_ARGUMENT and lib.kvc_last_error().contents.layer == 1
+    short = layer(lib, p, max_pos=3)
+    st, _ = session(lib, [l0, l1, short])
+    d = lib.kvc_last_error().contents
+    assert st == capi.KVC_ERR_CAPACITY_EXCEEDS_POSITIONS and d.layer == 2 and (d.expected, d.actual) == (3, 4)
+    st, s = session(lib, [l0, l1])
+    assert st == capi.KVC_OK
+    lib.kvc_session_destroy(s)
+
+
+def test_session_layer_caches_are_read_only_views(lib):
+    """A session's layer cache answers the read-only calls but refuses compute,
+    truncate and reset (every layer must move together), and destroying it is a no-op."""
+    p = params(lib)
+    l0, l1 = layer(lib, p), layer(lib, p)
+    st, s = session(lib, [l0, l1])
+    assert st == 0
+    c = C.c_void_p()
+    assert lib.kvc_session_layer_cache(s, 2, C.byref(c)) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_session_layer_cache(s, 1, C.byref(c)) == 0
+    cut, cp = np.zeros(2, np.int32), None
+    cp = cut.ctypes.data_as(capi.PI32)
+    assert lib.kvc_truncate(c, cp, 0) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_reset(c) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_continue_chunk(l1, c, DUMMY, 1, None, DUMMY, 0, None) == capi.KVC_ERR_BAD_ARGUMENT
+    assert append(lib, l1, c, [2, 1, 4]) == capi.KVC_ERR_BAD_ARGUMENT
+    assert state(lib, c, batch=2)[:2] == ([0, 0], [0, 0])
+    lib.kvc_cache_destroy(c)  # ignored: the session owns it
+    assert lib.kvc_lengths(c, None, None) == 0
+    lib.kvc_session_destroy(s)
+
+
+def test_session_request_checks(lib):
+    """Session calls check rows, each layer's binding in layer order (detail.layer),
+    then cuts; a valid request reaches the launch point (no kernels in this build)."""
+    p0, p1 = params(lib), params(lib)
+    l0, l1 = layer(lib, p0), layer(lib, p1)
+    st, s = session(lib, [l0, l1])
+    assert st == 0
+    w = capi.Work()
+    assert lib.kvc_session_chunk(s, DUMMY, 0, None, DUMMY, 0, C.byref(w)) == capi.KVC_ERR_CHUNK_ROWS
+    assert lib.kvc_session_chunk(s, DUMMY, 5, None, DUMMY, 0, C.byref(w)) == capi.KVC_ERR_CHUNK_ROWS
+    rows = np.array([1, 3], np.int32)
+    assert lib.kvc_session_chunk(s, DUMMY, 2, rows.ctypes.data_as(capi.PI32), DUMMY, 0, C.byref(w)) == \
+        capi.KVC_ERR_CHUNK_ROWS
+    assert lib.kvc_session_decode(s, DUMMY, DUMMY, 0, C.byref(w)) == capi.KVC_ERR_DEVICE
+    assert lib.kvc_session_decode(s, None, DUMMY, 0, C.byref(w)) == capi.KVC_ERR_NULL_ARGUMENT
+    assert lib.kvc_params_mark_updated(p1, 1) == 0
+    assert lib.kvc_session_decode(s, DUMMY, DUMMY, 0, C.byref(w)) == capi.KVC_ERR_CACHE_LAYER_REVISION_MISMATCH
+    d = lib.kvc_last_error().contents
+    assert d.layer == 1 and d.parameter == 1
+    cut = np.array([1, 0], np.int32)
+    assert lib.kvc_session_truncate(s, cut.ctypes.data_as(capi.PI32), 0) == capi.KVC_ERR_BAD_CUT
+    assert lib.kvc_last_error().contents.layer == 0
+    cut[:] = 0
+    assert lib.kvc_session_truncate(s, cut.ctypes.data_as(capi.PI32), 0) == 0
+    assert lib.kvc_session_reset(s) == 0
+    lib.kvc_session_destroy(s)

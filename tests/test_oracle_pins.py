@@ -15,6 +15,7 @@ import pytest
 from incremental_kv_cache_amd import synth
 from oracle import attention as A
 from oracle import prefix as P
+from oracle import stack as S
 from oracle import toy_decoder as T
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -328,6 +329,65 @@ def test_sinusoidal_encoding_values():
     np.testing.assert_array_equal(pe[0], [0.0, 1.0] * 8)
     assert pe[1, 0] == math.sin(1.0) and pe[2, 1] == math.cos(3.0)
     assert pe[2, 14] == pytest.approx(math.sin(3.0 / 10000 ** (14 / 16)), rel=1e-15)
+
+
+# ----------------------------------------------------------------- stack ---
+
+def _stack_layers(seed, D=32, heads=(2, 4, 1), rope=(True, False, True), wo=(False, True, False)):
+    layers = []
+    for l, (h, r, o) in enumerate(zip(heads, rope, wo)):
+        w = [synth.normal(seed, 40 + 4 * l + j, (D, D), std=D ** -0.5) for j in range(4)]
+        layers.append(S.Layer(w[0], w[1], w[2], heads=h, rope=r, wo=w[3] if o else None))
+    return layers
+
+
+def test_stack_reduces_to_the_toy_decoder():
+    """Two one-head, width-16 layers without rotation or W_o and with sinusoidal
+    positions are the note's toy decoder (written independently in toy_decoder)."""
+    e, ws = synth.toy_model_arrays(11)
+    toy = T.ToyModel(e, ws)
+    layers = [S.Layer(*w, heads=1, rope=False) for w in ws]
+    tokens = [3, 1, 4, 1, 5, 9, 2, 6, 5, 3]
+    a, _ = T.full_forward(toy, tokens)
+    b, _ = S.forward(e, layers, tokens)
+    np.testing.assert_allclose(b, a, rtol=0, atol=1e-14)
+
+
+def test_stack_with_zero_values_keeps_the_input_rows():
+    """W_v = 0 makes every attention output 0 and tanh(0) = 0: the rows leave the
+    stack exactly as they entered (embedding + positions)."""
+    D = 32
+    e = synth.normal(5, 6, (20, D))
+    z = np.zeros((D, D))
+    layers = [S.Layer(synth.normal(5, 40 + l, (D, D)), synth.normal(5, 50 + l, (D, D)), z, heads=2)
+              for l in range(3)]
+    tokens = [4, 19, 0, 7, 7]
+    h, _ = S.forward(e, layers, tokens)
+    np.testing.assert_array_equal(h, e[tokens] + S.sinusoidal(range(5), D))
+
+
+def test_stack_rows_do_not_depend_on_later_tokens():
+    """Causality through the whole stack (prefix-reuse note, 'First, one history
+    edit': the state of a common prefix does not depend on later tokens), and the
+    first layer's cache is causal_layer's cache of the input rows."""
+    D = 32
+    e = synth.normal(6, 6, (40, D))
+    layers = _stack_layers(6, D)
+    tokens = [int(t) for t in synth.uniform_int(6, synth.STREAM_TOKENS, 12, 0, 39)]
+    full, kv = S.forward(e, layers, tokens)
+    part, kv_part = S.forward(e, layers, tokens[:7])
+    np.testing.assert_allclose(part, full[:7], rtol=0, atol=1e-13)
+    for (k, v), (kp, vp) in zip(kv, kv_part):
+        np.testing.assert_allclose(kp, k[:, :7], rtol=0, atol=1e-13)
+    h0 = e[tokens] + S.sinusoidal(range(12), D)
+    r = A.causal_layer(h0, *layers[0].w, heads=2, rope=True)
+    np.testing.assert_array_equal(kv[0][0], r["keys"])
+    np.testing.assert_array_equal(kv[0][1], r["values"])
+    edited = list(tokens)
+    edited[7] = (edited[7] + 1) % 40
+    alt, _ = S.forward(e, layers, edited)
+    np.testing.assert_array_equal(alt[:7], full[:7])
+    assert np.max(np.abs(alt[7:] - full[7:])) > 1e-3
 
 
 # ---------------------------------------------------------------- inputs ---
