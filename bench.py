@@ -15,6 +15,9 @@ Workloads (default: headline):
   long      B=4, C=32768, t=32768 for every sequence
   chunk     B=8, C=16384, cut_b uniform on [0, 8192], 512-row suffix chunk per
             sequence (step = truncate to cut + kvc_continue_chunk)
+  session   a 4-layer model-wide session of headline-shaped layers (vocab 8192,
+            sinusoidal positions, tanh residual), t=4096: step = kvc_session_truncate
+            + kvc_session_decode of the whole stack
 
 Prints one JSON line (rank 0).  `roofline` describes the dominant kernel, timed
 with HIP events recorded by the library on the cache's stream.  `cpu_baseline`
@@ -68,6 +71,7 @@ WORKLOADS = {
     "ragged": dict(B=32, H=32, dh=128, C=4096, t="uniform", kind="decode"),
     "long": dict(B=4, H=32, dh=128, C=32768, t="full", kind="decode"),
     "chunk": dict(B=8, H=32, dh=128, C=16384, cut_max=8192, n=512, kind="chunk"),
+    "session": dict(B=32, H=32, dh=128, C=4096, layers=4, vocab=8192, kind="session"),
 }
 
 
@@ -399,6 +403,74 @@ def run_chunk(name, wl, steps, warmup, cpu):
     return res
 
 
+def run_session(name, wl, steps, warmup, cpu):
+    """Whole-stack decode through a kvc_session: embedding, L layers of headline
+    shape, residuals, all-layer commit.  The CPU baseline is omitted: the oracle's
+    stack recomputes every row of every layer (no cached step)."""
+    import torch
+    from incremental_kv_cache_amd import kvcache as K
+    from incremental_kv_cache_amd import synth
+
+    B, H, dh, C, L, V = wl["B"], wl["H"], wl["dh"], wl["C"], wl["layers"], wl["vocab"]
+    D = H * dh
+    t0 = time.time()
+    layers = []
+    with _pool() as ex:
+        for l in range(L):
+            ws = list(ex.map(lambda st: synth.round_to_bf16_bits(
+                synth.normal(SEED + 100 * l, st, (D, D), std=D ** -0.5)),
+                (synth.STREAM_WQ, synth.STREAM_WK, synth.STREAM_WV)))
+            params = K.kvc_params_create(*[to_dev_bf16(w) for w in ws])
+            layers.append(K.kvc_layer_create(params, H, K.KVC_POS_ROPE, 10000.0, C))
+    emb = torch.from_numpy(synth.normal(SEED, synth.STREAM_EMBED, (V, D)).astype(np.float32)).cuda()
+    sess = K.kvc_session_create(layers, emb, V, K.KVC_PE_SINUSOIDAL, B, C, max_chunk_rows=512)
+    start = C - 1
+    toks = synth.uniform_int(SEED, synth.STREAM_TOKENS, B * C, 0, V - 1).reshape(B, C).astype(np.int32)
+    for first in range(0, start, 512):
+        n = min(512, start - first)
+        K.kvc_session_chunk(sess, torch.from_numpy(np.ascontiguousarray(toks[:, first:first + n])).cuda(),
+                            flags=K.KVC_ASYNC)
+    K.kvc_session_sync(sess)
+    log(f"setup: {L} layers, prefilled {B * start} rows per layer in {time.time() - t0:.1f}s")
+    tok = torch.from_numpy(np.ascontiguousarray(toks[:, start])).cuda()
+    out = torch.empty(B, 1, D, dtype=torch.float32, device="cuda")
+
+    def step():
+        K.kvc_session_truncate(sess, [start] * B)
+        K.kvc_session_decode(sess, tok, out=out, flags=K.KVC_ASYNC)
+
+    sec = time_steps(step, steps, warmup)
+    K.kvc_session_sync(sess)
+    for c in sess.caches:
+        K.kvc_profile_enable(c, steps)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    att = []
+    for c in sess.caches:
+        ms, calls = K.kvc_profile_read(c)
+        att.append(ms[1] / calls[1])
+        K.kvc_profile_enable(c, 0)
+    K.kvc_session_sync(sess)
+    pct = step_percentiles(step, steps)
+    K.kvc_session_sync(sess)
+    kv_bytes = 2 * B * H * C * dh * 2  # per layer: t = C rows per lane
+    attend_ms = float(np.mean(att))
+    att_gbps = kv_bytes / (attend_ms * 1e-3) / 1e9
+    return {
+        "metric": f"model-wide decode tokens/s ({L} layers)", "value": B / sec, "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{name}: {L}-layer session, B={B} H={H} d_h={dh} C={C} t={C}, vocab {V}, "
+                               f"sinusoidal positions, tanh residual, bf16 K/V", "layers": L, "seed": SEED},
+        "step_ms_percentiles": pct,
+        "attend_ms_per_layer": att,
+        "roofline": {"bound": "hbm", "kernel": "attend_decode_bf16_kernel", "achieved": att_gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": att_gbps / HBM_PEAK_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": kv_bytes},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -428,7 +500,7 @@ def main():
     from incremental_kv_cache_amd import capi
     capi.lib()  # fails loudly if the HIP library is missing
     wl = WORKLOADS[a.workload]
-    fn = run_decode if wl["kind"] == "decode" else run_chunk
+    fn = {"decode": run_decode, "chunk": run_chunk, "session": run_session}[wl["kind"]]
     res = fn(a.workload, wl, a.steps, a.warmup, not a.no_cpu_baseline)
     print(json.dumps(res), flush=True)
 
