@@ -18,6 +18,9 @@ Workloads (default: headline):
   session   a 4-layer model-wide session of headline-shaped layers (vocab 8192,
             sinusoidal positions, tanh residual), t=4096: step = kvc_session_truncate
             + kvc_session_decode of the whole stack
+  paged     headline with block-paged K/V (kvc_cache_create_paged, 512-row blocks,
+            pool = B x C / 512 blocks, handed out across sequences by the prefill)
+  paged_ragged  ragged lengths with a pool of exactly sum_b ceil(t_b / 512) blocks
 
 Prints one JSON line (rank 0).  `roofline` describes the dominant kernel, timed
 with HIP events recorded by the library on the cache's stream.  `cpu_baseline`
@@ -72,6 +75,8 @@ WORKLOADS = {
     "long": dict(B=4, H=32, dh=128, C=32768, t="full", kind="decode"),
     "chunk": dict(B=8, H=32, dh=128, C=16384, cut_max=8192, n=512, kind="chunk"),
     "session": dict(B=32, H=32, dh=128, C=4096, layers=4, vocab=8192, kind="session"),
+    "paged": dict(B=32, H=32, dh=128, C=4096, t="full", kind="decode", block_rows=512),
+    "paged_ragged": dict(B=32, H=32, dh=128, C=4096, t="uniform", kind="decode", block_rows=512),
 }
 
 
@@ -118,7 +123,6 @@ def setup(wl, max_chunk=512):
     wdev = [to_dev_bf16(w) for w in ws]
     params = K.kvc_params_create(*wdev)
     layer = K.kvc_layer_create(params, H, K.KVC_POS_ROPE, 10000.0, C)
-    cache = K.kvc_cache_create(layer, B, C, max_chunk_rows=max_chunk)
     if wl["kind"] == "decode":
         if wl["t"] == "full":
             start = [C - 1] * B
@@ -126,6 +130,13 @@ def setup(wl, max_chunk=512):
             start = [int(v) - 1 for v in synth.uniform_int(SEED, synth.STREAM_LENGTHS, B, 1, C)]
     else:
         start = [int(v) for v in synth.uniform_int(SEED, synth.STREAM_LENGTHS, B, 0, wl["cut_max"])]
+    br = wl.get("block_rows")
+    if br:
+        # blocks for every row a step holds (start + the appended row)
+        pool = sum((s + 1 + br - 1) // br for s in start)
+        cache = K.kvc_cache_create_paged(layer, B, C, br, pool, max_chunk_rows=max_chunk)
+    else:
+        cache = K.kvc_cache_create(layer, B, C, max_chunk_rows=max_chunk)
     L = max(start)
     pre_out = torch.empty(B, max_chunk, D, dtype=torch.float32, device="cuda")
     for first in range(0, L, max_chunk):
@@ -140,6 +151,18 @@ def setup(wl, max_chunk=512):
     assert ln.tolist() == start, "prefill lengths differ"
     log(f"setup: prefilled {sum(start)} rows in {time.time() - t0:.1f}s")
     return dict(weights_bits=ws, wdev=wdev, params=params, layer=layer, cache=cache, start=start, D=D)
+
+
+def paging_summary(env, wl):
+    """Pool geometry of a paged workload next to the contiguous footprint."""
+    from incremental_kv_cache_amd import kvcache as K
+    cache = env["cache"]
+    d = cache.desc
+    used, free = K.kvc_pool_usage(cache)
+    row_bytes = 2 * wl["H"] * wl["dh"] * 2  # K and V, bf16
+    return {"block_rows": d["block_rows"], "pool_blocks": d["pool_blocks"], "blocks_in_use": used,
+            "pool_bytes": d["pool_blocks"] * d["block_rows"] * row_bytes,
+            "contiguous_bytes": wl["B"] * wl["C"] * row_bytes}
 
 
 def measured_traffic(name):
@@ -318,6 +341,7 @@ def run_decode(name, wl, steps, warmup, cpu):
     st = stage_times(cache, step, steps)
     K.kvc_sync(cache)
     pct = step_percentiles(step, steps)
+    paging = paging_summary(env, wl) if wl.get("block_rows") else None
     K.kvc_sync(cache)
     torch.cuda.synchronize()
     achievable = achievable_read_gbps()
@@ -331,7 +355,8 @@ def run_decode(name, wl, steps, warmup, cpu):
         "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{name}: one-layer cached decode, B={B} H={H} d_h={dh} C={wl['C']} "
-                               f"t={'uniform[1,%d]' % wl['C'] if wl['t'] == 'uniform' else t[0]}, bf16 K/V, "
+                               f"t={'uniform[1,%d]' % wl['C'] if wl['t'] == 'uniform' else t[0]}, bf16 K/V"
+                               f"{', block-paged %d-row blocks' % wl['block_rows'] if paging else ''}, "
                                f"fp32 accumulate", "batch": B, "heads": H, "head_width": dh,
                    "capacity": wl["C"], "t_mean": float(np.mean(t)), "seed": SEED},
         "kv_read_GBps": attn_merge_gbps, "kv_read_frac_of_peak": attn_merge_gbps / HBM_PEAK_GBPS,
@@ -342,6 +367,8 @@ def run_decode(name, wl, steps, warmup, cpu):
                      "traffic": measured_traffic(name), "algorithmic_bytes_per_launch": kv_bytes,
                      "achievable_read_GBps": achievable, "frac_of_achievable": att_gbps / achievable},
     }
+    if paging:
+        res["paging"] = paging
     out_np = out.double().cpu().numpy()[:, 0]
     if cpu:
         cb, worst, n = cpu_baseline_decode(env, wl, out_np, x_bits)

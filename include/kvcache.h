@@ -59,6 +59,9 @@ enum {
   KVC_ERR_CACHE_LAYER_REVISION_MISMATCH = 18, /* bound weights were updated in place    */
   KVC_ERR_CACHE_ROPE_MISMATCH = 19,           /* feature width, max positions or base   */
   KVC_ERR_FULL = 20,                          /* a sequence has no room for the rows    */
+  KVC_ERR_OUT_OF_BLOCKS = 21,                 /* paged cache: the pool has fewer free blocks
+                                                 than the call needs (expected = needed,
+                                                 actual = free)                          */
   /* Found on the device before the commit; the commit is then suppressed.
    * Precedence when several hold: key, value, query, position, output. */
   KVC_ERR_NONFINITE_KEY = 30,    /* candidate rotated key has a NaN/Inf (first flat index) */
@@ -142,6 +145,7 @@ typedef struct {
   int32_t batch, heads, head_width, model_width, capacity, max_chunk_rows;
   int32_t kv_dtype, pos_mode, rope_max_positions, device;
   double rope_base;
+  int32_t block_rows, pool_blocks; /* paged caches; 0 for contiguous storage */
 } kvc_cache_desc;
 
 typedef struct kvc_params kvc_params; /* W_q, W_k, W_v (, W_o) with an identity and revisions */
@@ -193,6 +197,44 @@ void kvc_layer_destroy(kvc_layer* layer);
 kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capacity,
                             int32_t max_chunk_rows, void* hip_stream, kvc_cache** out);
 void kvc_cache_destroy(kvc_cache* cache);
+
+/* Block-paged cache (Chapter 37, "From causal attention to managed LLM
+ * inference state": serving systems keep growing KV caches as logical blocks
+ * mapped onto non-contiguous physical memory; the prefix-reuse note names
+ * block storage as the next step after its copy-per-branch ownership, "Lookup
+ * flow and cache ownership").  Same calls and results as kvc_cache_create,
+ * with K and V held in one pool per tensor of `pool_blocks` blocks, each
+ * [H, block_rows, d_h]: logical row r of sequence b is row r % block_rows of
+ * the block that b's table names at r / block_rows.  block_rows is a power of
+ * two >= 256 that divides `capacity`; the pool may hold fewer blocks than
+ * B * capacity / block_rows (sequences share the pool).  Appends take free
+ * blocks as rows cross a block boundary and fail with OUT_OF_BLOCKS (state
+ * unchanged) when the pool runs out; kvc_truncate and kvc_reset return blocks
+ * wholly past the cut; kvc_fork shares blocks, and an append into a block that
+ * another sequence still names first copies it (copy-on-write).  Attention
+ * results are bit-identical to a contiguous cache fed the same calls.
+ * kvc_storage_pointers / kvc_copy_storage cover the pools
+ * ([pool_blocks, H, block_rows, d_h] each).
+ * Errors: those of kvc_cache_create, then BAD_ARGUMENT (block_rows or
+ * pool_blocks invalid). */
+kvc_status kvc_cache_create_paged(const kvc_layer* layer, int32_t batch, int32_t capacity,
+                                  int32_t max_chunk_rows, int32_t block_rows, int32_t pool_blocks,
+                                  void* hip_stream, kvc_cache** out);
+
+/* Branches a sequence (prefix-reuse note, "Lookup flow and cache ownership":
+ * a lookup that continues another branch's prefix must not modify that
+ * branch): sequence dst becomes the first `rows` rows of sequence src (keys,
+ * values and row positions) with next_position[dst] = rows, as if it were a
+ * copy of src truncated at `rows`; src is unchanged.  A paged cache shares
+ * src's blocks (no K/V data moves; a later append into a shared block copies
+ * it first); a contiguous cache copies the rows.  Stream-ordered, no
+ * allocation.  Errors: NULL_ARGUMENT, BAD_ARGUMENT (src or dst out of range,
+ * or equal), BAD_CUT (rows outside [0, len[src]]), DEVICE. */
+kvc_status kvc_fork(kvc_cache* cache, int32_t src, int32_t dst, int32_t rows);
+
+/* Blocks of a paged cache's pool named by some sequence, and free ones (HOST,
+ * each nullable).  Errors: NULL_ARGUMENT, BAD_ARGUMENT (not paged), DEFERRED. */
+kvc_status kvc_pool_usage(kvc_cache* cache, int32_t* blocks_in_use, int32_t* blocks_free);
 
 /* The cached decode step (Chapter 37, "Bind the state, calculate completely,
  * then commit", and the incremental-attention listing).  x: DEVICE, shape

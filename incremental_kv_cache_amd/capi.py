@@ -25,6 +25,7 @@ KVC_ERR_CACHE_LAYER_MISMATCH = 17
 KVC_ERR_CACHE_LAYER_REVISION_MISMATCH = 18
 KVC_ERR_CACHE_ROPE_MISMATCH = 19
 KVC_ERR_FULL = 20
+KVC_ERR_OUT_OF_BLOCKS = 21
 KVC_ERR_NONFINITE_KEY = 30
 KVC_ERR_NONFINITE_VALUE = 31
 KVC_ERR_NONFINITE_QUERY = 32
@@ -82,7 +83,7 @@ class CacheDesc(C.Structure):
         ("batch", C.c_int32), ("heads", C.c_int32), ("head_width", C.c_int32), ("model_width", C.c_int32),
         ("capacity", C.c_int32), ("max_chunk_rows", C.c_int32), ("kv_dtype", C.c_int32),
         ("pos_mode", C.c_int32), ("rope_max_positions", C.c_int32), ("device", C.c_int32),
-        ("rope_base", C.c_double),
+        ("rope_base", C.c_double), ("block_rows", C.c_int32), ("pool_blocks", C.c_int32),
     ]
 
 
@@ -100,7 +101,10 @@ PROTOTYPES = {
     "kvc_layer_create": (I32, [P, I32, I32, C.c_double, I32, PP]),
     "kvc_layer_destroy": (None, [P]),
     "kvc_cache_create": (I32, [P, I32, I32, I32, P, PP]),
+    "kvc_cache_create_paged": (I32, [P, I32, I32, I32, I32, I32, P, PP]),
     "kvc_cache_destroy": (None, [P]),
+    "kvc_fork": (I32, [P, I32, I32, I32]),
+    "kvc_pool_usage": (I32, [P, PI32, PI32]),
     "kvc_append_and_attend": (I32, [P, P, P, I32, PI64, P, I32, C.POINTER(Work)]),
     "kvc_continue_chunk": (I32, [P, P, P, I32, PI32, P, I32, C.POINTER(Work)]),
     "kvc_truncate": (I32, [P, PI32, I32]),

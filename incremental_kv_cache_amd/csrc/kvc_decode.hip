@@ -70,13 +70,14 @@ __device__ __forceinline__ uint4 load_stream(const bf16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int DH, int U>
+template <int DH, int U, bool PAGED>
 __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevState s, SeqOrder order,
                                                                         float* __restrict__ out) {
   constexpr int G = DH / 8;
   constexpr int RPW = 64 / G;
   constexpr int GROUPS = kWaves * RPW;
   constexpr int STEP = GROUPS * U;
+  static_assert(kMinBlockRows % STEP == 0 && kDecodeTileRows % STEP == 0, "a step must stay inside one block");
   __shared__ float sm_m[GROUPS], sm_l[GROUPS];
   __shared__ float sm_acc[GROUPS][DH + 4];
 
@@ -96,8 +97,8 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
   const int g = lane % G;
   const int grp = wave * RPW + lane / G;
   const size_t lane_id = size_t(b) * s.heads + h;
-  const bf16_t* kc = static_cast<const bf16_t*>(s.keys) + lane_id * C * DH + g * 8;
-  const bf16_t* vc = static_cast<const bf16_t*>(s.values) + lane_id * C * DH + g * 8;
+  const bf16_t* kpool = static_cast<const bf16_t*>(s.keys) + g * 8;
+  const bf16_t* vpool = static_cast<const bf16_t*>(s.values) + g * 8;
   const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + lane_id * DH + g * 8;
   const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + lane_id * DH + g * 8;
 
@@ -121,6 +122,12 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 
   for (int base = r0; base < r1; base += STEP) {
+    // the STEP rows from base lie in one block of a paged cache (block rows are
+    // a power-of-two multiple of STEP, tiles start on multiples of 512)
+    const ptrdiff_t lane_base =
+        PAGED ? kv_block_base(s, b, h, min(base, max(len - 1, 0))) : ptrdiff_t(lane_id * C) * DH;
+    const bf16_t* kc = kpool + lane_base;
+    const bf16_t* vc = vpool + lane_base;
     uint4 kr[U], vr[U];
     bool ok[U];
 #pragma unroll
@@ -256,12 +263,18 @@ inline hipStream_t st(void* p) { return static_cast<hipStream_t>(p); }
 int fast_attend_decode(const DevState& s, const SeqOrder& order, void* out) {
   if (s.dtype != KVC_BF16) return -1;
   dim3 grid((s.capacity + s.tile_rows - 1) / s.tile_rows, s.heads, s.batch);
+  float* o = static_cast<float*>(out);
+  const dim3 block(64 * kWaves);
   if (s.head_width == 128) {
-    hipLaunchKernelGGL((attend_decode_bf16_kernel<128, 8>), grid, dim3(64 * kWaves), 0, st(s.stream), s, order,
-                       static_cast<float*>(out));
+    if (s.paged)
+      hipLaunchKernelGGL((attend_decode_bf16_kernel<128, 8, true>), grid, block, 0, st(s.stream), s, order, o);
+    else
+      hipLaunchKernelGGL((attend_decode_bf16_kernel<128, 8, false>), grid, block, 0, st(s.stream), s, order, o);
   } else if (s.head_width == 64) {
-    hipLaunchKernelGGL((attend_decode_bf16_kernel<64, 4>), grid, dim3(64 * kWaves), 0, st(s.stream), s, order,
-                       static_cast<float*>(out));
+    if (s.paged)
+      hipLaunchKernelGGL((attend_decode_bf16_kernel<64, 4, true>), grid, block, 0, st(s.stream), s, order, o);
+    else
+      hipLaunchKernelGGL((attend_decode_bf16_kernel<64, 4, false>), grid, block, 0, st(s.stream), s, order, o);
   } else {
     return -1;
   }

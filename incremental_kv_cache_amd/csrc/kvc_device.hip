@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void project_kernel(DevState s, const XT* __re
 // LDS at the end.  Returns the tile's max and sum in M/L and the weighted
 // values in acc_out[0..DH) (LDS), visible to the whole block after return.
 template <typename T, int DH, int NW>
-__device__ __forceinline__ void attend_rows(const typename Acc<T>::type* __restrict__ q,
+__device__ __forceinline__ void attend_rows(const DevState& s, int b, int h, const typename Acc<T>::type* __restrict__ q,
                                             const T* __restrict__ kc, const T* __restrict__ vc,
                                             const T* __restrict__ kn, const T* __restrict__ vn, int len,
                                             int r0, int r1, typename Acc<T>::type scale,
@@ -151,8 +151,9 @@ __device__ __forceinline__ void attend_rows(const typename Acc<T>::type* __restr
   for (int e = 0; e < VEC; ++e) acc[e] = 0;
 
   for (int r = r0 + grp; r < r1; r += GROUPS) {
-    const T* kr = (r < len) ? kc + size_t(r) * DH : kn + size_t(r - len) * DH;
-    const T* vr = (r < len) ? vc + size_t(r) * DH : vn + size_t(r - len) * DH;
+    const size_t off = r < len ? kv_offset(s, b, h, r) : 0;
+    const T* kr = (r < len) ? kc + off : kn + size_t(r - len) * DH;
+    const T* vr = (r < len) ? vc + off : vn + size_t(r - len) * DH;
     A kv[VEC], vv[VEC];
     load_row_chunk<T, VEC>(kr + g * VEC, kv);
     load_row_chunk<T, VEC>(vr + g * VEC, vv);
@@ -211,13 +212,13 @@ __global__ __launch_bounds__(64 * kAttendWaves) void attend_decode_kernel(DevSta
   if (r0 >= t) return;
   const int r1 = min(t, r0 + s.tile_rows);
   const size_t lane_id = size_t(b) * s.heads + h;
-  const T* kc = static_cast<const T*>(s.keys) + lane_id * C * DH;
-  const T* vc = static_cast<const T*>(s.values) + lane_id * C * DH;
+  const T* kc = static_cast<const T*>(s.keys);
+  const T* vc = static_cast<const T*>(s.values);
   const T* kn = static_cast<const T*>(s.cand_k) + lane_id * DH;
   const T* vn = static_cast<const T*>(s.cand_v) + lane_id * DH;
   const A* q = static_cast<const A*>(s.q) + lane_id * DH;
   A M, L;
-  attend_rows<T, DH, kAttendWaves>(q, kc, vc, kn, vn, len, r0, r1, A(s.scale), sm_m, sm_l, sm_acc, M, L,
+  attend_rows<T, DH, kAttendWaves>(s, b, h, q, kc, vc, kn, vn, len, r0, r1, A(s.scale), sm_m, sm_l, sm_acc, M, L,
                                    out_acc);
   A* part = static_cast<A*>(s.partials) + (lane_id * s.max_tiles + tile) * (DH + 2);
   if (threadIdx.x == 0) {
@@ -265,14 +266,14 @@ __global__ __launch_bounds__(64 * kAttendWaves) void attend_chunk_kernel(DevStat
   const int C = s.capacity;
   const int len = min(max(s.len[b], 0), C);
   const size_t lane_id = size_t(b) * s.heads + h;
-  const T* kc = static_cast<const T*>(s.keys) + lane_id * C * DH;
-  const T* vc = static_cast<const T*>(s.values) + lane_id * C * DH;
+  const T* kc = static_cast<const T*>(s.keys);
+  const T* vc = static_cast<const T*>(s.values);
   const T* kn = static_cast<const T*>(s.cand_k) + lane_id * n_max * DH;
   const T* vn = static_cast<const T*>(s.cand_v) + lane_id * n_max * DH;
   const A* q = static_cast<const A*>(s.q) + (lane_id * n_max + i) * DH;
   A M, L;
-  attend_rows<T, DH, kAttendWaves>(q, kc, vc, kn, vn, len, 0, len + i + 1, A(s.scale), sm_m, sm_l, sm_acc, M, L,
-                                   out_acc);
+  attend_rows<T, DH, kAttendWaves>(s, b, h, q, kc, vc, kn, vn, len, 0, len + i + 1, A(s.scale), sm_m, sm_l, sm_acc,
+                                   M, L, out_acc);
   for (int j = threadIdx.x; j < DH; j += blockDim.x) {
     const A o = out_acc[j] / L;
     const size_t flat = (size_t(b) * n_max + i) * s.model_width + size_t(h) * DH + j;
@@ -298,22 +299,27 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max,
   const int nr = min(kCommitRows, n_b - r0);
   const int dh = s.head_width;
   const size_t lane_id = size_t(b) * s.heads + h;
-  const size_t bytes = size_t(nr) * dh * sizeof(T);
-  const char* sk = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_k) + (lane_id * n_max + r0) * dh);
-  const char* sv = reinterpret_cast<const char*>(static_cast<const T*>(s.cand_v) + (lane_id * n_max + r0) * dh);
-  char* dk = reinterpret_cast<char*>(static_cast<T*>(s.keys) + (lane_id * C + len + r0) * dh);
-  char* dv = reinterpret_cast<char*>(static_cast<T*>(s.values) + (lane_id * C + len + r0) * dh);
-  if ((bytes & 15) == 0 && ((reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(sk)) & 15) == 0) {
-    const size_t n16 = bytes / 16;
-    for (size_t k = threadIdx.x; k < n16; k += blockDim.x) {
-      reinterpret_cast<uint4*>(dk)[k] = reinterpret_cast<const uint4*>(sk)[k];
-      reinterpret_cast<uint4*>(dv)[k] = reinterpret_cast<const uint4*>(sv)[k];
+  const T* sk = static_cast<const T*>(s.cand_k) + (lane_id * n_max + r0) * dh;
+  const T* sv = static_cast<const T*>(s.cand_v) + (lane_id * n_max + r0) * dh;
+  T* keys = static_cast<T*>(s.keys);
+  T* values = static_cast<T*>(s.values);
+  // row by row: in a paged cache consecutive rows may sit in different blocks
+  if ((dh * sizeof(T)) % 16 == 0) {
+    const int per_row = int(dh * sizeof(T) / 16);
+    for (int idx = threadIdx.x; idx < nr * per_row; idx += blockDim.x) {
+      const int k = idx / per_row;
+      const int c = idx - k * per_row;
+      const size_t off = kv_offset(s, b, h, len + r0 + k);
+      reinterpret_cast<uint4*>(keys + off)[c] = reinterpret_cast<const uint4*>(sk + size_t(k) * dh)[c];
+      reinterpret_cast<uint4*>(values + off)[c] = reinterpret_cast<const uint4*>(sv + size_t(k) * dh)[c];
     }
   } else {
-    const size_t n = bytes / sizeof(T);
-    for (size_t k = threadIdx.x; k < n; k += blockDim.x) {
-      reinterpret_cast<T*>(dk)[k] = reinterpret_cast<const T*>(sk)[k];
-      reinterpret_cast<T*>(dv)[k] = reinterpret_cast<const T*>(sv)[k];
+    for (int idx = threadIdx.x; idx < nr * dh; idx += blockDim.x) {
+      const int k = idx / dh;
+      const int c = idx - k * dh;
+      const size_t off = kv_offset(s, b, h, len + r0 + k);
+      keys[off + c] = sk[size_t(k) * dh + c];
+      values[off + c] = sv[size_t(k) * dh + c];
     }
   }
   if (h == 0) {
@@ -341,9 +347,10 @@ __global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
       const int h = idx / per_row;
       const int c = idx - h * per_row;
       const size_t lane_id = seq_rows + h;
-      reinterpret_cast<uint4*>(static_cast<T*>(s.keys) + (lane_id * C + len) * dh)[c] =
+      const size_t off = kv_offset(s, b, h, len);
+      reinterpret_cast<uint4*>(static_cast<T*>(s.keys) + off)[c] =
           reinterpret_cast<const uint4*>(static_cast<const T*>(s.cand_k) + lane_id * dh)[c];
-      reinterpret_cast<uint4*>(static_cast<T*>(s.values) + (lane_id * C + len) * dh)[c] =
+      reinterpret_cast<uint4*>(static_cast<T*>(s.values) + off)[c] =
           reinterpret_cast<const uint4*>(static_cast<const T*>(s.cand_v) + lane_id * dh)[c];
     }
   } else {
@@ -351,8 +358,9 @@ __global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
       const int h = idx / dh;
       const int c = idx - h * dh;
       const size_t lane_id = seq_rows + h;
-      static_cast<T*>(s.keys)[(lane_id * C + len) * dh + c] = static_cast<const T*>(s.cand_k)[lane_id * dh + c];
-      static_cast<T*>(s.values)[(lane_id * C + len) * dh + c] = static_cast<const T*>(s.cand_v)[lane_id * dh + c];
+      const size_t off = kv_offset(s, b, h, len);
+      static_cast<T*>(s.keys)[off + c] = static_cast<const T*>(s.cand_k)[lane_id * dh + c];
+      static_cast<T*>(s.values)[off + c] = static_cast<const T*>(s.cand_v)[lane_id * dh + c];
     }
   }
   __syncthreads();
@@ -399,6 +407,72 @@ __global__ __launch_bounds__(256) void set_lengths_kernel(DevState s, SetArgs a)
 
 __global__ __launch_bounds__(256) void set_rows_kernel(DevState s, SetArgs a) {
   for (int k = threadIdx.x; k < a.count; k += blockDim.x) s.rows[a.first + k] = a.vals[k];
+}
+
+struct TableArgs {
+  int32_t idx[kSetChunk / 2];
+  int32_t val[kSetChunk / 2];
+  int count;
+};
+
+__global__ __launch_bounds__(256) void set_table_kernel(DevState s, TableArgs a) {
+  if (gate_closed(s)) return;  // block moves are state changes like the length updates
+  int32_t* table = const_cast<int32_t*>(s.block_table);
+  for (int k = threadIdx.x; k < a.count; k += blockDim.x) table[a.idx[k]] = a.val[k];
+}
+
+// Rows [0, rows) of every head of block src into block dst, 16 bytes a thread.
+__global__ __launch_bounds__(256) void clear_table_kernel(DevState s) {
+  if (gate_closed(s)) return;
+  int32_t* table = const_cast<int32_t*>(s.block_table);
+  const size_t n = size_t(s.batch) * s.table_width;
+  for (size_t k = size_t(blockIdx.x) * blockDim.x + threadIdx.x; k < n; k += size_t(gridDim.x) * blockDim.x)
+    table[k] = -1;
+}
+
+// Grid-strided copy of `bytes` (a multiple of 4: rows are at least 4 bytes) in
+// 16-byte units when both ends allow it, else in 4-byte units.
+__device__ __forceinline__ void copy_span(char* to, const char* from, size_t bytes) {
+  const size_t t = size_t(blockIdx.x) * blockDim.x + threadIdx.x, stride = size_t(gridDim.x) * blockDim.x;
+  if (((reinterpret_cast<uintptr_t>(to) | reinterpret_cast<uintptr_t>(from) | bytes) & 15) == 0) {
+    for (size_t k = t; k < bytes / 16; k += stride)
+      reinterpret_cast<uint4*>(to)[k] = reinterpret_cast<const uint4*>(from)[k];
+  } else {
+    for (size_t k = t; k < bytes / 4; k += stride)
+      reinterpret_cast<uint32_t*>(to)[k] = reinterpret_cast<const uint32_t*>(from)[k];
+  }
+}
+
+// Paged caches: rows [0, rows) of head blockIdx.y, block src to block dst.
+__global__ __launch_bounds__(256) void copy_block_rows_kernel(DevState s, int dst, int src, int rows, int es) {
+  if (gate_closed(s)) return;
+  const size_t row_bytes = size_t(s.head_width) * es;
+  const size_t head_bytes = row_bytes << s.block_rows_log2;
+  const int h = blockIdx.y;
+  for (int part = 0; part < 2; ++part) {
+    char* base = static_cast<char*>(part ? s.values : s.keys);
+    copy_span(base + (size_t(dst) * s.heads + h) * head_bytes, base + (size_t(src) * s.heads + h) * head_bytes,
+              size_t(rows) * row_bytes);
+  }
+}
+
+__global__ __launch_bounds__(256) void copy_positions_kernel(DevState s, int dst_seq, int src_seq, int rows) {
+  if (gate_closed(s)) return;
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < rows; k += gridDim.x * blockDim.x)
+    s.positions[size_t(dst_seq) * s.capacity + k] = s.positions[size_t(src_seq) * s.capacity + k];
+}
+
+// Contiguous caches: rows [0, rows) of head blockIdx.y, sequence src to dst.
+__global__ __launch_bounds__(256) void copy_seq_rows_kernel(DevState s, int dst_seq, int src_seq, int rows, int es) {
+  if (gate_closed(s)) return;
+  const size_t row_bytes = size_t(s.head_width) * es;
+  const size_t lane_bytes = size_t(s.capacity) * row_bytes;
+  const int h = blockIdx.y;
+  for (int part = 0; part < 2; ++part) {
+    char* base = static_cast<char*>(part ? s.values : s.keys);
+    copy_span(base + (size_t(dst_seq) * s.heads + h) * lane_bytes, base + (size_t(src_seq) * s.heads + h) * lane_bytes,
+              size_t(rows) * row_bytes);
+  }
 }
 
 __global__ void clear_err_kernel(ErrWords* e) {
@@ -632,6 +706,61 @@ int dev_set_rows(const DevState& s, const int32_t* vals) {
     if (rc) return rc;
   }
   return 0;
+}
+
+static int elem_bytes(int dtype) { return dtype == KVC_F64 ? 8 : (dtype == KVC_F32 ? 4 : 2); }
+
+int dev_set_table(const DevState& s, const int32_t* idx, const int32_t* val, int count) {
+  for (int first = 0; first < count; first += kSetChunk / 2) {
+    TableArgs a{};
+    a.count = count - first < kSetChunk / 2 ? count - first : kSetChunk / 2;
+    for (int k = 0; k < a.count; ++k) {
+      a.idx[k] = idx[first + k];
+      a.val[k] = val[first + k];
+    }
+    hipLaunchKernelGGL(set_table_kernel, dim3(1), dim3(256), 0, st(s.stream), s, a);
+    int rc = last_launch();
+    if (rc) return rc;
+  }
+  return 0;
+}
+
+int dev_clear_table(const DevState& s) {
+  const size_t n = size_t(s.batch) * s.table_width;
+  const int blocks = int(n / 256 + 1 < 1024 ? n / 256 + 1 : 1024);
+  hipLaunchKernelGGL(clear_table_kernel, dim3(blocks), dim3(256), 0, st(s.stream), s);
+  return last_launch();
+}
+
+int dev_set_seq_length(const DevState& s, int seq, int32_t value) {
+  SetArgs a{};
+  a.first = seq;
+  a.count = 1;
+  a.mode = 0;
+  a.vals[0] = value;
+  hipLaunchKernelGGL(set_lengths_kernel, dim3(1), dim3(256), 0, st(s.stream), s, a);
+  return last_launch();
+}
+
+int dev_copy_block_rows(const DevState& s, int dst, int src, int rows) {
+  if (rows <= 0) return 0;
+  hipLaunchKernelGGL(copy_block_rows_kernel, dim3(8, s.heads), dim3(256), 0, st(s.stream), s, dst, src, rows,
+                     elem_bytes(s.dtype));
+  return last_launch();
+}
+
+int dev_copy_positions(const DevState& s, int dst_seq, int src_seq, int rows) {
+  if (rows <= 0) return 0;
+  hipLaunchKernelGGL(copy_positions_kernel, dim3((rows + 255) / 256), dim3(256), 0, st(s.stream), s, dst_seq, src_seq,
+                     rows);
+  return last_launch();
+}
+
+int dev_copy_seq_rows(const DevState& s, int dst_seq, int src_seq, int rows) {
+  if (rows <= 0) return 0;
+  hipLaunchKernelGGL(copy_seq_rows_kernel, dim3(32, s.heads), dim3(256), 0, st(s.stream), s, dst_seq, src_seq, rows,
+                     elem_bytes(s.dtype));
+  return last_launch();
 }
 
 int mfma_project(const DevState& s, const void* x, int n_max, int per_seq_rows);

@@ -71,6 +71,12 @@ struct kvc_cache {
   ChunkOrder order{};     // work order of the last chunk call
   SeqOrder seq_order{};   // sequence order of the last decode call
   bool session = false;   // a layer cache of a kvc_session: its failure words belong to the session
+  // block paging (paged caches only): host copy of the block table and the pool's bookkeeping
+  bool paged = false;
+  int32_t block_rows = 0, block_lg = 0, table_width = 0, pool_blocks = 0;
+  std::vector<int32_t> table;        // [B * table_width], -1 = no block
+  std::vector<int32_t> refcount;     // [pool_blocks]: table entries naming the block
+  std::vector<int32_t> free_blocks;  // unreferenced blocks (a stack)
 };
 
 struct kvc_session {
@@ -291,6 +297,114 @@ kvc_status resync_lengths(kvc_cache* c) {
   return KVC_OK;
 }
 
+// ---- block paging ---------------------------------------------------------
+
+// Sends table entries idx[k] = c->table[idx[k]] to the device (gated there like
+// the length updates).
+kvc_status upload_table(kvc_cache* c, const std::vector<int32_t>& idx) {
+  if (idx.empty()) return KVC_OK;
+  std::vector<int32_t> val(idx.size());
+  for (size_t k = 0; k < idx.size(); ++k) val[k] = c->table[idx[k]];
+  const int rc = dev_set_table(c->ds, idx.data(), val.data(), int(idx.size()));
+  if (rc) return device_fail(rc, "block table update");
+  return KVC_OK;
+}
+
+// Blocks holding rows [0, rows).
+int blocks_for(const kvc_cache* c, int rows) { return (rows + c->block_rows - 1) >> c->block_lg; }
+
+// Drops one reference to block `blk` (back to the free list at zero).
+void release_block(kvc_cache* c, int32_t blk) {
+  if (blk < 0) return;
+  if (--c->refcount[blk] == 0) c->free_blocks.push_back(blk);
+}
+
+// Releases the blocks of sequence b from logical block `keep` on (host mirror);
+// appends the changed table indices to `changed`.
+void release_tail(kvc_cache* c, int b, int keep, std::vector<int32_t>& changed) {
+  for (int j = keep; j < c->table_width; ++j) {
+    const int idx = b * c->table_width + j;
+    if (c->table[idx] < 0) continue;
+    release_block(c, c->table[idx]);
+    c->table[idx] = -1;
+    changed.push_back(idx);
+  }
+}
+
+// Rebuilds the host table, reference counts and free list from the device
+// table (after a deferred failure suppressed table updates).  Stream idle.
+kvc_status resync_paging(kvc_cache* c) {
+  if (!c->paged) return KVC_OK;
+  const int rc = dev_copy_d2h_sync(c->table.data(), c->ds.block_table, sizeof(int32_t) * c->table.size(),
+                                   c->ds.stream);
+  if (rc) return device_fail(rc, "reading the block table");
+  std::fill(c->refcount.begin(), c->refcount.end(), 0);
+  for (int32_t blk : c->table)
+    if (blk >= 0) c->refcount[blk]++;
+  c->free_blocks.clear();
+  for (int blk = c->pool_blocks - 1; blk >= 0; --blk)
+    if (c->refcount[blk] == 0) c->free_blocks.push_back(blk);
+  // a failed call may have left blocks past the committed rows: give them back
+  std::vector<int32_t> changed;
+  for (int b = 0; b < c->batch; ++b) release_tail(c, b, blocks_for(c, c->len[b]), changed);
+  return upload_table(c, changed);
+}
+
+// Blocks a call takes before it launches: fresh blocks for rows past the
+// sequence's last block, and private copies of shared blocks the call appends
+// into (copy-on-write).  Undone by revert_blocks when the call fails.
+struct BlockReservation {
+  std::vector<int32_t> idx, old_val;  // table entries changed, and their previous values
+};
+
+kvc_status reserve_blocks(kvc_cache* c, int n_max, const int32_t* n_rows, BlockReservation& r) {
+  struct Need {
+    int idx, old, copy_rows;
+  };
+  std::vector<Need> need;
+  for (int b = 0; b < c->batch; ++b) {
+    const int n = n_rows ? n_rows[b] : n_max;
+    if (n <= 0) continue;
+    const int len = c->len[b];
+    const int first = len >> c->block_lg, last = (len + n - 1) >> c->block_lg;
+    for (int j = first; j <= last; ++j) {
+      const int idx = b * c->table_width + j;
+      const int cur = c->table[idx];
+      if (cur >= 0 && c->refcount[cur] == 1) continue;  // private block already in place
+      const int copy_rows = cur >= 0 && j == first ? len - (j << c->block_lg) : 0;
+      need.push_back({idx, cur, copy_rows});
+    }
+  }
+  if (need.empty()) return KVC_OK;
+  if (need.size() > c->free_blocks.size())
+    return fail_ea(KVC_ERR_OUT_OF_BLOCKS, int64_t(need.size()), int64_t(c->free_blocks.size()),
+                   "the block pool has %zu free blocks, the call needs %zu", c->free_blocks.size(), need.size());
+  for (const Need& nd : need) {
+    const int32_t blk = c->free_blocks.back();
+    c->free_blocks.pop_back();
+    c->refcount[blk] = 1;
+    if (nd.old >= 0) c->refcount[nd.old]--;  // still referenced elsewhere: it was shared
+    c->table[nd.idx] = blk;
+    r.idx.push_back(nd.idx);
+    r.old_val.push_back(nd.old);
+    if (nd.old >= 0) {
+      const int rc = dev_copy_block_rows(c->ds, blk, nd.old, nd.copy_rows);
+      if (rc) return device_fail(rc, "copy-on-write of a shared block");
+    }
+  }
+  return upload_table(c, r.idx);
+}
+
+void revert_blocks(kvc_cache* c, const BlockReservation& r) {
+  for (size_t k = r.idx.size(); k-- > 0;) {
+    const int idx = r.idx[k];
+    release_block(c, c->table[idx]);
+    if (r.old_val[k] >= 0) c->refcount[r.old_val[k]]++;
+    c->table[idx] = r.old_val[k];
+  }
+  (void)upload_table(c, r.idx);
+}
+
 // Reports an error left by earlier KVC_ASYNC calls (synchronises).
 kvc_status check_deferred(kvc_cache* c) {
   if (!c->pending_async) return KVC_OK;
@@ -301,8 +415,11 @@ kvc_status check_deferred(kvc_cache* c) {
   if (st == KVC_ERR_DEVICE) return st;
   if (st != KVC_OK) {
     const kvc_status orig = st;
+    const kvc_error_detail saved = g_last;
     kvc_status rs = resync_lengths(c);
+    if (rs == KVC_OK) rs = resync_paging(c);
     if (rs != KVC_OK) return rs;
+    g_last = saved;
     g_last.actual = orig;
     return fail(KVC_ERR_DEFERRED, "an earlier asynchronous call failed: %s (%s)", kvc_status_name(orig),
                 std::string(g_last.message).c_str());
@@ -336,6 +453,7 @@ void free_cache(kvc_cache* c) {
   dev_free(c->ds.rope_cos);
   dev_free(c->ds.rope_sin);
   if (!c->session) dev_free(c->ds.err);
+  dev_free(const_cast<int32_t*>(c->ds.block_table));
   dev_free(c->ds.merged);
   dev_host_free(c->err_host);
   for (void* e : c->prof.events) dev_event_destroy(e);
@@ -403,21 +521,38 @@ void advance_mirror(kvc_cache* c, int n_max, const int32_t* n_rows) {
 }
 
 // Runs the stages of one call and the sync-mode error collection.
+// Paged caches first take the blocks the appended rows land in (and private
+// copies of shared blocks they append into); a call that fails gives them back.
 kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_rows, void* out, int32_t flags,
                     bool decode) {
-  kvc_status st = compute_stages(c, x, n_max, n_rows, out, decode);
-  if (st != KVC_OK) return st;
-  st = commit_stage(c, n_max, n_rows);
-  if (st != KVC_OK) return st;
-  if (flags & KVC_ASYNC) {
+  BlockReservation r;
+  kvc_status st = KVC_OK;
+  if (c->paged) {
+    st = reserve_blocks(c, n_max, n_rows, r);
+    if (st != KVC_OK) {
+      const kvc_error_detail saved = g_last;
+      revert_blocks(c, r);
+      g_last = saved;
+      return st;
+    }
+  }
+  st = compute_stages(c, x, n_max, n_rows, out, decode);
+  if (st == KVC_OK) st = commit_stage(c, n_max, n_rows);
+  if (st == KVC_OK && (flags & KVC_ASYNC)) {
     c->pending_async = true;
     advance_mirror(c, n_max, n_rows);
     return KVC_OK;
   }
-  const int rc = dev_sync(c->ds.stream);
-  if (rc) return device_fail(rc, "stream synchronisation");
-  st = collect_device_error(c, n_max);
-  if (st != KVC_OK) return st;
+  if (st == KVC_OK) {
+    const int rc = dev_sync(c->ds.stream);
+    st = rc ? device_fail(rc, "stream synchronisation") : collect_device_error(c, n_max);
+  }
+  if (st != KVC_OK) {
+    const kvc_error_detail saved = g_last;
+    revert_blocks(c, r);
+    g_last = saved;
+    return st;
+  }
   advance_mirror(c, n_max, n_rows);
   return KVC_OK;
 }
@@ -450,7 +585,7 @@ kvc_status reject_session_cache(const char* what) {
 // inside a session's block, and gate / gate_count the whole block.
 kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity, int32_t max_chunk_rows,
                         void* hip_stream, ErrWords* shared_err, const ErrWords* gate, int gate_count,
-                        kvc_cache** out) {
+                        kvc_cache** out, int32_t block_rows = 0, int32_t pool_blocks = 0) {
   *out = nullptr;
   // Chapter 37, layer-kv-cache listing: batch, capacity, position capacity,
   // element-count overflow, then allocation.
@@ -461,10 +596,23 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
                    "KV cache capacity %d exceeds RoPE position capacity %d", capacity, layer->rope_max_positions);
   if (max_chunk_rows <= 0)
     return fail(KVC_ERR_BAD_ARGUMENT, "max_chunk_rows must be at least 1, got %d", max_chunk_rows);
+  const bool paged = block_rows != 0;
+  if (paged) {
+    // Paged storage: a decode split-K step (at most 256 rows) and a 64-row
+    // chunk-attention tile must each fall inside one block.
+    if (!is_pow2(block_rows) || block_rows < kMinBlockRows || capacity % block_rows != 0)
+      return fail_ea(KVC_ERR_BAD_ARGUMENT, kMinBlockRows, block_rows,
+                     "block_rows %d must be a power of two >= %d that divides the capacity %d", block_rows,
+                     kMinBlockRows, capacity);
+    if (pool_blocks <= 0)
+      return fail_ea(KVC_ERR_BAD_ARGUMENT, 1, pool_blocks, "the block pool needs at least one block, got %d",
+                     pool_blocks);
+  }
   const kvc_params* p = layer->params;
   const int H = layer->heads, dh = layer->head_width;
   int64_t elements = 0, cand = 0, pos_elems = 0;
-  if (!checked_mul(batch, H, &elements) || !checked_mul(elements, capacity, &elements) ||
+  if (!checked_mul(paged ? pool_blocks : batch, H, &elements) ||
+      !checked_mul(elements, paged ? block_rows : capacity, &elements) ||
       !checked_mul(elements, dh, &elements) || !checked_mul(int64_t(batch) * H, int64_t(max_chunk_rows), &cand) ||
       !checked_mul(cand, dh, &cand) || !checked_mul(batch, capacity, &pos_elems) ||
       elements > (INT64_MAX / 16) || cand > (INT64_MAX / 16)) {
@@ -491,6 +639,16 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
   c->len.assign(batch, 0);
   c->next_pos.assign(batch, 0);
   c->session = shared_err != nullptr;
+  if (paged) {
+    c->paged = true;
+    c->block_rows = block_rows;
+    while ((1 << c->block_lg) < block_rows) ++c->block_lg;
+    c->table_width = capacity / block_rows;
+    c->pool_blocks = pool_blocks;
+    c->table.assign(size_t(batch) * c->table_width, -1);
+    c->refcount.assign(pool_blocks, 0);
+    for (int blk = pool_blocks - 1; blk >= 0; --blk) c->free_blocks.push_back(blk);
+  }
   int rc = dev_current_device(&c->device);
   if (rc) {
     free_cache(c);
@@ -518,6 +676,9 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
   s.max_tiles = max_tiles;
   s.tile_rows = kDecodeTileRows;
   s.stream = hip_stream;
+  s.paged = paged;
+  s.block_rows_log2 = c->block_lg;
+  s.table_width = c->table_width;
   c->storage_bytes = int64_t(round16(size_t(elements) * es));
   struct Alloc {
     void** p;
@@ -535,6 +696,8 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
       {&s.partials, round16(size_t(batch) * H * max_tiles * (dh + 2) * as)},
       {reinterpret_cast<void**>(&s.err), shared_err ? 0 : round16(sizeof(ErrWords))},
       {&s.merged, p->w[3] ? round16(size_t(cand) * as) : 0},  // [B, max_chunk_rows, D]
+      {reinterpret_cast<void**>(const_cast<int32_t**>(&s.block_table)),
+       paged ? round16(sizeof(int32_t) * c->table.size()) : 0},
   };
   for (auto& a : allocs) {
     if (a.bytes == 0) continue;
@@ -560,9 +723,18 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
     free_cache(c);
     return fail(KVC_ERR_ALLOCATION_FAILED, "cannot allocate pinned host memory");
   }
-  // Zero-filled storage (Chapter 37: zeroed backing buffers), zero lengths.
+  // Zero-filled storage (Chapter 37: zeroed backing buffers), zero lengths;
+  // an empty block table.
   for (auto& a : allocs) {
     if (*a.p == s.err || a.bytes == 0) continue;
+    if (*a.p == s.block_table) {
+      rc = dev_copy_h2d_sync(*a.p, c->table.data(), sizeof(int32_t) * c->table.size(), s.stream);
+      if (rc) {
+        free_cache(c);
+        return device_fail(rc, "block table init");
+      }
+      continue;
+    }
     rc = dev_zero(*a.p, a.bytes, s.stream);
     if (rc) {
       free_cache(c);
@@ -791,6 +963,7 @@ const char* kvc_status_name(kvc_status s) {
     N(KVC_ERR_CACHE_LAYER_REVISION_MISMATCH)
     N(KVC_ERR_CACHE_ROPE_MISMATCH)
     N(KVC_ERR_FULL)
+    N(KVC_ERR_OUT_OF_BLOCKS)
     N(KVC_ERR_NONFINITE_KEY)
     N(KVC_ERR_NONFINITE_VALUE)
     N(KVC_ERR_NONFINITE_QUERY)
@@ -883,6 +1056,15 @@ kvc_status kvc_cache_create(const kvc_layer* layer, int32_t batch, int32_t capac
   reset_detail();
   if (!layer || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_cache_create");
   return create_cache(layer, batch, capacity, max_chunk_rows, hip_stream, nullptr, nullptr, 0, out);
+}
+
+kvc_status kvc_cache_create_paged(const kvc_layer* layer, int32_t batch, int32_t capacity, int32_t max_chunk_rows,
+                                  int32_t block_rows, int32_t pool_blocks, void* hip_stream, kvc_cache** out) {
+  reset_detail();
+  if (!layer || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_cache_create_paged");
+  if (block_rows == 0) return fail(KVC_ERR_BAD_ARGUMENT, "block_rows must be nonzero");
+  return create_cache(layer, batch, capacity, max_chunk_rows, hip_stream, nullptr, nullptr, 0, out, block_rows,
+                      pool_blocks);
 }
 
 void kvc_cache_destroy(kvc_cache* cache) {
@@ -1040,6 +1222,13 @@ kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags) {
     cache->len[b] = cut[b];
     if (!stale) cache->next_pos[b] = cut[b];
   }
+  if (cache->paged) {
+    // blocks wholly past the cut go back to the pool (a block other
+    // sequences still name stays with them)
+    std::vector<int32_t> changed;
+    for (int b = 0; b < cache->batch; ++b) release_tail(cache, b, blocks_for(cache, cut[b]), changed);
+    return upload_table(cache, changed);
+  }
   return KVC_OK;
 }
 
@@ -1051,6 +1240,68 @@ kvc_status kvc_reset(kvc_cache* cache) {
   if (rc) return device_fail(rc, "length reset");
   std::fill(cache->len.begin(), cache->len.end(), 0);
   std::fill(cache->next_pos.begin(), cache->next_pos.end(), 0);
+  if (cache->paged) {
+    rc = dev_clear_table(cache->ds);
+    if (rc) return device_fail(rc, "block table reset");
+    std::fill(cache->table.begin(), cache->table.end(), -1);
+    std::fill(cache->refcount.begin(), cache->refcount.end(), 0);
+    cache->free_blocks.clear();
+    for (int blk = cache->pool_blocks - 1; blk >= 0; --blk) cache->free_blocks.push_back(blk);
+  }
+  return KVC_OK;
+}
+
+kvc_status kvc_fork(kvc_cache* cache, int32_t src, int32_t dst, int32_t rows) {
+  reset_detail();
+  if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
+  if (cache->session) return reject_session_cache("kvc_fork");
+  if (src < 0 || src >= cache->batch || dst < 0 || dst >= cache->batch || src == dst)
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, cache->batch, src == dst ? src : (src < 0 || src >= cache->batch ? src : dst),
+                   "fork needs two different sequences in [0, %d), got %d -> %d", cache->batch, src, dst);
+  if (rows < 0 || rows > cache->len[src]) {
+    g_last.sequence = src;
+    return fail_ea(KVC_ERR_BAD_CUT, cache->len[src], rows, "fork of %d rows outside [0, %d] of sequence %d", rows,
+                   cache->len[src], src);
+  }
+  DevState& s = cache->ds;
+  int rc = 0;
+  if (cache->paged) {
+    // dst names src's blocks (shared, copied on a later append into them)
+    const int nb = blocks_for(cache, rows);
+    for (int j = 0; j < nb; ++j)
+      if (cache->table[src * cache->table_width + j] < 0)
+        return fail(KVC_ERR_INTERNAL, "sequence %d has no block for row %d", src, j * cache->block_rows);
+    std::vector<int32_t> changed;
+    release_tail(cache, dst, 0, changed);
+    for (int j = 0; j < nb; ++j) {
+      const int32_t blk = cache->table[src * cache->table_width + j];
+      const int idx = dst * cache->table_width + j;
+      cache->table[idx] = blk;
+      cache->refcount[blk]++;
+      if (std::find(changed.begin(), changed.end(), idx) == changed.end()) changed.push_back(idx);
+    }
+    kvc_status st = upload_table(cache, changed);
+    if (st != KVC_OK) return st;
+  } else {
+    rc = dev_copy_seq_rows(s, dst, src, rows);
+    if (rc) return device_fail(rc, "row copy");
+  }
+  rc = dev_copy_positions(s, dst, src, rows);
+  if (rc == 0) rc = dev_set_seq_length(s, dst, rows);
+  if (rc) return device_fail(rc, "fork bookkeeping");
+  cache->len[dst] = rows;
+  cache->next_pos[dst] = rows;
+  return KVC_OK;
+}
+
+kvc_status kvc_pool_usage(kvc_cache* cache, int32_t* blocks_in_use, int32_t* blocks_free) {
+  reset_detail();
+  if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
+  if (!cache->paged) return fail(KVC_ERR_BAD_ARGUMENT, "the cache is not paged");
+  kvc_status st = check_deferred(cache);
+  if (st != KVC_OK) return st;
+  if (blocks_in_use) *blocks_in_use = cache->pool_blocks - int32_t(cache->free_blocks.size());
+  if (blocks_free) *blocks_free = int32_t(cache->free_blocks.size());
   return KVC_OK;
 }
 
@@ -1092,9 +1343,31 @@ kvc_status kvc_snapshot(kvc_cache* cache, int32_t seq, void* keys_out, void* val
                    (long long)rows_capacity, len);
   const size_t es = elem_size(cache->dtype);
   const size_t row_bytes = size_t(cache->head_width) * es;
+  int rc = 0;
+  if (cache->paged) {
+    // [H, len, d_h] gathered block by block: [H, block rows, d_h] per block
+    const size_t head_bytes = size_t(cache->block_rows) * row_bytes;
+    for (int j = 0; j < blocks_for(cache, len) && rc == 0; ++j) {
+      const int blk = cache->table[seq * cache->table_width + j];
+      const int r0 = j * cache->block_rows, nr = std::min(len - r0, cache->block_rows);
+      const size_t src_off = size_t(blk) * cache->heads * head_bytes;
+      if (keys_out)
+        rc = dev_copy_d2h_2d_sync(static_cast<char*>(keys_out) + r0 * row_bytes, size_t(len) * row_bytes,
+                                  static_cast<char*>(cache->ds.keys) + src_off, head_bytes, nr * row_bytes,
+                                  cache->heads, cache->ds.stream);
+      if (rc == 0 && values_out)
+        rc = dev_copy_d2h_2d_sync(static_cast<char*>(values_out) + r0 * row_bytes, size_t(len) * row_bytes,
+                                  static_cast<char*>(cache->ds.values) + src_off, head_bytes, nr * row_bytes,
+                                  cache->heads, cache->ds.stream);
+    }
+    if (rc == 0 && positions_out && len > 0)
+      rc = dev_copy_d2h_sync(positions_out, cache->ds.positions + size_t(seq) * cache->capacity,
+                             sizeof(int32_t) * size_t(len), cache->ds.stream);
+    if (rc) return device_fail(rc, "snapshot copy");
+    return KVC_OK;
+  }
   const size_t lane_bytes = size_t(cache->capacity) * row_bytes;
   const size_t seq_off = size_t(seq) * cache->heads * lane_bytes;
-  int rc = 0;
   // [H, len, d_h] out of [H, C, d_h]: one strided copy per buffer.
   if (keys_out)
     rc = dev_copy_d2h_2d_sync(keys_out, size_t(len) * row_bytes, static_cast<char*>(cache->ds.keys) + seq_off,
@@ -1137,6 +1410,8 @@ kvc_status kvc_cache_describe(const kvc_cache* cache, kvc_cache_desc* out) {
   out->rope_max_positions = cache->rope_max_positions;
   out->device = cache->device;
   out->rope_base = cache->rope_base;
+  out->block_rows = cache->block_rows;
+  out->pool_blocks = cache->pool_blocks;
   return KVC_OK;
 }
 

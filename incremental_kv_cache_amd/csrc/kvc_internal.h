@@ -27,6 +27,9 @@ constexpr unsigned long long kErrClear = ~0ull;
 // Smallest number of attention rows per split-K work item of the decode
 // kernel (sizes the partial buffer); each call picks tile_rows >= this.
 constexpr int kDecodeTileRows = 512;
+// Smallest rows per block of a paged cache: every run of rows a kernel reads
+// through one block base (a decode step, a 64-row chunk-attention tile) fits.
+constexpr int kMinBlockRows = 256;
 // Values per by-value length update (kernel-argument payload).
 constexpr int kSetChunk = 480;
 
@@ -58,6 +61,14 @@ struct DevState {
   int single_tile;     // 1 when every lane of the current decode call fits one tile
   void* rope_cos;  // [max_positions, d_h / 2] accumulate type (null without rotation)
   void* rope_sin;
+  // Block-paged storage (paged = 1): keys and values are pools
+  // [blocks, H, block_rows, d_h] and row r of sequence b lives in block
+  // block_table[b * table_width + (r >> block_rows_log2)] (capacity =
+  // table_width << block_rows_log2).  paged = 0: [B, H, C, d_h].
+  int paged;
+  int block_rows_log2;
+  int table_width;
+  const int32_t* block_table;
   ErrWords* err;
   // The failure words every state-changing kernel checks before it writes:
   // the cache's own (gate_count 1), or those of every layer of a session, so
@@ -89,6 +100,19 @@ int dev_clear_err(ErrWords* err, void* stream);
 int dev_set_lengths(const DevState& s, const int32_t* vals, int mode);
 // rows[b] = vals[b] for the next chunk call.
 int dev_set_rows(const DevState& s, const int32_t* vals);
+// Paged caches: table[idx[k]] = val[k] for k < count (kernel arguments).
+int dev_set_table(const DevState& s, const int32_t* idx, const int32_t* val, int count);
+// Paged caches: every table entry = -1 (no block).
+int dev_clear_table(const DevState& s);
+// len[seq] = next_pos[seq] = value (one sequence; the others unchanged).
+int dev_set_seq_length(const DevState& s, int seq, int32_t value);
+// Paged caches: rows [0, rows) of every head of block `src` into block `dst`
+// (copy-on-write of a shared block before an append into it).
+int dev_copy_block_rows(const DevState& s, int dst, int src, int rows);
+// positions[dst_seq, 0..rows) = positions[src_seq, 0..rows).
+int dev_copy_positions(const DevState& s, int dst_seq, int src_seq, int rows);
+// Contiguous caches: K/V rows [0, rows) of every head of src_seq into dst_seq.
+int dev_copy_seq_rows(const DevState& s, int dst_seq, int src_seq, int rows);
 
 // Pipeline stages.  n_max: rows per sequence of this call (1 for decode);
 // per_seq_rows: 0 = every sequence has n_max rows, 1 = rows[] holds them.

@@ -650,6 +650,7 @@ template <int DH>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_flash_kernel(
     DevState s, int n_max, int per_seq_rows, ChunkOrder order, float* __restrict__ out) {
   constexpr int KT = 64;
+  static_assert(kMinBlockRows % KT == 0, "a key tile must stay inside one block");
   constexpr int LDK = DH + 8;   // K row stride: conflict-free 16-byte fragment reads
   constexpr int LDV = DH + 16;  // V row stride: conflict-free transposing reads
   constexpr int DSTEPS = DH / 16;
@@ -688,8 +689,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int total = len + i_max + 1;
   const int ntiles = (total + KT - 1) / KT;
   const size_t lane_id = size_t(b) * H + h;
-  const bf16_t* kc = static_cast<const bf16_t*>(s.keys) + lane_id * C * DH;
-  const bf16_t* vc = static_cast<const bf16_t*>(s.values) + lane_id * C * DH;
+  const bf16_t* kc = static_cast<const bf16_t*>(s.keys);  // rows through kv_block_base / kv_offset
+  const bf16_t* vc = static_cast<const bf16_t*>(s.values);
   const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + lane_id * n_max * DH;
   const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + lane_id * n_max * DH;
 
@@ -730,8 +731,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto fetch = [&](int j0) {
     const bool cached = j0 + KT <= len;
     const size_t r0 = size_t(cached ? j0 : j0 - len) + lrow;
-    const uint4* kp = reinterpret_cast<const uint4*>((cached ? kc : kn) + r0 * DH + lch * 8);
-    const uint4* vp = reinterpret_cast<const uint4*>((cached ? vc : vn) + r0 * DH + lch * 8);
+    // a 64-row tile lies in one block of a paged cache
+    const ptrdiff_t tile_base = cached ? kv_block_base(s, b, h, j0) : 0;
+    const uint4* kp = reinterpret_cast<const uint4*>((cached ? kc + tile_base : kn) + r0 * DH + lch * 8);
+    const uint4* vp = reinterpret_cast<const uint4*>((cached ? vc + tile_base : vn) + r0 * DH + lch * 8);
     constexpr int STRIDE = RPI * DH / 8;  // uint4 between a thread's pieces
     pk0 = kp[0];
     pv0 = vp[0];
@@ -765,7 +768,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int k = 0; k < PIECES; ++k) {
       const int j = min(j0 + lrow + k * RPI, total - 1);
-      const size_t off = size_t(j < len ? j : j - len) * DH + lch * 8;
+      const size_t off = (j < len ? kv_offset(s, b, h, j) : size_t(j - len) * DH) + lch * 8;
       const uint4 kk = *reinterpret_cast<const uint4*>((j < len ? kc : kn) + off);
       const uint4 vv = *reinterpret_cast<const uint4*>((j < len ? vc : vn) + off);
       *reinterpret_cast<uint4*>(&Ks[buf][(lrow + k * RPI) * LDK + lch * 8]) = kk;

@@ -153,22 +153,52 @@ def kvc_layer_create(params: Params, heads: int, pos_mode: int = KVC_POS_ROPE, r
     return h
 
 
-def kvc_cache_create(layer: Layer, batch: int, capacity: int, max_chunk_rows: int = 1, stream=None) -> Cache:
-    """Allocates the cache on the current device; its work runs on ``stream``
-    (default: torch's current stream)."""
-    lib = layer._lib
+def _stream_arg(stream):
     if stream is None:
         try:
             stream = _torch().cuda.current_stream().cuda_stream
         except Exception:
             stream = 0
+    return C.c_void_p(stream or 0)
+
+
+def kvc_cache_create(layer: Layer, batch: int, capacity: int, max_chunk_rows: int = 1, stream=None) -> Cache:
+    """Allocates the cache on the current device; its work runs on ``stream``
+    (default: torch's current stream)."""
+    lib = layer._lib
     out = C.c_void_p()
-    _check(lib, lib.kvc_cache_create(layer.ptr, batch, capacity, max_chunk_rows, C.c_void_p(stream or 0),
+    _check(lib, lib.kvc_cache_create(layer.ptr, batch, capacity, max_chunk_rows, _stream_arg(stream),
                                      C.byref(out)))
     h = Cache(lib, out)
     h.layer = layer
     h.desc = kvc_cache_describe(h)
     return h
+
+
+def kvc_cache_create_paged(layer: Layer, batch: int, capacity: int, block_rows: int, pool_blocks: int,
+                           max_chunk_rows: int = 1, stream=None) -> Cache:
+    """A cache whose K/V rows live in a shared pool of ``pool_blocks`` blocks of
+    ``block_rows`` rows (same calls and results as kvc_cache_create)."""
+    lib = layer._lib
+    out = C.c_void_p()
+    _check(lib, lib.kvc_cache_create_paged(layer.ptr, batch, capacity, max_chunk_rows, block_rows, pool_blocks,
+                                           _stream_arg(stream), C.byref(out)))
+    h = Cache(lib, out)
+    h.layer = layer
+    h.desc = kvc_cache_describe(h)
+    return h
+
+
+def kvc_fork(cache: Cache, src: int, dst: int, rows: int) -> None:
+    """Sequence ``dst`` becomes the first ``rows`` rows of ``src`` (next position = rows)."""
+    _check(cache._lib, cache._lib.kvc_fork(cache.ptr, src, dst, rows))
+
+
+def kvc_pool_usage(cache: Cache):
+    """(blocks in use, free blocks) of a paged cache's pool."""
+    used, free = C.c_int32(), C.c_int32()
+    _check(cache._lib, cache._lib.kvc_pool_usage(cache.ptr, C.byref(used), C.byref(free)))
+    return used.value, free.value
 
 
 def kvc_cache_describe(cache: Cache) -> dict:

@@ -5,6 +5,7 @@
 // attention.  Built by tests/test_host_manager.py; never shipped.
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 
 #include "../incremental_kv_cache_amd/csrc/kvc_internal.h"
 
@@ -70,12 +71,109 @@ int dev_set_rows(const DevState& s, const int32_t* vals) {
   for (int b = 0; b < s.batch; ++b) s.rows[b] = vals[b];
   return 0;
 }
-int dev_project(const DevState&, const void*, int, int) { return 1; }
-int dev_attend_decode(const DevState&, const SeqOrder&, void*) { return 1; }
-int dev_merge_decode(const DevState&, void*) { return 1; }
-int dev_attend_chunk(const DevState&, int, int, const ChunkOrder&, void*) { return 1; }
-int dev_output_project(const DevState&, int, int, void*) { return 1; }
-int dev_commit(const DevState&, int, int) { return 1; }
+// Block moves on host memory, with the device kernels' gating.
+static int elem_bytes(int dtype) { return dtype == KVC_F64 ? 8 : (dtype == KVC_F32 ? 4 : 2); }
+int dev_set_table(const DevState& s, const int32_t* idx, const int32_t* val, int count) {
+  if (gate_closed(s)) return 0;
+  for (int k = 0; k < count; ++k) const_cast<int32_t*>(s.block_table)[idx[k]] = val[k];
+  return 0;
+}
+int dev_clear_table(const DevState& s) {
+  if (gate_closed(s)) return 0;
+  for (size_t k = 0; k < size_t(s.batch) * s.table_width; ++k) const_cast<int32_t*>(s.block_table)[k] = -1;
+  return 0;
+}
+int dev_set_seq_length(const DevState& s, int seq, int32_t value) {
+  if (gate_closed(s)) return 0;
+  s.len[seq] = value;
+  s.next_pos[seq] = value;
+  return 0;
+}
+int dev_copy_block_rows(const DevState& s, int dst, int src, int rows) {
+  if (gate_closed(s) || rows <= 0) return 0;
+  const size_t row = size_t(s.head_width) * elem_bytes(s.dtype), head = row << s.block_rows_log2;
+  for (int h = 0; h < s.heads; ++h)
+    for (void* base : {s.keys, s.values})
+      std::memcpy(static_cast<char*>(base) + (size_t(dst) * s.heads + h) * head,
+                  static_cast<char*>(base) + (size_t(src) * s.heads + h) * head, size_t(rows) * row);
+  return 0;
+}
+int dev_copy_positions(const DevState& s, int dst_seq, int src_seq, int rows) {
+  if (gate_closed(s)) return 0;
+  for (int k = 0; k < rows; ++k)
+    s.positions[size_t(dst_seq) * s.capacity + k] = s.positions[size_t(src_seq) * s.capacity + k];
+  return 0;
+}
+int dev_copy_seq_rows(const DevState& s, int dst_seq, int src_seq, int rows) {
+  if (gate_closed(s) || rows <= 0) return 0;
+  const size_t row = size_t(s.head_width) * elem_bytes(s.dtype), lane = row * s.capacity;
+  for (int h = 0; h < s.heads; ++h)
+    for (void* base : {s.keys, s.values})
+      std::memcpy(static_cast<char*>(base) + (size_t(dst_seq) * s.heads + h) * lane,
+                  static_cast<char*>(base) + (size_t(src_seq) * s.heads + h) * lane, size_t(rows) * row);
+  return 0;
+}
+// Fake kernels (off by default; kvc_test_fake_kernels turns them on): no
+// attention is computed, but the projection fills the candidate rows with a
+// tag of (call, sequence, row, head, element) and the commit appends them
+// through the block table, so the manager's block bookkeeping can be checked
+// row by row.  kvc_test_fail_next makes the next projection set a failure
+// word (a non-finite key at the given flat index).
+static bool g_fake = false;
+static int g_call = 0;
+static long long g_fail_next = -1;
+static size_t kv_off(const DevState& s, int b, int h, int r) {
+  if (!s.paged) return ((size_t(b) * s.heads + h) * s.capacity + r) * s.head_width;
+  const int lg = s.block_rows_log2;
+  const int blk = s.block_table[size_t(b) * s.table_width + (r >> lg)];
+  return (((size_t(blk) * s.heads + h) << lg) + (r & ((1 << lg) - 1))) * s.head_width;
+}
+int dev_project(const DevState& s, const void*, int n_max, int per_seq) {
+  if (!g_fake) return 1;
+  ++g_call;
+  for (int b = 0; b < s.batch; ++b) {
+    const int n = per_seq ? s.rows[b] : n_max;
+    for (int h = 0; h < s.heads; ++h)
+      for (int i = 0; i < n; ++i)
+        for (int e = 0; e < s.head_width; ++e) {
+          const size_t at = ((size_t(b) * s.heads + h) * n_max + i) * s.head_width + e;
+          const double tag = g_call * 1e6 + b * 1e4 + i * 1e2 + h * 10 + e;
+          static_cast<double*>(s.cand_k)[at] = tag;
+          static_cast<double*>(s.cand_v)[at] = -tag;
+        }
+  }
+  if (g_fail_next >= 0) {
+    s.err->key = (unsigned long long)g_fail_next;
+    g_fail_next = -1;
+  }
+  return 0;
+}
+int dev_attend_decode(const DevState&, const SeqOrder&, void*) { return g_fake ? 0 : 1; }
+int dev_merge_decode(const DevState&, void*) { return g_fake ? 0 : 1; }
+int dev_attend_chunk(const DevState&, int, int, const ChunkOrder&, void*) { return g_fake ? 0 : 1; }
+int dev_output_project(const DevState&, int, int, void*) { return g_fake ? 0 : 1; }
+int dev_commit(const DevState& s, int n_max, int per_seq) {
+  if (!g_fake) return 1;
+  if (gate_closed(s)) return 0;
+  for (int b = 0; b < s.batch; ++b) {
+    const int n = per_seq ? s.rows[b] : n_max;
+    for (int i = 0; i < n; ++i) {
+      const int r = s.len[b] + i;
+      for (int h = 0; h < s.heads; ++h) {
+        const size_t src = ((size_t(b) * s.heads + h) * n_max + i) * s.head_width;
+        const size_t dst = kv_off(s, b, h, r);
+        for (int e = 0; e < s.head_width; ++e) {
+          static_cast<double*>(s.keys)[dst + e] = static_cast<const double*>(s.cand_k)[src + e];
+          static_cast<double*>(s.values)[dst + e] = static_cast<const double*>(s.cand_v)[src + e];
+        }
+      }
+      s.positions[size_t(b) * s.capacity + r] = s.next_pos[b] + i;
+    }
+    s.len[b] += n;
+    s.next_pos[b] += n;
+  }
+  return 0;
+}
 int dev_embed(const DevState&, const int32_t*, const void*, int, int, int, int, void*, void*) { return 1; }
 int dev_residual(const DevState&, const void*, const void*, void*, void*, int, int) { return 1; }
 int dev_event_create(void** e) {
@@ -89,11 +187,17 @@ int dev_event_elapsed(float* ms, void*, void*) {
   return 0;
 }
 int dev_stream_read(const void*, int64_t, void*, void*) { return 1; }
-bool dev_has_kernels() { return false; }
+bool dev_has_kernels() { return g_fake; }
 
 }  // namespace kvc
 
-// Test hooks for the host-side work orders (not part of the library ABI).
+// Test hooks (not part of the library ABI).
+extern "C" void kvc_test_fake_kernels(int on) {
+  kvc::g_fake = on != 0;
+  kvc::g_call = 0;
+  kvc::g_fail_next = -1;
+}
+extern "C" void kvc_test_fail_next(long long flat_index) { kvc::g_fail_next = flat_index; }
 extern "C" int kvc_test_chunk_order(int batch, int n_max, const int32_t* len, const int32_t* rows, int32_t* qtiles,
                                     int32_t* items) {
   kvc::ChunkOrder o;

@@ -1,0 +1,287 @@
+"""Block-paged caches on the CPU: the manager's block bookkeeping.
+
+Chapter 37 ("From causal attention to managed LLM inference state") points to
+serving systems that keep growing KV caches as logical blocks mapped onto
+non-contiguous physical memory; the prefix-reuse note ("Lookup flow and cache
+ownership") keeps branches from modifying each other by copying, and names
+block storage as the next step.  Here the manager (kvc_host.cpp) runs against
+tests/hostcheck_backend.cpp with its fake kernels switched on: no attention is
+computed, the projection writes a tag of (call, sequence, chunk row, head,
+element) into the candidate rows and the commit appends them through the
+block table.  Every paged cache is checked row by row against a contiguous
+cache given the same calls, and pool usage against the block counts the
+sharing rules imply.
+"""
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+from incremental_kv_cache_amd import capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DUMMY = C.c_void_p(64)
+BR = 256  # block rows
+
+
+@pytest.fixture(scope="module")
+def lib(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("hostpaging") / "libkvc_hostcheck.so")
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "incremental_kv_cache_amd", "csrc"),
+           os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_host.cpp"),
+           os.path.join(ROOT, "tests", "hostcheck_backend.cpp"), "-o", out]
+    subprocess.run(cmd, check=True)
+    lib = capi.declare(C.CDLL(out))
+    lib.kvc_test_fake_kernels.argtypes = [C.c_int]
+    lib.kvc_test_fail_next.argtypes = [C.c_longlong]
+    return lib
+
+
+@pytest.fixture
+def fake(lib):
+    lib.kvc_test_fake_kernels(1)
+    yield lib
+    lib.kvc_test_fake_kernels(0)
+
+
+def _layer(lib, max_pos=4096):
+    p = C.c_void_p()
+    assert lib.kvc_params_create(4, capi.KVC_F64, DUMMY, DUMMY, DUMMY, None, C.byref(p)) == 0
+    lay = C.c_void_p()
+    assert lib.kvc_layer_create(p, 2, capi.KVC_POS_ROPE, 10000.0, max_pos, C.byref(lay)) == 0
+    return lay
+
+
+def _paged(lib, lay, batch, cap, pool, chunk=320):
+    c = C.c_void_p()
+    st = lib.kvc_cache_create_paged(lay, batch, cap, chunk, BR, pool, None, C.byref(c))
+    assert st == 0, lib.kvc_last_error().contents.message
+    return c
+
+
+def _contig(lib, lay, batch, cap, chunk=320):
+    c = C.c_void_p()
+    assert lib.kvc_cache_create(lay, batch, cap, chunk, None, C.byref(c)) == 0
+    return c
+
+
+def _chunk(lib, lay, c, rows, flags=0):
+    arr = np.ascontiguousarray(np.asarray(rows, np.int32))
+    w = capi.Work()
+    return lib.kvc_continue_chunk(lay, c, DUMMY, max(1, int(arr.max())), arr.ctypes.data_as(capi.PI32), DUMMY,
+                                  flags, C.byref(w))
+
+
+def _usage(lib, c):
+    u, f = C.c_int32(), C.c_int32()
+    assert lib.kvc_pool_usage(c, C.byref(u), C.byref(f)) == 0, lib.kvc_last_error().contents.message
+    return u.value, f.value
+
+
+def _snap(lib, c, seq):
+    n = C.c_int32()
+    assert lib.kvc_snapshot(c, seq, None, None, None, 0, C.byref(n)) == 0
+    k = np.zeros((2, n.value, 2))
+    v = np.zeros((2, n.value, 2))
+    pos = np.zeros(n.value, np.int32)
+    assert lib.kvc_snapshot(c, seq, k.ctypes.data_as(C.c_void_p), v.ctypes.data_as(C.c_void_p),
+                            pos.ctypes.data_as(capi.PI32), n.value, C.byref(n)) == 0
+    return k, v, pos
+
+
+def _lengths(lib, c, batch):
+    ln = np.zeros(batch, np.int32)
+    npos = np.zeros(batch, np.int32)
+    assert lib.kvc_lengths(c, ln.ctypes.data_as(capi.PI32), npos.ctypes.data_as(capi.PI32)) == 0
+    return ln.tolist(), npos.tolist()
+
+
+def _same(lib, a, b, batch):
+    assert _lengths(lib, a, batch) == _lengths(lib, b, batch)
+    for s in range(batch):
+        for x, y in zip(_snap(lib, a, s), _snap(lib, b, s)):
+            assert np.array_equal(x, y), f"sequence {s}"
+
+
+def test_paged_create_checks_and_geometry(lib):
+    lay = _layer(lib)
+    c = C.c_void_p()
+    for br, pool in ((100, 4), (128, 4), (512, 4), (256, 0)):
+        # not a power of two, below 256, not dividing the capacity 768, empty pool
+        assert lib.kvc_cache_create_paged(lay, 2, 768, 1, br, pool, None, C.byref(c)) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_cache_create_paged(lay, 2, 768, 1, 0, 4, None, C.byref(c)) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_cache_create_paged(lay, 0, 768, 1, 256, 4, None, C.byref(c)) == capi.KVC_ERR_ZERO_BATCH
+    c = _paged(lib, lay, 2, 768, 5)
+    d = capi.CacheDesc()
+    assert lib.kvc_cache_describe(c, C.byref(d)) == 0
+    assert (d.capacity, d.block_rows, d.pool_blocks) == (768, 256, 5)
+    assert _usage(lib, c) == (0, 5)
+    k, v, n = C.c_void_p(), C.c_void_p(), C.c_int64()
+    assert lib.kvc_storage_pointers(c, C.byref(k), C.byref(v), C.byref(n)) == 0
+    assert n.value == 5 * 2 * 256 * 2 * 8  # [pool, H, block rows, d_h] float64
+    contig = _contig(lib, lay, 2, 768)
+    assert lib.kvc_pool_usage(contig, None, None) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_cache_describe(contig, C.byref(d)) == 0 and (d.block_rows, d.pool_blocks) == (0, 0)
+    for h in (c, contig):
+        lib.kvc_cache_destroy(h)
+
+
+def test_ragged_appends_truncates_and_decodes_match_a_contiguous_cache(fake):
+    """Chunks crossing block boundaries, truncations into and onto block
+    boundaries and one-row decodes leave the paged cache row-for-row equal to
+    the contiguous one; blocks in use = sum of ceil(len_b / 256)."""
+    lib = fake
+    lay = _layer(lib)
+    B = 3
+    p, c = _paged(lib, lay, B, 1024, 12), _contig(lib, lay, B, 1024)
+    rng = np.random.default_rng(5)
+    lens = np.zeros(B, np.int64)
+
+    def both(fn):
+        for h in (p, c):
+            lib.kvc_test_fake_kernels(1)  # the same tags on both caches
+            assert fn(h) == 0, lib.kvc_last_error().contents.message
+
+    shape = (C.c_int64 * 3)(B, 1, 4)
+    for step in range(14):
+        if step % 4 == 3:
+            cut = [int(rng.integers(0, l + 1)) for l in lens]
+            cut[0] = (int(lens[0]) // BR) * BR  # onto a block boundary
+            both(lambda h: lib.kvc_truncate(h, np.asarray(cut, np.int32).ctypes.data_as(capi.PI32), 0))
+            lens = np.asarray(cut)
+        elif step % 4 == 2:
+            both(lambda h: lib.kvc_append_and_attend(lay, h, DUMMY, 3, shape, DUMMY, 0, None))
+            lens += 1
+        else:
+            rows = [int(min(rng.integers(0, 320), 1024 - l)) for l in lens]
+            both(lambda h: _chunk(lib, lay, h, rows))
+            lens += rows
+        _same(lib, p, c, B)
+        assert _usage(lib, p)[0] == sum((int(l) + BR - 1) // BR for l in lens)
+    assert lib.kvc_reset(p) == 0
+    assert _usage(lib, p) == (0, 12)
+
+
+def test_fork_shares_blocks_and_copies_on_write(fake):
+    """kvc_fork shares the source's blocks; an append into a shared block copies it
+    first and leaves the source unchanged; an append at a block boundary takes
+    a fresh block and copies nothing.  A contiguous cache given the same calls
+    holds the same rows."""
+    lib = fake
+    lay = _layer(lib)
+    p, c = _paged(lib, lay, 3, 1024, 8), _contig(lib, lay, 3, 1024)
+
+    def both(fn):
+        for h in (p, c):
+            lib.kvc_test_fake_kernels(1)
+            fn(h)
+
+    both(lambda h: _chunk(lib, lay, h, [300, 0, 0]) == 0 or pytest.fail("prefill"))
+    src_before = _snap(lib, p, 0)
+    both(lambda h: lib.kvc_fork(h, 0, 1, 300) == 0 or pytest.fail("fork"))
+    assert _usage(lib, p)[0] == 2  # shared
+    both(lambda h: lib.kvc_fork(h, 0, 2, 256) == 0 or pytest.fail("fork"))
+    assert _usage(lib, p)[0] == 2
+    assert _lengths(lib, p, 3) == ([300, 300, 256], [300, 300, 256])
+    both(lambda h: _chunk(lib, lay, h, [0, 5, 0]) == 0 or pytest.fail("append"))
+    assert _usage(lib, p)[0] == 3  # sequence 1 copied block 1
+    for x, y in zip(src_before, _snap(lib, p, 0)):
+        assert np.array_equal(x, y)  # the source is unchanged
+    k1, _, pos1 = _snap(lib, p, 1)
+    assert np.array_equal(k1[:, :300], src_before[0]) and list(pos1) == list(range(305))
+    both(lambda h: _chunk(lib, lay, h, [0, 0, 7]) == 0 or pytest.fail("append"))
+    assert _usage(lib, p)[0] == 4  # a fresh block at row 256, nothing copied
+    both(lambda h: _chunk(lib, lay, h, [4, 0, 0]) == 0 or pytest.fail("append"))
+    assert _usage(lib, p)[0] == 4  # block 1 is sequence 0's alone again
+    _same(lib, p, c, 3)
+    # forking over a sequence drops its old blocks
+    both(lambda h: lib.kvc_fork(h, 2, 1, 10) == 0 or pytest.fail("fork"))
+    assert _usage(lib, p)[0] == 3
+    _same(lib, p, c, 3)
+
+
+def test_fork_argument_checks(lib):
+    lay = _layer(lib)
+    for h in (_paged(lib, lay, 2, 512, 4), _contig(lib, lay, 2, 512)):
+        assert lib.kvc_fork(h, 0, 0, 0) == capi.KVC_ERR_BAD_ARGUMENT
+        assert lib.kvc_fork(h, 0, 2, 0) == capi.KVC_ERR_BAD_ARGUMENT
+        assert lib.kvc_fork(h, -1, 1, 0) == capi.KVC_ERR_BAD_ARGUMENT
+        assert lib.kvc_fork(h, 0, 1, 1) == capi.KVC_ERR_BAD_CUT
+        assert lib.kvc_fork(h, 0, 1, 0) == 0
+        assert _lengths(lib, h, 2) == ([0, 0], [0, 0])
+
+
+def test_out_of_blocks_is_rejected_with_state_unchanged(fake):
+    lib = fake
+    lay = _layer(lib)
+    p = _paged(lib, lay, 2, 1024, 2)
+    assert _chunk(lib, lay, p, [300, 0]) == 0
+    before = (_lengths(lib, p, 2), [_snap(lib, p, s) for s in range(2)], _usage(lib, p))
+    assert _chunk(lib, lay, p, [0, 1]) == capi.KVC_ERR_OUT_OF_BLOCKS
+    e = lib.kvc_last_error().contents
+    assert (e.expected, e.actual) == (1, 0)
+    after = (_lengths(lib, p, 2), [_snap(lib, p, s) for s in range(2)], _usage(lib, p))
+    assert before[0] == after[0] and before[2] == after[2]
+    for s in range(2):
+        for x, y in zip(before[1][s], after[1][s]):
+            assert np.array_equal(x, y)
+    # a truncation returns a block; the append then fits
+    assert lib.kvc_truncate(p, np.asarray([100, 0], np.int32).ctypes.data_as(capi.PI32), 0) == 0
+    assert _usage(lib, p) == (1, 1)
+    assert _chunk(lib, lay, p, [0, 1]) == 0
+    assert _usage(lib, p) == (2, 0)
+
+
+def test_failed_call_returns_its_blocks(fake):
+    """A device-found failure (a non-finite key) after the blocks were taken, also
+    after a copy-on-write: pool usage, lengths and both sequences' rows are as
+    before the call."""
+    lib = fake
+    lay = _layer(lib)
+    p = _paged(lib, lay, 2, 1024, 6)
+    assert _chunk(lib, lay, p, [300, 0]) == 0
+    assert lib.kvc_fork(p, 0, 1, 300) == 0
+    before = (_lengths(lib, p, 2), [_snap(lib, p, s) for s in range(2)], _usage(lib, p))
+    for rows in ([0, 5], [250, 250]):
+        lib.kvc_test_fail_next(3)
+        assert _chunk(lib, lay, p, rows) == capi.KVC_ERR_NONFINITE_KEY
+        assert _lengths(lib, p, 2) == before[0] and _usage(lib, p) == before[2]
+        for s in range(2):
+            for x, y in zip(before[1][s], _snap(lib, p, s)):
+                assert np.array_equal(x, y)
+    assert _chunk(lib, lay, p, [0, 5]) == 0 and _usage(lib, p) == (3, 3)
+
+
+def test_async_failure_is_deferred_and_the_table_resynchronised(fake):
+    """KVC_ASYNC: a failed call and the calls after it change nothing on the
+    device; kvc_sync reports DEFERRED and the pool again holds exactly the
+    blocks of the committed rows."""
+    lib = fake
+    lay = _layer(lib)
+    p = _paged(lib, lay, 2, 1024, 8)
+    assert _chunk(lib, lay, p, [200, 10]) == 0
+    before = (_lengths(lib, p, 2), _usage(lib, p))
+    lib.kvc_test_fail_next(0)
+    assert _chunk(lib, lay, p, [100, 300], flags=capi.KVC_ASYNC) == 0  # takes 3 blocks on the device
+    assert _chunk(lib, lay, p, [300, 0], flags=capi.KVC_ASYNC) == 0   # suppressed
+    assert lib.kvc_truncate(p, np.asarray([0, 0], np.int32).ctypes.data_as(capi.PI32), 0) == 0  # suppressed
+    assert lib.kvc_sync(p) == capi.KVC_ERR_DEFERRED
+    assert lib.kvc_last_error().contents.actual == capi.KVC_ERR_NONFINITE_KEY
+    assert _lengths(lib, p, 2) == before[0]
+    assert _usage(lib, p) == before[1]
+    assert _chunk(lib, lay, p, [60, 0]) == 0 and _usage(lib, p) == (3, 5)
+
+
+def test_contiguous_fork_copies_rows(fake):
+    lib = fake
+    lay = _layer(lib)
+    c = _contig(lib, lay, 2, 512)
+    assert _chunk(lib, lay, c, [40, 3]) == 0
+    assert lib.kvc_fork(c, 0, 1, 25) == 0
+    k0, v0, p0 = _snap(lib, c, 0)
+    k1, v1, p1 = _snap(lib, c, 1)
+    assert np.array_equal(k1, k0[:, :25]) and np.array_equal(v1, v0[:, :25]) and np.array_equal(p1, p0[:25])
+    assert _lengths(lib, c, 2) == ([40, 25], [40, 25])
