@@ -20,6 +20,13 @@ Readings taken where the pages leave a step open:
   (Chapter 37, "Bind the state, calculate completely, then commit" and the
   incremental-attention listing's scoring loop).
 * The newest query scores itself: the candidate key is the last scored row.
+* Grouped key/value heads (Chapter 37, "From causal attention to managed LLM
+  inference state": Shazeer's analysis of reloading the retained keys and
+  values as the bandwidth bottleneck, and multi-query attention as its remedy).
+  A layer may project keys and values to H_kv heads, H_kv dividing H; W_k and
+  W_v are then [H_kv * d_h, D] and query head h reads key/value head
+  h // (H / H_kv), so consecutive query heads share one key/value head.
+  H_kv = 1 is multi-query attention, H_kv = H the chapter's layer.
 """
 from __future__ import annotations
 
@@ -91,16 +98,18 @@ def attend(q: np.ndarray, keys: np.ndarray, values: np.ndarray):
     return w @ values, w
 
 
-def layer_projections(x_rows, wq, wk, wv, heads: int, positions, base: float, rope: bool):
+def layer_projections(x_rows, wq, wk, wv, heads: int, positions, base: float, rope: bool, kv_heads=None):
     """Per-row rotated queries, rotated keys and values for one layer.
 
-    ``x_rows`` [L, D] at absolute ``positions`` [L].  Returns q, k, v as [L, H, d_h].
-    With ``rope=False`` (the prefix-reuse note's absolute-position model) no
+    ``x_rows`` [L, D] at absolute ``positions`` [L].  Returns q as [L, H, d_h]
+    and k, v as [L, H_kv, d_h] (H_kv = ``kv_heads``, default H).  With
+    ``rope=False`` (the prefix-reuse note's absolute-position model) no
     rotation is applied.
     """
+    kv_heads = heads if kv_heads is None else kv_heads
     q = split_heads(project(x_rows, wq), heads)
-    k = split_heads(project(x_rows, wk), heads)
-    v = split_heads(project(x_rows, wv), heads)
+    k = split_heads(project(x_rows, wk), kv_heads)
+    v = split_heads(project(x_rows, wv), kv_heads)
     if rope:
         pos = np.asarray(positions, F64)
         q = rotate(q, pos, base)
@@ -109,7 +118,7 @@ def layer_projections(x_rows, wq, wk, wv, heads: int, positions, base: float, ro
 
 
 def causal_layer(x_rows, wq, wk, wv, heads: int, base: float = 10000.0,
-                 rope: bool = True, positions=None, rows=None, wo=None):
+                 rope: bool = True, positions=None, rows=None, wo=None, kv_heads=None):
     """Full-prefix causal attention of one layer, recomputed from hidden rows.
 
     This is the reference every cached result must reproduce (Chapter 37,
@@ -119,22 +128,28 @@ def causal_layer(x_rows, wq, wk, wv, heads: int, base: float = 10000.0,
     all).  ``wo``: the layer's output projection, applied to the merged heads
     (Chapter 37, "Bind the state, calculate completely, then commit": merge
     heads, then the output projection); None returns the merged heads.
+    ``kv_heads``: key/value heads H_kv (default H); query head h reads
+    key/value head h // (H / H_kv).
     Returns dict with ``out`` [len(rows), D], ``keys`` / ``values``
-    [H, L, d_h] (the layer's full logical cache), ``weights`` (list per row of
-    [H, p+1]).
+    [H_kv, L, d_h] (the layer's full logical cache), ``weights`` (list per row
+    of [H, p+1]).
     """
     x_rows = np.asarray(x_rows, F64)
     n = x_rows.shape[0]
+    kv_heads = heads if kv_heads is None else kv_heads
+    if heads % kv_heads:
+        raise ValueError("key/value heads must divide the query heads")
+    group = heads // kv_heads
     if positions is None:
         positions = np.arange(n)
-    q, k, v = layer_projections(x_rows, wq, wk, wv, heads, positions, base, rope)
+    q, k, v = layer_projections(x_rows, wq, wk, wv, heads, positions, base, rope, kv_heads)
     if rows is None:
         rows = range(n)
     outs, weights = [], []
     for p in rows:
         o_heads, w_heads = [], []
         for h in range(heads):
-            o, w = attend(q[p, h], k[: p + 1, h], v[: p + 1, h])
+            o, w = attend(q[p, h], k[: p + 1, h // group], v[: p + 1, h // group])
             o_heads.append(o)
             w_heads.append(w)
         outs.append(np.concatenate(o_heads))

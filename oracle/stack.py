@@ -42,12 +42,13 @@ def sinusoidal(positions, width: int) -> np.ndarray:
 
 
 class Layer:
-    """One attention layer: W_q, W_k, W_v (and W_o or None), each [D, D] as [out, in]."""
+    """One attention layer: W_q (and W_o or None) [D, D], W_k and W_v [H_kv * d_h, D], as [out, in]."""
 
-    def __init__(self, wq, wk, wv, heads: int, rope: bool = True, base: float = 10000.0, wo=None):
+    def __init__(self, wq, wk, wv, heads: int, rope: bool = True, base: float = 10000.0, wo=None, kv_heads=None):
         self.w = tuple(np.asarray(m, F64) for m in (wq, wk, wv))
         self.wo = None if wo is None else np.asarray(wo, F64)
         self.heads = heads
+        self.kv_heads = heads if kv_heads is None else kv_heads
         self.rope = rope
         self.base = base
 
@@ -66,7 +67,8 @@ def forward(embed, layers, tokens, sinusoidal_pe: bool = True):
         h = h + sinusoidal(pos, embed.shape[1])
     kv = []
     for lay in layers:
-        r = A.causal_layer(h, *lay.w, heads=lay.heads, base=lay.base, rope=lay.rope, positions=pos, wo=lay.wo)
+        r = A.causal_layer(h, *lay.w, heads=lay.heads, base=lay.base, rope=lay.rope, positions=pos, wo=lay.wo,
+                           kv_heads=lay.kv_heads)
         kv.append((r["keys"], r["values"]))
         h = h + np.tanh(r["out"])
     return h, kv

@@ -179,6 +179,62 @@ def test_projection_orientation_and_head_blocks():
     np.testing.assert_array_equal(A.split_heads(np.arange(8.0), 2), [[0, 1, 2, 3], [4, 5, 6, 7]])
 
 
+def _repeat_kv_heads(w, kv_heads, group):
+    """MHA weights whose head blocks repeat each key/value head block `group` times in order."""
+    d = w.shape[1]
+    dh = w.shape[0] // kv_heads
+    return np.repeat(w.reshape(kv_heads, dh, d), group, axis=0).reshape(kv_heads * group * dh, d)
+
+
+@pytest.mark.parametrize("heads,kv_heads", [(8, 2), (8, 1), (6, 3), (4, 4)])
+def test_grouped_heads_equal_multi_head_with_shared_weights(heads, kv_heads):
+    """Grouped key/value heads (Chapter 37, "From causal attention to managed LLM
+    inference state": multi-query attention as the remedy for reloading the
+    retained keys and values).  A layer with H_kv key/value heads equals the
+    chapter's multi-head layer whose W_k / W_v repeat each key/value head block
+    for its H / H_kv consecutive query heads: same outputs, and the shared
+    keys and values are the repeated heads' keys and values.  A wrong
+    query-to-key/value-head assignment (h % H_kv) fails here."""
+    dh, L = 4, 7
+    D = heads * dh
+    group = heads // kv_heads
+    x = synth.normal(9, 2, (L, D))
+    wq = synth.normal(9, 3, (D, D), std=D ** -0.5)
+    wk = synth.normal(9, 4, (kv_heads * dh, D), std=D ** -0.5)
+    wv = synth.normal(9, 5, (kv_heads * dh, D), std=D ** -0.5)
+    wo = synth.normal(9, 10, (D, D), std=D ** -0.5)
+    for rope in (True, False):
+        g = A.causal_layer(x, wq, wk, wv, heads=heads, kv_heads=kv_heads, rope=rope, wo=wo)
+        m = A.causal_layer(x, wq, _repeat_kv_heads(wk, kv_heads, group), _repeat_kv_heads(wv, kv_heads, group),
+                           heads=heads, rope=rope, wo=wo)
+        np.testing.assert_allclose(g["out"], m["out"], rtol=0, atol=1e-14)
+        assert g["keys"].shape == (kv_heads, L, dh)
+        np.testing.assert_array_equal(g["keys"], m["keys"][::group])
+        np.testing.assert_array_equal(g["values"], m["values"][::group])
+        for p in range(L):
+            np.testing.assert_array_equal(g["weights"][p], m["weights"][p])
+    if 1 < kv_heads < heads:
+        # the assignment h % H_kv instead of h // (H / H_kv) gives another layer
+        wrong = np.tile(wk.reshape(kv_heads, dh, D), (group, 1, 1)).reshape(D, D)
+        wv_wrong = np.tile(wv.reshape(kv_heads, dh, D), (group, 1, 1)).reshape(D, D)
+        other = A.causal_layer(x, wq, wrong, wv_wrong, heads=heads)["out"]
+        assert np.max(np.abs(other - A.causal_layer(x, wq, wk, wv, heads=heads, kv_heads=kv_heads)["out"])) > 1e-3
+
+
+def test_multi_query_single_row_returns_the_shared_value():
+    """H_kv = 1 (Shazeer's multi-query form) with one row: every query head's weight
+    on the single key is 1, so every head block of the output is the one shared
+    value row, exactly."""
+    D, heads = 12, 3
+    x = synth.normal(10, 2, (1, D))
+    wq = synth.normal(10, 3, (D, D))
+    wk = synth.normal(10, 4, (D // heads, D))
+    wv = synth.normal(10, 5, (D // heads, D))
+    r = A.causal_layer(x, wq, wk, wv, heads=heads, kv_heads=1)
+    v = A.project(x, wv)[0]
+    np.testing.assert_array_equal(r["out"][0], np.tile(v, heads))
+
+
 @pytest.mark.parametrize("seed", [37, 7, 11, 23])
 def test_seeded_incremental_equals_full_prefix(seed):
     """Chapter 37 'Predict the third result': cached equals full prefix within 1e-12,
