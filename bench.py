@@ -21,6 +21,9 @@ Workloads (default: headline):
   paged     headline with block-paged K/V (kvc_cache_create_paged, 512-row blocks,
             pool = B x C / 512 blocks, handed out across sequences by the prefill)
   paged_ragged  ragged lengths with a pool of exactly sum_b ceil(t_b / 512) blocks
+  grouped   headline with 8 key/value heads for the 32 query heads (W_k, W_v
+            [1024 x 4096]); each decode workgroup serves the 4 query heads of one
+            key/value head from one read of its rows
 
 Prints one JSON line (rank 0).  `roofline` describes the dominant kernel, timed
 with HIP events recorded by the library on the cache's stream.  `cpu_baseline`
@@ -77,6 +80,7 @@ WORKLOADS = {
     "session": dict(B=32, H=32, dh=128, C=4096, layers=4, vocab=8192, kind="session"),
     "paged": dict(B=32, H=32, dh=128, C=4096, t="full", kind="decode", block_rows=512),
     "paged_ragged": dict(B=32, H=32, dh=128, C=4096, t="uniform", kind="decode", block_rows=512),
+    "grouped": dict(B=32, H=32, dh=128, C=4096, t="full", kind="decode", kv_heads=8),
 }
 
 
@@ -116,12 +120,14 @@ def setup(wl, max_chunk=512):
 
     B, H, dh, C = wl["B"], wl["H"], wl["dh"], wl["C"]
     D = H * dh
+    KVW = wl.get("kv_heads", H) * dh
     t0 = time.time()
+    shapes = {synth.STREAM_WQ: (D, D), synth.STREAM_WK: (KVW, D), synth.STREAM_WV: (KVW, D)}
     with _pool() as ex:
-        ws = list(ex.map(lambda s: synth.round_to_bf16_bits(synth.normal(SEED, s, (D, D), std=D ** -0.5)),
+        ws = list(ex.map(lambda s: synth.round_to_bf16_bits(synth.normal(SEED, s, shapes[s], std=D ** -0.5)),
                          (synth.STREAM_WQ, synth.STREAM_WK, synth.STREAM_WV)))
     wdev = [to_dev_bf16(w) for w in ws]
-    params = K.kvc_params_create(*wdev)
+    params = K.kvc_params_create_grouped(*wdev) if KVW != D else K.kvc_params_create(*wdev)
     layer = K.kvc_layer_create(params, H, K.KVC_POS_ROPE, 10000.0, C)
     if wl["kind"] == "decode":
         if wl["t"] == "full":
@@ -159,7 +165,7 @@ def paging_summary(env, wl):
     cache = env["cache"]
     d = cache.desc
     used, free = K.kvc_pool_usage(cache)
-    row_bytes = 2 * wl["H"] * wl["dh"] * 2  # K and V, bf16
+    row_bytes = 2 * wl.get("kv_heads", wl["H"]) * wl["dh"] * 2  # K and V, bf16
     return {"block_rows": d["block_rows"], "pool_blocks": d["pool_blocks"], "blocks_in_use": used,
             "pool_bytes": d["pool_blocks"] * d["block_rows"] * row_bytes,
             "contiguous_bytes": wl["B"] * wl["C"] * row_bytes}
@@ -220,6 +226,7 @@ def cpu_baseline_decode(env, wl, out_gpu, x_bits, budget_s=20.0):
     from incremental_kv_cache_amd import synth
     from oracle import attention as A
     D, H, dh = env["D"], wl["H"], wl["dh"]
+    HK = wl.get("kv_heads", H)
     w = [synth.bf16_bits_to_f64(b) for b in env["weights_bits"]]
     done, t_full, t_inc, worst = 0, 0.0, 0.0, 0.0
     for b in range(wl["B"]):
@@ -229,15 +236,15 @@ def cpu_baseline_decode(env, wl, out_gpu, x_bits, budget_s=20.0):
         x_new = synth.bf16_bits_to_f64(x_bits[b])
         rows = np.concatenate([prefix, x_new])
         t0 = time.perf_counter()
-        ref = A.full_prefix_decode(rows, *w, heads=H)
+        ref = A.full_prefix_decode(rows, *w, heads=H, kv_heads=HK)
         t_full += time.perf_counter() - t0
-        cache = A.DecodeCache(H, dh, s + 1)
+        cache = A.DecodeCache(HK, dh, s + 1)
         cache.keys[:, :s] = ref["keys"][:, :s]
         cache.values[:, :s] = ref["values"][:, :s]
         cache.positions[:s] = np.arange(s)
         cache.len = cache.next_position = s
         t0 = time.perf_counter()
-        inc, _, _ = A.incremental_step(cache, x_new[0], *w, heads=H)
+        inc, _, _ = A.incremental_step(cache, x_new[0], *w, heads=H, kv_heads=HK)
         t_inc += time.perf_counter() - t0
         worst = max(worst, float(np.max(np.abs(out_gpu[b] - ref["out"]))),
                     float(np.max(np.abs(out_gpu[b] - inc))))
@@ -346,7 +353,8 @@ def run_decode(name, wl, steps, warmup, cpu):
     torch.cuda.synchronize()
     achievable = achievable_read_gbps()
     t = [s + 1 for s in start]
-    kv_bytes = sum(2 * H * tb * dh * 2 for tb in t)
+    HK = wl.get("kv_heads", H)
+    kv_bytes = sum(2 * HK * tb * dh * 2 for tb in t)
     attend_ms = st[1]
     att_gbps = kv_bytes / (attend_ms * 1e-3) / 1e9
     attn_merge_gbps = kv_bytes / ((st[1] + st[2]) * 1e-3) / 1e9
@@ -356,8 +364,9 @@ def run_decode(name, wl, steps, warmup, cpu):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{name}: one-layer cached decode, B={B} H={H} d_h={dh} C={wl['C']} "
                                f"t={'uniform[1,%d]' % wl['C'] if wl['t'] == 'uniform' else t[0]}, bf16 K/V"
-                               f"{', block-paged %d-row blocks' % wl['block_rows'] if paging else ''}, "
-                               f"fp32 accumulate", "batch": B, "heads": H, "head_width": dh,
+                               f"{', block-paged %d-row blocks' % wl['block_rows'] if paging else ''}"
+                               f"{', %d key/value heads' % HK if HK != H else ''}, "
+                               f"fp32 accumulate", "batch": B, "heads": H, "kv_heads": HK, "head_width": dh,
                    "capacity": wl["C"], "t_mean": float(np.mean(t)), "seed": SEED},
         "kv_read_GBps": attn_merge_gbps, "kv_read_frac_of_peak": attn_merge_gbps / HBM_PEAK_GBPS,
         "step_ms_percentiles": pct,

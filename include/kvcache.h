@@ -64,7 +64,8 @@ enum {
                                                  actual = free)                          */
   /* Found on the device before the commit; the commit is then suppressed.
    * Precedence when several hold: key, value, query, position, output. */
-  KVC_ERR_NONFINITE_KEY = 30,    /* candidate rotated key has a NaN/Inf (first flat index) */
+  KVC_ERR_NONFINITE_KEY = 30,    /* candidate rotated key has a NaN/Inf (first flat index
+                                    over [B, H_kv, n, d_h])                                */
   KVC_ERR_NONFINITE_VALUE = 31,  /* candidate value has a NaN/Inf                          */
   KVC_ERR_NONFINITE_QUERY = 32,  /* rotated query has a NaN/Inf                            */
   KVC_ERR_ROTARY_POSITION = 33,  /* a row's position reaches the rotary max positions      */
@@ -146,6 +147,7 @@ typedef struct {
   int32_t kv_dtype, pos_mode, rope_max_positions, device;
   double rope_base;
   int32_t block_rows, pool_blocks; /* paged caches; 0 for contiguous storage */
+  int32_t kv_heads;                /* key/value heads H_kv (= heads without grouping) */
 } kvc_cache_desc;
 
 typedef struct kvc_params kvc_params; /* W_q, W_k, W_v (, W_o) with an identity and revisions */
@@ -165,6 +167,22 @@ kvc_status kvc_params_create(int32_t model_width, kvc_dtype dtype, const void* w
                              const void* w_k, const void* w_v, const void* w_o,
                              kvc_params** out);
 
+/* A parameter set with grouped key/value heads (Chapter 37, "From causal
+ * attention to managed LLM inference state": Shazeer's analysis names the
+ * repeated loading of the retained keys and values as the bandwidth bottleneck
+ * and answers it with multi-query attention).  w_q and w_o are [D, D] as for
+ * kvc_params_create; w_k and w_v are DEVICE [kv_width, D] row-major: they
+ * project a row to H_kv = kv_width / d_h key/value heads, and query head h
+ * reads key/value head h / (H / H_kv) (H_kv = 1: multi-query; kv_width = D:
+ * the same as kvc_params_create).  A cache of such a layer stores
+ * [B, H_kv, C, d_h], so every retained row is H / H_kv times smaller to keep
+ * and to read.  kvc_layer_create checks that kv_width is a whole number of
+ * head widths dividing the head count.  Errors: those of kvc_params_create,
+ * and BAD_ARGUMENT (kv_width <= 0 or not dividing D). */
+kvc_status kvc_params_create_grouped(int32_t model_width, int32_t kv_width, kvc_dtype dtype,
+                                     const void* w_q, const void* w_k, const void* w_v,
+                                     const void* w_o, kvc_params** out);
+
 /* Records an in-place update of weight `which` (0 W_q, 1 W_k, 2 W_v, 3 W_o, -1
  * all): its value revision advances and caches bound to the old revision
  * reject further calls (Chapter 37: an optimiser step keeps the identity but
@@ -178,14 +196,16 @@ void kvc_params_destroy(kvc_params* params);
  * SHAPE_UNSUPPORTED).  Several layers may share one parameter set with
  * different rotary configurations (Chapter 37 error evidence: same parameters,
  * doubled base or one more max position).  rope_base > 0, rope_max_positions > 0.
- * The params handle must outlive the layer.  Errors: NULL_ARGUMENT,
- * BAD_ARGUMENT, SHAPE_UNSUPPORTED. */
+ * With grouped parameters the layer has H_kv = kv_width / d_h key/value
+ * heads, which must divide `heads`.  The params handle must outlive the layer.
+ * Errors: NULL_ARGUMENT, BAD_ARGUMENT, SHAPE_UNSUPPORTED. */
 kvc_status kvc_layer_create(const kvc_params* params, int32_t heads, kvc_pos_mode pos_mode,
                             double rope_base, int32_t rope_max_positions, kvc_layer** out);
 void kvc_layer_destroy(kvc_layer* layer);
 
 /* Creates an empty cache bound to `layer` (Chapter 37, the cache constructor):
- * K/V storage [B, H, C, d_h] in the weights' type, zero-filled; lengths and
+ * K/V storage [B, H_kv, C, d_h] in the weights' type (H_kv = H unless the
+ * parameter set groups its key/value heads), zero-filled; lengths and
  * next positions 0; binding = the layer's parameter identity and current
  * revisions and its rotary configuration.  max_chunk_rows (>= 1) bounds n_max
  * of kvc_continue_chunk and sizes its scratch.  hip_stream: a hipStream_t (or
@@ -283,7 +303,7 @@ kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags);
 kvc_status kvc_reset(kvc_cache* cache);
 
 /* Logical snapshot of sequence `seq` (Chapter 37, logical key/value
- * accessors): keys_out, values_out HOST [H, len, d_h] in the storage type,
+ * accessors): keys_out, values_out HOST [H_kv, len, d_h] in the storage type,
  * positions_out HOST int32[len] (each nullable).  rows_capacity: rows the
  * buffers hold; rows_out (HOST): len.  Synchronises the stream.  Errors:
  * NULL_ARGUMENT, BAD_ARGUMENT (seq out of range or rows_capacity < len),

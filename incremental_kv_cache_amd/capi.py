@@ -84,6 +84,7 @@ class CacheDesc(C.Structure):
         ("capacity", C.c_int32), ("max_chunk_rows", C.c_int32), ("kv_dtype", C.c_int32),
         ("pos_mode", C.c_int32), ("rope_max_positions", C.c_int32), ("device", C.c_int32),
         ("rope_base", C.c_double), ("block_rows", C.c_int32), ("pool_blocks", C.c_int32),
+        ("kv_heads", C.c_int32),
     ]
 
 
@@ -96,6 +97,7 @@ PI64 = C.POINTER(C.c_int64)
 
 PROTOTYPES = {
     "kvc_params_create": (I32, [I32, I32, P, P, P, P, PP]),
+    "kvc_params_create_grouped": (I32, [I32, I32, I32, P, P, P, P, PP]),
     "kvc_params_mark_updated": (I32, [P, I32]),
     "kvc_params_destroy": (None, [P]),
     "kvc_layer_create": (I32, [P, I32, I32, C.c_double, I32, PP]),

@@ -70,7 +70,10 @@ __device__ __forceinline__ uint4 load_stream(const bf16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-template <int DH, int U, bool PAGED>
+// QPW query heads (consecutive, sharing key/value head hk) per workgroup: every
+// K/V row is loaded once and scored against all of them, so grouped layers read
+// each retained row once per key/value head rather than once per query head.
+template <int DH, int U, bool PAGED, int QPW>
 __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevState s, SeqOrder order,
                                                                         float* __restrict__ out) {
   constexpr int G = DH / 8;
@@ -78,11 +81,11 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
   constexpr int GROUPS = kWaves * RPW;
   constexpr int STEP = GROUPS * U;
   static_assert(kMinBlockRows % STEP == 0 && kDecodeTileRows % STEP == 0, "a step must stay inside one block");
-  __shared__ float sm_m[GROUPS], sm_l[GROUPS];
-  __shared__ float sm_acc[GROUPS][DH + 4];
+  __shared__ float sm_m[QPW][GROUPS], sm_l[QPW][GROUPS];
+  __shared__ float sm_acc[QPW][GROUPS][DH + 4];
 
   // sequences with the most rows first (blocks are dispatched with z slowest)
-  const int tile = blockIdx.x, h = blockIdx.y, b = order.count ? order.seq[blockIdx.z] : blockIdx.z;
+  const int tile = blockIdx.x, h0 = blockIdx.y * QPW, b = order.count ? order.seq[blockIdx.z] : blockIdx.z;
   const int C = s.capacity;
   const int len = min(max(s.len[b], 0), C - 1);
   const int t = len + 1;
@@ -96,36 +99,44 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
   const int wave = threadIdx.x >> 6;
   const int g = lane % G;
   const int grp = wave * RPW + lane / G;
-  const size_t lane_id = size_t(b) * s.heads + h;
+  const int hk = h0 / (s.heads / s.kv_heads);
+  const size_t kv_lane = size_t(b) * s.kv_heads + hk;
+  const size_t lane0 = size_t(b) * s.heads + h0;  // query lane of the first head
   const bf16_t* kpool = static_cast<const bf16_t*>(s.keys) + g * 8;
   const bf16_t* vpool = static_cast<const bf16_t*>(s.values) + g * 8;
-  const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + lane_id * DH + g * 8;
-  const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + lane_id * DH + g * 8;
+  const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + kv_lane * DH + g * 8;
+  const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + kv_lane * DH + g * 8;
 
   const float sl2 = float(s.scale) * 1.4426950408889634f;
-  float qv[8];
-  {
-    const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(s.q) + lane_id * DH + g * 8);
-    const float4 a = qp[0], c = qp[1];
-    qv[0] = a.x * sl2;
-    qv[1] = a.y * sl2;
-    qv[2] = a.z * sl2;
-    qv[3] = a.w * sl2;
-    qv[4] = c.x * sl2;
-    qv[5] = c.y * sl2;
-    qv[6] = c.z * sl2;
-    qv[7] = c.w * sl2;
-  }
-  float m = -INFINITY, l = 0.f;
-  float acc[8];
+  float qv[QPW][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int qh = 0; qh < QPW; ++qh) {
+    const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(s.q) + (lane0 + qh) * DH + g * 8);
+    const float4 a = qp[0], c = qp[1];
+    qv[qh][0] = a.x * sl2;
+    qv[qh][1] = a.y * sl2;
+    qv[qh][2] = a.z * sl2;
+    qv[qh][3] = a.w * sl2;
+    qv[qh][4] = c.x * sl2;
+    qv[qh][5] = c.y * sl2;
+    qv[qh][6] = c.z * sl2;
+    qv[qh][7] = c.w * sl2;
+  }
+  float m[QPW], l[QPW];
+  float acc[QPW][8];
+#pragma unroll
+  for (int qh = 0; qh < QPW; ++qh) {
+    m[qh] = -INFINITY;
+    l[qh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[qh][e] = 0.f;
+  }
 
   for (int base = r0; base < r1; base += STEP) {
     // the STEP rows from base lie in one block of a paged cache (block rows are
     // a power-of-two multiple of STEP, tiles start on multiples of 512)
     const ptrdiff_t lane_base =
-        PAGED ? kv_block_base(s, b, h, min(base, max(len - 1, 0))) : ptrdiff_t(lane_id * C) * DH;
+        PAGED ? kv_block_base(s, b, hk, min(base, max(len - 1, 0))) : ptrdiff_t(kv_lane * C) * DH;
     const bf16_t* kc = kpool + lane_base;
     const bf16_t* vc = vpool + lane_base;
     uint4 kr[U], vr[U];
@@ -140,74 +151,94 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
       kr[u] = load_stream(kp);
       vr[u] = load_stream(vp);
     }
-    float sc[U];
+    float sc[QPW][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float kf[8];
       unpack_bf16x8(kr[u], kf);
-      float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) d = fmaf(qv[e], kf[e], d);
-      sc[u] = d;
+      for (int qh = 0; qh < QPW; ++qh) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = fmaf(qv[qh][e], kf[e], d);
+        sc[qh][u] = d;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) sc[u] = group_sum_dpp<G>(sc[u]);
-    float mx = m;
+    for (int qh = 0; qh < QPW; ++qh)
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      sc[u] = ok[u] ? sc[u] : -INFINITY;
-      mx = fmaxf(mx, sc[u]);
+      for (int u = 0; u < U; ++u) sc[qh][u] = group_sum_dpp<G>(sc[qh][u]);
+    float corr[QPW];
+#pragma unroll
+    for (int qh = 0; qh < QPW; ++qh) {
+      float mx = m[qh];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        sc[qh][u] = ok[u] ? sc[qh][u] : -INFINITY;
+        mx = fmaxf(mx, sc[qh][u]);
+      }
+      // a row group past the tile end sees only masked rows: keep its state at (-inf, 0, 0)
+      corr[qh] = mx == -INFINITY ? 1.f : exp2f(m[qh] - mx);
+      l[qh] *= corr[qh];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[qh][e] *= corr[qh];
+#pragma unroll
+      for (int u = 0; u < U; ++u) sc[qh][u] = ok[u] ? exp2f(sc[qh][u] - mx) : 0.f;
+      m[qh] = mx;
     }
-    // a row group past the tile end sees only masked rows: keep its state at (-inf, 0, 0)
-    const float corr = mx == -INFINITY ? 1.f : exp2f(m - mx);
-    l *= corr;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] *= corr;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const float p = ok[u] ? exp2f(sc[u] - mx) : 0.f;
-      l += p;
       float vf[8];
       unpack_bf16x8(vr[u], vf);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(p, vf[e], acc[e]);
+      for (int qh = 0; qh < QPW; ++qh) {
+        const float p = sc[qh][u];
+        l[qh] += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[qh][e] = fmaf(p, vf[e], acc[qh][e]);
+      }
     }
-    m = mx;
   }
 
-  if (g == 0) {
-    sm_m[grp] = m;
-    sm_l[grp] = l;
-  }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) sm_acc[grp][g * 8 + e] = acc[e];
+  for (int qh = 0; qh < QPW; ++qh) {
+    if (g == 0) {
+      sm_m[qh][grp] = m[qh];
+      sm_l[qh][grp] = l[qh];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm_acc[qh][grp][g * 8 + e] = acc[qh][e];
+  }
   __syncthreads();
 
   const int j = threadIdx.x;  // output feature handled by this thread (j < DH)
-  float M = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < GROUPS; ++k) M = fmaxf(M, sm_m[k]);
-  float L = 0.f, A = 0.f;
+  for (int qh = 0; qh < QPW; ++qh) {
+    float M = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < GROUPS; ++k) {
-    const float w = exp2f(sm_m[k] - M);  // 0 for groups that saw no row
-    L += sm_l[k] * w;
-    if (j < DH) A += sm_acc[k][j] * w;
-  }
-  const size_t out_base = size_t(b) * s.model_width + size_t(h) * DH;
-  if (ntiles == 1) {
-    if (j < DH) {
-      const float o = A / L;
-      out[out_base + j] = o;
-      if (!isfinite(o)) flag_min(&s.err->output, out_base + j);
+    for (int k = 0; k < GROUPS; ++k) M = fmaxf(M, sm_m[qh][k]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int k = 0; k < GROUPS; ++k) {
+      const float w = exp2f(sm_m[qh][k] - M);  // 0 for groups that saw no row
+      L += sm_l[qh][k] * w;
+      if (j < DH) A += sm_acc[qh][k][j] * w;
     }
-    return;
-  }
-  float* part = static_cast<float*>(s.partials) + (lane_id * s.max_tiles + tile) * (DH + 2);
-  if (j < DH) part[2 + j] = A;
-  if (j == 0) {
-    part[0] = M;
-    part[1] = L;
+    const size_t out_base = size_t(b) * s.model_width + size_t(h0 + qh) * DH;
+    if (ntiles == 1) {
+      if (j < DH) {
+        const float o = A / L;
+        out[out_base + j] = o;
+        if (!isfinite(o)) flag_min(&s.err->output, out_base + j);
+      }
+      continue;
+    }
+    float* part = static_cast<float*>(s.partials) + ((lane0 + qh) * s.max_tiles + tile) * (DH + 2);
+    if (j < DH) part[2 + j] = A;
+    if (j == 0) {
+      part[0] = M;
+      part[1] = L;
+    }
   }
 }
 
@@ -262,22 +293,39 @@ inline hipStream_t st(void* p) { return static_cast<hipStream_t>(p); }
 // other shapes (the vector kernels then run).
 int fast_attend_decode(const DevState& s, const SeqOrder& order, void* out) {
   if (s.dtype != KVC_BF16) return -1;
-  dim3 grid((s.capacity + s.tile_rows - 1) / s.tile_rows, s.heads, s.batch);
   float* o = static_cast<float*>(out);
   const dim3 block(64 * kWaves);
+  const int qpw = decode_heads_per_block(s.dtype, s.head_width, s.heads / s.kv_heads);
+  const dim3 grid((s.capacity + s.tile_rows - 1) / s.tile_rows, s.heads / qpw, s.batch);
+#define KVC_DECODE_LAUNCH(DH_, U_, QPW_)                                                                     \
+  do {                                                                                                    \
+    if (s.paged)                                                                                          \
+      hipLaunchKernelGGL((attend_decode_bf16_kernel<DH_, U_, true, QPW_>), grid, block, 0, st(s.stream), s, \
+                         order, o);                                                                       \
+    else                                                                                                  \
+      hipLaunchKernelGGL((attend_decode_bf16_kernel<DH_, U_, false, QPW_>), grid, block, 0, st(s.stream),   \
+                         s, order, o);                                                                    \
+  } while (0)
+  // eight query heads per workgroup hold 8 x 16 accumulators per lane: half the
+  // row groups in flight keeps them in registers
   if (s.head_width == 128) {
-    if (s.paged)
-      hipLaunchKernelGGL((attend_decode_bf16_kernel<128, 8, true>), grid, block, 0, st(s.stream), s, order, o);
-    else
-      hipLaunchKernelGGL((attend_decode_bf16_kernel<128, 8, false>), grid, block, 0, st(s.stream), s, order, o);
+    switch (qpw) {
+      case 1: KVC_DECODE_LAUNCH(128, 8, 1); break;
+      case 2: KVC_DECODE_LAUNCH(128, 8, 2); break;
+      case 4: KVC_DECODE_LAUNCH(128, 8, 4); break;
+      default: KVC_DECODE_LAUNCH(128, 4, 8); break;
+    }
   } else if (s.head_width == 64) {
-    if (s.paged)
-      hipLaunchKernelGGL((attend_decode_bf16_kernel<64, 4, true>), grid, block, 0, st(s.stream), s, order, o);
-    else
-      hipLaunchKernelGGL((attend_decode_bf16_kernel<64, 4, false>), grid, block, 0, st(s.stream), s, order, o);
+    switch (qpw) {
+      case 1: KVC_DECODE_LAUNCH(64, 4, 1); break;
+      case 2: KVC_DECODE_LAUNCH(64, 4, 2); break;
+      case 4: KVC_DECODE_LAUNCH(64, 4, 4); break;
+      default: KVC_DECODE_LAUNCH(64, 2, 8); break;
+    }
   } else {
     return -1;
   }
+#undef KVC_DECODE_LAUNCH
   return int(hipGetLastError());
 }
 

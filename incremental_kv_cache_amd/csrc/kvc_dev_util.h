@@ -92,14 +92,15 @@ __device__ __forceinline__ bool any_error(const ErrWords* e) {
   return (e->key & e->value & e->query & e->position & e->output & e->token) != kErrClear;
 }
 
-// Element offset of row r of lane (b, h) in the K or V storage (contiguous
-// [B, H, C, d_h], or the block pool through the sequence's block table).
+// Element offset of row r of key/value lane (b, h), h < H_kv, in the K or V
+// storage (contiguous [B, H_kv, C, d_h], or the block pool through the
+// sequence's block table).
 __device__ __forceinline__ size_t kv_offset(const DevState& s, int b, int h, int r) {
   const int dh = s.head_width;
-  if (!s.paged) return ((size_t(b) * s.heads + h) * s.capacity + r) * dh;
+  if (!s.paged) return ((size_t(b) * s.kv_heads + h) * s.capacity + r) * dh;
   const int lg = s.block_rows_log2;
   const int blk = s.block_table[size_t(b) * s.table_width + (r >> lg)];
-  return (((size_t(blk) * s.heads + h) << lg) + (r & ((1 << lg) - 1))) * dh;
+  return (((size_t(blk) * s.kv_heads + h) << lg) + (r & ((1 << lg) - 1))) * dh;
 }
 
 // Element offset that row r0's block would have at row 0 of the same block:
@@ -107,11 +108,11 @@ __device__ __forceinline__ size_t kv_offset(const DevState& s, int b, int h, int
 // (contiguous).  Used where a run of rows is known to lie in one block.
 __device__ __forceinline__ ptrdiff_t kv_block_base(const DevState& s, int b, int h, int r0) {
   const int dh = s.head_width;
-  if (!s.paged) return ptrdiff_t((size_t(b) * s.heads + h) * s.capacity) * dh;
+  if (!s.paged) return ptrdiff_t((size_t(b) * s.kv_heads + h) * s.capacity) * dh;
   const int lg = s.block_rows_log2;
   // an unassigned block (-1) is only reached by callers that read no cache row
   const int blk = max(s.block_table[size_t(b) * s.table_width + (r0 >> lg)], 0);
-  return (ptrdiff_t(size_t(blk) * s.heads + h) << lg) * dh - ptrdiff_t((r0 >> lg) << lg) * dh;
+  return (ptrdiff_t(size_t(blk) * s.kv_heads + h) << lg) * dh - ptrdiff_t((r0 >> lg) << lg) * dh;
 }
 
 // True when a failure word of the cache's gate (its own words, or every layer

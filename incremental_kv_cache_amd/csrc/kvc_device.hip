@@ -51,7 +51,8 @@ __global__ __launch_bounds__(256) void project_kernel(DevState s, const XT* __re
   const int dh = s.head_width;
   const int half = dh >> 1;
   const int pair = blockIdx.x * blockDim.x + threadIdx.x;
-  const bool active = pair < s.heads * half;
+  const int heads_p = (p == 1 || p == 2) ? s.kv_heads : s.heads;  // K and V may have fewer heads
+  const bool active = pair < heads_p * half;
   const int h = active ? pair / half : 0;
   const int f = active ? pair - h * half : 0;
   const T* W = static_cast<const T*>(p == 0 ? s.wq : (p == 1 ? s.wk : (p == 2 ? s.wv : s.wo)));
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(256) void project_kernel(DevState s, const XT* __re
     r0 = acc0 * c - acc1 * sn;
     r1 = acc1 * c + acc0 * sn;
   }
-  const size_t flat0 = (size_t(b * s.heads + h) * n_max + i) * dh + f;
+  const size_t flat0 = (size_t(b * heads_p + h) * n_max + i) * dh + f;
   const size_t flat1 = flat0 + half;
   if (p == 0) {
     A* q = static_cast<A*>(s.q);
@@ -124,8 +125,9 @@ __global__ __launch_bounds__(256) void project_kernel(DevState s, const XT* __re
 // each); groups keep private (max, sum, weighted values) and are merged through
 // LDS at the end.  Returns the tile's max and sum in M/L and the weighted
 // values in acc_out[0..DH) (LDS), visible to the whole block after return.
+// hk: the key/value head the query reads.
 template <typename T, int DH, int NW>
-__device__ __forceinline__ void attend_rows(const DevState& s, int b, int h, const typename Acc<T>::type* __restrict__ q,
+__device__ __forceinline__ void attend_rows(const DevState& s, int b, int hk, const typename Acc<T>::type* __restrict__ q,
                                             const T* __restrict__ kc, const T* __restrict__ vc,
                                             const T* __restrict__ kn, const T* __restrict__ vn, int len,
                                             int r0, int r1, typename Acc<T>::type scale,
@@ -151,7 +153,7 @@ __device__ __forceinline__ void attend_rows(const DevState& s, int b, int h, con
   for (int e = 0; e < VEC; ++e) acc[e] = 0;
 
   for (int r = r0 + grp; r < r1; r += GROUPS) {
-    const size_t off = r < len ? kv_offset(s, b, h, r) : 0;
+    const size_t off = r < len ? kv_offset(s, b, hk, r) : 0;
     const T* kr = (r < len) ? kc + off : kn + size_t(r - len) * DH;
     const T* vr = (r < len) ? vc + off : vn + size_t(r - len) * DH;
     A kv[VEC], vv[VEC];
@@ -212,13 +214,15 @@ __global__ __launch_bounds__(64 * kAttendWaves) void attend_decode_kernel(DevSta
   if (r0 >= t) return;
   const int r1 = min(t, r0 + s.tile_rows);
   const size_t lane_id = size_t(b) * s.heads + h;
+  const int hk = h / (s.heads / s.kv_heads);
+  const size_t kv_lane = size_t(b) * s.kv_heads + hk;
   const T* kc = static_cast<const T*>(s.keys);
   const T* vc = static_cast<const T*>(s.values);
-  const T* kn = static_cast<const T*>(s.cand_k) + lane_id * DH;
-  const T* vn = static_cast<const T*>(s.cand_v) + lane_id * DH;
+  const T* kn = static_cast<const T*>(s.cand_k) + kv_lane * DH;
+  const T* vn = static_cast<const T*>(s.cand_v) + kv_lane * DH;
   const A* q = static_cast<const A*>(s.q) + lane_id * DH;
   A M, L;
-  attend_rows<T, DH, kAttendWaves>(s, b, h, q, kc, vc, kn, vn, len, r0, r1, A(s.scale), sm_m, sm_l, sm_acc, M, L,
+  attend_rows<T, DH, kAttendWaves>(s, b, hk, q, kc, vc, kn, vn, len, r0, r1, A(s.scale), sm_m, sm_l, sm_acc, M, L,
                                    out_acc);
   A* part = static_cast<A*>(s.partials) + (lane_id * s.max_tiles + tile) * (DH + 2);
   if (threadIdx.x == 0) {
@@ -266,13 +270,15 @@ __global__ __launch_bounds__(64 * kAttendWaves) void attend_chunk_kernel(DevStat
   const int C = s.capacity;
   const int len = min(max(s.len[b], 0), C);
   const size_t lane_id = size_t(b) * s.heads + h;
+  const int hk = h / (s.heads / s.kv_heads);
+  const size_t kv_lane = size_t(b) * s.kv_heads + hk;
   const T* kc = static_cast<const T*>(s.keys);
   const T* vc = static_cast<const T*>(s.values);
-  const T* kn = static_cast<const T*>(s.cand_k) + lane_id * n_max * DH;
-  const T* vn = static_cast<const T*>(s.cand_v) + lane_id * n_max * DH;
+  const T* kn = static_cast<const T*>(s.cand_k) + kv_lane * n_max * DH;
+  const T* vn = static_cast<const T*>(s.cand_v) + kv_lane * n_max * DH;
   const A* q = static_cast<const A*>(s.q) + (lane_id * n_max + i) * DH;
   A M, L;
-  attend_rows<T, DH, kAttendWaves>(s, b, h, q, kc, vc, kn, vn, len, 0, len + i + 1, A(s.scale), sm_m, sm_l, sm_acc,
+  attend_rows<T, DH, kAttendWaves>(s, b, hk, q, kc, vc, kn, vn, len, 0, len + i + 1, A(s.scale), sm_m, sm_l, sm_acc,
                                    M, L, out_acc);
   for (int j = threadIdx.x; j < DH; j += blockDim.x) {
     const A o = out_acc[j] / L;
@@ -284,8 +290,8 @@ __global__ __launch_bounds__(64 * kAttendWaves) void attend_chunk_kernel(DevStat
 
 // --------------------------------------------------------------- commit ----
 
-// Copies candidate rows 64 r .. 64 r + 63 of lane (b, h) (block (r, h, b)) into
-// rows len[b] + i of the cache.
+// Copies candidate rows 64 r .. 64 r + 63 of key/value lane (b, h) (block
+// (r, h, b), h < H_kv) into rows len[b] + i of the cache.
 constexpr int kCommitRows = 64;
 
 template <typename T>
@@ -298,7 +304,7 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max,
   if (r0 >= n_b || len < 0 || len + n_b > C) return;
   const int nr = min(kCommitRows, n_b - r0);
   const int dh = s.head_width;
-  const size_t lane_id = size_t(b) * s.heads + h;
+  const size_t lane_id = size_t(b) * s.kv_heads + h;
   const T* sk = static_cast<const T*>(s.cand_k) + (lane_id * n_max + r0) * dh;
   const T* sv = static_cast<const T*>(s.cand_v) + (lane_id * n_max + r0) * dh;
   T* keys = static_cast<T*>(s.keys);
@@ -340,10 +346,10 @@ __global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
   if (len < 0 || len + 1 > C) return;
   const int dh = s.head_width;
   const size_t row_bytes = size_t(dh) * sizeof(T);
-  const size_t seq_rows = size_t(b) * s.heads;
+  const size_t seq_rows = size_t(b) * s.kv_heads;
   if ((row_bytes & 15) == 0) {
     const int per_row = int(row_bytes / 16);
-    for (int idx = threadIdx.x; idx < s.heads * per_row; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < s.kv_heads * per_row; idx += blockDim.x) {
       const int h = idx / per_row;
       const int c = idx - h * per_row;
       const size_t lane_id = seq_rows + h;
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
           reinterpret_cast<const uint4*>(static_cast<const T*>(s.cand_v) + lane_id * dh)[c];
     }
   } else {
-    for (int idx = threadIdx.x; idx < s.heads * dh; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < s.kv_heads * dh; idx += blockDim.x) {
       const int h = idx / dh;
       const int c = idx - h * dh;
       const size_t lane_id = seq_rows + h;
@@ -451,7 +457,7 @@ __global__ __launch_bounds__(256) void copy_block_rows_kernel(DevState s, int ds
   const int h = blockIdx.y;
   for (int part = 0; part < 2; ++part) {
     char* base = static_cast<char*>(part ? s.values : s.keys);
-    copy_span(base + (size_t(dst) * s.heads + h) * head_bytes, base + (size_t(src) * s.heads + h) * head_bytes,
+    copy_span(base + (size_t(dst) * s.kv_heads + h) * head_bytes, base + (size_t(src) * s.kv_heads + h) * head_bytes,
               size_t(rows) * row_bytes);
   }
 }
@@ -470,7 +476,8 @@ __global__ __launch_bounds__(256) void copy_seq_rows_kernel(DevState s, int dst_
   const int h = blockIdx.y;
   for (int part = 0; part < 2; ++part) {
     char* base = static_cast<char*>(part ? s.values : s.keys);
-    copy_span(base + (size_t(dst_seq) * s.heads + h) * lane_bytes, base + (size_t(src_seq) * s.heads + h) * lane_bytes,
+    copy_span(base + (size_t(dst_seq) * s.kv_heads + h) * lane_bytes,
+              base + (size_t(src_seq) * s.kv_heads + h) * lane_bytes,
               size_t(rows) * row_bytes);
   }
 }
@@ -615,7 +622,7 @@ int commit_t(const DevState& s, int n_max, int per_seq_rows) {
     hipLaunchKernelGGL((commit_decode_kernel<T>), dim3(s.batch), dim3(256), 0, st(s.stream), s);
     return last_launch();
   }
-  hipLaunchKernelGGL((commit_copy_kernel<T>), dim3((n_max + kCommitRows - 1) / kCommitRows, s.heads, s.batch),
+  hipLaunchKernelGGL((commit_copy_kernel<T>), dim3((n_max + kCommitRows - 1) / kCommitRows, s.kv_heads, s.batch),
                      dim3(256), 0, st(s.stream), s, n_max, per_seq_rows);
   int rc = last_launch();
   if (rc) return rc;
@@ -744,7 +751,7 @@ int dev_set_seq_length(const DevState& s, int seq, int32_t value) {
 
 int dev_copy_block_rows(const DevState& s, int dst, int src, int rows) {
   if (rows <= 0) return 0;
-  hipLaunchKernelGGL(copy_block_rows_kernel, dim3(8, s.heads), dim3(256), 0, st(s.stream), s, dst, src, rows,
+  hipLaunchKernelGGL(copy_block_rows_kernel, dim3(8, s.kv_heads), dim3(256), 0, st(s.stream), s, dst, src, rows,
                      elem_bytes(s.dtype));
   return last_launch();
 }
@@ -758,7 +765,7 @@ int dev_copy_positions(const DevState& s, int dst_seq, int src_seq, int rows) {
 
 int dev_copy_seq_rows(const DevState& s, int dst_seq, int src_seq, int rows) {
   if (rows <= 0) return 0;
-  hipLaunchKernelGGL(copy_seq_rows_kernel, dim3(32, s.heads), dim3(256), 0, st(s.stream), s, dst_seq, src_seq, rows,
+  hipLaunchKernelGGL(copy_seq_rows_kernel, dim3(32, s.kv_heads), dim3(256), 0, st(s.stream), s, dst_seq, src_seq, rows,
                      elem_bytes(s.dtype));
   return last_launch();
 }

@@ -22,6 +22,7 @@ using namespace kvc;
 
 struct kvc_params {
   int32_t model_width;
+  int32_t kv_width;      // rows of W_k and W_v: H_kv * d_h (= model_width without grouping)
   kvc_dtype dtype;
   const void* w[4];      // W_q, W_k, W_v, W_o (W_o may be null)
   int32_t nweights;      // 3 without W_o, 4 with it
@@ -32,6 +33,7 @@ struct kvc_params {
 struct kvc_layer {
   const kvc_params* params;
   int32_t heads, head_width;
+  int32_t kv_heads;  // key/value heads; query head h reads key/value head h / (heads / kv_heads)
   kvc_pos_mode pos_mode;
   double rope_base;
   int32_t rope_max_positions;
@@ -52,6 +54,7 @@ struct Profile {
 struct kvc_cache {
   // geometry and binding (Chapter 37, layer-kv-cache listing: the cache struct)
   int32_t batch, heads, head_width, model_width, capacity, max_chunk_rows;
+  int32_t kv_heads;
   kvc_dtype dtype;
   uint64_t params_id;
   uint64_t revision[4];
@@ -183,6 +186,10 @@ kvc_status check_binding(const kvc_layer* layer, const kvc_cache* c) {
   if (c->heads != layer->heads)
     return fail_ea(KVC_ERR_CACHE_HEAD_COUNT_MISMATCH, layer->heads, c->heads,
                    "cache head count %d does not match layer head count %d", c->heads, layer->heads);
+  if (c->kv_heads != layer->kv_heads)
+    return fail_ea(KVC_ERR_CACHE_HEAD_COUNT_MISMATCH, layer->kv_heads, c->kv_heads,
+                   "cache key/value head count %d does not match layer key/value head count %d", c->kv_heads,
+                   layer->kv_heads);
   if (c->head_width != layer->head_width)
     return fail_ea(KVC_ERR_CACHE_HEAD_WIDTH_MISMATCH, layer->head_width, c->head_width,
                    "cache head width %d does not match layer head width %d", c->head_width,
@@ -568,7 +575,9 @@ void choose_decode_tiles(kvc_cache* cache) {
   for (int64_t cand = kDecodeTileRows; cand <= (int64_t(1) << 30); cand *= 2) {
     int64_t blocks = 0;
     for (int b = 0; b < cache->batch; ++b) blocks += (int64_t(cache->len[b]) + cand) / cand;
-    if (blocks * cache->heads < 1024) break;
+    if (blocks * (cache->heads / decode_heads_per_block(cache->dtype, cache->head_width,
+                                                        cache->heads / cache->kv_heads)) < 1024)
+      break;
     tile = int(cand);
     if (cand > max_len) break;
   }
@@ -609,12 +618,13 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
                      pool_blocks);
   }
   const kvc_params* p = layer->params;
-  const int H = layer->heads, dh = layer->head_width;
-  int64_t elements = 0, cand = 0, pos_elems = 0;
-  if (!checked_mul(paged ? pool_blocks : batch, H, &elements) ||
+  const int H = layer->heads, HK = layer->kv_heads, dh = layer->head_width;
+  int64_t elements = 0, cand = 0, qrows = 0, pos_elems = 0;
+  if (!checked_mul(paged ? pool_blocks : batch, HK, &elements) ||
       !checked_mul(elements, paged ? block_rows : capacity, &elements) ||
-      !checked_mul(elements, dh, &elements) || !checked_mul(int64_t(batch) * H, int64_t(max_chunk_rows), &cand) ||
-      !checked_mul(cand, dh, &cand) || !checked_mul(batch, capacity, &pos_elems) ||
+      !checked_mul(elements, dh, &elements) || !checked_mul(int64_t(batch) * HK, int64_t(max_chunk_rows), &cand) ||
+      !checked_mul(cand, dh, &cand) || !checked_mul(int64_t(batch) * H, int64_t(max_chunk_rows), &qrows) ||
+      !checked_mul(qrows, dh, &qrows) || !checked_mul(batch, capacity, &pos_elems) ||
       elements > (INT64_MAX / 16) || cand > (INT64_MAX / 16)) {
     return fail(KVC_ERR_ELEMENT_COUNT_OVERFLOW,
                 "KV cache element count overflows for batch %d, %d heads, capacity %d, and head width %d", batch,
@@ -624,6 +634,7 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
   if (!c) return fail(KVC_ERR_ALLOCATION_FAILED, "host allocation failed");
   c->batch = batch;
   c->heads = H;
+  c->kv_heads = HK;
   c->head_width = dh;
   c->model_width = p->model_width;
   c->capacity = capacity;
@@ -662,8 +673,10 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
   s.dtype = p->dtype;
   s.batch = batch;
   s.heads = H;
+  s.kv_heads = HK;
   s.head_width = dh;
   s.model_width = p->model_width;
+  s.kv_width = p->kv_width;
   s.capacity = capacity;
   s.max_chunk_rows = max_chunk_rows;
   s.rope = layer->pos_mode == KVC_POS_ROPE;
@@ -692,10 +705,10 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
       {reinterpret_cast<void**>(&s.rows), round16(sizeof(int32_t) * batch)},
       {&s.cand_k, round16(size_t(cand) * es)},
       {&s.cand_v, round16(size_t(cand) * es)},
-      {&s.q, round16(size_t(cand) * as)},
+      {&s.q, round16(size_t(qrows) * as)},
       {&s.partials, round16(size_t(batch) * H * max_tiles * (dh + 2) * as)},
       {reinterpret_cast<void**>(&s.err), shared_err ? 0 : round16(sizeof(ErrWords))},
-      {&s.merged, p->w[3] ? round16(size_t(cand) * as) : 0},  // [B, max_chunk_rows, D]
+      {&s.merged, p->w[3] ? round16(size_t(qrows) * as) : 0},  // [B, max_chunk_rows, D]
       {reinterpret_cast<void**>(const_cast<int32_t**>(&s.block_table)),
        paged ? round16(sizeof(int32_t) * c->table.size()) : 0},
   };
@@ -989,15 +1002,24 @@ const kvc_error_detail* kvc_last_error(void) { return &g_last; }
 
 kvc_status kvc_params_create(int32_t model_width, kvc_dtype dtype, const void* w_q, const void* w_k,
                              const void* w_v, const void* w_o, kvc_params** out) {
+  return kvc_params_create_grouped(model_width, model_width, dtype, w_q, w_k, w_v, w_o, out);
+}
+
+kvc_status kvc_params_create_grouped(int32_t model_width, int32_t kv_width, kvc_dtype dtype, const void* w_q,
+                                     const void* w_k, const void* w_v, const void* w_o, kvc_params** out) {
   reset_detail();
   if (!out || !w_q || !w_k || !w_v) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_params_create");
   *out = nullptr;
   if (model_width <= 0) return fail(KVC_ERR_BAD_ARGUMENT, "model width must be positive, got %d", model_width);
+  if (kv_width <= 0 || model_width % kv_width != 0)
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, model_width, kv_width,
+                   "key/value width %d must be positive and divide the model width %d", kv_width, model_width);
   if (dtype != KVC_F64 && dtype != KVC_F32 && dtype != KVC_BF16)
     return fail(KVC_ERR_DTYPE_UNSUPPORTED, "unsupported weight type %d", int(dtype));
   kvc_params* p = new (std::nothrow) kvc_params;
   if (!p) return fail(KVC_ERR_ALLOCATION_FAILED, "host allocation failed");
   p->model_width = model_width;
+  p->kv_width = kv_width;
   p->dtype = dtype;
   p->w[0] = w_q;
   p->w[1] = w_k;
@@ -1037,10 +1059,15 @@ kvc_status kvc_layer_create(const kvc_params* params, int32_t heads, kvc_pos_mod
   if (dh < 2 || !is_pow2(dh) || dh > max_head_width(params->dtype))
     return fail(KVC_ERR_SHAPE_UNSUPPORTED, "head width %d must be a power of two in [2, %d] for this type", dh,
                 max_head_width(params->dtype));
+  if (params->kv_width % dh != 0 || heads % (params->kv_width / dh) != 0)
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, dh, params->kv_width,
+                   "key/value width %d must be a whole number of %d-wide heads that divides the %d query heads",
+                   params->kv_width, dh, heads);
   kvc_layer* l = new (std::nothrow) kvc_layer;
   if (!l) return fail(KVC_ERR_ALLOCATION_FAILED, "host allocation failed");
   l->params = params;
   l->heads = heads;
+  l->kv_heads = params->kv_width / dh;
   l->head_width = dh;
   l->pos_mode = pos_mode;
   l->rope_base = rope_base;
@@ -1350,15 +1377,15 @@ kvc_status kvc_snapshot(kvc_cache* cache, int32_t seq, void* keys_out, void* val
     for (int j = 0; j < blocks_for(cache, len) && rc == 0; ++j) {
       const int blk = cache->table[seq * cache->table_width + j];
       const int r0 = j * cache->block_rows, nr = std::min(len - r0, cache->block_rows);
-      const size_t src_off = size_t(blk) * cache->heads * head_bytes;
+      const size_t src_off = size_t(blk) * cache->kv_heads * head_bytes;
       if (keys_out)
         rc = dev_copy_d2h_2d_sync(static_cast<char*>(keys_out) + r0 * row_bytes, size_t(len) * row_bytes,
                                   static_cast<char*>(cache->ds.keys) + src_off, head_bytes, nr * row_bytes,
-                                  cache->heads, cache->ds.stream);
+                                  cache->kv_heads, cache->ds.stream);
       if (rc == 0 && values_out)
         rc = dev_copy_d2h_2d_sync(static_cast<char*>(values_out) + r0 * row_bytes, size_t(len) * row_bytes,
                                   static_cast<char*>(cache->ds.values) + src_off, head_bytes, nr * row_bytes,
-                                  cache->heads, cache->ds.stream);
+                                  cache->kv_heads, cache->ds.stream);
     }
     if (rc == 0 && positions_out && len > 0)
       rc = dev_copy_d2h_sync(positions_out, cache->ds.positions + size_t(seq) * cache->capacity,
@@ -1367,14 +1394,14 @@ kvc_status kvc_snapshot(kvc_cache* cache, int32_t seq, void* keys_out, void* val
     return KVC_OK;
   }
   const size_t lane_bytes = size_t(cache->capacity) * row_bytes;
-  const size_t seq_off = size_t(seq) * cache->heads * lane_bytes;
+  const size_t seq_off = size_t(seq) * cache->kv_heads * lane_bytes;
   // [H, len, d_h] out of [H, C, d_h]: one strided copy per buffer.
   if (keys_out)
     rc = dev_copy_d2h_2d_sync(keys_out, size_t(len) * row_bytes, static_cast<char*>(cache->ds.keys) + seq_off,
-                              lane_bytes, size_t(len) * row_bytes, cache->heads, cache->ds.stream);
+                              lane_bytes, size_t(len) * row_bytes, cache->kv_heads, cache->ds.stream);
   if (rc == 0 && values_out)
     rc = dev_copy_d2h_2d_sync(values_out, size_t(len) * row_bytes, static_cast<char*>(cache->ds.values) + seq_off,
-                              lane_bytes, size_t(len) * row_bytes, cache->heads, cache->ds.stream);
+                              lane_bytes, size_t(len) * row_bytes, cache->kv_heads, cache->ds.stream);
   if (rc == 0 && positions_out && len > 0)
     rc = dev_copy_d2h_sync(positions_out, cache->ds.positions + size_t(seq) * cache->capacity,
                            sizeof(int32_t) * size_t(len), cache->ds.stream);
@@ -1401,6 +1428,7 @@ kvc_status kvc_cache_describe(const kvc_cache* cache, kvc_cache_desc* out) {
   if (!cache || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_cache_describe");
   out->batch = cache->batch;
   out->heads = cache->heads;
+  out->kv_heads = cache->kv_heads;
   out->head_width = cache->head_width;
   out->model_width = cache->model_width;
   out->capacity = cache->capacity;

@@ -30,6 +30,15 @@ constexpr int kDecodeTileRows = 512;
 // Smallest rows per block of a paged cache: every run of rows a kernel reads
 // through one block base (a decode step, a 64-row chunk-attention tile) fits.
 constexpr int kMinBlockRows = 256;
+// Query heads that one bf16 decode workgroup serves from a single read of
+// their shared key/value head: the largest power of two <= 8 dividing the
+// group size heads / kv_heads (1 for the generic kernels).
+inline int decode_heads_per_block(int dtype, int head_width, int group) {
+  if (dtype != KVC_BF16 || (head_width != 64 && head_width != 128)) return 1;
+  int q = 1;
+  while (q < 8 && group % (2 * q) == 0) q *= 2;
+  return q;
+}
 // Values per by-value length update (kernel-argument payload).
 constexpr int kSetChunk = 480;
 
@@ -37,6 +46,8 @@ constexpr int kSetChunk = 480;
 struct DevState {
   int dtype;  // kvc_dtype of storage and weights
   int batch, heads, head_width, model_width, capacity, max_chunk_rows;
+  int kv_heads;  // key/value heads H_kv (divides heads); query head h reads h / (heads / kv_heads)
+  int kv_width;  // H_kv * d_h: rows of W_k and W_v
   int rope;           // 1: rotate q, k
   int max_positions;  // rotary table rows
   double scale;       // 1 / sqrt(d_h)
@@ -44,14 +55,14 @@ struct DevState {
   const void* wk;
   const void* wv;
   const void* wo;      // output projection, or null
-  void* keys;          // [B, H, C, d_h] storage type
-  void* values;        // [B, H, C, d_h]
+  void* keys;          // [B, H_kv, C, d_h] storage type
+  void* values;        // [B, H_kv, C, d_h]
   int32_t* len;        // [B] committed rows
   int32_t* next_pos;   // [B] position of the next row
   int32_t* positions;  // [B, C] absolute position of each row
   int32_t* rows;       // [B] rows of the current chunk call
-  void* cand_k;        // [B, H, n, d_h] storage type (n = rows of the call)
-  void* cand_v;        // [B, H, n, d_h]
+  void* cand_k;        // [B, H_kv, n, d_h] storage type (n = rows of the call)
+  void* cand_v;        // [B, H_kv, n, d_h]
   void* q;             // [B, H, n, d_h] accumulate type
   void* merged;        // [B, n, D] accumulate type: merged heads before W_o (null without W_o)
   void* out_proj_dst;  // [B, n, D] accumulate type: destination of the W_o projection (per call)
@@ -62,7 +73,7 @@ struct DevState {
   void* rope_cos;  // [max_positions, d_h / 2] accumulate type (null without rotation)
   void* rope_sin;
   // Block-paged storage (paged = 1): keys and values are pools
-  // [blocks, H, block_rows, d_h] and row r of sequence b lives in block
+  // [blocks, H_kv, block_rows, d_h] and row r of sequence b lives in block
   // block_table[b * table_width + (r >> block_rows_log2)] (capacity =
   // table_width << block_rows_log2).  paged = 0: [B, H, C, d_h].
   int paged;

@@ -34,6 +34,23 @@ __device__ __forceinline__ const bf16_t* weight_of(const DevState& s, int p) {
   return static_cast<const bf16_t*>(p == 0 ? s.wq : (p == 1 ? s.wk : (p == 2 ? s.wv : s.wo)));
 }
 
+// Heads of projection p: W_k and W_v may project to fewer (grouped) heads.
+__device__ __forceinline__ int heads_of(const DevState& s, int p) { return (p == 1 || p == 2) ? s.kv_heads : s.heads; }
+
+// Column tile t (tiles of `cols` output columns) of a launch over projections
+// proj_first, proj_first + 1, ...: returns the projection and leaves in t the
+// tile's index within it.
+__device__ __forceinline__ int tile_proj(const DevState& s, int proj_first, int cols, int& t) {
+  int p = proj_first;
+  while (p < 3) {
+    const int n = heads_of(s, p) * s.head_width / cols;
+    if (t < n) break;
+    t -= n;
+    ++p;
+  }
+  return p;
+}
+
 // 16 input elements starting at p as two bf16x8 pieces (float input is rounded).
 __device__ __forceinline__ void load16(const bf16_t* p, uint4& lo, uint4& hi) {
   lo = reinterpret_cast<const uint4*>(p)[0];
@@ -109,7 +126,7 @@ __device__ __forceinline__ void put_pair(const DevState& s, int p, const RowDst&
     r0 = lo * c - hi * sn;
     r1 = hi * c + lo * sn;
   }
-  const size_t flat0 = (size_t(d.b * s.heads + h) * n_max + d.i) * dh + f;
+  const size_t flat0 = (size_t(d.b * heads_of(s, p) + h) * n_max + d.i) * dh + f;
   const size_t flat1 = flat0 + half;
   if (p == 0) {
     float* q = static_cast<float*>(s.q);
@@ -169,7 +186,7 @@ __device__ __forceinline__ void put_pairs4(const DevState& s, int p, const RowDs
     r1 = make_float4(hi.x * c.x + lo.x * sn.x, hi.y * c.y + lo.y * sn.y, hi.z * c.z + lo.z * sn.z,
                      hi.w * c.w + lo.w * sn.w);
   }
-  const size_t flat0 = (size_t(d.b * s.heads + h) * n_max + d.i) * dh + f;
+  const size_t flat0 = (size_t(d.b * heads_of(s, p) + h) * n_max + d.i) * dh + f;
   if (p == 0) {
     float* q = static_cast<float*>(s.q) + flat0;
     *reinterpret_cast<float4*>(q) = r0;
@@ -231,10 +248,9 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const X
   __shared__ __attribute__((aligned(16))) bf16_t Xs[2][32 * SLDX];
   const int D = s.model_width;
   const int half = s.head_width >> 1;
-  const int tiles_per_proj = D / 64;
-  const int pt = blockIdx.x / tiles_per_proj;
-  const int p = proj_first + pt;
-  const int pair_base = (blockIdx.x - pt * tiles_per_proj) * 32;
+  int tile = blockIdx.x;
+  const int p = tile_proj(s, proj_first, 64, tile);
+  const int pair_base = tile * 32;
   const int m0 = blockIdx.y * 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -335,10 +351,9 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT
   const int D = s.model_width;
   const int dh = s.head_width;
   const int half = dh >> 1;
-  const int tiles_per_proj = D / TBN;  // (D/2 pairs) / 64
-  const int pt = blockIdx.x / tiles_per_proj;
-  const int p = proj_first + pt;
-  const int pair_base = (blockIdx.x - pt * tiles_per_proj) * 64;
+  int tile = blockIdx.x;
+  const int p = tile_proj(s, proj_first, TBN, tile);  // 64 pairs per tile
+  const int pair_base = tile * 64;
   const int m0 = blockIdx.y * TBM;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -449,10 +464,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int rows_in_group = min(GGROUP, m_tiles - group * GGROUP);
   const int mt = group * GGROUP + within % rows_in_group;
   const int nt = within / rows_in_group;
-  const int blocks_per_proj = D / GBN;  // 128 pairs per block
-  const int pt = nt / blocks_per_proj;
-  const int p = proj_first + pt;
-  const int pair_base = (nt - pt * blocks_per_proj) * 128;
+  int ntp = nt;
+  const int p = tile_proj(s, proj_first, GBN, ntp);  // 128 pairs per tile
+  const int pair_base = ntp * 128;
   const int m0 = mt * GBM;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -664,7 +678,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   const int H = s.heads;
   const int item = blockIdx.x / H;
-  const int h = blockIdx.x - item * H;
+  const int slot = blockIdx.x - item * H;
+  // grouped layers: the query heads of one key/value head run on one XCD
+  // (blocks are dealt to the eight XCDs in turn), so their shared K/V tiles
+  // are fetched into one L2
+  const int h = (s.kv_heads < H && (H & 7) == 0) ? (slot & 7) * (H >> 3) + (slot >> 3) : slot;
   int b, qt;
   if (order.count) {
     b = order.item[item] >> 16;
@@ -689,10 +707,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int total = len + i_max + 1;
   const int ntiles = (total + KT - 1) / KT;
   const size_t lane_id = size_t(b) * H + h;
+  const int hk = h / (H / s.kv_heads);  // the key/value head this query head reads
+  const size_t kv_lane = size_t(b) * s.kv_heads + hk;
   const bf16_t* kc = static_cast<const bf16_t*>(s.keys);  // rows through kv_block_base / kv_offset
   const bf16_t* vc = static_cast<const bf16_t*>(s.values);
-  const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + lane_id * n_max * DH;
-  const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + lane_id * n_max * DH;
+  const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + kv_lane * n_max * DH;
+  const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + kv_lane * n_max * DH;
 
   // B operand of S^T: lane holds q[qi][16 u + 8 g + e] * scale * log2(e), rounded
   // to bf16, so scores come out of the MFMA already in base-2 softmax units.
@@ -732,7 +752,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bool cached = j0 + KT <= len;
     const size_t r0 = size_t(cached ? j0 : j0 - len) + lrow;
     // a 64-row tile lies in one block of a paged cache
-    const ptrdiff_t tile_base = cached ? kv_block_base(s, b, h, j0) : 0;
+    const ptrdiff_t tile_base = cached ? kv_block_base(s, b, hk, j0) : 0;
     const uint4* kp = reinterpret_cast<const uint4*>((cached ? kc + tile_base : kn) + r0 * DH + lch * 8);
     const uint4* vp = reinterpret_cast<const uint4*>((cached ? vc + tile_base : vn) + r0 * DH + lch * 8);
     constexpr int STRIDE = RPI * DH / 8;  // uint4 between a thread's pieces
@@ -768,7 +788,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int k = 0; k < PIECES; ++k) {
       const int j = min(j0 + lrow + k * RPI, total - 1);
-      const size_t off = (j < len ? kv_offset(s, b, h, j) : size_t(j - len) * DH) + lch * 8;
+      const size_t off = (j < len ? kv_offset(s, b, hk, j) : size_t(j - len) * DH) + lch * 8;
       const uint4 kk = *reinterpret_cast<const uint4*>((j < len ? kc : kn) + off);
       const uint4 vv = *reinterpret_cast<const uint4*>((j < len ? vc : vn) + off);
       *reinterpret_cast<uint4*>(&Ks[buf][(lrow + k * RPI) * LDK + lch * 8]) = kk;
@@ -903,8 +923,12 @@ template <typename XT>
 int mfma_project_t(const DevState& s, const XT* xb, int n_max, int per_seq_rows, int proj_first, int nproj) {
   if (s.dtype != KVC_BF16 || s.model_width % 128 != 0) return -1;
   const int M = s.batch * n_max;
+  // output columns of the launch: Q, K, V (K and V kv_width wide) or O
+  const int cols = nproj == 3 ? s.model_width + 2 * s.kv_width : s.model_width;
+  const int kv_cols = nproj == 3 ? s.kv_width : s.model_width;
   if (M <= 64) {
-    dim3 grid(nproj * (s.model_width / 64), (M + 31) / 32);
+    if (kv_cols % 64 != 0) return -1;
+    dim3 grid(cols / 64, (M + 31) / 32);
     switch (s.model_width) {
       case 2048:
         hipLaunchKernelGGL((project_skinny_kernel<16, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
@@ -922,14 +946,15 @@ int mfma_project_t(const DevState& s, const XT* xb, int n_max, int per_seq_rows,
         hipLaunchKernelGGL((project_skinny_kernel<0, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
                            per_seq_rows, proj_first);
     }
-  } else if (std::is_same<XT, bf16_t>::value && M >= 2048 && s.model_width % GBN == 0 && s.head_width % 64 == 0 &&
-             int64_t(M) * s.model_width < (int64_t(1) << 31)) {
+  } else if (std::is_same<XT, bf16_t>::value && M >= 2048 && s.model_width % GBN == 0 && kv_cols % GBN == 0 &&
+             s.head_width % 64 == 0 && int64_t(M) * s.model_width < (int64_t(1) << 31)) {
     const int m_tiles = (M + GBM - 1) / GBM;
-    const int n_tiles = nproj * (s.model_width / GBN);
+    const int n_tiles = cols / GBN;
     hipLaunchKernelGGL(project_wide_kernel, dim3(m_tiles * n_tiles), dim3(256), 0, st(s.stream), s,
                        reinterpret_cast<const bf16_t*>(xb), M, n_max, per_seq_rows, proj_first, m_tiles, n_tiles);
   } else {
-    dim3 grid(nproj * (s.model_width / TBN), (M + TBM - 1) / TBM);
+    if (kv_cols % TBN != 0) return -1;
+    dim3 grid(cols / TBN, (M + TBM - 1) / TBM);
     hipLaunchKernelGGL((project_tiled_kernel<XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
                        per_seq_rows, proj_first);
   }

@@ -137,6 +137,28 @@ def kvc_params_create(w_q, w_k, w_v, w_o=None, *, lib=None) -> Params:
     return h
 
 
+def kvc_params_create_grouped(w_q, w_k, w_v, w_o=None, *, lib=None) -> Params:
+    """Grouped key/value heads: W_q (and W_o) [D, D], W_k and W_v [kv_width, D]
+    (contiguous device tensors, one dtype); kv_width = H_kv * d_h."""
+    lib = _lib(lib)
+    code = _dtype_code(w_q)
+    ws = (w_q, w_k, w_v) + ((w_o,) if w_o is not None else ())
+    if any(_dtype_code(w) != code or w.dim() != 2 for w in ws):
+        raise TypeError("weights must be matrices of one dtype")
+    d, kvw = int(w_q.shape[0]), int(w_k.shape[0])
+    if tuple(w_q.shape) != (d, d) or tuple(w_k.shape) != (kvw, d) or tuple(w_v.shape) != (kvw, d) or (
+            w_o is not None and tuple(w_o.shape) != (d, d)):
+        raise ValueError("W_q and W_o must be [D, D], W_k and W_v [kv_width, D]")
+    out = C.c_void_p()
+    _check(lib, lib.kvc_params_create_grouped(d, kvw, code, _dev_ptr(w_q), _dev_ptr(w_k), _dev_ptr(w_v),
+                                              _dev_ptr(w_o) if w_o is not None else None, C.byref(out)))
+    h = Params(lib, out)
+    h.tensors = ws
+    h.dtype_code = code
+    h.model_width = d
+    return h
+
+
 def kvc_params_mark_updated(params: Params, which: int = -1) -> None:
     _check(params._lib, params._lib.kvc_params_mark_updated(params.ptr, which))
 
@@ -272,13 +294,13 @@ _NP_STORAGE = {KVC_F64: np.float64, KVC_F32: np.float32, KVC_BF16: np.uint16}
 
 
 def kvc_snapshot(cache: Cache, seq: int):
-    """Logical rows of sequence ``seq``: keys, values [H, len, d_h] in the storage
+    """Logical rows of sequence ``seq``: keys, values [H_kv, len, d_h] in the storage
     type (bf16 as uint16 bit patterns) and positions [len]."""
     lib = cache._lib
     rows = C.c_int32()
     _check(lib, lib.kvc_snapshot(cache.ptr, seq, None, None, None, 0, C.byref(rows)))
     n = rows.value
-    h, dh = cache.desc["heads"], cache.desc["head_width"]
+    h, dh = cache.desc["kv_heads"], cache.desc["head_width"]
     dt = _NP_STORAGE[cache.desc["kv_dtype"]]
     k = np.zeros((h, n, dh), dt)
     v = np.zeros((h, n, dh), dt)

@@ -152,6 +152,13 @@ def decode_weights(seed: int, model_width: int, std: float, dtype: str):
     return out
 
 
+def grouped_weights(seed: int, model_width: int, kv_width: int, std: float, dtype: str):
+    """W_q [D, D] and W_k, W_v [kv_width, D] ([D_out, D_in]): (storage, float64 value) pairs."""
+    shapes = ((model_width, model_width), (kv_width, model_width), (kv_width, model_width))
+    return [quantize(normal(seed, stream, shape, std=std), dtype)
+            for stream, shape in zip((STREAM_WQ, STREAM_WK, STREAM_WV), shapes)]
+
+
 def hidden_rows(seed: int, stream: int, seq: int, first_row: int, rows: int,
                 model_width: int, row_stride: int) -> np.ndarray:
     """float64 N(0,1) hidden rows ``first_row .. first_row+rows-1`` of sequence ``seq``.

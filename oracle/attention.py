@@ -165,14 +165,15 @@ def causal_layer(x_rows, wq, wk, wv, heads: int, base: float = 10000.0,
     }
 
 
-def full_prefix_decode(x_rows, wq, wk, wv, heads: int, base: float = 10000.0, rope: bool = True, wo=None):
+def full_prefix_decode(x_rows, wq, wk, wv, heads: int, base: float = 10000.0, rope: bool = True, wo=None,
+                       kv_heads=None):
     """Output of the newest row t-1 of a t-row prefix, recomputed from scratch.
 
     Equivalent to ``causal_layer(...)`` restricted to the last row; returns the
     same dict (``out`` [D], ``weights`` [H, t]).
     """
     n = np.asarray(x_rows).shape[0]
-    r = causal_layer(x_rows, wq, wk, wv, heads, base, rope, rows=[n - 1], wo=wo)
+    r = causal_layer(x_rows, wq, wk, wv, heads, base, rope, rows=[n - 1], wo=wo, kv_heads=kv_heads)
     r["out"] = r["out"][0]
     r["weights"] = r["weights"][0]
     return r
@@ -188,7 +189,8 @@ def full_prefix_decode(x_rows, wq, wk, wv, heads: int, base: float = 10000.0, ro
 class DecodeCache:
     """A one-sequence, one-layer cache as Chapter 37 describes it.
 
-    Fixed capacity, rotated keys and unrotated values stored [H, C, d_h], a
+    Fixed capacity, rotated keys and unrotated values stored [H, C, d_h] (H: the
+    layer's key/value heads), a
     logical length, and (prefix-reuse note, "What must be trimmed together")
     the absolute position of every row plus ``next_position``.
     """
@@ -207,25 +209,29 @@ class DecodeCache:
 
 
 def incremental_step(cache: DecodeCache, x_row, wq, wk, wv, heads: int,
-                     base: float = 10000.0, rope: bool = True):
+                     base: float = 10000.0, rope: bool = True, kv_heads=None):
     """One checked append-and-attend step (Chapter 37, "Bind the state, calculate
     completely, then commit").
 
     Projects only the new row, rotates q and k at ``cache.next_position`` (the
     old logical length unless a caller broke that invariant), scores the new
     query against the retained rows plus its own candidate row, mixes values,
-    and only then appends the candidate pair and advances the length.
+    and only then appends the candidate pair and advances the length.  With
+    ``kv_heads`` the cache holds H_kv heads and query head h reads h // (H / H_kv).
     Returns (output [D], weights [H, len+1], work dict).
     """
     if cache.len == cache.capacity:
         raise OverflowError("cache is full")
+    kv_heads = heads if kv_heads is None else kv_heads
+    group = heads // kv_heads
     pos = cache.next_position
-    q, k, v = layer_projections(np.asarray(x_row, F64)[None], wq, wk, wv, heads, [pos], base, rope)
+    q, k, v = layer_projections(np.asarray(x_row, F64)[None], wq, wk, wv, heads, [pos], base, rope, kv_heads)
     q, k, v = q[0], k[0], v[0]
     outs, ws = [], []
     for h in range(heads):
-        keys = np.concatenate([cache.keys[h, : cache.len], k[h][None]])
-        vals = np.concatenate([cache.values[h, : cache.len], v[h][None]])
+        j = h // group
+        keys = np.concatenate([cache.keys[j, : cache.len], k[j][None]])
+        vals = np.concatenate([cache.values[j, : cache.len], v[j][None]])
         o, w = attend(q[h], keys, vals)
         outs.append(o)
         ws.append(w)

@@ -92,10 +92,10 @@ int dev_set_seq_length(const DevState& s, int seq, int32_t value) {
 int dev_copy_block_rows(const DevState& s, int dst, int src, int rows) {
   if (gate_closed(s) || rows <= 0) return 0;
   const size_t row = size_t(s.head_width) * elem_bytes(s.dtype), head = row << s.block_rows_log2;
-  for (int h = 0; h < s.heads; ++h)
+  for (int h = 0; h < s.kv_heads; ++h)
     for (void* base : {s.keys, s.values})
-      std::memcpy(static_cast<char*>(base) + (size_t(dst) * s.heads + h) * head,
-                  static_cast<char*>(base) + (size_t(src) * s.heads + h) * head, size_t(rows) * row);
+      std::memcpy(static_cast<char*>(base) + (size_t(dst) * s.kv_heads + h) * head,
+                  static_cast<char*>(base) + (size_t(src) * s.kv_heads + h) * head, size_t(rows) * row);
   return 0;
 }
 int dev_copy_positions(const DevState& s, int dst_seq, int src_seq, int rows) {
@@ -107,10 +107,10 @@ int dev_copy_positions(const DevState& s, int dst_seq, int src_seq, int rows) {
 int dev_copy_seq_rows(const DevState& s, int dst_seq, int src_seq, int rows) {
   if (gate_closed(s) || rows <= 0) return 0;
   const size_t row = size_t(s.head_width) * elem_bytes(s.dtype), lane = row * s.capacity;
-  for (int h = 0; h < s.heads; ++h)
+  for (int h = 0; h < s.kv_heads; ++h)
     for (void* base : {s.keys, s.values})
-      std::memcpy(static_cast<char*>(base) + (size_t(dst_seq) * s.heads + h) * lane,
-                  static_cast<char*>(base) + (size_t(src_seq) * s.heads + h) * lane, size_t(rows) * row);
+      std::memcpy(static_cast<char*>(base) + (size_t(dst_seq) * s.kv_heads + h) * lane,
+                  static_cast<char*>(base) + (size_t(src_seq) * s.kv_heads + h) * lane, size_t(rows) * row);
   return 0;
 }
 // Fake kernels (off by default; kvc_test_fake_kernels turns them on): no
@@ -123,20 +123,20 @@ static bool g_fake = false;
 static int g_call = 0;
 static long long g_fail_next = -1;
 static size_t kv_off(const DevState& s, int b, int h, int r) {
-  if (!s.paged) return ((size_t(b) * s.heads + h) * s.capacity + r) * s.head_width;
+  if (!s.paged) return ((size_t(b) * s.kv_heads + h) * s.capacity + r) * s.head_width;
   const int lg = s.block_rows_log2;
   const int blk = s.block_table[size_t(b) * s.table_width + (r >> lg)];
-  return (((size_t(blk) * s.heads + h) << lg) + (r & ((1 << lg) - 1))) * s.head_width;
+  return (((size_t(blk) * s.kv_heads + h) << lg) + (r & ((1 << lg) - 1))) * s.head_width;
 }
 int dev_project(const DevState& s, const void*, int n_max, int per_seq) {
   if (!g_fake) return 1;
   ++g_call;
   for (int b = 0; b < s.batch; ++b) {
     const int n = per_seq ? s.rows[b] : n_max;
-    for (int h = 0; h < s.heads; ++h)
+    for (int h = 0; h < s.kv_heads; ++h)
       for (int i = 0; i < n; ++i)
         for (int e = 0; e < s.head_width; ++e) {
-          const size_t at = ((size_t(b) * s.heads + h) * n_max + i) * s.head_width + e;
+          const size_t at = ((size_t(b) * s.kv_heads + h) * n_max + i) * s.head_width + e;
           const double tag = g_call * 1e6 + b * 1e4 + i * 1e2 + h * 10 + e;
           static_cast<double*>(s.cand_k)[at] = tag;
           static_cast<double*>(s.cand_v)[at] = -tag;
@@ -159,8 +159,8 @@ int dev_commit(const DevState& s, int n_max, int per_seq) {
     const int n = per_seq ? s.rows[b] : n_max;
     for (int i = 0; i < n; ++i) {
       const int r = s.len[b] + i;
-      for (int h = 0; h < s.heads; ++h) {
-        const size_t src = ((size_t(b) * s.heads + h) * n_max + i) * s.head_width;
+      for (int h = 0; h < s.kv_heads; ++h) {
+        const size_t src = ((size_t(b) * s.kv_heads + h) * n_max + i) * s.head_width;
         const size_t dst = kv_off(s, b, h, r);
         for (int e = 0; e < s.head_width; ++e) {
           static_cast<double*>(s.keys)[dst + e] = static_cast<const double*>(s.cand_k)[src + e];

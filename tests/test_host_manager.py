@@ -377,3 +377,48 @@ def test_session_request_checks(lib):
     assert lib.kvc_session_truncate(s, cut.ctypes.data_as(capi.PI32), 0) == 0
     assert lib.kvc_session_reset(s) == 0
     lib.kvc_session_destroy(s)
+
+
+def test_grouped_parameters_layers_and_caches(lib):
+    """Grouped key/value heads (Chapter 37, "From causal attention to managed LLM
+    inference state": multi-query attention against the K/V reload bottleneck):
+    W_k / W_v are [kv_width, D]; the layer has kv_width / d_h key/value heads,
+    which must divide the query heads; the cache keeps [B, H_kv, C, d_h]; a
+    layer with another key/value head count does not bind to the cache."""
+    p = C.c_void_p()
+    assert lib.kvc_params_create_grouped(8, 3, capi.KVC_F64, DUMMY, DUMMY, DUMMY, None, C.byref(p)) == \
+        capi.KVC_ERR_BAD_ARGUMENT  # 3 does not divide 8
+    assert lib.kvc_params_create_grouped(8, 0, capi.KVC_F64, DUMMY, DUMMY, DUMMY, None, C.byref(p)) == \
+        capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_params_create_grouped(8, 4, capi.KVC_F64, DUMMY, DUMMY, DUMMY, None, C.byref(p)) == 0
+    l = C.c_void_p()
+    # 4 heads of width 2: 2 key/value heads
+    assert lib.kvc_layer_create(p, 4, capi.KVC_POS_ROPE, 10000.0, 8, C.byref(l)) == 0
+    # 1 head of width 8: the key/value width 4 is not a whole head
+    bad = C.c_void_p()
+    assert lib.kvc_layer_create(p, 1, capi.KVC_POS_ROPE, 10000.0, 8, C.byref(bad)) == capi.KVC_ERR_BAD_ARGUMENT
+    p6 = C.c_void_p()
+    assert lib.kvc_params_create_grouped(12, 6, capi.KVC_F64, DUMMY, DUMMY, DUMMY, None, C.byref(p6)) == 0
+    # 3 heads of width 4 cannot share 6 / 4 heads; 6 heads of width 2 share 3 key/value heads
+    assert lib.kvc_layer_create(p6, 3, capi.KVC_POS_ROPE, 10000.0, 8, C.byref(bad)) == capi.KVC_ERR_BAD_ARGUMENT
+    c = cache(lib, l, batch=3, cap=4, chunk=2)
+    d = capi.CacheDesc()
+    assert lib.kvc_cache_describe(c, C.byref(d)) == 0
+    assert (d.heads, d.kv_heads, d.head_width) == (4, 2, 2)
+    *_, kb, vb = state(lib, c, 3)
+    assert len(kb) == 3 * 2 * 4 * 2 * 8  # [B, H_kv, C, d_h] float64
+    n = C.c_int32()
+    assert lib.kvc_snapshot(c, 0, None, None, None, 0, C.byref(n)) == 0 and n.value == 0
+    # the same query heads over the full key/value width: the head check comes first
+    full = layer(lib, params(lib, d=8), heads=4, max_pos=8)
+    assert append(lib, full, c, (3, 1, 8)) == capi.KVC_ERR_CACHE_HEAD_COUNT_MISMATCH
+    e = lib.kvc_last_error().contents
+    assert (e.expected, e.actual) == (4, 2)
+    pf = params(lib, d=8)
+    lf = layer(lib, pf, heads=4, max_pos=8)
+    cf = cache(lib, lf, batch=3, cap=4)
+    assert append(lib, l, cf, (3, 1, 8)) == capi.KVC_ERR_CACHE_HEAD_COUNT_MISMATCH
+    e = lib.kvc_last_error().contents
+    assert (e.expected, e.actual) == (2, 4)
+    for h in (c, cf):
+        lib.kvc_cache_destroy(h)

@@ -221,6 +221,26 @@ def test_grouped_heads_equal_multi_head_with_shared_weights(heads, kv_heads):
         assert np.max(np.abs(other - A.causal_layer(x, wq, wk, wv, heads=heads, kv_heads=kv_heads)["out"])) > 1e-3
 
 
+def test_grouped_incremental_steps_equal_full_prefix():
+    """Cached decode with grouped key/value heads (Chapter 37, "Bind the state,
+    calculate completely, then commit" over a cache of H_kv heads) equals the
+    grouped full-prefix recompute at every step."""
+    heads, kv_heads, dh, L = 6, 2, 4, 6
+    D = heads * dh
+    x = synth.normal(12, 2, (L, D))
+    wq = synth.normal(12, 3, (D, D), std=D ** -0.5)
+    wk = synth.normal(12, 4, (kv_heads * dh, D), std=D ** -0.5)
+    wv = synth.normal(12, 5, (kv_heads * dh, D), std=D ** -0.5)
+    cache = A.DecodeCache(kv_heads, dh, L)
+    for p in range(L):
+        out, w, _ = A.incremental_step(cache, x[p], wq, wk, wv, heads=heads, kv_heads=kv_heads)
+        ref = A.full_prefix_decode(x[: p + 1], wq, wk, wv, heads=heads, kv_heads=kv_heads)
+        np.testing.assert_allclose(out, ref["out"], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(w, ref["weights"], rtol=0, atol=1e-13)
+    full = A.causal_layer(x, wq, wk, wv, heads=heads, kv_heads=kv_heads, rows=[])
+    np.testing.assert_allclose(cache.keys, full["keys"], rtol=0, atol=1e-13)
+
+
 def test_multi_query_single_row_returns_the_shared_value():
     """H_kv = 1 (Shazeer's multi-query form) with one row: every query head's weight
     on the single key is 1, so every head block of the output is the one shared
