@@ -27,6 +27,10 @@ Readings taken where the pages leave a step open:
   W_v are then [H_kv * d_h, D] and query head h reads key/value head
   h // (H / H_kv), so consecutive query heads share one key/value head.
   H_kv = 1 is multi-query attention, H_kv = H the chapter's layer.
+* Sliding window (prefix-reuse note, "Why a sliding-window partial hit must
+  fall back"): with window W, the row at index p reads rows
+  max(0, p - W + 1) .. p, and a window cache only needs (and keeps) the most
+  recent rows.  W = None reads the whole prefix.
 """
 from __future__ import annotations
 
@@ -118,7 +122,7 @@ def layer_projections(x_rows, wq, wk, wv, heads: int, positions, base: float, ro
 
 
 def causal_layer(x_rows, wq, wk, wv, heads: int, base: float = 10000.0,
-                 rope: bool = True, positions=None, rows=None, wo=None, kv_heads=None):
+                 rope: bool = True, positions=None, rows=None, wo=None, kv_heads=None, window=None):
     """Full-prefix causal attention of one layer, recomputed from hidden rows.
 
     This is the reference every cached result must reproduce (Chapter 37,
@@ -129,7 +133,8 @@ def causal_layer(x_rows, wq, wk, wv, heads: int, base: float = 10000.0,
     (Chapter 37, "Bind the state, calculate completely, then commit": merge
     heads, then the output projection); None returns the merged heads.
     ``kv_heads``: key/value heads H_kv (default H); query head h reads
-    key/value head h // (H / H_kv).
+    key/value head h // (H / H_kv).  ``window``: row p reads rows
+    max(0, p - window + 1) .. p only (None: rows 0 .. p).
     Returns dict with ``out`` [len(rows), D], ``keys`` / ``values``
     [H_kv, L, d_h] (the layer's full logical cache), ``weights`` (list per row
     of [H, p+1]).
@@ -147,9 +152,10 @@ def causal_layer(x_rows, wq, wk, wv, heads: int, base: float = 10000.0,
         rows = range(n)
     outs, weights = [], []
     for p in rows:
+        lo = 0 if window is None else max(0, p - window + 1)
         o_heads, w_heads = [], []
         for h in range(heads):
-            o, w = attend(q[p, h], k[: p + 1, h // group], v[: p + 1, h // group])
+            o, w = attend(q[p, h], k[lo: p + 1, h // group], v[lo: p + 1, h // group])
             o_heads.append(o)
             w_heads.append(w)
         outs.append(np.concatenate(o_heads))

@@ -63,3 +63,21 @@ def continuation_projection_rows(layers: int, query_len: int, cut: int) -> tuple
     """(rows this call, rows of a full recompute): layers x {Q,K,V} x tokens
     (prefix-reuse note, the 27-case table and the formula under it)."""
     return 3 * layers * (query_len - cut), 3 * layers * query_len
+
+
+def window_reuse_cut(cached, query) -> int:
+    """The note's conservative rule for a sliding-window cache (prefix-reuse note,
+    "Why a sliding-window partial hit must fall back"): the rows before the
+    window are gone, so the existing window is reused only when the whole
+    cached prefix matches and the query adds a suffix; any partial hit
+    recomputes from the start (cut 0)."""
+    cut = lcp_cut(cached, query)
+    return cut if cut == len(cached) else 0
+
+
+def window_continuable(length: int, cut: int, window: int, retained: int) -> bool:
+    """Whether a window cache holding the last ``retained`` of ``length`` rows can
+    continue from ``cut``: the continuation's first row reads rows
+    cut - window + 1 .. cut - 1, which must all still be held (or cut = 0,
+    a recompute).  The note's rule above is the case that demands cut = length."""
+    return cut == 0 or (0 <= cut <= length and cut - window + 1 >= length - retained)

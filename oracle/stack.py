@@ -44,11 +44,13 @@ def sinusoidal(positions, width: int) -> np.ndarray:
 class Layer:
     """One attention layer: W_q (and W_o or None) [D, D], W_k and W_v [H_kv * d_h, D], as [out, in]."""
 
-    def __init__(self, wq, wk, wv, heads: int, rope: bool = True, base: float = 10000.0, wo=None, kv_heads=None):
+    def __init__(self, wq, wk, wv, heads: int, rope: bool = True, base: float = 10000.0, wo=None, kv_heads=None,
+                 window=None):
         self.w = tuple(np.asarray(m, F64) for m in (wq, wk, wv))
         self.wo = None if wo is None else np.asarray(wo, F64)
         self.heads = heads
         self.kv_heads = heads if kv_heads is None else kv_heads
+        self.window = window
         self.rope = rope
         self.base = base
 
@@ -68,7 +70,7 @@ def forward(embed, layers, tokens, sinusoidal_pe: bool = True):
     kv = []
     for lay in layers:
         r = A.causal_layer(h, *lay.w, heads=lay.heads, base=lay.base, rope=lay.rope, positions=pos, wo=lay.wo,
-                           kv_heads=lay.kv_heads)
+                           kv_heads=lay.kv_heads, window=lay.window)
         kv.append((r["keys"], r["values"]))
         h = h + np.tanh(r["out"])
     return h, kv

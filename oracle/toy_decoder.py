@@ -15,7 +15,10 @@ model those facts allow:
     PE(p, 2i) = sin(p / 10000**(2i/16)),  PE(p, 2i+1) = cos(p / 10000**(2i/16))
 
 The cache keeps, per layer, K, V and the absolute position of every row, plus
-``next_position`` (note, "What must be trimmed together").  Parity of this
+``next_position`` (note, "What must be trimmed together").  A model with a
+sliding window W (note, "Why a sliding-window partial hit must fall back")
+lets the row at position p read positions p - W + 1 .. p only, and its cache
+keeps only the most recent rows (``retain``).  Parity of this
 model to the note's own model is unpinned (its weights and random generator
 are not published); what is pinned is the note's invariants: the reuse path
 equals a full recompute and the stale-position path does not.
@@ -44,11 +47,13 @@ def sinusoidal(positions, width: int = WIDTH) -> np.ndarray:
 
 
 class ToyModel:
-    """Embedding [VOCAB, WIDTH] and per layer (W_q, W_k, W_v), each [WIDTH, WIDTH] as [out, in]."""
+    """Embedding [VOCAB, WIDTH] and per layer (W_q, W_k, W_v), each [WIDTH, WIDTH] as [out, in];
+    ``window``: sliding-window width W, or None for full causal attention."""
 
-    def __init__(self, embed, layers):
+    def __init__(self, embed, layers, window=None):
         self.embed = np.asarray(embed, F64)
         self.layers = [tuple(np.asarray(w, F64) for w in ws) for ws in layers]
+        self.window = window
 
 
 def embed(model: ToyModel, tokens, positions) -> np.ndarray:
@@ -66,10 +71,19 @@ def full_forward(model: ToyModel, tokens):
     h = embed(model, tokens, pos)
     layers = []
     for wq, wk, wv in model.layers:
-        r = A.causal_layer(h, wq, wk, wv, heads=1, rope=False, positions=pos)
+        r = A.causal_layer(h, wq, wk, wv, heads=1, rope=False, positions=pos, window=model.window)
         layers.append((r["keys"][0].copy(), r["values"][0].copy(), pos.copy()))
         h = h + np.tanh(r["out"])
     return h, {"next_position": n, "layers": layers}
+
+
+def retain(cache, rows: int):
+    """A window cache: keep only the last ``rows`` rows of every layer (their
+    positions say which); next_position is unchanged."""
+    return {
+        "next_position": cache["next_position"],
+        "layers": [(k[-rows:].copy(), v[-rows:].copy(), p[-rows:].copy()) for k, v, p in cache["layers"]],
+    }
 
 
 def trim(cache, cut: int, keep_stale_position: bool = False):
@@ -83,6 +97,17 @@ def trim(cache, cut: int, keep_stale_position: bool = False):
         "next_position": cache["next_position"] if keep_stale_position else cut,
         "layers": [(k[:cut].copy(), v[:cut].copy(), p[:cut].copy()) for k, v, p in cache["layers"]],
     }
+
+
+def trim_window(cache, cut: int):
+    """A window cache (rows in position order, the oldest ones gone) cut back to
+    positions 0..cut-1: it keeps the rows it still holds below ``cut``;
+    next_position = cut."""
+    out = []
+    for k, v, p in cache["layers"]:
+        keep = p < cut
+        out.append((k[keep].copy(), v[keep].copy(), p[keep].copy()))
+    return {"next_position": cut, "layers": out}
 
 
 def chunk(model: ToyModel, tokens, cache):
@@ -105,6 +130,10 @@ def chunk(model: ToyModel, tokens, cache):
         for i in range(n):
             keys = np.concatenate([kc, k[: i + 1]])
             vals = np.concatenate([vc, v[: i + 1]])
+            if model.window is not None:
+                # rows by position: the window of position pos[i]
+                seen = np.concatenate([pc, pos[: i + 1]]) > pos[i] - model.window
+                keys, vals = keys[seen], vals[seen]
             a[i] = A.attend(q[i], keys, vals)[0]
         new_layers.append((np.concatenate([kc, k]), np.concatenate([vc, v]), np.concatenate([pc, pos])))
         h = h + np.tanh(a)

@@ -352,9 +352,9 @@ def test_lcp_rules():
         P.lcp_cut([1, 2], [True, 2])
 
 
-def _toy(seed):
+def _toy(seed, window=None):
     e, ws = synth.toy_model_arrays(seed)
-    return T.ToyModel(e, ws)
+    return T.ToyModel(e, ws, window=window)
 
 
 @pytest.mark.parametrize("seed", [7, 11, 23])
@@ -387,6 +387,68 @@ def test_toy_decoder_reuse_equals_recompute_and_stale_diverges(seed):
         else:
             assert err_nc <= 1e-12
     assert worst < 1e-13
+
+
+def test_window_attention_reads_only_the_last_w_rows():
+    """Sliding window (prefix-reuse note, "Why a sliding-window partial hit must
+    fall back"): a window as long as the sequence is full causal attention; a
+    window of 1 returns each row's own value exactly; with window W the row at
+    p equals the last row of a full recompute over rows p - W + 1 .. p at their
+    own positions (so exactly W rows are read, not W - 1 or W + 1)."""
+    D, heads, L, W = 8, 2, 9, 3
+    x = synth.normal(13, 2, (L, D))
+    w = [synth.normal(13, s, (D, D), std=0.5) for s in (3, 4, 5)]
+    full = A.causal_layer(x, *w, heads=heads)
+    np.testing.assert_array_equal(A.causal_layer(x, *w, heads=heads, window=L)["out"], full["out"])
+    one = A.causal_layer(x, *w, heads=heads, window=1)["out"]
+    np.testing.assert_array_equal(one, A.project(x, w[2]))
+    win = A.causal_layer(x, *w, heads=heads, window=W)["out"]
+    for p in range(L):
+        lo = max(0, p - W + 1)
+        ref = A.causal_layer(x[lo: p + 1], *w, heads=heads, positions=np.arange(lo, p + 1))["out"][-1]
+        np.testing.assert_allclose(win[p], ref, rtol=0, atol=1e-14)
+    assert np.max(np.abs(win[W:] - full["out"][W:])) > 1e-3
+
+
+def test_window_table_cuts_and_rows():
+    """The note's two sliding-window rows: with window 4 the cache of 1..8 holds
+    positions 4..7; an edit of the fifth token falls back to cut 0 (72 rows), an
+    append reuses the whole prefix (cut 8, 24 rows)."""
+    g = _load("p3_window_table.json")
+    model = _toy(7, window=g["window"])
+    _, cache = T.full_forward(model, g["cached"])
+    held = T.retain(cache, g["window"])
+    for _, _, pos in held["layers"]:
+        assert list(pos) == g["retained_positions"]
+    for c in g["conditions"]:
+        cut = P.window_reuse_cut(g["cached"], c["query"])
+        assert cut == c["cut"], c["name"]
+        assert P.continuation_projection_rows(g["layers"], len(c["query"]), cut) == (c["rows"], c["full_rows"])
+
+
+@pytest.mark.parametrize("seed", [7, 11, 23])
+def test_window_cache_continues_exactly_where_its_rows_suffice(seed):
+    """A window-4 toy decoder whose cache holds only the last 4 of 8 rows: for every
+    cut, continuing from the held rows equals the full recompute exactly when
+    window_continuable says so (cut 0, or every row the first new row reads is
+    still held: cut >= 7), and diverges otherwise -- which is why the note falls
+    back on a partial hit.  The note's own rule (whole-prefix match) is among the
+    continuable cuts."""
+    W = 4
+    model = _toy(seed, window=W)
+    cached = list(range(1, 9))
+    _, cache = T.full_forward(model, cached)
+    held = T.retain(cache, W)
+    for cut in range(0, 9):
+        query = cached[:cut] + [20, 21, 22, 23]
+        full, _ = T.full_forward(model, query)
+        h, _ = T.chunk(model, query[cut:], T.trim_window(held, cut))
+        err = float(np.max(np.abs(h - full[cut:])))
+        if P.window_continuable(len(cached), cut, W, W):
+            assert err <= 1e-12, (cut, err)
+        else:
+            assert err > 1e-3, (cut, err)
+    assert P.window_continuable(8, P.window_reuse_cut(cached, cached + [9]), W, W)
 
 
 def test_toy_decoder_layers_are_causal():
