@@ -62,6 +62,8 @@ enum {
   KVC_ERR_OUT_OF_BLOCKS = 21,                 /* paged cache: the pool has fewer free blocks
                                                  than the call needs (expected = needed,
                                                  actual = free)                          */
+  KVC_ERR_CACHE_WINDOW_MISMATCH = 22,         /* the layer's sliding window differs from the
+                                                 cache's (checked after the rotary setup)  */
   /* Found on the device before the commit; the commit is then suppressed.
    * Precedence when several hold: key, value, query, position, output. */
   KVC_ERR_NONFINITE_KEY = 30,    /* candidate rotated key has a NaN/Inf (first flat index
@@ -148,6 +150,7 @@ typedef struct {
   double rope_base;
   int32_t block_rows, pool_blocks; /* paged caches; 0 for contiguous storage */
   int32_t kv_heads;                /* key/value heads H_kv (= heads without grouping) */
+  int32_t window;                  /* sliding window (0: every row)                  */
 } kvc_cache_desc;
 
 typedef struct kvc_params kvc_params; /* W_q, W_k, W_v (, W_o) with an identity and revisions */
@@ -201,6 +204,27 @@ void kvc_params_destroy(kvc_params* params);
  * Errors: NULL_ARGUMENT, BAD_ARGUMENT, SHAPE_UNSUPPORTED. */
 kvc_status kvc_layer_create(const kvc_params* params, int32_t heads, kvc_pos_mode pos_mode,
                             double rope_base, int32_t rope_max_positions, kvc_layer** out);
+
+/* A layer with sliding-window attention (prefix-reuse note, "Why a
+ * sliding-window partial hit must fall back": the window is part of the
+ * computation a cache is bound to): a query at row r reads rows
+ * max(0, r - window + 1) .. r only; window 0 is kvc_layer_create.  Its cache
+ * (contiguous only) is a ring of `capacity` rows: row r lives in slot
+ * r % capacity, lengths and positions keep counting past the capacity (no
+ * FULL; the rotary table still bounds positions), and only the last
+ * `capacity` rows are held.  kvc_cache_create then requires capacity >=
+ * window, capacity a multiple of 256 and max_chunk_rows <= capacity.  The
+ * cache's binding includes the window (CACHE_WINDOW_MISMATCH).  A sequence
+ * holds rows h .. len - 1, where h rises as appends write over the oldest
+ * slots (a truncation keeps h; a cut to 0 or a reset clears it).  A cut
+ * other than 0 must keep every row its continuation reads,
+ * max(0, cut - window + 1) >= h; others are rejected (kvc_truncate,
+ * kvc_fork: BAD_CUT with `expected` = the smallest nonzero cut allowed);
+ * kvc_reuse_cut gives the cut to continue from.  kvc_snapshot returns the
+ * held rows.  Errors: those of kvc_layer_create, BAD_ARGUMENT (window < 0). */
+kvc_status kvc_layer_create_windowed(const kvc_params* params, int32_t heads, kvc_pos_mode pos_mode,
+                                     double rope_base, int32_t rope_max_positions, int32_t window,
+                                     kvc_layer** out);
 void kvc_layer_destroy(kvc_layer* layer);
 
 /* Creates an empty cache bound to `layer` (Chapter 37, the cache constructor):
@@ -303,7 +327,9 @@ kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags);
 kvc_status kvc_reset(kvc_cache* cache);
 
 /* Logical snapshot of sequence `seq` (Chapter 37, logical key/value
- * accessors): keys_out, values_out HOST [H_kv, len, d_h] in the storage type,
+ * accessors; a window cache gives the rows it still holds, h .. len - 1, and
+ * `len` below means their count): keys_out, values_out HOST
+ * [H_kv, len, d_h] in the storage type,
  * positions_out HOST int32[len] (each nullable).  rows_capacity: rows the
  * buffers hold; rows_out (HOST): len.  Synchronises the stream.  Errors:
  * NULL_ARGUMENT, BAD_ARGUMENT (seq out of range or rows_capacity < len),
@@ -328,6 +354,16 @@ kvc_status kvc_sync(kvc_cache* cache);
  * pointer with a positive count), EMPTY_QUERY, BAD_ARGUMENT (n_cached < 0). */
 kvc_status kvc_lcp_cut(const int32_t* cached, int64_t n_cached, const int32_t* query,
                        int64_t n_query, int64_t* cut_out);
+
+/* The cut to continue sequence `seq` from, given the longest common prefix
+ * `lcp_cut` of its cached tokens and a query (kvc_lcp_cut): lcp_cut itself
+ * when every row the continuation reads is still held, else 0 -- a full
+ * recompute (prefix-reuse note, "Why a sliding-window partial hit must fall
+ * back": with window 4 a cache of positions 0..7 holds only 4..7, so an edit
+ * at position 4 recomputes while an append reuses all 8 rows).  Caches
+ * without a window return lcp_cut.  HOST cut_out.  Errors: NULL_ARGUMENT,
+ * BAD_ARGUMENT (seq), BAD_CUT (lcp_cut outside [0, len]), DEFERRED. */
+kvc_status kvc_reuse_cut(kvc_cache* cache, int32_t seq, int64_t lcp_cut, int64_t* cut_out);
 
 /* Geometry of a cache.  Errors: NULL_ARGUMENT. */
 kvc_status kvc_cache_describe(const kvc_cache* cache, kvc_cache_desc* out);

@@ -26,6 +26,7 @@ KVC_ERR_CACHE_LAYER_REVISION_MISMATCH = 18
 KVC_ERR_CACHE_ROPE_MISMATCH = 19
 KVC_ERR_FULL = 20
 KVC_ERR_OUT_OF_BLOCKS = 21
+KVC_ERR_CACHE_WINDOW_MISMATCH = 22
 KVC_ERR_NONFINITE_KEY = 30
 KVC_ERR_NONFINITE_VALUE = 31
 KVC_ERR_NONFINITE_QUERY = 32
@@ -84,7 +85,7 @@ class CacheDesc(C.Structure):
         ("capacity", C.c_int32), ("max_chunk_rows", C.c_int32), ("kv_dtype", C.c_int32),
         ("pos_mode", C.c_int32), ("rope_max_positions", C.c_int32), ("device", C.c_int32),
         ("rope_base", C.c_double), ("block_rows", C.c_int32), ("pool_blocks", C.c_int32),
-        ("kv_heads", C.c_int32),
+        ("kv_heads", C.c_int32), ("window", C.c_int32),
     ]
 
 
@@ -101,7 +102,9 @@ PROTOTYPES = {
     "kvc_params_mark_updated": (I32, [P, I32]),
     "kvc_params_destroy": (None, [P]),
     "kvc_layer_create": (I32, [P, I32, I32, C.c_double, I32, PP]),
+    "kvc_layer_create_windowed": (I32, [P, I32, I32, C.c_double, I32, I32, PP]),
     "kvc_layer_destroy": (None, [P]),
+    "kvc_reuse_cut": (I32, [P, I32, I64, PI64]),
     "kvc_cache_create": (I32, [P, I32, I32, I32, P, PP]),
     "kvc_cache_create_paged": (I32, [P, I32, I32, I32, I32, I32, P, PP]),
     "kvc_cache_destroy": (None, [P]),

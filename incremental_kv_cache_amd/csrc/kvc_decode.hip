@@ -73,7 +73,9 @@ __device__ __forceinline__ uint4 load_stream(const bf16_t* p) {
 // QPW query heads (consecutive, sharing key/value head hk) per workgroup: every
 // K/V row is loaded once and scored against all of them, so grouped layers read
 // each retained row once per key/value head rather than once per query head.
-template <int DH, int U, bool PAGED, int QPW>
+// LAYOUT: 0 contiguous (one lane base), 1 block-paged, 2 windowed ring (row
+// bases through kv_block_base; rows below the window start are masked).
+template <int DH, int U, int LAYOUT, int QPW>
 __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevState s, SeqOrder order,
                                                                         float* __restrict__ out) {
   constexpr int G = DH / 8;
@@ -87,13 +89,15 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
   // sequences with the most rows first (blocks are dispatched with z slowest)
   const int tile = blockIdx.x, h0 = blockIdx.y * QPW, b = order.count ? order.seq[blockIdx.z] : blockIdx.z;
   const int C = s.capacity;
-  const int len = min(max(s.len[b], 0), C - 1);
+  const int len = decode_len(s, b);
   const int t = len + 1;
   const int TR = s.tile_rows;
-  const int r0 = tile * TR;
+  const DecodeSpan span = decode_span(s, len);
+  const int r0 = span.base0 + tile * TR;
   if (r0 >= t) return;
   const int r1 = min(t, r0 + TR);
-  const int ntiles = (t + TR - 1) / TR;
+  const int rs = span.rs;  // rows below rs lie outside the window (LAYOUT 2)
+  const int ntiles = span.ntiles;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
     // the STEP rows from base lie in one block of a paged cache (block rows are
     // a power-of-two multiple of STEP, tiles start on multiples of 512)
     const ptrdiff_t lane_base =
-        PAGED ? kv_block_base(s, b, hk, min(base, max(len - 1, 0))) : ptrdiff_t(kv_lane * C) * DH;
+        LAYOUT ? kv_block_base(s, b, hk, min(base, max(len - 1, 0))) : ptrdiff_t(kv_lane * C) * DH;
     const bf16_t* kc = kpool + lane_base;
     const bf16_t* vc = vpool + lane_base;
     uint4 kr[U], vr[U];
@@ -144,8 +148,8 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = base + u * GROUPS + grp;
-      ok[u] = r < r1;
-      const int rr = ok[u] ? r : r1 - 1;
+      ok[u] = r < r1 && (LAYOUT != 2 || r >= rs);
+      const int rr = r < r1 ? r : r1 - 1;  // masked rows still load a held row
       const bf16_t* kp = rr < len ? kc + size_t(rr) * DH : kn;
       const bf16_t* vp = rr < len ? vc + size_t(rr) * DH : vn;
       kr[u] = load_stream(kp);
@@ -251,9 +255,7 @@ __global__ __launch_bounds__(DH) void merge_decode_bf16_kernel(DevState s, float
   const size_t lane_id = blockIdx.x;
   const int b = int(lane_id / s.heads);
   const int h = int(lane_id - size_t(b) * s.heads);
-  const int C = s.capacity;
-  const int len = min(max(s.len[b], 0), C - 1);
-  const int ntiles = (len + 1 + s.tile_rows - 1) / s.tile_rows;
+  const int ntiles = decode_span(s, decode_len(s, b)).ntiles;
   if (ntiles == 1) return;
   const int j = threadIdx.x;
   const float* p0 = static_cast<const float*>(s.partials) + lane_id * s.max_tiles * (DH + 2);
@@ -296,15 +298,18 @@ int fast_attend_decode(const DevState& s, const SeqOrder& order, void* out) {
   float* o = static_cast<float*>(out);
   const dim3 block(64 * kWaves);
   const int qpw = decode_heads_per_block(s.dtype, s.head_width, s.heads / s.kv_heads);
-  const dim3 grid((s.capacity + s.tile_rows - 1) / s.tile_rows, s.heads / qpw, s.batch);
-#define KVC_DECODE_LAUNCH(DH_, U_, QPW_)                                                                     \
-  do {                                                                                                    \
-    if (s.paged)                                                                                          \
-      hipLaunchKernelGGL((attend_decode_bf16_kernel<DH_, U_, true, QPW_>), grid, block, 0, st(s.stream), s, \
-                         order, o);                                                                       \
-    else                                                                                                  \
-      hipLaunchKernelGGL((attend_decode_bf16_kernel<DH_, U_, false, QPW_>), grid, block, 0, st(s.stream),   \
-                         s, order, o);                                                                    \
+  const dim3 grid((s.span_rows + s.tile_rows - 1) / s.tile_rows, s.heads / qpw, s.batch);
+#define KVC_DECODE_LAUNCH(DH_, U_, QPW_)                                                                    \
+  do {                                                                                                   \
+    if (s.ring)                                                                                          \
+      hipLaunchKernelGGL((attend_decode_bf16_kernel<DH_, U_, 2, QPW_>), grid, block, 0, st(s.stream), s,   \
+                         order, o);                                                                      \
+    else if (s.paged)                                                                                    \
+      hipLaunchKernelGGL((attend_decode_bf16_kernel<DH_, U_, 1, QPW_>), grid, block, 0, st(s.stream), s,   \
+                         order, o);                                                                      \
+    else                                                                                                 \
+      hipLaunchKernelGGL((attend_decode_bf16_kernel<DH_, U_, 0, QPW_>), grid, block, 0, st(s.stream), s,   \
+                         order, o);                                                                      \
   } while (0)
   // eight query heads per workgroup hold 8 x 16 accumulators per lane: half the
   // row groups in flight keeps them in registers

@@ -97,6 +97,7 @@ __device__ __forceinline__ bool any_error(const ErrWords* e) {
 // sequence's block table).
 __device__ __forceinline__ size_t kv_offset(const DevState& s, int b, int h, int r) {
   const int dh = s.head_width;
+  if (s.ring) return ((size_t(b) * s.kv_heads + h) * s.capacity + r % s.capacity) * dh;
   if (!s.paged) return ((size_t(b) * s.kv_heads + h) * s.capacity + r) * dh;
   const int lg = s.block_rows_log2;
   const int blk = s.block_table[size_t(b) * s.table_width + (r >> lg)];
@@ -108,11 +109,41 @@ __device__ __forceinline__ size_t kv_offset(const DevState& s, int b, int h, int
 // (contiguous).  Used where a run of rows is known to lie in one block.
 __device__ __forceinline__ ptrdiff_t kv_block_base(const DevState& s, int b, int h, int r0) {
   const int dh = s.head_width;
+  // a ring's runs never cross a multiple of the capacity (a multiple of kMinBlockRows)
+  if (s.ring) return ptrdiff_t((size_t(b) * s.kv_heads + h) * s.capacity) * dh - ptrdiff_t(r0 - r0 % s.capacity) * dh;
   if (!s.paged) return ptrdiff_t((size_t(b) * s.kv_heads + h) * s.capacity) * dh;
   const int lg = s.block_rows_log2;
   // an unassigned block (-1) is only reached by callers that read no cache row
   const int blk = max(s.block_table[size_t(b) * s.table_width + (r0 >> lg)], 0);
   return (ptrdiff_t(size_t(blk) * s.kv_heads + h) << lg) * dh - ptrdiff_t((r0 >> lg) << lg) * dh;
+}
+
+// Slot of row r in the per-sequence position table [B, C].
+__device__ __forceinline__ int pos_slot(const DevState& s, int r) { return s.ring ? r % s.capacity : r; }
+
+// First row a query at row r reads (sliding window), else 0.
+__device__ __forceinline__ int window_start(const DevState& s, int r) {
+  return s.window ? max(0, r - s.window + 1) : 0;
+}
+
+// The candidate row index (= committed rows) of sequence b in a decode call,
+// clamped to what the storage can address.
+__device__ __forceinline__ int decode_len(const DevState& s, int b) {
+  const int len = max(s.len[b], 0);
+  return s.ring ? len : min(len, s.capacity - 1);
+}
+
+// Rows a decode query at row len reads, [rs, len], in split-K tiles of
+// tile_rows starting at base0 (rs rounded down to kDecodeTileRows).
+struct DecodeSpan {
+  int rs, base0, ntiles;
+};
+__device__ __forceinline__ DecodeSpan decode_span(const DevState& s, int len) {
+  DecodeSpan d;
+  d.rs = window_start(s, len);
+  d.base0 = d.rs - d.rs % kDecodeTileRows;
+  d.ntiles = (len + 1 - d.base0 + s.tile_rows - 1) / s.tile_rows;
+  return d;
 }
 
 // True when a failure word of the cache's gate (its own words, or every layer

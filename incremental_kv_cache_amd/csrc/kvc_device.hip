@@ -207,12 +207,13 @@ __global__ __launch_bounds__(64 * kAttendWaves) void attend_decode_kernel(DevSta
   constexpr int GROUPS = kAttendWaves * Geo::RPW;
   __shared__ A sm_m[GROUPS], sm_l[GROUPS], sm_acc[GROUPS * DH], out_acc[DH];
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int C = s.capacity;
-  const int len = min(max(s.len[b], 0), C - 1);
+  const int len = decode_len(s, b);
   const int t = len + 1;
-  const int r0 = tile * s.tile_rows;
-  if (r0 >= t) return;
-  const int r1 = min(t, r0 + s.tile_rows);
+  const DecodeSpan span = decode_span(s, len);
+  const int tile0 = span.base0 + tile * s.tile_rows;
+  if (tile0 >= t) return;
+  const int r0 = max(tile0, span.rs);
+  const int r1 = min(t, tile0 + s.tile_rows);
   const size_t lane_id = size_t(b) * s.heads + h;
   const int hk = h / (s.heads / s.kv_heads);
   const size_t kv_lane = size_t(b) * s.kv_heads + hk;
@@ -237,9 +238,7 @@ template <typename T, int DH>
 __global__ __launch_bounds__(64) void merge_decode_kernel(DevState s, typename Acc<T>::type* __restrict__ out) {
   using A = typename Acc<T>::type;
   const int h = blockIdx.x, b = blockIdx.y;
-  const int C = s.capacity;
-  const int len = min(max(s.len[b], 0), C - 1);
-  const int ntiles = (len + 1 + s.tile_rows - 1) / s.tile_rows;
+  const int ntiles = decode_span(s, decode_len(s, b)).ntiles;
   const size_t lane_id = size_t(b) * s.heads + h;
   const A* part = static_cast<const A*>(s.partials) + lane_id * s.max_tiles * (DH + 2);
   A mx = -INFINITY;
@@ -267,8 +266,7 @@ __global__ __launch_bounds__(64 * kAttendWaves) void attend_chunk_kernel(DevStat
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
   if (i >= n_b) return;
-  const int C = s.capacity;
-  const int len = min(max(s.len[b], 0), C);
+  const int len = s.ring ? max(s.len[b], 0) : min(max(s.len[b], 0), s.capacity);
   const size_t lane_id = size_t(b) * s.heads + h;
   const int hk = h / (s.heads / s.kv_heads);
   const size_t kv_lane = size_t(b) * s.kv_heads + hk;
@@ -278,8 +276,8 @@ __global__ __launch_bounds__(64 * kAttendWaves) void attend_chunk_kernel(DevStat
   const T* vn = static_cast<const T*>(s.cand_v) + kv_lane * n_max * DH;
   const A* q = static_cast<const A*>(s.q) + (lane_id * n_max + i) * DH;
   A M, L;
-  attend_rows<T, DH, kAttendWaves>(s, b, hk, q, kc, vc, kn, vn, len, 0, len + i + 1, A(s.scale), sm_m, sm_l, sm_acc,
-                                   M, L, out_acc);
+  attend_rows<T, DH, kAttendWaves>(s, b, hk, q, kc, vc, kn, vn, len, window_start(s, len + i), len + i + 1,
+                                   A(s.scale), sm_m, sm_l, sm_acc, M, L, out_acc);
   for (int j = threadIdx.x; j < DH; j += blockDim.x) {
     const A o = out_acc[j] / L;
     const size_t flat = (size_t(b) * n_max + i) * s.model_width + size_t(h) * DH + j;
@@ -301,7 +299,8 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max,
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
   const int len = s.len[b];
   const int C = s.capacity;
-  if (r0 >= n_b || len < 0 || len + n_b > C) return;
+  // a ring takes any length (rows wrap; n_b <= C is checked on the host)
+  if (r0 >= n_b || len < 0 || (!s.ring && len + n_b > C)) return;
   const int nr = min(kCommitRows, n_b - r0);
   const int dh = s.head_width;
   const size_t lane_id = size_t(b) * s.kv_heads + h;
@@ -330,7 +329,8 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max,
   }
   if (h == 0) {
     const int np = s.next_pos[b];
-    for (int k = threadIdx.x; k < nr; k += blockDim.x) s.positions[size_t(b) * C + len + r0 + k] = np + r0 + k;
+    for (int k = threadIdx.x; k < nr; k += blockDim.x)
+      s.positions[size_t(b) * C + pos_slot(s, len + r0 + k)] = np + r0 + k;
   }
 }
 
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
   const int b = blockIdx.x;
   const int len = s.len[b];
   const int C = s.capacity;
-  if (len < 0 || len + 1 > C) return;
+  if (len < 0 || (!s.ring && len + 1 > C)) return;
   const int dh = s.head_width;
   const size_t row_bytes = size_t(dh) * sizeof(T);
   const size_t seq_rows = size_t(b) * s.kv_heads;
@@ -372,7 +372,8 @@ __global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
   __syncthreads();
   if (threadIdx.x == 0) {
     const int np = s.next_pos[b];
-    s.positions[size_t(b) * C + len] = np;
+    s.positions[size_t(b) * C + pos_slot(s, len)] = np;
+    if (s.ring) s.held[b] = max(s.held[b], len + 1 - C);  // row len took the slot of row len - C
     s.len[b] = len + 1;
     s.next_pos[b] = np + 1;
   }
@@ -385,7 +386,8 @@ __global__ __launch_bounds__(256) void commit_advance_kernel(DevState s, int n_m
   if (b >= s.batch) return;
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
   const int len = s.len[b];
-  if (n_b <= 0 || len < 0 || len + n_b > s.capacity) return;
+  if (n_b <= 0 || len < 0 || (!s.ring && len + n_b > s.capacity)) return;
+  if (s.ring) s.held[b] = max(s.held[b], len + n_b - s.capacity);
   s.len[b] = len + n_b;
   s.next_pos[b] = s.next_pos[b] + n_b;
 }
@@ -395,6 +397,7 @@ __global__ __launch_bounds__(256) void commit_advance_kernel(DevState s, int n_m
 struct SetArgs {
   int32_t vals[kSetChunk];
   int first, count, mode;
+  int held_src;  // dev_set_seq_length on a ring: sequence whose held row is copied (-1: 0)
 };
 
 __global__ __launch_bounds__(256) void set_lengths_kernel(DevState s, SetArgs a) {
@@ -404,9 +407,16 @@ __global__ __launch_bounds__(256) void set_lengths_kernel(DevState s, SetArgs a)
     if (a.mode == 2) {
       s.len[b] = 0;
       s.next_pos[b] = 0;
+      if (s.ring) s.held[b] = 0;
+    } else if (a.mode == 3) {  // one sequence, after a fork
+      s.len[b] = a.vals[k];
+      s.next_pos[b] = a.vals[k];
+      if (s.ring) s.held[b] = a.held_src >= 0 ? s.held[a.held_src] : 0;
     } else {
       s.len[b] = a.vals[k];
       if (a.mode == 0) s.next_pos[b] = a.vals[k];
+      // a ring cut below its held rows (only a cut to 0 is allowed) starts afresh
+      if (s.ring && a.vals[k] < s.held[b]) s.held[b] = a.vals[k];
     }
   }
 }
@@ -581,7 +591,7 @@ int dispatch(int dtype, int dh, Args&&... args) {
 template <typename T, int DH>
 struct AttendDecode {
   static int run(const DevState& s) {
-    dim3 grid((s.capacity + s.tile_rows - 1) / s.tile_rows, s.heads, s.batch);
+    dim3 grid((s.span_rows + s.tile_rows - 1) / s.tile_rows, s.heads, s.batch);
     hipLaunchKernelGGL((attend_decode_kernel<T, DH>), grid, dim3(64 * kAttendWaves), 0, st(s.stream), s);
     return last_launch();
   }
@@ -739,11 +749,12 @@ int dev_clear_table(const DevState& s) {
   return last_launch();
 }
 
-int dev_set_seq_length(const DevState& s, int seq, int32_t value) {
+int dev_set_seq_length(const DevState& s, int seq, int32_t value, int held_src) {
   SetArgs a{};
   a.first = seq;
   a.count = 1;
-  a.mode = 0;
+  a.mode = 3;
+  a.held_src = held_src;
   a.vals[0] = value;
   hipLaunchKernelGGL(set_lengths_kernel, dim3(1), dim3(256), 0, st(s.stream), s, a);
   return last_launch();

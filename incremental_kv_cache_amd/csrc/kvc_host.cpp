@@ -34,6 +34,7 @@ struct kvc_layer {
   const kvc_params* params;
   int32_t heads, head_width;
   int32_t kv_heads;  // key/value heads; query head h reads key/value head h / (heads / kv_heads)
+  int32_t window;    // sliding window (rows a query reads, itself included); 0 = the whole prefix
   kvc_pos_mode pos_mode;
   double rope_base;
   int32_t rope_max_positions;
@@ -55,6 +56,7 @@ struct kvc_cache {
   // geometry and binding (Chapter 37, layer-kv-cache listing: the cache struct)
   int32_t batch, heads, head_width, model_width, capacity, max_chunk_rows;
   int32_t kv_heads;
+  int32_t window;  // sliding window of the bound layer (0: none); window caches are rings of `capacity` rows
   kvc_dtype dtype;
   uint64_t params_id;
   uint64_t revision[4];
@@ -65,6 +67,7 @@ struct kvc_cache {
   int device;
   // host copy of the committed state
   std::vector<int32_t> len, next_pos;
+  std::vector<int32_t> held;  // window (ring) caches: oldest row each sequence still holds
   bool pending_async = false;
   // device state
   DevState ds{};
@@ -223,7 +226,25 @@ kvc_status check_binding(const kvc_layer* layer, const kvc_cache* c) {
                 c->rope_feature_width, c->rope_max_positions, c->rope_base, layer->rope_feature_width(),
                 layer->rope_max_positions, layer->rope_base);
   }
+  if (c->window != layer->window)
+    return fail_ea(KVC_ERR_CACHE_WINDOW_MISMATCH, layer->window, c->window,
+                   "cache sliding window %d does not match layer window %d", c->window, layer->window);
   return KVC_OK;
+}
+
+// Whether sequence b of a window cache can continue from `cut`: cut 0 (a
+// recompute), or every row the continuation's first row reads (cut - window + 1
+// .. cut - 1) is still held, i.e. not older than the last `capacity` rows
+// (prefix-reuse note, "Why a sliding-window partial hit must fall back").
+bool window_continuable(const kvc_cache* c, int b, int64_t cut) {
+  if (cut == 0) return true;
+  if (cut < 0 || cut > c->len[b]) return false;
+  return c->window == 0 || std::max<int64_t>(0, cut - c->window + 1) >= c->held[b];
+}
+
+// Smallest nonzero cut a window cache's sequence b can continue from.
+int32_t window_min_cut(const kvc_cache* c, int b) {
+  return std::max(1, c->window ? c->held[b] + c->window - 1 : 1);
 }
 
 // Reads the device failure words; on a failure fills the detail, clears the
@@ -300,6 +321,7 @@ kvc_status resync_lengths(kvc_cache* c) {
   const size_t bytes = sizeof(int32_t) * size_t(c->batch);
   int rc = dev_copy_d2h_sync(c->len.data(), c->ds.len, bytes, c->ds.stream);
   if (rc == 0) rc = dev_copy_d2h_sync(c->next_pos.data(), c->ds.next_pos, bytes, c->ds.stream);
+  if (rc == 0 && c->ds.ring) rc = dev_copy_d2h_sync(c->held.data(), c->ds.held, bytes, c->ds.stream);
   if (rc) return device_fail(rc, "reading lengths");
   return KVC_OK;
 }
@@ -453,6 +475,7 @@ void free_cache(kvc_cache* c) {
   dev_free(c->ds.next_pos);
   dev_free(c->ds.positions);
   dev_free(c->ds.rows);
+  dev_free(c->ds.held);
   dev_free(c->ds.cand_k);
   dev_free(c->ds.cand_v);
   dev_free(c->ds.q);
@@ -522,8 +545,10 @@ kvc_status commit_stage(kvc_cache* c, int n_max, const int32_t* n_rows) {
 void advance_mirror(kvc_cache* c, int n_max, const int32_t* n_rows) {
   for (int b = 0; b < c->batch; ++b) {
     const int n = n_rows ? n_rows[b] : n_max;
+    if (n <= 0) continue;
     c->len[b] += n;
     c->next_pos[b] += n;
+    if (c->window) c->held[b] = std::max(c->held[b], c->len[b] - c->capacity);  // slots reused
   }
 }
 
@@ -570,11 +595,19 @@ kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_row
 // finer split.
 void choose_decode_tiles(kvc_cache* cache) {
   int tile = kDecodeTileRows;
-  int max_len = 0;
-  for (int b = 0; b < cache->batch; ++b) max_len = std::max(max_len, cache->len[b]);
+  // rows each query reads from its tile-aligned start (the whole prefix, or
+  // the window rounded down to a tile boundary)
+  std::vector<int64_t> span(cache->batch);
+  int64_t max_len = 0;
+  for (int b = 0; b < cache->batch; ++b) {
+    const int64_t len = cache->len[b];
+    const int64_t rs = cache->window ? std::max<int64_t>(0, len - cache->window + 1) : 0;
+    span[b] = len + 1 - (rs - rs % kDecodeTileRows);
+    max_len = std::max(max_len, span[b] - 1);
+  }
   for (int64_t cand = kDecodeTileRows; cand <= (int64_t(1) << 30); cand *= 2) {
     int64_t blocks = 0;
-    for (int b = 0; b < cache->batch; ++b) blocks += (int64_t(cache->len[b]) + cand) / cand;
+    for (int b = 0; b < cache->batch; ++b) blocks += (span[b] - 1 + cand) / cand;
     if (blocks * (cache->heads / decode_heads_per_block(cache->dtype, cache->head_width,
                                                         cache->heads / cache->kv_heads)) < 1024)
       break;
@@ -606,6 +639,18 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
   if (max_chunk_rows <= 0)
     return fail(KVC_ERR_BAD_ARGUMENT, "max_chunk_rows must be at least 1, got %d", max_chunk_rows);
   const bool paged = block_rows != 0;
+  const int W = layer->window;
+  if (W > 0) {
+    // a window cache is a ring of `capacity` rows: it must hold a whole window,
+    // whole 256-row runs (the fast kernels' aligned reads never wrap), and a
+    // whole chunk (a chunk never overwrites its own rows)
+    if (paged) return fail(KVC_ERR_BAD_ARGUMENT, "a sliding-window layer uses a contiguous (ring) cache");
+    if (capacity < W || capacity % kMinBlockRows != 0 || max_chunk_rows > capacity)
+      return fail_ea(KVC_ERR_BAD_ARGUMENT, W, capacity,
+                     "a window cache needs capacity >= window %d, a multiple of %d, and >= max_chunk_rows %d "
+                     "(capacity %d)",
+                     W, kMinBlockRows, max_chunk_rows, capacity);
+  }
   if (paged) {
     // Paged storage: a decode split-K step (at most 256 rows) and a 64-row
     // chunk-attention tile must each fall inside one block.
@@ -635,6 +680,7 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
   c->batch = batch;
   c->heads = H;
   c->kv_heads = HK;
+  c->window = W;
   c->head_width = dh;
   c->model_width = p->model_width;
   c->capacity = capacity;
@@ -649,6 +695,7 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
   c->pos_mode = layer->pos_mode;
   c->len.assign(batch, 0);
   c->next_pos.assign(batch, 0);
+  c->held.assign(batch, 0);
   c->session = shared_err != nullptr;
   if (paged) {
     c->paged = true;
@@ -667,7 +714,9 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
   }
 
   const size_t es = elem_size(p->dtype), as = acc_size(p->dtype);
-  const int max_tiles = (capacity + kDecodeTileRows - 1) / kDecodeTileRows;
+  // rows one decode query can read (a window, plus its start's misalignment)
+  const int span_rows = W > 0 ? std::min(capacity, W) + kDecodeTileRows : capacity;
+  const int max_tiles = (span_rows + kDecodeTileRows - 1) / kDecodeTileRows;
   auto round16 = [](size_t b) { return (b + 15) & ~size_t(15); };
   DevState& s = c->ds;
   s.dtype = p->dtype;
@@ -689,6 +738,9 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
   s.max_tiles = max_tiles;
   s.tile_rows = kDecodeTileRows;
   s.stream = hip_stream;
+  s.window = W;
+  s.ring = W > 0;
+  s.span_rows = span_rows;
   s.paged = paged;
   s.block_rows_log2 = c->block_lg;
   s.table_width = c->table_width;
@@ -703,6 +755,7 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
       {reinterpret_cast<void**>(&s.next_pos), round16(sizeof(int32_t) * batch)},
       {reinterpret_cast<void**>(&s.positions), round16(sizeof(int32_t) * size_t(pos_elems))},
       {reinterpret_cast<void**>(&s.rows), round16(sizeof(int32_t) * batch)},
+      {reinterpret_cast<void**>(&s.held), W > 0 ? round16(sizeof(int32_t) * batch) : 0},
       {&s.cand_k, round16(size_t(cand) * es)},
       {&s.cand_v, round16(size_t(cand) * es)},
       {&s.q, round16(size_t(qrows) * as)},
@@ -873,7 +926,7 @@ kvc_status session_call(kvc_session* S, const int32_t* tokens, int n_max, const 
     const kvc_cache* c = S->caches[l];
     for (int b = 0; b < c->batch; ++b) {
       const int n = n_rows ? n_rows[b] : n_max;
-      if (int64_t(c->len[b]) + n > c->capacity) {
+      if (!c->window && int64_t(c->len[b]) + n > c->capacity) {
         g_last.layer = l;
         g_last.sequence = b;
         return fail_ea(KVC_ERR_FULL, c->capacity, int64_t(c->len[b]) + n,
@@ -977,6 +1030,7 @@ const char* kvc_status_name(kvc_status s) {
     N(KVC_ERR_CACHE_ROPE_MISMATCH)
     N(KVC_ERR_FULL)
     N(KVC_ERR_OUT_OF_BLOCKS)
+    N(KVC_ERR_CACHE_WINDOW_MISMATCH)
     N(KVC_ERR_NONFINITE_KEY)
     N(KVC_ERR_NONFINITE_VALUE)
     N(KVC_ERR_NONFINITE_QUERY)
@@ -1046,6 +1100,11 @@ void kvc_params_destroy(kvc_params* params) { delete params; }
 
 kvc_status kvc_layer_create(const kvc_params* params, int32_t heads, kvc_pos_mode pos_mode, double rope_base,
                             int32_t rope_max_positions, kvc_layer** out) {
+  return kvc_layer_create_windowed(params, heads, pos_mode, rope_base, rope_max_positions, 0, out);
+}
+
+kvc_status kvc_layer_create_windowed(const kvc_params* params, int32_t heads, kvc_pos_mode pos_mode,
+                                     double rope_base, int32_t rope_max_positions, int32_t window, kvc_layer** out) {
   reset_detail();
   if (!params || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_layer_create");
   *out = nullptr;
@@ -1059,6 +1118,7 @@ kvc_status kvc_layer_create(const kvc_params* params, int32_t heads, kvc_pos_mod
   if (dh < 2 || !is_pow2(dh) || dh > max_head_width(params->dtype))
     return fail(KVC_ERR_SHAPE_UNSUPPORTED, "head width %d must be a power of two in [2, %d] for this type", dh,
                 max_head_width(params->dtype));
+  if (window < 0) return fail_ea(KVC_ERR_BAD_ARGUMENT, 0, window, "sliding window %d must be >= 0", window);
   if (params->kv_width % dh != 0 || heads % (params->kv_width / dh) != 0)
     return fail_ea(KVC_ERR_BAD_ARGUMENT, dh, params->kv_width,
                    "key/value width %d must be a whole number of %d-wide heads that divides the %d query heads",
@@ -1068,6 +1128,7 @@ kvc_status kvc_layer_create(const kvc_params* params, int32_t heads, kvc_pos_mod
   l->params = params;
   l->heads = heads;
   l->kv_heads = params->kv_width / dh;
+  l->window = window;
   l->head_width = dh;
   l->pos_mode = pos_mode;
   l->rope_base = rope_base;
@@ -1128,7 +1189,7 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
   kvc_status st = check_binding(layer, cache);
   if (st != KVC_OK) return st;
   for (int b = 0; b < cache->batch; ++b) {
-    if (cache->len[b] >= cache->capacity) {
+    if (!cache->window && cache->len[b] >= cache->capacity) {  // a window cache is a ring
       g_last.sequence = b;
       return fail_ea(KVC_ERR_FULL, cache->capacity, cache->len[b], "KV cache is full at capacity %d",
                      cache->capacity);
@@ -1187,7 +1248,7 @@ kvc_status kvc_continue_chunk(const kvc_layer* layer, kvc_cache* cache, const vo
   if (st != KVC_OK) return st;
   for (int b = 0; b < cache->batch; ++b) {
     const int n = n_rows ? n_rows[b] : n_max;
-    if (int64_t(cache->len[b]) + n > cache->capacity) {
+    if (!cache->window && int64_t(cache->len[b]) + n > cache->capacity) {
       g_last.sequence = b;
       return fail_ea(KVC_ERR_FULL, cache->capacity, int64_t(cache->len[b]) + n,
                      "KV cache is full at capacity %d (sequence %d needs %d more rows)", cache->capacity, b, n);
@@ -1241,6 +1302,13 @@ kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags) {
       return fail_ea(KVC_ERR_BAD_CUT, cache->len[b], cut[b], "cut %d of sequence %d is outside [0, %d]", cut[b], b,
                      cache->len[b]);
     }
+    if (!window_continuable(cache, b, cut[b])) {
+      g_last.sequence = b;
+      return fail_ea(KVC_ERR_BAD_CUT, window_min_cut(cache, b), cut[b],
+                     "cut %d of sequence %d needs rows the window cache no longer holds (continue from 0 or from "
+                     "%d .. %d)",
+                     cut[b], b, window_min_cut(cache, b), cache->len[b]);
+    }
   }
   const bool stale = flags & KVC_TRUNCATE_KEEP_STALE_POSITION;
   int rc = dev_set_lengths(cache->ds, cut, stale ? 1 : 0);
@@ -1248,6 +1316,7 @@ kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags) {
   for (int b = 0; b < cache->batch; ++b) {
     cache->len[b] = cut[b];
     if (!stale) cache->next_pos[b] = cut[b];
+    if (cut[b] < cache->held[b]) cache->held[b] = cut[b];
   }
   if (cache->paged) {
     // blocks wholly past the cut go back to the pool (a block other
@@ -1267,6 +1336,7 @@ kvc_status kvc_reset(kvc_cache* cache) {
   if (rc) return device_fail(rc, "length reset");
   std::fill(cache->len.begin(), cache->len.end(), 0);
   std::fill(cache->next_pos.begin(), cache->next_pos.end(), 0);
+  std::fill(cache->held.begin(), cache->held.end(), 0);
   if (cache->paged) {
     rc = dev_clear_table(cache->ds);
     if (rc) return device_fail(rc, "block table reset");
@@ -1290,6 +1360,11 @@ kvc_status kvc_fork(kvc_cache* cache, int32_t src, int32_t dst, int32_t rows) {
     return fail_ea(KVC_ERR_BAD_CUT, cache->len[src], rows, "fork of %d rows outside [0, %d] of sequence %d", rows,
                    cache->len[src], src);
   }
+  if (!window_continuable(cache, src, rows)) {
+    g_last.sequence = src;
+    return fail_ea(KVC_ERR_BAD_CUT, window_min_cut(cache, src), rows,
+                   "fork of %d rows needs rows the window cache no longer holds", rows);
+  }
   DevState& s = cache->ds;
   int rc = 0;
   if (cache->paged) {
@@ -1310,14 +1385,16 @@ kvc_status kvc_fork(kvc_cache* cache, int32_t src, int32_t dst, int32_t rows) {
     kvc_status st = upload_table(cache, changed);
     if (st != KVC_OK) return st;
   } else {
-    rc = dev_copy_seq_rows(s, dst, src, rows);
+    // a ring's rows sit in slots r % capacity: copy every slot
+    rc = dev_copy_seq_rows(s, dst, src, cache->window ? cache->capacity : rows);
     if (rc) return device_fail(rc, "row copy");
   }
-  rc = dev_copy_positions(s, dst, src, rows);
-  if (rc == 0) rc = dev_set_seq_length(s, dst, rows);
+  rc = dev_copy_positions(s, dst, src, cache->window ? cache->capacity : rows);
+  if (rc == 0) rc = dev_set_seq_length(s, dst, rows, rows > 0 ? src : -1);
   if (rc) return device_fail(rc, "fork bookkeeping");
   cache->len[dst] = rows;
   cache->next_pos[dst] = rows;
+  cache->held[dst] = rows > 0 ? cache->held[src] : 0;
   return KVC_OK;
 }
 
@@ -1364,13 +1441,40 @@ kvc_status kvc_snapshot(kvc_cache* cache, int32_t seq, void* keys_out, void* val
   st = resync_lengths(cache);
   if (st != KVC_OK) return st;
   const int len = cache->len[seq];
-  if (rows_out) *rows_out = len;
-  if ((keys_out || values_out || positions_out) && rows_capacity < len)
-    return fail_ea(KVC_ERR_BAD_ARGUMENT, len, rows_capacity, "snapshot buffers hold %lld rows, need %d",
-                   (long long)rows_capacity, len);
+  // a window cache holds (and returns) rows held[seq] .. len - 1 only
+  const int held = cache->window ? len - cache->held[seq] : len;
+  if (rows_out) *rows_out = held;
+  if ((keys_out || values_out || positions_out) && rows_capacity < held)
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, held, rows_capacity, "snapshot buffers hold %lld rows, need %d",
+                   (long long)rows_capacity, held);
   const size_t es = elem_size(cache->dtype);
   const size_t row_bytes = size_t(cache->head_width) * es;
   int rc = 0;
+  if (cache->window) {
+    // rows len - held .. len - 1 sit in slots r % C: at most two runs
+    const size_t lane_bytes = size_t(cache->capacity) * row_bytes;
+    const size_t seq_off = size_t(seq) * cache->kv_heads * lane_bytes;
+    int done = 0;
+    while (done < held && rc == 0) {
+      const int r = len - held + done;
+      const int slot = r % cache->capacity;
+      const int n = std::min(held - done, cache->capacity - slot);
+      if (keys_out)
+        rc = dev_copy_d2h_2d_sync(static_cast<char*>(keys_out) + done * row_bytes, size_t(held) * row_bytes,
+                                  static_cast<char*>(cache->ds.keys) + seq_off + slot * row_bytes, lane_bytes,
+                                  n * row_bytes, cache->kv_heads, cache->ds.stream);
+      if (rc == 0 && values_out)
+        rc = dev_copy_d2h_2d_sync(static_cast<char*>(values_out) + done * row_bytes, size_t(held) * row_bytes,
+                                  static_cast<char*>(cache->ds.values) + seq_off + slot * row_bytes, lane_bytes,
+                                  n * row_bytes, cache->kv_heads, cache->ds.stream);
+      if (rc == 0 && positions_out)
+        rc = dev_copy_d2h_sync(positions_out + done, cache->ds.positions + size_t(seq) * cache->capacity + slot,
+                               sizeof(int32_t) * size_t(n), cache->ds.stream);
+      done += n;
+    }
+    if (rc) return device_fail(rc, "snapshot copy");
+    return KVC_OK;
+  }
   if (cache->paged) {
     // [H, len, d_h] gathered block by block: [H, block rows, d_h] per block
     const size_t head_bytes = size_t(cache->block_rows) * row_bytes;
@@ -1423,6 +1527,20 @@ kvc_status kvc_lcp_cut(const int32_t* cached, int64_t n_cached, const int32_t* q
   return KVC_OK;
 }
 
+kvc_status kvc_reuse_cut(kvc_cache* cache, int32_t seq, int64_t lcp_cut, int64_t* cut_out) {
+  reset_detail();
+  if (!cache || !cut_out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_reuse_cut");
+  if (seq < 0 || seq >= cache->batch)
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, cache->batch, seq, "sequence %d out of range", seq);
+  kvc_status st = check_deferred(cache);
+  if (st != KVC_OK) return st;
+  if (lcp_cut < 0 || lcp_cut > cache->len[seq])
+    return fail_ea(KVC_ERR_BAD_CUT, cache->len[seq], lcp_cut, "common prefix %lld outside [0, %d]",
+                   (long long)lcp_cut, cache->len[seq]);
+  *cut_out = window_continuable(cache, seq, lcp_cut) ? lcp_cut : 0;
+  return KVC_OK;
+}
+
 kvc_status kvc_cache_describe(const kvc_cache* cache, kvc_cache_desc* out) {
   reset_detail();
   if (!cache || !out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_cache_describe");
@@ -1440,6 +1558,7 @@ kvc_status kvc_cache_describe(const kvc_cache* cache, kvc_cache_desc* out) {
   out->rope_base = cache->rope_base;
   out->block_rows = cache->block_rows;
   out->pool_blocks = cache->pool_blocks;
+  out->window = cache->window;
   return KVC_OK;
 }
 
@@ -1638,6 +1757,12 @@ kvc_status kvc_session_truncate(kvc_session* session, const int32_t* cut, int32_
         g_last.sequence = b;
         return fail_ea(KVC_ERR_BAD_CUT, c->len[b], cut[b], "cut %d of sequence %d is outside [0, %d]", cut[b], b,
                        c->len[b]);
+      }
+      if (!window_continuable(c, b, cut[b])) {
+        g_last.layer = int32_t(l);
+        g_last.sequence = b;
+        return fail_ea(KVC_ERR_BAD_CUT, window_min_cut(c, b), cut[b],
+                       "cut %d of sequence %d needs rows layer %zu's window cache no longer holds", cut[b], b, l);
       }
     }
   }

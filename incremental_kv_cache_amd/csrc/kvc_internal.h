@@ -61,6 +61,7 @@ struct DevState {
   int32_t* next_pos;   // [B] position of the next row
   int32_t* positions;  // [B, C] absolute position of each row
   int32_t* rows;       // [B] rows of the current chunk call
+  int32_t* held;       // ring caches: [B] oldest row still held (older slots were written over)
   void* cand_k;        // [B, H_kv, n, d_h] storage type (n = rows of the call)
   void* cand_v;        // [B, H_kv, n, d_h]
   void* q;             // [B, H, n, d_h] accumulate type
@@ -80,6 +81,13 @@ struct DevState {
   int block_rows_log2;
   int table_width;
   const int32_t* block_table;
+  // Sliding window (window > 0): a query at row r reads rows r - window + 1 .. r,
+  // and the contiguous storage is a ring: row r lives in slot r % capacity
+  // (ring = 1), so lengths grow past the capacity while the last `capacity`
+  // rows stay held.  window = 0: every row 0 .. r, no ring.
+  int window;
+  int ring;
+  int span_rows;  // most rows one decode query reads, plus tile alignment (sizes the split-K grid)
   ErrWords* err;
   // The failure words every state-changing kernel checks before it writes:
   // the cache's own (gate_count 1), or those of every layer of a session, so
@@ -115,8 +123,10 @@ int dev_set_rows(const DevState& s, const int32_t* vals);
 int dev_set_table(const DevState& s, const int32_t* idx, const int32_t* val, int count);
 // Paged caches: every table entry = -1 (no block).
 int dev_clear_table(const DevState& s);
-// len[seq] = next_pos[seq] = value (one sequence; the others unchanged).
-int dev_set_seq_length(const DevState& s, int seq, int32_t value);
+// len[seq] = next_pos[seq] = value (one sequence; the others unchanged); for a
+// ring cache held[seq] = held[held_src] (a fork that copied every slot), or 0
+// when held_src < 0.
+int dev_set_seq_length(const DevState& s, int seq, int32_t value, int held_src);
 // Paged caches: rows [0, rows) of every head of block `src` into block `dst`
 // (copy-on-write of a shared block before an append into it).
 int dev_copy_block_rows(const DevState& s, int dst, int src, int rows);

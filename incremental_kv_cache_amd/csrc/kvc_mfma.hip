@@ -660,7 +660,8 @@ __device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
-template <int DH>
+// WIN: sliding-window layer (ring storage, a lower key bound per query).
+template <int DH, bool WIN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_flash_kernel(
     DevState s, int n_max, int per_seq_rows, ChunkOrder order, float* __restrict__ out) {
   constexpr int KT = 64;
@@ -693,8 +694,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
   if (qt * 128 >= n_b) return;
-  const int C = s.capacity;
-  const int len = min(max(s.len[b], 0), C);
+  const int len = WIN ? max(s.len[b], 0) : min(max(s.len[b], 0), s.capacity);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -706,6 +706,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int i_max = min(qt * 128 + 127, n_b - 1);
   const int total = len + i_max + 1;
   const int ntiles = (total + KT - 1) / KT;
+  // sliding window: query qi reads keys lo .. limit; the block starts at the key
+  // tile holding its first query's lowest key
+  const int lo = WIN ? window_start(s, limit) : 0;
+  const int it_first = WIN ? window_start(s, len + qt * 128) / KT : 0;
+  const int wave_lo_max = WIN ? window_start(s, len + min(qt * 128 + wave * 32 + 31, n_b - 1)) : 0;
   const size_t lane_id = size_t(b) * H + h;
   const int hk = h / (H / s.kv_heads);  // the key/value head this query head reads
   const size_t kv_lane = size_t(b) * s.kv_heads + hk;
@@ -799,16 +804,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int li = lane & 15;
   const int vlane = (4 * g + (li >> 2)) * LDV + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
 
-  if (contiguous(0)) {
-    fetch(0);
+  if (contiguous(it_first * KT)) {
+    fetch(it_first * KT);
     stash(0);
   } else {
-    fetch_mixed(0, 0);
+    fetch_mixed(it_first * KT, 0);
   }
   __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+  for (int it = it_first; it < ntiles; ++it) {
     const int j0 = it * KT;
-    const int buf = it & 1;
+    const int buf = (it - it_first) & 1;
     // the other buffer was last read before the previous barrier: fill it now
     // (contiguous tiles land in registers first and are written after this tile)
     const bool more = it + 1 < ntiles;
@@ -831,14 +836,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         st[kt] = mfma32(a.v, qf[u].v, st[kt]);
       }
     }
-    // causal mask only where the tile reaches past the wave's first query
-    if (j0 + KT - 1 > wave_limit_min) {
+    // causal mask only where the tile reaches past the wave's first query, the
+    // window's lower edge only where the tile starts below the wave's last one
+    if (j0 + KT - 1 > wave_limit_min || (WIN && j0 < wave_lo_max)) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key > limit) st[kt][r] = -INFINITY;
+          if (key > limit || (WIN && key < lo)) st[kt][r] = -INFINITY;
         }
     }
     float tmax = -INFINITY;
@@ -974,12 +980,20 @@ int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, const Chun
   const int items = order.count ? order.count : s.batch * order.qtiles;
   if (items == 0) return 0;
   const dim3 grid(unsigned(items) * unsigned(s.heads));
+#define KVC_FLASH_LAUNCH(DH_, WIN_)                                                                      \
+  hipLaunchKernelGGL((attend_flash_kernel<DH_, WIN_>), grid, dim3(256), 0, st(s.stream), s, n_max, per_seq_rows, \
+                     order, static_cast<float*>(out))
   if (s.head_width == 128) {
-    hipLaunchKernelGGL(attend_flash_kernel<128>, grid, dim3(256), 0, st(s.stream), s, n_max, per_seq_rows, order,
-                       static_cast<float*>(out));
+    if (s.window)
+      KVC_FLASH_LAUNCH(128, true);
+    else
+      KVC_FLASH_LAUNCH(128, false);
   } else if (s.head_width == 64) {
-    hipLaunchKernelGGL(attend_flash_kernel<64>, grid, dim3(256), 0, st(s.stream), s, n_max, per_seq_rows, order,
-                       static_cast<float*>(out));
+    if (s.window)
+      KVC_FLASH_LAUNCH(64, true);
+    else
+      KVC_FLASH_LAUNCH(64, false);
+#undef KVC_FLASH_LAUNCH
   } else {
     return -1;
   }

@@ -184,6 +184,26 @@ def _stream_arg(stream):
     return C.c_void_p(stream or 0)
 
 
+def kvc_layer_create_windowed(params: Params, heads: int, window: int, pos_mode: int = KVC_POS_ROPE,
+                              rope_base: float = 10000.0, rope_max_positions: int = 4096) -> Layer:
+    """A layer whose queries read only the last ``window`` rows (itself included)."""
+    lib = params._lib
+    out = C.c_void_p()
+    _check(lib, lib.kvc_layer_create_windowed(params.ptr, heads, pos_mode, float(rope_base), rope_max_positions,
+                                              window, C.byref(out)))
+    h = Layer(lib, out)
+    h.params = params
+    h.heads = heads
+    return h
+
+
+def kvc_reuse_cut(cache: Cache, seq: int, lcp_cut: int) -> int:
+    """The cut to continue sequence ``seq`` from, given its longest common prefix."""
+    out = C.c_int64()
+    _check(cache._lib, cache._lib.kvc_reuse_cut(cache.ptr, seq, int(lcp_cut), C.byref(out)))
+    return out.value
+
+
 def kvc_cache_create(layer: Layer, batch: int, capacity: int, max_chunk_rows: int = 1, stream=None) -> Cache:
     """Allocates the cache on the current device; its work runs on ``stream``
     (default: torch's current stream)."""

@@ -60,9 +60,11 @@ int dev_set_lengths(const DevState& s, const int32_t* vals, int mode) {
     if (mode == 2) {
       s.len[b] = 0;
       s.next_pos[b] = 0;
+      if (s.ring) s.held[b] = 0;
     } else {
       s.len[b] = vals[b];
       if (mode == 0) s.next_pos[b] = vals[b];
+      if (s.ring && vals[b] < s.held[b]) s.held[b] = vals[b];
     }
   }
   return 0;
@@ -83,10 +85,11 @@ int dev_clear_table(const DevState& s) {
   for (size_t k = 0; k < size_t(s.batch) * s.table_width; ++k) const_cast<int32_t*>(s.block_table)[k] = -1;
   return 0;
 }
-int dev_set_seq_length(const DevState& s, int seq, int32_t value) {
+int dev_set_seq_length(const DevState& s, int seq, int32_t value, int held_src) {
   if (gate_closed(s)) return 0;
   s.len[seq] = value;
   s.next_pos[seq] = value;
+  if (s.ring) s.held[seq] = held_src >= 0 ? s.held[held_src] : 0;
   return 0;
 }
 int dev_copy_block_rows(const DevState& s, int dst, int src, int rows) {
@@ -123,6 +126,7 @@ static bool g_fake = false;
 static int g_call = 0;
 static long long g_fail_next = -1;
 static size_t kv_off(const DevState& s, int b, int h, int r) {
+  if (s.ring) r %= s.capacity;
   if (!s.paged) return ((size_t(b) * s.kv_heads + h) * s.capacity + r) * s.head_width;
   const int lg = s.block_rows_log2;
   const int blk = s.block_table[size_t(b) * s.table_width + (r >> lg)];
@@ -167,10 +171,11 @@ int dev_commit(const DevState& s, int n_max, int per_seq) {
           static_cast<double*>(s.values)[dst + e] = static_cast<const double*>(s.cand_v)[src + e];
         }
       }
-      s.positions[size_t(b) * s.capacity + r] = s.next_pos[b] + i;
+      s.positions[size_t(b) * s.capacity + (s.ring ? r % s.capacity : r)] = s.next_pos[b] + i;
     }
     s.len[b] += n;
     s.next_pos[b] += n;
+    if (s.ring && n > 0 && s.len[b] - s.capacity > s.held[b]) s.held[b] = s.len[b] - s.capacity;
   }
   return 0;
 }
