@@ -485,6 +485,7 @@ void free_cache(kvc_cache* c) {
   if (!c->session) dev_free(c->ds.err);
   dev_free(const_cast<int32_t*>(c->ds.block_table));
   dev_free(c->ds.merged);
+  dev_free(c->ds.proj_partials);
   dev_host_free(c->err_host);
   for (void* e : c->prof.events) dev_event_destroy(e);
   delete c;
@@ -762,6 +763,12 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
       {&s.partials, round16(size_t(batch) * H * max_tiles * (dh + 2) * as)},
       {reinterpret_cast<void**>(&s.err), shared_err ? 0 : round16(sizeof(ErrWords))},
       {&s.merged, p->w[3] ? round16(size_t(qrows) * as) : 0},  // [B, max_chunk_rows, D]
+      // split-K partial sums of the bf16 decode projection (one 32-row tile)
+      {reinterpret_cast<void**>(&s.proj_partials),
+       p->dtype == KVC_BF16 && batch <= 32 && (p->model_width == 2048 || p->model_width == 4096 ||
+                                               p->model_width == 8192)
+           ? round16(sizeof(float) * kSkinnySplitMax * 64 * size_t(p->model_width + 2 * p->kv_width))
+           : 0},
       {reinterpret_cast<void**>(const_cast<int32_t**>(&s.block_table)),
        paged ? round16(sizeof(int32_t) * c->table.size()) : 0},
   };

@@ -39,6 +39,8 @@ inline int decode_heads_per_block(int dtype, int head_width, int group) {
   while (q < 8 && group % (2 * q) == 0) q *= 2;
   return q;
 }
+// Largest reduction-axis split of the skinny (at most 64-row) bf16 projection.
+constexpr int kSkinnySplitMax = 8;
 // Values per by-value length update (kernel-argument payload).
 constexpr int kSetChunk = 480;
 
@@ -68,6 +70,8 @@ struct DevState {
   void* merged;        // [B, n, D] accumulate type: merged heads before W_o (null without W_o)
   void* out_proj_dst;  // [B, n, D] accumulate type: destination of the W_o projection (per call)
   void* partials;      // [B, H, max_tiles, d_h + 2] accumulate type
+  float* proj_partials;  // bf16 caches: [kSkinnySplitMax, 64, D + 2 kv_width] float32 split-K sums of
+                         // the skinny projection (null: that projection runs unsplit)
   int max_tiles;       // ceil(C / kDecodeTileRows)
   int tile_rows;       // split-K tile of the current decode call (multiple of kDecodeTileRows)
   int single_tile;     // 1 when every lane of the current decode call fits one tile

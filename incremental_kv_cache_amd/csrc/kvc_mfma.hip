@@ -242,9 +242,15 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 
 // NCH > 0: the reduction axis has exactly NCH chunks (fully unrolled); 0: any D.
 // XT: input element type (bf16 rows, or the float32 merged heads for W_o).
-template <int NCH, typename XT>
+// KSPLIT > 1: block z sums chunks z NCH/KSPLIT .. (z+1) NCH/KSPLIT - 1 only and
+// stores its float32 partial sums at s.proj_partials[z][m][64 t + 16 w + c16]
+// (tile t, wave w, MFMA column c16); skinny_reduce_kernel adds them in order z
+// and runs the epilogue.  Splitting gives a 32-row projection (192 blocks at
+// D = 4096) enough blocks and loads in flight to fill the chip.
+template <int NCH, typename XT, int KSPLIT>
 __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const XT* __restrict__ x, int M,
                                                              int n_max, int per_seq_rows, int proj_first) {
+  static_assert(KSPLIT == 1 || (NCH > 0 && NCH % KSPLIT == 0), "a split needs a fixed chunk count");
   __shared__ __attribute__((aligned(16))) bf16_t Xs[2][32 * SLDX];
   const int D = s.model_width;
   const int half = s.head_width >> 1;
@@ -262,14 +268,16 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const X
   const int h = pair / half;
   const int f = pair - h * half;
   const int wrow = h * s.head_width + f + ((c16 >> 3) ? half : 0);
-  const bf16_t* wp = weight_of(s, p) + size_t(wrow) * D + 8 * g4;
+  constexpr int NCHK = NCH / KSPLIT;  // chunks of this block (split launches)
+  const int k0 = KSPLIT > 1 ? int(blockIdx.z) * NCHK * SKC : 0;
+  const bf16_t* wp = weight_of(s, p) + size_t(wrow) * D + 8 * g4 + k0;
   // input staging: thread copies 32 bytes of row tid/8
   const int xrow = tid >> 3;
   const int xseg = (tid & 7) * 16;
-  const XT* xg = x + size_t(min(m0 + xrow, M - 1)) * D + xseg;
+  const XT* xg = x + size_t(min(m0 + xrow, M - 1)) * D + xseg + k0;
 
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int nch = NCH > 0 ? NCH : D / SKC;
+  const int nch = NCH > 0 ? NCHK : D / SKC;
   // weight fragments and input chunks are loaded SRING - 1 chunks ahead of the
   // multiply, into rings indexed by chunk % SRING (static: chunks are unrolled
   // in groups of SUNROLL).  The two streams share the distance because vector
@@ -312,7 +320,7 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const X
   };
   if constexpr (NCH > 0) {
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) step(c, c % SRING, (c + SRING - 1) % SRING, (c + 1) % SRING, c & 1);
+    for (int c = 0; c < NCHK; ++c) step(c, c % SRING, (c + SRING - 1) % SRING, (c + 1) % SRING, c & 1);
   } else {
     int c = 0;
     for (; c + SUNROLL <= nch; c += SUNROLL) {
@@ -324,6 +332,16 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const X
       if (c + k < nch) step(c + k, k % SRING, (k + SRING - 1) % SRING, (k + 1) % SRING, k & 1);
   }
 
+  if constexpr (KSPLIT > 1) {
+    const int cols = gridDim.x * 64;
+    float* part = s.proj_partials + size_t(blockIdx.z) * 64 * cols + blockIdx.x * 64 + wave * 16 + c16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      part[size_t(4 * g4 + r) * cols] = acc0[r];
+      part[size_t(16 + 4 * g4 + r) * cols] = acc1[r];
+    }
+    return;
+  }
   // pairs: lanes with column j < 8 take the high feature from lane + 8
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -334,6 +352,32 @@ __global__ __launch_bounds__(256) void project_skinny_kernel(DevState s, const X
       store_pair(s, p, m0 + 16 + 4 * g4 + r, pair, acc1[r], hi1, M, n_max, per_seq_rows);
     }
   }
+}
+
+// Sums the KSPLIT partials of a split skinny projection (in order z, so the
+// result does not depend on scheduling) and runs its epilogue: thread
+// (m, tile, wave, j < 8) owns rotary pair 32 tile + 8 wave + j of row m.
+// Launched for M <= 32 rows (one row tile).
+template <int KSPLIT>
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(DevState s, int M, int n_max, int per_seq_rows,
+                                                            int proj_first, int tiles) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int per_row = tiles * 32;
+  const int m = idx / per_row;
+  if (m >= M) return;
+  const int q = idx - m * per_row;
+  int tile = q >> 5;
+  const int w = (q >> 3) & 3, j = q & 7;
+  const int cols = tiles * 64;
+  const float* part = s.proj_partials + size_t(m) * cols + tile * 64 + w * 16 + j;
+  float lo = 0.f, hi = 0.f;
+#pragma unroll
+  for (int z = 0; z < KSPLIT; ++z) {
+    lo += part[size_t(z) * 64 * cols];
+    hi += part[size_t(z) * 64 * cols + 8];
+  }
+  const int p = tile_proj(s, proj_first, 64, tile);
+  store_pair(s, p, m, tile * 32 + w * 8 + j, lo, hi, M, n_max, per_seq_rows);
 }
 
 // ------------------------------------------------------------- tiled GEMM --
@@ -934,23 +978,47 @@ int mfma_project_t(const DevState& s, const XT* xb, int n_max, int per_seq_rows,
   const int kv_cols = nproj == 3 ? s.kv_width : s.model_width;
   if (M <= 64) {
     if (kv_cols % 64 != 0) return -1;
-    dim3 grid(cols / 64, (M + 31) / 32);
+    const int tiles = cols / 64;
+    const int mtiles = (M + 31) / 32;
+    // split the reduction axis until the launch has about 512 blocks (one row
+    // tile and a fixed chunk count only: the partial buffer holds 32 rows)
+    const int nch = s.model_width / SKC;
+    int split = 1;
+    if (s.proj_partials && mtiles == 1 && (nch == 16 || nch == 32 || nch == 64))
+      while (split < kSkinnySplitMax && tiles * split < 512 && nch % (2 * split) == 0 && nch / (2 * split) >= SRING)
+        split *= 2;
+    dim3 grid(tiles, mtiles, split);
+#define KVC_SKINNY(NCH_, SPLIT_)                                                                           \
+  hipLaunchKernelGGL((project_skinny_kernel<NCH_, XT, SPLIT_>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max, \
+                     per_seq_rows, proj_first)
+#define KVC_SKINNY_SPLITS(NCH_)      \
+  switch (split) {                   \
+    case 1: KVC_SKINNY(NCH_, 1); break; \
+    case 2: KVC_SKINNY(NCH_, 2); break; \
+    case 4: KVC_SKINNY(NCH_, 4); break; \
+    default: KVC_SKINNY(NCH_, 8); break; \
+  }
     switch (s.model_width) {
-      case 2048:
-        hipLaunchKernelGGL((project_skinny_kernel<16, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
-                           per_seq_rows, proj_first);
-        break;
-      case 4096:
-        hipLaunchKernelGGL((project_skinny_kernel<32, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
-                           per_seq_rows, proj_first);
-        break;
-      case 8192:
-        hipLaunchKernelGGL((project_skinny_kernel<64, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
-                           per_seq_rows, proj_first);
-        break;
-      default:
-        hipLaunchKernelGGL((project_skinny_kernel<0, XT>), grid, dim3(256), 0, st(s.stream), s, xb, M, n_max,
-                           per_seq_rows, proj_first);
+      case 2048: KVC_SKINNY_SPLITS(16); break;
+      case 4096: KVC_SKINNY_SPLITS(32); break;
+      case 8192: KVC_SKINNY_SPLITS(64); break;
+      default: KVC_SKINNY(0, 1);
+    }
+#undef KVC_SKINNY_SPLITS
+#undef KVC_SKINNY
+    if (split > 1) {
+      const int rc = int(hipGetLastError());
+      if (rc) return rc;
+      const unsigned threads = unsigned(M) * unsigned(tiles) * 32u;
+      const dim3 rgrid((threads + 255) / 256);
+      switch (split) {
+        case 2: hipLaunchKernelGGL(skinny_reduce_kernel<2>, rgrid, dim3(256), 0, st(s.stream), s, M, n_max,
+                                   per_seq_rows, proj_first, tiles); break;
+        case 4: hipLaunchKernelGGL(skinny_reduce_kernel<4>, rgrid, dim3(256), 0, st(s.stream), s, M, n_max,
+                                   per_seq_rows, proj_first, tiles); break;
+        default: hipLaunchKernelGGL(skinny_reduce_kernel<8>, rgrid, dim3(256), 0, st(s.stream), s, M, n_max,
+                                    per_seq_rows, proj_first, tiles); break;
+      }
     }
   } else if (std::is_same<XT, bf16_t>::value && M >= 2048 && s.model_width % GBN == 0 && kv_cols % GBN == 0 &&
              s.head_width % 64 == 0 && int64_t(M) * s.model_width < (int64_t(1) << 31)) {

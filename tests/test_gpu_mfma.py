@@ -13,7 +13,7 @@ from incremental_kv_cache_amd import kvcache as K
 from incremental_kv_cache_amd import synth
 from oracle import attention as A
 
-from tests.gpu_util import assert_parity, hidden, make_layer, storage_f64, to_f64
+from tests.gpu_util import assert_parity, hidden, make_layer, storage_f64, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -173,3 +173,35 @@ def test_wide_projection_chunk(B, n_max, H, rows, cuts):
             assert list(pos) == list(range(len(seq)))
             assert_parity(storage_f64(k, "bf16"), full["keys"], "bf16", f"keys {b}")
             assert_parity(storage_f64(v, "bf16"), full["values"], "bf16", f"values {b}")
+
+
+@pytest.mark.parametrize("D,heads,kv_heads,B,wo", [(2048, 16, 16, 5, True), (4096, 32, 8, 32, False),
+                                                   (4096, 32, 32, 1, False)])
+def test_split_decode_projection(D, heads, kv_heads, B, wo):
+    """The decode projection of up to 32 rows at D = 2048 / 4096 splits its
+    reduction axis over 4-8 blocks per column tile and adds the float32
+    partials in a second kernel (W_o too): outputs, keys and values equal the
+    float64 layer over two decode steps."""
+    dh = D // heads
+    ws = synth.grouped_weights(51, D, kv_heads * dh, D ** -0.5, "bf16")
+    tens = [to_device(s, "bf16") for s, _ in ws]
+    w = [f for _, f in ws]
+    wo_f = None
+    if wo:
+        wo_s, wo_f = synth.output_weight(51, D, D ** -0.5, "bf16")
+        tens.append(to_device(wo_s, "bf16"))
+    params = K.kvc_params_create_grouped(*tens)
+    layer = K.kvc_layer_create(params, heads, K.KVC_POS_ROPE, 10000.0, 64)
+    cache = K.kvc_cache_create(layer, B, 64)
+    x_dev, x = hidden(52, synth.STREAM_X, B, 2, D, "bf16")
+    outs = []
+    for s in range(2):
+        out, _ = K.kvc_append_and_attend(layer, cache, x_dev[:, s:s + 1].contiguous())
+        outs.append(to_f64(out)[:, 0])
+    for b in range(B):
+        full = A.causal_layer(x[b], *w, heads=heads, kv_heads=kv_heads, wo=wo_f)
+        for s in range(2):
+            assert_parity(outs[s][b], full["out"][s], "bf16", f"seq {b} step {s}")
+        k, v, _ = K.kvc_snapshot(cache, b)
+        assert_parity(storage_f64(k, "bf16"), full["keys"], "bf16", f"keys {b}")
+        assert_parity(storage_f64(v, "bf16"), full["values"], "bf16", f"values {b}")
