@@ -48,6 +48,23 @@ __device__ __forceinline__ float group_sum_dpp(float v) {
   return v;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Dot product of 8 bf16 pairs held as 4 packed words, accumulated in float32
+// (v_dot2c_f32_bf16: both products exact, summed in float32).
+__device__ __forceinline__ float dot8_bf16(const uint32_t (&q)[4], const uint4& k) {
+  float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[0]), __builtin_bit_cast(bf16x2_t, k.x), 0.f,
+                                            false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[1]), __builtin_bit_cast(bf16x2_t, k.y), d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[2]), __builtin_bit_cast(bf16x2_t, k.z), d, false);
+  d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q[3]), __builtin_bit_cast(bf16x2_t, k.w), d, false);
+  return d;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)lo)) | (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)hi)) << 16);
+}
+
 __device__ __forceinline__ void unpack_bf16x8(const uint4& u, float (&f)[8]) {
   f[0] = __uint_as_float(u.x << 16);
   f[1] = __uint_as_float(u.x & 0xffff0000u);
@@ -111,20 +128,31 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
   const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + kv_lane * DH + g * 8;
   const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + kv_lane * DH + g * 8;
 
+  // one query: q in float32; several: q rounded to bf16 pairs (scaled first),
+  // scored with packed bf16 dot products straight from the stored keys, which
+  // keeps the vector work per K/V byte close to the one-query kernel's
   const float sl2 = float(s.scale) * 1.4426950408889634f;
-  float qv[QPW][8];
+  float qv[QPW == 1 ? 8 : 1];
+  uint32_t qb[QPW][4];
 #pragma unroll
   for (int qh = 0; qh < QPW; ++qh) {
     const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(s.q) + (lane0 + qh) * DH + g * 8);
     const float4 a = qp[0], c = qp[1];
-    qv[qh][0] = a.x * sl2;
-    qv[qh][1] = a.y * sl2;
-    qv[qh][2] = a.z * sl2;
-    qv[qh][3] = a.w * sl2;
-    qv[qh][4] = c.x * sl2;
-    qv[qh][5] = c.y * sl2;
-    qv[qh][6] = c.z * sl2;
-    qv[qh][7] = c.w * sl2;
+    if constexpr (QPW == 1) {
+      qv[0] = a.x * sl2;
+      qv[1] = a.y * sl2;
+      qv[2] = a.z * sl2;
+      qv[3] = a.w * sl2;
+      qv[4] = c.x * sl2;
+      qv[5] = c.y * sl2;
+      qv[6] = c.z * sl2;
+      qv[7] = c.w * sl2;
+    } else {
+      qb[qh][0] = pack_bf16x2(a.x * sl2, a.y * sl2);
+      qb[qh][1] = pack_bf16x2(a.z * sl2, a.w * sl2);
+      qb[qh][2] = pack_bf16x2(c.x * sl2, c.y * sl2);
+      qb[qh][3] = pack_bf16x2(c.z * sl2, c.w * sl2);
+    }
   }
   float m[QPW], l[QPW];
   float acc[QPW][8];
@@ -158,14 +186,16 @@ __global__ __launch_bounds__(64 * kWaves) void attend_decode_bf16_kernel(DevStat
     float sc[QPW][U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float kf[8];
-      unpack_bf16x8(kr[u], kf);
-#pragma unroll
-      for (int qh = 0; qh < QPW; ++qh) {
+      if constexpr (QPW == 1) {
+        float kf[8];
+        unpack_bf16x8(kr[u], kf);
         float d = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) d = fmaf(qv[qh][e], kf[e], d);
-        sc[qh][u] = d;
+        for (int e = 0; e < 8; ++e) d = fmaf(qv[e], kf[e], d);
+        sc[0][u] = d;
+      } else {
+#pragma unroll
+        for (int qh = 0; qh < QPW; ++qh) sc[qh][u] = dot8_bf16(qb[qh], kr[u]);
       }
     }
 #pragma unroll

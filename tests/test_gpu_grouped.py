@@ -100,10 +100,9 @@ def test_grouped_equals_multi_head_with_repeated_weights(dtype, dh, heads, kv_he
     query heads computes the same keys and values per head and the same
     attention per query head: chunk and decode outputs are bit-identical to
     the grouped layer's, and its cache holds each key/value head repeated.
-    (Up to four query heads per decode workgroup the rows are grouped as in
-    the one-head kernel; the eight-head variant streams half as many rows per
-    softmax step, so it matches only within rounding and is checked against
-    the oracle above.)"""
+    (The bf16 decode of a grouped layer scores with q rounded to bf16 and packed
+    dot products, so there the two agree within the bf16 bar; both are checked
+    against the oracle above.)"""
     import torch
     D = heads * dh
     g = heads // kv_heads
@@ -123,7 +122,12 @@ def test_grouped_equals_multi_head_with_repeated_weights(dtype, dh, heads, kv_he
     for s in range(2):
         og, _ = K.kvc_append_and_attend(lay_g, cg, xd_dev[:, s:s + 1].contiguous())
         om, _ = K.kvc_append_and_attend(lay_m, cm, xd_dev[:, s:s + 1].contiguous())
-        assert torch.equal(og, om), f"decode step {s}"
+        if dtype == "bf16":
+            # the grouped bf16 decode scores with q rounded to bf16 (packed dot products),
+            # the one-head kernel with float32 q: equal within the bf16 bar
+            assert float((og - om).abs().max()) <= TOL["bf16"], f"decode step {s}"
+        else:
+            assert torch.equal(og, om), f"decode step {s}"
     for b in range(B):
         kg, vg, _ = K.kvc_snapshot(cg, b)
         km, vm, _ = K.kvc_snapshot(cm, b)
