@@ -591,7 +591,8 @@ kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_row
 }
 
 // Split-K tile of a decode call: the largest power-of-two multiple of 512
-// rows that still gives at least 1024 workgroups (four per compute unit);
+// rows that still gives at least 1024 workgroups (four per compute unit; 512
+// when a workgroup serves several query heads);
 // measured on the bench workloads, fewer and longer tiles stream faster than a
 // finer split.
 void choose_decode_tiles(kvc_cache* cache) {
@@ -606,12 +607,14 @@ void choose_decode_tiles(kvc_cache* cache) {
     span[b] = len + 1 - (rs - rs % kDecodeTileRows);
     max_len = std::max(max_len, span[b] - 1);
   }
+  // a workgroup serving several query heads does that many times the work per
+  // row it reads: half as many (longer) tiles measured faster for them
+  const int qpw = decode_heads_per_block(cache->dtype, cache->head_width, cache->heads / cache->kv_heads);
+  const int64_t min_blocks = qpw > 1 ? 512 : 1024;
   for (int64_t cand = kDecodeTileRows; cand <= (int64_t(1) << 30); cand *= 2) {
     int64_t blocks = 0;
     for (int b = 0; b < cache->batch; ++b) blocks += (span[b] - 1 + cand) / cand;
-    if (blocks * (cache->heads / decode_heads_per_block(cache->dtype, cache->head_width,
-                                                        cache->heads / cache->kv_heads)) < 1024)
-      break;
+    if (blocks * (cache->heads / qpw) < min_blocks) break;
     tile = int(cand);
     if (cand > max_len) break;
   }
