@@ -152,11 +152,29 @@ __device__ __forceinline__ void flush_bad(const DevState& s, int p, unsigned lon
     flag_min(p == 0 ? &s.err->query : (p == 1 ? &s.err->key : (p == 2 ? &s.err->value : &s.err->output)), bad);
 }
 
+// Rotary factors (cos, sin) of four consecutive pairs of a row, or (1, 0) when
+// the projection is not rotated or the row is not stored.  Loaded apart from
+// put_pairs4 so that a caller can issue the loads of several rows before any
+// of their stores (the compiler may not move a load past a store it cannot
+// prove disjoint).
+struct Rope4 {
+  float4 c, sn;
+};
+__device__ __forceinline__ Rope4 rope4(const DevState& s, int p, const RowDst& d, int pair0) {
+  Rope4 r{make_float4(1.f, 1.f, 1.f, 1.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+  if (d.i < 0 || p >= 2 || !s.rope) return r;
+  const int half = s.head_width >> 1;
+  const int f = pair0 % half;
+  r.c = *reinterpret_cast<const float4*>(static_cast<const float*>(s.rope_cos) + size_t(d.pos) * half + f);
+  r.sn = *reinterpret_cast<const float4*>(static_cast<const float*>(s.rope_sin) + size_t(d.pos) * half + f);
+  return r;
+}
+
 // Four consecutive pairs pair0 .. pair0 + 3 of one head (pair0 % 4 == 0 and
 // d_h / 2 % 4 == 0): the same as four put_pair calls, with 16-byte (float) or
-// 8-byte (bf16) stores and one table load per rotary factor.
+// 8-byte (bf16) stores, rotated by the factors from rope4.
 __device__ __forceinline__ void put_pairs4(const DevState& s, int p, const RowDst& d, int pair0, float4 lo,
-                                           float4 hi, int n_max, unsigned long long& bad) {
+                                           float4 hi, const Rope4& rf, int n_max, unsigned long long& bad) {
   if (d.i < 0) return;
   const int dh = s.head_width;
   const int half = dh >> 1;
@@ -179,8 +197,7 @@ __device__ __forceinline__ void put_pairs4(const DevState& s, int p, const RowDs
   }
   float4 r0 = lo, r1 = hi;
   if (p < 2 && s.rope) {
-    const float4 c = *reinterpret_cast<const float4*>(static_cast<const float*>(s.rope_cos) + size_t(d.pos) * half + f);
-    const float4 sn = *reinterpret_cast<const float4*>(static_cast<const float*>(s.rope_sin) + size_t(d.pos) * half + f);
+    const float4 c = rf.c, sn = rf.sn;
     r0 = make_float4(lo.x * c.x - hi.x * sn.x, lo.y * c.y - hi.y * sn.y, lo.z * c.z - hi.z * sn.z,
                      lo.w * c.w - hi.w * sn.w);
     r1 = make_float4(hi.x * c.x + lo.x * sn.x, hi.y * c.y + lo.y * sn.y, hi.z * c.z + lo.z * sn.z,
@@ -651,8 +668,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + 4 * g + (r & 3)) * EPS + j * 32 + c32] = q[j][r];
   };
+  // where each quarter's rows land (lane c32: row c32 of quarter i), all four at
+  // once; the row's lanes fetch them by shuffle
+  RowDst mine[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mine[i] = row_dst(s, p, wrow0 + i * 32 + c32, M, n_max, per_seq_rows, bad_pos);
 #pragma unroll 1
   for (int i = 0; i < 4; ++i) {
+    // the quarter's rotary factors are loaded before its staging barrier
+    RowDst d[8];
+    Rope4 rf[8];
+    RowDst mi = mine[0];
+    switch (i) {
+      case 0: break;
+      case 1: mi = mine[1]; break;
+      case 2: mi = mine[2]; break;
+      default: mi = mine[3]; break;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int row = 4 * k + r4;
+      d[k] = RowDst{__shfl(mi.b, row, 64), __shfl(mi.i, row, 64), __shfl(mi.pos, row, 64)};
+      rf[k] = rope4(s, p, d[k], pair0);
+    }
     switch (i) {
       case 0: stage(acc[0]); break;
       case 1: stage(acc[1]); break;
@@ -660,15 +698,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       default: stage(acc[3]); break;
     }
     __syncthreads();
-    // lane c32 finds where row c32 of the quarter lands; the row's lanes fetch it by shuffle
-    const RowDst mine = row_dst(s, p, wrow0 + i * 32 + c32, M, n_max, per_seq_rows, bad_pos);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int row = 4 * k + r4;
-      const RowDst d{__shfl(mine.b, row, 64), __shfl(mine.i, row, 64), __shfl(mine.pos, row, 64)};
-      const float* er = ep + row * EPS + gi * 64 + c4;
-      put_pairs4(s, p, d, pair0, *reinterpret_cast<const float4*>(er), *reinterpret_cast<const float4*>(er + 32),
-                 n_max, bad);
+      const float* er = ep + (4 * k + r4) * EPS + gi * 64 + c4;
+      put_pairs4(s, p, d[k], pair0, *reinterpret_cast<const float4*>(er), *reinterpret_cast<const float4*>(er + 32),
+                 rf[k], n_max, bad);
     }
     __syncthreads();
   }
