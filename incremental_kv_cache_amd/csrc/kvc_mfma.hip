@@ -536,24 +536,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
-  // global -> LDS: thread copies 16 bytes at k-chunk lk of rows lrow + 32 i (i < 8)
-  const int lrow = tid >> 3;
-  const int lk = (tid & 7) * 8;
-  // element offsets of the thread's rows (32-bit: the dispatch checks M * D < 2^31):
-  // X rows lrow + 32 i (clamped to the last row); W rows of virtual columns
-  // lrow + 32 i, where odd i is the high half of even i's pairs (+ d_h / 2 rows)
-  const bf16_t* xg = x + lk;
-  const bf16_t* wg = weight_of(s, p) + lk;
-  int ao[8], bo[4];
+  // global -> LDS with the 16-byte direct loads: a tile (256 rows of 64
+  // elements, rows padded to GLD) is 2304 16-byte slots, slot q = 9 r + c
+  // holding elements 8 min(c, 7) .. of row r (c = 8 is the padding; it gets a
+  // copy of c = 7), and one wave instruction fills 64 consecutive slots, lane l
+  // slot 64 j + l (LDS byte 16 (64 j + l): the padded row-major layout).  Waves
+  // 0-1 fill the X tile (36 instructions), waves 2-3 the W tile; element
+  // offsets are 32-bit (the dispatch checks M * D < 2^31).
+  // W tile row v = 32 i + c (c < 32) is virtual column v: pair pair_base +
+  // 32 (i / 2) + c, its high feature (+ d_h / 2 rows) for odd i.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool fills_x = wave_u < 2;
+  const bf16_t* gsrc = fills_x ? x : weight_of(s, p);
+  int off[18];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ao[i] = min(m0 + lrow + 32 * i, M - 1) * D;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int vpair = pair_base + 32 * k + lrow;
-    const int vh = vpair / half;
-    bo[k] = (vh * dh + (vpair - vh * half)) * D;
+  for (int j = 0; j < 18; ++j) {
+    const int q = (wave_u & 1) * 18 + j;  // instruction within the tile
+    const int slot = q * 64 + lane;
+    const int r = slot / 9, c = slot - r * 9;
+    int row_off;
+    if (fills_x) {
+      row_off = min(m0 + r, M - 1) * D;
+    } else {
+      const int i = r >> 5;
+      const int vpair = pair_base + 32 * (i >> 1) + (r & 31);
+      const int vh = vpair / half;
+      row_off = (vh * dh + (vpair - vh * half) + ((i & 1) ? half : 0)) * D;
+    }
+    off[j] = row_off + 8 * min(c, 7);
   }
-  const int hoff = half * D;
   f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -562,50 +573,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // the staged next K tile: 8 pieces of X and 8 of W per thread, in named
-  // registers (arrays or structs here are kept in scratch memory)
-  uint4 xa0, xa1, xa2, xa3, xa4, xa5, xa6, xa7, xb0, xb1, xb2, xb3, xb4, xb5, xb6, xb7;
-  constexpr int S = 32 * GLD / 8;  // uint4 between a thread's rows in LDS
-#define KVC_FETCH(T, k0)                                     \
-  do {                                                       \
-    T##a0 = *reinterpret_cast<const uint4*>(xg + ao[0] + (k0));   \
-    T##b0 = *reinterpret_cast<const uint4*>(wg + bo[0] + (k0));   \
-    T##a1 = *reinterpret_cast<const uint4*>(xg + ao[1] + (k0));   \
-    T##b1 = *reinterpret_cast<const uint4*>(wg + bo[0] + hoff + (k0));   \
-    T##a2 = *reinterpret_cast<const uint4*>(xg + ao[2] + (k0));   \
-    T##b2 = *reinterpret_cast<const uint4*>(wg + bo[1] + (k0));   \
-    T##a3 = *reinterpret_cast<const uint4*>(xg + ao[3] + (k0));   \
-    T##b3 = *reinterpret_cast<const uint4*>(wg + bo[1] + hoff + (k0));   \
-    T##a4 = *reinterpret_cast<const uint4*>(xg + ao[4] + (k0));   \
-    T##b4 = *reinterpret_cast<const uint4*>(wg + bo[2] + (k0));   \
-    T##a5 = *reinterpret_cast<const uint4*>(xg + ao[5] + (k0));   \
-    T##b5 = *reinterpret_cast<const uint4*>(wg + bo[2] + hoff + (k0));   \
-    T##a6 = *reinterpret_cast<const uint4*>(xg + ao[6] + (k0));   \
-    T##b6 = *reinterpret_cast<const uint4*>(wg + bo[3] + (k0));   \
-    T##a7 = *reinterpret_cast<const uint4*>(xg + ao[7] + (k0));   \
-    T##b7 = *reinterpret_cast<const uint4*>(wg + bo[3] + hoff + (k0));   \
-  } while (0)
-#define KVC_STASH(T, buf)                                                  \
-  do {                                                                     \
-    uint4* ad = reinterpret_cast<uint4*>(&As[buf][lrow * GLD + lk]);       \
-    uint4* bd = reinterpret_cast<uint4*>(&Bs[buf][lrow * GLD + lk]);       \
-    ad[0] = T##a0;                                                         \
-    ad[S] = T##a1;                                                         \
-    ad[2 * S] = T##a2;                                                     \
-    ad[3 * S] = T##a3;                                                     \
-    ad[4 * S] = T##a4;                                                     \
-    ad[5 * S] = T##a5;                                                     \
-    ad[6 * S] = T##a6;                                                     \
-    ad[7 * S] = T##a7;                                                     \
-    bd[0] = T##b0;                                                         \
-    bd[S] = T##b1;                                                         \
-    bd[2 * S] = T##b2;                                                     \
-    bd[3 * S] = T##b3;                                                     \
-    bd[4 * S] = T##b4;                                                     \
-    bd[5 * S] = T##b5;                                                     \
-    bd[6 * S] = T##b6;                                                     \
-    bd[7 * S] = T##b7;                                                     \
-  } while (0)
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  typedef __attribute__((address_space(1))) void glb_void_t;
+  // issue the K tile at k0 into buffer buf (completion: s_waitcnt vmcnt(0))
+  auto fetch = [&](int k0, int buf) {
+    bf16_t* dst = (fills_x ? &As[buf][0] : &Bs[buf][0]) + (wave_u & 1) * 18 * 64 * 8;
+#pragma unroll
+    for (int j = 0; j < 18; ++j)
+      __builtin_amdgcn_global_load_lds((glb_void_t*)(gsrc + off[j] + k0), (lds_void_t*)(dst + j * 64 * 8), 16, 0, 0);
+  };
   // fragments of one 16-wide step, double-buffered in registers: step ks + 1
   // is read from LDS while step ks's 16 MFMAs run
   Frag8 fa[2][4], fb[2][4];
@@ -634,21 +610,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // the next K tile is loaded into registers while this one is multiplied,
   // then written to the other LDS buffer
   const int ktiles = D / GBK;
-  KVC_FETCH(x, 0);
-  KVC_STASH(x, 0);
+  fetch(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   read_frags(0, 0, 0);
   for (int kt = 0; kt < ktiles; ++kt) {
     const int buf = kt & 1;
     const bool more = kt + 1 < ktiles;
-    if (more) KVC_FETCH(x, (kt + 1) * GBK);
+    // the other buffer was last read before the previous barrier
+    if (more) fetch((kt + 1) * GBK, buf ^ 1);
     multiply(buf);
-    if (more) KVC_STASH(x, buf ^ 1);
+    if (more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (more) read_frags(buf ^ 1, 0, 0);
   }
-#undef KVC_FETCH
-#undef KVC_STASH
   // epilogue, one 32-row quarter of the wave's tile at a time, through LDS (the
   // K-tile buffers are free now).  Lane (row r4, group gi, c4) then handles four
   // consecutive pairs of rows r4, r4 + 4, ..: 16 lanes cover one row's 64 pairs,
