@@ -704,13 +704,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 //
 // Softmax: base 2 with the scale folded into q; the running maximum is only
 // raised (and the accumulators rescaled) when a score exceeds it by more than
-// 2^8, so probabilities stay below 256 and most tiles skip the rescale.
+// 2^8, so probabilities stay below 256 and most tiles skip the rescale.  The
+// maximum is kept as a bf16 value and subtracted by the score MFMAs (a 1 in
+// the keys against -max in the queries), and the normaliser adds the
+// probabilities as rounded to bf16 for P V, so numerator and denominator
+// weight every key alike.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
   const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4_t*)(const_cast<bf16_t*>(p)));
   return __builtin_bit_cast(uint2, v);
+}
+
+// acc plus the eight bf16 values of f (packed dot products with ones)
+__device__ __forceinline__ float add_bf16x8(const Frag8& f, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.z), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, f.u.w), one, acc, false);
 }
 
 // WIN: sliding-window layer (ring storage, a lower key bound per query).
@@ -720,7 +734,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int KT = 64;
   static_assert(kMinBlockRows % KT == 0, "a key tile must stay inside one block");
   constexpr int LDK = DH + 8;   // K row stride: conflict-free 16-byte fragment reads
-  constexpr int LDV = DH + 16;  // V row stride: conflict-free transposing reads
+  constexpr int LDV = DH + 32;  // V row stride: conflict-free transposing reads (64 banks)
   constexpr int DSTEPS = DH / 16;
   constexpr int DTILES = DH / 32;
   constexpr int CPR = DH / 8;        // 16-byte pieces per row
@@ -796,6 +810,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  // Scores are taken against a reference maximum mref (0 until a key is seen,
+  // else m_run, a bf16 value): the matrix core subtracts it as one more
+  // 16-deep step with key feature 1 and query feature -mref.
+  float mref = 0.f;
+  Frag8 onek, mq;
+  onek.u = make_uint4(g == 0 ? 0x3f80u : 0u, 0u, 0u, 0u);
+  mq.u = make_uint4(0u, 0u, 0u, 0u);
   const int wave_limit_min = len + min(qt * 128 + wave * 32, n_b - 1);  // smallest limit in the wave
 
   // global -> register -> LDS staging: thread loads piece lch of rows lrow + RPI k
@@ -882,6 +903,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
+      st[kt] = mfma32(onek.v, mq.v, st[kt]);
 #pragma unroll
       for (int u = 0; u < DSTEPS; ++u) {
         Frag8 a;
@@ -906,8 +928,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[kt][r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    if (__any(tmax > m_run + kRescale)) {
-      const float m_new = fmaxf(m_run, tmax);
+    // tmax is relative to mref
+    if (__any(tmax + mref > m_run + kRescale)) {
+      const float m_new = float((__bf16)fmaxf(m_run, tmax + mref));
       const float corr = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
       l_run *= corr;
 #pragma unroll
@@ -915,16 +938,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] *= corr;
       m_run = m_new;
+      // this tile's scores were taken against the old reference
+      const float shift = (m_new == -INFINITY ? 0.f : m_new) - mref;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[kt][r] -= shift;
+      mref += shift;
+      mq.v[0] = g == 0 ? (__bf16)(-mref) : (__bf16)0.f;
     }
-    const float mref = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         // v_exp_f32 directly: probabilities below 2^-126 flush to zero
-        const float pr = __builtin_amdgcn_exp2f(st[kt][r] - mref);
-        st[kt][r] = pr;
-        l_run += pr;
+        st[kt][r] = __builtin_amdgcn_exp2f(st[kt][r]);
       }
     const bf16_t* vt = &Vs[buf][vlane];
 #pragma unroll
@@ -934,6 +962,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         Frag8 pb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb.v[e] = (__bf16)st[kt][8 * u + e];
+        // the normaliser adds the probabilities as rounded for P V
+        l_run = add_bf16x8(pb, l_run);
         // keys kt*32 + 16u + 4g + {0..3} and + {8..11} of feature t*32 + c32
         const int krow = (kt * 32 + 16 * u) * LDV;
 #pragma unroll
