@@ -60,14 +60,14 @@ SEED = 37
 MEASURED_TRAFFIC = {
     # attend_decode_bf16_kernel, headline decode (B=32, t=4096)
     "headline": {"source": "decode", "fetch_kib": 1048893.0, "fetch_scale": 2.0, "write_kib": 512.0, "write_scale": 1.0,
-                 "kernel_source_sha256": "326af22b59cdcff5ed1ee472ef59aa78d77f180a1bc9a813c6f2dea56d548c71"},
+                 "kernel_source_sha256": "33632cb638dacae9e5a0927280e6032fd103a8e5312bb67e58d63950f7eb2599"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
-    "chunk": {"source": "mfma", "fetch_kib": 299343.8, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
-              "kernel_source_sha256": "365518ebfa9cfa8aff57b34d9542484fb702dcc184e0507b1da02aecef592735"},
+    "chunk": {"source": "mfma", "fetch_kib": 299400.3, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
+              "kernel_source_sha256": "3ef274e9b24f4f0cd0825cd0ff24d90e4775e274d0c0a06880284c1b224001d6"},
     # attend_flash_kernel, suffix chunk (B=8, n=512)
-    "chunk_attention": {"source": "mfma", "fetch_kib": 546923.4, "fetch_scale": 2.0, "write_kib": 65542.6,
+    "chunk_attention": {"source": "mfma", "fetch_kib": 553351.5, "fetch_scale": 2.0, "write_kib": 65541.9,
                         "write_scale": 1.0,
-                        "kernel_source_sha256": "365518ebfa9cfa8aff57b34d9542484fb702dcc184e0507b1da02aecef592735"},
+                        "kernel_source_sha256": "3ef274e9b24f4f0cd0825cd0ff24d90e4775e274d0c0a06880284c1b224001d6"},
 }
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
                   "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}
