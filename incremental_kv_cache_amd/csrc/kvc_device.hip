@@ -649,6 +649,10 @@ const char* dev_error_string(int code) { return hipGetErrorString(hipError_t(cod
 
 int dev_current_device(int* device) { return int(hipGetDevice(device)); }
 
+int dev_compute_units(int device, int* units) {
+  return int(hipDeviceGetAttribute(units, hipDeviceAttributeMultiprocessorCount, device));
+}
+
 int dev_malloc(void** p, size_t bytes) { return int(hipMalloc(p, bytes ? bytes : 16)); }
 
 void dev_free(void* p) {

@@ -65,6 +65,7 @@ struct kvc_cache {
   double rope_base;
   kvc_pos_mode pos_mode;
   int device;
+  int compute_units = 256;
   // host copy of the committed state
   std::vector<int32_t> len, next_pos;
   std::vector<int32_t> held;  // window (ring) caches: oldest row each sequence still holds
@@ -118,11 +119,14 @@ void kvc::build_chunk_order(ChunkOrder* o, int batch, int n_max, const int32_t* 
   o->count = int32_t(w.size());
 }
 
-void kvc::build_seq_order(SeqOrder* o, int batch, const int32_t* len) {
+void kvc::build_seq_order(SeqOrder* o, int batch, const int32_t* len, int per_round) {
   o->count = 0;
   if (batch > kMaxSeqOrder) return;
   for (int b = 0; b < batch; ++b) o->seq[b] = b;
   std::stable_sort(o->seq, o->seq + batch, [&](int32_t a, int32_t c) { return len[a] > len[c]; });
+  per_round = std::max(per_round, 1);
+  for (int r0 = per_round; r0 < batch; r0 += 2 * per_round)
+    std::reverse(o->seq + r0, o->seq + std::min(batch, r0 + per_round));
   o->count = batch;
 }
 
@@ -510,7 +514,9 @@ kvc_status compute_stages(kvc_cache* c, const void* x, int n_max, const int32_t*
   void* heads = s.wo ? s.merged : out;
   profile_mark(c, KVC_STAGE_ATTEND, 0);
   if (decode) {
-    build_seq_order(&c->seq_order, c->batch, c->len.data());
+    // one round: the sequences whose workgroups put one on every compute unit
+    const int qpw = decode_heads_per_block(c->dtype, c->head_width, c->heads / c->kv_heads);
+    build_seq_order(&c->seq_order, c->batch, c->len.data(), c->compute_units / (c->heads / qpw));
     rc = dev_attend_decode(s, c->seq_order, heads);
   } else {
     build_chunk_order(&c->order, c->batch, n_max, c->len.data(), per_seq ? n_rows : nullptr);
@@ -712,6 +718,7 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
     for (int blk = pool_blocks - 1; blk >= 0; --blk) c->free_blocks.push_back(blk);
   }
   int rc = dev_current_device(&c->device);
+  if (!rc) rc = dev_compute_units(c->device, &c->compute_units);
   if (rc) {
     free_cache(c);
     return device_fail(rc, "hipGetDevice");

@@ -106,6 +106,7 @@ struct DevState {
 // dev_error_string() describes the last one.
 const char* dev_error_string(int code);
 int dev_current_device(int* device);
+int dev_compute_units(int device, int* units);
 int dev_malloc(void** p, size_t bytes);
 void dev_free(void* p);
 int dev_host_malloc(void** p, size_t bytes);
@@ -142,16 +143,18 @@ int dev_copy_seq_rows(const DevState& s, int dst_seq, int src_seq, int rows);
 // Pipeline stages.  n_max: rows per sequence of this call (1 for decode);
 // per_seq_rows: 0 = every sequence has n_max rows, 1 = rows[] holds them.
 int dev_project(const DevState& s, const void* x, int n_max, int per_seq_rows);
-// Sequences of a decode call with the most retained rows first: the bf16
-// split-K attention deals its workgroups out in this order so that the longest
-// lanes start early (ragged batches).  count is 0 when the batch exceeds the
-// table (sequence order).
+// Sequences of a decode call with the most retained rows first, dealt out in
+// rounds of per_round sequences (as many as one workgroup per compute unit
+// covers), every other round reversed: the bf16 split-K attention launches its
+// workgroups in this order, so the longest lanes start early and a unit that
+// takes a long lane in one round takes a short one in the next (ragged
+// batches).  count is 0 when the batch exceeds the table (sequence order).
 constexpr int kMaxSeqOrder = 256;
 struct SeqOrder {
   int32_t count;
   int32_t seq[kMaxSeqOrder];
 };
-void build_seq_order(SeqOrder* o, int batch, const int32_t* len);
+void build_seq_order(SeqOrder* o, int batch, const int32_t* len, int per_round);
 int dev_attend_decode(const DevState& s, const SeqOrder& order, void* out);
 int dev_merge_decode(const DevState& s, void* out);
 // Work items of the bf16 chunk attention kernel: one per (sequence, tile of

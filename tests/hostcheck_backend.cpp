@@ -16,6 +16,10 @@ int dev_current_device(int* device) {
   *device = -1;
   return 0;
 }
+int dev_compute_units(int, int* units) {
+  *units = 256;
+  return 0;
+}
 int dev_malloc(void** p, size_t bytes) {
   *p = std::aligned_alloc(256, (bytes + 255) & ~size_t(255));
   return *p ? 0 : 2;
@@ -211,9 +215,9 @@ extern "C" int kvc_test_chunk_order(int batch, int n_max, const int32_t* len, co
   for (int k = 0; k < o.count; ++k) items[k] = o.item[k];
   return o.count;
 }
-extern "C" int kvc_test_seq_order(int batch, const int32_t* len, int32_t* seq) {
+extern "C" int kvc_test_seq_order(int batch, const int32_t* len, int per_round, int32_t* seq) {
   kvc::SeqOrder o;
-  kvc::build_seq_order(&o, batch, len);
+  kvc::build_seq_order(&o, batch, len, per_round);
   for (int k = 0; k < o.count; ++k) seq[k] = o.seq[k];
   return o.count;
 }

@@ -287,13 +287,24 @@ def test_chunk_work_order_lists_every_item_heaviest_first(lib):
 
 def test_decode_sequence_order_longest_first(lib):
     """The decode attention's sequence order: most retained rows first, ties in
-    sequence order; a batch larger than the table keeps sequence order."""
+    sequence order, dealt in rounds of per_round sequences with every other
+    round reversed (a unit that takes a long lane in one round takes a short one
+    in the next); a batch larger than the table keeps sequence order."""
     la, lp = _i32([3, 9, 9, 0, 4])
     seq = np.zeros(256, np.int32)
-    n = lib.kvc_test_seq_order(5, lp, seq.ctypes.data_as(C.POINTER(C.c_int32)))
-    assert n == 5 and list(seq[:5]) == [1, 2, 4, 0, 3]
+    sp = seq.ctypes.data_as(C.POINTER(C.c_int32))
+    for per_round in (1, 5, 8):
+        assert lib.kvc_test_seq_order(5, lp, per_round, sp) == 5 and list(seq[:5]) == [1, 2, 4, 0, 3]
+    assert lib.kvc_test_seq_order(5, lp, 2, sp) == 5 and list(seq[:5]) == [1, 2, 0, 4, 3]
+    # 32 sequences in rounds of 8 (32 heads on 256 units): rank sums per unit even out
+    lens = np.random.default_rng(5).permutation(np.arange(1, 33) * 100)
+    _, lp32 = _i32(lens)
+    assert lib.kvc_test_seq_order(32, lp32, 8, sp) == 32
+    ranks = np.argsort(np.argsort(-lens))[seq[:32]]
+    assert list(ranks) == list(range(8)) + list(range(15, 7, -1)) + list(range(16, 24)) + list(range(31, 23, -1))
+    assert len({int(ranks[k] + ranks[8 + k] + ranks[16 + k] + ranks[24 + k]) for k in range(8)}) == 1
     big, bp = _i32(np.arange(300))
-    assert lib.kvc_test_seq_order(300, bp, seq.ctypes.data_as(C.POINTER(C.c_int32))) == 0
+    assert lib.kvc_test_seq_order(300, bp, 8, sp) == 0
 
 
 # ------------------------------------------------------------- session ----
