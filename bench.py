@@ -62,12 +62,12 @@ MEASURED_TRAFFIC = {
     "headline": {"source": "decode", "fetch_kib": 1048893.0, "fetch_scale": 2.0, "write_kib": 512.0, "write_scale": 1.0,
                  "kernel_source_sha256": "33632cb638dacae9e5a0927280e6032fd103a8e5312bb67e58d63950f7eb2599"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
-    "chunk": {"source": "mfma", "fetch_kib": 299400.3, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
-              "kernel_source_sha256": "3ef274e9b24f4f0cd0825cd0ff24d90e4775e274d0c0a06880284c1b224001d6"},
+    "chunk": {"source": "mfma", "fetch_kib": 299467.2, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
+              "kernel_source_sha256": "5293d7714c44f5cca9fd6fbcc1831444a182ca29b10810e4186cc451f33f90ec"},
     # attend_flash_kernel, suffix chunk (B=8, n=512)
-    "chunk_attention": {"source": "mfma", "fetch_kib": 553351.5, "fetch_scale": 2.0, "write_kib": 65541.9,
+    "chunk_attention": {"source": "mfma", "fetch_kib": 556104.6, "fetch_scale": 2.0, "write_kib": 65544.9,
                         "write_scale": 1.0,
-                        "kernel_source_sha256": "3ef274e9b24f4f0cd0825cd0ff24d90e4775e274d0c0a06880284c1b224001d6"},
+                        "kernel_source_sha256": "5293d7714c44f5cca9fd6fbcc1831444a182ca29b10810e4186cc451f33f90ec"},
 }
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
                   "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}

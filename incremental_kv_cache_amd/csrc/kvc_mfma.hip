@@ -499,8 +499,9 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT
 // 256-thread workgroup per compute unit, each wave a 128 x 128 quarter held in
 // sixteen 32x32 accumulators, so a 16-wide step reads 8 fragments from LDS for
 // 16 MFMAs.  The 64-wide K tiles of X and W are double-buffered in LDS
-// (144 KB): the next tile is loaded into registers while the current one is
-// multiplied, then written to the other buffer, one barrier per tile.
+// (144 KB): the next tile goes straight from global memory into the other
+// buffer by 16-byte direct loads while the current one is multiplied, one
+// wait and barrier per tile.
 // Columns: block virtual column v holds pair pair_base + 32 (v / 64) + v % 32,
 // low feature for (v / 32) even, high feature for odd, so a wave's
 // n-subtiles 2 gi and 2 gi + 1 hold the two halves of the same 32 pairs.
@@ -598,17 +599,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
       const int cur = ks & 1;
+      // four MFMAs, the next step's fragment reads, then the other twelve: the
+      // reads are issued after this step's operands are known to be in
+      // registers, so no wait covers them until the next step
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[0][j] = mfma32(fa[cur][0].v, fb[cur][j].v, acc[0][j]);
+      __builtin_amdgcn_sched_barrier(0);
       if (ks + 1 < GBK / 16) read_frags(buf, ks + 1, cur ^ 1);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 1; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[cur][i].v, fb[cur][j].v, acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // the next K tile is loaded into registers while this one is multiplied,
-  // then written to the other LDS buffer
+  // the next K tile streams into the other LDS buffer while this one is
+  // multiplied
   const int ktiles = D / GBK;
   fetch(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
