@@ -576,12 +576,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   typedef __attribute__((address_space(3))) void lds_void_t;
   typedef __attribute__((address_space(1))) void glb_void_t;
-  // issue the K tile at k0 into buffer buf (completion: s_waitcnt vmcnt(0))
-  auto fetch = [&](int k0, int buf) {
+  // load instruction j of the K tile at k0 into buffer buf (completion: s_waitcnt vmcnt(0))
+  auto fetch_one = [&](int j, int k0, int buf) {
     bf16_t* dst = (fills_x ? &As[buf][0] : &Bs[buf][0]) + (wave_u & 1) * 18 * 64 * 8;
+    __builtin_amdgcn_global_load_lds((glb_void_t*)(gsrc + off[j] + k0), (lds_void_t*)(dst + j * 64 * 8), 16, 0, 0);
+  };
+  auto fetch = [&](int k0, int buf) {
 #pragma unroll
-    for (int j = 0; j < 18; ++j)
-      __builtin_amdgcn_global_load_lds((glb_void_t*)(gsrc + off[j] + k0), (lds_void_t*)(dst + j * 64 * 8), 16, 0, 0);
+    for (int j = 0; j < 18; ++j) fetch_one(j, k0, buf);
   };
   // fragments of one 16-wide step, double-buffered in registers: step ks + 1
   // is read from LDS while step ks's 16 MFMAs run
@@ -595,13 +597,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       fb[slot][i].u = *reinterpret_cast<const uint4*>(br + i * 32 * GLD);
     }
   };
-  auto multiply = [&](int buf) {
+  // The 18 load instructions of the next K tile (at k_next, into buffer
+  // next_buf) go out one after each of the first 18 of the last twelve MFMAs
+  // of steps 0 and 1, so the wave keeps the matrix core busy while the load
+  // path takes them.
+  auto multiply = [&](int buf, int k_next, int next_buf) {
 #pragma unroll
     for (int ks = 0; ks < GBK / 16; ++ks) {
       const int cur = ks & 1;
-      // four MFMAs, the next step's fragment reads, then the other twelve: the
-      // reads are issued after this step's operands are known to be in
-      // registers, so no wait covers them until the next step
+      // this step's fragments in registers (an LDS-only wait: lgkmcnt(0),
+      // vmcnt and expcnt left alone), four MFMAs, the next step's fragment
+      // reads, then the other twelve: no wait covers those reads until the
+      // next step
+      __builtin_amdgcn_s_waitcnt(0xC07F);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[0][j] = mfma32(fa[cur][0].v, fb[cur][j].v, acc[0][j]);
       __builtin_amdgcn_sched_barrier(0);
@@ -610,8 +618,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int i = 1; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(fa[cur][i].v, fb[cur][j].v, acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int j = 0; j < 4; ++j) {
+          acc[i][j] = mfma32(fa[cur][i].v, fb[cur][j].v, acc[i][j]);
+          const int d = ks * 12 + (i - 1) * 4 + j;
+          if (d < 18) fetch_one(d, k_next, next_buf);
+          __builtin_amdgcn_sched_barrier(0);
+        }
     }
   };
   // the next K tile streams into the other LDS buffer while this one is
@@ -623,13 +635,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   read_frags(0, 0, 0);
   for (int kt = 0; kt < ktiles; ++kt) {
     const int buf = kt & 1;
-    const bool more = kt + 1 < ktiles;
-    // the other buffer was last read before the previous barrier
-    if (more) fetch((kt + 1) * GBK, buf ^ 1);
-    multiply(buf);
-    if (more) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the next tile into the other buffer, last read before the previous
+    // barrier (after the last tile the last one is loaded again, unread)
+    multiply(buf, min(kt + 1, ktiles - 1) * GBK, buf ^ 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (more) read_frags(buf ^ 1, 0, 0);
+    read_frags(buf ^ 1, 0, 0);
   }
   // epilogue, one 32-row quarter of the wave's tile at a time, through LDS (the
   // K-tile buffers are free now).  Lane (row r4, group gi, c4) then handles four
