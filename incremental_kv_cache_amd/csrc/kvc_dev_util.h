@@ -17,13 +17,9 @@ using bf16_t = uint16_t;
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
-// Round-to-nearest-even float -> bfloat16 (NaN kept quiet).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return bf16_t(u >> 16);
-}
+// Round-to-nearest-even float -> bfloat16, a NaN staying a NaN (gfx950
+// converts two values per v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 template <typename T> struct Acc;
 template <> struct Acc<double> { using type = double; };

@@ -180,7 +180,10 @@ __device__ __forceinline__ void put_pairs4(const DevState& s, int p, const RowDs
   const int half = dh >> 1;
   const int h = pair0 / half;
   const int f = pair0 - h * half;
+  // a non-finite value makes the sum non-finite (a sum that only overflows
+  // sends the four values through the exact checks, which then find none)
   auto note = [&](const float4& v, size_t flat) {
+    if (isfinite((v.x + v.y) + (v.z + v.w))) return;
     if (!isfinite(v.x)) bad = min(bad, (unsigned long long)flat);
     else if (!isfinite(v.y)) bad = min(bad, (unsigned long long)(flat + 1));
     else if (!isfinite(v.z)) bad = min(bad, (unsigned long long)(flat + 2));
@@ -906,15 +909,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int it = it_first; it < ntiles; ++it) {
     const int j0 = it * KT;
     const int buf = (it - it_first) & 1;
-    // the other buffer was last read before the previous barrier: fill it now
-    // (contiguous tiles land in registers first and are written after this tile)
     const bool more = it + 1 < ntiles;
     const bool staged = more && contiguous(j0 + KT);
-    if (staged) {
-      fetch(j0 + KT);
-    } else if (more) {
-      fetch_mixed(j0 + KT, buf ^ 1);
-    }
 
     f32x16_t st[2];
 #pragma unroll
@@ -928,6 +924,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         a.u = *reinterpret_cast<const uint4*>(&Ks[buf][(kt * 32 + c32) * LDK + 16 * u + 8 * g]);
         st[kt] = mfma32(a.v, qf[u].v, st[kt]);
       }
+    }
+    // the other buffer was last read before the previous barrier: fill it now,
+    // with the score MFMAs already issued (contiguous tiles land in registers
+    // first and are written after this tile)
+    __builtin_amdgcn_sched_barrier(0);
+    if (staged) {
+      fetch(j0 + KT);
+    } else if (more) {
+      fetch_mixed(j0 + KT, buf ^ 1);
     }
     // causal mask only where the tile reaches past the wave's first query, the
     // window's lower edge only where the tile starts below the wave's last one
