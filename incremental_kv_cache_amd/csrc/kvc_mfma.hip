@@ -502,9 +502,9 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT
 // 256-thread workgroup per compute unit, each wave a 128 x 128 quarter held in
 // sixteen 32x32 accumulators, so a 16-wide step reads 8 fragments from LDS for
 // 16 MFMAs.  The 64-wide K tiles of X and W are double-buffered in LDS
-// (144 KB): the next tile goes straight from global memory into the other
-// buffer by 16-byte direct loads while the current one is multiplied, one
-// wait and barrier per tile.
+// (144 KB) and go straight from global memory into their buffer by 16-byte
+// direct loads while the tile before is multiplied, one wait and barrier per
+// tile.
 // Columns: block virtual column v holds pair pair_base + 32 (v / 64) + v % 32,
 // low feature for (v / 32) even, high feature for odd, so a wave's
 // n-subtiles 2 gi and 2 gi + 1 hold the two halves of the same 32 pairs.
@@ -600,51 +600,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       fb[slot][i].u = *reinterpret_cast<const uint4*>(br + i * 32 * GLD);
     }
   };
-  // The 18 load instructions of the next K tile (at k_next, into buffer
-  // next_buf) go out one after each of the first 18 of the last twelve MFMAs
-  // of steps 0 and 1, so the wave keeps the matrix core busy while the load
-  // path takes them.
-  auto multiply = [&](int buf, int k_next, int next_buf) {
+  // One 16-wide step: an LDS-only wait (lgkmcnt(0), vmcnt and expcnt left
+  // alone) for its operands in slot cur, four MFMAs, the next step's fragments
+  // (K tile in buffer rbuf, step rks, into slot cur ^ 1), then the other twelve
+  // MFMAs with up to twelve load instructions of a K tile (dma_first ..., at k0
+  // into buffer dbuf) between them: the load path takes loads far slower than a
+  // wave issues them, and a wave stuck issuing loads issues no MFMAs.
+  auto step = [&](int cur, int rbuf, int rks, int dma_first, int dma_count, int dk, int dbuf) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
 #pragma unroll
-    for (int ks = 0; ks < GBK / 16; ++ks) {
-      const int cur = ks & 1;
-      // this step's fragments in registers (an LDS-only wait: lgkmcnt(0),
-      // vmcnt and expcnt left alone), four MFMAs, the next step's fragment
-      // reads, then the other twelve: no wait covers those reads until the
-      // next step
-      __builtin_amdgcn_s_waitcnt(0xC07F);
+    for (int j = 0; j < 4; ++j) acc[0][j] = mfma32(fa[cur][0].v, fb[cur][j].v, acc[0][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(rbuf, rks, cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[0][j] = mfma32(fa[cur][0].v, fb[cur][j].v, acc[0][j]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ks + 1 < GBK / 16) read_frags(buf, ks + 1, cur ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int i = 1; i < 4; ++i)
 #pragma unroll
-      for (int i = 1; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[i][j] = mfma32(fa[cur][i].v, fb[cur][j].v, acc[i][j]);
-          const int d = ks * 12 + (i - 1) * 4 + j;
-          if (d < 18) fetch_one(d, k_next, next_buf);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    }
+      for (int j = 0; j < 4; ++j) {
+        acc[i][j] = mfma32(fa[cur][i].v, fb[cur][j].v, acc[i][j]);
+        const int m = (i - 1) * 4 + j;
+        if (m < dma_count) fetch_one(dma_first + m, dk, dbuf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
   };
-  // the next K tile streams into the other LDS buffer while this one is
-  // multiplied
+  // Steps 0-2 of K tile kt run before the tile's barrier and step 3 after it,
+  // so the next tile's first fragments are read under step 3's MFMAs; tile
+  // kt + 2 starts loading into tile kt's buffer in step 3 (12 instructions) and
+  // step 0 of the next tile (6), and is waited for four steps later.  Past the
+  // last tile the last one is loaded again (never read).
   const int ktiles = D / GBK;
+  auto k_of = [&](int t) { return min(t, ktiles - 1) * GBK; };
   fetch(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   read_frags(0, 0, 0);
   for (int kt = 0; kt < ktiles; ++kt) {
     const int buf = kt & 1;
-    // the next tile into the other buffer, last read before the previous
-    // barrier (after the last tile the last one is loaded again, unread)
-    multiply(buf, min(kt + 1, ktiles - 1) * GBK, buf ^ 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (kt == 0) {
+      step(0, buf, 1, 0, 12, k_of(1), buf ^ 1);
+      step(1, buf, 2, 12, 6, k_of(1), buf ^ 1);
+    } else {
+      step(0, buf, 1, 12, 6, k_of(kt + 1), buf ^ 1);
+      step(1, buf, 2, 0, 0, 0, 0);
+    }
+    step(0, buf, 3, 0, 0, 0, 0);
+    // tile kt + 1 in LDS, and this wave's reads of tile kt done (its buffer is
+    // reloaded after the barrier)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    read_frags(buf ^ 1, 0, 0);
+    step(1, buf ^ 1, 0, 0, 12, k_of(kt + 2), buf);
   }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
   // epilogue, one 32-row quarter of the wave's tile at a time, through LDS (the
   // K-tile buffers are free now).  Lane (row r4, group gi, c4) then handles four
   // consecutive pairs of rows r4, r4 + 4, ..: 16 lanes cover one row's 64 pairs,
