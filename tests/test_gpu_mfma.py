@@ -205,3 +205,34 @@ def test_split_decode_projection(D, heads, kv_heads, B, wo):
         k, v, _ = K.kvc_snapshot(cache, b)
         assert_parity(storage_f64(k, "bf16"), full["keys"], "bf16", f"keys {b}")
         assert_parity(storage_f64(v, "bf16"), full["values"], "bf16", f"values {b}")
+
+
+@pytest.mark.parametrize("which", ["key", "value"])
+def test_wide_projection_reports_first_nonfinite_flat_index(which):
+    """The 2048-row chunk projection (wide MFMA kernel): one W_k (then W_v) output row
+    of 3e38 makes feature 5 of every row's key (value) overflow.  The call fails with
+    the first non-finite flat index, 5 (sequence 0, head 0, row 0; Chapter 37 cache
+    validation reports the first offending element in flat order), and the cache is
+    unchanged; the same weights with that row restored project and commit."""
+    import torch
+    B, n, H, dh = 8, 256, 2, 128
+    D = H * dh
+    ws = synth.decode_weights(91, D, D ** -0.5, "bf16")
+    idx = {"key": 1, "value": 2}[which]
+    bad_w = ws[idx][1].copy()
+    bad_w[5, :] = 3e38
+    tensors = [to_device(s, "bf16") for s, _ in ws]
+    tensors[idx] = to_device(synth.quantize(bad_w, "bf16")[0], "bf16")
+    layer = K.kvc_layer_create(K.kvc_params_create(*tensors), H, K.KVC_POS_ROPE, 10000.0, 512)
+    cache = K.kvc_cache_create(layer, B, 512, max_chunk_rows=n)
+    x_dev, _ = hidden(92, synth.STREAM_X, B, n, D, "bf16")
+    with pytest.raises(K.KvcError) as ei:
+        K.kvc_continue_chunk(layer, cache, x_dev)
+    assert ei.value.name == f"KVC_ERR_NONFINITE_{which.upper()}"
+    assert ei.value.detail["flat_index"] == 5
+    assert [a.tolist() for a in K.kvc_lengths(cache)] == [[0] * B, [0] * B]
+    good = K.kvc_layer_create(K.kvc_params_create(*[to_device(s, "bf16") for s, _ in ws]), H, K.KVC_POS_ROPE,
+                              10000.0, 512)
+    cache = K.kvc_cache_create(good, B, 512, max_chunk_rows=n)
+    out, _ = K.kvc_continue_chunk(good, cache, x_dev)
+    assert torch.isfinite(out).all() and [a.tolist() for a in K.kvc_lengths(cache)] == [[n] * B, [n] * B]
