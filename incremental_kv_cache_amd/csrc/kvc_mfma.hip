@@ -499,9 +499,10 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT
 
 // ------------------------------------------------------- wide tiled GEMM --
 // Many bf16 rows (suffix chunks, prefill): 256 x 256 output tiles, one
-// 256-thread workgroup per compute unit, each wave a 128 x 128 quarter held in
-// sixteen 32x32 accumulators, so a 16-wide step reads 8 fragments from LDS for
-// 16 MFMAs.  The 64-wide K tiles of X and W are double-buffered in LDS
+// 512-thread workgroup per compute unit (two waves per SIMD, so one wave's
+// waits and epilogue instructions overlap the other's MFMAs), each wave a
+// 128 x 64 block held in eight 32x32 accumulators, so a 16-wide step reads 6
+// fragments from LDS for 8 MFMAs.  The 64-wide K tiles of X and W are double-buffered in LDS
 // (144 KB) and go straight from global memory into their buffer by 16-byte
 // direct loads while the tile before is multiplied, one wait and barrier per
 // tile.
@@ -511,9 +512,9 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT
 // Tile order: consecutive tile ids run on one XCD (blocks are dealt to the
 // eight XCDs in turn) and walk 4 row tiles per column step, so the 32 tiles an
 // XCD runs at once share their X and W tiles through its L2.
-constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8, GGROUP = 4;
+constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8, GGROUP = 4, GWAVES = 8;
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void project_wide_kernel(
+__global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void project_wide_kernel(
     DevState s, const bf16_t* __restrict__ x, int M, int n_max, int per_seq_rows, int proj_first, int m_tiles,
     int n_tiles) {
   __shared__ __attribute__((aligned(16))) bf16_t As[2][GBM * GLD];
@@ -536,7 +537,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;  // rows 128 wm .., columns 64 wn ..
   const int g = lane >> 5;
   const int c32 = lane & 31;
 
@@ -545,17 +546,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // holding elements 8 min(c, 7) .. of row r (c = 8 is the padding; it gets a
   // copy of c = 7), and one wave instruction fills 64 consecutive slots, lane l
   // slot 64 j + l (LDS byte 16 (64 j + l): the padded row-major layout).  Waves
-  // 0-1 fill the X tile (36 instructions), waves 2-3 the W tile; element
-  // offsets are 32-bit (the dispatch checks M * D < 2^31).
+  // 0-3 fill the X tile (36 instructions, 9 each), waves 4-7 the W tile;
+  // element offsets are 32-bit (the dispatch checks M * D < 2^31).
   // W tile row v = 32 i + c (c < 32) is virtual column v: pair pair_base +
   // 32 (i / 2) + c, its high feature (+ d_h / 2 rows) for odd i.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const bool fills_x = wave_u < 2;
+  const bool fills_x = wave_u < 4;
   const bf16_t* gsrc = fills_x ? x : weight_of(s, p);
-  int off[18];
+  constexpr int NDMA = 9;  // load instructions per wave and K tile
+  int off[NDMA];
 #pragma unroll
-  for (int j = 0; j < 18; ++j) {
-    const int q = (wave_u & 1) * 18 + j;  // instruction within the tile
+  for (int j = 0; j < NDMA; ++j) {
+    const int q = (wave_u & 3) * NDMA + j;  // instruction within the tile
     const int slot = q * 64 + lane;
     const int r = slot / 9, c = slot - r * 9;
     int row_off;
@@ -569,11 +571,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     off[j] = row_off + 8 * min(c, 7);
   }
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -581,52 +583,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   typedef __attribute__((address_space(1))) void glb_void_t;
   // load instruction j of the K tile at k0 into buffer buf (completion: s_waitcnt vmcnt(0))
   auto fetch_one = [&](int j, int k0, int buf) {
-    bf16_t* dst = (fills_x ? &As[buf][0] : &Bs[buf][0]) + (wave_u & 1) * 18 * 64 * 8;
+    bf16_t* dst = (fills_x ? &As[buf][0] : &Bs[buf][0]) + (wave_u & 3) * NDMA * 64 * 8;
     __builtin_amdgcn_global_load_lds((glb_void_t*)(gsrc + off[j] + k0), (lds_void_t*)(dst + j * 64 * 8), 16, 0, 0);
   };
   auto fetch = [&](int k0, int buf) {
 #pragma unroll
-    for (int j = 0; j < 18; ++j) fetch_one(j, k0, buf);
+    for (int j = 0; j < NDMA; ++j) fetch_one(j, k0, buf);
   };
   // fragments of one 16-wide step, double-buffered in registers: step ks + 1
   // is read from LDS while step ks's 16 MFMAs run
-  Frag8 fa[2][4], fb[2][4];
+  Frag8 fa[2][4], fb[2][2];
   auto read_frags = [&](int buf, int ks, int slot) {
     const bf16_t* ar = &As[buf][(wm * 128 + c32) * GLD + 8 * g + 16 * ks];
-    const bf16_t* br = &Bs[buf][(wn * 128 + c32) * GLD + 8 * g + 16 * ks];
+    const bf16_t* br = &Bs[buf][(wn * 64 + c32) * GLD + 8 * g + 16 * ks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[slot][i].u = *reinterpret_cast<const uint4*>(ar + i * 32 * GLD);
-      fb[slot][i].u = *reinterpret_cast<const uint4*>(br + i * 32 * GLD);
-    }
+    for (int i = 0; i < 4; ++i) fa[slot][i].u = *reinterpret_cast<const uint4*>(ar + i * 32 * GLD);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[slot][j].u = *reinterpret_cast<const uint4*>(br + j * 32 * GLD);
   };
   // One 16-wide step: an LDS-only wait (lgkmcnt(0), vmcnt and expcnt left
-  // alone) for its operands in slot cur, four MFMAs, the next step's fragments
-  // (K tile in buffer rbuf, step rks, into slot cur ^ 1), then the other twelve
-  // MFMAs with up to twelve load instructions of a K tile (dma_first ..., at k0
+  // alone) for its operands in slot cur, two MFMAs, the next step's fragments
+  // (K tile in buffer rbuf, step rks, into slot cur ^ 1), then the other six
+  // MFMAs with up to six load instructions of a K tile (dma_first ..., at k0
   // into buffer dbuf) between them: the load path takes loads far slower than a
   // wave issues them, and a wave stuck issuing loads issues no MFMAs.
   auto step = [&](int cur, int rbuf, int rks, int dma_first, int dma_count, int dk, int dbuf) {
     __builtin_amdgcn_s_waitcnt(0xC07F);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[0][j] = mfma32(fa[cur][0].v, fb[cur][j].v, acc[0][j]);
+    for (int j = 0; j < 2; ++j) acc[0][j] = mfma32(fa[cur][0].v, fb[cur][j].v, acc[0][j]);
     __builtin_amdgcn_sched_barrier(0);
     read_frags(rbuf, rks, cur ^ 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 1; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 2; ++j) {
         acc[i][j] = mfma32(fa[cur][i].v, fb[cur][j].v, acc[i][j]);
-        const int m = (i - 1) * 4 + j;
+        const int m = (i - 1) * 2 + j;
         if (m < dma_count) fetch_one(dma_first + m, dk, dbuf);
         __builtin_amdgcn_sched_barrier(0);
       }
   };
   // Steps 0-2 of K tile kt run before the tile's barrier and step 3 after it,
   // so the next tile's first fragments are read under step 3's MFMAs; tile
-  // kt + 2 starts loading into tile kt's buffer in step 3 (12 instructions) and
-  // step 0 of the next tile (6), and is waited for four steps later.  Past the
+  // kt + 2 starts loading into tile kt's buffer in step 3 (6 instructions) and
+  // step 0 of the next tile (3), and is waited for four steps later.  Past the
   // last tile the last one is loaded again (never read).
   const int ktiles = D / GBK;
   auto k_of = [&](int t) { return min(t, ktiles - 1) * GBK; };
@@ -637,10 +638,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int kt = 0; kt < ktiles; ++kt) {
     const int buf = kt & 1;
     if (kt == 0) {
-      step(0, buf, 1, 0, 12, k_of(1), buf ^ 1);
-      step(1, buf, 2, 12, 6, k_of(1), buf ^ 1);
+      step(0, buf, 1, 0, 6, k_of(1), buf ^ 1);
+      step(1, buf, 2, 6, 3, k_of(1), buf ^ 1);
     } else {
-      step(0, buf, 1, 12, 6, k_of(kt + 1), buf ^ 1);
+      step(0, buf, 1, 6, 3, k_of(kt + 1), buf ^ 1);
       step(1, buf, 2, 0, 0, 0, 0);
     }
     step(0, buf, 3, 0, 0, 0, 0);
@@ -648,26 +649,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // reloaded after the barrier)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    step(1, buf ^ 1, 0, 0, 12, k_of(kt + 2), buf);
+    step(1, buf ^ 1, 0, 0, 6, k_of(kt + 2), buf);
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
-  // epilogue, one 32-row quarter of the wave's tile at a time, through LDS (the
-  // K-tile buffers are free now).  Lane (row r4, group gi, c4) then handles four
-  // consecutive pairs of rows r4, r4 + 4, ..: 16 lanes cover one row's 64 pairs,
-  // with one rotary table load per factor and 16-byte stores.
-  constexpr int EPS = 128 + 4;  // staging row stride (floats)
+  // epilogue, one 32-row quarter of the wave's block at a time, through LDS
+  // (the K-tile buffers are free now).  The wave's 64 columns are the low and
+  // high features of 32 pairs; lane (row r8, c4) then handles four consecutive
+  // pairs of rows r8, r8 + 8, ..: 8 lanes cover one row's 32 pairs, with one
+  // rotary table load per factor and 16-byte stores.
+  constexpr int EPS = 64 + 4;  // staging row stride (floats)
+  static_assert(GWAVES * 32 * EPS * 4 <= 2 * GBM * GLD * 2, "staging fits the X buffers");
   float* ep = reinterpret_cast<float*>(&As[0][0]) + __builtin_amdgcn_readfirstlane(wave) * 32 * EPS;
   const int wrow0 = m0 + __builtin_amdgcn_readfirstlane(wm) * 128;
-  const int r4 = lane >> 4;
-  const int gi = (lane >> 3) & 1;
+  const int r8 = lane >> 3;
   const int c4 = (lane & 7) * 4;
-  const int pair0 = pair_base + (2 * __builtin_amdgcn_readfirstlane(wn) + gi) * 32 + c4;
+  const int pair0 = pair_base + __builtin_amdgcn_readfirstlane(wn) * 32 + c4;
   unsigned long long bad = kErrClear, bad_pos = kErrClear;
   // accumulators are only ever indexed by constants (a runtime index would move them to scratch)
-  auto stage = [&](const f32x16_t (&q)[4]) {
+  auto stage = [&](const f32x16_t (&q)[2]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) ep[(8 * (r >> 2) + 4 * g + (r & 3)) * EPS + j * 32 + c32] = q[j][r];
   };
@@ -679,8 +681,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll 1
   for (int i = 0; i < 4; ++i) {
     // the quarter's rotary factors are loaded before its staging barrier
-    RowDst d[8];
-    Rope4 rf[8];
+    RowDst d[4];
+    Rope4 rf[4];
     RowDst mi = mine[0];
     switch (i) {
       case 0: break;
@@ -689,8 +691,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       default: mi = mine[3]; break;
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int row = 4 * k + r4;
+    for (int k = 0; k < 4; ++k) {
+      const int row = 8 * k + r8;
       d[k] = RowDst{__shfl(mi.b, row, 64), __shfl(mi.i, row, 64), __shfl(mi.pos, row, 64)};
       rf[k] = rope4(s, p, d[k], pair0);
     }
@@ -702,8 +704,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float* er = ep + (4 * k + r4) * EPS + gi * 64 + c4;
+    for (int k = 0; k < 4; ++k) {
+      const float* er = ep + (8 * k + r8) * EPS + c4;
       put_pairs4(s, p, d[k], pair0, *reinterpret_cast<const float4*>(er), *reinterpret_cast<const float4*>(er + 32),
                  rf[k], n_max, bad);
     }
@@ -1093,7 +1095,7 @@ int mfma_project_t(const DevState& s, const XT* xb, int n_max, int per_seq_rows,
              s.head_width % 64 == 0 && int64_t(M) * s.model_width < (int64_t(1) << 31)) {
     const int m_tiles = (M + GBM - 1) / GBM;
     const int n_tiles = cols / GBN;
-    hipLaunchKernelGGL(project_wide_kernel, dim3(m_tiles * n_tiles), dim3(256), 0, st(s.stream), s,
+    hipLaunchKernelGGL(project_wide_kernel, dim3(m_tiles * n_tiles), dim3(64 * GWAVES), 0, st(s.stream), s,
                        reinterpret_cast<const bf16_t*>(xb), M, n_max, per_seq_rows, proj_first, m_tiles, n_tiles);
   } else {
     if (kv_cols % TBN != 0) return -1;
