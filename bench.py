@@ -62,12 +62,12 @@ MEASURED_TRAFFIC = {
     "headline": {"source": "decode", "fetch_kib": 1048893.0, "fetch_scale": 2.0, "write_kib": 512.0, "write_scale": 1.0,
                  "kernel_source_sha256": "33632cb638dacae9e5a0927280e6032fd103a8e5312bb67e58d63950f7eb2599"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
-    "chunk": {"source": "mfma", "fetch_kib": 299497.5, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
-              "kernel_source_sha256": "8f78b16ac57e0a6c4ee1bbae9953d8640ecf9ca25e0b1298be6c0133cd046c36"},
+    "chunk": {"source": "mfma", "fetch_kib": 299326.6, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
+              "kernel_source_sha256": "23c54f251291b3f1a5badbfc95d451a80ba0ee12ac81d03f367ca8fd54576de1"},
     # attend_flash_kernel, suffix chunk (B=8, n=512)
-    "chunk_attention": {"source": "mfma", "fetch_kib": 495395.9, "fetch_scale": 2.0, "write_kib": 65540.0,
+    "chunk_attention": {"source": "mfma", "fetch_kib": 498706.3, "fetch_scale": 2.0, "write_kib": 65540.1,
                         "write_scale": 1.0,
-                        "kernel_source_sha256": "8f78b16ac57e0a6c4ee1bbae9953d8640ecf9ca25e0b1298be6c0133cd046c36"},
+                        "kernel_source_sha256": "23c54f251291b3f1a5badbfc95d451a80ba0ee12ac81d03f367ca8fd54576de1"},
 }
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
                   "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}
