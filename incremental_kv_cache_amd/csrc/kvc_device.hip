@@ -311,12 +311,33 @@ __global__ __launch_bounds__(256) void commit_copy_kernel(DevState s, int n_max,
   // row by row: in a paged cache consecutive rows may sit in different blocks
   if ((dh * sizeof(T)) % 16 == 0) {
     const int per_row = int(dh * sizeof(T) / 16);
-    for (int idx = threadIdx.x; idx < nr * per_row; idx += blockDim.x) {
+    const int total = nr * per_row;
+    // four 16-byte pieces of K and of V loaded before any is stored (the
+    // compiler cannot move a load past a store to memory it cannot prove
+    // disjoint, which would leave one load in flight per thread); past the end
+    // a thread loads the last piece again and stores nothing
+    constexpr int THREADS = 256;
+    auto src = [&](int idx, const T* base) {
+      const int i = min(idx, total - 1);
+      const int k = i / per_row;
+      return reinterpret_cast<const uint4*>(base + size_t(k) * dh)[i - k * per_row];
+    };
+    auto put = [&](int idx, const uint4 kk, const uint4 vv) {
+      if (idx >= total) return;
       const int k = idx / per_row;
       const int c = idx - k * per_row;
       const size_t off = kv_offset(s, b, h, len + r0 + k);
-      reinterpret_cast<uint4*>(keys + off)[c] = reinterpret_cast<const uint4*>(sk + size_t(k) * dh)[c];
-      reinterpret_cast<uint4*>(values + off)[c] = reinterpret_cast<const uint4*>(sv + size_t(k) * dh)[c];
+      reinterpret_cast<uint4*>(keys + off)[c] = kk;
+      reinterpret_cast<uint4*>(values + off)[c] = vv;
+    };
+    for (int i0 = threadIdx.x; i0 < total; i0 += 4 * THREADS) {
+      const int i1 = i0 + THREADS, i2 = i1 + THREADS, i3 = i2 + THREADS;
+      const uint4 k0 = src(i0, sk), v0 = src(i0, sv), k1 = src(i1, sk), v1 = src(i1, sv);
+      const uint4 k2 = src(i2, sk), v2 = src(i2, sv), k3 = src(i3, sk), v3 = src(i3, sv);
+      put(i0, k0, v0);
+      put(i1, k1, v1);
+      put(i2, k2, v2);
+      put(i3, k3, v3);
     }
   } else {
     for (int idx = threadIdx.x; idx < nr * dh; idx += blockDim.x) {
