@@ -63,11 +63,11 @@ MEASURED_TRAFFIC = {
                  "kernel_source_sha256": "33632cb638dacae9e5a0927280e6032fd103a8e5312bb67e58d63950f7eb2599"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
     "chunk": {"source": "mfma", "fetch_kib": 299326.6, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
-              "kernel_source_sha256": "23c54f251291b3f1a5badbfc95d451a80ba0ee12ac81d03f367ca8fd54576de1"},
+              "kernel_source_sha256": "a6de2d829e74af27f3f3371b67d03e91ba815cc7c24ba0cbb874d06ad6adeafe"},
     # attend_flash_kernel, suffix chunk (B=8, n=512)
     "chunk_attention": {"source": "mfma", "fetch_kib": 498706.3, "fetch_scale": 2.0, "write_kib": 65540.1,
                         "write_scale": 1.0,
-                        "kernel_source_sha256": "23c54f251291b3f1a5badbfc95d451a80ba0ee12ac81d03f367ca8fd54576de1"},
+                        "kernel_source_sha256": "a6de2d829e74af27f3f3371b67d03e91ba815cc7c24ba0cbb874d06ad6adeafe"},
 }
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
                   "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}

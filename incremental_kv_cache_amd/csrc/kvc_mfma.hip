@@ -502,13 +502,14 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT
 // 512-thread workgroup per compute unit (two waves per SIMD, so one wave's
 // waits and epilogue instructions overlap the other's MFMAs), each wave a
 // 128 x 64 block held in eight 32x32 accumulators, so a 16-wide step reads 6
-// fragments from LDS for 8 MFMAs.  The 64-wide K tiles of X and W are double-buffered in LDS
-// (144 KB) and go straight from global memory into their buffer by 16-byte
-// direct loads while the tile before is multiplied, one wait and barrier per
-// tile.
+// fragments from LDS for 8 MFMAs.  The 64-wide K tiles of X and W are
+// double-buffered in LDS (144 KB) and go straight from global memory into
+// their buffer by 16-byte direct loads while the tile before is multiplied,
+// one wait and barrier per tile.
 // Columns: block virtual column v holds pair pair_base + 32 (v / 64) + v % 32,
-// low feature for (v / 32) even, high feature for odd, so a wave's
-// n-subtiles 2 gi and 2 gi + 1 hold the two halves of the same 32 pairs.
+// low feature for (v / 32) even, high feature for odd, so the two 32-column
+// subtiles of wave column wn (2 wn and 2 wn + 1) hold the two halves of the
+// same 32 pairs.
 // Tile order: consecutive tile ids run on one XCD (blocks are dealt to the
 // eight XCDs in turn) and walk 4 row tiles per column step, so the 32 tiles an
 // XCD runs at once share their X and W tiles through its L2.
