@@ -527,7 +527,7 @@ __global__ __launch_bounds__(256) void zero_kernel(uint4* p, size_t n16) {
 // encoding PE(p, 2i) = sin(p / 10000^(2i/D)), PE(p, 2i+1) = cos(same), with p =
 // next_position + i (prefix-reuse note, "Work and error over 27 cases": the toy
 // decoder's absolute sinusoidal positions; the angle is evaluated in double).
-// Block = one row (b, i).
+// Block = 256 columns of one row (b, i): blockIdx.x the row, blockIdx.y the columns.
 template <typename A, typename W>
 __global__ __launch_bounds__(256) void embed_kernel(DevState s, const int32_t* __restrict__ tokens,
                                                     const A* __restrict__ emb, int vocab, int sinusoidal, int n_max,
@@ -539,20 +539,20 @@ __global__ __launch_bounds__(256) void embed_kernel(DevState s, const int32_t* _
   if (i >= n_b) return;
   const int tok = tokens[row];
   if (tok < 0 || tok >= vocab) {
-    if (threadIdx.x == 0) flag_min(&s.err->token, (unsigned long long)row);
+    if (threadIdx.x == 0 && blockIdx.y == 0) flag_min(&s.err->token, (unsigned long long)row);
     return;
   }
   const int D = s.model_width;
+  const int j = blockIdx.y * blockDim.x + threadIdx.x;  // a row's columns are spread over blockIdx.y
+  if (j >= D) return;
   const double p = double(s.next_pos[b] + i);
-  for (int j = threadIdx.x; j < D; j += blockDim.x) {
-    A v = emb[size_t(tok) * D + j];
-    if (sinusoidal) {
-      const double ang = p / pow(10000.0, double(2 * (j >> 1)) / double(D));
-      v += A((j & 1) ? cos(ang) : sin(ang));
-    }
-    h[size_t(row) * D + j] = v;
-    if (x) x[size_t(row) * D + j] = from_acc<W>(v);
+  A v = emb[size_t(tok) * D + j];
+  if (sinusoidal) {
+    const double ang = p / pow(10000.0, double(2 * (j >> 1)) / double(D));
+    v += A((j & 1) ? cos(ang) : sin(ang));
   }
+  h[size_t(row) * D + j] = v;
+  if (x) x[size_t(row) * D + j] = from_acc<W>(v);
 }
 
 __device__ __forceinline__ double tanh_acc(double v) { return tanh(v); }
@@ -569,12 +569,12 @@ __global__ __launch_bounds__(256) void residual_kernel(DevState s, const A* __re
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
   if (i >= n_b) return;
   const int D = s.model_width;
-  for (int j = threadIdx.x; j < D; j += blockDim.x) {
-    const size_t k = size_t(row) * D + j;
-    const A v = h_in[k] + tanh_acc(a[k]);
-    h_out[k] = v;
-    if (x) x[k] = from_acc<W>(v);
-  }
+  const int j = blockIdx.y * blockDim.x + threadIdx.x;  // a row's columns are spread over blockIdx.y
+  if (j >= D) return;
+  const size_t k = size_t(row) * D + j;
+  const A v = h_in[k] + tanh_acc(a[k]);
+  h_out[k] = v;
+  if (x) x[k] = from_acc<W>(v);
 }
 
 inline hipStream_t st(void* s) { return static_cast<hipStream_t>(s); }
@@ -881,7 +881,7 @@ bool dev_has_kernels() { return true; }
 
 int dev_embed(const DevState& s, const int32_t* tokens, const void* embedding, int vocab, int sinusoidal,
               int n_max, int per_seq_rows, void* h, void* x) {
-  const dim3 grid(unsigned(s.batch) * unsigned(n_max));
+  const dim3 grid(unsigned(s.batch) * unsigned(n_max), unsigned(s.model_width + 255) / 256);
   switch (s.dtype) {
     case KVC_F64:
       hipLaunchKernelGGL((embed_kernel<double, double>), grid, dim3(256), 0, st(s.stream), s, tokens,
@@ -906,7 +906,7 @@ int dev_embed(const DevState& s, const int32_t* tokens, const void* embedding, i
 
 int dev_residual(const DevState& s, const void* h_in, const void* a, void* h_out, void* x, int n_max,
                  int per_seq_rows) {
-  const dim3 grid(unsigned(s.batch) * unsigned(n_max));
+  const dim3 grid(unsigned(s.batch) * unsigned(n_max), unsigned(s.model_width + 255) / 256);
   switch (s.dtype) {
     case KVC_F64:
       hipLaunchKernelGGL((residual_kernel<double, double>), grid, dim3(256), 0, st(s.stream), s,
