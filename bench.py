@@ -532,7 +532,7 @@ def main():
                     help="only run a plain device copy of this many MiB (5 times), to scale HBM byte counters")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1"}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

@@ -982,7 +982,7 @@ kvc_status session_call(kvc_session* S, const int32_t* tokens, int n_max, const 
     if (work) *work = w;
     return KVC_OK;
   }
-  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "this build has no device kernels");
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "library built without device kernels");
   const int per_seq = n_rows != nullptr;
   DevState& s0 = S->caches[0]->ds;
   int rc = 0;
@@ -1222,7 +1222,7 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
       }
     }
   }
-  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "this build has no device kernels");
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "library built without device kernels");
   kvc_work w{};
   w.position_min = INT32_MAX;
   w.position_max = -1;
@@ -1302,7 +1302,7 @@ kvc_status kvc_continue_chunk(const kvc_layer* layer, kvc_cache* cache, const vo
     if (work) *work = w;
     return KVC_OK;
   }
-  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "this build has no device kernels");
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "library built without device kernels");
   st = run_call(cache, x, n_max, n_rows, out, flags, false);
   if (st == KVC_OK && work) *work = w;
   return st;
@@ -1652,7 +1652,7 @@ kvc_status kvc_stream_read(const void* buf, int64_t bytes, void* sink, void* hip
     return fail_ea(KVC_ERR_BAD_ARGUMENT, kProbeUnitBytes, bytes,
                    "stream read needs a 16-byte aligned buffer and a positive multiple of %lld bytes",
                    static_cast<long long>(kProbeUnitBytes));
-  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "no device kernels in this build");
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "library built without device kernels");
   const int rc = dev_stream_read(buf, bytes, sink, hip_stream);
   if (rc) return device_fail(rc, "stream read launch");
   return KVC_OK;

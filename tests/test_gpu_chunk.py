@@ -141,7 +141,7 @@ def _toy_chunk(model, layers, caches, tokens):
 
 @pytest.mark.parametrize("seed", [7, 11, 23])
 def test_toy_decoder_prefix_reuse(seed):
-    """Prefix-reuse note, 27-case matrix rows that this build covers: append, edit first,
+    """Prefix-reuse note, the rows of its 27-case matrix covered here: append, edit first,
     edit fifth, edit eighth, shorten, the exercise, and the seeded edit.  Correct reuse is
     within 1e-12 of the float64 full recompute; projection rows are 6 x (len - cut); the
     stale-position control diverges whenever cut < 8."""

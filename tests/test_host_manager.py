@@ -250,7 +250,7 @@ def test_stream_read_argument_checks(lib):
     assert lib.kvc_stream_read(C.c_void_p(4100), 32768, sink, None) == capi.KVC_ERR_BAD_ARGUMENT
     d = lib.kvc_last_error().contents
     assert (d.expected, d.actual) == (32768, 32768)
-    assert lib.kvc_stream_read(buf, 65536, sink, None) == capi.KVC_ERR_DEVICE  # no kernels in this build
+    assert lib.kvc_stream_read(buf, 65536, sink, None) == capi.KVC_ERR_DEVICE  # host-check library: no kernels
 
 
 def _i32(v):
@@ -364,7 +364,7 @@ def test_session_layer_caches_are_read_only_views(lib):
 
 def test_session_request_checks(lib):
     """Session calls check rows, each layer's binding in layer order (detail.layer),
-    then cuts; a valid request reaches the launch point (no kernels in this build)."""
+    then cuts; a valid request reaches the launch point (the host-check library has no kernels)."""
     p0, p1 = params(lib), params(lib)
     l0, l1 = layer(lib, p0), layer(lib, p1)
     st, s = session(lib, [l0, l1])
