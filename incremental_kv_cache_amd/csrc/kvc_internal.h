@@ -162,7 +162,7 @@ int dev_merge_decode(const DevState& s, void* out);
 // that the longest items start early and the ragged tail is short.  With more
 // items than the table holds, count is 0 and the kernel walks sequences in
 // order (query tiles from the last one down).
-constexpr int kChunkQueryTile = 128;
+constexpr int kChunkQueryTile = 256;
 constexpr int kMaxChunkOrder = 256;
 struct ChunkOrder {
   int32_t count;                 // items listed (0: natural order)

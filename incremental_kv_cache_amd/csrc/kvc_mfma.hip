@@ -716,8 +716,11 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
 }
 
 // ---------------------------------------------------------- flash attention --
-// Block = one work item (sequence b, chunk queries 128 qt .. +128) of head h:
-// 32 queries per wave.  Virtual key j < len is cache row j, else chunk row
+// Block = one work item (sequence b, chunk queries QT qt .. +QT, QT =
+// kChunkQueryTile = 256) of head h: eight waves of 32 queries, which share
+// every K/V tile the block loads (twice the queries per loaded tile of a
+// four-wave block, at the same two waves per SIMD).  Virtual key j < len is
+// cache row j, else chunk row
 // j - len; query i sees j <= len + i.  Scores are formed transposed
 // (S^T = K Q^T) so that a lane holds every score of one query: the softmax
 // scale factor is per lane, and the probabilities are already in the operand
@@ -760,7 +763,7 @@ __device__ __forceinline__ float add_bf16x8(const Frag8& f, float acc) {
 
 // WIN: sliding-window layer (ring storage, a lower key bound per query).
 template <int DH, bool WIN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_flash_kernel(
+__global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_flash_kernel(
     DevState s, int n_max, int per_seq_rows, ChunkOrder order, float* __restrict__ out) {
   constexpr int KT = 64;
   static_assert(kMinBlockRows % KT == 0, "a key tile must stay inside one block");
@@ -769,7 +772,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int DSTEPS = DH / 16;
   constexpr int DTILES = DH / 32;
   constexpr int CPR = DH / 8;        // 16-byte pieces per row
-  constexpr int RPI = 256 / CPR;     // rows covered by one load of the workgroup
+  constexpr int QT = kChunkQueryTile;  // queries of the workgroup, 32 per wave
+  constexpr int THREADS = 2 * QT;
+  constexpr int RPI = THREADS / CPR;  // rows covered by one load of the workgroup
   constexpr int PIECES = KT / RPI;   // pieces per thread per tile, each of K and V
   constexpr float kRescale = 8.f;    // log2 of the largest probability kept unscaled
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * LDK];
@@ -791,24 +796,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     qt = order.qtiles - 1 - (item - b * order.qtiles);
   }
   const int n_b = per_seq_rows ? s.rows[b] : n_max;
-  if (qt * 128 >= n_b) return;
+  if (qt * QT >= n_b) return;
   const int len = WIN ? max(s.len[b], 0) : min(max(s.len[b], 0), s.capacity);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int g = lane >> 5;
   const int c32 = lane & 31;
-  const int qi = qt * 128 + wave * 32 + c32;
+  const int qi = qt * QT + wave * 32 + c32;
   const int qi_eff = min(qi, n_b - 1);
   const int limit = len + qi_eff;
-  const int i_max = min(qt * 128 + 127, n_b - 1);
+  const int i_max = min(qt * QT + QT - 1, n_b - 1);
   const int total = len + i_max + 1;
   const int ntiles = (total + KT - 1) / KT;
   // sliding window: query qi reads keys lo .. limit; the block starts at the key
   // tile holding its first query's lowest key
   const int lo = WIN ? window_start(s, limit) : 0;
-  const int it_first = WIN ? window_start(s, len + qt * 128) / KT : 0;
-  const int wave_lo_max = WIN ? window_start(s, len + min(qt * 128 + wave * 32 + 31, n_b - 1)) : 0;
+  const int it_first = WIN ? window_start(s, len + qt * QT) / KT : 0;
+  const int wave_lo_max = WIN ? window_start(s, len + min(qt * QT + wave * 32 + 31, n_b - 1)) : 0;
   const size_t lane_id = size_t(b) * H + h;
   const int hk = h / (H / s.kv_heads);  // the key/value head this query head reads
   const size_t kv_lane = size_t(b) * s.kv_heads + hk;
@@ -848,12 +853,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   Frag8 onek, mq;
   onek.u = make_uint4(g == 0 ? 0x3f80u : 0u, 0u, 0u, 0u);
   mq.u = make_uint4(0u, 0u, 0u, 0u);
-  const int wave_limit_min = len + min(qt * 128 + wave * 32, n_b - 1);  // smallest limit in the wave
+  const int wave_limit_min = len + min(qt * QT + wave * 32, n_b - 1);  // smallest limit in the wave
 
   // global -> register -> LDS staging: thread loads piece lch of rows lrow + RPI k
   const int lrow = tid / CPR;
   const int lch = tid - lrow * CPR;
-  static_assert(PIECES == 2 || PIECES == 4, "tile staging assumes 2 or 4 pieces per thread");
+  static_assert(PIECES == 1 || PIECES == 2 || PIECES == 4, "tile staging assumes 1, 2 or 4 pieces per thread");
   // staged pieces in named registers (an indexed array here is kept in scratch memory)
   uint4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
   // tile of contiguous rows (all cache rows, or all chunk rows): loads into registers
@@ -868,8 +873,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int STRIDE = RPI * DH / 8;  // uint4 between a thread's pieces
     pk0 = kp[0];
     pv0 = vp[0];
-    pk1 = kp[STRIDE];
-    pv1 = vp[STRIDE];
+    if constexpr (PIECES >= 2) {
+      pk1 = kp[STRIDE];
+      pv1 = vp[STRIDE];
+    }
     if constexpr (PIECES == 4) {
       pk2 = kp[2 * STRIDE];
       pv2 = vp[2 * STRIDE];
@@ -883,8 +890,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int KS = RPI * LDK / 8, VS = RPI * LDV / 8;
     kd[0] = pk0;
     vd[0] = pv0;
-    kd[KS] = pk1;
-    vd[VS] = pv1;
+    if constexpr (PIECES >= 2) {
+      kd[KS] = pk1;
+      vd[VS] = pv1;
+    }
     if constexpr (PIECES == 4) {
       kd[2 * KS] = pk2;
       vd[2 * VS] = pv2;
@@ -1121,7 +1130,8 @@ int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, const Chun
   if (items == 0) return 0;
   const dim3 grid(unsigned(items) * unsigned(s.heads));
 #define KVC_FLASH_LAUNCH(DH_, WIN_)                                                                      \
-  hipLaunchKernelGGL((attend_flash_kernel<DH_, WIN_>), grid, dim3(256), 0, st(s.stream), s, n_max, per_seq_rows, \
+  hipLaunchKernelGGL((attend_flash_kernel<DH_, WIN_>), grid, dim3(2 * kChunkQueryTile), 0, st(s.stream), s, n_max, \
+                     per_seq_rows, \
                      order, static_cast<float*>(out))
   if (s.head_width == 128) {
     if (s.window)

@@ -3,7 +3,7 @@
 The projection switches to MFMA kernels for bf16 when D % 128 == 0 (a skinny
 kernel for up to 64 rows, a tiled one above), and chunk attention uses the
 flash kernel for d_h in {64, 128}.  Shapes here cross every tile edge: rows not
-a multiple of 32 or 128, several query tiles of 128, key tiles straddling the
+a multiple of 32 or 128, several query tiles of 256, key tiles straddling the
 retained/chunk boundary, empty and single-row chunks.
 """
 import numpy as np
@@ -50,12 +50,12 @@ def test_decode_projection_rows(B):
 
 @pytest.mark.parametrize("dh", [64, 128])
 def test_flash_chunk_ragged(dh):
-    """Two query tiles (n_max = 200), cuts that end inside a 64-key tile, rows 0/1/200/137."""
+    """Two query tiles (n_max = 300), cuts that end inside a 64-key tile, rows 0/1/300/263."""
     H = 2
     D = H * dh
     B = 4
-    lens, cuts, rows = [130, 70, 0, 257], [65, 70, 0, 3], [1, 200, 137, 0]
-    n_max, cap = 200, 480
+    lens, cuts, rows = [130, 70, 0, 257], [65, 70, 0, 3], [1, 300, 263, 0]
+    n_max, cap = 300, 480
     layer, w = make_layer(17, D, H, "bf16", max_positions=cap)
     cache = K.kvc_cache_create(layer, B, cap, max_chunk_rows=512)
     xp_dev, xp = hidden(17, synth.STREAM_PREFIX_X, B, max(lens), D, "bf16")
@@ -79,13 +79,13 @@ def test_flash_chunk_ragged(dh):
 
 
 def test_flash_chunk_prefill_matches_causal_reference():
-    """A 150-row bf16 prefill (two query tiles, three key tiles) through the tiled
+    """A 300-row bf16 prefill (two query tiles, five key tiles) through the tiled
     projection and the flash kernel matches the float64 causal reference."""
-    H, dh, n = 4, 128, 150
+    H, dh, n = 4, 128, 300
     D = H * dh
-    layer, w = make_layer(19, D, H, "bf16", max_positions=160)
+    layer, w = make_layer(19, D, H, "bf16", max_positions=320)
     x_dev, x = hidden(19, synth.STREAM_PREFIX_X, 1, n, D, "bf16")
-    cache = K.kvc_cache_create(layer, 1, 160, max_chunk_rows=256)
+    cache = K.kvc_cache_create(layer, 1, 320, max_chunk_rows=512)
     out_chunk, _ = K.kvc_continue_chunk(layer, cache, x_dev)
     ref = A.causal_layer(x[0], *w, heads=H)["out"]
     assert_parity(to_f64(out_chunk)[0], ref, "bf16", "chunk")

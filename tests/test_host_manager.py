@@ -259,10 +259,11 @@ def _i32(v):
 
 
 def test_chunk_work_order_lists_every_item_heaviest_first(lib):
-    """The chunk attention's work order: every (sequence, 128-row query tile) with
+    """The chunk attention's work order: every (sequence, 256-row query tile) with
     rows appears once, the keys its last query reads never increase along the
     list, and equal loads keep sequence order."""
-    lens, rows, n_max = [10, 500, 0, 37, 200], [300, 1, 0, 129, 256], 300
+    tile = 256  # chunk rows per work item of the bf16 chunk attention
+    lens, rows, n_max = [10, 500, 0, 37, 200], [600, 1, 0, 257, 512], 600
     la, lp = _i32(lens)
     ra, rp = _i32(rows)
     items = np.zeros(256, np.int32)
@@ -270,15 +271,15 @@ def test_chunk_work_order_lists_every_item_heaviest_first(lib):
     n = lib.kvc_test_chunk_order(5, n_max, lp, rp, C.byref(qt), items.ctypes.data_as(C.POINTER(C.c_int32)))
     assert qt.value == 3
     got = [(int(i) >> 16, int(i) & 0xFFFF) for i in items[:n]]
-    want = {(b, q) for b in range(5) for q in range(3) if q * 128 < rows[b]}
+    want = {(b, q) for b in range(5) for q in range(3) if q * tile < rows[b]}
     assert len(got) == len(want) and set(got) == want
-    keys = [lens[b] + min(rows[b], 128 * (q + 1)) for b, q in got]
+    keys = [lens[b] + min(rows[b], tile * (q + 1)) for b, q in got]
     assert all(keys[k] >= keys[k + 1] for k in range(len(keys) - 1))
     for k in range(len(keys) - 1):
         if keys[k] == keys[k + 1]:
             assert got[k] < got[k + 1]
     # no per-sequence rows: every sequence has n_max rows
-    n2 = lib.kvc_test_chunk_order(2, 130, lp, None, C.byref(qt), items.ctypes.data_as(C.POINTER(C.c_int32)))
+    n2 = lib.kvc_test_chunk_order(2, tile + 2, lp, None, C.byref(qt), items.ctypes.data_as(C.POINTER(C.c_int32)))
     assert n2 == 4 and qt.value == 2
     # more items than the table holds: natural order (count 0)
     big, bp = _i32(np.arange(300))
