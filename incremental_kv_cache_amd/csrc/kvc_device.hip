@@ -369,16 +369,30 @@ __global__ __launch_bounds__(256) void commit_decode_kernel(DevState s) {
   const size_t row_bytes = size_t(dh) * sizeof(T);
   const size_t seq_rows = size_t(b) * s.kv_heads;
   if ((row_bytes & 15) == 0) {
+    // two 16-byte pieces of K and of V per thread and pass, all four loaded
+    // before any store (the stores may alias the loads as far as the compiler
+    // knows, so it would not move a load past one)
     const int per_row = int(row_bytes / 16);
-    for (int idx = threadIdx.x; idx < s.kv_heads * per_row; idx += blockDim.x) {
+    const int n = s.kv_heads * per_row;
+    auto src = [&](const void* cand, int idx) {
       const int h = idx / per_row;
-      const int c = idx - h * per_row;
-      const size_t lane_id = seq_rows + h;
-      const size_t off = kv_offset(s, b, h, len);
-      reinterpret_cast<uint4*>(static_cast<T*>(s.keys) + off)[c] =
-          reinterpret_cast<const uint4*>(static_cast<const T*>(s.cand_k) + lane_id * dh)[c];
-      reinterpret_cast<uint4*>(static_cast<T*>(s.values) + off)[c] =
-          reinterpret_cast<const uint4*>(static_cast<const T*>(s.cand_v) + lane_id * dh)[c];
+      return reinterpret_cast<const uint4*>(static_cast<const T*>(cand) + (seq_rows + h) * dh)[idx - h * per_row];
+    };
+    auto put = [&](void* cache, int idx, uint4 v) {
+      const int h = idx / per_row;
+      reinterpret_cast<uint4*>(static_cast<T*>(cache) + kv_offset(s, b, h, len))[idx - h * per_row] = v;
+    };
+    for (int i0 = threadIdx.x; i0 < n; i0 += 2 * blockDim.x) {
+      const int i1 = i0 + blockDim.x;
+      const int i1c = min(i1, n - 1);
+      const uint4 k0 = src(s.cand_k, i0), v0 = src(s.cand_v, i0);
+      const uint4 k1 = src(s.cand_k, i1c), v1 = src(s.cand_v, i1c);
+      put(s.keys, i0, k0);
+      put(s.values, i0, v0);
+      if (i1 < n) {
+        put(s.keys, i1, k1);
+        put(s.values, i1, v1);
+      }
     }
   } else {
     for (int idx = threadIdx.x; idx < s.kv_heads * dh; idx += blockDim.x) {
