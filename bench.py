@@ -62,12 +62,12 @@ MEASURED_TRAFFIC = {
     "headline": {"source": "decode", "fetch_kib": 1048893.0, "fetch_scale": 2.0, "write_kib": 512.0, "write_scale": 1.0,
                  "kernel_source_sha256": "33632cb638dacae9e5a0927280e6032fd103a8e5312bb67e58d63950f7eb2599"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
-    "chunk": {"source": "mfma", "fetch_kib": 299356.2, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
-              "kernel_source_sha256": "6e43a5052dd08ee578c9a51146bc981d66bd4235eaff8e6e4bd2fbf1d2cfea09"},
+    "chunk": {"source": "mfma", "fetch_kib": 299376.9, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
+              "kernel_source_sha256": "3ca02bc0e5cf0c307e214779354a43c7506b0215cc37e25d576dbd2cdd7b7741"},
     # attend_flash_kernel, suffix chunk (B=8, n=512)
-    "chunk_attention": {"source": "mfma", "fetch_kib": 354586.5, "fetch_scale": 2.0, "write_kib": 65563.0,
+    "chunk_attention": {"source": "mfma", "fetch_kib": 354611.7, "fetch_scale": 2.0, "write_kib": 65585.1,
                         "write_scale": 1.0,
-                        "kernel_source_sha256": "6e43a5052dd08ee578c9a51146bc981d66bd4235eaff8e6e4bd2fbf1d2cfea09"},
+                        "kernel_source_sha256": "3ca02bc0e5cf0c307e214779354a43c7506b0215cc37e25d576dbd2cdd7b7741"},
 }
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
                   "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}

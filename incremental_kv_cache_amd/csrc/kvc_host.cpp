@@ -662,7 +662,7 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
                      W, kMinBlockRows, max_chunk_rows, capacity);
   }
   if (paged) {
-    // Paged storage: a decode split-K step (at most 256 rows) and a 64-row
+    // Paged storage: a decode split-K step (at most 256 rows) and a 128-row
     // chunk-attention tile must each fall inside one block.
     if (!is_pow2(block_rows) || block_rows < kMinBlockRows || capacity % block_rows != 0)
       return fail_ea(KVC_ERR_BAD_ARGUMENT, kMinBlockRows, block_rows,

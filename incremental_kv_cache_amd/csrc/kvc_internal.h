@@ -28,7 +28,7 @@ constexpr unsigned long long kErrClear = ~0ull;
 // kernel (sizes the partial buffer); each call picks tile_rows >= this.
 constexpr int kDecodeTileRows = 512;
 // Smallest rows per block of a paged cache: every run of rows a kernel reads
-// through one block base (a decode step, a 64-row chunk-attention tile) fits.
+// through one block base (a decode step, a 128-row chunk-attention tile) fits.
 constexpr int kMinBlockRows = 256;
 // Query heads that one bf16 decode workgroup serves from a single read of
 // their shared key/value head: the largest power of two <= 8 dividing the

@@ -726,7 +726,7 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
 // scale factor is per lane, and the probabilities are already in the operand
 // layout of O^T += V^T P^T.
 //
-// Keys and values pass through LDS in tiles of 64 rows, double-buffered: the
+// Keys and values pass through LDS in tiles of 128 rows, double-buffered: the
 // next tile's rows are loaded into registers (16 lanes per 256-byte row, so a
 // load instruction covers whole rows) while the current tile is multiplied,
 // then written to the other buffer, with one barrier per tile.  V stays
@@ -765,7 +765,7 @@ __device__ __forceinline__ float add_bf16x8(const Frag8& f, float acc) {
 template <int DH, bool WIN>
 __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_flash_kernel(
     DevState s, int n_max, int per_seq_rows, ChunkOrder order, float* __restrict__ out) {
-  constexpr int KT = 64;
+  constexpr int KT = 128;  // keys per LDS tile (two buffers of K and V: 148 KB at d_h = 128)
   static_assert(kMinBlockRows % KT == 0, "a key tile must stay inside one block");
   constexpr int LDK = DH + 8;   // K row stride: conflict-free 16-byte fragment reads
   constexpr int LDV = DH + 32;  // V row stride: conflict-free transposing reads (64 banks)
@@ -866,7 +866,7 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
   auto fetch = [&](int j0) {
     const bool cached = j0 + KT <= len;
     const size_t r0 = size_t(cached ? j0 : j0 - len) + lrow;
-    // a 64-row tile lies in one block of a paged cache
+    // a 128-row tile lies in one block of a paged cache
     const ptrdiff_t tile_base = cached ? kv_block_base(s, b, hk, j0) : 0;
     const uint4* kp = reinterpret_cast<const uint4*>((cached ? kc + tile_base : kn) + r0 * DH + lch * 8);
     const uint4* vp = reinterpret_cast<const uint4*>((cached ? vc + tile_base : vn) + r0 * DH + lch * 8);
@@ -931,9 +931,9 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
     const bool more = it + 1 < ntiles;
     const bool staged = more && contiguous(j0 + KT);
 
-    f32x16_t st[2];
+    f32x16_t st[KT / 32];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT / 32; ++kt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
       st[kt] = mfma32(onek.v, mq.v, st[kt]);
@@ -957,7 +957,7 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
     // window's lower edge only where the tile starts below the wave's last one
     if (j0 + KT - 1 > wave_limit_min || (WIN && j0 < wave_lo_max)) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
@@ -966,7 +966,7 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
     }
     float tmax = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[kt][r]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
@@ -983,14 +983,14 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
       // this tile's scores were taken against the old reference
       const float shift = (m_new == -INFINITY ? 0.f : m_new) - mref;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[kt][r] -= shift;
       mref += shift;
       mq.v[0] = g == 0 ? (__bf16)(-mref) : (__bf16)0.f;
     }
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         // v_exp_f32 directly: probabilities below 2^-126 flush to zero
@@ -998,7 +998,7 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
       }
     const bf16_t* vt = &Vs[buf][vlane];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         Frag8 pb;

@@ -50,7 +50,7 @@ def test_decode_projection_rows(B):
 
 @pytest.mark.parametrize("dh", [64, 128])
 def test_flash_chunk_ragged(dh):
-    """Two query tiles (n_max = 300), cuts that end inside a 64-key tile, rows 0/1/300/263."""
+    """Two query tiles (n_max = 300), cuts that end inside a 128-key tile, rows 0/1/300/263."""
     H = 2
     D = H * dh
     B = 4
