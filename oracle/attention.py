@@ -293,24 +293,3 @@ def continue_chunk(cache: DecodeCache, x_rows, wq, wk, wv, heads: int,
     cache.len += n
     cache.next_position += n
     return (np.stack(outs) if n else np.zeros((0, x_rows.shape[1]))), work
-
-
-# ------------------------------------------------------------------------------
-# Checks at full size: attention of one newest query over a given (downloaded)
-# cache, and the new row's projections -- the pieces a sampled comparison needs.
-# ------------------------------------------------------------------------------
-
-def attend_over_cache(q_heads, keys, values, cand_k, cand_v):
-    """Newest-query attention over retained rows plus the candidate row, all heads.
-
-    ``q_heads`` [H, d_h]; ``keys``/``values`` [H, len, d_h] (retained logical
-    rows); ``cand_k``/``cand_v`` [H, d_h].  Returns merged output [H*d_h].
-    Chapter 37, incremental-attention listing: the candidate is scored at
-    position ``len``.
-    """
-    out = []
-    for h in range(q_heads.shape[0]):
-        kk = np.concatenate([keys[h], cand_k[h][None]])
-        vv = np.concatenate([values[h], cand_v[h][None]])
-        out.append(attend(q_heads[h], kk, vv)[0])
-    return np.concatenate(out)

@@ -338,6 +338,27 @@ def test_cut_table_and_projection_rows():
         assert P.continuation_projection_rows(g["layers"], len(c["query"]), cut) == (c["rows"], c["full_rows"])
 
 
+def test_chunk_work_counts_match_the_cut_table():
+    """The per-call row counts the library reports for a continuation, summed over
+    the note's two layers and three projections, are the 27-case table's columns:
+    rows this call = 6 x (queryLength - cut), full recompute = 6 x queryLength, and
+    the cut rows of K and V are reused (prefix-reuse note, "Work and error over 27
+    cases" and the formula under it)."""
+    g = _load("p3_cut_table.json")
+    per_layer_projections = g["layers"] * 3
+    for c in g["conditions"]:
+        n = len(c["query"])
+        w = P.chunk_work([c["cut"]], [n - c["cut"]])
+        assert per_layer_projections * w["incremental_rows_per_projection"] == c["rows"], c["name"]
+        assert per_layer_projections * w["full_prefix_rows_per_projection"] == c["full_rows"], c["name"]
+        assert w["reused_key_value_rows"] == c["cut"], c["name"]
+    # a batch sums its sequences' counts
+    conds = g["conditions"]
+    w = P.chunk_work([c["cut"] for c in conds], [len(c["query"]) - c["cut"] for c in conds])
+    assert per_layer_projections * w["incremental_rows_per_projection"] == sum(c["rows"] for c in conds)
+    assert per_layer_projections * w["full_prefix_rows_per_projection"] == sum(c["full_rows"] for c in conds)
+
+
 def test_lcp_rules():
     """Contiguous prefix only; last query token always recomputed; non-empty integer IDs."""
     assert P.lcp_cut([1, 2, 3, 4, 5, 6, 7, 8], [1, 2, 3, 4, 20, 6, 7, 8]) == 4
