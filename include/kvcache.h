@@ -104,7 +104,12 @@ enum {
   KVC_ASYNC = 1  /* return after enqueueing; a device-found error is sticky, every
                     later commit on the cache is suppressed, and the next KVC_SYNC
                     call or kvc_sync() returns KVC_ERR_DEFERRED with its detail.
-                    Outputs of calls made after a failed one are undefined. */
+                    Outputs of calls made after a failed one are undefined.
+                    kvc_truncate, kvc_reset and kvc_fork never wait for the
+                    stream: enqueued while such a failure is still unreported,
+                    their device updates are suppressed like the commits (they
+                    return KVC_OK); the DEFERRED report then restores the host's
+                    lengths from the device and the caller repeats them. */
 };
 
 /* kvc_truncate flags. */
@@ -316,14 +321,16 @@ kvc_status kvc_continue_chunk(const kvc_layer* layer, kvc_cache* cache, const vo
 /* Keeps rows 0..cut[b]-1 of every sequence and sets next_position[b] = cut[b]
  * (prefix-reuse note, "What must be trimmed together").  cut: HOST int32[B],
  * 0 <= cut[b] <= len[b].  Moves no K/V data and allocates nothing.
- * flags: 0 or KVC_TRUNCATE_KEEP_STALE_POSITION.  Errors: NULL_ARGUMENT,
- * BAD_CUT, BAD_ARGUMENT, DEFERRED, DEVICE. */
+ * flags: 0 or KVC_TRUNCATE_KEEP_STALE_POSITION.  After a KVC_ASYNC call see
+ * KVC_ASYNC (a pending device failure suppresses the update).  Errors:
+ * NULL_ARGUMENT, BAD_CUT, BAD_ARGUMENT, DEVICE. */
 kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags);
 
 /* Logical reset (Chapter 37, "Keep layer, logical length, and capacity
  * separate"): every length and next position becomes 0; capacity, storage
  * contents, allocation and the parameter binding are unchanged, so a cache
- * bound to updated weights stays rejected.  Errors: NULL_ARGUMENT, DEVICE. */
+ * bound to updated weights stays rejected.  After a KVC_ASYNC call see
+ * KVC_ASYNC.  Errors: NULL_ARGUMENT, DEVICE. */
 kvc_status kvc_reset(kvc_cache* cache);
 
 /* Logical snapshot of sequence `seq` (Chapter 37, logical key/value
@@ -337,14 +344,19 @@ kvc_status kvc_reset(kvc_cache* cache);
 kvc_status kvc_snapshot(kvc_cache* cache, int32_t seq, void* keys_out, void* values_out,
                         int32_t* positions_out, int64_t rows_capacity, int32_t* rows_out);
 
-/* Lengths and next positions as committed on the device: HOST int32[B] each
- * (nullable).  Synchronises the stream.  Errors: NULL_ARGUMENT, DEFERRED, DEVICE. */
+/* Lengths and next positions as committed on the device (Chapter 37, "Keep
+ * layer, logical length, and capacity separate": the cache's length accessors
+ * report the logical rows apart from the capacity; per sequence here): HOST
+ * int32[B] each (nullable).  Synchronises the stream.  Errors: NULL_ARGUMENT,
+ * DEFERRED, DEVICE. */
 kvc_status kvc_lengths(kvc_cache* cache, int32_t* len_out, int32_t* next_position_out);
 
 /* Waits for the cache's stream and reports a deferred device-found error
  * (KVC_ERR_DEFERRED; kvc_last_error() then holds the original status in
  * `actual` and the original detail).  Clears the sticky error and resyncs
- * the host copy of the lengths. */
+ * the host copy of the lengths.  The rejection it reports is the one Chapter
+ * 37 requires under "Reset or reject without corrupting retained state": the
+ * failed call and everything queued behind it left the cache unchanged. */
 kvc_status kvc_sync(kvc_cache* cache);
 
 /* Longest-common-prefix cut (prefix-reuse note, "First, one history edit" and
@@ -454,7 +466,9 @@ kvc_status kvc_session_decode(kvc_session* session, const int32_t* tokens, void*
  * kvc_truncate (KVC_TRUNCATE_KEEP_STALE_POSITION: the note's negative
  * control).  Errors: NULL_ARGUMENT, BAD_CUT, BAD_ARGUMENT, DEVICE. */
 kvc_status kvc_session_truncate(kvc_session* session, const int32_t* cut, int32_t flags);
-/* Every layer's lengths and next positions to 0 (kvc_reset per layer). */
+/* Every layer's lengths and next positions to 0 (kvc_reset per layer).
+ * After a KVC_ASYNC call, session truncations and resets behave as
+ * kvc_truncate and kvc_reset do (see KVC_ASYNC). */
 kvc_status kvc_session_reset(kvc_session* session);
 /* Waits for the stream and reports a deferred failure of any layer, as kvc_sync. */
 kvc_status kvc_session_sync(kvc_session* session);

@@ -307,9 +307,9 @@ kvc_status collect_device_error(kvc_cache* c, int64_t n_max_for_index) {
   if (rc) return device_fail(rc, "clearing the device error words");
   switch (st) {
     case KVC_ERR_NONFINITE_KEY:
-      return fail(st, "appended key value at flat index %llu must be finite, got %g", idx, g_last.value);
+      return fail(st, "candidate key element %llu is not finite (%g); nothing was appended", idx, g_last.value);
     case KVC_ERR_NONFINITE_VALUE:
-      return fail(st, "appended value at flat index %llu must be finite, got %g", idx, g_last.value);
+      return fail(st, "candidate value element %llu is not finite (%g); nothing was appended", idx, g_last.value);
     case KVC_ERR_NONFINITE_QUERY:
       return fail(st, "rotated query at flat index %llu is not finite", idx);
     case KVC_ERR_ROTARY_POSITION:
@@ -641,11 +641,14 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
   *out = nullptr;
   // Chapter 37, layer-kv-cache listing: batch, capacity, position capacity,
   // element-count overflow, then allocation.
-  if (batch <= 0) return fail_ea(KVC_ERR_ZERO_BATCH, 1, batch, "KV cache batch size must be nonzero");
-  if (capacity <= 0) return fail_ea(KVC_ERR_ZERO_CAPACITY, 1, capacity, "KV cache capacity must be nonzero");
+  if (batch <= 0)
+    return fail_ea(KVC_ERR_ZERO_BATCH, 1, batch, "a cache needs at least one sequence, got %d", batch);
+  if (capacity <= 0)
+    return fail_ea(KVC_ERR_ZERO_CAPACITY, 1, capacity, "a cache needs room for at least one row, got %d", capacity);
   if (capacity > layer->rope_max_positions)
     return fail_ea(KVC_ERR_CAPACITY_EXCEEDS_POSITIONS, layer->rope_max_positions, capacity,
-                   "KV cache capacity %d exceeds RoPE position capacity %d", capacity, layer->rope_max_positions);
+                   "%d rows per sequence need more rotary positions than the layer's %d", capacity,
+                   layer->rope_max_positions);
   if (max_chunk_rows <= 0)
     return fail(KVC_ERR_BAD_ARGUMENT, "max_chunk_rows must be at least 1, got %d", max_chunk_rows);
   const bool paged = block_rows != 0;
@@ -682,7 +685,7 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
       !checked_mul(qrows, dh, &qrows) || !checked_mul(batch, capacity, &pos_elems) ||
       elements > (INT64_MAX / 16) || cand > (INT64_MAX / 16)) {
     return fail(KVC_ERR_ELEMENT_COUNT_OVERFLOW,
-                "KV cache element count overflows for batch %d, %d heads, capacity %d, and head width %d", batch,
+                "storage of %d sequences x %d heads x %d rows x %d features is too large to index", batch,
                 H, capacity, dh);
   }
   kvc_cache* c = new (std::nothrow) kvc_cache;
@@ -947,8 +950,8 @@ kvc_status session_call(kvc_session* S, const int32_t* tokens, int n_max, const 
         g_last.layer = l;
         g_last.sequence = b;
         return fail_ea(KVC_ERR_FULL, c->capacity, int64_t(c->len[b]) + n,
-                       "KV cache of layer %d is full at capacity %d (sequence %d needs %d more rows)", l,
-                       c->capacity, b, n);
+                       "layer %d: sequence %d holds %d of %d rows and cannot take %d more", l, b, c->len[b],
+                       c->capacity, n);
       }
       if (c->ds.rope && n > 0 && int64_t(c->next_pos[b]) + n > c->rope_max_positions) {
         g_last.layer = l;
@@ -1208,8 +1211,8 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
   for (int b = 0; b < cache->batch; ++b) {
     if (!cache->window && cache->len[b] >= cache->capacity) {  // a window cache is a ring
       g_last.sequence = b;
-      return fail_ea(KVC_ERR_FULL, cache->capacity, cache->len[b], "KV cache is full at capacity %d",
-                     cache->capacity);
+      return fail_ea(KVC_ERR_FULL, cache->capacity, cache->len[b],
+                     "sequence %d already holds %d rows, all the cache has room for", b, cache->capacity);
     }
   }
   if (cache->ds.rope) {
@@ -1268,7 +1271,7 @@ kvc_status kvc_continue_chunk(const kvc_layer* layer, kvc_cache* cache, const vo
     if (!cache->window && int64_t(cache->len[b]) + n > cache->capacity) {
       g_last.sequence = b;
       return fail_ea(KVC_ERR_FULL, cache->capacity, int64_t(cache->len[b]) + n,
-                     "KV cache is full at capacity %d (sequence %d needs %d more rows)", cache->capacity, b, n);
+                     "sequence %d holds %d of %d rows and cannot take %d more", b, cache->len[b], cache->capacity, n);
     }
   }
   if (cache->ds.rope) {
@@ -1792,6 +1795,7 @@ kvc_status kvc_session_truncate(kvc_session* session, const int32_t* cut, int32_
     for (int b = 0; b < c->batch; ++b) {
       c->len[b] = cut[b];
       if (!stale) c->next_pos[b] = cut[b];
+      if (cut[b] < c->held[b]) c->held[b] = cut[b];  // as the device's length update does
     }
   }
   return KVC_OK;
@@ -1807,6 +1811,7 @@ kvc_status kvc_session_reset(kvc_session* session) {
   for (kvc_cache* c : session->caches) {
     std::fill(c->len.begin(), c->len.end(), 0);
     std::fill(c->next_pos.begin(), c->next_pos.end(), 0);
+    std::fill(c->held.begin(), c->held.end(), 0);
   }
   return KVC_OK;
 }

@@ -64,6 +64,28 @@ def _out_dtype(code: int):
     return torch.float64 if code == KVC_F64 else torch.float32
 
 
+def _check_out(out, shape, code: int, like) -> None:
+    """A caller-supplied output must be exactly what the kernels write: the
+    accumulate type, the call's shape, on the input's device."""
+    want = _out_dtype(code)
+    if out.dtype != want:
+        raise TypeError(f"out must be {want}, got {out.dtype}")
+    if tuple(out.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"out must have shape {tuple(int(v) for v in shape)}, got {tuple(out.shape)}")
+    if out.device != like.device:
+        raise ValueError(f"out is on {out.device}, the input on {like.device}")
+
+
+def _rows_arg(n_rows, batch: int):
+    """Host int32 [B] row counts (or None) as a pointer; the array is returned to keep it alive."""
+    if n_rows is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(n_rows, dtype=np.int32))
+    if arr.shape != (batch,):
+        raise ValueError(f"n_rows must hold one count per sequence ({batch}), got shape {arr.shape}")
+    return arr, arr.ctypes.data_as(capi.PI32)
+
+
 def _dev_ptr(t) -> int:
     if not t.is_cuda:
         raise TypeError("expected a device tensor")
@@ -254,12 +276,13 @@ def kvc_append_and_attend(layer: Layer, cache: Cache, x, out=None, flags: int = 
     Returns (out [B, 1, D], work dict)."""
     lib = cache._lib
     code = cache.desc["kv_dtype"]
-    if out is None:
-        torch = _torch()
-        out = torch.empty((cache.desc["batch"], 1, cache.desc["model_width"]), dtype=_out_dtype(code),
-                          device=x.device)
     if _dtype_code(x) != code:
         raise TypeError("input type differs from the cache's type")
+    out_shape = (cache.desc["batch"], 1, cache.desc["model_width"])
+    if out is None:
+        torch = _torch()
+        out = torch.empty(out_shape, dtype=_out_dtype(code), device=x.device)
+    _check_out(out, out_shape, code, x)
     shape = (C.c_int64 * max(1, x.dim()))(*[int(s) for s in x.shape])
     w = capi.Work()
     _check(lib, lib.kvc_append_and_attend(layer.ptr, cache.ptr, _dev_ptr(x), x.dim(), shape, _dev_ptr(out), flags,
@@ -276,13 +299,11 @@ def kvc_continue_chunk(layer: Layer, cache: Cache, x, n_rows=None, out=None, fla
     if x.dim() != 3 or x.shape[0] != cache.desc["batch"] or x.shape[2] != cache.desc["model_width"]:
         raise ValueError(f"chunk input must be [B, n, D], got {tuple(x.shape)}")
     n_max = int(x.shape[1])
+    arr, rows_ptr = _rows_arg(n_rows, cache.desc["batch"])
     if out is None:
         torch = _torch()
         out = torch.zeros((x.shape[0], n_max, x.shape[2]), dtype=_out_dtype(code), device=x.device)
-    rows_ptr = None
-    if n_rows is not None:
-        arr = np.ascontiguousarray(np.asarray(n_rows, dtype=np.int32))
-        rows_ptr = arr.ctypes.data_as(capi.PI32)
+    _check_out(out, (x.shape[0], n_max, x.shape[2]), code, x)
     w = capi.Work()
     _check(lib, lib.kvc_continue_chunk(layer.ptr, cache.ptr, _dev_ptr(x), n_max, rows_ptr, _dev_ptr(out), flags,
                                        C.byref(w)))
@@ -430,13 +451,14 @@ def kvc_session_chunk(session: Session, tokens, n_rows=None, out=None, flags: in
     if tokens.dtype != torch.int32 or tokens.dim() != 2:
         raise TypeError("tokens must be a device int32 tensor [B, n]")
     n_max = int(tokens.shape[1])
+    batch = session.desc["batch"]
+    if tokens.shape[0] != batch:
+        raise ValueError(f"tokens must be [B={batch}, n], got {tuple(tokens.shape)}")
+    arr, rows_ptr = _rows_arg(n_rows, batch)
+    out_shape = (batch, n_max, session.desc["model_width"])
     if out is None:
-        out = torch.zeros((session.desc["batch"], n_max, session.desc["model_width"]),
-                          dtype=_out_dtype(session.desc["kv_dtype"]), device=tokens.device)
-    rows_ptr = None
-    if n_rows is not None:
-        arr = np.ascontiguousarray(np.asarray(n_rows, dtype=np.int32))
-        rows_ptr = arr.ctypes.data_as(capi.PI32)
+        out = torch.zeros(out_shape, dtype=_out_dtype(session.desc["kv_dtype"]), device=tokens.device)
+    _check_out(out, out_shape, session.desc["kv_dtype"], tokens)
     w = capi.Work()
     _check(lib, lib.kvc_session_chunk(session.ptr, _dev_ptr(tokens), n_max, rows_ptr, _dev_ptr(out), flags,
                                       C.byref(w)))
@@ -449,9 +471,13 @@ def kvc_session_decode(session: Session, tokens, out=None, flags: int = KVC_SYNC
     torch = _torch()
     if tokens.dtype != torch.int32:
         raise TypeError("tokens must be a device int32 tensor [B]")
+    batch = session.desc["batch"]
+    if tuple(tokens.shape) != (batch,):
+        raise ValueError(f"tokens must be [B={batch}], got {tuple(tokens.shape)}")
+    out_shape = (batch, 1, session.desc["model_width"])
     if out is None:
-        out = torch.empty((session.desc["batch"], 1, session.desc["model_width"]),
-                          dtype=_out_dtype(session.desc["kv_dtype"]), device=tokens.device)
+        out = torch.empty(out_shape, dtype=_out_dtype(session.desc["kv_dtype"]), device=tokens.device)
+    _check_out(out, out_shape, session.desc["kv_dtype"], tokens)
     w = capi.Work()
     _check(lib, lib.kvc_session_decode(session.ptr, _dev_ptr(tokens), _dev_ptr(out), flags, C.byref(w)))
     return out, w.as_dict()

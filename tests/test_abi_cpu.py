@@ -73,7 +73,52 @@ def test_params_and_layer_validation_without_device(lib):
     assert lib.kvc_cache_create(layer, 1, 5, 1, None, C.byref(cache)) == capi.KVC_ERR_CAPACITY_EXCEEDS_POSITIONS
     d = lib.kvc_last_error().contents
     assert (d.expected, d.actual) == (4, 5)
-    assert b"exceeds RoPE position capacity" in d.message
+    assert b"need more rotary positions than the layer" in d.message
     assert lib.kvc_params_mark_updated(params, 3) == capi.KVC_ERR_BAD_ARGUMENT
     lib.kvc_layer_destroy(layer)
     lib.kvc_params_destroy(params)
+
+
+def test_binding_rejects_outputs_and_row_counts_the_kernels_would_overrun():
+    """The binding checks a caller-supplied output (type, shape, device) and the
+    per-sequence row counts before any pointer reaches the library: a wrong one
+    would make the kernels write past the buffer or read past the host array."""
+    import types
+
+    import torch
+
+    from incremental_kv_cache_amd import kvcache as K
+
+    B, D = 2, 8
+    desc = {"kv_dtype": K.KVC_F32, "batch": B, "model_width": D}
+    cache = types.SimpleNamespace(_lib=None, ptr=None, desc=desc)
+    layer = types.SimpleNamespace(ptr=None)
+    x1 = torch.zeros((B, 1, D), dtype=torch.float32)
+    for bad, exc in ((torch.zeros((B, 1, D), dtype=torch.float64), TypeError),
+                     (torch.zeros((B, 1, D), dtype=torch.bfloat16), TypeError),
+                     (torch.zeros((B, 1, D - 1), dtype=torch.float32), ValueError),
+                     (torch.zeros((B + 1, 1, D), dtype=torch.float32), ValueError),
+                     (torch.zeros((B * D,), dtype=torch.float32), ValueError)):
+        with pytest.raises(exc, match="out"):
+            K.kvc_append_and_attend(layer, cache, x1, out=bad)
+    xn = torch.zeros((B, 4, D), dtype=torch.float32)
+    with pytest.raises(ValueError, match="out"):
+        K.kvc_continue_chunk(layer, cache, xn, out=torch.zeros((B, 3, D), dtype=torch.float32))
+    with pytest.raises(TypeError, match="out"):
+        K.kvc_continue_chunk(layer, cache, xn, out=torch.zeros((B, 4, D), dtype=torch.float64))
+    for rows in ([4], [4, 4, 4], [[4, 4]]):
+        with pytest.raises(ValueError, match="n_rows"):
+            K.kvc_continue_chunk(layer, cache, xn, n_rows=rows)
+    session = types.SimpleNamespace(_lib=None, ptr=None, desc=desc)
+    tok = torch.zeros((B, 4), dtype=torch.int32)
+    with pytest.raises(ValueError, match="n_rows"):
+        K.kvc_session_chunk(session, tok, n_rows=[1])
+    with pytest.raises(ValueError, match="tokens"):
+        K.kvc_session_chunk(session, torch.zeros((B + 1, 4), dtype=torch.int32))
+    with pytest.raises(ValueError, match="out"):
+        K.kvc_session_chunk(session, tok, out=torch.zeros((B, 5, D), dtype=torch.float32))
+    with pytest.raises(ValueError, match="tokens"):
+        K.kvc_session_decode(session, torch.zeros((B, 1), dtype=torch.int32))
+    with pytest.raises(TypeError, match="out"):
+        K.kvc_session_decode(session, torch.zeros((B,), dtype=torch.int32),
+                             out=torch.zeros((B, 1, D), dtype=torch.float64))

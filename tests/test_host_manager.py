@@ -9,26 +9,18 @@ order ("Bind the state, calculate completely, then commit") and its
 error-evidence cases.
 """
 import ctypes as C
-import os
-import subprocess
 
 import numpy as np
 import pytest
 
 from incremental_kv_cache_amd import capi
+from tests import hostcheck
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 @pytest.fixture(scope="module")
 def lib(tmp_path_factory):
-    out = str(tmp_path_factory.mktemp("hostcheck") / "libkvc_hostcheck.so")
-    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "incremental_kv_cache_amd", "csrc"),
-           os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_host.cpp"),
-           os.path.join(ROOT, "tests", "hostcheck_backend.cpp"), "-o", out]
-    subprocess.run(cmd, check=True)
-    return capi.declare(C.CDLL(out))
+    return hostcheck.build(tmp_path_factory, "hostcheck")
 
 
 DUMMY = C.c_void_p(64)
@@ -98,7 +90,7 @@ def test_create_checks_in_order(lib):
     big = layer(lib, params(lib, d=128, dtype=capi.KVC_BF16), heads=1, max_pos=2 ** 31 - 1)
     assert lib.kvc_cache_create(big, 2 ** 31 - 1, 2 ** 31 - 1, 1, None, C.byref(c)) == \
         capi.KVC_ERR_ELEMENT_COUNT_OVERFLOW
-    assert b"overflows" in lib.kvc_last_error().contents.message
+    assert b"too large to index" in lib.kvc_last_error().contents.message
 
 
 def test_request_checks_follow_the_chapter_order_and_leave_state_unchanged(lib):

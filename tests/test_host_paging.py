@@ -13,28 +13,20 @@ cache given the same calls, and pool usage against the block counts the
 sharing rules imply.
 """
 import ctypes as C
-import os
-import subprocess
 
 import numpy as np
 import pytest
 
 from incremental_kv_cache_amd import capi
+from tests import hostcheck
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DUMMY = C.c_void_p(64)
 BR = 256  # block rows
 
 
 @pytest.fixture(scope="module")
 def lib(tmp_path_factory):
-    out = str(tmp_path_factory.mktemp("hostpaging") / "libkvc_hostcheck.so")
-    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "incremental_kv_cache_amd", "csrc"),
-           os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_host.cpp"),
-           os.path.join(ROOT, "tests", "hostcheck_backend.cpp"), "-o", out]
-    subprocess.run(cmd, check=True)
-    lib = capi.declare(C.CDLL(out))
+    lib = hostcheck.build(tmp_path_factory, "hostpaging")
     lib.kvc_test_fake_kernels.argtypes = [C.c_int]
     lib.kvc_test_fail_next.argtypes = [C.c_longlong]
     return lib

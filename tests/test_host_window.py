@@ -9,28 +9,20 @@ tests/hostcheck_backend.cpp with its stand-in kernels (tagged rows, appended
 through the ring), as in tests/test_host_paging.py.
 """
 import ctypes as C
-import os
-import subprocess
 
 import numpy as np
 import pytest
 
 from incremental_kv_cache_amd import capi
+from tests import hostcheck
 from oracle import prefix as P
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DUMMY = C.c_void_p(64)
 
 
 @pytest.fixture(scope="module")
 def lib(tmp_path_factory):
-    out = str(tmp_path_factory.mktemp("hostwindow") / "libkvc_hostcheck.so")
-    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "incremental_kv_cache_amd", "csrc"),
-           os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_host.cpp"),
-           os.path.join(ROOT, "tests", "hostcheck_backend.cpp"), "-o", out]
-    subprocess.run(cmd, check=True)
-    lib = capi.declare(C.CDLL(out))
+    lib = hostcheck.build(tmp_path_factory, "hostwindow")
     lib.kvc_test_fake_kernels.argtypes = [C.c_int]
     return lib
 
@@ -201,3 +193,49 @@ def test_window_fork_copies_the_ring(fake):
     k1, p1 = _snap(lib, c, 1)
     assert list(p1) == list(range(144, 350))
     np.testing.assert_array_equal(k1, k0[:, :350 - 144])
+
+
+def _reuse(lib, c, lcp):
+    out = C.c_int64()
+    assert lib.kvc_reuse_cut(c, 0, lcp, C.byref(out)) == 0, lib.kvc_last_error().contents.message
+    return out.value
+
+
+def test_session_reset_and_truncate_keep_the_held_rows_in_step(fake):
+    """A session's window layer wraps its ring, then is reset (or cut to 0) and
+    refilled: the oldest held row starts again from 0 on the host as on the
+    device, so a cut whose window the refilled ring holds is accepted
+    (prefix-reuse note, "Why a sliding-window partial hit must fall back": a cut
+    is refused only when the rows its continuation reads are gone)."""
+    lib = fake
+    W, cap = 100, 256
+    lay = _layer(lib, _params(lib), W)
+    layers = (C.c_void_p * 1)(lay)
+    for rewind in ("reset", "cut0"):
+        s = C.c_void_p()
+        st = lib.kvc_session_create(layers, 1, DUMMY, 32, capi.KVC_PE_NONE, 1, cap, 200, None, C.byref(s))
+        assert st == 0, lib.kvc_last_error().contents.message
+        c = C.c_void_p()
+        assert lib.kvc_session_layer_cache(s, 0, C.byref(c)) == 0
+        rows = np.array([200], np.int32)
+        for _ in range(2):  # 400 rows: slots 0 .. 143 written twice, rows 0 .. 143 gone
+            assert lib.kvc_session_chunk(s, DUMMY, 200, rows.ctypes.data_as(capi.PI32), DUMMY, 0, None) == 0
+        assert _reuse(lib, c, 150) == 0  # row 51 .. 149 of the continuation are gone
+        if rewind == "reset":
+            assert lib.kvc_session_reset(s) == 0
+        else:
+            zero = np.array([0], np.int32)
+            assert lib.kvc_session_truncate(s, zero.ctypes.data_as(capi.PI32), 0) == 0
+        assert lib.kvc_session_chunk(s, DUMMY, 200, rows.ctypes.data_as(capi.PI32), DUMMY, 0, None) == 0
+        host_view = [_reuse(lib, c, lcp) for lcp in (0, 50, 150, 200)]
+        assert host_view == [0, 50, 150, 200], rewind
+        cut = np.array([150], np.int32)
+        assert lib.kvc_session_truncate(s, cut.ctypes.data_as(capi.PI32), 0) == 0, \
+            lib.kvc_last_error().contents.message
+        assert _lengths(lib, c, 1) == ([150], [150])
+        # the device's bookkeeping agrees: resyncing the host copy changes nothing
+        assert lib.kvc_session_sync(s) == 0
+        assert [_reuse(lib, c, lcp) for lcp in (0, 50, 150)] == [0, 50, 150]
+        _, pos = _snap(lib, c, 0)
+        assert list(pos) == list(range(150))
+        lib.kvc_session_destroy(s)
