@@ -4,8 +4,10 @@
 // retained rows of the cache plus the candidate row (Chapter 37, the
 // incremental-attention listing; "Count projection rows, not hardware time":
 // the newest query still reads every retained row).  The position axis is
-// split into tiles of 512 to 2048 rows (chosen per call for about 2048
-// workgroups), one workgroup each.
+// split into tiles of 512 * 2^k rows, one workgroup each: the host picks the
+// longest tile that still gives at least 1024 workgroups (512 when a
+// workgroup serves several query heads), so a 4096-row lane of 32 x 32 lanes
+// is one whole-lane tile and a 32768-row lane of 4 x 32 lanes is eight.
 //
 // Inside a workgroup a row is read by G = d_h / 8 lanes, one 16-byte load of
 // K and one of V per lane; a wave covers 64 / G rows per load and issues U

@@ -5,7 +5,8 @@
 //   project   : new rows through W_q, W_k, W_v, rotary at next_position + i,
 //               candidate key/value rows and the query; non-finite checks.
 //   attend    : decode -- split-K over the position axis, one partial
-//               (max, sum, weighted values) per 256-row tile of each lane;
+//               (max, sum, weighted values) per split-K tile of each lane
+//               (512 * 2^k rows, chosen per call);
 //               chunk  -- one workgroup per query row, causal over the
 //               retained rows plus chunk rows 0..i.
 //   merge     : log-sum-exp merge of a decode lane's partials into its head

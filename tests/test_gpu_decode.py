@@ -175,8 +175,8 @@ def _decode_case(dtype, B, H, dh, lens, steps, seed, chunk_rows=512):
 
 @pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
 def test_multi_tile_ragged_decode(dtype):
-    """Lengths span several 256-row split-K tiles with ragged tails, an empty prefix and
-    a single row; H=4, d_h=64."""
+    """Ragged lengths: an empty prefix, a single row, one partial tile and a lane of
+    518 rows that crosses the 512-row split-K tile (two partials merged); H=4, d_h=64."""
     _decode_case(dtype, B=4, H=4, dh=64, lens=[0, 1, 300, 517], steps=3, seed=37)
 
 
