@@ -83,6 +83,9 @@ enum {
   KVC_ERR_DTYPE_UNSUPPORTED = 51,
   KVC_ERR_SHAPE_UNSUPPORTED = 52, /* head width not a power of two in [2, 16 B * 64 / elem] */
   KVC_ERR_BAD_ARGUMENT = 53,
+  KVC_ERR_SCRATCH_EXCEEDED = 54, /* kvc_append_and_attend_static: the call needs more scratch
+                                    than the static array holds (expected = its size in bytes,
+                                    actual = bytes needed)                               */
   KVC_ERR_DEVICE = 60,           /* a HIP runtime call failed                              */
   KVC_ERR_DEFERRED = 61,         /* an earlier KVC_ASYNC call failed on the device         */
   KVC_ERR_INTERNAL = 62
@@ -302,6 +305,37 @@ kvc_status kvc_pool_usage(kvc_cache* cache, int32_t* blocks_in_use, int32_t* blo
 kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const void* x,
                                  int32_t rank, const int64_t* shape, void* out, int32_t flags,
                                  kvc_work* work);
+
+/* kvc_append_and_attend for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, checks, results and cache transition as
+ * kvc_append_and_attend (the same kernels with the same launch shapes), but
+ * the call's scratch -- rotated queries, candidate key/value rows, split-K
+ * partials, the projection's split sums and, with W_o, the merged heads --
+ * lives in one file-scope device array of KVC_STATIC_SCRATCH_BYTES per device
+ * instead of the cache's own buffers.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); the array is part of the
+ * library's code object, each device holds its copy until the process ends,
+ * and its address on a device is looked up on the first call there.  The
+ * scratch a call needs, with a = 8 bytes for F64 caches and 4 otherwise and e
+ * the storage element size: queries B * H * d_h * a, candidates
+ * 2 * B * kv_width * e, partials B * H * T * (d_h + 2) * a with
+ * T = ceil(C / 512) (a window cache: ceil((min(C, window) + 512) / 512)),
+ * for bf16 caches of width 2048, 4096 or 8192 with B <= 32 the projection's
+ * split sums 8 * 64 * (D + 2 * kv_width) * 4, and with W_o B * D * a; each
+ * rounded up to 256 bytes.  A call needing more than the array holds (e.g. a
+ * bf16 cache of B = 32, D = 8192, C = 512) fails with SCRATCH_EXCEEDED before
+ * any work; the B = 32, H = 32, d_h = 128, C = 4096 bf16 layer needs 30.5 MB.
+ * Every call on one device shares its array and keeps the previous call's
+ * contents: calls whose stream work overlaps on one device (several threads,
+ * or several streams in KVC_ASYNC mode) race and give undefined results;
+ * serialise them.  In a DEFERRED report after KVC_ASYNC calls, `value` may
+ * not be the offending element (the scratch has been reused).
+ * Errors: those of kvc_append_and_attend, then SCRATCH_EXCEEDED. */
+#define KVC_STATIC_SCRATCH_BYTES (32u << 20)
+kvc_status kvc_append_and_attend_static(const kvc_layer* layer, kvc_cache* cache, const void* x,
+                                        int32_t rank, const int64_t* shape, void* out, int32_t flags,
+                                        kvc_work* work);
 
 /* Suffix-chunk continuation (prefix-reuse note, "What must be trimmed
  * together"): x DEVICE [B, n_max, D]; n_rows HOST int32[B] with 0 <= n_b <=

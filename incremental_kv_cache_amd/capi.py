@@ -40,6 +40,7 @@ KVC_ERR_NULL_ARGUMENT = 50
 KVC_ERR_DTYPE_UNSUPPORTED = 51
 KVC_ERR_SHAPE_UNSUPPORTED = 52
 KVC_ERR_BAD_ARGUMENT = 53
+KVC_ERR_SCRATCH_EXCEEDED = 54
 KVC_ERR_DEVICE = 60
 KVC_ERR_DEFERRED = 61
 KVC_ERR_INTERNAL = 62
@@ -51,6 +52,7 @@ KVC_TRUNCATE_KEEP_STALE_POSITION = 1
 KVC_STAGE_PROJECT, KVC_STAGE_ATTEND, KVC_STAGE_MERGE, KVC_STAGE_COMMIT, KVC_STAGE_OUTPUT = 0, 1, 2, 3, 4
 KVC_STAGES = 5
 KVC_PE_NONE, KVC_PE_SINUSOIDAL = 0, 1
+KVC_STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class ErrorDetail(C.Structure):
@@ -111,6 +113,7 @@ PROTOTYPES = {
     "kvc_fork": (I32, [P, I32, I32, I32]),
     "kvc_pool_usage": (I32, [P, PI32, PI32]),
     "kvc_append_and_attend": (I32, [P, P, P, I32, PI64, P, I32, C.POINTER(Work)]),
+    "kvc_append_and_attend_static": (I32, [P, P, P, I32, PI64, P, I32, C.POINTER(Work)]),
     "kvc_continue_chunk": (I32, [P, P, P, I32, PI32, P, I32, C.POINTER(Work)]),
     "kvc_truncate": (I32, [P, PI32, I32]),
     "kvc_reset": (I32, [P]),

@@ -18,6 +18,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <utility>
 
 #include "kvc_dev_util.h"
@@ -893,6 +894,42 @@ int dev_event_elapsed(float* ms, void* start, void* stop) {
 }
 
 bool dev_has_kernels() { return true; }
+
+}  // namespace kvc
+
+// Scratch of the entry point that allocates nothing (kvc_append_and_attend_static):
+// the query, candidate rows, split-K partials and projection sums of one decode
+// call live here instead of in the cache's own buffers.  Host code must never
+// use this name as an address: it is a host-side stand-in, and only the address
+// hipGetSymbolAddress returns for the current device is valid on that device.
+static __device__ __align__(256) unsigned char scratch[kvc::kStaticScratchBytes];
+
+namespace kvc {
+
+int dev_static_scratch(int device, void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return int(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != device) e = hipSetDevice(device);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != device) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return int(e);
+    if (!p) return int(hipErrorInvalidSymbol);
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  *bytes = kStaticScratchBytes;
+  return 0;
+}
 
 int dev_embed(const DevState& s, const int32_t* tokens, const void* embedding, int vocab, int sinusoidal,
               int n_max, int per_seq_rows, void* h, void* x) {

@@ -601,25 +601,25 @@ kvc_status run_call(kvc_cache* c, const void* x, int n_max, const int32_t* n_row
 // when a workgroup serves several query heads);
 // measured on the bench workloads, fewer and longer tiles stream faster than a
 // finer split.
+int64_t decode_span_rows(const kvc_cache* cache, int b) {
+  // rows the newest query of sequence b reads from its tile-aligned start (the
+  // whole prefix, or the window rounded down to a tile boundary)
+  const int64_t len = cache->len[b];
+  const int64_t rs = cache->window ? std::max<int64_t>(0, len - cache->window + 1) : 0;
+  return len + 1 - (rs - rs % kDecodeTileRows);
+}
+
 void choose_decode_tiles(kvc_cache* cache) {
   int tile = kDecodeTileRows;
-  // rows each query reads from its tile-aligned start (the whole prefix, or
-  // the window rounded down to a tile boundary)
-  std::vector<int64_t> span(cache->batch);
   int64_t max_len = 0;
-  for (int b = 0; b < cache->batch; ++b) {
-    const int64_t len = cache->len[b];
-    const int64_t rs = cache->window ? std::max<int64_t>(0, len - cache->window + 1) : 0;
-    span[b] = len + 1 - (rs - rs % kDecodeTileRows);
-    max_len = std::max(max_len, span[b] - 1);
-  }
+  for (int b = 0; b < cache->batch; ++b) max_len = std::max(max_len, decode_span_rows(cache, b) - 1);
   // a workgroup serving several query heads does that many times the work per
   // row it reads: half as many (longer) tiles measured faster for them
   const int qpw = decode_heads_per_block(cache->dtype, cache->head_width, cache->heads / cache->kv_heads);
   const int64_t min_blocks = qpw > 1 ? 512 : 1024;
   for (int64_t cand = kDecodeTileRows; cand <= (int64_t(1) << 30); cand *= 2) {
     int64_t blocks = 0;
-    for (int b = 0; b < cache->batch; ++b) blocks += (span[b] - 1 + cand) / cand;
+    for (int b = 0; b < cache->batch; ++b) blocks += (decode_span_rows(cache, b) - 1 + cand) / cand;
     if (blocks * (cache->heads / qpw) < min_blocks) break;
     tile = int(cand);
     if (cand > max_len) break;
@@ -630,6 +630,99 @@ void choose_decode_tiles(kvc_cache* cache) {
 
 kvc_status reject_session_cache(const char* what) {
   return fail(KVC_ERR_BAD_ARGUMENT, "%s: this cache is a layer of a session; use the kvc_session_* calls", what);
+}
+
+// The request checks of a decode call, in Chapter 37's order ("Bind the state,
+// calculate completely, then commit": rank, one token, batch, width, binding,
+// capacity), then the rotary position; fills the call's row counts.
+kvc_status decode_checks(const char* what, const kvc_layer* layer, kvc_cache* cache, const void* x, int32_t rank,
+                         const int64_t* shape, void* out, int32_t flags, kvc_work* w) {
+  if (!layer || !cache || !x || !out || (rank > 0 && !shape))
+    return fail(KVC_ERR_NULL_ARGUMENT, "null argument to %s", what);
+  if (cache->session) return reject_session_cache(what);
+  if (flags & ~int32_t(KVC_ASYNC)) return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
+  if (!(flags & KVC_ASYNC)) {
+    kvc_status d = check_deferred(cache);
+    if (d != KVC_OK) return d;
+  }
+  if (rank != 3) return fail_ea(KVC_ERR_INPUT_RANK, 3, rank, "incremental input must have rank 3, got %d", rank);
+  if (shape[1] != 1)
+    return fail_ea(KVC_ERR_SINGLE_TOKEN_REQUIRED, 1, shape[1],
+                   "incremental attention accepts exactly one token, got %lld", (long long)shape[1]);
+  if (shape[0] != cache->batch)
+    return fail_ea(KVC_ERR_INPUT_BATCH_MISMATCH, cache->batch, shape[0],
+                   "incremental input batch %lld does not match cache batch %d", (long long)shape[0],
+                   cache->batch);
+  if (shape[2] != layer->params->model_width)
+    return fail_ea(KVC_ERR_INPUT_WIDTH_MISMATCH, layer->params->model_width, shape[2],
+                   "incremental input width %lld does not match model width %d", (long long)shape[2],
+                   layer->params->model_width);
+  kvc_status st = check_binding(layer, cache);
+  if (st != KVC_OK) return st;
+  for (int b = 0; b < cache->batch; ++b) {
+    if (!cache->window && cache->len[b] >= cache->capacity) {  // a window cache is a ring
+      g_last.sequence = b;
+      return fail_ea(KVC_ERR_FULL, cache->capacity, cache->len[b],
+                     "sequence %d already holds %d rows, all the cache has room for", b, cache->capacity);
+    }
+  }
+  if (cache->ds.rope) {
+    for (int b = 0; b < cache->batch; ++b) {
+      if (cache->next_pos[b] >= cache->rope_max_positions) {
+        g_last.sequence = b;
+        return fail_ea(KVC_ERR_ROTARY_POSITION, cache->rope_max_positions, cache->next_pos[b],
+                       "position %d of sequence %d reaches the rotary position capacity %d",
+                       cache->next_pos[b], b, cache->rope_max_positions);
+      }
+    }
+  }
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "library built without device kernels");
+  *w = kvc_work{};
+  w->position_min = INT32_MAX;
+  w->position_max = -1;
+  for (int b = 0; b < cache->batch; ++b) {
+    w->full_prefix_rows_per_projection += cache->len[b] + 1;
+    w->incremental_rows_per_projection += 1;
+    w->reused_key_value_rows += cache->len[b];
+    w->position_min = std::min(w->position_min, cache->next_pos[b]);
+    w->position_max = std::max(w->position_max, cache->next_pos[b]);
+  }
+  return KVC_OK;
+}
+
+// Byte offsets, inside one scratch region, of the buffers a decode call of a
+// cache uses beyond its inputs and outputs: the rotated queries [B, H, d_h],
+// the candidate key and value rows [B, H_kv, d_h], the split-K partials
+// [B, H, max_tiles, d_h + 2], the skinny projection's split sums (when the
+// cache has them) and the merged heads before W_o [B, D] (when it has W_o);
+// each starts on a 256-byte boundary.  The sizes are those of the cache's own
+// buffers at one row per sequence, so both entry points run the same kernels
+// with the same launch shapes.
+struct ScratchLayout {
+  size_t q, cand_k, cand_v, partials, proj, merged, total;
+};
+
+ScratchLayout decode_scratch_layout(const kvc_cache* c) {
+  auto r256 = [](size_t b) { return (b + 255) & ~size_t(255); };
+  const size_t es = elem_size(c->dtype), as = acc_size(c->dtype);
+  const size_t B = size_t(c->batch), H = size_t(c->heads), HK = size_t(c->kv_heads), dh = size_t(c->head_width);
+  ScratchLayout L{};
+  size_t at = 0;
+  L.q = at;
+  at += r256(B * H * dh * as);
+  L.cand_k = at;
+  at += r256(B * HK * dh * es);
+  L.cand_v = at;
+  at += r256(B * HK * dh * es);
+  L.partials = at;
+  at += r256(B * H * size_t(c->ds.max_tiles) * (dh + 2) * as);
+  L.proj = at;
+  if (c->ds.proj_partials)
+    at += r256(sizeof(float) * kSkinnySplitMax * 64 * size_t(c->model_width + 2 * c->ds.kv_width));
+  L.merged = at;
+  if (c->ds.merged) at += r256(B * size_t(c->model_width) * as);
+  L.total = at;
+  return L;
 }
 
 // Cache construction.  shared_err: NULL for a standalone cache (it allocates
@@ -1064,6 +1157,7 @@ const char* kvc_status_name(kvc_status s) {
     N(KVC_ERR_DTYPE_UNSUPPORTED)
     N(KVC_ERR_SHAPE_UNSUPPORTED)
     N(KVC_ERR_BAD_ARGUMENT)
+    N(KVC_ERR_SCRATCH_EXCEEDED)
     N(KVC_ERR_DEVICE)
     N(KVC_ERR_DEFERRED)
     N(KVC_ERR_INTERNAL)
@@ -1184,60 +1278,48 @@ void kvc_cache_destroy(kvc_cache* cache) {
 kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const void* x, int32_t rank,
                                  const int64_t* shape, void* out, int32_t flags, kvc_work* work) {
   reset_detail();
-  if (!layer || !cache || !x || !out || (rank > 0 && !shape))
-    return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_append_and_attend");
-  if (cache->session) return reject_session_cache("kvc_append_and_attend");
-  if (flags & ~int32_t(KVC_ASYNC)) return fail(KVC_ERR_BAD_ARGUMENT, "unknown flags %d", flags);
-  if (!(flags & KVC_ASYNC)) {
-    kvc_status d = check_deferred(cache);
-    if (d != KVC_OK) return d;
-  }
-  // Chapter 37, "Bind the state, calculate completely, then commit": rank,
-  // one token, batch, width, binding, capacity -- in that order.
-  if (rank != 3) return fail_ea(KVC_ERR_INPUT_RANK, 3, rank, "incremental input must have rank 3, got %d", rank);
-  if (shape[1] != 1)
-    return fail_ea(KVC_ERR_SINGLE_TOKEN_REQUIRED, 1, shape[1],
-                   "incremental attention accepts exactly one token, got %lld", (long long)shape[1]);
-  if (shape[0] != cache->batch)
-    return fail_ea(KVC_ERR_INPUT_BATCH_MISMATCH, cache->batch, shape[0],
-                   "incremental input batch %lld does not match cache batch %d", (long long)shape[0],
-                   cache->batch);
-  if (shape[2] != layer->params->model_width)
-    return fail_ea(KVC_ERR_INPUT_WIDTH_MISMATCH, layer->params->model_width, shape[2],
-                   "incremental input width %lld does not match model width %d", (long long)shape[2],
-                   layer->params->model_width);
-  kvc_status st = check_binding(layer, cache);
-  if (st != KVC_OK) return st;
-  for (int b = 0; b < cache->batch; ++b) {
-    if (!cache->window && cache->len[b] >= cache->capacity) {  // a window cache is a ring
-      g_last.sequence = b;
-      return fail_ea(KVC_ERR_FULL, cache->capacity, cache->len[b],
-                     "sequence %d already holds %d rows, all the cache has room for", b, cache->capacity);
-    }
-  }
-  if (cache->ds.rope) {
-    for (int b = 0; b < cache->batch; ++b) {
-      if (cache->next_pos[b] >= cache->rope_max_positions) {
-        g_last.sequence = b;
-        return fail_ea(KVC_ERR_ROTARY_POSITION, cache->rope_max_positions, cache->next_pos[b],
-                       "position %d of sequence %d reaches the rotary position capacity %d",
-                       cache->next_pos[b], b, cache->rope_max_positions);
-      }
-    }
-  }
-  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "library built without device kernels");
   kvc_work w{};
-  w.position_min = INT32_MAX;
-  w.position_max = -1;
-  for (int b = 0; b < cache->batch; ++b) {
-    w.full_prefix_rows_per_projection += cache->len[b] + 1;
-    w.incremental_rows_per_projection += 1;
-    w.reused_key_value_rows += cache->len[b];
-    w.position_min = std::min(w.position_min, cache->next_pos[b]);
-    w.position_max = std::max(w.position_max, cache->next_pos[b]);
-  }
+  kvc_status st = decode_checks("kvc_append_and_attend", layer, cache, x, rank, shape, out, flags, &w);
+  if (st != KVC_OK) return st;
   choose_decode_tiles(cache);
   st = run_call(cache, x, 1, nullptr, out, flags, true);
+  if (st == KVC_OK && work) *work = w;
+  return st;
+}
+
+kvc_status kvc_append_and_attend_static(const kvc_layer* layer, kvc_cache* cache, const void* x, int32_t rank,
+                                        const int64_t* shape, void* out, int32_t flags, kvc_work* work) {
+  reset_detail();
+  kvc_work w{};
+  kvc_status st = decode_checks("kvc_append_and_attend_static", layer, cache, x, rank, shape, out, flags, &w);
+  if (st != KVC_OK) return st;
+  void* base = nullptr;
+  size_t cap = 0;
+  const int rc = dev_static_scratch(cache->device, &base, &cap);
+  if (rc) return device_fail(rc, "looking up the static scratch");
+  const ScratchLayout L = decode_scratch_layout(cache);
+  if (L.total > cap)
+    return fail_ea(KVC_ERR_SCRATCH_EXCEEDED, int64_t(cap), int64_t(L.total),
+                   "a decode step of this cache needs %zu bytes of scratch, the static scratch holds %zu", L.total,
+                   cap);
+  // the call's scratch pointers point into the static array for its duration
+  DevState& s = cache->ds;
+  void* const own[6] = {s.q, s.cand_k, s.cand_v, s.partials, s.proj_partials, s.merged};
+  char* b = static_cast<char*>(base);
+  s.q = b + L.q;
+  s.cand_k = b + L.cand_k;
+  s.cand_v = b + L.cand_v;
+  s.partials = b + L.partials;
+  s.proj_partials = s.proj_partials ? reinterpret_cast<float*>(b + L.proj) : nullptr;
+  s.merged = s.merged ? b + L.merged : nullptr;
+  choose_decode_tiles(cache);
+  st = run_call(cache, x, 1, nullptr, out, flags, true);
+  s.q = own[0];
+  s.cand_k = own[1];
+  s.cand_v = own[2];
+  s.partials = own[3];
+  s.proj_partials = static_cast<float*>(own[4]);
+  s.merged = own[5];
   if (st == KVC_OK && work) *work = w;
   return st;
 }

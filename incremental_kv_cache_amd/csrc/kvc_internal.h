@@ -201,4 +201,11 @@ int dev_stream_read(const void* buf, int64_t bytes, void* sink, void* stream);
 // True when the backend can run kernels (false in the CPU-only host-check build).
 bool dev_has_kernels();
 
+// Scratch of kvc_append_and_attend_static: a file-scope device array of this
+// many bytes in the backend's code object (one copy per device, held until the
+// process ends).  Its device address on `device` is looked up once per device,
+// with that device current, and kept; later calls return the kept address.
+constexpr size_t kStaticScratchBytes = KVC_STATIC_SCRATCH_BYTES;
+int dev_static_scratch(int device, void** ptr, size_t* bytes);
+
 }  // namespace kvc

@@ -274,6 +274,17 @@ def kvc_cache_describe(cache: Cache) -> dict:
 def kvc_append_and_attend(layer: Layer, cache: Cache, x, out=None, flags: int = KVC_SYNC):
     """x: device tensor [B, 1, D] (any rank is passed through for the rank check).
     Returns (out [B, 1, D], work dict)."""
+    return _decode_call("kvc_append_and_attend", layer, cache, x, out, flags)
+
+
+def kvc_append_and_attend_static(layer: Layer, cache: Cache, x, out=None, flags: int = KVC_SYNC):
+    """kvc_append_and_attend whose scratch is the library's static device array:
+    the call allocates nothing (pass ``out`` to keep the binding from allocating
+    either).  Returns (out [B, 1, D], work dict)."""
+    return _decode_call("kvc_append_and_attend_static", layer, cache, x, out, flags)
+
+
+def _decode_call(name: str, layer: Layer, cache: Cache, x, out, flags: int):
     lib = cache._lib
     code = cache.desc["kv_dtype"]
     if _dtype_code(x) != code:
@@ -285,8 +296,8 @@ def kvc_append_and_attend(layer: Layer, cache: Cache, x, out=None, flags: int = 
     _check_out(out, out_shape, code, x)
     shape = (C.c_int64 * max(1, x.dim()))(*[int(s) for s in x.shape])
     w = capi.Work()
-    _check(lib, lib.kvc_append_and_attend(layer.ptr, cache.ptr, _dev_ptr(x), x.dim(), shape, _dev_ptr(out), flags,
-                                          C.byref(w)))
+    _check(lib, getattr(lib, name)(layer.ptr, cache.ptr, _dev_ptr(x), x.dim(), shape, _dev_ptr(out), flags,
+                                   C.byref(w)))
     return out, w.as_dict()
 
 

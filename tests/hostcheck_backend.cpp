@@ -199,6 +199,16 @@ int dev_event_elapsed(float* ms, void*, void*) {
 }
 int dev_stream_read(const void*, int64_t, void*, void*) { return 1; }
 bool dev_has_kernels() { return g_fake; }
+// The no-allocation entry point's scratch: host memory here, and a smaller
+// size (kvc_test_static_scratch_bytes) so that the size check can be tested.
+static size_t g_static_bytes = kStaticScratchBytes;
+int dev_static_scratch(int, void** ptr, size_t* bytes) {
+  static void* mem = std::aligned_alloc(256, kStaticScratchBytes);
+  if (!mem) return 2;
+  *ptr = mem;
+  *bytes = g_static_bytes;
+  return 0;
+}
 
 }  // namespace kvc
 
@@ -209,6 +219,9 @@ extern "C" void kvc_test_fake_kernels(int on) {
   kvc::g_fail_next = -1;
 }
 extern "C" void kvc_test_fail_next(long long flat_index) { kvc::g_fail_next = flat_index; }
+extern "C" void kvc_test_static_scratch_bytes(unsigned long long bytes) {
+  kvc::g_static_bytes = bytes ? size_t(bytes) : kvc::kStaticScratchBytes;
+}
 extern "C" int kvc_test_chunk_order(int batch, int n_max, const int32_t* len, const int32_t* rows, int32_t* qtiles,
                                     int32_t* items) {
   kvc::ChunkOrder o;

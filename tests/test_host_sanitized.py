@@ -15,7 +15,8 @@ import sys
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SUITES = ["tests/test_host_manager.py", "tests/test_host_paging.py", "tests/test_host_window.py"]
+SUITES = ["tests/test_host_manager.py", "tests/test_host_paging.py", "tests/test_host_window.py",
+          "tests/test_host_static_scratch.py"]
 
 
 def _runtime(name):
