@@ -5,9 +5,17 @@
 A step is one cached decode step of one layer over the whole batch: the new
 rows' Q/K/V projection with RoPE, split-K attention over every retained row
 plus the candidate row, the log-sum-exp merge, and the predicated append
-(kvc_append_and_attend), preceded by kvc_truncate back to the starting length
-so that every timed step sees the same t.  Inputs (weights, hidden rows, the
+(kvc_append_and_attend).  Each step is timed with HIP events recorded on the
+cache's stream around that call alone; before each step, outside the event
+pair, kvc_truncate cuts the cache back to its starting length so that every
+timed step sees the same t (the wall-clock time of the whole loop, truncation
+included, is reported beside it).  Inputs (weights, hidden rows, the
 prefilled cache) are seeded synthetic data resident in HBM before timing.
+
+The default run (headline workload) also measures the long-context decode
+and the suffix-chunk workloads and reports them under "other_configs" of the
+same line, with the achievable streaming-read bandwidth and matrix-core rate
+of the box as yardsticks.
 
 Workloads (default: headline):
   headline  B=32, H=32, d_h=128, C=4096, t=4096 for every sequence, bf16 K/V
@@ -184,25 +192,39 @@ def measured_traffic(name):
     return m["fetch_kib"] * 1024 * m["fetch_scale"] + m["write_kib"] * 1024 * m["write_scale"]
 
 
-def time_steps(step, steps, warmup):
+def time_steps(pre, call, steps, warmup):
+    """W untimed warm-up steps, then K steps, each `pre()` (outside the timing)
+    then `call()` between two HIP events on the current stream (the cache's).
+    Returns (mean event ms per step, p10/p50/p90 of the event ms, wall-clock ms
+    per step of the whole loop, `pre` and host time included)."""
     import torch
     for _ in range(warmup):
-        step()
+        pre()
+        call()
     torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
+    for a, b in ev:
+        pre()
+        a.record()
+        call()
+        b.record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    pct = {"p10": float(np.percentile(ms, 10)), "p50": float(np.percentile(ms, 50)),
+           "p90": float(np.percentile(ms, 90))}
+    return float(ms.mean()), pct, wall
 
 
-def stage_times(cache, step, steps):
+def stage_times(cache, pre, call, steps):
     """Average per-stage kernel time (ms) from the library's HIP events."""
     import torch
     from incremental_kv_cache_amd import kvcache as K
     K.kvc_profile_enable(cache, steps)
     for _ in range(steps):
-        step()
+        pre()
+        call()
     torch.cuda.synchronize()
     ms, calls = K.kvc_profile_read(cache)
     K.kvc_profile_enable(cache, 0)
@@ -215,6 +237,20 @@ def _cores():
         return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         return os.cpu_count() or 1
+
+
+def _blas_threads():
+    """Threads of the BLAS library numpy calls (the oracle's matrix products)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return {i.get("internal_api", "?"): i.get("num_threads") for i in threadpool_info()
+                if i.get("user_api") == "blas"}
+    except Exception:
+        return {}
+
+
+def host_info():
+    return {"cpu_count": os.cpu_count(), "blas_threads": _blas_threads()}
 
 
 def cpu_baseline_decode(env, wl, out_gpu, x_bits, budget_s=25.0, step_budget_s=10.0):
@@ -271,7 +307,12 @@ def cpu_baseline_decode(env, wl, out_gpu, x_bits, budget_s=25.0, step_budget_s=1
                       f"({reps} per sequence), {t_inc:.2f}s of CPU work",
             "full_prefix_recompute": {"value": done / t_full, "unit": "tokens/s",
                                       "sample": f"same sequences, projection of all t rows + newest-row "
-                                                f"attention, {t_full:.1f}s of CPU work"}}, worst, done
+                                                f"attention, {t_full:.1f}s of CPU work",
+                                      "seconds_per_sequence": t_full / done,
+                                      "scaled_step_seconds": wl["B"] * t_full / done,
+                                      "scaled": f"one sequence's measured time x B = {wl['B']} "
+                                                f"(a whole-batch step, not measured)"},
+            **host_info()}, worst, done
 
 
 def cpu_baseline_chunk(env, wl, out_gpu, x_bits, budget_rows=512):
@@ -301,7 +342,7 @@ def cpu_baseline_chunk(env, wl, out_gpu, x_bits, budget_rows=512):
     worst = float(np.max(np.abs(out_gpu[b, :n] - out)))
     return {"value": n / dt, "unit": "tokens/s", "cores": int(_cores()), "kind": "oracle",
             "sample": f"float64 oracle continue_chunk of {n} rows on sequence {b} (cut {cut}), "
-                      f"{dt:.1f}s of CPU work"}, worst
+                      f"{dt:.1f}s of CPU work", **host_info()}, worst
 
 
 def achievable_read_gbps(nbytes=4 << 30, reps=10):
@@ -325,18 +366,26 @@ def achievable_read_gbps(nbytes=4 << 30, reps=10):
     return gbps
 
 
-def step_percentiles(step, steps):
-    """p10 / p50 / p90 of one step's duration (ms), from events around each step."""
+def achievable_mfma_tflops(iters=5000, reps=5):
+    """bf16 matrix-core rate of a register-only MFMA loop over every compute unit
+    (kvc_mfma_rate), timed with events on the current stream."""
     import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for a, b in ev:
-        a.record()
-        step()
-        b.record()
+    from incremental_kv_cache_amd import kvcache as K
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    K.kvc_mfma_rate(iters // 10, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flops = sum(K.kvc_mfma_rate(iters, sink) for _ in range(reps))
+    e1.record()
     torch.cuda.synchronize()
-    ms = np.array([a.elapsed_time(b) for a, b in ev])
-    return {"p10": float(np.percentile(ms, 10)), "p50": float(np.percentile(ms, 50)),
-            "p90": float(np.percentile(ms, 90))}
+    return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
+def inputs_sha256(env, *arrays):
+    """SHA-256 of the workload's synthetic inputs: weight bits, starting lengths,
+    and the step's input rows."""
+    from incremental_kv_cache_amd import synth
+    return synth.sha256(*env["weights_bits"], np.asarray(env["start"], np.int64), *arrays)
 
 
 def run_decode(name, wl, steps, warmup, cpu):
@@ -353,17 +402,18 @@ def run_decode(name, wl, steps, warmup, cpu):
     x = to_dev_bf16(x_bits.reshape(B, 1, D).copy())
     out = torch.empty(B, 1, D, dtype=torch.float32, device="cuda")
 
-    def step():
+    def pre():
         K.kvc_truncate(cache, start)
+
+    def call():
         K.kvc_append_and_attend(layer, cache, x, out=out, flags=K.KVC_ASYNC)
 
-    sec = time_steps(step, steps, warmup)
+    ms, pct, wall_ms = time_steps(pre, call, steps, warmup)
+    sec = ms * 1e-3
     K.kvc_sync(cache)
-    st = stage_times(cache, step, steps)
+    st = stage_times(cache, pre, call, steps)
     K.kvc_sync(cache)
-    pct = step_percentiles(step, steps)
     paging = paging_summary(env, wl) if wl.get("block_rows") else None
-    K.kvc_sync(cache)
     torch.cuda.synchronize()
     achievable = achievable_read_gbps()
     t = [s + 1 for s in start]
@@ -374,8 +424,9 @@ def run_decode(name, wl, steps, warmup, cpu):
     attn_merge_gbps = kv_bytes / ((st[1] + st[2]) * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": B / sec, "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
-        "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
+        "ms_per_step": sec * 1e3, "wall_ms_per_step": wall_ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "inputs_sha256": inputs_sha256(env, x_bits),
         "config": {"workload": f"{name}: one-layer cached decode, B={B} H={H} d_h={dh} C={wl['C']} "
                                f"t={'uniform[1,%d]' % wl['C'] if wl['t'] == 'uniform' else t[0]}, bf16 K/V"
                                f"{', block-paged %d-row blocks' % wl['block_rows'] if paging else ''}"
@@ -414,25 +465,28 @@ def run_chunk(name, wl, steps, warmup, cpu):
     x = to_dev_bf16(bits)
     out = torch.zeros(B, n, D, dtype=torch.float32, device="cuda")
 
-    def step():
+    def pre():
         K.kvc_truncate(cache, start)
+
+    def call():
         K.kvc_continue_chunk(layer, cache, x, out=out, flags=K.KVC_ASYNC)
 
-    sec = time_steps(step, steps, warmup)
+    ms, pct, wall_ms = time_steps(pre, call, steps, warmup)
+    sec = ms * 1e-3
     K.kvc_sync(cache)
-    st = stage_times(cache, step, steps)
-    K.kvc_sync(cache)
-    pct = step_percentiles(step, steps)
+    st = stage_times(cache, pre, call, steps)
     K.kvc_sync(cache)
     torch.cuda.synchronize()
+    mfma_tf = achievable_mfma_tflops()
     attn_flops = sum(4 * H * dh * sum(c + i + 1 for i in range(n)) for c in start)
     proj_flops = 2 * B * n * D * 3 * D
     att_tf = attn_flops / (st[1] * 1e-3) / 1e12
     proj_tf = proj_flops / (st[0] * 1e-3) / 1e12
     res = {
         "metric": "suffix-chunk tokens/s (MFMA utilisation)", "value": B * n / sec, "unit": "tokens/s",
-        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "n_gpus": 1, "steps": steps, "warmup": warmup, "ms_per_step": sec * 1e3, "wall_ms_per_step": wall_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "inputs_sha256": inputs_sha256(env, bits),
         "config": {"workload": f"{name}: suffix chunk n={n}, B={B} H={H} d_h={dh} C={wl['C']} "
                                f"cut uniform[0,{wl['cut_max']}], bf16", "cuts": start, "seed": SEED},
         "step_ms_percentiles": pct,
@@ -440,11 +494,13 @@ def run_chunk(name, wl, steps, warmup, cpu):
         # the projection is the step's largest kernel; the attention's figures follow it
         "roofline": {"bound": "mfma", "kernel": "project_wide_kernel", "achieved": proj_tf,
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": proj_tf / BF16_PEAK_TFLOPS,
-                     "traffic": measured_traffic(name), "algorithmic_flops_per_launch": proj_flops},
+                     "traffic": measured_traffic(name), "algorithmic_flops_per_launch": proj_flops,
+                     "achievable_tflops": mfma_tf, "frac_of_achievable": proj_tf / mfma_tf},
         "attention_roofline": {"bound": "mfma", "kernel": "attend_flash_kernel", "achieved": att_tf,
                                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": att_tf / BF16_PEAK_TFLOPS,
                                "traffic": measured_traffic("chunk_attention"),
-                               "algorithmic_flops_per_launch": attn_flops},
+                               "algorithmic_flops_per_launch": attn_flops,
+                               "achievable_tflops": mfma_tf, "frac_of_achievable": att_tf / mfma_tf},
     }
     if cpu:
         cb, worst = cpu_baseline_chunk(env, wl, out.double().cpu().numpy(), bits)
@@ -485,16 +541,20 @@ def run_session(name, wl, steps, warmup, cpu):
     tok = torch.from_numpy(np.ascontiguousarray(toks[:, start])).cuda()
     out = torch.empty(B, 1, D, dtype=torch.float32, device="cuda")
 
-    def step():
+    def pre():
         K.kvc_session_truncate(sess, [start] * B)
+
+    def call():
         K.kvc_session_decode(sess, tok, out=out, flags=K.KVC_ASYNC)
 
-    sec = time_steps(step, steps, warmup)
+    ms, pct, wall_ms = time_steps(pre, call, steps, warmup)
+    sec = ms * 1e-3
     K.kvc_session_sync(sess)
     for c in sess.caches:
         K.kvc_profile_enable(c, steps)
     for _ in range(steps):
-        step()
+        pre()
+        call()
     torch.cuda.synchronize()
     att = []
     for c in sess.caches:
@@ -502,15 +562,13 @@ def run_session(name, wl, steps, warmup, cpu):
         att.append(ms[1] / calls[1])
         K.kvc_profile_enable(c, 0)
     K.kvc_session_sync(sess)
-    pct = step_percentiles(step, steps)
-    K.kvc_session_sync(sess)
     kv_bytes = 2 * B * H * C * dh * 2  # per layer: t = C rows per lane
     attend_ms = float(np.mean(att))
     att_gbps = kv_bytes / (attend_ms * 1e-3) / 1e9
     return {
         "metric": f"model-wide decode tokens/s ({L} layers)", "value": B / sec, "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": warmup, "ms_per_step": sec * 1e3, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "steps": steps, "warmup": warmup, "ms_per_step": sec * 1e3, "wall_ms_per_step": wall_ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{name}: {L}-layer session, B={B} H={H} d_h={dh} C={C} t={C}, vocab {V}, "
                                f"sinusoidal positions, tanh residual, bf16 K/V", "layers": L, "seed": SEED},
         "step_ms_percentiles": pct,
@@ -528,6 +586,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="headline only: skip the long-context and suffix-chunk measurements")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times), to scale HBM byte counters")
     a = ap.parse_args()
@@ -552,6 +612,21 @@ def main():
     wl = WORKLOADS[a.workload]
     fn = {"decode": run_decode, "chunk": run_chunk, "session": run_session}[wl["kind"]]
     res = fn(a.workload, wl, a.steps, a.warmup, not a.no_cpu_baseline)
+    if a.workload == "headline" and not a.no_other_configs:
+        # the other measured workloads, one after the other on the same GPU
+        # (each cache freed before the next is built); no CPU baselines for them
+        import gc
+        res["other_configs"] = {}
+        for other in ("long", "chunk"):
+            gc.collect()
+            torch.cuda.empty_cache()
+            log(f"other config: {other}")
+            r = {"decode": run_decode, "chunk": run_chunk}[WORKLOADS[other]["kind"]](
+                other, WORKLOADS[other], a.steps, a.warmup, False)
+            res["other_configs"][other] = {k: r[k] for k in (
+                "metric", "value", "unit", "ms_per_step", "wall_ms_per_step", "step_ms_percentiles", "stage_ms",
+                "roofline", "attention_roofline", "kv_read_GBps", "kv_read_frac_of_peak", "config",
+                "inputs_sha256") if k in r}
     print(json.dumps(res), flush=True)
 
 

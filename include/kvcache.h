@@ -447,6 +447,19 @@ kvc_status kvc_profile_read(kvc_cache* cache, float* ms_out, int32_t* calls_out)
  * Errors: NULL_ARGUMENT, BAD_ARGUMENT (size or alignment), DEVICE. */
 kvc_status kvc_stream_read(const void* buf, int64_t bytes, void* sink, void* hip_stream);
 
+/* Measurement helper: the achievable bf16 matrix-core rate, the yardstick of
+ * the suffix chunk's projection and causal attention (prefix-reuse note, "What
+ * must be trimmed together": the suffix rows go through the model as one
+ * chunk, a dense contraction) besides the nominal peak.  Launches, on
+ * `hip_stream` (NULL: the default stream), two waves per SIMD on every compute
+ * unit, each issuing `iterations` rounds of eight independent 32x32x16 bf16
+ * MFMAs on register operands with no memory traffic; *flops_out (HOST)
+ * receives the launch's floating-point operations, so timing the launch gives
+ * FLOP/s.  `sink`: DEVICE, 16 writable bytes (written only for one improbable
+ * sum).  No synchronisation.  Errors: NULL_ARGUMENT, BAD_ARGUMENT (iterations
+ * outside [1, 2^24]), DEVICE. */
+kvc_status kvc_mfma_rate(int64_t iterations, void* sink, void* hip_stream, double* flops_out);
+
 /* ---- Model-wide session ----------------------------------------------
  * Several layers behind one token stream, with one cache per layer (Chapter
  * 37, "Give every decoder block its own state next": a model-wide session

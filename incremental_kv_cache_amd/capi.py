@@ -127,6 +127,7 @@ PROTOTYPES = {
     "kvc_profile_enable": (I32, [P, I32]),
     "kvc_profile_read": (I32, [P, C.POINTER(C.c_float), PI32]),
     "kvc_stream_read": (I32, [P, I64, P, P]),
+    "kvc_mfma_rate": (I32, [I64, P, P, C.POINTER(C.c_double)]),
     "kvc_session_create": (I32, [PP, I32, P, I32, I32, I32, I32, I32, P, PP]),
     "kvc_session_destroy": (None, [P]),
     "kvc_session_chunk": (I32, [P, P, I32, PI32, P, I32, C.POINTER(Work)]),

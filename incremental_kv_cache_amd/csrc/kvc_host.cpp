@@ -1743,6 +1743,18 @@ kvc_status kvc_stream_read(const void* buf, int64_t bytes, void* sink, void* hip
   return KVC_OK;
 }
 
+kvc_status kvc_mfma_rate(int64_t iterations, void* sink, void* hip_stream, double* flops_out) {
+  reset_detail();
+  if (!sink || !flops_out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_mfma_rate");
+  if (iterations <= 0 || iterations > (int64_t(1) << 24))
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, int64_t(1) << 24, iterations, "iterations %lld outside [1, 2^24]",
+                   (long long)iterations);
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "library built without device kernels");
+  const int rc = dev_mfma_rate(iterations, sink, hip_stream, flops_out);
+  if (rc) return device_fail(rc, "matrix-core probe launch");
+  return KVC_OK;
+}
+
 kvc_status kvc_session_create(const kvc_layer* const* layers, int32_t n_layers, const void* embedding,
                               int32_t vocab, int32_t position_encoding, int32_t batch, int32_t capacity,
                               int32_t max_chunk_rows, void* hip_stream, kvc_session** out) {

@@ -197,6 +197,11 @@ int dev_event_elapsed(float* ms, void* start, void* stop);
 // `sink` receives a store only for one improbable xor of the data.
 constexpr int64_t kProbeUnitBytes = 32768;
 int dev_stream_read(const void* buf, int64_t bytes, void* sink, void* stream);
+// Matrix-core rate probe: `iterations` rounds of independent bf16 32x32x16
+// MFMAs per wave, two waves per SIMD on every compute unit; *flops receives the
+// launch's floating-point operations.  `sink` receives a store only for one
+// improbable sum.
+int dev_mfma_rate(int64_t iterations, void* sink, void* stream, double* flops);
 
 // True when the backend can run kernels (false in the CPU-only host-check build).
 bool dev_has_kernels();

@@ -401,6 +401,18 @@ def kvc_stream_read(buf, sink, stream=None, *, lib=None) -> None:
     _check(lib, lib.kvc_stream_read(_dev_ptr(buf), nbytes, _dev_ptr(sink), C.c_void_p(stream or 0)))
 
 
+def kvc_mfma_rate(iterations: int, sink, stream=None, *, lib=None) -> float:
+    """Launches the matrix-core rate probe on ``stream`` (default: torch's current
+    stream); returns the launch's floating-point operations.  ``sink``: >= 16-byte
+    device tensor."""
+    lib = _lib(lib)
+    if stream is None:
+        stream = _torch().cuda.current_stream().cuda_stream
+    flops = C.c_double()
+    _check(lib, lib.kvc_mfma_rate(int(iterations), _dev_ptr(sink), C.c_void_p(stream or 0), C.byref(flops)))
+    return flops.value
+
+
 def kvc_lcp_cut(cached, query, *, lib=None) -> int:
     lib = _lib(lib)
     a = np.ascontiguousarray(np.asarray(cached, dtype=np.int32))

@@ -198,6 +198,10 @@ int dev_event_elapsed(float* ms, void*, void*) {
   return 0;
 }
 int dev_stream_read(const void*, int64_t, void*, void*) { return 1; }
+int dev_mfma_rate(int64_t, void*, void*, double* flops) {
+  *flops = 0;
+  return 1;
+}
 bool dev_has_kernels() { return g_fake; }
 // The no-allocation entry point's scratch: host memory here, and a smaller
 // size (kvc_test_static_scratch_bytes) so that the size check can be tested.

@@ -232,7 +232,7 @@ def test_null_arguments(lib):
 
 
 def test_stream_read_argument_checks(lib):
-    """The bandwidth probe checks its arguments on the host before any launch."""
+    """The bandwidth and matrix-core probes check their arguments on the host before any launch."""
     buf = C.c_void_p(4096)
     sink = C.c_void_p(8192)
     assert lib.kvc_stream_read(None, 32768, sink, None) == capi.KVC_ERR_NULL_ARGUMENT
@@ -243,6 +243,12 @@ def test_stream_read_argument_checks(lib):
     d = lib.kvc_last_error().contents
     assert (d.expected, d.actual) == (32768, 32768)
     assert lib.kvc_stream_read(buf, 65536, sink, None) == capi.KVC_ERR_DEVICE  # host-check library: no kernels
+    flops = C.c_double()
+    assert lib.kvc_mfma_rate(100, None, None, C.byref(flops)) == capi.KVC_ERR_NULL_ARGUMENT
+    assert lib.kvc_mfma_rate(100, sink, None, None) == capi.KVC_ERR_NULL_ARGUMENT
+    assert lib.kvc_mfma_rate(0, sink, None, C.byref(flops)) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_mfma_rate((1 << 24) + 1, sink, None, C.byref(flops)) == capi.KVC_ERR_BAD_ARGUMENT
+    assert lib.kvc_mfma_rate(100, sink, None, C.byref(flops)) == capi.KVC_ERR_DEVICE
 
 
 def _i32(v):
