@@ -337,6 +337,23 @@ kvc_status kvc_append_and_attend_static(const kvc_layer* layer, kvc_cache* cache
                                         int32_t rank, const int64_t* shape, void* out, int32_t flags,
                                         kvc_work* work);
 
+/* Readout of the newest query's attention weights, for small caches and tests
+ * (Chapter 37, figure "Advance the layer cache one position at a time": the
+ * trace prints, after each step, the softmax weights of the newest query of
+ * each head over every retained row).  For sequence `seq`, right after a
+ * successful kvc_append_and_attend on the cache (any call since that moves
+ * the cache -- chunk, truncate, reset, fork, the static variant -- makes it
+ * BAD_ARGUMENT): the weights softmax(q . k_j / sqrt(d_h)) of that call's
+ * rotated query of each head over the committed rows j, the newest included
+ * (a window cache: its last `window` rows), recomputed on the device from the
+ * stored keys.  weights_out: DEVICE [H, rows] in the accumulate type (double
+ * for F64 caches, float otherwise), or NULL to query `rows` only;
+ * rows_capacity: rows per head the buffer holds; rows_out (HOST): rows.
+ * Synchronises the stream.  Errors: NULL_ARGUMENT, BAD_ARGUMENT, DEFERRED,
+ * DEVICE. */
+kvc_status kvc_newest_weights(kvc_cache* cache, int32_t seq, void* weights_out, int64_t rows_capacity,
+                              int32_t* rows_out);
+
 /* Suffix-chunk continuation (prefix-reuse note, "What must be trimmed
  * together"): x DEVICE [B, n_max, D]; n_rows HOST int32[B] with 0 <= n_b <=
  * n_max (NULL: every n_b = n_max).  Row i < n_b of sequence b is projected,

@@ -115,6 +115,7 @@ PROTOTYPES = {
     "kvc_append_and_attend": (I32, [P, P, P, I32, PI64, P, I32, C.POINTER(Work)]),
     "kvc_append_and_attend_static": (I32, [P, P, P, I32, PI64, P, I32, C.POINTER(Work)]),
     "kvc_continue_chunk": (I32, [P, P, P, I32, PI32, P, I32, C.POINTER(Work)]),
+    "kvc_newest_weights": (I32, [P, I32, P, I64, PI32]),
     "kvc_truncate": (I32, [P, PI32, I32]),
     "kvc_reset": (I32, [P]),
     "kvc_snapshot": (I32, [P, I32, P, P, PI32, I64, PI32]),

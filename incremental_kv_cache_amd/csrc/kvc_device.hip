@@ -663,6 +663,45 @@ int project_t(const DevState& s, const XT* x, int n_max, int per_seq_rows, int p
   return last_launch();
 }
 
+// Readout of the newest query's softmax weights (Chapter 37 prints them for its
+// worked trace): block = one head h of sequence b; q is the last decode call's
+// rotated query, the rows r0 .. r0 + rows - 1 are the committed keys (the newest
+// one included).  Scores q . k / sqrt(d_h), then a max-subtracted softmax, all
+// in the accumulate type; one wave, each lane a strided subset of the rows.
+template <typename T>
+__global__ __launch_bounds__(64) void newest_weights_kernel(DevState s, int b, int r0, int rows,
+                                                            typename Acc<T>::type* __restrict__ w) {
+  using A = typename Acc<T>::type;
+  const int h = blockIdx.x;
+  const int hk = h / (s.heads / s.kv_heads);
+  const int dh = s.head_width;
+  const A* q = static_cast<const A*>(s.q) + (size_t(b) * s.heads + h) * dh;
+  const T* keys = static_cast<const T*>(s.keys);
+  const A scale = A(s.scale);
+  A* wh = w + size_t(h) * rows;
+  A mx = -INFINITY;
+  for (int k = threadIdx.x; k < rows; k += 64) {
+    const T* kr = keys + kv_offset(s, b, hk, r0 + k);
+    A d = 0;
+    for (int e = 0; e < dh; ++e) d += q[e] * to_acc<A>(kr[e]);
+    d *= scale;
+    wh[k] = d;
+    mx = d > mx ? d : mx;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const A other = __shfl_xor(mx, o, 64);
+    mx = other > mx ? other : mx;
+  }
+  A sum = 0;
+  for (int k = threadIdx.x; k < rows; k += 64) {
+    const A e = exp(wh[k] - mx);
+    wh[k] = e;
+    sum += e;
+  }
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  for (int k = threadIdx.x; k < rows; k += 64) wh[k] /= sum;
+}
+
 template <typename T>
 int commit_t(const DevState& s, int n_max, int per_seq_rows) {
   if (n_max == 1 && !per_seq_rows) {
@@ -856,6 +895,24 @@ int dev_attend_decode(const DevState& s, const SeqOrder& order, void* out) {
   const int rc = fast_attend_decode(s, order, out);
   if (rc >= 0) return rc;
   return dispatch<AttendDecode>(s.dtype, s.head_width, s);
+}
+
+int dev_newest_weights(const DevState& s, int b, int r0, int rows, void* w) {
+  switch (s.dtype) {
+    case KVC_F64:
+      hipLaunchKernelGGL(newest_weights_kernel<double>, dim3(s.heads), dim3(64), 0, st(s.stream), s, b, r0, rows,
+                         static_cast<double*>(w));
+      break;
+    case KVC_F32:
+      hipLaunchKernelGGL(newest_weights_kernel<float>, dim3(s.heads), dim3(64), 0, st(s.stream), s, b, r0, rows,
+                         static_cast<float*>(w));
+      break;
+    default:
+      hipLaunchKernelGGL(newest_weights_kernel<bf16_t>, dim3(s.heads), dim3(64), 0, st(s.stream), s, b, r0, rows,
+                         static_cast<float*>(w));
+      break;
+  }
+  return last_launch();
 }
 
 int dev_merge_decode(const DevState& s, void* out) {

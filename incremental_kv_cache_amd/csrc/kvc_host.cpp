@@ -78,6 +78,10 @@ struct kvc_cache {
   ChunkOrder order{};     // work order of the last chunk call
   SeqOrder seq_order{};   // sequence order of the last decode call
   bool session = false;   // a layer cache of a kvc_session: its failure words belong to the session
+  // the query scratch holds the rotated queries of the newest committed rows
+  // (set by a successful kvc_append_and_attend, cleared by every other call
+  // that moves the cache)
+  bool newest_q_valid = false;
   // block paging (paged caches only): host copy of the block table and the pool's bookkeeping
   bool paged = false;
   int32_t block_rows = 0, block_lg = 0, table_width = 0, pool_blocks = 0;
@@ -1282,7 +1286,9 @@ kvc_status kvc_append_and_attend(const kvc_layer* layer, kvc_cache* cache, const
   kvc_status st = decode_checks("kvc_append_and_attend", layer, cache, x, rank, shape, out, flags, &w);
   if (st != KVC_OK) return st;
   choose_decode_tiles(cache);
+  cache->newest_q_valid = false;
   st = run_call(cache, x, 1, nullptr, out, flags, true);
+  if (st == KVC_OK) cache->newest_q_valid = true;
   if (st == KVC_OK && work) *work = w;
   return st;
 }
@@ -1293,6 +1299,7 @@ kvc_status kvc_append_and_attend_static(const kvc_layer* layer, kvc_cache* cache
   kvc_work w{};
   kvc_status st = decode_checks("kvc_append_and_attend_static", layer, cache, x, rank, shape, out, flags, &w);
   if (st != KVC_OK) return st;
+  cache->newest_q_valid = false;  // this call's queries live in the static scratch
   void* base = nullptr;
   size_t cap = 0;
   const int rc = dev_static_scratch(cache->device, &base, &cap);
@@ -1322,6 +1329,32 @@ kvc_status kvc_append_and_attend_static(const kvc_layer* layer, kvc_cache* cache
   s.merged = own[5];
   if (st == KVC_OK && work) *work = w;
   return st;
+}
+
+kvc_status kvc_newest_weights(kvc_cache* cache, int32_t seq, void* weights_out, int64_t rows_capacity,
+                              int32_t* rows_out) {
+  reset_detail();
+  if (!cache || !rows_out) return fail(KVC_ERR_NULL_ARGUMENT, "null argument to kvc_newest_weights");
+  if (seq < 0 || seq >= cache->batch)
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, cache->batch, seq, "sequence %d out of range", seq);
+  kvc_status st = check_deferred(cache);
+  if (st != KVC_OK) return st;
+  if (!cache->newest_q_valid)
+    return fail(KVC_ERR_BAD_ARGUMENT,
+                "the cache has moved since its last kvc_append_and_attend: no newest query to read out");
+  const int len = cache->len[seq];
+  const int r0 = cache->window ? std::max(0, len - cache->window) : 0;
+  const int rows = len - r0;
+  *rows_out = rows;
+  if (!weights_out) return KVC_OK;
+  if (rows_capacity < rows)
+    return fail_ea(KVC_ERR_BAD_ARGUMENT, rows, rows_capacity, "the weight buffer holds %lld of %d rows per head",
+                   (long long)rows_capacity, rows);
+  if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "library built without device kernels");
+  int rc = dev_newest_weights(cache->ds, seq, r0, rows, weights_out);
+  if (rc == 0) rc = dev_sync(cache->ds.stream);
+  if (rc) return device_fail(rc, "weight readout");
+  return KVC_OK;
 }
 
 kvc_status kvc_continue_chunk(const kvc_layer* layer, kvc_cache* cache, const void* x, int32_t n_max,
@@ -1388,6 +1421,7 @@ kvc_status kvc_continue_chunk(const kvc_layer* layer, kvc_cache* cache, const vo
     return KVC_OK;
   }
   if (!dev_has_kernels()) return fail(KVC_ERR_DEVICE, "library built without device kernels");
+  cache->newest_q_valid = false;
   st = run_call(cache, x, n_max, n_rows, out, flags, false);
   if (st == KVC_OK && work) *work = w;
   return st;
@@ -1413,6 +1447,7 @@ kvc_status kvc_truncate(kvc_cache* cache, const int32_t* cut, int32_t flags) {
     }
   }
   const bool stale = flags & KVC_TRUNCATE_KEEP_STALE_POSITION;
+  cache->newest_q_valid = false;
   int rc = dev_set_lengths(cache->ds, cut, stale ? 1 : 0);
   if (rc) return device_fail(rc, "length update");
   for (int b = 0; b < cache->batch; ++b) {
@@ -1434,6 +1469,7 @@ kvc_status kvc_reset(kvc_cache* cache) {
   reset_detail();
   if (!cache) return fail(KVC_ERR_NULL_ARGUMENT, "null cache");
   if (cache->session) return reject_session_cache("kvc_reset");
+  cache->newest_q_valid = false;
   int rc = dev_set_lengths(cache->ds, nullptr, 2);
   if (rc) return device_fail(rc, "length reset");
   std::fill(cache->len.begin(), cache->len.end(), 0);
@@ -1469,6 +1505,7 @@ kvc_status kvc_fork(kvc_cache* cache, int32_t src, int32_t dst, int32_t rows) {
   }
   DevState& s = cache->ds;
   int rc = 0;
+  cache->newest_q_valid = false;
   if (cache->paged) {
     // dst names src's blocks (shared, copied on a later append into them)
     const int nb = blocks_for(cache, rows);

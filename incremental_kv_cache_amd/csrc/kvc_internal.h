@@ -157,6 +157,9 @@ struct SeqOrder {
 void build_seq_order(SeqOrder* o, int batch, const int32_t* len, int per_round);
 int dev_attend_decode(const DevState& s, const SeqOrder& order, void* out);
 int dev_merge_decode(const DevState& s, void* out);
+// Softmax weights [H, rows] (accumulate type, device) of the last decode call's
+// query of sequence b over its committed rows r0 .. r0 + rows - 1.
+int dev_newest_weights(const DevState& s, int b, int r0, int rows, void* w);
 // Work items of the bf16 chunk attention kernel: one per (sequence, tile of
 // kChunkQueryTile chunk rows), listed with the most keys to read first, so
 // that the longest items start early and the ragged tail is short.  With more

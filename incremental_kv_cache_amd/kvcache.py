@@ -321,6 +321,19 @@ def kvc_continue_chunk(layer: Layer, cache: Cache, x, n_rows=None, out=None, fla
     return out, w.as_dict()
 
 
+def kvc_newest_weights(cache: Cache, seq: int):
+    """Softmax weights [H, rows] (device tensor, accumulate type) of the last
+    decode call's query of each head of sequence ``seq`` over its committed rows."""
+    torch = _torch()
+    lib = cache._lib
+    rows = C.c_int32()
+    _check(lib, lib.kvc_newest_weights(cache.ptr, seq, None, 0, C.byref(rows)))
+    w = torch.zeros((cache.desc["heads"], rows.value), dtype=_out_dtype(cache.desc["kv_dtype"]),
+                    device=f"cuda:{cache.desc['device']}")
+    _check(lib, lib.kvc_newest_weights(cache.ptr, seq, _dev_ptr(w), rows.value, C.byref(rows)))
+    return w
+
+
 def kvc_truncate(cache: Cache, cut, flags: int = 0) -> None:
     arr = np.ascontiguousarray(np.broadcast_to(np.asarray(cut, dtype=np.int32), (cache.desc["batch"],)))
     _check(cache._lib, cache._lib.kvc_truncate(cache.ptr, arr.ctypes.data_as(capi.PI32), flags))

@@ -158,6 +158,7 @@ int dev_project(const DevState& s, const void*, int n_max, int per_seq) {
 }
 int dev_attend_decode(const DevState&, const SeqOrder&, void*) { return g_fake ? 0 : 1; }
 int dev_merge_decode(const DevState&, void*) { return g_fake ? 0 : 1; }
+int dev_newest_weights(const DevState&, int, int, int, void*) { return 1; }
 int dev_attend_chunk(const DevState&, int, int, const ChunkOrder&, void*) { return g_fake ? 0 : 1; }
 int dev_output_project(const DevState&, int, int, void*) { return g_fake ? 0 : 1; }
 int dev_commit(const DevState& s, int n_max, int per_seq) {

@@ -84,6 +84,55 @@ def test_chapter_trace_through_the_library():
     assert sum(w["reused_key_value_rows"] for w in works) == g["work"]["reused_rows_per_kv_projection"]
 
 
+def test_chapter_trace_weights_read_out_of_the_library():
+    """The trace's newest-query weights of each head (12 d.p.) after every step, read
+    from the library (kvc_newest_weights recomputes them on the device from the
+    step's rotated query and the stored keys); any later call that moves the cache
+    ends the readout."""
+    import json
+    import os
+    import torch
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "p2_trace.json")))
+    x = _trace_fixture()
+    layer = _identity_layer()
+    cache = K.kvc_cache_create(layer, 1, 4)
+    for p, step in enumerate(g["steps"]):
+        xt = torch.tensor(x[p][None, None, :], dtype=torch.float64, device="cuda:0")
+        K.kvc_append_and_attend(layer, cache, xt)
+        w = to_f64(K.kvc_newest_weights(cache, 0))
+        assert w.shape == (2, p + 1)
+        for h, head in enumerate(step["heads"]):
+            np.testing.assert_allclose(w[h], head["weights"], rtol=0, atol=5.1e-13)
+    K.kvc_truncate(cache, [2])
+    with pytest.raises(K.KvcError) as e:
+        K.kvc_newest_weights(cache, 0)
+    assert e.value.name == "KVC_ERR_BAD_ARGUMENT"
+
+
+def test_newest_weights_match_the_oracle_in_every_type():
+    """Ragged lengths, several heads: the readout equals the oracle's weights of the
+    newest row (float64 1e-12; float32 and bf16 storage within their bars)."""
+    import torch
+    for dtype in ("f64", "f32", "bf16"):
+        B, H, dh, lens = 3, 4, 64, [0, 37, 300]
+        D = H * dh
+        layer, w = make_layer(17, D, H, dtype, max_positions=512)
+        cache = K.kvc_cache_create(layer, B, 512, max_chunk_rows=max(lens))
+        xp_dev, xp = hidden(17, synth.STREAM_PREFIX_X, B, max(lens), D, dtype)
+        K.kvc_continue_chunk(layer, cache, xp_dev, n_rows=lens)
+        xn_dev, xn = hidden(17, synth.STREAM_X, B, 1, D, dtype)
+        K.kvc_append_and_attend(layer, cache, xn_dev)
+        for b in range(B):
+            got = to_f64(K.kvc_newest_weights(cache, b))
+            rows = np.concatenate([xp[b, : lens[b]], xn[b]])
+            ref = A.causal_layer(rows, *w, heads=H, rows=[lens[b]])["weights"][0]
+            assert got.shape == ref.shape == (H, lens[b] + 1)
+            tol = {"f64": 1e-12, "f32": 1e-5, "bf16": 2e-2}[dtype]
+            assert float(np.max(np.abs(got - ref))) <= tol, (dtype, b)
+            np.testing.assert_allclose(got.sum(axis=1), 1.0, rtol=0, atol=1e-6)
+        torch.cuda.synchronize()
+
+
 def test_reset_reuses_allocation_and_replays_identically():
     """Chapter 37 reset evidence: 3 -> 0, allocation reused, storage unchanged, replay identical."""
     x = _trace_fixture()
