@@ -68,7 +68,7 @@ SEED = 37
 MEASURED_TRAFFIC = {
     # attend_decode_bf16_kernel, headline decode (B=32, t=4096)
     "headline": {"source": "decode", "fetch_kib": 1048893.0, "fetch_scale": 2.0, "write_kib": 512.0, "write_scale": 1.0,
-                 "kernel_source_sha256": "33632cb638dacae9e5a0927280e6032fd103a8e5312bb67e58d63950f7eb2599"},
+                 "kernel_source_sha256": "ff3b3a9411d402a8edf4b3a8f93d5def7cd1c117ebc40b471aaa0ac8c98fb43f"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
     "chunk": {"source": "mfma", "fetch_kib": 299376.9, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
               "kernel_source_sha256": "3ca02bc0e5cf0c307e214779354a43c7506b0215cc37e25d576dbd2cdd7b7741"},
