@@ -176,11 +176,15 @@ def test_session_with_grouped_layers_matches_the_stack(dtype):
     toks = synth.uniform_int(86, synth.STREAM_TOKENS, B * 20, 0, vocab - 1).reshape(B, 20).astype(np.int32)
     out, _ = K.kvc_session_chunk(sess, torch.tensor(toks[:, :16], device="cuda:0"))
     tol = TOL[dtype] * (2 if dtype == "bf16" else 1)
+    worst = 0.0
     for b in range(B):
         ref, _ = S.forward(ef, olayers, toks[b, :16])
-        assert float(np.max(np.abs(to_f64(out)[b] - ref))) <= tol
+        worst = max(worst, float(np.max(np.abs(to_f64(out)[b] - ref))))
+        assert worst <= tol
     for s in range(16, 20):
         out, _ = K.kvc_session_decode(sess, torch.tensor(toks[:, s], device="cuda:0"))
         for b in range(B):
             ref, _ = S.forward(ef, olayers, toks[b, : s + 1])
-            assert float(np.max(np.abs(to_f64(out)[b, 0] - ref[-1]))) <= tol
+            worst = max(worst, float(np.max(np.abs(to_f64(out)[b, 0] - ref[-1]))))
+            assert worst <= tol
+    print(f"{dtype} grouped two-layer stack: worst output error {worst:.3e} (bar {tol:.0e})", flush=True)

@@ -103,6 +103,7 @@ def _parity(gpu, ref, dtype, layers, what):
     if dtype == "f32":
         e /= max(float(np.max(np.abs(ref))), 1e-300)
     assert e <= _stack_tol(dtype, layers), f"{what}: error {e:.3e} above {_stack_tol(dtype, layers):.0e} ({dtype})"
+    return e
 
 
 def _stack_session(dtype, B, cap, seed=61, D=128, vocab=50, specs=((2, True, False), (4, False, True), (2, True, False))):
@@ -135,10 +136,11 @@ def test_session_prefill_and_decode_match_the_stack(dtype):
     out, work = K.kvc_session_chunk(sess, _tokens(pre), n_rows=lens)
     assert work["incremental_rows_per_projection"] == 3 * sum(lens)
     o = to_f64(out)
+    worst_out = 0.0
     for b in range(B):
         if lens[b]:
             ref, _ = S.forward(ef, olayers, toks[b, : lens[b]])
-            _parity(o[b, : lens[b]], ref, dtype, 3, f"prefill seq {b}")
+            worst_out = max(worst_out, _parity(o[b, : lens[b]], ref, dtype, 3, f"prefill seq {b}"))
     for step in range(3):
         cur = [toks[b, lens[b] + step] for b in range(B)]
         out, work = K.kvc_session_decode(sess, _tokens(cur))
@@ -146,14 +148,19 @@ def test_session_prefill_and_decode_match_the_stack(dtype):
         o = to_f64(out)[:, 0]
         for b in range(B):
             ref, _ = S.forward(ef, olayers, toks[b, : lens[b] + step + 1])
-            _parity(o[b], ref[-1], dtype, 3, f"step {step} seq {b}")
+            worst_out = max(worst_out, _parity(o[b], ref[-1], dtype, 3, f"step {step} seq {b}"))
+    worst_kv = [0.0] * len(sess.caches)
     for b in range(B):
         _, kv = S.forward(ef, olayers, toks[b, : lens[b] + 3])
         for l, (c, (kf, vf)) in enumerate(zip(sess.caches, kv)):
             k, v, pos = K.kvc_snapshot(c, b)
             assert list(pos) == list(range(lens[b] + 3))
-            _parity(storage_f64(k, dtype), kf, dtype, l + 1, f"layer {l} keys {b}")
-            _parity(storage_f64(v, dtype), vf, dtype, l + 1, f"layer {l} values {b}")
+            worst_kv[l] = max(worst_kv[l], _parity(storage_f64(k, dtype), kf, dtype, l + 1, f"layer {l} keys {b}"),
+                              _parity(storage_f64(v, dtype), vf, dtype, l + 1, f"layer {l} values {b}"))
+    # the measured errors beside the bars (reported with pytest -s)
+    print(f"{dtype} stack: worst key/value error per layer "
+          f"{', '.join(f'{e:.3e} (bar {_stack_tol(dtype, l + 1):.0e})' for l, e in enumerate(worst_kv))}; "
+          f"worst output error {worst_out:.3e} (bar {_stack_tol(dtype, 3):.0e})", flush=True)
 
 
 def _all_state(sess):
