@@ -90,3 +90,35 @@ def test_static_entry_point_refuses_a_call_beyond_its_scratch():
     assert work["incremental_rows_per_projection"] == B
     assert K.kvc_lengths(cache)[0].tolist() == [1] * B
     assert bool(torch.isfinite(out).all())
+
+
+def test_static_entry_point_on_paged_windowed_and_grouped_caches():
+    """The same kernels with the block-table, ring and grouped-head addressing: twin
+    caches stay bit-identical over three decode steps each."""
+    import torch
+    from tests.test_gpu_grouped import grouped_layer
+    from tests.test_gpu_window import window_layer
+    print("case: bf16 paged (256-row blocks), windowed (window 300, ring 512), grouped (8 of 32 heads)", flush=True)
+    D, B = 1024, 3
+    lens = [0, 257, 700]
+    # paged: a pool shared by the sequences, blocks taken as rows cross 256-row boundaries
+    layer, _ = make_layer(51, D, 8, "bf16", max_positions=2048)
+    paged = [K.kvc_cache_create_paged(layer, B, 2048, 256, 12, max_chunk_rows=max(lens)) for _ in range(2)]
+    # windowed ring of 512 rows for a window of 300, written past its wrap by a second prefill
+    wlayer, _ = window_layer(52, D, 8, 8, 300, "bf16")
+    ring = [K.kvc_cache_create(wlayer, B, 512, max_chunk_rows=512) for _ in range(2)]
+    # grouped: 32 query heads over 8 key/value heads
+    glayer, _ = grouped_layer(53, D, 32, 8, "bf16", 2048)
+    grouped = [K.kvc_cache_create(glayer, B, 2048, max_chunk_rows=max(lens)) for _ in range(2)]
+    xp, _ = hidden(54, synth.STREAM_PREFIX_X, B, max(lens), D, "bf16")
+    xn, _ = hidden(54, synth.STREAM_X, B, 3, D, "bf16")
+    for lay, pair, what in ((layer, paged, "paged"), (wlayer, ring, "windowed"), (glayer, grouped, "grouped")):
+        for c in pair:
+            if what == "windowed":  # 700 rows through a 512-row ring in two chunks
+                K.kvc_continue_chunk(lay, c, xp[:, :400].contiguous(), n_rows=[min(n, 400) for n in lens])
+                K.kvc_continue_chunk(lay, c, xp[:, 400:].contiguous(), n_rows=[max(n - 400, 0) for n in lens])
+            else:
+                K.kvc_continue_chunk(lay, c, xp, n_rows=lens)
+        for i in range(3):
+            _same_step(lay, pair, xn[:, i:i + 1].contiguous(), f"{what} step {i + 1}")
+    torch.cuda.synchronize()
