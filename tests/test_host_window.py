@@ -239,3 +239,30 @@ def test_session_reset_and_truncate_keep_the_held_rows_in_step(fake):
         _, pos = _snap(lib, c, 0)
         assert list(pos) == list(range(150))
         lib.kvc_session_destroy(s)
+
+
+def test_reset_after_a_failed_async_call_is_suppressed_then_repeated(fake):
+    """KVC_ASYNC: a reset enqueued behind a call that failed on the device is
+    suppressed like the commits (it returns OK without waiting); the next
+    synchronous call reports DEFERRED and restores the host's lengths and held
+    rows from the device, and the repeated reset then takes effect."""
+    lib = fake
+    lib.kvc_test_fail_next.argtypes = [C.c_longlong]
+    W, cap = 100, 256
+    lay = _layer(lib, _params(lib), W)
+    c = _cache(lib, lay, 1, cap, 200)
+    for _ in range(2):
+        assert _chunk(lib, lay, c, [200]) == 0  # 400 rows: the ring has wrapped
+    before = _lengths(lib, c, 1), _snap(lib, c, 0)[1].tolist()
+    lib.kvc_test_fail_next(0)
+    rows = np.array([10], np.int32)
+    assert lib.kvc_continue_chunk(lay, c, DUMMY, 10, rows.ctypes.data_as(capi.PI32), DUMMY, capi.KVC_ASYNC,
+                                  None) == 0
+    assert lib.kvc_reset(c) == 0  # suppressed on the device
+    assert lib.kvc_sync(c) == capi.KVC_ERR_DEFERRED
+    assert (_lengths(lib, c, 1), _snap(lib, c, 0)[1].tolist()) == before
+    assert _reuse(lib, c, 150) == 0  # the held rows are the device's again
+    assert lib.kvc_reset(c) == 0
+    assert _lengths(lib, c, 1) == ([0], [0])
+    assert _chunk(lib, lay, c, [5]) == 0
+    assert _snap(lib, c, 0)[1].tolist() == list(range(5))
