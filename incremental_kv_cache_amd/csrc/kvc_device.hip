@@ -103,9 +103,16 @@ __global__ __launch_bounds__(256) void project_kernel(DevState s, const XT* __re
   const size_t flat0 = (size_t(b * heads_p + h) * n_max + i) * dh + f;
   const size_t flat1 = flat0 + half;
   if (p == 0) {
-    A* q = static_cast<A*>(s.q);
-    q[flat0] = r0;
-    q[flat1] = r1;
+    if (sizeof(T) == 2 && s.q_bf16) {  // bf16 layers: the flash kernel's operand (see DevState::q_bf16)
+      const A sl2 = A(s.scale) * A(1.4426950408889634);
+      bf16_t* q = static_cast<bf16_t*>(s.q);
+      q[flat0] = f32_to_bf16(float(r0 * sl2));
+      q[flat1] = f32_to_bf16(float(r1 * sl2));
+    } else {
+      A* q = static_cast<A*>(s.q);
+      q[flat0] = r0;
+      q[flat1] = r1;
+    }
     if (!finite(r0)) flag_min(&s.err->query, flat0);
     if (!finite(r1)) flag_min(&s.err->query, flat1);
   } else {

@@ -509,6 +509,9 @@ kvc_status compute_stages(kvc_cache* c, const void* x, int n_max, const int32_t*
     rc = dev_set_rows(s, n_rows);
     if (rc) return device_fail(rc, "chunk row upload");
   }
+  // a chunk call's queries go to the flash kernel (bf16, d_h 64 or 128) as
+  // its scaled bf16 operand; decode calls keep float32 queries
+  s.q_bf16 = !decode && s.dtype == KVC_BF16 && (s.head_width == 64 || s.head_width == 128);
   profile_mark(c, KVC_STAGE_PROJECT, 0);
   rc = dev_project(s, x, n_max, per_seq);
   profile_mark(c, KVC_STAGE_PROJECT, 1);

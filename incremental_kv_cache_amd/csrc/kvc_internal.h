@@ -66,7 +66,11 @@ struct DevState {
   int32_t* held;       // ring caches: [B] oldest row still held (older slots were written over)
   void* cand_k;        // [B, H_kv, n, d_h] storage type (n = rows of the call)
   void* cand_v;        // [B, H_kv, n, d_h]
-  void* q;             // [B, H, n, d_h] accumulate type
+  void* q;             // [B, H, n, d_h] accumulate type; with q_bf16, bf16 of q * scale * log2(e)
+  // q_bf16 = 1 (chunk calls of bf16 layers whose attention is the matrix-core
+  // flash kernel): the projection stores each rotated query already scaled to
+  // base-2 softmax units and rounded to bf16, the flash kernel's operand type
+  int q_bf16;
   void* merged;        // [B, n, D] accumulate type: merged heads before W_o (null without W_o)
   void* out_proj_dst;  // [B, n, D] accumulate type: destination of the W_o projection (per call)
   void* partials;      // [B, H, max_tiles, d_h + 2] accumulate type

@@ -129,9 +129,16 @@ __device__ __forceinline__ void put_pair(const DevState& s, int p, const RowDst&
   const size_t flat0 = (size_t(d.b * heads_of(s, p) + h) * n_max + d.i) * dh + f;
   const size_t flat1 = flat0 + half;
   if (p == 0) {
-    float* q = static_cast<float*>(s.q);
-    q[flat0] = r0;
-    q[flat1] = r1;
+    if (s.q_bf16) {
+      const float sl2 = float(s.scale) * 1.4426950408889634f;
+      bf16_t* q = static_cast<bf16_t*>(s.q);
+      q[flat0] = f32_to_bf16(r0 * sl2);
+      q[flat1] = f32_to_bf16(r1 * sl2);
+    } else {
+      float* q = static_cast<float*>(s.q);
+      q[flat0] = r0;
+      q[flat1] = r1;
+    }
     if (!isfinite(r0)) bad = min(bad, (unsigned long long)flat0);
     if (!isfinite(r1)) bad = min(bad, (unsigned long long)flat1);
   } else {
@@ -208,9 +215,28 @@ __device__ __forceinline__ void put_pairs4(const DevState& s, int p, const RowDs
   }
   const size_t flat0 = (size_t(d.b * heads_of(s, p) + h) * n_max + d.i) * dh + f;
   if (p == 0) {
-    float* q = static_cast<float*>(s.q) + flat0;
-    *reinterpret_cast<float4*>(q) = r0;
-    *reinterpret_cast<float4*>(q + half) = r1;
+    if (s.q_bf16) {
+      const float sl2 = float(s.scale) * 1.4426950408889634f;
+      bf16_t* q = static_cast<bf16_t*>(s.q) + flat0;
+      union {
+        uint2 u;
+        bf16_t e[4];
+      } a, c;
+      a.e[0] = f32_to_bf16(r0.x * sl2);
+      a.e[1] = f32_to_bf16(r0.y * sl2);
+      a.e[2] = f32_to_bf16(r0.z * sl2);
+      a.e[3] = f32_to_bf16(r0.w * sl2);
+      c.e[0] = f32_to_bf16(r1.x * sl2);
+      c.e[1] = f32_to_bf16(r1.y * sl2);
+      c.e[2] = f32_to_bf16(r1.z * sl2);
+      c.e[3] = f32_to_bf16(r1.w * sl2);
+      *reinterpret_cast<uint2*>(q) = a.u;
+      *reinterpret_cast<uint2*>(q + half) = c.u;
+    } else {
+      float* q = static_cast<float*>(s.q) + flat0;
+      *reinterpret_cast<float4*>(q) = r0;
+      *reinterpret_cast<float4*>(q + half) = r1;
+    }
     note(r0, flat0);
     note(r1, flat0 + half);
   } else {
@@ -824,21 +850,29 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
 
   // B operand of S^T: lane holds q[qi][16 u + 8 g + e] * scale * log2(e), rounded
   // to bf16, so scores come out of the MFMA already in base-2 softmax units.
+  // (the projection of a chunk call stores q already scaled and rounded so,
+  // s.q_bf16; otherwise q is float32 and is scaled and rounded here)
   const float sl2 = float(s.scale) * 1.4426950408889634f;
-  const float* qp = static_cast<const float*>(s.q) + (lane_id * n_max + qi_eff) * DH;
   Frag8 qf[DSTEPS];
+  if (s.q_bf16) {
+    const bf16_t* qp = static_cast<const bf16_t*>(s.q) + (lane_id * n_max + qi_eff) * DH;
 #pragma unroll
-  for (int u = 0; u < DSTEPS; ++u) {
-    const float4 q0 = reinterpret_cast<const float4*>(qp + 16 * u + 8 * g)[0];
-    const float4 q1 = reinterpret_cast<const float4*>(qp + 16 * u + 8 * g)[1];
-    qf[u].v[0] = (__bf16)(q0.x * sl2);
-    qf[u].v[1] = (__bf16)(q0.y * sl2);
-    qf[u].v[2] = (__bf16)(q0.z * sl2);
-    qf[u].v[3] = (__bf16)(q0.w * sl2);
-    qf[u].v[4] = (__bf16)(q1.x * sl2);
-    qf[u].v[5] = (__bf16)(q1.y * sl2);
-    qf[u].v[6] = (__bf16)(q1.z * sl2);
-    qf[u].v[7] = (__bf16)(q1.w * sl2);
+    for (int u = 0; u < DSTEPS; ++u) qf[u].u = *reinterpret_cast<const uint4*>(qp + 16 * u + 8 * g);
+  } else {
+    const float* qp = static_cast<const float*>(s.q) + (lane_id * n_max + qi_eff) * DH;
+#pragma unroll
+    for (int u = 0; u < DSTEPS; ++u) {
+      const float4 q0 = reinterpret_cast<const float4*>(qp + 16 * u + 8 * g)[0];
+      const float4 q1 = reinterpret_cast<const float4*>(qp + 16 * u + 8 * g)[1];
+      qf[u].v[0] = (__bf16)(q0.x * sl2);
+      qf[u].v[1] = (__bf16)(q0.y * sl2);
+      qf[u].v[2] = (__bf16)(q0.z * sl2);
+      qf[u].v[3] = (__bf16)(q0.w * sl2);
+      qf[u].v[4] = (__bf16)(q1.x * sl2);
+      qf[u].v[5] = (__bf16)(q1.y * sl2);
+      qf[u].v[6] = (__bf16)(q1.z * sl2);
+      qf[u].v[7] = (__bf16)(q1.w * sl2);
+    }
   }
   f32x16_t o[DTILES];
 #pragma unroll
