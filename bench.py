@@ -12,10 +12,10 @@ timed step sees the same t (the wall-clock time of the whole loop, truncation
 included, is reported beside it).  Inputs (weights, hidden rows, the
 prefilled cache) are seeded synthetic data resident in HBM before timing.
 
-The default run (headline workload) also measures the long-context decode
-and the suffix-chunk workloads and reports them under "other_configs" of the
-same line, with the achievable streaming-read bandwidth and matrix-core rate
-of the box as yardsticks.
+The default run (headline workload) also measures the ragged-length decode,
+the long-context decode and the suffix-chunk workloads and reports them under
+"other_configs" of the same line, with the achievable streaming-read
+bandwidth and matrix-core rate of the box as yardsticks.
 
 Workloads (default: headline):
   headline  B=32, H=32, d_h=128, C=4096, t=4096 for every sequence, bf16 K/V
@@ -587,7 +587,7 @@ def main():
     ap.add_argument("--workload", default="headline", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
-                    help="headline only: skip the long-context and suffix-chunk measurements")
+                    help="headline only: skip the ragged, long-context and suffix-chunk measurements")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times), to scale HBM byte counters")
     a = ap.parse_args()
@@ -617,7 +617,7 @@ def main():
         # (each cache freed before the next is built); no CPU baselines for them
         import gc
         res["other_configs"] = {}
-        for other in ("long", "chunk"):
+        for other in ("ragged", "long", "chunk"):
             gc.collect()
             torch.cuda.empty_cache()
             log(f"other config: {other}")
