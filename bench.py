@@ -70,12 +70,12 @@ MEASURED_TRAFFIC = {
     "headline": {"source": "decode", "fetch_kib": 1048893.0, "fetch_scale": 2.0, "write_kib": 512.0, "write_scale": 1.0,
                  "kernel_source_sha256": "ff3b3a9411d402a8edf4b3a8f93d5def7cd1c117ebc40b471aaa0ac8c98fb43f"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
-    "chunk": {"source": "mfma", "fetch_kib": 299376.9, "fetch_scale": 2.0, "write_kib": 131072.0, "write_scale": 1.0,
-              "kernel_source_sha256": "3ca02bc0e5cf0c307e214779354a43c7506b0215cc37e25d576dbd2cdd7b7741"},
+    "chunk": {"source": "mfma", "fetch_kib": 299334.1, "fetch_scale": 2.0, "write_kib": 98304.0, "write_scale": 1.0,
+              "kernel_source_sha256": "02a133d84abb05be11925ed52e25290235a257131a8f6bb2e7b1df9c6723c964"},
     # attend_flash_kernel, suffix chunk (B=8, n=512)
-    "chunk_attention": {"source": "mfma", "fetch_kib": 354611.7, "fetch_scale": 2.0, "write_kib": 65585.1,
+    "chunk_attention": {"source": "mfma", "fetch_kib": 338238.9, "fetch_scale": 2.0, "write_kib": 65555.1,
                         "write_scale": 1.0,
-                        "kernel_source_sha256": "3ca02bc0e5cf0c307e214779354a43c7506b0215cc37e25d576dbd2cdd7b7741"},
+                        "kernel_source_sha256": "02a133d84abb05be11925ed52e25290235a257131a8f6bb2e7b1df9c6723c964"},
 }
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
                   "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}
