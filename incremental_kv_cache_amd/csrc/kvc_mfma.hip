@@ -752,10 +752,10 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
 // scale factor is per lane, and the probabilities are already in the operand
 // layout of O^T += V^T P^T.
 //
-// Keys and values pass through LDS in tiles of 128 rows, double-buffered: the
-// next tile's rows are loaded into registers (16 lanes per 256-byte row, so a
-// load instruction covers whole rows) while the current tile is multiplied,
-// then written to the other buffer, with one barrier per tile.  V stays
+// Keys and values pass through LDS in tiles of 128 rows, two buffers of each,
+// filled by direct global-to-LDS loads (16 lanes per 256-byte row, so a load
+// instruction covers whole rows) while the current tiles are multiplied
+// (schedule below).  V stays
 // row-major in LDS; the V^T operand comes from the transposing LDS read
 // (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
 // i % 4 of the 8-byte pieces addressed by lanes i / 4 + 4 m, m = 0..3, so
@@ -791,20 +791,33 @@ __device__ __forceinline__ float add_bf16x8(const Frag8& f, float acc) {
 template <int DH, bool WIN>
 __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_flash_kernel(
     DevState s, int n_max, int per_seq_rows, ChunkOrder order, float* __restrict__ out) {
-  constexpr int KT = 128;  // keys per LDS tile (two buffers of K and V: 148 KB at d_h = 128)
+  constexpr int KT = 128;  // keys per LDS tile (two buffers of K and V: 128 KB at d_h = 128)
   static_assert(kMinBlockRows % KT == 0, "a key tile must stay inside one block");
-  constexpr int LDK = DH + 8;   // K row stride: conflict-free 16-byte fragment reads
-  constexpr int LDV = DH + 32;  // V row stride: conflict-free transposing reads (64 banks)
   constexpr int DSTEPS = DH / 16;
   constexpr int DTILES = DH / 32;
-  constexpr int CPR = DH / 8;        // 16-byte pieces per row
+  constexpr int SPR = DH / 8;         // 16-byte slots per row
+  constexpr int RPS = 16 / SPR;       // rows per 256-byte sweep of the 64 banks
+  constexpr int RPL = 64 / SPR;       // rows filled by one wave's load instruction
+  constexpr int NI = KT / RPL / 8;    // load instructions per eighth of a tile
+  static_assert((NI == 2 || NI == 4) && NI * RPL * 8 == KT, "a tile is 16 or 32 load instructions");
   constexpr int QT = kChunkQueryTile;  // queries of the workgroup, 32 per wave
-  constexpr int THREADS = 2 * QT;
-  constexpr int RPI = THREADS / CPR;  // rows covered by one load of the workgroup
-  constexpr int PIECES = KT / RPI;   // pieces per thread per tile, each of K and V
   constexpr float kRescale = 8.f;    // log2 of the largest probability kept unscaled
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][KT * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Vs[2][KT * LDV];
+  // two buffers each of K and V, as four arrays: the compiler tells direct
+  // loads into one array from reads of another apart, so the reads of the
+  // current tiles do not wait for the loads into the next ones
+  __shared__ __attribute__((aligned(16))) bf16_t K0[KT * DH];
+  __shared__ __attribute__((aligned(16))) bf16_t K1[KT * DH];
+  __shared__ __attribute__((aligned(16))) bf16_t V0[KT * DH];
+  __shared__ __attribute__((aligned(16))) bf16_t V1[KT * DH];
+  __shared__ int counters[6];  // waves seen per SIMD, leading and trailing waves seen
+  using Zero = std::integral_constant<int, 0>;
+  using One = std::integral_constant<int, 1>;
+  auto kbuf = [&](auto p) __attribute__((always_inline)) -> bf16_t* {
+    if constexpr (decltype(p)::value == 0) return K0; else return K1;
+  };
+  auto vbuf = [&](auto p) __attribute__((always_inline)) -> bf16_t* {
+    if constexpr (decltype(p)::value == 0) return V0; else return V1;
+  };
 
   const int H = s.heads;
   const int item = blockIdx.x / H;
@@ -839,11 +852,12 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
   // tile holding its first query's lowest key
   const int lo = WIN ? window_start(s, limit) : 0;
   const int it_first = WIN ? window_start(s, len + qt * QT) / KT : 0;
+  const int n_it = ntiles - it_first;  // key tiles the block walks, >= 1
   const int wave_lo_max = WIN ? window_start(s, len + min(qt * QT + wave * 32 + 31, n_b - 1)) : 0;
   const size_t lane_id = size_t(b) * H + h;
   const int hk = h / (H / s.kv_heads);  // the key/value head this query head reads
   const size_t kv_lane = size_t(b) * s.kv_heads + hk;
-  const bf16_t* kc = static_cast<const bf16_t*>(s.keys);  // rows through kv_block_base / kv_offset
+  const bf16_t* kc = static_cast<const bf16_t*>(s.keys);  // rows through the block base
   const bf16_t* vc = static_cast<const bf16_t*>(s.values);
   const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + kv_lane * n_max * DH;
   const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + kv_lane * n_max * DH;
@@ -889,120 +903,176 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
   mq.u = make_uint4(0u, 0u, 0u, 0u);
   const int wave_limit_min = len + min(qt * QT + wave * 32, n_b - 1);  // smallest limit in the wave
 
-  // global -> register -> LDS staging: thread loads piece lch of rows lrow + RPI k
-  const int lrow = tid / CPR;
-  const int lch = tid - lrow * CPR;
-  static_assert(PIECES == 1 || PIECES == 2 || PIECES == 4, "tile staging assumes 1, 2 or 4 pieces per thread");
-  // staged pieces in named registers (an indexed array here is kept in scratch memory)
-  uint4 pk0, pk1, pk2, pk3, pv0, pv1, pv2, pv3;
-  // tile of contiguous rows (all cache rows, or all chunk rows): loads into registers
-  auto contiguous = [&](int j0) { return j0 + KT <= len || (j0 >= len && j0 + KT <= total); };
-  auto fetch = [&](int j0) {
-    const bool cached = j0 + KT <= len;
-    const size_t r0 = size_t(cached ? j0 : j0 - len) + lrow;
-    // a 128-row tile lies in one block of a paged cache
-    const ptrdiff_t tile_base = cached ? kv_block_base(s, b, hk, j0) : 0;
-    const uint4* kp = reinterpret_cast<const uint4*>((cached ? kc + tile_base : kn) + r0 * DH + lch * 8);
-    const uint4* vp = reinterpret_cast<const uint4*>((cached ? vc + tile_base : vn) + r0 * DH + lch * 8);
-    constexpr int STRIDE = RPI * DH / 8;  // uint4 between a thread's pieces
-    pk0 = kp[0];
-    pv0 = vp[0];
-    if constexpr (PIECES >= 2) {
-      pk1 = kp[STRIDE];
-      pv1 = vp[STRIDE];
-    }
-    if constexpr (PIECES == 4) {
-      pk2 = kp[2 * STRIDE];
-      pv2 = vp[2 * STRIDE];
-      pk3 = kp[3 * STRIDE];
-      pv3 = vp[3 * STRIDE];
+  // Tiles are unpadded rows of d_h elements whose 16-byte slots are permuted
+  // within each row (slot c of row r holds piece c ^ f(r)), so that the
+  // fragment reads below hit every bank once per sweep: for K, f(r) =
+  // (r / RPS) mod SPR (the 16 rows a 16-lane group reads start in different
+  // banks); for V, f(r) = 4 ((r / RPS) mod (SPR / 4)) (the four rows a 32-lane
+  // transposing read takes 16 bytes from fall in different bank quarters).
+  // Global -> LDS with the 16-byte direct loads: one wave instruction fills
+  // RPL whole rows (lane l: row l / SPR, slot l mod SPR), instruction q of a
+  // tile rows RPL q ..; a tile is 8 NI instructions.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto kswz = [](int r) __attribute__((always_inline)) { return (r / RPS) & (SPR - 1); };
+  auto vswz = [](int r) __attribute__((always_inline)) { return 4 * ((r / RPS) & (SPR / 4 - 1)); };
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  typedef __attribute__((address_space(1))) void glb_void_t;
+  // byte offset of this lane's slot within the rows of instruction q: V the
+  // same for every q, K koff0 ^ 64 (q mod NI) (f(RPL q + l / SPR) differs from
+  // f(l / SPR) in the slot bits worth 64 bytes, by 4 (q mod NI))
+  const int lr = lane / SPR, lc = lane & (SPR - 1);
+  const uint32_t voff = uint32_t(lr * DH + 8 * (lc ^ vswz(lr))) * 2u;
+  const uint32_t koff0 = uint32_t(lr * DH + 8 * (lc ^ kswz(lr))) * 2u;
+  // Block base (kv_block_base) of a run of rows starting at r0 of this lane's
+  // cache, with the block table read through the scalar cache (it is not
+  // written while the kernel runs), so no vector-memory wait orders it behind
+  // the tile loads in flight.
+  auto block_base = [&](int r0) __attribute__((always_inline)) -> ptrdiff_t {
+    if (!s.paged) return kv_block_base(s, b, hk, r0);
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_t;
+    const int lg = s.block_rows_log2;
+    const int blk = max(((const_i32_t)s.block_table)[size_t(b) * s.table_width + (r0 >> lg)], 0);
+    return (ptrdiff_t(size_t(blk) * s.kv_heads + hk) << lg) * DH - ptrdiff_t((r0 >> lg) << lg) * DH;
+  };
+  // Where tile t (absolute) of K or V comes from: a tile of contiguous rows
+  // (all cache rows, or all chunk rows) from one base; otherwise row by row (a
+  // tile across the cache end, or past the last key: rows after it repeat the
+  // last key, which the mask hides).  A 128-row tile lies in one block of a
+  // paged cache, so one block base serves all its cached rows.
+  struct TileSrc {
+    const char* base;       // contiguous: the tile's first row
+    const bf16_t* cached;   // row by row: row j < len at cached + j d_h
+    const bf16_t* chunk;    //             row j >= len at chunk + (j - len) d_h
+    int j0;
+    bool contiguous;
+  };
+  auto tile_src = [&](auto is_v, int t) __attribute__((always_inline)) {
+    TileSrc src;
+    const bf16_t* cache = is_v ? vc : kc;
+    src.chunk = is_v ? vn : kn;
+    src.j0 = t * KT;
+    src.cached = cache + block_base(min(src.j0, max(len - 1, 0)));
+    src.contiguous = src.j0 + KT <= len || (src.j0 >= len && src.j0 + KT <= total);
+    src.base = reinterpret_cast<const char*>(src.j0 < len ? src.cached + ptrdiff_t(src.j0) * DH
+                                                          : src.chunk + size_t(src.j0 - len) * DH);
+    return src;
+  };
+  // Direct load of instruction q of a contiguous tile whose first row is at
+  // `first`, in the buffer form: a buffer descriptor spanning the tile, the
+  // lane's byte offset off and the instruction's rows as the scalar offset.
+  // (The compiler counts the global form as an LDS access as well and then
+  // waits for every LDS read in flight behind it; the buffer form counts as a
+  // vector-memory load only.)
+  auto dma_tile = [&](const char* first, bf16_t* tile, int q, uint32_t off) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(first), (short)0, KT * DH * 2, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(tile + q * RPL * DH), 16, off, q * (RPL * DH * 2), 0, 0);
+  };
+  // issues instruction q of the tile src into `tile`.  (The lane offsets are
+  // copied opaquely here, so what they give for each q is formed per
+  // instruction rather than held in registers across the loop.)
+  auto load_one = [&](auto is_v, const TileSrc& src, bf16_t* tile, int q) __attribute__((always_inline)) {
+    uint32_t off = is_v ? voff : koff0;
+    asm volatile("" : "+v"(off));
+    if (!is_v) off ^= 64u * uint32_t(q & (NI - 1));
+    if (src.contiguous) {
+      dma_tile(src.base, tile, q, off);
+    } else {
+      int row = lr;
+      asm volatile("" : "+v"(row));
+      const int j = min(src.j0 + RPL * q + row, total - 1);
+      const int c = int(off & (DH * 2 - 1)) >> 1;  // element of the row
+      const bf16_t* g_addr = (j < len ? src.cached + ptrdiff_t(j) * DH : src.chunk + size_t(j - len) * DH) + c;
+      __builtin_amdgcn_global_load_lds((glb_void_t*)g_addr, (lds_void_t*)(tile + q * RPL * DH), 16, 0, 0);
     }
   };
-  auto stash = [&](int buf) {
-    uint4* kd = reinterpret_cast<uint4*>(&Ks[buf][lrow * LDK + lch * 8]);
-    uint4* vd = reinterpret_cast<uint4*>(&Vs[buf][lrow * LDV + lch * 8]);
-    constexpr int KS = RPI * LDK / 8, VS = RPI * LDV / 8;
-    kd[0] = pk0;
-    vd[0] = pv0;
-    if constexpr (PIECES >= 2) {
-      kd[KS] = pk1;
-      vd[VS] = pv1;
-    }
-    if constexpr (PIECES == 4) {
-      kd[2 * KS] = pk2;
-      vd[2 * VS] = pv2;
-      kd[3 * KS] = pk3;
-      vd[3 * VS] = pv3;
-    }
-  };
-  // a tile across the cache end or past the last key (rows after it repeat the
-  // last key, which the mask hides): loaded row by row straight into LDS
-  auto fetch_mixed = [&](int j0, int buf) {
+
+  // Work of the block on key tile j (local index, tile it_first + j; buffers
+  // by the parity of j):
+  //   S_j  scores of tile j (matrix cores, K tile from LDS)
+  //   X_j  mask, maximum, rescale, exponentials, bf16 probabilities (vector unit)
+  //   P_j  O^T += V^T P^T (matrix cores, V tile from LDS)
+  // A wave runs S_0, then X_j and [P_j, S_j+1] alternately, one barrier after
+  // each.  One of the two waves on each SIMD (its second by an LDS ticket)
+  // runs one segment behind the other, so on every SIMD one wave's
+  // exponentials overlap the other wave's matrix products instead of both
+  // waves switching between them together.  The pair (V_j, K_j+1) is read in
+  // segments 2j+2 (leading waves) and 2j+3 (trailing waves).  Each wave loads
+  // a quarter of every other tile, one load instruction after each step of
+  // its S_j+1 (its P_j, the last read of the buffers it loads, done): the
+  // leading waves K_j+2 in segment 2j+2, the trailing waves V_j+2 in segment
+  // 2j+3; a leading wave waits for its loads at the end of its next X, a
+  // trailing wave at the end of its next [P, S] (its V_j+2 is first read in
+  // segment 2j+6), before the barrier that precedes the first reader.  (A load
+  // instruction holds up the
+  // wave that issues it for tens of cycles: spread this way, each wave loads
+  // a quarter of a pair per tile.)  Should the tickets not come out as one
+  // leading and one trailing wave per SIMD, every wave leads and loads an
+  // eighth of K_j+2 and of V_j+1.
+  f32x16_t st[KT / 32];
+  Frag8 pb[KT / 32][2];
+  const int kx = kswz(c32);  // the K rows this lane reads are c32 plus multiples of 32
+  // S_j from the buffer `kt_tile`: the four 32-key blocks advance together one
+  // 16-feature step at a time; the fragment of block kt for step u + 1 is read
+  // right after the MFMA of step u that last used its registers, three MFMAs
+  // ahead of its use; after step u, hook(u).  (The lane's swizzle is copied
+  // opaquely per tile: the eight step offsets it gives are recomputed here
+  // rather than held across the loop.)
+  auto scores = [&](const bf16_t* kt_tile, auto&& hook) __attribute__((always_inline)) {
+    kt_tile += c32 * DH;
+    int kxo = kx;
+    asm volatile("" : "+v"(kxo));
+    Frag8 kf[KT / 32];
+    auto read_k = [&](int u, int kt) __attribute__((always_inline)) {
+      kf[kt].u = *reinterpret_cast<const uint4*>(&kt_tile[kt * 32 * DH + 8 * ((2 * u + g) ^ kxo)]);
+    };
 #pragma unroll
-    for (int k = 0; k < PIECES; ++k) {
-      const int j = min(j0 + lrow + k * RPI, total - 1);
-      const size_t off = (j < len ? kv_offset(s, b, hk, j) : size_t(j - len) * DH) + lch * 8;
-      const uint4 kk = *reinterpret_cast<const uint4*>((j < len ? kc : kn) + off);
-      const uint4 vv = *reinterpret_cast<const uint4*>((j < len ? vc : vn) + off);
-      *reinterpret_cast<uint4*>(&Ks[buf][(lrow + k * RPI) * LDK + lch * 8]) = kk;
-      *reinterpret_cast<uint4*>(&Vs[buf][(lrow + k * RPI) * LDV + lch * 8]) = vv;
-    }
-  };
-  // transposing-read address of this lane within a V tile (see above)
-  const int li = lane & 15;
-  const int vlane = (4 * g + (li >> 2)) * LDV + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
-
-  if (contiguous(it_first * KT)) {
-    fetch(it_first * KT);
-    stash(0);
-  } else {
-    fetch_mixed(it_first * KT, 0);
-  }
-  __syncthreads();
-  for (int it = it_first; it < ntiles; ++it) {
-    const int j0 = it * KT;
-    const int buf = (it - it_first) & 1;
-    const bool more = it + 1 < ntiles;
-    const bool staged = more && contiguous(j0 + KT);
-
-    f32x16_t st[KT / 32];
+    for (int kt = 0; kt < KT / 32; ++kt) read_k(0, kt);
 #pragma unroll
     for (int kt = 0; kt < KT / 32; ++kt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
       st[kt] = mfma32(onek.v, mq.v, st[kt]);
+    }
 #pragma unroll
-      for (int u = 0; u < DSTEPS; ++u) {
-        Frag8 a;
-        a.u = *reinterpret_cast<const uint4*>(&Ks[buf][(kt * 32 + c32) * LDK + 16 * u + 8 * g]);
-        st[kt] = mfma32(a.v, qf[u].v, st[kt]);
+    for (int u = 0; u < DSTEPS; ++u) {
+#pragma unroll
+      for (int kt = 0; kt < KT / 32; ++kt) {
+        st[kt] = mfma32(kf[kt].v, qf[u].v, st[kt]);
+        if (u + 1 < DSTEPS) read_k(u + 1, kt);
+        // (kept in this order: the compiler would otherwise issue each read
+        // just before its MFMA, too late to cover the LDS latency)
+        __builtin_amdgcn_sched_barrier(0);
       }
+      hook(u);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // the other buffer was last read before the previous barrier: fill it now,
-    // with the score MFMAs already issued (contiguous tiles land in registers
-    // first and are written after this tile)
-    __builtin_amdgcn_sched_barrier(0);
-    if (staged) {
-      fetch(j0 + KT);
-    } else if (more) {
-      fetch_mixed(j0 + KT, buf ^ 1);
-    }
+  };
+  auto softmax = [&](int j) __attribute__((always_inline)) {
+    const int j0 = (it_first + j) * KT;
     // causal mask only where the tile reaches past the wave's first query, the
     // window's lower edge only where the tile starts below the wave's last one
     if (j0 + KT - 1 > wave_limit_min || (WIN && j0 < wave_lo_max)) {
 #pragma unroll
-      for (int kt = 0; kt < KT / 32; ++kt)
+      for (int kt = 0; kt < KT / 32; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
           if (key > limit || (WIN && key < lo)) st[kt][r] = -INFINITY;
         }
+        // (keeps the compiler from holding all 64 comparisons in scalar registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    float tmax = -INFINITY;
+    // maximum: one chain per 32-key block, then across blocks and lane halves
+    float bmax[KT / 32];
 #pragma unroll
-    for (int kt = 0; kt < KT / 32; ++kt)
+    for (int kt = 0; kt < KT / 32; ++kt) {
+      bmax[kt] = st[kt][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[kt][r]);
+      for (int r = 1; r < 16; ++r) bmax[kt] = fmaxf(bmax[kt], st[kt][r]);
+    }
+    float tmax = fmaxf(fmaxf(bmax[0], bmax[1]), fmaxf(bmax[2], bmax[3]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     // tmax is relative to mref
     if (__any(tmax + mref > m_run + kRescale)) {
@@ -1026,35 +1096,219 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
 #pragma unroll
     for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // v_exp_f32 directly: probabilities below 2^-126 flush to zero
-        st[kt][r] = __builtin_amdgcn_exp2f(st[kt][r]);
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // v_exp_f32 directly: probabilities below 2^-126 flush to zero
+          pb[kt][u].v[e] = (__bf16)__builtin_amdgcn_exp2f(st[kt][8 * u + e]);
+        }
+        // the normaliser adds the probabilities as rounded for P V
+        l_run = add_bf16x8(pb[kt][u], l_run);
       }
-    const bf16_t* vt = &Vs[buf][vlane];
+    // the probabilities and the normaliser are computed here, not moved past
+    // the barrier into the matrix segment
 #pragma unroll
     for (int kt = 0; kt < KT / 32; ++kt)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        Frag8 pb;
+      for (int u = 0; u < 2; ++u) asm volatile("" : "+v"(pb[kt][u].v));
+    asm volatile("" : "+v"(l_run));
+  };
+  // transposing-read address of this lane within a V tile (see above): key
+  // row 4 g + li / 4 (+ 32 kt + 16 u, + 8), features 32 t + 16 ((lane >> 4) & 1)
+  // + 4 (li & 3), whose slot lies in the slot quarter t ^ vq of the row
+  const int li = lane & 15;
+  const int vrow = 4 * g + (li >> 2);
+  const int vq = vswz(vrow) >> 2;
+  const int vlane = vrow * DH + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+  // P_j from the buffer `v_tile`: eight groups of 16 keys (kt, u); the fragment
+  // of feature tile t for group e + 1 is read right after the MFMA of group e
+  // that last used its registers; after group e, hook(e)
+  auto pv = [&](const bf16_t* v_tile, auto&& hook) __attribute__((always_inline)) {
+    const bf16_t* vt = v_tile + vlane;
+    union VFrag {
+      uint2 h[2];
+      bf16x8_t v;
+    };
+    VFrag vf[DTILES];
+    int vqo = vq;
+    asm volatile("" : "+v"(vqo));
+    // keys 16 e + 4 g + {0..3} and + {8..11} of feature t*32 + c32
+    auto read_v = [&](int e, int t) __attribute__((always_inline)) {
+      const bf16_t* vtt = vt + 16 * e * DH + 32 * (t ^ vqo);
+      vf[t].h[0] = lds_read_tr16(vtt);
+      vf[t].h[1] = lds_read_tr16(vtt + 8 * DH);
+    };
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb.v[e] = (__bf16)st[kt][8 * u + e];
-        // the normaliser adds the probabilities as rounded for P V
-        l_run = add_bf16x8(pb, l_run);
-        // keys kt*32 + 16u + 4g + {0..3} and + {8..11} of feature t*32 + c32
-        const int krow = (kt * 32 + 16 * u) * LDV;
+    for (int t = 0; t < DTILES; ++t) read_v(0, t);
 #pragma unroll
-        for (int t = 0; t < DTILES; ++t) {
-          union {
-            uint2 h[2];
-            bf16x8_t v;
-          } a;
-          a.h[0] = lds_read_tr16(vt + krow + t * 32);
-          a.h[1] = lds_read_tr16(vt + krow + 8 * LDV + t * 32);
-          o[t] = mfma32(a.v, pb.v, o[t]);
-        }
+    for (int e = 0; e < KT / 16; ++e) {
+#pragma unroll
+      for (int t = 0; t < DTILES; ++t) {
+        o[t] = mfma32(vf[t].v, pb[e >> 1][e & 1].v, o[t]);
+        if (e + 1 < KT / 16) read_v(e + 1, t);
+        __builtin_amdgcn_sched_barrier(0);  // (order kept, as for the scores)
       }
-    if (staged) stash(buf ^ 1);
+      hook(e);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // completion of this wave's direct loads
+  auto wait_loads = []() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // a workgroup barrier that waits for this wave's LDS reads but not for its
+  // direct loads (__syncthreads' fence would wait for those too; their own
+  // wait comes a segment later)
+  auto barrier_lds = []() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  auto no_hook = [](int) __attribute__((always_inline)) {};
+
+  // prologue: every wave loads its eighth of K_0 and of (V_0, K_1)
+  if (tid < 6) counters[tid] = 0;
+  {
+    const TileSrc k0 = tile_src(std::false_type(), it_first);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) load_one(std::false_type(), k0, K0, NI * wave_u + i);
+    if (n_it > 1) {
+      const TileSrc v0 = tile_src(std::true_type(), it_first);
+      const TileSrc k1 = tile_src(std::false_type(), it_first + 1);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        load_one(std::true_type(), v0, V0, NI * wave_u + i);
+        load_one(std::false_type(), k1, K1, NI * wave_u + i);
+      }
+    } else {
+      const TileSrc v0 = tile_src(std::true_type(), it_first);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) load_one(std::true_type(), v0, V0, NI * wave_u + i);
+    }
+  }
+  __syncthreads();
+  // tickets: per SIMD (hardware register HW_ID, bits 5:4), then among the
+  // SIMDs' first waves and among their second waves
+  int ticket = 0, idx = 0;
+  if (lane == 0) {
+    ticket = atomicAdd(&counters[(__builtin_amdgcn_s_getreg(0xF804) >> 4) & 3], 1);
+    idx = atomicAdd(&counters[ticket == 0 ? 4 : 5], 1);
+  }
+  ticket = __builtin_amdgcn_readfirstlane(ticket);
+  idx = __builtin_amdgcn_readfirstlane(idx);
+  wait_loads();  // this wave's eighths of K_0, V_0 and K_1
+  __syncthreads();
+  const bool paired = counters[4] == 4 && counters[5] == 4;  // one leading, one trailing wave on each SIMD
+  const bool trail = paired && ticket != 0;
+  // instructions of a tile this wave loads (a quarter paired, else an eighth)
+  // and the first of them
+  const int nq = paired ? 2 * NI : NI;
+  const int q_first = paired ? 2 * NI * idx : NI * wave_u;
+  // the loads of this wave in [P_j, S_j+1] (j = -1: the segment of S_0), one
+  // instruction after each 16-feature step of S_j+1: paired, the leading waves
+  // load K_j+2 and the trailing ones V_j+2; unpaired, every wave loads K_j+2
+  // and V_j+1.  K_j+2 goes into the buffer of K_j, V_j+2 into that of V_j and
+  // V_j+1 into that of V_j-1, each read for the last time by both halves in
+  // or before this wave's P_j.
+  struct Plan {
+    TileSrc k, v;
+    bf16_t* kdst;
+    bf16_t* vdst;
+    int nk, nv;
+  };
+  auto plan_for = [&](auto P, int j) __attribute__((always_inline)) {
+    using Q = std::integral_constant<int, 1 - decltype(P)::value>;
+    Plan pl;
+    pl.nk = 0;
+    pl.nv = 0;
+    pl.kdst = kbuf(P);  // K_j+2: the buffer of K_j
+    if (j >= 0 && (!paired || !trail) && j + 2 < n_it) {
+      pl.nk = nq;
+      pl.k = tile_src(std::false_type(), it_first + j + 2);
+    }
+    if (paired) {
+      pl.vdst = vbuf(P);  // V_j+2: the buffer of V_j
+      if (trail && j + 2 < n_it) {
+        pl.nv = nq;
+        pl.v = tile_src(std::true_type(), it_first + j + 2);
+      }
+    } else {
+      pl.vdst = vbuf(Q());  // V_j+1: the buffer of V_j-1
+      if (j >= 0 && j + 1 < n_it) {
+        pl.nv = nq;
+        pl.v = tile_src(std::true_type(), it_first + j + 1);
+      }
+    }
+    return pl;
+  };
+  auto plan_hook = [&](const Plan& pl) __attribute__((always_inline)) {
+    return [&pl, &load_one, q_first](int u) __attribute__((always_inline)) {
+      if (u < pl.nk) load_one(std::false_type(), pl.k, pl.kdst, q_first + u);
+      else if (u - pl.nk < pl.nv) load_one(std::true_type(), pl.v, pl.vdst, q_first + u - pl.nk);
+    };
+  };
+  if (trail) barrier_lds();
+  {
+    // j = -1 (parity 1): the trailing waves load V_1 into the buffer of V_-1
+    const Plan pl = plan_for(One(), -1);
+    __builtin_amdgcn_s_setprio(1);
+    scores(K0, plan_hook(pl));
+    __builtin_amdgcn_s_setprio(0);
+  }
+  barrier_lds();
+  // one tile: X_j, then [P_j, S_j+1] with this wave's loads; P the parity of j
+  auto step = [&](auto P, int j) __attribute__((always_inline)) {
+    using Q = std::integral_constant<int, 1 - decltype(P)::value>;
+    // X_j; a leading wave's loads from its last [P, S] complete at its end
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(j);
+    if (!trail) wait_loads();
     __syncthreads();
+    // [P_j, S_j+1], at raised priority: the SIMD's other wave is in its X,
+    // whose vector instructions would otherwise be issued first whenever that
+    // wave is the older one, leaving the matrix core waiting
+    const bool more = j + 1 < n_it;
+    __builtin_amdgcn_s_setprio(1);
+    pv(vbuf(P), no_hook);
+    __builtin_amdgcn_sched_barrier(0);
+    bool just_issued = false;  // DSTEPS loads issued below, the newest in flight
+    if (more) {
+      const Plan pl = plan_for(P, j);
+      const bool is_k = pl.nk > 0;
+      const TileSrc& ts = is_k ? pl.k : pl.v;
+      if (pl.nk + pl.nv == 0) {
+        scores(kbuf(Q()), no_hook);
+      } else if (pl.nk + pl.nv == DSTEPS && (pl.nk == 0 || pl.nv == 0) && ts.contiguous) {
+        just_issued = true;
+        // one contiguous tile, one instruction a step: no branch inside the
+        // step sequence (a branch there costs the fragment reads' overlap)
+        const char* base = ts.base;
+        bf16_t* dst = is_k ? pl.kdst : pl.vdst;
+        uint32_t ob = is_k ? koff0 : voff;
+        asm volatile("" : "+v"(ob));
+        scores(kbuf(Q()), [&](int u) __attribute__((always_inline)) {
+          // q_first is a multiple of NI: q mod NI = u mod NI
+          dma_tile(base, dst, q_first + u, ob ^ (is_k ? 64u * uint32_t(u & (NI - 1)) : 0u));
+        });
+      } else {
+        scores(kbuf(Q()), plan_hook(pl));
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // a trailing wave's loads from its last [P, S] complete here (those of
+    // this one may stay in flight: they are read two segments later)
+    if (trail) {
+      if (just_issued) {
+        if constexpr (DSTEPS == 8)
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else {
+        wait_loads();
+      }
+    }
+    // the trailing waves' last segment is the block's last: no barrier after it
+    if (more || !trail) barrier_lds();
+  };
+  for (int j = 0; j < n_it; j += 2) {
+    step(Zero(), j);
+    if (j + 1 < n_it) step(One(), j + 1);
   }
   l_run += __shfl_xor(l_run, 32, 64);
   if (qi < n_b) {
