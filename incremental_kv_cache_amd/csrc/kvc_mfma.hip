@@ -777,6 +777,17 @@ __device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// The larger of v in lanes l and l ^ 32, in every lane, by the vector unit's
+// half-swap (v_permlane32_swap exchanges lanes 32-63 of the first register
+// with lanes 0-31 of the second: copies of v become [lo, lo] and [hi, hi]),
+// not through the LDS pipe as a cross-lane shuffle would be.  (Wait states
+// around it: the compiler sees no hazard through inline asm.)
+__device__ __forceinline__ float max_halves(float v) {
+  float a = v, b = v;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
 // acc plus the eight bf16 values of f (packed dot products with ones)
 __device__ __forceinline__ float add_bf16x8(const Frag8& f, float acc) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -1072,8 +1083,9 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
 #pragma unroll
       for (int r = 1; r < 16; ++r) bmax[kt] = fmaxf(bmax[kt], st[kt][r]);
     }
-    float tmax = fmaxf(fmaxf(bmax[0], bmax[1]), fmaxf(bmax[2], bmax[3]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    // (the maximum gates the exponentials: the LDS pipe, busy with the other
+    // waves' fragment reads, would delay a shuffle)
+    const float tmax = max_halves(fmaxf(fmaxf(bmax[0], bmax[1]), fmaxf(bmax[2], bmax[3])));
     // tmax is relative to mref
     if (__any(tmax + mref > m_run + kRescale)) {
       const float m_new = float((__bf16)fmaxf(m_run, tmax + mref));
