@@ -607,11 +607,18 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   typedef __attribute__((address_space(3))) void lds_void_t;
-  typedef __attribute__((address_space(1))) void glb_void_t;
-  // load instruction j of the K tile at k0 into buffer buf (completion: s_waitcnt vmcnt(0))
+  // load instruction j of the K tile at k0 into buffer buf (completion: s_waitcnt vmcnt(0)), in
+  // the buffer form: a descriptor over the wave's whole source matrix, the lane's row offset in
+  // bytes as the vector offset and the K tile's as the scalar one.  (The global form is counted
+  // as an LDS access as well, so each step's wait for its fragments would also wait for the
+  // tile loads in flight, and it takes the issuing wave several times longer.)
+  const uint32_t src_bytes = uint32_t(fills_x ? M : heads_of(s, p) * dh) * uint32_t(D) * 2u;
+  const __amdgpu_buffer_rsrc_t src_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(gsrc), (short)0, src_bytes, 0x00020000);
   auto fetch_one = [&](int j, int k0, int buf) {
     bf16_t* dst = (fills_x ? &As[buf][0] : &Bs[buf][0]) + (wave_u & 3) * NDMA * 64 * 8;
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(gsrc + off[j] + k0), (lds_void_t*)(dst + j * 64 * 8), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src_rsrc, (lds_void_t*)(dst + j * 64 * 8), 16, uint32_t(off[j]) * 2u,
+                                             uint32_t(k0) * 2u, 0, 0);
   };
   auto fetch = [&](int k0, int buf) {
 #pragma unroll
@@ -1402,7 +1409,8 @@ int mfma_project_t(const DevState& s, const XT* xb, int n_max, int per_seq_rows,
       }
     }
   } else if (std::is_same<XT, bf16_t>::value && M >= 2048 && s.model_width % GBN == 0 && kv_cols % GBN == 0 &&
-             s.head_width % 64 == 0 && int64_t(M) * s.model_width < (int64_t(1) << 31)) {
+             s.head_width % 64 == 0 && int64_t(M) * s.model_width < (int64_t(1) << 31) &&
+             int64_t(std::max(s.heads, s.kv_heads)) * s.head_width * s.model_width < (int64_t(1) << 31)) {
     const int m_tiles = (M + GBM - 1) / GBM;
     const int n_tiles = cols / GBN;
     hipLaunchKernelGGL(project_wide_kernel, dim3(m_tiles * n_tiles), dim3(64 * GWAVES), 0, st(s.stream), s,
