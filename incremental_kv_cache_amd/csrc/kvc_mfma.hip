@@ -529,9 +529,9 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT
 // waits and epilogue instructions overlap the other's MFMAs), each wave a
 // 128 x 64 block held in eight 32x32 accumulators, so a 16-wide step reads 6
 // fragments from LDS for 8 MFMAs.  The 64-wide K tiles of X and W are
-// double-buffered in LDS (144 KB) and go straight from global memory into
-// their buffer by 16-byte direct loads while the tile before is multiplied,
-// one wait and barrier per tile.
+// double-buffered in LDS (128 KB, unpadded rows with swizzled 16-byte slots)
+// and go straight from global memory into their buffer by 16-byte direct
+// loads while the tile before is multiplied, one wait and barrier per tile.
 // Columns: block virtual column v holds pair pair_base + 32 (v / 64) + v % 32,
 // low feature for (v / 32) even, high feature for odd, so the two 32-column
 // subtiles of wave column wn (2 wn and 2 wn + 1) hold the two halves of the
@@ -539,13 +539,26 @@ __global__ __launch_bounds__(256) void project_tiled_kernel(DevState s, const XT
 // Tile order: consecutive tile ids run on one XCD (blocks are dealt to the
 // eight XCDs in turn) and walk 4 row tiles per column step, so the 32 tiles an
 // XCD runs at once share their X and W tiles through its L2.
-constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK + 8, GGROUP = 4, GWAVES = 8;
+constexpr int GBM = 256, GBN = 256, GBK = 64, GLD = GBK, GGROUP = 4, GWAVES = 8;
 
 __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 2))) void project_wide_kernel(
     DevState s, const bf16_t* __restrict__ x, int M, int n_max, int per_seq_rows, int proj_first, int m_tiles,
     int n_tiles) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[2][GBM * GLD];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][GBN * GLD];
+  // two buffers each of the X and W tiles, as four arrays: the compiler tells
+  // direct loads into one array from reads of another apart, so the fragment
+  // reads of the current tiles do not wait for the loads into the next ones
+  __shared__ __attribute__((aligned(16))) bf16_t X0[GBM * GLD];
+  __shared__ __attribute__((aligned(16))) bf16_t X1[GBM * GLD];
+  __shared__ __attribute__((aligned(16))) bf16_t W0[GBN * GLD];
+  __shared__ __attribute__((aligned(16))) bf16_t W1[GBN * GLD];
+  using Zero = std::integral_constant<int, 0>;
+  using One = std::integral_constant<int, 1>;
+  auto xbuf = [&](auto b) __attribute__((always_inline)) -> bf16_t* {
+    if constexpr (decltype(b)::value == 0) return X0; else return X1;
+  };
+  auto wbuf = [&](auto b) __attribute__((always_inline)) -> bf16_t* {
+    if constexpr (decltype(b)::value == 0) return W0; else return W1;
+  };
   const int D = s.model_width;
   const int dh = s.head_width;
   const int half = dh >> 1;
@@ -569,24 +582,26 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
   const int c32 = lane & 31;
 
   // global -> LDS with the 16-byte direct loads: a tile (256 rows of 64
-  // elements, rows padded to GLD) is 2304 16-byte slots, slot q = 9 r + c
-  // holding elements 8 min(c, 7) .. of row r (c = 8 is the padding; it gets a
-  // copy of c = 7), and one wave instruction fills 64 consecutive slots, lane l
-  // slot 64 j + l (LDS byte 16 (64 j + l): the padded row-major layout).  Waves
-  // 0-3 fill the X tile (36 instructions, 9 each), waves 4-7 the W tile;
-  // element offsets are 32-bit (the dispatch checks M * D < 2^31).
+  // elements, 128 bytes) is 2048 16-byte slots, physical slot p = 8 r + s of row
+  // r holding elements 8 (s ^ f(r)) .. of the row, f(r) = (r / 2) mod 8, and one
+  // wave instruction fills 64 consecutive slots, lane l slot 64 j + l (LDS byte
+  // 16 (64 j + l)).  The swizzle puts the 16 rows a 16-lane fragment read takes
+  // on distinct bank groups: row parity picks the half of the 64 banks, f(r)
+  // the 16-byte group within it.  Waves 0-3 fill the X tile (32 instructions,
+  // 8 each), waves 4-7 the W tile; element offsets are 32-bit (the dispatch
+  // checks M * D < 2^31).
   // W tile row v = 32 i + c (c < 32) is virtual column v: pair pair_base +
   // 32 (i / 2) + c, its high feature (+ d_h / 2 rows) for odd i.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const bool fills_x = wave_u < 4;
   const bf16_t* gsrc = fills_x ? x : weight_of(s, p);
-  constexpr int NDMA = 9;  // load instructions per wave and K tile
+  constexpr int NDMA = 8;  // load instructions per wave and K tile
   int off[NDMA];
 #pragma unroll
   for (int j = 0; j < NDMA; ++j) {
     const int q = (wave_u & 3) * NDMA + j;  // instruction within the tile
     const int slot = q * 64 + lane;
-    const int r = slot / 9, c = slot - r * 9;
+    const int r = slot >> 3, c = (slot & 7) ^ ((r >> 1) & 7);
     int row_off;
     if (fills_x) {
       row_off = min(m0 + r, M - 1) * D;
@@ -596,7 +611,7 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
       const int vh = vpair / half;
       row_off = (vh * dh + (vpair - vh * half) + ((i & 1) ? half : 0)) * D;
     }
-    off[j] = row_off + 8 * min(c, 7);
+    off[j] = row_off + 8 * c;
   }
   f32x16_t acc[4][2];
 #pragma unroll
@@ -615,21 +630,24 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
   const uint32_t src_bytes = uint32_t(fills_x ? M : heads_of(s, p) * dh) * uint32_t(D) * 2u;
   const __amdgpu_buffer_rsrc_t src_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(gsrc), (short)0, src_bytes, 0x00020000);
-  auto fetch_one = [&](int j, int k0, int buf) {
-    bf16_t* dst = (fills_x ? &As[buf][0] : &Bs[buf][0]) + (wave_u & 3) * NDMA * 64 * 8;
+  auto fetch_one = [&](int j, int k0, auto buf) __attribute__((always_inline)) {
+    bf16_t* dst = (fills_x ? xbuf(buf) : wbuf(buf)) + (wave_u & 3) * NDMA * 64 * 8;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src_rsrc, (lds_void_t*)(dst + j * 64 * 8), 16, uint32_t(off[j]) * 2u,
                                              uint32_t(k0) * 2u, 0, 0);
   };
-  auto fetch = [&](int k0, int buf) {
+  auto fetch = [&](int k0, auto buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < NDMA; ++j) fetch_one(j, k0, buf);
   };
   // fragments of one 16-wide step, double-buffered in registers: step ks + 1
   // is read from LDS while step ks's 16 MFMAs run
   Frag8 fa[2][4], fb[2][2];
-  auto read_frags = [&](int buf, int ks, int slot) {
-    const bf16_t* ar = &As[buf][(wm * 128 + c32) * GLD + 8 * g + 16 * ks];
-    const bf16_t* br = &Bs[buf][(wn * 64 + c32) * GLD + 8 * g + 16 * ks];
+  // (rows 32 i + c32 of either tile: f(row) = (c32 / 2) mod 8 for every i)
+  const int fsw = (c32 >> 1) & 7;
+  auto read_frags = [&](auto buf, int ks, int slot) __attribute__((always_inline)) {
+    const int ps = 8 * (((2 * ks + g) ^ fsw) & 7);
+    const bf16_t* ar = xbuf(buf) + (wm * 128 + c32) * GLD + ps;
+    const bf16_t* br = wbuf(buf) + (wn * 64 + c32) * GLD + ps;
 #pragma unroll
     for (int i = 0; i < 4; ++i) fa[slot][i].u = *reinterpret_cast<const uint4*>(ar + i * 32 * GLD);
 #pragma unroll
@@ -641,7 +659,8 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
   // MFMAs with up to six load instructions of a K tile (dma_first ..., at k0
   // into buffer dbuf) between them: the load path takes loads far slower than a
   // wave issues them, and a wave stuck issuing loads issues no MFMAs.
-  auto step = [&](int cur, int rbuf, int rks, int dma_first, int dma_count, int dk, int dbuf) {
+  auto step = [&](int cur, auto rbuf, int rks, int dma_first, int dma_count, int dk, auto dbuf)
+                  __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xC07F);
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[0][j] = mfma32(fa[cur][0].v, fb[cur][j].v, acc[0][j]);
@@ -661,40 +680,52 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
   // Steps 0-2 of K tile kt run before the tile's barrier and step 3 after it,
   // so the next tile's first fragments are read under step 3's MFMAs; tile
   // kt + 2 starts loading into tile kt's buffer in step 3 (6 instructions) and
-  // step 0 of the next tile (3), and is waited for four steps later.  Past the
+  // step 0 of the next tile (2), and is waited for four steps later.  Past the
   // last tile the last one is loaded again (never read).
   const int ktiles = D / GBK;
   auto k_of = [&](int t) { return min(t, ktiles - 1) * GBK; };
-  fetch(0, 0);
+  fetch(0, Zero());
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  read_frags(0, 0, 0);
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int buf = kt & 1;
+  read_frags(Zero(), 0, 0);
+  // K tile kt in buffer B (the parity of kt), the next one in NB
+  auto ktile = [&](auto B, int kt) __attribute__((always_inline)) {
+    using NB = std::integral_constant<int, 1 - decltype(B)::value>;
     if (kt == 0) {
-      step(0, buf, 1, 0, 6, k_of(1), buf ^ 1);
-      step(1, buf, 2, 6, 3, k_of(1), buf ^ 1);
+      step(0, B, 1, 0, 6, k_of(1), NB());
+      step(1, B, 2, 6, 2, k_of(1), NB());
     } else {
-      step(0, buf, 1, 6, 3, k_of(kt + 1), buf ^ 1);
-      step(1, buf, 2, 0, 0, 0, 0);
+      step(0, B, 1, 6, 2, k_of(kt + 1), NB());
+      step(1, B, 2, 0, 0, 0, NB());
     }
-    step(0, buf, 3, 0, 0, 0, 0);
+    step(0, B, 3, 0, 0, 0, NB());
     // tile kt + 1 in LDS, and this wave's reads of tile kt done (its buffer is
     // reloaded after the barrier)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    step(1, buf ^ 1, 0, 0, 6, k_of(kt + 2), buf);
+    step(1, NB(), 0, 0, 6, k_of(kt + 2), B);
+  };
+  for (int kt = 0; kt < ktiles; kt += 2) {
+    ktile(Zero(), kt);
+    if (kt + 1 < ktiles) ktile(One(), kt + 1);
   }
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
   // epilogue, one 32-row quarter of the wave's block at a time, through LDS
-  // (the K-tile buffers are free now).  The wave's 64 columns are the low and
+  // (the K-tile buffers are free now: two waves stage into each).  The wave's 64 columns are the low and
   // high features of 32 pairs; lane (row r8, c4) then handles four consecutive
   // pairs of rows r8, r8 + 8, ..: 8 lanes cover one row's 32 pairs, with one
   // rotary table load per factor and 16-byte stores.
   constexpr int EPS = 64 + 4;  // staging row stride (floats)
-  static_assert(GWAVES * 32 * EPS * 4 <= 2 * GBM * GLD * 2, "staging fits the X buffers");
-  float* ep = reinterpret_cast<float*>(&As[0][0]) + __builtin_amdgcn_readfirstlane(wave) * 32 * EPS;
+  static_assert(2 * 32 * EPS * 4 <= GBM * GLD * 2 && GBM == GBN, "staging of two waves fits one tile buffer");
+  bf16_t* stage_base = X0;
+  switch (wave_u >> 1) {
+    case 0: break;
+    case 1: stage_base = X1; break;
+    case 2: stage_base = W0; break;
+    default: stage_base = W1; break;
+  }
+  float* ep = reinterpret_cast<float*>(stage_base) + (wave_u & 1) * 32 * EPS;
   const int wrow0 = m0 + __builtin_amdgcn_readfirstlane(wm) * 128;
   const int r8 = lane >> 3;
   const int c4 = (lane & 7) * 4;
