@@ -175,6 +175,41 @@ def test_wide_projection_chunk(B, n_max, H, rows, cuts):
             assert_parity(storage_f64(v, "bf16"), full["values"], "bf16", f"values {b}")
 
 
+def test_wide_projection_grouped_heads_and_output_projection():
+    """2250 bf16 rows of a grouped layer (8 query heads over 2 key/value heads, d_h
+    128, D 1024) with W_o bound: the 256 x 256 projection kernel takes W_q and the
+    narrower W_k and W_v column tiles, and the float32 merged heads go through
+    W_o; outputs (after W_o), stored keys and values match the float64 grouped
+    layer for ragged rows and retained prefixes."""
+    D, heads, kv_heads, dh = 1024, 8, 2, 128
+    B, n_max = 5, 450
+    rows, cuts = [450, 1, 0, 300, 449], [0, 5, 3, 100, 17]
+    cap = max(cuts) + n_max + 8
+    ws = synth.grouped_weights(61, D, kv_heads * dh, D ** -0.5, "bf16")
+    wo_s, wo_f = synth.output_weight(61, D, D ** -0.5, "bf16")
+    params = K.kvc_params_create_grouped(*[to_device(s, "bf16") for s, _ in ws], to_device(wo_s, "bf16"))
+    layer = K.kvc_layer_create(params, heads, K.KVC_POS_ROPE, 10000.0, cap)
+    w = [f for _, f in ws]
+    cache = K.kvc_cache_create(layer, B, cap, max_chunk_rows=n_max)
+    xp_dev, xp = hidden(62, synth.STREAM_PREFIX_X, B, max(cuts), D, "bf16")
+    K.kvc_continue_chunk(layer, cache, xp_dev, n_rows=cuts)
+    xn_dev, xn = hidden(62, synth.STREAM_X, B, n_max, D, "bf16")
+    out, _ = K.kvc_continue_chunk(layer, cache, xn_dev, n_rows=rows)
+    o = to_f64(out)
+    for b in range(B):
+        seq = np.concatenate([xp[b, : cuts[b]], xn[b, : rows[b]]])
+        full = A.causal_layer(seq, *w, heads=heads, kv_heads=kv_heads, wo=wo_f,
+                              rows=range(cuts[b], cuts[b] + rows[b]))
+        if rows[b]:
+            assert_parity(o[b, : rows[b]], full["out"], "bf16", f"seq {b}")
+        assert not np.any(o[b, rows[b]:])
+        if len(seq):
+            k, v, pos = K.kvc_snapshot(cache, b)
+            assert k.shape == (kv_heads, len(seq), dh) and list(pos) == list(range(len(seq)))
+            assert_parity(storage_f64(k, "bf16"), full["keys"], "bf16", f"keys {b}")
+            assert_parity(storage_f64(v, "bf16"), full["values"], "bf16", f"values {b}")
+
+
 @pytest.mark.parametrize("D,heads,kv_heads,B,wo", [(2048, 16, 16, 5, True), (4096, 32, 8, 32, False),
                                                    (4096, 32, 32, 1, False)])
 def test_split_decode_projection(D, heads, kv_heads, B, wo):
