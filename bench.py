@@ -192,6 +192,26 @@ def measured_traffic(name):
     return m["fetch_kib"] * 1024 * m["fetch_scale"] + m["write_kib"] * 1024 * m["write_scale"]
 
 
+def decode_kv_bytes(rows, kv_heads, head_width):
+    """Algorithmic bytes of one decode attention launch: every row a newest query
+    reads (the retained rows plus the candidate, `rows` per sequence), K and V of
+    every key/value head, bf16."""
+    return sum(2 * kv_heads * t * head_width * 2 for t in rows)
+
+
+def chunk_attention_flops(cuts, n, heads, head_width):
+    """Algorithmic flops of the chunk attention: chunk row i of a sequence cut at c
+    attends keys 0 .. c + i; each (query, key) pair costs q.k and p v, 2 d_h flops
+    each, per head."""
+    return sum(4 * heads * head_width * sum(c + i + 1 for i in range(n)) for c in cuts)
+
+
+def chunk_projection_flops(rows, model_width, kv_width):
+    """Algorithmic flops of the chunk projection: every row through W_q [D, D] and
+    W_k, W_v [kv_width, D]."""
+    return 2 * rows * model_width * (model_width + 2 * kv_width)
+
+
 def time_steps(pre, call, steps, warmup):
     """W untimed warm-up steps, then K steps, each `pre()` (outside the timing)
     then `call()` between two HIP events on the current stream (the cache's).
@@ -418,7 +438,7 @@ def run_decode(name, wl, steps, warmup, cpu):
     achievable = achievable_read_gbps()
     t = [s + 1 for s in start]
     HK = wl.get("kv_heads", H)
-    kv_bytes = sum(2 * HK * tb * dh * 2 for tb in t)
+    kv_bytes = decode_kv_bytes(t, HK, dh)
     attend_ms = st[1]
     att_gbps = kv_bytes / (attend_ms * 1e-3) / 1e9
     attn_merge_gbps = kv_bytes / ((st[1] + st[2]) * 1e-3) / 1e9
@@ -478,8 +498,8 @@ def run_chunk(name, wl, steps, warmup, cpu):
     K.kvc_sync(cache)
     torch.cuda.synchronize()
     mfma_tf = achievable_mfma_tflops()
-    attn_flops = sum(4 * H * dh * sum(c + i + 1 for i in range(n)) for c in start)
-    proj_flops = 2 * B * n * D * 3 * D
+    attn_flops = chunk_attention_flops(start, n, H, dh)
+    proj_flops = chunk_projection_flops(B * n, D, wl.get("kv_heads", H) * dh)
     att_tf = attn_flops / (st[1] * 1e-3) / 1e12
     proj_tf = proj_flops / (st[0] * 1e-3) / 1e12
     res = {
@@ -562,7 +582,7 @@ def run_session(name, wl, steps, warmup, cpu):
         att.append(ms[1] / calls[1])
         K.kvc_profile_enable(c, 0)
     K.kvc_session_sync(sess)
-    kv_bytes = 2 * B * H * C * dh * 2  # per layer: t = C rows per lane
+    kv_bytes = decode_kv_bytes([C] * B, H, dh)  # per layer: t = C rows per lane
     attend_ms = float(np.mean(att))
     att_gbps = kv_bytes / (attend_ms * 1e-3) / 1e9
     return {
