@@ -71,11 +71,11 @@ MEASURED_TRAFFIC = {
                  "kernel_source_sha256": "ff3b3a9411d402a8edf4b3a8f93d5def7cd1c117ebc40b471aaa0ac8c98fb43f"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
     "chunk": {"source": "mfma", "fetch_kib": 299400.2, "fetch_scale": 2.0, "write_kib": 98304.0, "write_scale": 1.0,
-              "kernel_source_sha256": "89502459353e7309cb55db143fed4fdb3881edb460fa5fbfa6679bbed7778930"},
+              "kernel_source_sha256": "5b5fad770cdfe8d46fb878812d862d4a8181a5b23c6dc7d5dba163bf3d16e685"},
     # attend_flash_kernel, suffix chunk (B=8, n=512)
     "chunk_attention": {"source": "mfma", "fetch_kib": 338479.6, "fetch_scale": 2.0, "write_kib": 65539.6,
                         "write_scale": 1.0,
-                        "kernel_source_sha256": "89502459353e7309cb55db143fed4fdb3881edb460fa5fbfa6679bbed7778930"},
+                        "kernel_source_sha256": "5b5fad770cdfe8d46fb878812d862d4a8181a5b23c6dc7d5dba163bf3d16e685"},
 }
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
                   "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}

@@ -582,14 +582,14 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
   const int c32 = lane & 31;
 
   // global -> LDS with the 16-byte direct loads: a tile (256 rows of 64
-  // elements, 128 bytes) is 2048 16-byte slots, physical slot p = 8 r + s of row
-  // r holding elements 8 (s ^ f(r)) .. of the row, f(r) = (r / 2) mod 8, and one
+  // elements, 128 bytes) is 2048 16-byte slots, slot 8 r + u (u < 8) of row r
+  // holding elements 8 (u ^ f(r)) .. of the row, f(r) = (r / 2) mod 8, and one
   // wave instruction fills 64 consecutive slots, lane l slot 64 j + l (LDS byte
   // 16 (64 j + l)).  The swizzle puts the 16 rows a 16-lane fragment read takes
   // on distinct bank groups: row parity picks the half of the 64 banks, f(r)
   // the 16-byte group within it.  Waves 0-3 fill the X tile (32 instructions,
   // 8 each), waves 4-7 the W tile; element offsets are 32-bit (the dispatch
-  // checks M * D < 2^31).
+  // checks M * D and the weight rows times D against 2^31).
   // W tile row v = 32 i + c (c < 32) is virtual column v: pair pair_base +
   // 32 (i / 2) + c, its high feature (+ d_h / 2 rows) for odd i.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
