@@ -488,6 +488,7 @@ void free_cache(kvc_cache* c) {
   dev_free(c->ds.cand_v);
   dev_free(c->ds.q);
   dev_free(c->ds.partials);
+  dev_free(c->ds.redo);
   dev_free(c->ds.rope_cos);
   dev_free(c->ds.rope_sin);
   if (!c->session) dev_free(c->ds.err);
@@ -874,6 +875,11 @@ kvc_status create_cache(const kvc_layer* layer, int32_t batch, int32_t capacity,
       {&s.cand_v, round16(size_t(cand) * es)},
       {&s.q, round16(size_t(qrows) * as)},
       {&s.partials, round16(size_t(batch) * H * max_tiles * (dh + 2) * as)},
+      // the role-split chunk attention's recompute flags, one per (work item, head)
+      {reinterpret_cast<void**>(&s.redo),
+       p->dtype == KVC_BF16 && dh == 128 && W == 0
+           ? round16(sizeof(int32_t) * size_t(batch) * ((max_chunk_rows + kChunkQueryTile - 1) / kChunkQueryTile) * H)
+           : 0},
       {reinterpret_cast<void**>(&s.err), shared_err ? 0 : round16(sizeof(ErrWords))},
       {&s.merged, p->w[3] ? round16(size_t(qrows) * as) : 0},  // [B, max_chunk_rows, D]
       // split-K partial sums of the bf16 decode projection (one 32-row tile)

@@ -74,6 +74,7 @@ struct DevState {
   void* merged;        // [B, n, D] accumulate type: merged heads before W_o (null without W_o)
   void* out_proj_dst;  // [B, n, D] accumulate type: destination of the W_o projection (per call)
   void* partials;      // [B, H, max_tiles, d_h + 2] accumulate type
+  int32_t* redo;       // bf16 chunk calls at d_h = 128: per workgroup of the role-split attention, 1 = recompute
   float* proj_partials;  // bf16 caches: [kSkinnySplitMax, 64, D + 2 kv_width] float32 split-K sums of
                          // the skinny projection (null: that projection runs unsplit)
   int max_tiles;       // ceil(C / kDecodeTileRows)

@@ -839,7 +839,10 @@ __device__ __forceinline__ float add_bf16x8(const Frag8& f, float acc) {
 // WIN: sliding-window layer (ring storage, a lower key bound per query).
 template <int DH, bool WIN>
 __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_flash_kernel(
-    DevState s, int n_max, int per_seq_rows, ChunkOrder order, float* __restrict__ out) {
+    DevState s, int n_max, int per_seq_rows, ChunkOrder order, float* __restrict__ out,
+    const int32_t* __restrict__ redo) {
+  // after the role-split kernel: only the work items it handed back
+  if (redo && redo[blockIdx.x] == 0) return;
   constexpr int KT = 128;  // keys per LDS tile (two buffers of K and V: 128 KB at d_h = 128)
   static_assert(kMinBlockRows % KT == 0, "a key tile must stay inside one block");
   constexpr int DSTEPS = DH / 16;
@@ -1381,6 +1384,470 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
   }
 }
 
+// Chunk attention with the two waves of each SIMD in different roles (bf16,
+// d_h = 128, no window; the same work items and results as the general
+// kernel).  The workgroup takes 256 queries in four groups of 64.  Wave p
+// (p < 4) forms the scores and probabilities of group p, its two 32-query
+// blocks sharing every K fragment read; wave p + 4 accumulates O^T += V^T P^T
+// for the same queries, the two blocks sharing every V^T fragment read, and
+// takes the probabilities through LDS, adding them up as it goes.  Per query
+// and key, LDS carries half the fragment bytes of the general kernel's 32
+// queries per wave, plus the probabilities.  Keys pass in 64-row tiles, three
+// buffers each of K and V and two of probabilities (160 KB).  Step t: the
+// scoring wave runs the scores of tile t's second 32 keys and of tile t + 1's
+// first 32 keys, each interleaved with the exponentials of the 32 keys before
+// (two register sets); the accumulating wave runs P V of tile t - 1 and loads
+// K_t+2 and V_t+1; one barrier.  Each query keeps one fixed reference, the
+// bf16-rounded maximum of its first 32 scores, and is never rescaled: the
+// probabilities relative to it lose nothing in floating point unless a later
+// score passes it by ~2^7 (base 2), which makes a sum or an accumulator
+// non-finite; a work item whose sums pass 2^100 or whose outputs come out
+// non-finite writes nothing, is marked in `redo` and is recomputed by the
+// general kernel, which raises its reference as the scores rise.
+template <int DH>
+__global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_split_kernel(
+    DevState s, int n_max, int per_seq_rows, ChunkOrder order, float* __restrict__ out) {
+  static_assert(DH == 128, "the split path takes d_h = 128");
+  constexpr int KT = 64;
+  static_assert(kMinBlockRows % KT == 0, "a key tile must stay inside one block");
+  constexpr int DSTEPS = DH / 16;
+  constexpr int DTILES = DH / 32;
+  constexpr int SPR = DH / 8;
+  constexpr int RPS = 16 / SPR;
+  constexpr int RPL = 64 / SPR;       // rows of one load instruction
+  constexpr int NLD = KT / RPL / 4;   // load instructions of a tile per loading wave
+  constexpr int QT = kChunkQueryTile;
+  static_assert(QT == 256, "four groups of 64 queries");
+  constexpr int TILE = KT * DH;
+  constexpr int PFR = 4 * 8 * 64;     // 16-byte pieces of a probability buffer
+  __shared__ __attribute__((aligned(16))) bf16_t K0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t K1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t K2[TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t V0[TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t V1[TILE];
+  __shared__ __attribute__((aligned(16))) bf16_t V2[TILE];
+  __shared__ __attribute__((aligned(16))) uint4 P0[PFR];
+  __shared__ __attribute__((aligned(16))) uint4 P1[PFR];
+  auto kbuf = [&](auto i) __attribute__((always_inline)) -> bf16_t* {
+    constexpr int v = decltype(i)::value % 3;
+    if constexpr (v == 0) return K0; else if constexpr (v == 1) return K1; else return K2;
+  };
+  auto vbuf = [&](auto i) __attribute__((always_inline)) -> bf16_t* {
+    constexpr int v = decltype(i)::value % 3;
+    if constexpr (v == 0) return V0; else if constexpr (v == 1) return V1; else return V2;
+  };
+  auto pbuf = [&](auto i) __attribute__((always_inline)) -> uint4* {
+    if constexpr (decltype(i)::value % 2 == 0) return P0; else return P1;
+  };
+
+  const int H = s.heads;
+  const int item = blockIdx.x / H;
+  const int slot = blockIdx.x - item * H;
+  const int h = (s.kv_heads < H && (H & 7) == 0) ? (slot & 7) * (H >> 3) + (slot >> 3) : slot;
+  int b, qt;
+  if (order.count) {
+    b = order.item[item] >> 16;
+    qt = order.item[item] & 0xffff;
+  } else {
+    b = item / order.qtiles;
+    qt = order.qtiles - 1 - (item - b * order.qtiles);
+  }
+  const int tid = threadIdx.x;
+  const int n_b = per_seq_rows ? s.rows[b] : n_max;
+  if (qt * QT >= n_b) {
+    if (tid == 0) s.redo[blockIdx.x] = 0;
+    return;
+  }
+  const int len = min(max(s.len[b], 0), s.capacity);
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave & 3;
+  const int g = lane >> 5;
+  const int c32 = lane & 31;
+  const int qbase = qt * QT + 64 * grp;
+  const int i_max = min(qt * QT + QT - 1, n_b - 1);
+  const int total = len + i_max + 1;
+  const int n_it = (total + KT - 1) / KT;  // key tiles of the workgroup, >= 1
+  // tiles holding a key that some query of the group sees (none when the
+  // group starts past the chunk's last row)
+  const int grp_tiles = qbase < n_b ? (len + min(qbase + 63, n_b - 1)) / KT + 1 : 0;
+  const int grp_limit_min = len + min(qbase, n_b - 1);
+  const size_t lane_id = size_t(b) * H + h;
+  const int hk = h / (H / s.kv_heads);
+  const size_t kv_lane = size_t(b) * s.kv_heads + hk;
+  const bf16_t* kc = static_cast<const bf16_t*>(s.keys);
+  const bf16_t* vc = static_cast<const bf16_t*>(s.values);
+  const bf16_t* kn = static_cast<const bf16_t*>(s.cand_k) + kv_lane * n_max * DH;
+  const bf16_t* vn = static_cast<const bf16_t*>(s.cand_v) + kv_lane * n_max * DH;
+
+  // tiles: unpadded rows, 16-byte slots permuted as in the general kernel
+  auto kswz = [](int r) __attribute__((always_inline)) { return (r / RPS) & (SPR - 1); };
+  auto vswz = [](int r) __attribute__((always_inline)) { return 4 * ((r / RPS) & (SPR / 4 - 1)); };
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  typedef __attribute__((address_space(1))) void glb_void_t;
+  auto wait_loads = []() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  auto barrier_lds = []() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  using Z0 = std::integral_constant<int, 0>;
+  using Z1 = std::integral_constant<int, 1>;
+  using Z2 = std::integral_constant<int, 2>;
+  using Z3 = std::integral_constant<int, 3>;
+  using Z4 = std::integral_constant<int, 4>;
+  using Z5 = std::integral_constant<int, 5>;
+  // steps 0 .. n_it, each ending in the workgroup barrier; the step's index
+  // modulo 6 as a type (it selects the buffers)
+  auto run_steps = [&](auto&& step) __attribute__((always_inline)) {
+    for (int t0 = 0;; t0 += 6) {
+      step(Z0(), t0);
+      if (t0 + 1 > n_it) break;
+      step(Z1(), t0 + 1);
+      if (t0 + 2 > n_it) break;
+      step(Z2(), t0 + 2);
+      if (t0 + 3 > n_it) break;
+      step(Z3(), t0 + 3);
+      if (t0 + 4 > n_it) break;
+      step(Z4(), t0 + 4);
+      if (t0 + 5 > n_it) break;
+      step(Z5(), t0 + 5);
+      if (t0 + 6 > n_it) break;
+    }
+  };
+
+  if (wave < 4) {
+    // ------------------------------------------------ scores and probabilities
+    // The scores go by 32-key blocks (block 2 t + kb: keys 32 kb .. of tile
+    // t): while one block's probabilities are formed (vector unit), the next
+    // block's scores run (matrix cores), in two sets of registers by kb.  Step
+    // t: [scores of block (t, 1) | probabilities of (t, 0)], then [scores of
+    // (t + 1, 0) | probabilities of (t, 1)].
+    Frag8 qf[2][DSTEPS];
+    int limit[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qe = min(qbase + 32 * qb + c32, n_b - 1);
+      limit[qb] = len + qe;
+      const bf16_t* qp = static_cast<const bf16_t*>(s.q) + (lane_id * n_max + qe) * DH;
+#pragma unroll
+      for (int u = 0; u < DSTEPS; ++u) qf[qb][u].u = *reinterpret_cast<const uint4*>(qp + 16 * u + 8 * g);
+    }
+    float mref[2] = {0.f, 0.f};  // the fixed references, subtracted before the exponentials
+    f32x16_t st[2][2];           // [kb][query block]
+    const int kx = kswz(c32);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    // S^T of the 32 keys at rows 32 KB .. of a K tile into set KB, each K
+    // fragment read two 16-feature steps ahead; hook(u) after step u's MFMAs
+    auto scores = [&](auto KB, const bf16_t* ktile, auto&& hook) __attribute__((always_inline)) {
+      constexpr int kb = decltype(KB)::value;
+      const bf16_t* kr = ktile + (32 * kb + c32) * DH;
+      int kxo = kx;
+      asm volatile("" : "+v"(kxo));
+      Frag8 kf[3];
+      auto read_k = [&](int u) __attribute__((always_inline)) {
+        kf[u % 3].u = *reinterpret_cast<const uint4*>(&kr[8 * ((2 * u + g) ^ kxo)]);
+      };
+      read_k(0);
+      read_k(1);
+      read_k(2);
+      f32x16_t z;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) z[r] = 0.f;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < DSTEPS; ++u) {
+        st[kb][0] = mfma32(kf[u % 3].v, qf[0][u].v, u == 0 ? z : st[kb][0]);
+        st[kb][1] = mfma32(kf[u % 3].v, qf[1][u].v, u == 0 ? z : st[kb][1]);
+        if (u + 3 < DSTEPS) read_k(u + 3);
+        hook(u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // keys past a query's last key, in set KB holding block (t, KB)
+    auto mask = [&](auto KB, int t) __attribute__((always_inline)) {
+      constexpr int kb = decltype(KB)::value;
+      const int j0 = t * KT + 32 * kb;
+      if (j0 + 31 > grp_limit_min) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key > limit[qb]) st[kb][qb][r] = -INFINITY;
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // slice i (of 8) of the probabilities of set KB: four exponentials of
+    // fragment f = (2 KB + qb) 2 + half, (qb, half) = (i / 4, (i / 2) mod 2);
+    // a fragment complete goes to the group's slice of the P buffer at
+    // f 64 + lane
+    Frag8 pcur;
+    auto prob_slice = [&](auto KB, uint4* pdst, int i) __attribute__((always_inline)) {
+      constexpr int kb = decltype(KB)::value;
+      const int qb = i >> 2, hf = (i >> 1) & 1, part = i & 1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pcur.v[4 * part + e] = (__bf16)__builtin_amdgcn_exp2f(st[kb][qb][8 * hf + 4 * part + e] - mref[qb]);
+      if (part) pdst[grp * 8 * 64 + ((2 * kb + qb) * 2 + hf) * 64 + lane] = pcur.u;
+    };
+    barrier_lds();  // K_0, K_1 in LDS
+    // block (0, 0) and the fixed references: maxima of its keys
+    if (grp_tiles > 0) {
+      scores(S0(), K0, [](int) {});
+      mask(S0(), 0);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float m = st[0][qb][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) m = fmaxf(m, st[0][qb][r]);
+        mref[qb] = float((__bf16)max_halves(m));
+      }
+    }
+    run_steps([&](auto T, int t) __attribute__((always_inline)) {
+      using TC = std::integral_constant<int, decltype(T)::value>;            // K_t
+      using TN = std::integral_constant<int, (decltype(T)::value + 1) % 6>;  // K_t+1
+      const int lim = min(n_it, grp_tiles);
+      if (t < lim) {
+        uint4* pdst = pbuf(T);
+        // [scores of (t, 1) | probabilities of (t, 0)]
+        __builtin_amdgcn_s_setprio(2);
+        scores(S1(), kbuf(TC()), [&](int u) __attribute__((always_inline)) { prob_slice(S0(), pdst, u); });
+        __builtin_amdgcn_s_setprio(0);
+        mask(S1(), t);
+        // [scores of (t + 1, 0) | probabilities of (t, 1)]
+        if (t + 1 < lim) {
+          __builtin_amdgcn_s_setprio(2);
+          scores(S0(), kbuf(TN()), [&](int u) __attribute__((always_inline)) { prob_slice(S1(), pdst, u); });
+          __builtin_amdgcn_s_setprio(0);
+          mask(S0(), t + 1);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) prob_slice(S1(), pdst, i);
+        }
+      }
+      barrier_lds();
+    });
+    barrier_lds();  // the accumulating waves' verdicts
+    return;
+  }
+
+  // ----------------------------------------------------------- P V and loads
+  const int lr = lane / SPR, lc = lane & (SPR - 1);
+  const uint32_t voff = uint32_t(lr * DH + 8 * (lc ^ vswz(lr))) * 2u;
+  const uint32_t koff0 = uint32_t(lr * DH + 8 * (lc ^ kswz(lr))) * 2u;
+  auto block_base = [&](int r0) __attribute__((always_inline)) -> ptrdiff_t {
+    if (!s.paged) return kv_block_base(s, b, hk, r0);
+    typedef const __attribute__((address_space(4))) int32_t* const_i32_t;
+    const int lg = s.block_rows_log2;
+    const int blk = max(((const_i32_t)s.block_table)[size_t(b) * s.table_width + (r0 >> lg)], 0);
+    return (ptrdiff_t(size_t(blk) * s.kv_heads + hk) << lg) * DH - ptrdiff_t((r0 >> lg) << lg) * DH;
+  };
+  struct TileSrc {
+    const char* base;
+    const bf16_t* cached;
+    const bf16_t* chunk;
+    int j0;
+    bool contiguous;
+  };
+  auto tile_src = [&](auto is_v, int t) __attribute__((always_inline)) {
+    TileSrc src;
+    const bf16_t* cache = is_v ? vc : kc;
+    src.chunk = is_v ? vn : kn;
+    src.j0 = t * KT;
+    src.cached = cache + block_base(min(src.j0, max(len - 1, 0)));
+    src.contiguous = src.j0 + KT <= len || (src.j0 >= len && src.j0 + KT <= total);
+    src.base = reinterpret_cast<const char*>(src.j0 < len ? src.cached + ptrdiff_t(src.j0) * DH
+                                                          : src.chunk + size_t(src.j0 - len) * DH);
+    return src;
+  };
+  auto dma_tile = [&](const char* first, bf16_t* tile, int q, uint32_t off) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(first), (short)0, KT * DH * 2, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(tile + q * RPL * DH), 16, off, q * (RPL * DH * 2), 0, 0);
+  };
+  // load instruction q (rows RPL q ..) of tile src into `tile`.  A tile that
+  // is not one run of rows is loaded row by row, the lanes of cache rows and
+  // those of chunk rows each through a descriptor of their own (rows past the
+  // last key repeat it; the mask hides them).  (All loads take the buffer
+  // form: the compiler counts the global form as an LDS access too, and then
+  // waits for every LDS read in flight behind it.)
+  auto load_one = [&](auto is_v, const TileSrc& src, bf16_t* tile, int q) __attribute__((always_inline)) {
+    uint32_t off = is_v ? voff : koff0;
+    asm volatile("" : "+v"(off));
+    if (!is_v) off ^= 64u * uint32_t(q & 3);
+    if (src.contiguous) {
+      dma_tile(src.base, tile, q, off);
+    } else {
+      int row = lr;
+      asm volatile("" : "+v"(row));
+      const int j = min(src.j0 + RPL * q + row, total - 1);
+      const uint32_t in_row = off & uint32_t(DH * 2 - 1);
+      const uint32_t roff = uint32_t(j - src.j0) * uint32_t(DH * 2) + in_row;
+      if (j < len) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(src.cached + ptrdiff_t(src.j0) * DH), (short)0, KT * DH * 2, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(tile + q * RPL * DH), 16, roff, 0, 0, 0);
+      } else {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16_t*>(src.chunk + (ptrdiff_t(src.j0) - len) * DH), (short)0, KT * DH * 2, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(tile + q * RPL * DH), 16, roff, 0, 0, 0);
+      }
+    }
+  };
+  // this wave's quarter of the tiles: instructions NLD grp ..
+  const int q0 = NLD * grp;
+  {
+    const TileSrc k0 = tile_src(std::false_type(), 0);
+    const TileSrc v0 = tile_src(std::true_type(), 0);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) load_one(std::false_type(), k0, K0, q0 + i);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) load_one(std::true_type(), v0, V0, q0 + i);
+    if (n_it > 1) {
+      const TileSrc k1 = tile_src(std::false_type(), 1);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) load_one(std::false_type(), k1, K1, q0 + i);
+    }
+  }
+
+  float l_run[2] = {0.f, 0.f};
+  f32x16_t o[2][DTILES];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int t = 0; t < DTILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qb][t][r] = 0.f;
+  // transposing-read address of this lane within a V tile (as in the general
+  // kernel): key row 4 g + li / 4 (+ 16 e, + 8), features 32 t + 16 ((lane >> 4)
+  // & 1) + 4 (li & 3), in the slot quarter t ^ vq of the row
+  const int li = lane & 15;
+  const int vrow = 4 * g + (li >> 2);
+  const int vq = vswz(vrow) >> 2;
+  const int vlane = vrow * DH + 16 * ((lane >> 4) & 1) + 4 * (li & 3);
+  union VFrag {
+    uint2 hh[2];
+    bf16x8_t v;
+  };
+  // O^T += V^T P^T over the 64 keys of a V tile: 16 steps k (16-key group
+  // k / 4, feature tile k mod 4), V^T fragments read three steps ahead;
+  // hook(k) after step k
+  auto pv = [&](const bf16_t* vtile, const uint4* psrc, auto&& hook) __attribute__((always_inline)) {
+    Frag8 pf[8];
+    const uint4* pr = psrc + grp * 8 * 64 + lane;
+#pragma unroll
+    for (int f = 0; f < 8; ++f) pf[f].u = pr[f * 64];
+    // the sums add the probabilities as rounded (fragment f: query block (f >> 1) & 1)
+#pragma unroll
+    for (int f = 0; f < 8; ++f) l_run[(f >> 1) & 1] = add_bf16x8(pf[f], l_run[(f >> 1) & 1]);
+    const bf16_t* vt = vtile + vlane;
+    int vqo = vq;
+    asm volatile("" : "+v"(vqo));
+    VFrag vf[4];
+    auto read_v = [&](int k) __attribute__((always_inline)) {
+      const bf16_t* vtt = vt + 16 * (k >> 2) * DH + 32 * ((k & 3) ^ vqo);
+      vf[k & 3].hh[0] = lds_read_tr16(vtt);
+      vf[k & 3].hh[1] = lds_read_tr16(vtt + 8 * DH);
+    };
+    read_v(0);
+    read_v(1);
+    read_v(2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int e = k >> 2, t = k & 3;
+      o[0][t] = mfma32(vf[k & 3].v, pf[(2 * (e >> 1) + 0) * 2 + (e & 1)].v, o[0][t]);
+      o[1][t] = mfma32(vf[k & 3].v, pf[(2 * (e >> 1) + 1) * 2 + (e & 1)].v, o[1][t]);
+      if (k + 3 < 16) read_v(k + 3);
+      hook(k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  wait_loads();
+  barrier_lds();  // K_0, V_0, K_1 in LDS
+  run_steps([&](auto T, int t) __attribute__((always_inline)) {
+    using TK = std::integral_constant<int, (decltype(T)::value + 2) % 6>;  // K_t+2 (the buffer of K_t-1)
+    using TV = std::integral_constant<int, (decltype(T)::value + 1) % 6>;  // V_t+1, and P_t-1
+    using TR = std::integral_constant<int, (decltype(T)::value + 5) % 6>;  // V_t-1
+    const bool lk = t + 2 < n_it, lv = t + 1 < n_it;
+    TileSrc sk, sv;
+    if (lk) sk = tile_src(std::false_type(), t + 2);
+    if (lv) sv = tile_src(std::true_type(), t + 1);
+    auto load_all = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        if (lk) load_one(std::false_type(), sk, kbuf(TK()), q0 + i);
+#pragma unroll
+      for (int i = 0; i < NLD; ++i)
+        if (lv) load_one(std::true_type(), sv, vbuf(TV()), q0 + i);
+    };
+    // this step's loads: spread over the products when both tiles are one run
+    // of rows, else issued before them
+    const bool wk = t >= 1 && t - 1 < grp_tiles;
+    const bool fast = lk && lv && sk.contiguous && sv.contiguous;
+    if (!fast || !wk) load_all();
+    if (wk) {
+      const char* kbase = sk.base;
+      const char* vbase = sv.base;
+      uint32_t ko = koff0, vo = voff;
+      asm volatile("" : "+v"(ko), "+v"(vo));
+      pv(vbuf(TR()), pbuf(TV()), [&](int k) __attribute__((always_inline)) {
+        if (fast) {
+          if (k < NLD)
+            dma_tile(kbase, kbuf(TK()), q0 + k, ko ^ (64u * uint32_t(k & 3)));
+          else if (k < 2 * NLD)
+            dma_tile(vbase, vbuf(TV()), q0 + k - NLD, vo);
+        }
+      });
+    }
+    // K_t+2 (first read in the next step) and V_t complete; V_t+1, loaded
+    // after K_t+2, may stay in flight
+    if (lv)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      wait_loads();
+    barrier_lds();
+  });
+  // the verdict of each group (in a P buffer no longer read)
+  int* verdict = reinterpret_cast<int*>(P0);
+  float inv[2];
+  bool bad = false;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    bad |= !(l > 0.f && l < 0x1p100f);
+    inv[qb] = 1.f / l;
+#pragma unroll
+    for (int t = 0; t < DTILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bad |= !isfinite(o[qb][t][r]);
+  }
+  const bool wave_bad = __any(bad);
+  if (lane == 0) verdict[grp] = (qbase < n_b && wave_bad) ? 1 : 0;
+  barrier_lds();
+  const bool redo_item = (verdict[0] | verdict[1] | verdict[2] | verdict[3]) != 0;
+  if (grp == 0 && lane == 0) s.redo[blockIdx.x] = redo_item ? 1 : 0;
+  if (redo_item) return;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = qbase + 32 * qb + c32;
+    if (qi >= n_b) continue;
+    float* orow = out + (size_t(b) * n_max + qi) * s.model_width + size_t(h) * DH;
+#pragma unroll
+    for (int t = 0; t < DTILES; ++t)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float4 w;
+        w.x = o[qb][t][4 * rr + 0] * inv[qb];
+        w.y = o[qb][t][4 * rr + 1] * inv[qb];
+        w.z = o[qb][t][4 * rr + 2] * inv[qb];
+        w.w = o[qb][t][4 * rr + 3] * inv[qb];
+        *reinterpret_cast<float4*>(orow + t * 32 + 8 * rr + 4 * g) = w;
+      }
+  }
+}
+
 inline hipStream_t st(void* p) { return static_cast<hipStream_t>(p); }
 
 }  // namespace
@@ -1468,20 +1935,25 @@ int mfma_attend_chunk(const DevState& s, int n_max, int per_seq_rows, const Chun
   const int items = order.count ? order.count : s.batch * order.qtiles;
   if (items == 0) return 0;
   const dim3 grid(unsigned(items) * unsigned(s.heads));
-#define KVC_FLASH_LAUNCH(DH_, WIN_)                                                                      \
+#define KVC_FLASH_LAUNCH(DH_, WIN_, REDO_)                                                               \
   hipLaunchKernelGGL((attend_flash_kernel<DH_, WIN_>), grid, dim3(2 * kChunkQueryTile), 0, st(s.stream), s, n_max, \
-                     per_seq_rows, \
-                     order, static_cast<float*>(out))
+                     per_seq_rows, order, static_cast<float*>(out), REDO_)
   if (s.head_width == 128) {
-    if (s.window)
-      KVC_FLASH_LAUNCH(128, true);
-    else
-      KVC_FLASH_LAUNCH(128, false);
+    if (s.window) {
+      KVC_FLASH_LAUNCH(128, true, nullptr);
+    } else if (s.redo && s.q_bf16) {
+      // the role-split kernel, then the general one for the items it handed back
+      hipLaunchKernelGGL((attend_split_kernel<128>), grid, dim3(2 * kChunkQueryTile), 0, st(s.stream), s, n_max,
+                         per_seq_rows, order, static_cast<float*>(out));
+      KVC_FLASH_LAUNCH(128, false, s.redo);
+    } else {
+      KVC_FLASH_LAUNCH(128, false, nullptr);
+    }
   } else if (s.head_width == 64) {
     if (s.window)
-      KVC_FLASH_LAUNCH(64, true);
+      KVC_FLASH_LAUNCH(64, true, nullptr);
     else
-      KVC_FLASH_LAUNCH(64, false);
+      KVC_FLASH_LAUNCH(64, false, nullptr);
 #undef KVC_FLASH_LAUNCH
   } else {
     return -1;

@@ -141,6 +141,36 @@ def test_flash_chunk_rescales_when_scores_rise():
     assert_parity(to_f64(out)[0], ref["out"], "bf16", "rising scores")
 
 
+def test_flash_chunk_scores_far_above_the_first_keys():
+    """Scores that climb by about 2^200 past the first keys (retained keys 0..63
+    score about -100 in base 2, keys 64..149 about 0, the chunk's own keys about
+    +100) in the first of two sequences, plain scores in the second: a kernel
+    that keeps one reference per query from the first keys would overflow on the
+    first sequence, which must still match the oracle like the second."""
+    import torch
+    H, dh, cut, n = 2, 128, 150, 40
+    D = H * dh
+    eye = torch.eye(D, dtype=torch.bfloat16, device="cuda")
+    params = K.kvc_params_create(eye, eye.clone(), eye.clone())
+    layer = K.kvc_layer_create(params, H, K.KVC_POS_NONE, 10000.0, 256)
+    cache = K.kvc_cache_create(layer, 2, 256, max_chunk_rows=256)
+    a = np.sqrt(100.0 * np.sqrt(dh) / 1.4426950408889634)  # a^2 / sqrt(d_h) = 100 / log2(e)
+    e = np.full(D, a / np.sqrt(dh))
+    x = 0.3 * synth.normal(43, synth.STREAM_X, (2, cut + n, D))
+    x[0, :64] -= e
+    x[0, cut:] += e
+    s, xf = synth.quantize(x, "bf16")
+    xd = torch.from_numpy(s.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    K.kvc_continue_chunk(layer, cache, xd[:, :cut].contiguous())
+    out, _ = K.kvc_continue_chunk(layer, cache, xd[:, cut:].contiguous())
+    w = np.eye(D)
+    o = to_f64(out)
+    for b in range(2):
+        ref = A.causal_layer(xf[b], w, w, w, heads=H, rope=False, rows=range(cut, cut + n))
+        assert np.all(np.isfinite(o[b]))
+        assert_parity(o[b], ref["out"], "bf16", f"seq {b}")
+
+
 @pytest.mark.parametrize("B,n_max,H,rows,cuts", [
     # 2250 rows: a partial last row tile, 54 tiles (not a multiple of the eight XCDs)
     (5, 450, 4, [450, 1, 0, 300, 449], [0, 5, 3, 100, 17]),
