@@ -1537,7 +1537,7 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
     // S^T of the 32 keys at rows 32 KB .. of a K tile into set KB, each K
-    // fragment read two 16-feature steps ahead; hook(u) after step u's MFMAs
+    // fragment read three 16-feature steps ahead; hook(u) after step u's MFMAs
     auto scores = [&](auto KB, const bf16_t* ktile, auto&& hook) __attribute__((always_inline)) {
       constexpr int kb = decltype(KB)::value;
       const bf16_t* kr = ktile + (32 * kb + c32) * DH;
