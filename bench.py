@@ -71,13 +71,13 @@ MEASURED_TRAFFIC = {
                  "kernel_source_sha256": "ff3b3a9411d402a8edf4b3a8f93d5def7cd1c117ebc40b471aaa0ac8c98fb43f"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
     "chunk": {"source": "mfma", "fetch_kib": 299425.9, "fetch_scale": 2.0, "write_kib": 98304.0, "write_scale": 1.0,
-              "kernel_source_sha256": "db9bad238f96167780effc16e3abd5f293b5e6136ab91ed756cc13b266b9eed7"},
+              "kernel_source_sha256": "0845a7fd18e63735d857b27620113c1f4996c918619965860ae6f43370cec219"},
     # attend_split_kernel, suffix chunk (B=8, n=512); the general kernel's launch
     # for handed-back work items (none on this workload) writes nothing and
     # fetches about 30 KiB
     "chunk_attention": {"source": "mfma", "fetch_kib": 338559.2, "fetch_scale": 2.0, "write_kib": 65559.2,
                         "write_scale": 1.0,
-                        "kernel_source_sha256": "db9bad238f96167780effc16e3abd5f293b5e6136ab91ed756cc13b266b9eed7"},
+                        "kernel_source_sha256": "0845a7fd18e63735d857b27620113c1f4996c918619965860ae6f43370cec219"},
 }
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
                   "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}

@@ -1484,7 +1484,6 @@ __global__ __launch_bounds__(2 * kChunkQueryTile) __attribute__((amdgpu_waves_pe
   auto kswz = [](int r) __attribute__((always_inline)) { return (r / RPS) & (SPR - 1); };
   auto vswz = [](int r) __attribute__((always_inline)) { return 4 * ((r / RPS) & (SPR / 4 - 1)); };
   typedef __attribute__((address_space(3))) void lds_void_t;
-  typedef __attribute__((address_space(1))) void glb_void_t;
   auto wait_loads = []() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
   auto barrier_lds = []() __attribute__((always_inline)) {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
