@@ -261,6 +261,115 @@ __device__ __forceinline__ void put_pairs4(const DevState& s, int p, const RowDs
   }
 }
 
+// Rotary factors of eight consecutive pairs of a row (see rope4).
+struct Rope8 {
+  float4 c0, c1, s0, s1;
+};
+__device__ __forceinline__ Rope8 rope8(const DevState& s, int p, const RowDst& d, int pair0) {
+  Rope8 r{make_float4(1.f, 1.f, 1.f, 1.f), make_float4(1.f, 1.f, 1.f, 1.f), make_float4(0.f, 0.f, 0.f, 0.f),
+          make_float4(0.f, 0.f, 0.f, 0.f)};
+  if (d.i < 0 || p >= 2 || !s.rope) return r;
+  const int half = s.head_width >> 1;
+  const int f = pair0 % half;
+  const float4* cp = reinterpret_cast<const float4*>(static_cast<const float*>(s.rope_cos) + size_t(d.pos) * half + f);
+  const float4* sp = reinterpret_cast<const float4*>(static_cast<const float*>(s.rope_sin) + size_t(d.pos) * half + f);
+  r.c0 = cp[0];
+  r.c1 = cp[1];
+  r.s0 = sp[0];
+  r.s1 = sp[1];
+  return r;
+}
+
+// Eight consecutive pairs pair0 .. pair0 + 7 of one head (pair0 % 8 == 0 and
+// d_h / 2 % 8 == 0): the same as two put_pairs4 calls, with 16-byte stores.
+__device__ __forceinline__ void put_pairs8(const DevState& s, int p, const RowDst& d, int pair0, float4 lo0,
+                                           float4 lo1, float4 hi0, float4 hi1, const Rope8& rf, int n_max,
+                                           unsigned long long& bad) {
+  if (d.i < 0) return;
+  const int dh = s.head_width;
+  const int half = dh >> 1;
+  const int h = pair0 / half;
+  const int f = pair0 - h * half;
+  auto note = [&](const float4& v, size_t flat) {
+    if (isfinite((v.x + v.y) + (v.z + v.w))) return;
+    if (!isfinite(v.x)) bad = min(bad, (unsigned long long)flat);
+    else if (!isfinite(v.y)) bad = min(bad, (unsigned long long)(flat + 1));
+    else if (!isfinite(v.z)) bad = min(bad, (unsigned long long)(flat + 2));
+    else if (!isfinite(v.w)) bad = min(bad, (unsigned long long)(flat + 3));
+  };
+  if (p == 3) {
+    const size_t flat = (size_t(d.b) * n_max + d.i) * s.model_width + size_t(h) * dh + f;
+    float* o = static_cast<float*>(s.out_proj_dst) + flat;
+    reinterpret_cast<float4*>(o)[0] = lo0;
+    reinterpret_cast<float4*>(o)[1] = lo1;
+    reinterpret_cast<float4*>(o + half)[0] = hi0;
+    reinterpret_cast<float4*>(o + half)[1] = hi1;
+    note(lo0, flat);
+    note(lo1, flat + 4);
+    note(hi0, flat + half);
+    note(hi1, flat + half + 4);
+    return;
+  }
+  auto rot = [](float4 lo, float4 hi, float4 c, float4 sn, float4& r0, float4& r1) {
+    r0 = make_float4(lo.x * c.x - hi.x * sn.x, lo.y * c.y - hi.y * sn.y, lo.z * c.z - hi.z * sn.z,
+                     lo.w * c.w - hi.w * sn.w);
+    r1 = make_float4(hi.x * c.x + lo.x * sn.x, hi.y * c.y + lo.y * sn.y, hi.z * c.z + lo.z * sn.z,
+                     hi.w * c.w + lo.w * sn.w);
+  };
+  float4 a0 = lo0, a1 = lo1, b0 = hi0, b1 = hi1;
+  if (p < 2 && s.rope) {
+    rot(lo0, hi0, rf.c0, rf.s0, a0, b0);
+    rot(lo1, hi1, rf.c1, rf.s1, a1, b1);
+  }
+  const size_t flat0 = (size_t(d.b * heads_of(s, p) + h) * n_max + d.i) * dh + f;
+  union P8 {
+    uint4 u;
+    bf16_t e[8];
+  };
+  auto pack = [](float4 x, float4 y, float k) {
+    P8 r;
+    r.e[0] = f32_to_bf16(x.x * k);
+    r.e[1] = f32_to_bf16(x.y * k);
+    r.e[2] = f32_to_bf16(x.z * k);
+    r.e[3] = f32_to_bf16(x.w * k);
+    r.e[4] = f32_to_bf16(y.x * k);
+    r.e[5] = f32_to_bf16(y.y * k);
+    r.e[6] = f32_to_bf16(y.z * k);
+    r.e[7] = f32_to_bf16(y.w * k);
+    return r;
+  };
+  if (p == 0) {
+    if (s.q_bf16) {
+      const float sl2 = float(s.scale) * 1.4426950408889634f;
+      bf16_t* q = static_cast<bf16_t*>(s.q) + flat0;
+      *reinterpret_cast<uint4*>(q) = pack(a0, a1, sl2).u;
+      *reinterpret_cast<uint4*>(q + half) = pack(b0, b1, sl2).u;
+    } else {
+      float* q = static_cast<float*>(s.q) + flat0;
+      reinterpret_cast<float4*>(q)[0] = a0;
+      reinterpret_cast<float4*>(q)[1] = a1;
+      reinterpret_cast<float4*>(q + half)[0] = b0;
+      reinterpret_cast<float4*>(q + half)[1] = b1;
+    }
+    note(a0, flat0);
+    note(a1, flat0 + 4);
+    note(b0, flat0 + half);
+    note(b1, flat0 + half + 4);
+  } else {
+    bf16_t* dst = static_cast<bf16_t*>(p == 1 ? s.cand_k : s.cand_v) + flat0;
+    const P8 x = pack(a0, a1, 1.f), y = pack(b0, b1, 1.f);
+    *reinterpret_cast<uint4*>(dst) = x.u;
+    *reinterpret_cast<uint4*>(dst + half) = y.u;
+    auto back = [](const P8& v, int o) {
+      return make_float4(bf16_to_f32(v.e[o]), bf16_to_f32(v.e[o + 1]), bf16_to_f32(v.e[o + 2]), bf16_to_f32(v.e[o + 3]));
+    };
+    note(back(x, 0), flat0);
+    note(back(x, 4), flat0 + 4);
+    note(back(y, 0), flat0 + half);
+    note(back(y, 4), flat0 + half + 4);
+  }
+}
+
 __device__ __forceinline__ void store_pair(const DevState& s, int p, int m, int pair, float lo, float hi, int M,
                                            int n_max, int per_seq_rows) {
   unsigned long long bad = kErrClear, bad_pos = kErrClear;
@@ -713,9 +822,9 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
   __syncthreads();
   // epilogue, one 32-row quarter of the wave's block at a time, through LDS
   // (the K-tile buffers are free now: two waves stage into each).  The wave's 64 columns are the low and
-  // high features of 32 pairs; lane (row r8, c4) then handles four consecutive
-  // pairs of rows r8, r8 + 8, ..: 8 lanes cover one row's 32 pairs, with one
-  // rotary table load per factor and 16-byte stores.
+  // high features of 32 pairs; lane (row r16, c8) then handles eight consecutive
+  // pairs of rows r16, r16 + 16: 4 lanes cover one row's 32 pairs, with 16-byte
+  // stores.
   constexpr int EPS = 64 + 4;  // staging row stride (floats)
   static_assert(2 * 32 * EPS * 4 <= GBM * GLD * 2 && GBM == GBN, "staging of two waves fits one tile buffer");
   bf16_t* stage_base = X0;
@@ -727,9 +836,9 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
   }
   float* ep = reinterpret_cast<float*>(stage_base) + (wave_u & 1) * 32 * EPS;
   const int wrow0 = m0 + __builtin_amdgcn_readfirstlane(wm) * 128;
-  const int r8 = lane >> 3;
-  const int c4 = (lane & 7) * 4;
-  const int pair0 = pair_base + __builtin_amdgcn_readfirstlane(wn) * 32 + c4;
+  const int r16 = lane >> 2;
+  const int c8 = (lane & 3) * 8;
+  const int pair0 = pair_base + __builtin_amdgcn_readfirstlane(wn) * 32 + c8;
   unsigned long long bad = kErrClear, bad_pos = kErrClear;
   // accumulators are only ever indexed by constants (a runtime index would move them to scratch)
   auto stage = [&](const f32x16_t (&q)[2]) {
@@ -746,8 +855,8 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll 1
   for (int i = 0; i < 4; ++i) {
     // the quarter's rotary factors are loaded before its staging barrier
-    RowDst d[4];
-    Rope4 rf[4];
+    RowDst d[2];
+    Rope8 rf[2];
     RowDst mi = mine[0];
     switch (i) {
       case 0: break;
@@ -756,10 +865,10 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
       default: mi = mine[3]; break;
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int row = 8 * k + r8;
+    for (int k = 0; k < 2; ++k) {
+      const int row = 16 * k + r16;
       d[k] = RowDst{__shfl(mi.b, row, 64), __shfl(mi.i, row, 64), __shfl(mi.pos, row, 64)};
-      rf[k] = rope4(s, p, d[k], pair0);
+      rf[k] = rope8(s, p, d[k], pair0);
     }
     switch (i) {
       case 0: stage(acc[0]); break;
@@ -769,10 +878,9 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float* er = ep + (8 * k + r8) * EPS + c4;
-      put_pairs4(s, p, d[k], pair0, *reinterpret_cast<const float4*>(er), *reinterpret_cast<const float4*>(er + 32),
-                 rf[k], n_max, bad);
+    for (int k = 0; k < 2; ++k) {
+      const float4* er = reinterpret_cast<const float4*>(ep + (16 * k + r16) * EPS + c8);
+      put_pairs8(s, p, d[k], pair0, er[0], er[1], er[8], er[9], rf[k], n_max, bad);
     }
     __syncthreads();
   }
