@@ -70,14 +70,14 @@ MEASURED_TRAFFIC = {
     "headline": {"source": "decode", "fetch_kib": 1048893.0, "fetch_scale": 2.0, "write_kib": 512.0, "write_scale": 1.0,
                  "kernel_source_sha256": "ff3b3a9411d402a8edf4b3a8f93d5def7cd1c117ebc40b471aaa0ac8c98fb43f"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
-    "chunk": {"source": "mfma", "fetch_kib": 300561.5, "fetch_scale": 2.0, "write_kib": 98304.0, "write_scale": 1.0,
-              "kernel_source_sha256": "57778a14048ce1a844fe49aba2dad365a7935d528bd363b149e21e84f00fc5b8"},
+    "chunk": {"source": "mfma", "fetch_kib": 299386.8, "fetch_scale": 2.0, "write_kib": 98304.3, "write_scale": 1.0,
+              "kernel_source_sha256": "a3d8f0e28730fbc01dc81c7087306a226964d356e56e9b4f19a559d97973d6aa"},
     # attend_split_kernel, suffix chunk (B=8, n=512); the general kernel's launch
     # for handed-back work items (none on this workload) writes nothing and
     # fetches about 30 KiB
-    "chunk_attention": {"source": "mfma", "fetch_kib": 338568.2, "fetch_scale": 2.0, "write_kib": 65563.2,
+    "chunk_attention": {"source": "mfma", "fetch_kib": 338571.3, "fetch_scale": 2.0, "write_kib": 65557.2,
                         "write_scale": 1.0,
-                        "kernel_source_sha256": "57778a14048ce1a844fe49aba2dad365a7935d528bd363b149e21e84f00fc5b8"},
+                        "kernel_source_sha256": "a3d8f0e28730fbc01dc81c7087306a226964d356e56e9b4f19a559d97973d6aa"},
 }
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
                   "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}

@@ -824,7 +824,9 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
   // (the K-tile buffers are free now: two waves stage into each).  The wave's 64 columns are the low and
   // high features of 32 pairs; lane (row r16, c8) then handles eight consecutive
   // pairs of rows r16, r16 + 16: 4 lanes cover one row's 32 pairs, with 16-byte
-  // stores.
+  // stores.  A wave reads back only the block it staged itself, and its LDS
+  // operations complete in order, so the quarters need no barrier: the waves
+  // stage, rotate and store independently, their stores left in flight.
   constexpr int EPS = 64 + 4;  // staging row stride (floats)
   static_assert(2 * 32 * EPS * 4 <= GBM * GLD * 2 && GBM == GBN, "staging of two waves fits one tile buffer");
   bf16_t* stage_base = X0;
@@ -876,13 +878,11 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
       case 2: stage(acc[2]); break;
       default: stage(acc[3]); break;
     }
-    __syncthreads();
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const float4* er = reinterpret_cast<const float4*>(ep + (16 * k + r16) * EPS + c8);
       put_pairs8(s, p, d[k], pair0, er[0], er[1], er[8], er[9], rf[k], n_max, bad);
     }
-    __syncthreads();
   }
   flush_bad(s, p, bad, bad_pos);
 }
