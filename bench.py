@@ -71,13 +71,13 @@ MEASURED_TRAFFIC = {
                  "kernel_source_sha256": "ff3b3a9411d402a8edf4b3a8f93d5def7cd1c117ebc40b471aaa0ac8c98fb43f"},
     # project_wide_kernel, suffix chunk (B=8, n=512)
     "chunk": {"source": "mfma", "fetch_kib": 299386.8, "fetch_scale": 2.0, "write_kib": 98304.3, "write_scale": 1.0,
-              "kernel_source_sha256": "a3d8f0e28730fbc01dc81c7087306a226964d356e56e9b4f19a559d97973d6aa"},
+              "kernel_source_sha256": "5e828e7b7beca4c6421b041f2b511451a73ca3425226d96f4f1cf33dd184128b"},
     # attend_split_kernel, suffix chunk (B=8, n=512); the general kernel's launch
     # for handed-back work items (none on this workload) writes nothing and
     # fetches about 30 KiB
     "chunk_attention": {"source": "mfma", "fetch_kib": 338571.3, "fetch_scale": 2.0, "write_kib": 65557.2,
                         "write_scale": 1.0,
-                        "kernel_source_sha256": "a3d8f0e28730fbc01dc81c7087306a226964d356e56e9b4f19a559d97973d6aa"},
+                        "kernel_source_sha256": "5e828e7b7beca4c6421b041f2b511451a73ca3425226d96f4f1cf33dd184128b"},
 }
 KERNEL_SOURCES = {"decode": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_decode.hip"),
                   "mfma": os.path.join(ROOT, "incremental_kv_cache_amd", "csrc", "kvc_mfma.hip")}

@@ -856,7 +856,7 @@ __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(2, 
   for (int i = 0; i < 4; ++i) mine[i] = row_dst(s, p, wrow0 + i * 32 + c32, M, n_max, per_seq_rows, bad_pos);
 #pragma unroll 1
   for (int i = 0; i < 4; ++i) {
-    // the quarter's rotary factors are loaded before its staging barrier
+    // the quarter's rotary factors are loaded before it is staged
     RowDst d[2];
     Rope8 rf[2];
     RowDst mi = mine[0];
